@@ -1,0 +1,16 @@
+"""fp64 CPU oracle of the KDA core.
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, by __graft_entry__.smoke() and by
+bench.py's CPU-baseline leg, never by the library.  It shares no code, header,
+table or helper with the HIP path.
+
+* `gate`, `prefill`, `decode` call the plain C recurrence in kda_oracle.c
+  (token by token, fp64).
+* `chunked.prefill_chunked` is an independent fp64 chunked form used only to
+  pin the recurrence (the two must agree for every chunk size).
+
+Every function is pinned by a CPU test (closed forms, special cases, brute
+force, the audit page's printed exp(A_log) statistics); none is "parity
+unpinned".
+"""
+from .api import gate, prefill, decode, build_oracle, oracle_lib_path  # noqa: F401
