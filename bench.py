@@ -1,0 +1,220 @@
+#!/usr/bin/env python3
+"""KDA core benchmark on one MI355X.
+
+A step is one pass of the prefill hot path over one batch: kda_gate (raw
+gate/beta logits -> g, beta) then kda_chunk_prefill, on the K3-layer prefill
+workload (one sequence, T=4096, H=96, d=128, bf16 q/k/v, fp32 gate logits,
+zero initial state, bf16 o, fp32 final state).  `value` is sequence tokens/s
+of that step, inputs already resident in HBM.
+
+The same JSON line carries
+  roofline      the chunk-prefill kernel: algorithmic HBM bytes per launch /
+                its average launch time (HIP events on the launch stream),
+                against 8 TB/s; plus its algorithmic MFMA rate
+  decode        kda_recurrent_decode on 256 sequences x 96 heads (fp32 state
+                [256,96,128,128] updated in place), 64 steps: state-update GB/s
+  cpu_baseline  the fp64 oracle (gate + token-by-token recurrence) on a
+                bounded sample of the same workload, on this host's cores.
+Timing follows the audit page's protocol shape (warmup, repeated timed
+launches, event timing, output buffers reused).
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KDA prefill tokens/s (H=96,d=128) + decode state-update HBM GB/s"
+HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0
+
+T, H, D, C = 4096, 96, 128, 64
+# algorithmic bytes of one chunk-prefill launch: per token q,k,v bf16 + g f32
+# + beta f32 + o bf16, plus the fp32 final state written once (zero initial state)
+PREFILL_TOKEN_BYTES = H * (3 * D * 2 + D * 4 + 4 + D * 2)            # 147,840
+PREFILL_BYTES = T * PREFILL_TOKEN_BYTES + H * D * D * 4               # 611,844,096
+# algorithmic MACs per (chunk, head) at C=64: A 258,048, P 266,240, solve 41,664,
+# U 258,048, W 258,048, W.S / Qt.S / Khat^T.Delta 1,048,576 each, P.Delta 266,240
+MAC_PER_CHUNK_HEAD = 4_494_016
+PREFILL_FLOPS = 2 * MAC_PER_CHUNK_HEAD * (T // C) * H                 # 5.52e10
+# decode: per (sequence, head, step) state read + write, q/k/v bf16, g f32, beta, o bf16
+DEC_N, DEC_STEPS = 256, 64
+DEC_PAIR_BYTES = 2 * D * D * 4 + 3 * D * 2 + D * 4 + 4 + D * 2       # 132,612
+DEC_STEP_BYTES = DEC_N * H * DEC_PAIR_BYTES                           # 3,259,072,512
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--repeats", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=96,
+                    help="heads of the workload the CPU oracle runs (sample)")
+    return ap.parse_args()
+
+
+def bench_prefill(args, torch, kda, synth):
+    dev = "cuda:0"
+    dr = synth.draw_config(1, device=dev)
+    cu_h = dr.cu_seqlens
+    cu_d = cu_h.to(dev)
+    g = torch.empty((T, H, D), dtype=torch.float32, device=dev)
+    beta = torch.empty((T, H), dtype=torch.float32, device=dev)
+    o = torch.empty((T, H, D), dtype=torch.bfloat16, device=dev)
+    Sf = torch.empty((1, H, D, D), dtype=torch.float32, device=dev)
+
+    def gate():
+        kda.gate(dr.x, dr.b, dr.A_log, dr.dt_bias, g_out=g, beta_out=beta)
+
+    def prefill():
+        kda.chunk_prefill(dr.q, dr.k, dr.v, g, beta, cu_d, None, out=o, final_state=Sf,
+                          cu_seqlens_host=cu_h)
+
+    for _ in range(args.warmup):
+        gate()
+        prefill()
+    torch.cuda.synchronize()
+    step_ms, chunk_ms, gate_ms = [], [], []
+    for _ in range(args.repeats):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3 * args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            ev[3 * i].record()
+            gate()
+            ev[3 * i + 1].record()
+            prefill()
+            ev[3 * i + 2].record()
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) * 1e3 / args.steps
+        for i in range(args.steps):
+            gate_ms.append(ev[3 * i].elapsed_time(ev[3 * i + 1]))
+            chunk_ms.append(ev[3 * i + 1].elapsed_time(ev[3 * i + 2]))
+            step_ms.append(ev[3 * i].elapsed_time(ev[3 * i + 2]))
+        step_ms_wall = wall
+    return dict(step_ms=sum(step_ms) / len(step_ms), chunk_ms=sum(chunk_ms) / len(chunk_ms),
+                gate_ms=sum(gate_ms) / len(gate_ms), wall_ms=step_ms_wall,
+                p95_step_ms=sorted(step_ms)[int(0.95 * (len(step_ms) - 1))])
+
+
+def bench_decode(args, torch, kda, synth):
+    dev = "cuda:0"
+    c = synth.CONFIGS[4]
+    A_log, dt_bias, state = synth.draw_decode_params(DEC_N, H, seed=c["seed"], device=dev)
+    steps = []
+    for s in range(DEC_STEPS):
+        st = synth.draw_decode_step(DEC_N, H, s, seed=c["seed"], device=dev)
+        g, beta = kda.gate(st.x, st.b, A_log, dt_bias)
+        steps.append((st.q, st.k, st.v, g, beta))
+        del st
+    o = torch.empty((DEC_N, H, D), dtype=torch.bfloat16, device=dev)
+    for s in range(min(args.warmup, DEC_STEPS)):
+        q, k, v, g, beta = steps[s]
+        kda.recurrent_decode(q, k, v, g, beta, state, out=o)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(args.repeats):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(DEC_STEPS + 1)]
+        ev[0].record()
+        for s in range(DEC_STEPS):
+            q, k, v, g, beta = steps[s]
+            kda.recurrent_decode(q, k, v, g, beta, state, out=o)
+            ev[s + 1].record()
+        torch.cuda.synchronize()
+        times += [ev[s].elapsed_time(ev[s + 1]) for s in range(DEC_STEPS)]
+    ms = sum(times) / len(times)
+    gbs = DEC_STEP_BYTES / (ms * 1e-3) / 1e9
+    return dict(ms_per_step=ms, GBps=gbs, frac=gbs / HBM_PEAK_GBS, steps=DEC_STEPS,
+                bytes_per_step=DEC_STEP_BYTES)
+
+
+def cpu_baseline(args, synth):
+    """fp64 oracle on `cpu_heads` of the 96 heads of the same T=4096 workload."""
+    import numpy as np
+    import torch
+    import oracle
+    nh = max(1, min(args.cpu_heads, H))
+    dr = synth.draw_config(1, device="cpu")
+    heads = list(range(nh))
+    x = dr.x[:, heads].contiguous()
+    b = dr.b[:, heads].contiguous()
+    q = dr.q[:, heads].double().numpy()
+    k = dr.k[:, heads].double().numpy()
+    v = dr.v[:, heads].double().numpy()
+    t0 = time.perf_counter()
+    g, beta = oracle.gate(x, b, dr.A_log[heads], dr.dt_bias[heads])
+    o, S, threads = oracle.prefill(q, k, v, g, beta, dr.cu_seqlens, return_threads=True)
+    dt = time.perf_counter() - t0
+    full_s = dt * H / nh
+    return {"value": T / full_s, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": "T=4096 tokens on %d of 96 heads (fp64 gate + token-by-token recurrence), "
+                      "%.1f s, scaled to 96 heads" % (nh, dt)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import gated_delta_rule_58_amd as kda
+    import synth
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    kda.lib()
+    pre = bench_prefill(args, torch, kda, synth)
+    print("prefill: step %.4f ms (gate %.4f, chunk %.4f), p95 %.4f ms" %
+          (pre["step_ms"], pre["gate_ms"], pre["chunk_ms"], pre["p95_step_ms"]),
+          file=sys.stderr, flush=True)
+    dec = bench_decode(args, torch, kda, synth)
+    print("decode: %.4f ms/step, %.1f GB/s" % (dec["ms_per_step"], dec["GBps"]),
+          file=sys.stderr, flush=True)
+    chunk_s = pre["chunk_ms"] * 1e-3
+    ach = PREFILL_BYTES / chunk_s / 1e9
+    mfma = PREFILL_FLOPS / chunk_s / 1e12
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args, synth)
+    line = {
+        "metric": METRIC,
+        "value": T / (pre["step_ms"] * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": pre["step_ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16-mfma/f32-acc (bf16 q/k/v/o, f32 g/beta/state)",
+        "data": "synthetic",
+        "config": {"workload": "k3-layer-prefill T=4096 H=96 d=128: kda_gate + kda_chunk_prefill",
+                   "T": T, "H": H, "d": D, "chunk": C, "qkv": "bf16", "o": "bf16",
+                   "gate_logits": "f32", "initial_state": "zero", "repeats": args.repeats},
+        "prefill": {"step_ms": pre["step_ms"], "p95_step_ms": pre["p95_step_ms"],
+                    "chunk_kernel_ms": pre["chunk_ms"], "gate_kernel_ms": pre["gate_ms"],
+                    "prefill_only_tokens_per_s": T / chunk_s},
+        "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": ach / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "chunk_kernel (kda_chunk_prefill)",
+                     "alg_bytes_per_launch": PREFILL_BYTES},
+        "roofline_mfma": {"achieved": mfma, "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                          "frac": mfma / MFMA_F16_PEAK_TFLOPS,
+                          "alg_flops_per_launch": PREFILL_FLOPS},
+        "decode": {"workload": "256 seqs x 96 heads x 1 token, 64 steps, fp32 state in place",
+                   "ms_per_step": dec["ms_per_step"], "GBps": dec["GBps"], "frac": dec["frac"],
+                   "bytes_per_step": DEC_STEP_BYTES},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,155 @@
+"""ctypes binding of libkda.so (same names as the C entry points)."""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+KDA_F32 = 0
+KDA_BF16 = 1
+_STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARG", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_DTYPE",
+           4: "KDA_ERR_UNSUPPORTED", 5: "KDA_ERR_ALIGNMENT", 7: "KDA_ERR_LAUNCH"}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+_vp = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+
+
+class KdaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("%s: %s" % (_STATUS.get(status, str(status)), message))
+        self.status = status
+
+
+def lib_path() -> str:
+    return os.path.join(_HERE, "libkda.so")
+
+
+def lib():
+    """Load libkda.so (raises if it has not been built)."""
+    global _LIB
+    if _LIB is None:
+        path = lib_path()
+        if not os.path.exists(path):
+            raise ImportError("libkda.so not built: run __graft_entry__.build() or "
+                              "python gated_delta_rule_58_amd/build.py")
+        L = ctypes.CDLL(path)
+        L.kda_last_error.restype = ctypes.c_char_p
+        L.kda_last_error.argtypes = []
+        L.kda_version.restype = ctypes.c_char_p
+        L.kda_version.argtypes = []
+        L.kda_gate.restype = ctypes.c_int
+        L.kda_gate.argtypes = [_vp, ctypes.c_int, _vp, ctypes.c_int, _vp, _i64, _vp, _i64, _vp,
+                               _vp, _i64, _i32, _i32, _vp]
+        L.kda_chunk_prefill.restype = ctypes.c_int
+        L.kda_chunk_prefill.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _vp, _i32,
+                                        _vp, _vp, _vp, ctypes.c_int, _i64, _i32, _i32, _i32,
+                                        ctypes.c_float, _vp]
+        L.kda_recurrent_decode.restype = ctypes.c_int
+        L.kda_recurrent_decode.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _vp,
+                                           ctypes.c_int, _i32, _i32, _i32, _i32, ctypes.c_float,
+                                           _vp]
+        _LIB = L
+    return _LIB
+
+
+def exported_symbols():
+    return ["kda_last_error", "kda_version", "kda_gate", "kda_chunk_prefill",
+            "kda_recurrent_decode"]
+
+
+def _check(status: int):
+    if status != 0:
+        raise KdaError(status, lib().kda_last_error().decode())
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return KDA_F32
+    if t.dtype == torch.bfloat16:
+        return KDA_BF16
+    raise TypeError("unsupported dtype %s (float32 or bfloat16)" % t.dtype)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def gate(x: torch.Tensor, b: torch.Tensor, A_log: torch.Tensor, dt_bias: torch.Tensor,
+         g_out: Optional[torch.Tensor] = None, beta_out: Optional[torch.Tensor] = None
+         ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """kda_gate: x [T,H,d], b [T,H] -> g [T,H,d] fp32, beta [T,H] fp32."""
+    T, H, d = x.shape
+    if g_out is None:
+        g_out = torch.empty((T, H, d), dtype=torch.float32, device=x.device)
+    if beta_out is None:
+        beta_out = torch.empty((T, H), dtype=torch.float32, device=x.device)
+    st = lib().kda_gate(_ptr(x), _dt(x), _ptr(b), _dt(b), _ptr(A_log), A_log.numel(),
+                        _ptr(dt_bias), dt_bias.numel(), _ptr(g_out), _ptr(beta_out), T, H, d,
+                        _stream(x.device))
+    _check(st)
+    return g_out, beta_out
+
+
+def chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                  beta: torch.Tensor, cu_seqlens: Optional[torch.Tensor] = None,
+                  initial_state: Optional[torch.Tensor] = None, output_final_state: bool = True,
+                  scale: float = 1.0, o_dtype: Optional[torch.dtype] = None,
+                  out: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
+                  cu_seqlens_host: Optional[torch.Tensor] = None):
+    """kda_chunk_prefill on packed [T_tot, H, d] tensors.
+
+    cu_seqlens: int32 [N+1] (device); None means one sequence of length T_tot.
+    Returns (o [T_tot,H,dv], final_state [N,H,dk,dv] or None).
+    """
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    dev = q.device
+    if cu_seqlens is None:
+        cu_seqlens_host = torch.tensor([0, T], dtype=torch.int32)
+        cu_seqlens = cu_seqlens_host.to(dev)
+    if cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    if cu_seqlens_host is None:
+        cu_seqlens_host = cu_seqlens.cpu()
+    N = cu_seqlens.numel() - 1
+    o_dtype = o_dtype or q.dtype
+    if out is None:
+        out = torch.empty((T, H, dv), dtype=o_dtype, device=dev)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    hp = cu_seqlens_host.contiguous()
+    st = lib().kda_chunk_prefill(
+        _ptr(q), _ptr(k), _ptr(v), _dt(q), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
+        ctypes.cast(hp.data_ptr(), _vp), N, _ptr(initial_state), _ptr(final_state), _ptr(out),
+        _dt(out), T, H, dk, dv, float(scale), _stream(dev))
+    _check(st)
+    return out, final_state
+
+
+def recurrent_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                     beta: torch.Tensor, state: torch.Tensor, scale: float = 1.0,
+                     o_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None):
+    """kda_recurrent_decode: q/k/v [N,H,d], state [N,H,dk,dv] updated in place. Returns o."""
+    N, H, dk = q.shape
+    dv = v.shape[2]
+    if out is None:
+        out = torch.empty((N, H, dv), dtype=o_dtype or q.dtype, device=q.device)
+    st = lib().kda_recurrent_decode(_ptr(q), _ptr(k), _ptr(v), _dt(q), _ptr(g), _ptr(beta),
+                                    _ptr(state), _ptr(out), _dt(out), N, H, dk, dv, float(scale),
+                                    _stream(q.device))
+    _check(st)
+    return out

@@ -1,0 +1,158 @@
+// C ABI of libkda: argument validation, error reporting and launches.
+//
+// Every entry point validates all of its arguments before touching the HIP
+// runtime, so a refused call launches nothing, writes nothing and makes no
+// HIP call at all (which also lets the refusals be tested on a machine with
+// no GPU).
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "kda_internal.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+kda_status fail(kda_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+kda_status ok() {
+  g_err[0] = '\0';
+  return KDA_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool known_dtype(kda_dtype d) { return d == KDA_F32 || d == KDA_BF16; }
+
+kda_status launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(KDA_ERR_LAUNCH, "%s: launch failed: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kda_last_error(void) { return g_err; }
+
+const char* kda_version(void) { return "kda-gfx950 0.1"; }
+
+kda_status kda_gate(const void* x, kda_dtype x_dt, const void* b, kda_dtype b_dt,
+                    const float* A_log, int64_t A_log_len, const float* dt_bias,
+                    int64_t dt_bias_len, float* g_out, float* beta_out, int64_t n_tok,
+                    int32_t H, int32_t d, void* stream) {
+  if (n_tok < 0 || H <= 0 || d <= 0)
+    return fail(KDA_ERR_INVALID_ARG, "kda_gate: need n_tok >= 0, H > 0, d > 0 (got %lld, %d, %d)",
+                (long long)n_tok, H, d);
+  if (!known_dtype(x_dt) || !known_dtype(b_dt))
+    return fail(KDA_ERR_DTYPE, "kda_gate: x_dt and b_dt must be KDA_F32 or KDA_BF16");
+  if (A_log_len != H)
+    return fail(KDA_ERR_SHAPE,
+                "kda_gate: A_log has %lld values but H = %d; A_log must be one value per head "
+                "([H]); a per-channel or checkpoint-shaped A_log is refused, not reshaped",
+                (long long)A_log_len, H);
+  if (dt_bias_len != (int64_t)H * d)
+    return fail(KDA_ERR_SHAPE, "kda_gate: dt_bias has %lld values, need H*d = %lld",
+                (long long)dt_bias_len, (long long)H * d);
+  if (d % 4 != 0) return fail(KDA_ERR_UNSUPPORTED, "kda_gate: d must be a multiple of 4 (got %d)", d);
+  if (!A_log || !dt_bias) return fail(KDA_ERR_INVALID_ARG, "kda_gate: A_log/dt_bias is NULL");
+  if (n_tok == 0) return ok();
+  if (!x || !b || !g_out || !beta_out)
+    return fail(KDA_ERR_INVALID_ARG, "kda_gate: x, b, g_out and beta_out must be non-NULL");
+  if (!aligned(x, x_dt == KDA_BF16 ? 8 : 16) || !aligned(g_out, 16) || !aligned(dt_bias, 16))
+    return fail(KDA_ERR_ALIGNMENT, "kda_gate: x, g_out and dt_bias must be 16-byte aligned "
+                                   "(8-byte for bf16 x)");
+  return launched(kda::launch_gate(x, x_dt == KDA_BF16, b, b_dt == KDA_BF16, A_log, dt_bias, g_out,
+                                   beta_out, n_tok, H, d, static_cast<hipStream_t>(stream)),
+                  "kda_gate");
+}
+
+kda_status kda_chunk_prefill(const void* q, const void* k, const void* v, kda_dtype qkv_dt,
+                             const float* g, const float* beta, const int32_t* cu_seqlens,
+                             const int32_t* cu_seqlens_host, int32_t N,
+                             const float* initial_state, float* final_state, void* o,
+                             kda_dtype o_dt, int64_t T_tot, int32_t H, int32_t dk,
+                             int32_t dv, float scale, void* stream) {
+  if (N <= 0 || H <= 0 || T_tot < 0)
+    return fail(KDA_ERR_INVALID_ARG, "kda_chunk_prefill: need N > 0, H > 0, T_tot >= 0 "
+                                     "(got %d, %d, %lld)", N, H, (long long)T_tot);
+  if (!known_dtype(qkv_dt) || !known_dtype(o_dt))
+    return fail(KDA_ERR_DTYPE, "kda_chunk_prefill: qkv_dt and o_dt must be KDA_F32 or KDA_BF16");
+  if (dk != 128 || dv != 128)
+    return fail(KDA_ERR_UNSUPPORTED, "kda_chunk_prefill: only dk = dv = 128 is implemented "
+                                     "(got %d, %d)", dk, dv);
+  if (!(scale == scale) || scale > 3.0e38f || scale < -3.0e38f)
+    return fail(KDA_ERR_INVALID_ARG, "kda_chunk_prefill: scale must be finite");
+  if (T_tot > ((int64_t)1 << 31) - 1)
+    return fail(KDA_ERR_UNSUPPORTED, "kda_chunk_prefill: T_tot must fit in int32");
+  if (!cu_seqlens) return fail(KDA_ERR_INVALID_ARG, "kda_chunk_prefill: cu_seqlens is NULL");
+  if (cu_seqlens_host) {
+    if (cu_seqlens_host[0] != 0 || cu_seqlens_host[N] != T_tot)
+      return fail(KDA_ERR_SHAPE, "kda_chunk_prefill: cu_seqlens must start at 0 and end at "
+                                 "T_tot = %lld (got %d .. %d)", (long long)T_tot,
+                  cu_seqlens_host[0], cu_seqlens_host[N]);
+    for (int32_t n = 0; n < N; ++n)
+      if (cu_seqlens_host[n + 1] < cu_seqlens_host[n])
+        return fail(KDA_ERR_SHAPE, "kda_chunk_prefill: cu_seqlens decreases at index %d", n);
+  }
+  if (T_tot > 0 && (!q || !k || !v || !g || !beta || !o))
+    return fail(KDA_ERR_INVALID_ARG, "kda_chunk_prefill: q, k, v, g, beta and o must be non-NULL");
+  const void* ptrs[] = {q, k, v, g, beta, o, initial_state, final_state, cu_seqlens};
+  for (const void* p : ptrs)
+    if (p && !aligned(p, 16) && p != beta && p != cu_seqlens)
+      return fail(KDA_ERR_ALIGNMENT, "kda_chunk_prefill: tensors must be 16-byte aligned");
+  if (!aligned(beta, 4) || !aligned(cu_seqlens, 4))
+    return fail(KDA_ERR_ALIGNMENT, "kda_chunk_prefill: beta/cu_seqlens must be 4-byte aligned");
+  return launched(kda::launch_chunk_prefill(q, k, v, qkv_dt == KDA_BF16, g, beta, cu_seqlens, N,
+                                            initial_state, final_state, o, o_dt == KDA_BF16, T_tot,
+                                            H, scale, static_cast<hipStream_t>(stream)),
+                  "kda_chunk_prefill");
+}
+
+kda_status kda_recurrent_decode(const void* q, const void* k, const void* v, kda_dtype qkv_dt,
+                                const float* g, const float* beta, float* state, void* o,
+                                kda_dtype o_dt, int32_t N, int32_t H, int32_t dk, int32_t dv,
+                                float scale, void* stream) {
+  if (N < 0 || H <= 0)
+    return fail(KDA_ERR_INVALID_ARG, "kda_recurrent_decode: need N >= 0, H > 0 (got %d, %d)", N, H);
+  if (!known_dtype(qkv_dt) || !known_dtype(o_dt))
+    return fail(KDA_ERR_DTYPE, "kda_recurrent_decode: qkv_dt and o_dt must be KDA_F32 or KDA_BF16");
+  if (dk != 128 || dv != 128)
+    return fail(KDA_ERR_UNSUPPORTED, "kda_recurrent_decode: only dk = dv = 128 is implemented "
+                                     "(got %d, %d)", dk, dv);
+  if (!(scale == scale) || scale > 3.0e38f || scale < -3.0e38f)
+    return fail(KDA_ERR_INVALID_ARG, "kda_recurrent_decode: scale must be finite");
+  if (N == 0) return ok();
+  if (!q || !k || !v || !g || !beta || !state || !o)
+    return fail(KDA_ERR_INVALID_ARG, "kda_recurrent_decode: all tensor pointers must be non-NULL");
+  const void* ptrs[] = {q, k, v, g, state, o};
+  for (const void* p : ptrs)
+    if (!aligned(p, 16))
+      return fail(KDA_ERR_ALIGNMENT, "kda_recurrent_decode: tensors must be 16-byte aligned");
+  const char* sb = reinterpret_cast<const char*>(state);
+  const char* se = sb + (size_t)N * H * dk * dv * sizeof(float);
+  const size_t qkv_es = qkv_dt == KDA_BF16 ? 2 : 4;
+  const size_t o_es = o_dt == KDA_BF16 ? 2 : 4;
+  struct { const void* p; size_t n; } others[] = {
+      {q, (size_t)N * H * dk * qkv_es}, {k, (size_t)N * H * dk * qkv_es},
+      {v, (size_t)N * H * dv * qkv_es}, {g, (size_t)N * H * dk * 4},
+      {beta, (size_t)N * H * 4},        {o, (size_t)N * H * dv * o_es}};
+  for (auto& r : others) {
+    const char* b0 = static_cast<const char*>(r.p);
+    if (b0 < se && sb < b0 + r.n)
+      return fail(KDA_ERR_INVALID_ARG, "kda_recurrent_decode: state overlaps another tensor");
+  }
+  return launched(kda::launch_decode(q, k, v, qkv_dt == KDA_BF16, g, beta, state, o,
+                                     o_dt == KDA_BF16, N, H, scale,
+                                     static_cast<hipStream_t>(stream)),
+                  "kda_recurrent_decode");
+}
+
+}  // extern "C"

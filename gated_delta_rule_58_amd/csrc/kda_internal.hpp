@@ -1,0 +1,25 @@
+// Internal declarations shared by the HIP translation units of libkda.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kda.h"
+
+namespace kda {
+
+// ---- launchers (one per kernel family); return hipSuccess or the launch error
+hipError_t launch_gate(const void* x, bool x_bf16, const void* b, bool b_bf16, const float* A_log,
+                       const float* dt_bias, float* g, float* beta, int64_t n_tok, int H, int d,
+                       hipStream_t s);
+
+hipError_t launch_decode(const void* q, const void* k, const void* v, bool qkv_bf16,
+                         const float* g, const float* beta, float* state, void* o, bool o_bf16,
+                         int N, int H, float scale, hipStream_t s);
+
+hipError_t launch_chunk_prefill(const void* q, const void* k, const void* v, bool qkv_bf16,
+                                const float* g, const float* beta, const int32_t* cu, int N,
+                                const float* S0, float* S_final, void* o, bool o_bf16,
+                                int64_t T_tot, int H, float scale, hipStream_t s);
+
+}  // namespace kda

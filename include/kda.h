@@ -1,0 +1,148 @@
+/*
+ * kda.h - C ABI of the MI355X (gfx950) Kimi Delta Attention (KDA) core.
+ *
+ * KDA is the per-channel gated delta rule.  For one sequence and one head,
+ * with a d_k x d_v fp32 state S (element S[c][j]: c key channel, j value
+ * channel) and, per token t, alpha_t = exp(g_t) (one decay per key channel):
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
+ *     o_t = scale * S_t^T q_t
+ *
+ * The code audit of the Kimi remote modelling code (finding
+ * "dual-kda-execution-regimes") splits it into a chunked form for
+ * training/prefill and a fused recurrent form for one-token cached decode;
+ * kda_chunk_prefill and kda_recurrent_decode are those two forms, and
+ * kda_gate produces their g and beta inputs.  The Kimi K3 artifact audit
+ * (§4.1 KDA tensor table, §5.2 shape table, §7.1 FlashKDA interface) fixes
+ * the shapes: 96 heads of 128 dims, per-head A_log, per-(head,channel)
+ * dt_bias, bf16 q/k/v, fp32 A_log/dt_bias, variable-length batches and
+ * initial/final recurrent state.
+ *
+ * Conventions for every entry point:
+ *   - Tensors are dense, row-major (last index fastest), on the current HIP
+ *     device, and must not overlap unless stated.  The library never
+ *     allocates, frees or copies memory and never synchronises the stream.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = legacy default
+ *     stream) and runs asynchronously; outputs are ready when the stream is.
+ *   - Each call validates all arguments first.  On any status other than
+ *     KDA_OK returned before launch, nothing was launched and no output was
+ *     written.  KDA_ERR_LAUNCH means the kernel launch itself failed.
+ *   - kda_last_error() returns a thread-local message for the last failure.
+ *   - Inputs to the recurrence are assumed finite with g <= 0 and beta in
+ *     [0,1] (the gate produces exactly these); other values are not
+ *     checked and propagate into the outputs.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KDA_OK = 0,
+  KDA_ERR_INVALID_ARG = 1, /* null pointer, negative size, bad scale       */
+  KDA_ERR_SHAPE = 2,       /* inconsistent sizes (e.g. A_log length != H)  */
+  KDA_ERR_DTYPE = 3,       /* dtype code not supported for this argument   */
+  KDA_ERR_UNSUPPORTED = 4, /* valid but not implemented (e.g. d != 128)    */
+  KDA_ERR_ALIGNMENT = 5,   /* pointer not 16-byte aligned                  */
+  KDA_ERR_LAUNCH = 7       /* the HIP launch failed (see kda_last_error)   */
+} kda_status;
+
+typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+
+/* Thread-local text of the last non-OK status ("" if none). */
+const char* kda_last_error(void);
+
+/* Library version string. */
+const char* kda_version(void);
+
+/*
+ * kda_gate - log-decay and beta gate (one elementwise pass).
+ *
+ *   g[t,h,c]  = -exp(A_log[h]) * softplus(x[t,h,c] + dt_bias[h,c])
+ *   beta[t,h] = sigmoid(b[t,h])                     (computed in fp32)
+ *
+ * A_log holds one value per head and dt_bias one per (head, channel): the
+ * artifact audit's §5.2 shape table lists A_log as [H] in the model config,
+ * remote code and FlashKDA's host check, and dt_bias [12288] = [96,128].
+ * The checkpoint's own A_log is [128]; this library refuses any length but H
+ * (KDA_ERR_SHAPE) rather than guess a reshape, as that section advises.
+ * beta is squashed here, once, in fp32 (Model-Optimizer PR #2749 review,
+ * the KDA beta fix); the prefill and decode calls take it post-sigmoid and
+ * never apply a sigmoid themselves.
+ *
+ *   x        [n_tok, H, d]  gate logits, dtype x_dt (KDA_F32 or KDA_BF16)
+ *   b        [n_tok, H]     beta logits, dtype b_dt (KDA_F32 or KDA_BF16)
+ *   A_log    [A_log_len]    fp32, A_log_len must equal H
+ *   dt_bias  [dt_bias_len]  fp32, dt_bias_len must equal H*d
+ *   g_out    [n_tok, H, d]  fp32 output
+ *   beta_out [n_tok, H]     fp32 output
+ * Requires d % 4 == 0 and 16-byte aligned x/g_out (8-byte for bf16 x).
+ * n_tok == 0 is a no-op.
+ */
+kda_status kda_gate(const void* x, kda_dtype x_dt, const void* b, kda_dtype b_dt,
+                    const float* A_log, int64_t A_log_len, const float* dt_bias,
+                    int64_t dt_bias_len, float* g_out, float* beta_out, int64_t n_tok,
+                    int32_t H, int32_t d, void* stream);
+
+/*
+ * kda_chunk_prefill - chunked KDA over a packed variable-length batch.
+ *
+ * Sequence n owns tokens cu_seqlens[n] .. cu_seqlens[n+1]-1 of the packed
+ * token axis.  Each (sequence, head) starts from initial_state[n,h] (zeros
+ * if initial_state is NULL), runs the recurrence above over its tokens in
+ * chunks of 64 that never cross a sequence boundary (the tail chunk is
+ * partial), writes o for every token and, if final_state is not NULL, the
+ * state after its last token.  A zero-length sequence copies its initial
+ * state to its final state.
+ *
+ *   q, k        [T_tot, H, dk]   dtype qkv_dt (KDA_BF16 or KDA_F32)
+ *   v           [T_tot, H, dv]   dtype qkv_dt
+ *   g           [T_tot, H, dk]   fp32 log-decay (<= 0)
+ *   beta        [T_tot, H]       fp32, post-sigmoid
+ *   cu_seqlens  [N+1] int32, device copy (read by the kernels)
+ *   cu_seqlens_host [N+1] int32, host copy or NULL.  When given it is
+ *               validated (cu[0]=0, non-decreasing, cu[N]=T_tot) and must
+ *               equal the device copy.  The kernels clamp every sequence
+ *               range into [0, T_tot], so no value can make them read or
+ *               write out of bounds.
+ *   initial_state [N, H, dk, dv] fp32 or NULL; final_state [N, H, dk, dv]
+ *               fp32 or NULL; they may be the same buffer (in-place update).
+ *   o           [T_tot, H, dv]   dtype o_dt (KDA_BF16 or KDA_F32)
+ * Requires dk == dv == 128 (else KDA_ERR_UNSUPPORTED), N >= 1, H >= 1,
+ * 16-byte aligned tensors.  Matrix products run as fp16 MFMA tiles with fp32
+ * accumulation (bf16 inputs convert to fp16 exactly); the state and the
+ * intermediate products are carried as hi+lo fp16 pairs, so results match a
+ * full-precision recurrence to about 1e-4 of the state norm.
+ */
+kda_status kda_chunk_prefill(const void* q, const void* k, const void* v, kda_dtype qkv_dt,
+                             const float* g, const float* beta, const int32_t* cu_seqlens,
+                             const int32_t* cu_seqlens_host, int32_t N,
+                             const float* initial_state, float* final_state, void* o,
+                             kda_dtype o_dt, int64_t T_tot, int32_t H, int32_t dk,
+                             int32_t dv, float scale, void* stream);
+
+/*
+ * kda_recurrent_decode - one token per sequence, state updated in place.
+ *
+ *   q, k  [N, H, dk], v [N, H, dv]   dtype qkv_dt (KDA_BF16 or KDA_F32)
+ *   g     [N, H, dk] fp32, beta [N, H] fp32 (post-sigmoid)
+ *   state [N, H, dk, dv] fp32, read and overwritten with S_t
+ *   o     [N, H, dv] dtype o_dt
+ * Requires dk == dv == 128.  state must not overlap q/k/v/g/beta/o.
+ * All arithmetic is fp32.
+ */
+kda_status kda_recurrent_decode(const void* q, const void* k, const void* v, kda_dtype qkv_dt,
+                                const float* g, const float* beta, float* state, void* o,
+                                kda_dtype o_dt, int32_t N, int32_t H, int32_t dk, int32_t dv,
+                                float scale, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

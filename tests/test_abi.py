@@ -1,0 +1,107 @@
+"""The C ABI library loads, exports every entry point of include/kda.h, and
+refuses bad arguments on the host before any HIP call (CPU only: the refusal
+paths never touch the GPU, so fake device addresses are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _lib():
+    import gated_delta_rule_58_amd as kda
+    if not os.path.exists(kda.lib_path()):
+        from gated_delta_rule_58_amd.build import build_library
+        build_library()
+    return kda.lib()
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "kda.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    L = _lib()
+    names = _declared()
+    assert set(names) == {"kda_last_error", "kda_version", "kda_gate", "kda_chunk_prefill",
+                          "kda_recurrent_decode"}
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.kda_version().decode().startswith("kda-gfx950")
+
+
+# Fake, 256-byte aligned device addresses: only reached by code paths that
+# refuse before launching.
+DEV = [0x100000 * (i + 1) for i in range(12)]
+
+
+def _gate(L, **kw):
+    a = dict(x=DEV[0], x_dt=1, b=DEV[1], b_dt=0, A_log=DEV[2], A_log_len=96, dt_bias=DEV[3],
+             dt_bias_len=96 * 128, g=DEV[4], beta=DEV[5], n_tok=10, H=96, d=128)
+    a.update(kw)
+    return L.kda_gate(a["x"], a["x_dt"], a["b"], a["b_dt"], a["A_log"], a["A_log_len"],
+                      a["dt_bias"], a["dt_bias_len"], a["g"], a["beta"], a["n_tok"], a["H"],
+                      a["d"], None)
+
+
+def test_gate_refuses_checkpoint_shaped_A_log():
+    """A_log of length 128 with H=96 (the checkpoint's shape) is refused, not reshaped."""
+    L = _lib()
+    assert _gate(L, A_log_len=128) == 2
+    assert b"A_log" in L.kda_last_error()
+    assert _gate(L, dt_bias_len=12288 + 1) == 2
+    assert _gate(L, x_dt=5) == 3
+    assert _gate(L, d=126, dt_bias_len=96 * 126) == 4
+    assert _gate(L, n_tok=-1) == 1
+    assert _gate(L, x=None) == 1
+    assert _gate(L, x=DEV[0] + 4, x_dt=0) == 5
+
+
+def _prefill(L, cu_host, **kw):
+    a = dict(q=DEV[0], k=DEV[1], v=DEV[2], qkv_dt=1, g=DEV[3], beta=DEV[4], cu=DEV[5], N=2,
+             S0=None, Sf=DEV[6], o=DEV[7], o_dt=1, T=48, H=4, dk=128, dv=128, scale=1.0)
+    a.update(kw)
+    hp = None if cu_host is None else np.ascontiguousarray(np.asarray(cu_host, dtype=np.int32))
+    return L.kda_chunk_prefill(a["q"], a["k"], a["v"], a["qkv_dt"], a["g"], a["beta"], a["cu"],
+                               None if hp is None else hp.ctypes.data, a["N"], a["S0"], a["Sf"],
+                               a["o"], a["o_dt"], a["T"], a["H"], a["dk"], a["dv"], a["scale"],
+                               None)
+
+
+def test_prefill_refusals():
+    L = _lib()
+    assert _prefill(L, [0, 20, 48], dk=64) == 4
+    assert _prefill(L, [0, 20, 48], dv=256) == 4
+    assert _prefill(L, [0, 30, 20], T=20) == 2          # decreasing
+    assert _prefill(L, [1, 20, 48]) == 2                 # does not start at 0
+    assert _prefill(L, [0, 20, 47]) == 2                 # does not end at T_tot
+    assert _prefill(L, [0, 20, 48], qkv_dt=9) == 3
+    assert _prefill(L, [0, 20, 48], N=0) == 1
+    assert _prefill(L, [0, 20, 48], cu=None) == 1
+    assert _prefill(L, [0, 20, 48], q=None) == 1
+    assert _prefill(L, [0, 20, 48], scale=float("nan")) == 1
+    assert _prefill(L, [0, 20, 48], o=DEV[7] + 2) == 5
+    assert b"kda_chunk_prefill" in L.kda_last_error()
+
+
+def test_decode_refusals():
+    L = _lib()
+
+    def dec(**kw):
+        a = dict(q=DEV[0], k=DEV[1], v=DEV[2], qkv_dt=1, g=DEV[3], beta=DEV[4], S=DEV[5],
+                 o=DEV[6], o_dt=1, N=4, H=2, dk=128, dv=128, scale=1.0)
+        a.update(kw)
+        return L.kda_recurrent_decode(a["q"], a["k"], a["v"], a["qkv_dt"], a["g"], a["beta"],
+                                      a["S"], a["o"], a["o_dt"], a["N"], a["H"], a["dk"], a["dv"],
+                                      a["scale"], None)
+    assert dec(dk=64) == 4
+    assert dec(o_dt=3) == 3
+    assert dec(S=None) == 1
+    assert dec(S=DEV[5] + 8) == 5
+    assert dec(o=DEV[5] + 4096) == 1   # o inside the state buffer: overlap refused
+    assert dec(N=0, S=None) == 0       # empty batch is a no-op

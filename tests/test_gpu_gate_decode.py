@@ -1,0 +1,118 @@
+"""GPU parity of kda_gate and kda_recurrent_decode against the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import CONFIGS, draw_decode_params, draw_decode_step, draw_prefill
+from tests.gpu_util import DEV, need_gpu, oracle_gate_f32, say
+from tests.parity import assert_out, assert_state, to64
+import gated_delta_rule_58_amd as kda
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("xdt", [torch.float32, torch.bfloat16])
+def test_gate_parity(xdt):
+    need_gpu()
+    say("gate parity", xdt)
+    dr = draw_prefill([777], H=96, dtype=torch.bfloat16, seed=21)
+    x = dr.x.to(xdt)
+    b = dr.b.to(xdt)
+    g, beta = kda.gate(x.to(DEV), b.to(DEV), dr.A_log.to(DEV), dr.dt_bias.to(DEV))
+    torch.cuda.synchronize()
+    g_ref, b_ref = oracle.gate(x, b, dr.A_log, dr.dt_bias)
+    g_gpu, b_gpu = to64(g), to64(beta)
+    assert np.all(np.abs(g_gpu - g_ref) <= 1e-5 * np.abs(g_ref) + 1e-30)
+    assert np.max(np.abs(b_gpu - b_ref)) <= 1e-6
+    assert np.all(g_gpu <= 0)
+
+
+def test_gate_extreme_logits():
+    """Large |x + dt_bias| and |b| stay finite and match the asymptotes."""
+    need_gpu()
+    say("gate extremes")
+    H, d = 4, 128
+    x = torch.linspace(-80, 80, 3 * H * d).reshape(3, H, d)
+    b = torch.tensor([[-200.0, -20.0, 20.0, 200.0]] * 3)
+    A_log = torch.tensor([-0.75, 0.0, 0.5, 2.4661])
+    dt = torch.zeros(H, d)
+    g, beta = kda.gate(x.to(DEV), b.to(DEV), A_log.to(DEV), dt.to(DEV))
+    torch.cuda.synchronize()
+    g_ref, b_ref = oracle.gate(x, b, A_log, dt)
+    g_gpu = to64(g)
+    assert np.all(np.isfinite(g_gpu)) and np.all(np.isfinite(to64(beta)))
+    assert np.all(np.abs(g_gpu - g_ref) <= 1e-5 * np.abs(g_ref) + 1e-37)
+    assert np.max(np.abs(to64(beta) - b_ref)) <= 1e-6
+
+
+@pytest.mark.parametrize("qdt,odt", [(torch.float32, torch.float32),
+                                     (torch.bfloat16, torch.float32),
+                                     (torch.bfloat16, torch.bfloat16)])
+def test_decode_parity_small(qdt, odt):
+    need_gpu()
+    say("decode small", qdt, odt)
+    N, H = 7, 5
+    A_log, dt_bias, S0 = draw_decode_params(N, H, seed=31)
+    S0 = S0 * 10  # a state of order one, so the update matters
+    S_gpu = S0.to(DEV).contiguous()
+    S_ref = to64(S0)
+    for step in range(6):
+        st = draw_decode_step(N, H, step, seed=31, dtype=qdt)
+        g, beta = oracle.gate(st.x, st.b, A_log, dt_bias)
+        g32, b32 = torch.from_numpy(g).float(), torch.from_numpy(beta).float()
+        o = kda.recurrent_decode(st.q.to(DEV), st.k.to(DEV), st.v.to(DEV), g32.to(DEV),
+                                 b32.to(DEV), S_gpu, scale=0.8, o_dtype=odt)
+        torch.cuda.synchronize()
+        o_ref, S_ref = oracle.decode(st.q, st.k, st.v, g32, b32, S_ref, scale=0.8)
+        if odt == torch.float32:
+            assert_out(o, o_ref, "decode step %d" % step)
+        else:
+            from tests.parity import assert_out_bf16
+            assert_out_bf16(o, o_ref, "decode step %d" % step)
+        assert_state(S_gpu, S_ref, "decode step %d" % step)
+
+
+def test_decode_full_config_sampled():
+    """256 sequences x 96 heads x 64 steps, fp32 state [256,96,128,128] updated
+    in place, HIP gate -> HIP decode; sampled (sequence, head) pairs checked
+    against oracle gate -> oracle decode on every step."""
+    need_gpu()
+    c = CONFIGS[4]
+    N, H, steps, seed = c["N"], c["H"], c["steps"], c["seed"]
+    say("decode full config N=%d H=%d steps=%d" % (N, H, steps))
+    A_log, dt_bias, S0 = draw_decode_params(N, H, seed=seed, device=DEV)
+    rng = np.random.default_rng(4)
+    pairs = [(int(a), int(b)) for a, b in zip(rng.integers(0, N, 24), rng.integers(0, H, 24))]
+    ni = torch.tensor([p[0] for p in pairs])
+    hi = torch.tensor([p[1] for p in pairs])
+    S_ref = to64(S0[ni, hi])                             # [24, 128, 128]
+    state = S0
+    for step in range(steps):
+        st = draw_decode_step(N, H, step, seed=seed, dtype=c["dtype"], device=DEV)
+        g, beta = kda.gate(st.x, st.b, A_log, dt_bias)
+        o = kda.recurrent_decode(st.q, st.k, st.v, g, beta, state, o_dtype=torch.float32)
+        # oracle gate per sampled pair (each pair has its own head parameters)
+        x_s = st.x[ni, hi].cpu()[None]                  # [1, 24, 128] as tokens x "heads"
+        b_s = st.b[ni, hi].cpu()[None]
+        gr, br = oracle.gate(x_s, b_s, A_log[hi].cpu(), dt_bias[hi].cpu())
+        o_ref, S_ref = oracle.decode(st.q[ni, hi].cpu()[None], st.k[ni, hi].cpu()[None],
+                                     st.v[ni, hi].cpu()[None], gr, br, S_ref[None])
+        S_ref = S_ref[0]
+        assert_out(o[ni, hi], o_ref[0], "decode step %d" % step)
+    torch.cuda.synchronize()
+    assert_state(state[ni, hi], S_ref, "decode after %d steps" % steps)
+
+
+def test_decode_deterministic():
+    need_gpu()
+    say("decode determinism")
+    N, H = 32, 96
+    A_log, dt_bias, S0 = draw_decode_params(N, H, seed=5, device=DEV)
+    st = draw_decode_step(N, H, 0, seed=5, device=DEV)
+    g, beta = kda.gate(st.x, st.b, A_log, dt_bias)
+    S1, S2 = S0.clone(), S0.clone()
+    o1 = kda.recurrent_decode(st.q, st.k, st.v, g, beta, S1)
+    o2 = kda.recurrent_decode(st.q, st.k, st.v, g, beta, S2)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)

@@ -1,0 +1,178 @@
+"""GPU parity of kda_chunk_prefill against the fp64 oracle.
+
+Small cases feed both sides the same fp32 g/beta (from the oracle gate).  The
+full-size workloads run the HIP gate then the HIP prefill in the launch
+configuration the bench times, and compare sampled heads (heads are
+independent) against the oracle gate then the oracle recurrence.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import CONFIGS, draw_config, draw_prefill
+from tests.gpu_util import DEV, need_gpu, oracle_gate_f32, oracle_gate_f64, sample_heads, say
+from tests.parity import (assert_out, assert_out_bf16, assert_state, out_err, state_err, to64)
+import gated_delta_rule_58_amd as kda
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_gpu(dr, g, beta, o_dtype, scale=1.0, S0=None):
+    cu = dr.cu_seqlens
+    o, Sf = kda.chunk_prefill(dr.q.to(DEV), dr.k.to(DEV), dr.v.to(DEV), g.to(DEV),
+                              beta.to(DEV), cu_seqlens=cu.to(DEV), cu_seqlens_host=cu,
+                              initial_state=None if S0 is None else S0.to(DEV),
+                              scale=scale, o_dtype=o_dtype)
+    torch.cuda.synchronize()
+    return o, Sf
+
+
+def _check_small(lengths, H, qdt, init, seed, scale=1.0):
+    dr = draw_prefill(lengths, H=H, dtype=qdt, init_state=init, seed=seed)
+    g, beta = oracle_gate_f32(dr)
+    say("prefill case lengths=%s H=%d dtype=%s init=%s" % (lengths, H, qdt, init))
+    o_ref, S_ref = oracle.prefill(dr.q, dr.k, dr.v, g, beta, dr.cu_seqlens, dr.initial_state,
+                                  scale=scale)
+    o32, S32 = _run_gpu(dr, g, beta, torch.float32, scale, dr.initial_state)
+    eo = assert_out(o32, o_ref, str(lengths))
+    es = assert_state(S32, S_ref, str(lengths))
+    ob, Sb = _run_gpu(dr, g, beta, torch.bfloat16, scale, dr.initial_state)
+    assert_out_bf16(ob, o_ref, str(lengths))
+    assert torch.equal(Sb, S32)
+    return eo, es
+
+
+def test_config0_parity():
+    """T=256, H=2, fp32 q/k/v, chunk 64, zero initial state."""
+    need_gpu()
+    dr = draw_config(0)
+    g, beta = oracle_gate_f32(dr)
+    say("config 0")
+    o_ref, S_ref = oracle.prefill(dr.q, dr.k, dr.v, g, beta, dr.cu_seqlens)
+    o, S = _run_gpu(dr, g, beta, torch.float32)
+    assert o.shape == (256, 2, 128) and S.shape == (1, 2, 128, 128)
+    assert_out(o, o_ref, "config 0")
+    assert_state(S, S_ref, "config 0")
+
+
+# Shapes of the audit page's exact-match table (§7.3): one chunk [16],
+# partial tail [17], two chunks [32], multi-chunk/multi-head [65] H=2, the K3
+# head count [17] H=96, varlen partial chunks [17,31] H=2; plus the chunk-64
+# boundaries and a zero-length sequence.
+EDGE = [([16], 1), ([17], 1), ([32], 1), ([65], 2), ([17], 96), ([17, 31], 2),
+        ([1], 3), ([63], 2), ([64], 2), ([128], 2), ([129], 2), ([200, 0, 64, 1, 77], 3)]
+
+
+@pytest.mark.parametrize("lengths,H", EDGE)
+def test_edge_shapes(lengths, H):
+    need_gpu()
+    _check_small(lengths, H, torch.bfloat16, True, seed=100 + sum(lengths) + H, scale=0.7)
+
+
+def test_edge_no_initial_state_fp32_inputs():
+    need_gpu()
+    _check_small([65, 130], 4, torch.float32, False, seed=7)
+
+
+def test_delta_rule_recall_on_gpu():
+    """alpha=1, beta=1, q_t=k_t with unit keys: o_t = v_t exactly (any state)."""
+    need_gpu()
+    from synth import orthonormal_keys_pm_quarter
+    T, H = 100, 2
+    K = orthonormal_keys_pm_quarter(T if T <= 128 else 128)
+    k = K[None].repeat(H, 1, 1).permute(1, 0, 2).contiguous().to(torch.bfloat16)
+    v = torch.randn(T, H, 128, generator=torch.Generator().manual_seed(3)).to(torch.bfloat16)
+    g = torch.zeros(T, H, 128)
+    beta = torch.ones(T, H)
+    S0 = torch.randn(1, H, 128, 128, generator=torch.Generator().manual_seed(4))
+    say("recall on gpu")
+    o, S = kda.chunk_prefill(k.to(DEV), k.to(DEV), v.to(DEV), g.to(DEV), beta.to(DEV),
+                             initial_state=S0.to(DEV), o_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.max(torch.abs(o.cpu() - v.float())) < 2e-3
+
+
+def test_chunked_equals_decode_loop_and_resume():
+    """Prefill over T equals the GPU decode kernel looped token by token, a
+    split prefill resumed from the first part's final state, and the oracle."""
+    need_gpu()
+    T, T1, H = 150, 70, 4
+    dr = draw_prefill([T], H=H, dtype=torch.bfloat16, init_state=True, seed=9)
+    g, beta = oracle_gate_f32(dr)
+    say("prefill vs decode loop vs split")
+    o, S = _run_gpu(dr, g, beta, torch.float32, S0=dr.initial_state)
+    state = dr.initial_state.to(DEV).clone()
+    od = []
+    for t in range(T):
+        od.append(kda.recurrent_decode(dr.q[t:t + 1].to(DEV), dr.k[t:t + 1].to(DEV),
+                                       dr.v[t:t + 1].to(DEV), g[t:t + 1].to(DEV),
+                                       beta[t:t + 1].to(DEV), state, o_dtype=torch.float32))
+    od = torch.cat(od)
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle.prefill(dr.q, dr.k, dr.v, g, beta, dr.cu_seqlens, dr.initial_state)
+    assert_out(o, o_ref, "prefill")
+    assert_out(od, o_ref, "decode loop")
+    assert_state(S, S_ref, "prefill")
+    assert_state(state, S_ref, "decode loop")
+    assert out_err(o, od) <= 5e-3 and state_err(S, state) <= 1e-3
+    # split prefill: [0, T1) then [T1, T) from the first part's final state
+    d1 = draw_prefill([T1], H=H, dtype=torch.bfloat16, seed=0)
+    d1.q, d1.k, d1.v = dr.q[:T1], dr.k[:T1], dr.v[:T1]
+    o1, S1 = _run_gpu(d1, g[:T1], beta[:T1], torch.float32, S0=dr.initial_state)
+    d2 = draw_prefill([T - T1], H=H, dtype=torch.bfloat16, seed=0)
+    d2.q, d2.k, d2.v = dr.q[T1:], dr.k[T1:], dr.v[T1:]
+    o2, S2 = _run_gpu(d2, g[T1:], beta[T1:], torch.float32, S0=S1.cpu())
+    assert_out(torch.cat([o1, o2]), o_ref, "split")
+    assert_state(S2, S_ref, "split")
+
+
+def test_in_place_state_and_determinism():
+    need_gpu()
+    dr = draw_prefill([300, 45], H=8, dtype=torch.bfloat16, init_state=True, seed=12)
+    g, beta = oracle_gate_f32(dr)
+    say("in-place state + determinism")
+    q, k, v = dr.q.to(DEV), dr.k.to(DEV), dr.v.to(DEV)
+    gg, bb, cu = g.to(DEV), beta.to(DEV), dr.cu_seqlens.to(DEV)
+    o1, S1 = kda.chunk_prefill(q, k, v, gg, bb, cu, dr.initial_state.to(DEV))
+    o2, S2 = kda.chunk_prefill(q, k, v, gg, bb, cu, dr.initial_state.to(DEV))
+    st = dr.initial_state.to(DEV).clone()
+    o3, _ = kda.chunk_prefill(q, k, v, gg, bb, cu, st, final_state=st)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+    assert torch.equal(o1, o3) and torch.equal(S1, st)
+
+
+def _full_config(idx, n_heads, seed):
+    c = CONFIGS[idx]
+    say("full config %d (%s), sampled heads" % (idx, c["name"]))
+    dr = draw_config(idx, device=DEV)
+    cu_h = dr.cu_seqlens
+    g, beta = kda.gate(dr.x, dr.b, dr.A_log, dr.dt_bias)
+    o, S = kda.chunk_prefill(dr.q, dr.k, dr.v, g, beta, cu_h.to(DEV), dr.initial_state,
+                             cu_seqlens_host=cu_h, o_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    heads = sample_heads(c["H"], n_heads, seed)
+    say("  oracle on heads", heads)
+    gr, br = oracle_gate_f64(dr, heads)
+    S0 = None if dr.initial_state is None else dr.initial_state[:, heads].cpu()
+    o_ref, S_ref = oracle.prefill(dr.q[:, heads].cpu(), dr.k[:, heads].cpu(),
+                                  dr.v[:, heads].cpu(), gr, br, cu_h, S0)
+    eo = assert_out_bf16(o[:, heads], o_ref, "config %d" % idx)
+    es = assert_state(S[:, heads], S_ref, "config %d" % idx)
+    say("  bf16-o err ratio %.3f  state err %.3e" % (eo, es))
+
+
+def test_config1_full_sampled_heads():
+    need_gpu()
+    _full_config(1, 8, 1)
+
+
+def test_config2_full_sampled_heads():
+    need_gpu()
+    _full_config(2, 4, 2)
+
+
+def test_config3_full_sampled_heads():
+    need_gpu()
+    _full_config(3, 3, 3)
