@@ -55,7 +55,29 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=96,
                     help="heads of the workload the CPU oracle runs (sample)")
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "copy"], default="all",
+                    help="profiling aid: run one part only (prints a diagnostic line, "
+                         "not the bench line)")
     return ap.parse_args()
+
+
+def bench_copy(args, torch):
+    """A plain device copy of known size (1 GiB read + 1 GiB written per launch),
+    used to calibrate the FETCH_SIZE / WRITE_SIZE counters."""
+    n = 1 << 28
+    a = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    for _ in range(max(1, args.warmup)):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    return dict(bytes_read=4 * n, bytes_written=4 * n, ms=ms, GBps=8 * n / (ms * 1e-3) / 1e9)
 
 
 def bench_prefill(args, torch, kda, synth):
@@ -169,6 +191,12 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     kda.lib()
+    if args.only != "all":
+        fn = {"prefill": lambda: bench_prefill(args, torch, kda, synth),
+              "decode": lambda: bench_decode(args, torch, kda, synth),
+              "copy": lambda: bench_copy(args, torch)}[args.only]
+        print(json.dumps({"diagnostic": args.only, **fn()}), flush=True)
+        return
     pre = bench_prefill(args, torch, kda, synth)
     print("prefill: step %.4f ms (gate %.4f, chunk %.4f), p95 %.4f ms" %
           (pre["step_ms"], pre["gate_ms"], pre["chunk_ms"], pre["p95_step_ms"]),
