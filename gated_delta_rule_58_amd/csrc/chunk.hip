@@ -46,8 +46,6 @@
 // Precision.  MFMA operands are fp16 (bf16 inputs convert exactly); the state
 // S, X, Delta and P are split into hi+lo fp16 pairs, so their rounding does
 // not reach the result; accumulation is fp32.
-#include <type_traits>
-
 #include "kda_device.hpp"
 #include "kda_internal.hpp"
 
@@ -87,6 +85,10 @@ __device__ __forceinline__ void wave_lds_sync() {
 // 16(e>>2) + 4lg + (e&3).
 __device__ __forceinline__ int pperm(int L) { return ((L >> 2) & 3) * 8 + (L >> 4) * 4 + (L & 3); }
 __device__ __forceinline__ int ppos64(int s) { return (s & 32) + pperm(s & 31); }
+// float index of element (row, c) of the swizzled gamma buffer
+__device__ __forceinline__ int gidx(int row, int c) {
+  return row * 128 + ((((c >> 2) ^ (row & 15))) << 2) + (c & 3);
+}
 
 __device__ __forceinline__ void split_f16(float x, _Float16& hi, _Float16& lo) {
   hi = static_cast<_Float16>(x);
@@ -121,16 +123,17 @@ __device__ __forceinline__ void bfrag16_split(const f32x4& t, f16x4& hi, f16x4& 
 
 // LDS layout (bytes).
 struct Lds {
-  static constexpr int GAM_LD = 132;   // fp32 [64][132]   half-local gamma (log2 units)
-  static constexpr int OP_LD = 136;    // fp16 [64][136]   Kt, Qt (channel-permuted); R [48][136]
+  static constexpr int GAM_LD = 128;   // fp32 [64][128]   g of the next chunk, then gamma (log2 units);
+                                       // 16-byte chunk j of row r stored at chunk j ^ (r & 15)
+  static constexpr int OP_LD = 136;    // fp16 [64][136]   Kt, Qt (channel-permuted); R [48][136]; L3 [32][136]
   static constexpr int TT_LD = 72;     // fp16 [..][72]    Khat^T, P hi/lo (token-permuted)
   static constexpr int AT_LD = 72;     // fp16 [64][72]    -A_ij below the diagonal blocks, T_ii on them
-  static constexpr int SC_LD = 17;     // fp32 [4][16][17] per-wave A_ii scratch
+  static constexpr int SC_LD = 20;     // fp32 [4][16][20] per-wave transpose scratch
 
-  static constexpr int off_gam = 0;                       // P0..P1a
-  static constexpr int off_R = 0;                         // P1b..P2 (aliases gam)
-  static constexpr int end_gamR = C * GAM_LD * 4;
-  static constexpr int off_Kt = end_gamR;
+  static constexpr int off_gam = 0;
+  static constexpr int off_R = off_gam + C * GAM_LD * 4;
+  static constexpr int off_L3 = off_R + 48 * OP_LD * 2;
+  static constexpr int off_Kt = off_L3 + 32 * OP_LD * 2;
   static constexpr int off_Qt = off_Kt + C * OP_LD * 2;
   static constexpr int off_KhT = off_Qt + C * OP_LD * 2;
   static constexpr int off_Ph = off_KhT + D * TT_LD * 2;
@@ -139,12 +142,10 @@ struct Lds {
   static constexpr int off_scr = off_AT + C * AT_LD * 2;
   static constexpr int off_cst = off_scr + 4 * 16 * SC_LD * 4;
   static constexpr int off_beta = off_cst + 18 * D * 4;
-  static constexpr int off_tot = off_beta + C * 4;
-  static constexpr int off_seq = off_tot + D * 4;
+  static constexpr int off_seq = off_beta + C * 4;
   static constexpr int total = off_seq + 16;
 };
 static_assert(Lds::total <= 160 * 1024, "LDS budget");
-static_assert(3 * 16 * Lds::OP_LD * 2 <= Lds::end_gamR, "R fits in the gamma region");
 
 // Per-channel constant slots (after exp2, all <= 1):
 //  0..3   em_i = 2^gamma_{m_i}
@@ -155,6 +156,25 @@ static_assert(3 * 16 * Lds::OP_LD * 2 <= Lds::end_gamR, "R fits in the gamma reg
 //  17     eC = 2^gamma_C
 __device__ __forceinline__ int cij_slot(int i, int j) {
   return (j == i - 1) ? 7 + i : (i == 2 ? 11 : (j == 1 ? 12 : 13));
+}
+
+// Raw buffer resource over [base, base + nbytes): loads past the end return 0
+// and stores past the end are dropped, which is how partial chunks are masked.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_buf(const void* base, uint32_t nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes,
+                                           0x00020000);
+}
+__device__ __forceinline__ float buf_f32(__amdgpu_buffer_rsrc_t r, int off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+// 16 bytes per lane from a buffer straight into LDS (lane l writes dst + 16 l).
+// Kept out of templates: the size check of this builtin misfires in the host
+// pass of a template instantiation and silently drops the kernel's host stub.
+__device__ __forceinline__ void buf_to_lds16_inl(__amdgpu_buffer_rsrc_t r, lds_ptr_t dst,
+                                                 int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, soff, 0, 0);
 }
 
 template <bool BF16>
@@ -169,16 +189,21 @@ struct QKRaw<false> {
 };
 
 template <bool BF16>
-__device__ __forceinline__ void load_qk(QKRaw<BF16>& R, const void* base, int64_t tok, int lg) {
+__device__ __forceinline__ void load_qk(QKRaw<BF16>& R, __amdgpu_buffer_rsrc_t rs, int off0) {
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
-      const int c = 32 * kk + 16 * a + 4 * lg;
-      if constexpr (BF16)
-        R.v[kk][a] = *reinterpret_cast<const u16x4*>(static_cast<const uint16_t*>(base) + tok + c);
-      else
-        R.v[kk][a] = *reinterpret_cast<const f32x4*>(static_cast<const float*>(base) + tok + c);
+      const int c = 32 * kk + 16 * a;   // plus 4lg, folded into off0
+      if constexpr (BF16) {
+        typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+        const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(rs, off0 + 2 * c, 0, 0);
+        R.v[kk][a] = __builtin_bit_cast(u16x4, x);
+      } else {
+        typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+        const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rs, off0 + 4 * c, 0, 0);
+        R.v[kk][a] = __builtin_bit_cast(f32x4, x);
+      }
     }
 }
 
@@ -197,6 +222,7 @@ __global__ void __launch_bounds__(NTHR, 1) chunk_kernel(
   __shared__ __attribute__((aligned(16))) char lds[Lds::total];
   float* gam = reinterpret_cast<float*>(lds + Lds::off_gam);
   _Float16* Rb = reinterpret_cast<_Float16*>(lds + Lds::off_R);
+  _Float16* L3 = reinterpret_cast<_Float16*>(lds + Lds::off_L3);
   _Float16* Kt = reinterpret_cast<_Float16*>(lds + Lds::off_Kt);
   _Float16* Qt = reinterpret_cast<_Float16*>(lds + Lds::off_Qt);
   _Float16* KhT = reinterpret_cast<_Float16*>(lds + Lds::off_KhT);
@@ -205,11 +231,10 @@ __global__ void __launch_bounds__(NTHR, 1) chunk_kernel(
   _Float16* AT = reinterpret_cast<_Float16*>(lds + Lds::off_AT);
   float* cst = reinterpret_cast<float*>(lds + Lds::off_cst);
   float* s_beta = reinterpret_cast<float*>(lds + Lds::off_beta);
-  float* s_tot = reinterpret_cast<float*>(lds + Lds::off_tot);
   int* s_seq = reinterpret_cast<int*>(lds + Lds::off_seq);
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6;          // wave
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave (uniform)
   const int lane = tid & 63;
   const int lr = lane & 15;        // MFMA row/column within a 16x16 tile
   const int lg = lane >> 4;        // MFMA k-group
@@ -243,10 +268,11 @@ __global__ void __launch_bounds__(NTHR, 1) chunk_kernel(
   int bos = cu[n], eos = cu[n + 1];
   bos = bos < 0 ? 0 : (bos > T_tot ? T_tot : bos);
   eos = eos < bos ? bos : (eos > T_tot ? T_tot : eos);
-  const int64_t HD = (int64_t)H * D;
-  const int64_t hD = (int64_t)h * D;
+  const int HD = H * D;                  // elements per token row (fits int32: H <= 2^24/128)
   const int col0 = tile * DV;
   const int jcol = col0 + 16 * w + lr;   // value column owned by this lane (state products)
+  constexpr int QS = QKV_BF16 ? 2 : 4;   // q/k/v element size
+  constexpr int OS = O_BF16 ? 2 : 4;     // o element size
 
   // ---- state slice: wave w, tile t: key rows 16t + 4lg + i, value column jcol.
   f32x4 Sacc[8];
@@ -261,148 +287,219 @@ __global__ void __launch_bounds__(NTHR, 1) chunk_kernel(
     for (int t = 0; t < 8; ++t) Sacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // ---- prefetch registers for the next chunk.  Loads are unconditional,
-  // from rows clamped into the chunk (a partial chunk re-reads its last row);
-  // rows past the end are zeroed where the values are used, so no load sits
-  // behind a branch and none forces an early wait.
-  using VRaw = typename std::conditional<QKV_BF16, uint32_t, float>::type;
-  const int gc = tid & 127, ghf = tid >> 7;  // gamma pass: channel, half
-  const int rA = 16 * w + lr;                // chunk row of this lane in the operand phases
-  float gpf[32];
+  // ---- per-lane byte offsets inside one chunk (rows of the packed token axis)
+  const int gc = tid >> 1, ghf = tid & 1;    // gamma pass: channel, half (lane pairs)
+  const int rA = 16 * w + lr;                // chunk row of this lane in the operand phase
+  const int off_g = (32 * ghf * HD + gc) * 4;
+  const int off_qk = rA * HD * QS + 4 * lg * QS;
+  const int off_v = (4 * lg * HD + jcol) * QS;  // + 16 rt HD + i HD
+  const int off_o = (4 * lg * HD + jcol) * OS;
+
+  // chunk buffers: [t0, min(eos, t0 + C)) tokens of head h
+  auto rows_of = [&](int t0c) { return (eos - t0c) < C ? (eos - t0c) : C; };
+  auto buf_tok = [&](const void* base, int esz, int t0c) {
+    const char* b = static_cast<const char*>(base) + ((int64_t)t0c * HD + (int64_t)h * D) * esz;
+    return make_buf(b, (uint32_t)(rows_of(t0c) * HD * esz - h * D * esz));
+  };
+
+  // ---- next-chunk prefetch (loads past the chunk end return 0).  g goes
+  // straight to LDS (the gamma region, where P0 turns it into gamma in place);
+  // k, q, beta and v go to registers.
   QKRaw<QKV_BF16> kpf, qpf;
-  VRaw vraw[16];
+  uint32_t vraw[16];
   float bpf = 0.0f;
-  auto prefetch_gkq = [&](int t0n) {
-    const int rmax = ((eos - t0n) < C ? (eos - t0n) : C) - 1;
+  auto stage_g = [&](int t0n) {
+    const auto rg = buf_tok(g, 4, t0n);
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      const int rr = (32 * ghf + i) < rmax ? (32 * ghf + i) : rmax;
-      gpf[i] = g[(int64_t)(t0n + rr) * HD + hD + gc];
+    for (int j = 0; j < 8; ++j) {  // rows 16w + 2j + (lane >> 5): lane writes physical chunk lane & 31
+      const int row0 = 16 * w + 2 * j;
+      const int hi = lane >> 5;
+      const int lchunk = (lane & 31) ^ ((2 * j + hi) & 15);
+      buf_to_lds16_inl(rg, (lds_ptr_t)(gam + row0 * Lds::GAM_LD), hi * HD * 4 + lchunk * 16,
+                       row0 * HD * 4);
     }
-    const int rr = rA < rmax ? rA : rmax;
-    const int64_t tok = (int64_t)(t0n + rr) * HD + hD;
-    load_qk<QKV_BF16>(kpf, k, tok, lg);
-    load_qk<QKV_BF16>(qpf, q, tok, lg);
-    if (tid < C) bpf = beta[(int64_t)(t0n + (tid < rmax ? tid : rmax)) * H + h];
+  };
+  auto prefetch_kq = [&](int t0n) {
+    load_qk<QKV_BF16>(kpf, buf_tok(k, QS, t0n), off_qk);
+    load_qk<QKV_BF16>(qpf, buf_tok(q, QS, t0n), off_qk);
+    const char* bb = reinterpret_cast<const char*>(beta) + ((int64_t)t0n * H + h) * 4;
+    const auto rb = make_buf(bb, (uint32_t)(rows_of(t0n) * H * 4 - h * 4));
+    bpf = buf_f32(rb, lane * H * 4);
   };
   auto prefetch_v = [&](int t0n) {
-    const int rmax = ((eos - t0n) < C ? (eos - t0n) : C) - 1;
+    const auto rv = buf_tok(v, QS, t0n);
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        int rr = 16 * rt + 4 * lg + i;
-        rr = rr < rmax ? rr : rmax;
-        const int64_t vi = (int64_t)(t0n + rr) * HD + hD + jcol;
-        if constexpr (QKV_BF16) vraw[4 * rt + i] = static_cast<const uint16_t*>(v)[vi];
-        else vraw[4 * rt + i] = static_cast<const float*>(v)[vi];
+        const int soff = (16 * rt + i) * HD * QS;
+        if constexpr (QKV_BF16) vraw[4 * rt + i] = __builtin_amdgcn_raw_buffer_load_b16(rv, off_v, soff, 0);
+        else vraw[4 * rt + i] = __builtin_amdgcn_raw_buffer_load_b32(rv, off_v, soff, 0);
       }
   };
   auto vval = [&](int idx) -> float {
     if constexpr (QKV_BF16) return __uint_as_float(vraw[idx] << 16);
-    else return vraw[idx];
+    else return __uint_as_float(vraw[idx]);
   };
+  // all of this wave's loads (to LDS or registers) have landed
+  auto wait_loads = [&]() { __builtin_amdgcn_s_waitcnt(0x0f70); };
   if (bos < eos) {
-    prefetch_gkq(bos);
+    stage_g(bos);
+    prefetch_kq(bos);
     prefetch_v(bos);
+    wait_loads();
   }
+  __syncthreads();
 
   for (int t0 = bos; t0 < eos; t0 += C) {
-    const int Lc = (eos - t0) < C ? (eos - t0) : C;
+    const int Lc = rows_of(t0);
 
-    // ================= P0: gamma, cumsum of g within each 32-row half (log2 units)
-    // Blocks never straddle a half, so E/F (differences inside a block) need no
-    // offset; the constants add the first half's total to rows >= 32.
+    // ================= P0: gamma (cumsum of g, log2 units) and decay constants.
+    // Lanes 2c and 2c+1 own channel c, rows 0..31 and 32..63; they exchange
+    // their totals and the key-row values with a cross-lane shuffle.
     {
       float gv[32];
 #pragma unroll
-      for (int i = 0; i < 32; ++i) gv[i] = (32 * ghf + i < Lc) ? gpf[i] * LOG2E : 0.0f;
+      for (int i = 0; i < 32; ++i) gv[i] = gam[gidx(32 * ghf + i, gc)] * LOG2E;
 #pragma unroll
       for (int i = 1; i < 32; ++i) gv[i] += gv[i - 1];
+      const float tot0 = __shfl_xor(gv[31], 1);
+      if (ghf) {
 #pragma unroll
-      for (int i = 0; i < 32; ++i) gam[(32 * ghf + i) * Lds::GAM_LD + gc] = gv[i];
-      if (ghf == 0) s_tot[gc] = gv[31];
-      if (tid < C) s_beta[tid] = (tid < Lc) ? bpf : 0.0f;
+        for (int i = 0; i < 32; ++i) gv[i] += tot0;
+      }
+#pragma unroll
+      for (int i = 0; i < 32; ++i) gam[gidx(32 * ghf + i, gc)] = gv[i];
+      // key rows: block mids 7,23,39,55 and block ends 15,31,47,63
+      const float o7 = __shfl_xor(gv[7], 1), o15 = __shfl_xor(gv[15], 1);
+      const float o23 = __shfl_xor(gv[23], 1), o31 = __shfl_xor(gv[31], 1);
+      const float gm0 = ghf ? o7 : gv[7], gm1 = ghf ? o23 : gv[23];
+      const float gm2 = ghf ? gv[7] : o7, gm3 = ghf ? gv[23] : o23;
+      const float gb1 = ghf ? o15 : gv[15], gb2 = ghf ? o31 : gv[31];
+      const float gb3 = ghf ? gv[15] : o15, gl = ghf ? gv[31] : o31;
+      const int c = gc;
+      if (ghf == 0) {
+        cst[0 * D + c] = ex2(gm0);
+        cst[1 * D + c] = ex2(gm1);
+        cst[2 * D + c] = ex2(gm2);
+        cst[3 * D + c] = ex2(gm3);
+        cst[4 * D + c] = ex2(gl - gm0);
+        cst[5 * D + c] = ex2(gl - gm1);
+        cst[6 * D + c] = ex2(gl - gm2);
+        cst[7 * D + c] = ex2(gl - gm3);
+        cst[8 * D + c] = ex2(gm1 - gb1);
+      } else {
+        cst[9 * D + c] = ex2(gm2 - gb2);
+        cst[10 * D + c] = ex2(gm3 - gb3);
+        cst[11 * D + c] = ex2(gm2 - gb1);
+        cst[12 * D + c] = ex2(gm3 - gb2);
+        cst[13 * D + c] = ex2(gm3 - gb1);
+        cst[14 * D + c] = ex2(gb1 - gm0);
+        cst[15 * D + c] = ex2(gb2 - gm1);
+        cst[16 * D + c] = ex2(gb3 - gm2);
+        cst[17 * D + c] = ex2(gl);
+      }
+      if (tid < C) s_beta[tid] = bpf;
     }
     __syncthreads();
 
-    // ================= P1a: constants, decay factors, diagonal tiles and T_ii
+    // ================= P1: decay factors, operands, diagonal tiles and T_ii.
     // Lane (lr, lg) of wave i handles chunk row r = 16i + lr and, in k-step kk,
     // the 8 channels 32kk + 16a + 4lg + j (a < 2, j < 4), fragment element 4a + j.
     const int bi = w;
     const int r = rA;
-    const bool rvalid = r < Lc;
-    float kE[4][8], qE[4][8], kF[4][8];
+    float kE[4][8], qE[4][8];
     {
-      // per-channel constants: half 0 does slots 0..8, half 1 slots 9..17
-      {
-        const int c = gc;
-        const float off = s_tot[c];
-        const float gm0 = gam[7 * Lds::GAM_LD + c], gm1 = gam[23 * Lds::GAM_LD + c];
-        const float gm2 = gam[39 * Lds::GAM_LD + c] + off, gm3 = gam[55 * Lds::GAM_LD + c] + off;
-        const float gb1 = gam[15 * Lds::GAM_LD + c], gb2 = off;
-        const float gb3 = gam[47 * Lds::GAM_LD + c] + off, gl = gam[63 * Lds::GAM_LD + c] + off;
-        if (ghf == 0) {
-          cst[0 * D + c] = ex2(gm0);
-          cst[1 * D + c] = ex2(gm1);
-          cst[2 * D + c] = ex2(gm2);
-          cst[3 * D + c] = ex2(gm3);
-          cst[4 * D + c] = ex2(gl - gm0);
-          cst[5 * D + c] = ex2(gl - gm1);
-          cst[6 * D + c] = ex2(gl - gm2);
-          cst[7 * D + c] = ex2(gl - gm3);
-          cst[8 * D + c] = ex2(gm1 - gb1);
-        } else {
-          cst[9 * D + c] = ex2(gm2 - gb2);
-          cst[10 * D + c] = ex2(gm3 - gb3);
-          cst[11 * D + c] = ex2(gm2 - gb1);
-          cst[12 * D + c] = ex2(gm3 - gb2);
-          cst[13 * D + c] = ex2(gm3 - gb1);
-          cst[14 * D + c] = ex2(gb1 - gm0);
-          cst[15 * D + c] = ex2(gb2 - gm1);
-          cst[16 * D + c] = ex2(gb3 - gm2);
-          cst[17 * D + c] = ex2(gl);
-        }
-      }
-      f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
       const int mrow = 16 * bi + 7;
+      const int kpos = ppos64(r);  // token-permuted column of this row in Khat^T
+      float kF[4][8];
+      float dgmax = 0.0f;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        bf16x8 ekh, ekl, eqh, eql, fkh, fkl;
+        f16x8 kt, qt, rr8, l3k, l3q;
 #pragma unroll
         for (int a = 0; a < 2; ++a) {
           const int c = 32 * kk + 16 * a + 4 * lg;
-          const f32x4 gr = *reinterpret_cast<const f32x4*>(gam + r * Lds::GAM_LD + c);
-          const f32x4 gm = *reinterpret_cast<const f32x4*>(gam + mrow * Lds::GAM_LD + c);
+          const f32x4 gr = *reinterpret_cast<const f32x4*>(gam + gidx(r, c));
+          const f32x4 gm = *reinterpret_cast<const f32x4*>(gam + gidx(mrow, c));
+          const f32x4 em = *reinterpret_cast<const f32x4*>(cst + bi * D + c);
+          const f32x4 eL = *reinterpret_cast<const f32x4*>(cst + (4 + bi) * D + c);
+          const f32x4 eR = *reinterpret_cast<const f32x4*>(cst + (14 + (bi < 3 ? bi : 0)) * D + c);
+          const f32x4 c30 = *reinterpret_cast<const f32x4*>(cst + 13 * D + c);
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int e = 4 * a + j;
-            const float kv = rvalid ? qk_at<QKV_BF16>(kpf, kk, a, j) : 0.0f;
-            const float qv = rvalid ? qk_at<QKV_BF16>(qpf, kk, a, j) : 0.0f;
+            const float kv = qk_at<QKV_BF16>(kpf, kk, a, j);
+            const float qv = qk_at<QKV_BF16>(qpf, kk, a, j);
             const float dg = gr[j] - gm[j];
+            dgmax = fmaxf(dgmax, fabsf(dg));
             const float E = ex2(dg), F = ex2(-dg);
-            kE[kk][e] = kv * E;
-            qE[kk][e] = qv * E;
-            kF[kk][e] = kv * F;
+            const float ke = kv * E, qe = qv * E, kf = kv * F;
+            kE[kk][e] = ke;
+            qE[kk][e] = qe;
+            kF[kk][e] = kf;
+            kt[e] = static_cast<_Float16>(ke * em[j]);
+            qt[e] = static_cast<_Float16>(qe * em[j]);
+            KhT[(c + j) * Lds::TT_LD + kpos] = static_cast<_Float16>(kf * eL[j]);
+            if (bi < 3) rr8[e] = static_cast<_Float16>(kf * eR[j]);
+            if (bi == 3) {
+              l3k[e] = static_cast<_Float16>(ke * c30[j]);
+              l3q[e] = static_cast<_Float16>(qe * c30[j]);
+            }
+          }
+        }
+        *reinterpret_cast<f16x8*>(Kt + r * Lds::OP_LD + 32 * kk + 8 * lg) = kt;
+        *reinterpret_cast<f16x8*>(Qt + r * Lds::OP_LD + 32 * kk + 8 * lg) = qt;
+        if (bi < 3) *reinterpret_cast<f16x8*>(Rb + r * Lds::OP_LD + 32 * kk + 8 * lg) = rr8;
+        if (bi == 3) {  // left factors of tile (3,0), which wave 0 multiplies
+          *reinterpret_cast<f16x8*>(L3 + lr * Lds::OP_LD + 32 * kk + 8 * lg) = l3k;
+          *reinterpret_cast<f16x8*>(L3 + (16 + lr) * Lds::OP_LD + 32 * kk + 8 * lg) = l3q;
+        }
+      }
+      // Diagonal tiles A_ii = (k E)(k F)^T and P_ii = (q E)(k F)^T.  When every
+      // |gamma_r - gamma_mid| of the block is <= 7 (log2), E and F lie in
+      // [2^-7, 2^7] and the factors are plain fp16 operands; otherwise they
+      // are split into hi+lo bf16 pairs, which keep fp32 range.
+      f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
+      if (!__any(dgmax > 7.0f)) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          f16x8 ek, eq, fk;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            ek[e] = static_cast<_Float16>(kE[kk][e]);
+            eq[e] = static_cast<_Float16>(qE[kk][e]);
+            fk[e] = static_cast<_Float16>(kF[kk][e]);
+          }
+          accA = mma_f16(ek, fk, accA);
+          accP = mma_f16(eq, fk, accP);
+        }
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          bf16x8 ekh, ekl, eqh, eql, fkh, fkl;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
             __bf16 x0, x1;
             split_bf16(kE[kk][e], x0, x1); ekh[e] = x0; ekl[e] = x1;
             split_bf16(qE[kk][e], x0, x1); eqh[e] = x0; eql[e] = x1;
             split_bf16(kF[kk][e], x0, x1); fkh[e] = x0; fkl[e] = x1;
           }
+          accA = mma_bf16(ekh, fkh, accA);
+          accA = mma_bf16(ekh, fkl, accA);
+          accA = mma_bf16(ekl, fkh, accA);
+          accP = mma_bf16(eqh, fkh, accP);
+          accP = mma_bf16(eqh, fkl, accP);
+          accP = mma_bf16(eql, fkh, accP);
         }
-        accA = mma_bf16(ekh, fkh, accA);
-        accA = mma_bf16(ekh, fkl, accA);
-        accA = mma_bf16(ekl, fkh, accA);
-        accP = mma_bf16(eqh, fkh, accP);
-        accP = mma_bf16(eqh, fkl, accP);
-        accP = mma_bf16(eql, fkh, accP);
       }
-      // diagonal tile (bi, bi): lane holds rows 16bi + 4lg + i, column s = 16bi + lr
+      // -- P1w: diagonal tile (bi, bi): lane holds rows 16bi + 4lg + i, column s = 16bi + lr
       const int sp = ppos64(16 * bi + lr);
+      f32x4 nB;  // N = A_ii (strictly lower, beta-scaled rows) in accumulator layout
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int rr = 4 * lg + i, row = 16 * bi + rr;
-        scr[rr * Lds::SC_LD + lr] = (lr < rr) ? accA[i] * s_beta[row] : 0.0f;
+        nB[i] = (lr < rr) ? accA[i] * s_beta[row] : 0.0f;
         _Float16 x0, x1;
         split_f16((lr <= rr) ? accP[i] : 0.0f, x0, x1);
         Ph[row * Lds::TT_LD + sp] = x0;
@@ -413,118 +510,126 @@ __global__ void __launch_bounds__(NTHR, 1) chunk_kernel(
           Pl[row * Lds::TT_LD + su] = static_cast<_Float16>(0.0f);
         }
       }
-      // T_ii = (I + A_ii)^-1 by forward substitution, one column per lane
-      wave_lds_sync();
-      if (lane < 16) {
-        const int jj = lane;
-        float tc[16];
+      // -- P1t: T_ii = (I + N)^-1 = (I - N)(I + N^2)(I + N^4)(I + N^8), exact since
+      // N^16 = 0.  Products are 16x16x16 MFMAs: the left factor is read in operand
+      // layout through a wave-private LDS transpose, the right factor is an
+      // accumulator (hi+lo fp16).
+      auto to_a = [&](const f32x4& xb) -> f32x4 {  // accumulator layout -> A-operand layout
+        wave_lds_sync();
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-          float acc = (rr == jj) ? 1.0f : 0.0f;
+        for (int i = 0; i < 4; ++i) scr[(4 * lg + i) * Lds::SC_LD + lr] = xb[i];
+        wave_lds_sync();
+        return *reinterpret_cast<const f32x4*>(scr + lr * Lds::SC_LD + 4 * lg);
+      };
+      auto mul = [&](const f32x4& xa, const f32x4& yb) -> f32x4 {
+        f16x4 a, bh, bl;
 #pragma unroll
-          for (int s = 0; s < rr; ++s) acc -= scr[rr * Lds::SC_LD + s] * tc[s];
-          tc[rr] = acc;
-        }
+        for (int e = 0; e < 4; ++e) a[e] = static_cast<_Float16>(xa[e]);
+        bfrag16_split(yb, bh, bl);
+        f32x4 d = mma_f16_k16(a, bh, f32x4{0.f, 0.f, 0.f, 0.f});
+        return mma_f16_k16(a, bl, d);
+      };
+      f32x4 eye;
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr)
-          AT[(16 * bi + rr) * Lds::AT_LD + 16 * bi + jj] = static_cast<_Float16>(tc[rr]);
-      }
+      for (int i = 0; i < 4; ++i) eye[i] = (4 * lg + i == lr) ? 1.0f : 0.0f;  // same in both layouts
+      const f32x4 nA = to_a(nB);
+      const f32x4 n2B = mul(nA, nB);
+      const f32x4 n4B = mul(to_a(n2B), n2B);
+      const f32x4 n8B = mul(to_a(n4B), n4B);
+      const f32x4 m2B = mul(eye - nA, eye + n2B);
+      const f32x4 m3B = mul(to_a(m2B), eye + n4B);
+      const f32x4 tB = mul(to_a(m3B), eye + n8B);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        AT[(16 * bi + 4 * lg + i) * Lds::AT_LD + 16 * bi + lr] = static_cast<_Float16>(tB[i]);
     }
     __syncthreads();
 
-    // the chunk's q/k/g/beta are consumed: fetch the next chunk's
-    if (t0 + C < eos) prefetch_gkq(t0 + C);
-
-    // ================= P1b: operands that need the constants
+    // ================= P2: off-diagonal tiles (i, j<i): two per wave at most.
+    // Wave w multiplies its own left factors (rows of block w) except wave 0,
+    // which takes tile (3,0) with the left factors wave 3 left in LDS.
     {
-      const int kpos = ppos64(r);  // token-permuted column of this row in Khat^T
+      auto offdiag = [&](int ti, int tj) {
+        f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
+        const int slotc = cij_slot(ti, tj);
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        f16x8 kt, qt, rr8;
+        for (int kk = 0; kk < 4; ++kk) {
+          f16x8 lk, lq;
+          if (ti == bi) {
 #pragma unroll
-        for (int a = 0; a < 2; ++a) {
-          const int c = 32 * kk + 16 * a + 4 * lg;
-          const f32x4 em = *reinterpret_cast<const f32x4*>(cst + bi * D + c);
-          const f32x4 eL = *reinterpret_cast<const f32x4*>(cst + (4 + bi) * D + c);
-          const f32x4 eR = *reinterpret_cast<const f32x4*>(cst + (14 + (bi < 3 ? bi : 0)) * D + c);
+            for (int a = 0; a < 2; ++a) {
+              const f32x4 cc = *reinterpret_cast<const f32x4*>(cst + slotc * D + 32 * kk + 16 * a + 4 * lg);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int e = 4 * a + j;
-            kt[e] = static_cast<_Float16>(kE[kk][e] * em[j]);
-            qt[e] = static_cast<_Float16>(qE[kk][e] * em[j]);
-            KhT[(c + j) * Lds::TT_LD + kpos] = static_cast<_Float16>(kF[kk][e] * eL[j]);
-            rr8[e] = static_cast<_Float16>(kF[kk][e] * eR[j]);
+              for (int j = 0; j < 4; ++j) {
+                lk[4 * a + j] = static_cast<_Float16>(kE[kk][4 * a + j] * cc[j]);
+                lq[4 * a + j] = static_cast<_Float16>(qE[kk][4 * a + j] * cc[j]);
+              }
+            }
+          } else {
+            lk = *reinterpret_cast<const f16x8*>(L3 + lr * Lds::OP_LD + 32 * kk + 8 * lg);
+            lq = *reinterpret_cast<const f16x8*>(L3 + (16 + lr) * Lds::OP_LD + 32 * kk + 8 * lg);
           }
+          const f16x8 rb = *reinterpret_cast<const f16x8*>(Rb + (16 * tj + lr) * Lds::OP_LD + 32 * kk + 8 * lg);
+          accA = mma_f16(lk, rb, accA);
+          accP = mma_f16(lq, rb, accP);
         }
-        *reinterpret_cast<f16x8*>(Kt + r * Lds::OP_LD + 32 * kk + 8 * lg) = kt;
-        *reinterpret_cast<f16x8*>(Qt + r * Lds::OP_LD + 32 * kk + 8 * lg) = qt;
-        if (bi < 3) *reinterpret_cast<f16x8*>(Rb + r * Lds::OP_LD + 32 * kk + 8 * lg) = rr8;
-      }
-    }
-    __syncthreads();
-
-    // ================= P2: off-diagonal tiles (i, j<i), i = this wave's block
+        const int sp = ppos64(16 * tj + lr);
 #pragma unroll
-    for (int bj = 0; bj < 3; ++bj) {
-      if (bj >= bi) continue;
-      f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
-      const int slotc = cij_slot(bi, bj);
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        f16x8 lk, lq;
-#pragma unroll
-        for (int a = 0; a < 2; ++a) {
-          const f32x4 cc = *reinterpret_cast<const f32x4*>(cst + slotc * D + 32 * kk + 16 * a + 4 * lg);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            lk[4 * a + j] = static_cast<_Float16>(kE[kk][4 * a + j] * cc[j]);
-            lq[4 * a + j] = static_cast<_Float16>(qE[kk][4 * a + j] * cc[j]);
-          }
+        for (int i = 0; i < 4; ++i) {
+          const int row = 16 * ti + 4 * lg + i;
+          AT[row * Lds::AT_LD + 16 * tj + lr] = static_cast<_Float16>(-accA[i] * s_beta[row]);
+          _Float16 x0, x1;
+          split_f16(accP[i], x0, x1);
+          Ph[row * Lds::TT_LD + sp] = x0;
+          Pl[row * Lds::TT_LD + sp] = x1;
         }
-        const f16x8 rb = *reinterpret_cast<const f16x8*>(Rb + (16 * bj + lr) * Lds::OP_LD + 32 * kk + 8 * lg);
-        accA = mma_f16(lk, rb, accA);
-        accP = mma_f16(lq, rb, accP);
-      }
-      const int sp = ppos64(16 * bj + lr);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 16 * bi + 4 * lg + i;
-        AT[row * Lds::AT_LD + 16 * bj + lr] = static_cast<_Float16>(-accA[i] * s_beta[row]);
-        _Float16 x0, x1;
-        split_f16(accP[i], x0, x1);
-        Ph[row * Lds::TT_LD + sp] = x0;
-        Pl[row * Lds::TT_LD + sp] = x1;
+      };
+      if (bi == 0) {
+        offdiag(3, 0);
+      } else if (bi == 1) {
+        offdiag(1, 0);
+      } else if (bi == 2) {
+        offdiag(2, 0);
+        offdiag(2, 1);
+      } else {
+        offdiag(3, 1);
+        offdiag(3, 2);
       }
     }
     __syncthreads();
 
     // ================= P3: state products for value column jcol (no barriers)
     {
+      const bool more = t0 + C < eos;
+      if (more) {  // operands of this chunk are consumed: fetch the next chunk's
+        stage_g(t0 + C);
+        prefetch_kq(t0 + C);
+      }
       // S as B fragments (hi/lo), contraction over key channels
       f16x8 sbh[4], sbl[4];
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) bfrag_split(Sacc[2 * kk], Sacc[2 * kk + 1], sbh[kk], sbl[kk]);
-      // X = V - Kt S ;  O = Qt S
+      // X = V - Kt S ;  O = Qt S   (8 independent accumulator chains)
       f32x4 Xacc[4], Oacc[4];
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        f32x4 ax = {0.f, 0.f, 0.f, 0.f}, ao = {0.f, 0.f, 0.f, 0.f};
+      for (int rt = 0; rt < 4; ++rt) Xacc[rt] = Oacc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
+      for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
           const f16x8 ak = *reinterpret_cast<const f16x8*>(Kt + (16 * rt + lr) * Lds::OP_LD + 32 * kk + 8 * lg);
           const f16x8 aq = *reinterpret_cast<const f16x8*>(Qt + (16 * rt + lr) * Lds::OP_LD + 32 * kk + 8 * lg);
-          ax = mma_f16(ak, sbh[kk], ax);
-          ax = mma_f16(ak, sbl[kk], ax);
-          ao = mma_f16(aq, sbh[kk], ao);
-          ao = mma_f16(aq, sbl[kk], ao);
+          Xacc[rt] = mma_f16(ak, sbh[kk], Xacc[rt]);
+          Oacc[rt] = mma_f16(aq, sbh[kk], Oacc[rt]);
+          Xacc[rt] = mma_f16(ak, sbl[kk], Xacc[rt]);
+          Oacc[rt] = mma_f16(aq, sbl[kk], Oacc[rt]);
         }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ax[i] = ((16 * rt + 4 * lg + i < Lc) ? vval(4 * rt + i) : 0.0f) - ax[i];
-        Xacc[rt] = ax;
-        Oacc[rt] = ao;
       }
-      // the chunk's v is consumed: fetch the next chunk's
-      if (t0 + C < eos) prefetch_v(t0 + C);
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Xacc[rt][i] = vval(4 * rt + i) - Xacc[rt][i];
+      if (more) prefetch_v(t0 + C);  // v of this chunk is consumed
       // -- P3b: Delta_i = T_ii (b_i X_i - sum_{j<i} A_ij Delta_j), 16-row blocks
       f32x4 Dacc[4];
 #pragma unroll
@@ -550,7 +655,9 @@ __global__ void __launch_bounds__(NTHR, 1) chunk_kernel(
       f16x8 dbh[2], dbl[2];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) bfrag_split(Dacc[2 * ks], Dacc[2 * ks + 1], dbh[ks], dbl[ks]);
-      // -- P3c: O += P Delta ; store o
+      // -- P3c: O += P Delta ; store o (rows past the chunk end are dropped)
+      const char* ob = static_cast<const char*>(o) + ((int64_t)t0 * HD + (int64_t)h * D) * OS;
+      const auto ro = make_buf(ob, (uint32_t)(Lc * HD * OS - h * D * OS));
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
         f32x4 ao = Oacc[rt];
@@ -565,13 +672,13 @@ __global__ void __launch_bounds__(NTHR, 1) chunk_kernel(
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int rr = 16 * rt + 4 * lg + i;
-          if (rr < Lc) {
-            const int64_t oi = (int64_t)(t0 + rr) * HD + hD + jcol;
-            const float val = scale * ao[i];
-            if (O_BF16) static_cast<uint16_t*>(o)[oi] = f32_to_bf16_bits(val);
-            else static_cast<float*>(o)[oi] = val;
-          }
+          const int soff = (16 * rt + i) * HD * OS;
+          const float val = scale * ao[i];
+          if constexpr (O_BF16)
+            __builtin_amdgcn_raw_buffer_store_b16(
+                __builtin_bit_cast(uint16_t, static_cast<__bf16>(val)), ro, off_o, soff, 0);
+          else
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), ro, off_o, soff, 0);
         }
       }
       // -- P3d: S <- e^gamma_C S + Khat^T Delta
@@ -588,6 +695,7 @@ __global__ void __launch_bounds__(NTHR, 1) chunk_kernel(
         Sacc[t] = s;
       }
     }
+    wait_loads();
     __syncthreads();
   }
 

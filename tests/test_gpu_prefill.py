@@ -176,3 +176,23 @@ def test_config2_full_sampled_heads():
 def test_config3_full_sampled_heads():
     need_gpu()
     _full_config(3, 3, 3)
+
+
+def test_strong_decay_heads():
+    """Heads whose channels decay by tens of nats per 16-token block (the
+    checkpoint's A_log reaches 2.47): exercises the decay-factor references
+    and the wide-range path of the diagonal tiles."""
+    need_gpu()
+    dr = draw_prefill([200, 77], H=4, dtype=torch.bfloat16, init_state=True, seed=41)
+    dr.A_log = torch.tensor([1.5, -0.75, 1.0, 0.0])
+    dt = dr.dt_bias.clone()
+    dt[0] = 0.0                     # head 0: every channel fast (about 3.6 nats per token)
+    dt[2, :16] = 1.0                # head 2: a few fast channels among slow ones
+    dr.dt_bias = dt
+    g, beta = oracle_gate_f32(dr)
+    say("strong decay heads")
+    o_ref, S_ref = oracle.prefill(dr.q, dr.k, dr.v, g, beta, dr.cu_seqlens, dr.initial_state)
+    o, S = _run_gpu(dr, g, beta, torch.float32, S0=dr.initial_state)
+    assert torch.isfinite(o).all() and torch.isfinite(S).all()
+    assert_out(o, o_ref, "strong decay")
+    assert_state(S, S_ref, "strong decay")
