@@ -19,6 +19,7 @@ Timing follows the audit page's protocol shape (warmup, repeated timed
 launches, event timing, output buffers reused).
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -44,6 +45,29 @@ PREFILL_FLOPS = 2 * MAC_PER_CHUNK_HEAD * (T // C) * H                 # 5.52e10
 DEC_N, DEC_STEPS = 256, 64
 DEC_PAIR_BYTES = 2 * D * D * 4 + 3 * D * 2 + D * 4 + 4 + D * 2       # 132,612
 DEC_STEP_BYTES = DEC_N * H * DEC_PAIR_BYTES                           # 3,259,072,512
+
+
+# HBM traffic of one kda_chunk_prefill call, from the committed rocprofv3
+# FETCH_SIZE / WRITE_SIZE summary; valid only while the kernel sources hash to
+# the value recorded with the counters.
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "chunk_prefill_T4096_H96_hbm_traffic.md")
+CHUNK_SOURCES = ["gated_delta_rule_58_amd/csrc/chunk.hip"]
+
+
+def measured_traffic():
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+    except OSError:
+        return None
+    fields = dict(l.split(": ", 1) for l in text.splitlines()
+                  if l.startswith(("traffic_bytes_per_launch: ", "source_sha256: ")))
+    h = hashlib.sha256()
+    for f in CHUNK_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    if fields.get("source_sha256", "").strip() != h.hexdigest():
+        return None
+    return int(fields["traffic_bytes_per_launch"])
 
 
 def parse():
@@ -230,7 +254,7 @@ def main():
                     "chunk_kernel_ms": pre["chunk_ms"], "gate_kernel_ms": pre["gate_ms"],
                     "prefill_only_tokens_per_s": T / chunk_s},
         "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": ach / HBM_PEAK_GBS, "traffic": None,
+                     "frac": ach / HBM_PEAK_GBS, "traffic": measured_traffic(),
                      "kernel": "chunk_kernel (kda_chunk_prefill)",
                      "alg_bytes_per_launch": PREFILL_BYTES},
         "roofline_mfma": {"achieved": mfma, "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",

@@ -61,7 +61,11 @@ kda_status kda_gate(const void* x, kda_dtype x_dt, const void* b, kda_dtype b_dt
   if (dt_bias_len != (int64_t)H * d)
     return fail(KDA_ERR_SHAPE, "kda_gate: dt_bias has %lld values, need H*d = %lld",
                 (long long)dt_bias_len, (long long)H * d);
-  if (d % 4 != 0) return fail(KDA_ERR_UNSUPPORTED, "kda_gate: d must be a multiple of 4 (got %d)", d);
+  if (d % 4 != 0 || d > 1024)
+    return fail(KDA_ERR_UNSUPPORTED, "kda_gate: d must be a multiple of 4 and at most 1024 (got %d)",
+                d);
+  if ((H + 256 / (d / 4) - 1) / (256 / (d / 4)) > 65535)
+    return fail(KDA_ERR_UNSUPPORTED, "kda_gate: H = %d is too large for d = %d", H, d);
   if (!A_log || !dt_bias) return fail(KDA_ERR_INVALID_ARG, "kda_gate: A_log/dt_bias is NULL");
   if (n_tok == 0) return ok();
   if (!x || !b || !g_out || !beta_out)

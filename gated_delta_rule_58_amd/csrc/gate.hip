@@ -5,46 +5,92 @@
 // table): A_log one value per head, dt_bias one per (head, channel).  beta is
 // squashed here in fp32 (Model-Optimizer PR #2749 review, KDA beta fix).
 //
-// Each thread handles 4 consecutive channels (one 16-byte fp32 load of x, one
-// 16-byte store of g); the thread that owns channel 0 of a (token, head) row
-// also writes beta.  Grid-stride loop, launched with enough blocks to fill
-// every CU several times over.
+// Work split: blockIdx.y picks a group of R = 256 / (d/4) heads, blockIdx.x a
+// run of tokens.  A thread owns one (head, 4-channel) slot for the whole run,
+// so -exp(A_log[h]) and its dt_bias quad are loaded once and every token costs
+// one 16-byte load of x and one 16-byte store of g.  A wave covers 256
+// consecutive channels of one token: fully coalesced.  beta for the block's
+// (token, head) pairs is one extra pass by one lane per pair.
+//
+// Arithmetic: the softplus tail log1p(exp(-|z|)) uses the hardware exp2/log2
+// with two corrections that keep it within a few ulp of the exact value, where
+// a plain log2(1 + e) would lose up to all of the digits of a small e:
+//   e = 2^(-t) with t = |z| log2(e) rounded; the product's residual (an fma)
+//       and the fp32 constant's own error are folded back in to first order;
+//   log1p(e) = log(u) * e / (u - 1) with u = fl(1 + e) (exact when u = 1).
 #include "kda_device.hpp"
 #include "kda_internal.hpp"
 
 namespace kda {
 namespace {
 
-__device__ __forceinline__ float softplus_f32(float z) {
-  // max(z,0) + log1p(exp(-|z|)): no overflow, accurate for large |z|.
-  return fmaxf(z, 0.0f) + log1pf(expf(-fabsf(z)));
+constexpr float kLog2e = 1.4426950216293335f;     // fp32 nearest of log2(e)
+constexpr float kLog2eLo = 1.92596298909109e-08f;  // log2(e) - kLog2e
+constexpr float kLn2 = 0.6931471824645996f;
+
+constexpr int kThreads = 256;
+constexpr int kTokUnroll = 4;   // x loads in flight per thread
+constexpr int kTokPerBlock = 32;
+
+__device__ __forceinline__ float softplus_tail(float az) {
+  // log1p(exp(-az)) for az = |z| >= 0; beyond 200 the value is below fp32's
+  // range (and an infinite az must not reach the residual product).
+  az = fminf(az, 200.0f);
+  const float t = az * kLog2e;
+  const float r = fmaf(az, kLog2e, -t) + az * kLog2eLo;  // az*log2(e) - t
+  const float e = __builtin_amdgcn_exp2f(-t) * fmaf(-r, kLn2, 1.0f);
+  const float u = 1.0f + e;
+  const float d = u - 1.0f;
+  const float l = __builtin_amdgcn_logf(u) * kLn2 * (e * __builtin_amdgcn_rcpf(d));
+  return d == 0.0f ? e : l;
 }
 
 template <bool XBF16, bool BBF16>
-__global__ void __launch_bounds__(256) gate_kernel(const void* __restrict__ x,
-                                                   const void* __restrict__ b,
-                                                   const float* __restrict__ A_log,
-                                                   const float* __restrict__ dt_bias,
-                                                   float* __restrict__ g,
-                                                   float* __restrict__ beta, int64_t n_quads,
-                                                   int H, int d) {
-  const int quads_per_row = d >> 2;
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n_quads;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t row = i / quads_per_row;  // (token, head) row
-    const int c = static_cast<int>(i - row * quads_per_row) << 2;
-    const int h = static_cast<int>(row % H);
-    const f32x4 xv = load4(x, i << 2, XBF16);
-    const f32x4 db = *reinterpret_cast<const f32x4*>(dt_bias + (int64_t)h * d + c);
+__global__ void __launch_bounds__(kThreads) gate_kernel(
+    const void* __restrict__ x, const void* __restrict__ b, const float* __restrict__ A_log,
+    const float* __restrict__ dt_bias, float* __restrict__ g, float* __restrict__ beta,
+    int n_tok, int H, int d, int rows_per_block) {
+  const int qpr = d >> 2;
+  const int tid = threadIdx.x;
+  const int hh = tid / qpr;
+  const int h = blockIdx.y * rows_per_block + hh;
+  const int c = (tid - hh * qpr) << 2;
+  const int tok0 = blockIdx.x * kTokPerBlock;
+  const int ntk = min(kTokPerBlock, n_tok - tok0);
+  const int64_t tok_stride = (int64_t)H * d;
+
+  if (hh < rows_per_block && h < H) {
     const float a = -expf(A_log[h]);
-    f32x4 out;
+    const f32x4 db = *reinterpret_cast<const f32x4*>(dt_bias + (int64_t)h * d + c);
+    const int64_t base = (int64_t)tok0 * tok_stride + (int64_t)h * d + c;
+    for (int t = 0; t < ntk; t += kTokUnroll) {
+      f32x4 xv[kTokUnroll];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) out[e] = a * softplus_f32(xv[e] + db[e]);
-    *reinterpret_cast<f32x4*>(g + (i << 2)) = out;
-    if (c == 0) {
-      const float bl = load1(b, row, BBF16);
-      beta[row] = 1.0f / (1.0f + expf(-bl));
+      for (int u = 0; u < kTokUnroll; ++u)
+        if (t + u < ntk) xv[u] = load4(x, base + (t + u) * tok_stride, XBF16);
+#pragma unroll
+      for (int u = 0; u < kTokUnroll; ++u) {
+        if (t + u < ntk) {
+          f32x4 out;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float z = xv[u][e] + db[e];
+            out[e] = a * (fmaxf(z, 0.0f) + softplus_tail(fabsf(z)));
+          }
+          *reinterpret_cast<f32x4*>(g + base + (t + u) * tok_stride) = out;
+        }
+      }
     }
+  }
+
+  // beta = sigmoid(b) for the block's (token, head) pairs.
+  const int hbase = blockIdx.y * rows_per_block;
+  const int nh = min(rows_per_block, H - hbase);
+  for (int i = tid; i < ntk * nh; i += kThreads) {
+    const int tk = i / nh;
+    const int64_t row = (int64_t)(tok0 + tk) * H + hbase + (i - tk * nh);
+    const float bl = load1(b, row, BBF16);
+    beta[row] = 1.0f / (1.0f + expf(-bl));
   }
 }
 
@@ -53,21 +99,36 @@ __global__ void __launch_bounds__(256) gate_kernel(const void* __restrict__ x,
 hipError_t launch_gate(const void* x, bool x_bf16, const void* b, bool b_bf16, const float* A_log,
                        const float* dt_bias, float* g, float* beta, int64_t n_tok, int H, int d,
                        hipStream_t s) {
-  const int64_t n_quads = n_tok * H * (d / 4);
-  if (n_quads == 0) return hipSuccess;
-  const int threads = 256;
-  int64_t blocks = (n_quads + threads - 1) / threads;
-  const int64_t cap = 256 * 32;  // 32 blocks per CU on 256 CUs, then grid-stride
-  if (blocks > cap) blocks = cap;
-  if (x_bf16 && b_bf16)
-    gate_kernel<true, true><<<blocks, threads, 0, s>>>(x, b, A_log, dt_bias, g, beta, n_quads, H, d);
-  else if (x_bf16)
-    gate_kernel<true, false><<<blocks, threads, 0, s>>>(x, b, A_log, dt_bias, g, beta, n_quads, H, d);
-  else if (b_bf16)
-    gate_kernel<false, true><<<blocks, threads, 0, s>>>(x, b, A_log, dt_bias, g, beta, n_quads, H, d);
-  else
-    gate_kernel<false, false><<<blocks, threads, 0, s>>>(x, b, A_log, dt_bias, g, beta, n_quads, H, d);
-  return hipGetLastError();
+  if (n_tok == 0) return hipSuccess;
+  // d is a multiple of 4 with d/4 <= 256 (checked by the caller).
+  const int rows_per_block = kThreads / (d >> 2);
+  const int head_groups = (H + rows_per_block - 1) / rows_per_block;
+  // One launch covers at most 2^30 tokens so the block index stays in range.
+  const int64_t max_tok = (int64_t)1 << 30;
+  for (int64_t t0 = 0; t0 < n_tok; t0 += max_tok) {
+    const int nt = static_cast<int>(n_tok - t0 < max_tok ? n_tok - t0 : max_tok);
+    const int64_t off = t0 * H;
+    const void* xs = static_cast<const char*>(x) + off * d * (x_bf16 ? 2 : 4);
+    const void* bs = static_cast<const char*>(b) + off * (b_bf16 ? 2 : 4);
+    float* gs = g + off * d;
+    float* betas = beta + off;
+    const dim3 grid((nt + kTokPerBlock - 1) / kTokPerBlock, head_groups);
+    if (x_bf16 && b_bf16)
+      gate_kernel<true, true><<<grid, kThreads, 0, s>>>(xs, bs, A_log, dt_bias, gs, betas, nt, H,
+                                                        d, rows_per_block);
+    else if (x_bf16)
+      gate_kernel<true, false><<<grid, kThreads, 0, s>>>(xs, bs, A_log, dt_bias, gs, betas, nt, H,
+                                                         d, rows_per_block);
+    else if (b_bf16)
+      gate_kernel<false, true><<<grid, kThreads, 0, s>>>(xs, bs, A_log, dt_bias, gs, betas, nt, H,
+                                                         d, rows_per_block);
+    else
+      gate_kernel<false, false><<<grid, kThreads, 0, s>>>(xs, bs, A_log, dt_bias, gs, betas, nt,
+                                                          H, d, rows_per_block);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace kda

@@ -81,7 +81,7 @@ const char* kda_version(void);
  *   dt_bias  [dt_bias_len]  fp32, dt_bias_len must equal H*d
  *   g_out    [n_tok, H, d]  fp32 output
  *   beta_out [n_tok, H]     fp32 output
- * Requires d % 4 == 0 and 16-byte aligned x/g_out (8-byte for bf16 x).
+ * Requires d % 4 == 0, d <= 1024 and 16-byte aligned x/g_out (8-byte for bf16 x).
  * n_tok == 0 is a no-op.
  */
 kda_status kda_gate(const void* x, kda_dtype x_dt, const void* b, kda_dtype b_dt,
