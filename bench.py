@@ -51,7 +51,8 @@ DEC_STEP_BYTES = DEC_N * H * DEC_PAIR_BYTES                           # 3,259,07
 # FETCH_SIZE / WRITE_SIZE summary; valid only while the kernel sources hash to
 # the value recorded with the counters.
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "chunk_prefill_T4096_H96_hbm_traffic.md")
-CHUNK_SOURCES = ["gated_delta_rule_58_amd/csrc/chunk.hip"]
+CHUNK_SOURCES = ["gated_delta_rule_58_amd/csrc/prep.hip", "gated_delta_rule_58_amd/csrc/state.hip",
+                 "gated_delta_rule_58_amd/csrc/chunk_common.hpp"]
 
 
 def measured_traffic():
@@ -117,9 +118,12 @@ def bench_prefill(args, torch, kda, synth):
     def gate():
         kda.gate(dr.x, dr.b, dr.A_log, dr.dt_bias, g_out=g, beta_out=beta)
 
+    ws = torch.empty(kda.chunk_prefill_workspace_bytes(1, H, D, D, T // C), dtype=torch.uint8,
+                     device=dev)
+
     def prefill():
         kda.chunk_prefill(dr.q, dr.k, dr.v, g, beta, cu_d, None, out=o, final_state=Sf,
-                          cu_seqlens_host=cu_h)
+                          cu_seqlens_host=cu_h, workspace=ws)
 
     for _ in range(args.warmup):
         gate()
@@ -255,7 +259,7 @@ def main():
                     "prefill_only_tokens_per_s": T / chunk_s},
         "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": ach / HBM_PEAK_GBS, "traffic": measured_traffic(),
-                     "kernel": "chunk_kernel (kda_chunk_prefill)",
+                     "kernel": "kda_chunk_prefill (prep_kernel + state_kernel, one pass)",
                      "alg_bytes_per_launch": PREFILL_BYTES},
         "roofline_mfma": {"achieved": mfma, "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                           "frac": mfma / MFMA_F16_PEAK_TFLOPS,

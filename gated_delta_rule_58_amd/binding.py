@@ -10,7 +10,12 @@ import torch
 KDA_F32 = 0
 KDA_BF16 = 1
 _STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARG", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_DTYPE",
-           4: "KDA_ERR_UNSUPPORTED", 5: "KDA_ERR_ALIGNMENT", 7: "KDA_ERR_LAUNCH"}
+           4: "KDA_ERR_UNSUPPORTED", 5: "KDA_ERR_ALIGNMENT", 6: "KDA_ERR_WORKSPACE",
+           7: "KDA_ERR_LAUNCH"}
+# default cap on the prefill workspace the binding allocates (the chunk axis is
+# processed in passes when a batch needs more)
+DEFAULT_WORKSPACE_BYTES = 1 << 30
+CHUNK = 64
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -49,7 +54,9 @@ def lib():
         L.kda_chunk_prefill.restype = ctypes.c_int
         L.kda_chunk_prefill.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _vp, _i32,
                                         _vp, _vp, _vp, ctypes.c_int, _i64, _i32, _i32, _i32,
-                                        ctypes.c_float, _vp]
+                                        ctypes.c_float, _vp, ctypes.c_size_t, _vp]
+        L.kda_chunk_prefill_workspace_bytes.restype = ctypes.c_size_t
+        L.kda_chunk_prefill_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32, _i32]
         L.kda_recurrent_decode.restype = ctypes.c_int
         L.kda_recurrent_decode.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _vp,
                                            ctypes.c_int, _i32, _i32, _i32, _i32, ctypes.c_float,
@@ -60,7 +67,7 @@ def lib():
 
 def exported_symbols():
     return ["kda_last_error", "kda_version", "kda_gate", "kda_chunk_prefill",
-            "kda_recurrent_decode"]
+            "kda_chunk_prefill_workspace_bytes", "kda_recurrent_decode"]
 
 
 def _check(status: int):
@@ -104,15 +111,25 @@ def gate(x: torch.Tensor, b: torch.Tensor, A_log: torch.Tensor, dt_bias: torch.T
     return g_out, beta_out
 
 
+def chunk_prefill_workspace_bytes(N: int, H: int, dk: int = 128, dv: int = 128,
+                                  chunks_per_pass: int = 1) -> int:
+    """kda_chunk_prefill_workspace_bytes."""
+    return int(lib().kda_chunk_prefill_workspace_bytes(N, H, dk, dv, chunks_per_pass))
+
+
 def chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
                   beta: torch.Tensor, cu_seqlens: Optional[torch.Tensor] = None,
                   initial_state: Optional[torch.Tensor] = None, output_final_state: bool = True,
                   scale: float = 1.0, o_dtype: Optional[torch.dtype] = None,
                   out: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
-                  cu_seqlens_host: Optional[torch.Tensor] = None):
+                  cu_seqlens_host: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None,
+                  max_workspace_bytes: int = DEFAULT_WORKSPACE_BYTES):
     """kda_chunk_prefill on packed [T_tot, H, d] tensors.
 
     cu_seqlens: int32 [N+1] (device); None means one sequence of length T_tot.
+    workspace: uint8 device tensor; None allocates one that covers the longest
+    sequence in one pass, capped at max_workspace_bytes (at least the minimum).
     Returns (o [T_tot,H,dv], final_state [N,H,dk,dv] or None).
     """
     T, H, dk = q.shape
@@ -132,10 +149,18 @@ def chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
     if final_state is None and output_final_state:
         final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
     hp = cu_seqlens_host.contiguous()
+    if workspace is None:
+        lens = (hp[1:] - hp[:-1]).clamp(min=0)
+        max_chunks = max(1, int((int(lens.max()) + CHUNK - 1) // CHUNK)) if N > 0 else 1
+        one = chunk_prefill_workspace_bytes(N, H, dk, dv, 1)
+        per = chunk_prefill_workspace_bytes(N, H, dk, dv, 2) - one
+        fit = max(1, (max_workspace_bytes - (one - per)) // per) if per > 0 else 1
+        nbytes = chunk_prefill_workspace_bytes(N, H, dk, dv, int(min(max_chunks, fit)))
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
     st = lib().kda_chunk_prefill(
         _ptr(q), _ptr(k), _ptr(v), _dt(q), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
         ctypes.cast(hp.data_ptr(), _vp), N, _ptr(initial_state), _ptr(final_state), _ptr(out),
-        _dt(out), T, H, dk, dv, float(scale), _stream(dev))
+        _dt(out), T, H, dk, dv, float(scale), _ptr(workspace), workspace.numel(), _stream(dev))
     _check(st)
     return out, final_state
 

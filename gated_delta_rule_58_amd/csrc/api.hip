@@ -83,7 +83,8 @@ kda_status kda_chunk_prefill(const void* q, const void* k, const void* v, kda_dt
                              const int32_t* cu_seqlens_host, int32_t N,
                              const float* initial_state, float* final_state, void* o,
                              kda_dtype o_dt, int64_t T_tot, int32_t H, int32_t dk,
-                             int32_t dv, float scale, void* stream) {
+                             int32_t dv, float scale, void* workspace, size_t workspace_bytes,
+                             void* stream) {
   if (N <= 0 || H <= 0 || T_tot < 0)
     return fail(KDA_ERR_INVALID_ARG, "kda_chunk_prefill: need N > 0, H > 0, T_tot >= 0 "
                                      "(got %d, %d, %lld)", N, H, (long long)T_tot);
@@ -114,10 +115,25 @@ kda_status kda_chunk_prefill(const void* q, const void* k, const void* v, kda_dt
       return fail(KDA_ERR_ALIGNMENT, "kda_chunk_prefill: tensors must be 16-byte aligned");
   if (!aligned(beta, 4) || !aligned(cu_seqlens, 4))
     return fail(KDA_ERR_ALIGNMENT, "kda_chunk_prefill: beta/cu_seqlens must be 4-byte aligned");
-  return launched(kda::launch_chunk_prefill(q, k, v, qkv_dt == KDA_BF16, g, beta, cu_seqlens, N,
-                                            initial_state, final_state, o, o_dt == KDA_BF16, T_tot,
-                                            H, scale, static_cast<hipStream_t>(stream)),
+  const size_t ws_min = kda::chunk_workspace_bytes(N, H, 1);
+  if (!workspace || workspace_bytes < ws_min)
+    return fail(KDA_ERR_WORKSPACE, "kda_chunk_prefill: need a workspace of at least %zu bytes "
+                                   "(got %zu at %p)", ws_min, workspace_bytes, workspace);
+  if (!aligned(workspace, 256))
+    return fail(KDA_ERR_ALIGNMENT, "kda_chunk_prefill: workspace must be 256-byte aligned");
+  if ((int64_t)N * H > ((int64_t)1 << 24) || H > 16384)
+    return fail(KDA_ERR_UNSUPPORTED, "kda_chunk_prefill: need H <= 16384 and N*H <= 2^24");
+  return launched(kda::launch_chunk_prefill(q, k, v, qkv_dt == KDA_BF16, g, beta, cu_seqlens,
+                                            cu_seqlens_host, N, initial_state, final_state, o,
+                                            o_dt == KDA_BF16, T_tot, H, scale, workspace,
+                                            workspace_bytes, static_cast<hipStream_t>(stream)),
                   "kda_chunk_prefill");
+}
+
+size_t kda_chunk_prefill_workspace_bytes(int32_t N, int32_t H, int32_t dk, int32_t dv,
+                                         int32_t chunks_per_pass) {
+  if (dk != 128 || dv != 128) return 0;
+  return kda::chunk_workspace_bytes(N, H, chunks_per_pass);
 }
 
 kda_status kda_recurrent_decode(const void* q, const void* k, const void* v, kda_dtype qkv_dt,

@@ -1,0 +1,55 @@
+// Host side of kda_chunk_prefill: passes over the chunk axis.
+//
+// The workspace holds a state carry [N, H, 128, 128] fp32 followed by the
+// images of S_len chunks of every (sequence, head).  Each pass launches the
+// prep kernel on chunks [c_lo, c_lo + S_len) of every sequence, then the
+// state kernel, which walks those chunks from the carried state.  One pass
+// covers the whole batch when S_len reaches the longest sequence's chunk
+// count.
+#include "chunk_common.hpp"
+#include "kda_internal.hpp"
+
+namespace kda {
+
+size_t chunk_workspace_bytes(int N, int H, int chunks_per_pass) {
+  if (N <= 0 || H <= 0 || chunks_per_pass <= 0) return 0;
+  const size_t pairs = (size_t)N * H;
+  return pairs * chunk::D * chunk::D * sizeof(float) +
+         pairs * (size_t)chunks_per_pass * chunk::Ws::bytes;
+}
+
+hipError_t launch_chunk_prefill(const void* q, const void* k, const void* v, bool qkv_bf16,
+                                const float* g, const float* beta, const int32_t* cu,
+                                const int32_t* cu_host, int N, const float* S0, float* S_final,
+                                void* o, bool o_bf16, int64_t T_tot, int H, float scale,
+                                void* ws, size_t ws_bytes, hipStream_t s) {
+  using namespace chunk;
+  int64_t max_nch = (T_tot + C - 1) / C;
+  if (cu_host) {
+    max_nch = 0;
+    for (int n = 0; n < N; ++n) {
+      const int64_t nc = ((int64_t)cu_host[n + 1] - cu_host[n] + C - 1) / C;
+      if (nc > max_nch) max_nch = nc;
+    }
+  }
+  const size_t pairs = (size_t)N * H;
+  const size_t carry_bytes = pairs * D * D * sizeof(float);
+  int64_t S_len = (int64_t)((ws_bytes - carry_bytes) / (pairs * Ws::bytes));  // >= 1 (checked)
+  if (S_len > max_nch) S_len = max_nch > 0 ? max_nch : 1;
+  float* carry = S_final ? S_final : static_cast<float*>(ws);
+  char* images = static_cast<char*>(ws) + carry_bytes;
+  const int T = static_cast<int>(T_tot);
+  for (int64_t c_lo = 0;; c_lo += S_len) {
+    const bool last = c_lo + S_len >= max_nch;
+    hipError_t e = chunk::launch_prep(q, k, qkv_bf16, g, beta, cu, N, T, H, (int)c_lo,
+                                      (int)S_len, images, s);
+    if (e != hipSuccess) return e;
+    e = chunk::launch_state(v, qkv_bf16, cu, N, T, H, c_lo == 0 ? S0 : carry,
+                            last ? S_final : carry, o, o_bf16, scale, (int)c_lo, (int)S_len,
+                            images, s);
+    if (e != hipSuccess) return e;
+    if (last) return hipSuccess;
+  }
+}
+
+}  // namespace kda

@@ -1,0 +1,328 @@
+// State kernel of kda_chunk_prefill: the inter-chunk recurrence.
+//
+// One workgroup per (sequence, head, 64-column value tile); it walks the
+// chunks of its sequence in order.  Per chunk, with the chunk's workspace
+// image (written by the prep kernel) in LDS:
+//   X     = V - (K e^gamma) S                      (S the entry state)
+//   Delta_i = T_ii (b_i X_i - sum_{j<i} A_ij Delta_j)   16-row blocks i
+//   O     = scale ((Q e^gamma) S + P Delta)
+//   S    <- Diag(e^gamma_C) S + (K e^(gamma_C - gamma))^T Delta
+//
+// Waves 0..3 compute.  Every product is independent across value columns, so
+// compute wave w owns columns 16w..16w+15 of the tile and keeps its 128x16
+// slice of S, and its 64x16 slices of X, Delta and O, in MFMA accumulators:
+// no barriers inside a chunk.  The contraction index of every 16x16x32
+// product whose B operand comes from an accumulator is stored permuted in the
+// image (pperm), so an accumulator tile pair is directly the next product's B
+// fragment.
+//
+// Wave 4 moves data.  While chunk c is computed it stores chunk c-1's output
+// tile from LDS to o and copies chunk c+1's image (60 KiB) and v tile into
+// the other LDS buffers with 16-byte buffer-to-LDS loads, so the compute
+// waves never wait on a memory instruction.  One workgroup barrier per chunk.
+// (fp32 v or o, used only off the benchmarked path, go through the compute
+// waves' registers instead.)
+//
+// Precision: operands are fp16 MFMA fragments with fp32 accumulation; S, X
+// and Delta enter the products as hi+lo fp16 pairs.
+#include "chunk_common.hpp"
+#include "kda_internal.hpp"
+
+namespace kda {
+namespace chunk {
+namespace {
+
+constexpr int DV = 64;  // value columns per workgroup
+constexpr int NT = D / DV;
+constexpr int NTHR_S = NTHR + 64;  // 4 compute waves + 1 data wave
+constexpr int TILE_BYTES = C * DV * 2;  // bf16 v or o tile of one chunk
+
+struct StateLds {
+  static constexpr int off_img = 0;                             // 2 images
+  static constexpr int off_v = off_img + 2 * Ws::bytes;         // 2 bf16 v tiles
+  static constexpr int off_o = off_v + 2 * TILE_BYTES;          // 2 bf16 o tiles
+  static constexpr int total = off_o + 2 * TILE_BYTES;
+};
+static_assert(StateLds::total <= 160 * 1024, "LDS budget");
+
+// byte offset of (row r, column j < 64) in a bf16 v / o tile: 128-byte rows,
+// 16-byte chunk j>>3 swizzled so the four row groups 4lg+i of an accumulator
+// tile hit disjoint banks.
+__device__ __forceinline__ int tile_off(int r, int j) {
+  return r * 128 + ((((j >> 3) ^ (((r >> 2) & 3) << 1))) << 4) + ((j & 7) << 1);
+}
+
+template <bool QKV_BF16, bool O_BF16>
+__global__ void __launch_bounds__(NTHR_S, 1) state_kernel(
+    const void* __restrict__ v, const int32_t* __restrict__ cu, int N, int T_tot, int H, int Hp,
+    const float* S_in, float* S_out, void* __restrict__ o, float scale, int c_lo, int S_len,
+    const char* __restrict__ ws) {
+  __shared__ __attribute__((aligned(16))) char lds[StateLds::total];
+  __shared__ int s_seq[1];
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int lr = lane & 15;
+  const int lg = lane >> 4;
+  const bool mover = w == 4;
+
+  // ---- block -> (sequence rank, head, value tile); head % 8 == block % 8 so
+  // both tiles of a head, and the prep blocks of its chunks, share one XCD.
+  const int hx = blockIdx.x & 7;
+  int rest = blockIdx.x >> 3;
+  const int tile = rest % NT;
+  rest /= NT;
+  const int hgroups = Hp >> 3;
+  const int h = (rest % hgroups) * 8 + hx;
+  const int rank = rest / hgroups;
+  if (h >= H) return;
+  const int n = lpt_sequence(cu, N, T_tot, rank, s_seq);
+  int bos = cu[n], eos = cu[n + 1];
+  bos = bos < 0 ? 0 : (bos > T_tot ? T_tot : bos);
+  eos = eos < bos ? bos : (eos > T_tot ? T_tot : eos);
+  const int nch = (eos - bos + C - 1) / C;
+  const int c_end = (c_lo + S_len) < nch ? (c_lo + S_len) : nch;
+  const int HD = H * D;
+  const int col0 = tile * DV;
+  const int jl = 16 * (w & 3) + lr;  // column of the tile owned by this lane (compute waves)
+  const int jcol = col0 + jl;
+  constexpr int QS = QKV_BF16 ? 2 : 4;
+  constexpr int OS = O_BF16 ? 2 : 4;
+  auto rows_of = [&](int c) { return (eos - bos - c * C) < C ? (eos - bos - c * C) : C; };
+  auto img_of = [&](int c) { return lds + StateLds::off_img + ((c - c_lo) & 1) * Ws::bytes; };
+  auto vt_of = [&](int c) { return lds + StateLds::off_v + ((c - c_lo) & 1) * TILE_BYTES; };
+  auto ot_of = [&](int c) { return lds + StateLds::off_o + ((c - c_lo) & 1) * TILE_BYTES; };
+  // buffer over rows [bos + cC, bos + cC + rows) of head h, columns col0.. of the tile
+  auto tok_buf = [&](const void* base, int esz, int c) {
+    const char* b = static_cast<const char*>(base) +
+                    ((int64_t)(bos + c * C) * HD + (int64_t)h * D + col0) * esz;
+    return make_buf(b, (uint32_t)(rows_of(c) * HD * esz - (h * D + col0) * esz));
+  };
+
+  // ---- data wave: image and v tile of chunk c into LDS; o tile of chunk c out
+  auto load_chunk = [&](int c) {
+    const char* src = ws + ((int64_t)(n * S_len + (c - c_lo)) * H + h) * Ws::bytes;
+    const auto rs = make_buf(src, Ws::bytes);
+    char* dst = img_of(c);
+#pragma unroll 4
+    for (int u = 0; u < Ws::bytes / 1024; ++u)
+      buf_to_lds16(rs, (lds_ptr_t)(dst + u * 1024), lane * 16, u * 1024);
+    if constexpr (QKV_BF16) {  // 8 rows of 128 bytes per round; lane writes slot lane&7
+      const auto rv = tok_buf(v, 2, c);
+      char* vt = vt_of(c);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int r = 8 * u + (lane >> 3);
+        const int j = (lane & 7) ^ (((r >> 2) & 3) << 1);  // logical chunk for LDS slot lane&7
+        buf_to_lds16(rv, (lds_ptr_t)(vt + u * 1024), (lane >> 3) * HD * 2 + j * 16,
+                     8 * u * HD * 2);
+      }
+    }
+  };
+  auto store_o = [&](int c) {
+    const auto ro = tok_buf(o, 2, c);
+    const char* ot = ot_of(c);
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int r = 8 * u + (lane >> 3);
+      const int j = (lane & 7) ^ (((r >> 2) & 3) << 1);  // logical chunk held by slot lane&7
+      const u32x4 x = *reinterpret_cast<const u32x4*>(ot + r * 128 + (lane & 7) * 16);
+      __builtin_amdgcn_raw_buffer_store_b128(x, ro, (lane >> 3) * HD * 2 + j * 16,
+                                             8 * u * HD * 2, 0);
+    }
+  };
+
+  // ---- state slice (compute waves): tile t holds key rows 16t + 4lg + i, column jcol.
+  f32x4 Sacc[8];
+  const int64_t sbase = ((int64_t)n * H + h) * D * D;
+  if (!mover) {
+    if (S_in) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          Sacc[t][i] = S_in[sbase + (int64_t)(16 * t + 4 * lg + i) * D + jcol];
+    } else {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) Sacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+  // fp32 v: loaded by the compute waves one chunk ahead
+  uint32_t vraw[16];
+  auto load_v_regs = [&](int c) {
+    const auto rv = tok_buf(v, 4, c);
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        vraw[4 * rt + i] = __builtin_amdgcn_raw_buffer_load_b32(
+            rv, (4 * lg * HD + jl) * 4, (16 * rt + i) * HD * 4, 0);
+  };
+
+  if (c_lo < c_end) {
+    if (mover) load_chunk(c_lo);
+    else if constexpr (!QKV_BF16) load_v_regs(c_lo);
+    wait_vmem();
+  }
+  __syncthreads();
+
+  for (int c = c_lo; c < c_end; ++c) {
+    const bool more = c + 1 < c_end;
+    if (mover) {
+      if constexpr (O_BF16) {
+        if (c > c_lo) store_o(c - 1);
+      }
+      if (more) load_chunk(c + 1);
+      wait_vmem();
+    } else {
+      const char* im = img_of(c);
+      float vcur[16];
+      if constexpr (QKV_BF16) {
+        const char* vt = vt_of(c);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            vcur[4 * rt + i] = bf16_bits_to_f32(
+                *reinterpret_cast<const uint16_t*>(vt + tile_off(16 * rt + 4 * lg + i, jl)));
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) vcur[i] = __uint_as_float(vraw[i]);
+        if (more) load_v_regs(c + 1);
+      }
+
+      // S as B fragments (hi/lo), contraction over key channels
+      f16x8 sbh[4], sbl[4];
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) bfrag_split(Sacc[2 * kk], Sacc[2 * kk + 1], sbh[kk], sbl[kk]);
+      // X = V - Ke S ;  O = Qe S   (8 independent accumulator chains)
+      f32x4 Xacc[4], Oacc[4];
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) Xacc[rt] = Oacc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+          const int po = ke_off(16 * rt + lr, 32 * kk + 8 * lg);
+          const f16x8 ak = *reinterpret_cast<const f16x8*>(im + Ws::KE + po);
+          const f16x8 aq = *reinterpret_cast<const f16x8*>(im + Ws::QE + po);
+          Xacc[rt] = mma_f16(ak, sbh[kk], Xacc[rt]);
+          Oacc[rt] = mma_f16(aq, sbh[kk], Oacc[rt]);
+          Xacc[rt] = mma_f16(ak, sbl[kk], Xacc[rt]);
+          Oacc[rt] = mma_f16(aq, sbl[kk], Oacc[rt]);
+        }
+      }
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Xacc[rt][i] = vcur[4 * rt + i] - Xacc[rt][i];
+      // -- Delta_i = T_ii (b_i X_i - sum_{j<i} A_ij Delta_j), 16-row blocks
+      const float* bet = reinterpret_cast<const float*>(im + Ws::BETA);
+      f32x4 Dacc[4];
+#pragma unroll
+      for (int bi4 = 0; bi4 < 4; ++bi4) {
+        const f32x4 bb = *reinterpret_cast<const f32x4*>(bet + 16 * bi4 + 4 * lg);
+        f32x4 acc = bb * Xacc[bi4];
+#pragma unroll
+        for (int bj4 = 0; bj4 < 3; ++bj4) {
+          if (bj4 >= bi4) continue;
+          const f16x4 na =
+              *reinterpret_cast<const f16x4*>(im + Ws::AT + at_off(16 * bi4 + lr, 16 * bj4 + 4 * lg));
+          f16x4 dh, dl;
+          bfrag16_split(Dacc[bj4], dh, dl);
+          acc = mma_f16_k16(na, dh, acc);
+          acc = mma_f16_k16(na, dl, acc);
+        }
+        const f16x4 ti =
+            *reinterpret_cast<const f16x4*>(im + Ws::AT + at_off(16 * bi4 + lr, 16 * bi4 + 4 * lg));
+        f16x4 xh, xl;
+        bfrag16_split(acc, xh, xl);
+        f32x4 d = mma_f16_k16(ti, xh, f32x4{0.f, 0.f, 0.f, 0.f});
+        Dacc[bi4] = mma_f16_k16(ti, xl, d);
+      }
+      f16x8 dbh[2], dbl[2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) bfrag_split(Dacc[2 * ks], Dacc[2 * ks + 1], dbh[ks], dbl[ks]);
+      // -- O += P Delta ; bf16: into the LDS o tile (the data wave stores it);
+      // fp32: straight to o (rows past the chunk end are dropped)
+      const auto ro = tok_buf(o, OS, c);
+      char* ot = ot_of(c);
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        f32x4 ao = Oacc[rt];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          if (ks > (rt >> 1)) continue;
+          const f16x8 pm =
+              *reinterpret_cast<const f16x8*>(im + Ws::PM + pm_off(16 * rt + lr, 32 * ks + 8 * lg));
+          ao = mma_f16(pm, dbh[ks], ao);
+          ao = mma_f16(pm, dbl[ks], ao);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = 16 * rt + 4 * lg + i;
+          const float val = scale * ao[i];
+          if constexpr (O_BF16)
+            *reinterpret_cast<__bf16*>(ot + tile_off(row, jl)) = static_cast<__bf16>(val);
+          else
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), ro, (4 * lg * HD + jl) * 4,
+                                                  (16 * rt + i) * HD * 4, 0);
+        }
+      }
+      // -- S <- e^gamma_C S + Khat^T Delta
+      const float* ec = reinterpret_cast<const float*>(im + Ws::EC);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const f32x4 dec = *reinterpret_cast<const f32x4*>(ec + 16 * t + 4 * lg);
+        f32x4 s = Sacc[t] * dec;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const f16x8 a =
+              *reinterpret_cast<const f16x8*>(im + Ws::KDT + kdt_off(16 * t + lr, 32 * ks + 8 * lg));
+          s = mma_f16(a, dbh[ks], s);
+          s = mma_f16(a, dbl[ks], s);
+        }
+        Sacc[t] = s;
+      }
+      if constexpr (!QKV_BF16 || !O_BF16) wait_vmem();
+    }
+    __syncthreads();
+  }
+
+  if (mover) {
+    if constexpr (O_BF16) {
+      if (c_lo < c_end) store_o(c_end - 1);
+    }
+  } else if (S_out) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        S_out[sbase + (int64_t)(16 * t + 4 * lg + i) * D + jcol] = Sacc[t][i];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_state(const void* v, bool qkv_bf16, const int32_t* cu, int N, int T_tot,
+                        int H, const float* S_in, float* S_out, void* o, bool o_bf16,
+                        float scale, int c_lo, int S_len, const char* ws, hipStream_t s) {
+  const int Hp = (H + 7) & ~7;
+  const int64_t blocks = (int64_t)N * Hp * NT;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  dim3 grid(static_cast<unsigned>(blocks));
+#define KDA_LAUNCH(QB, OB)                                                                      \
+  state_kernel<QB, OB><<<grid, NTHR_S, 0, s>>>(v, cu, N, T_tot, H, Hp, S_in, S_out, o, scale, \
+                                               c_lo, S_len, ws)
+  if (qkv_bf16 && o_bf16) KDA_LAUNCH(true, true);
+  else if (qkv_bf16) KDA_LAUNCH(true, false);
+  else if (o_bf16) KDA_LAUNCH(false, true);
+  else KDA_LAUNCH(false, false);
+#undef KDA_LAUNCH
+  return hipGetLastError();
+}
+
+}  // namespace chunk
+}  // namespace kda

@@ -49,6 +49,7 @@ typedef enum {
   KDA_ERR_DTYPE = 3,       /* dtype code not supported for this argument   */
   KDA_ERR_UNSUPPORTED = 4, /* valid but not implemented (e.g. d != 128)    */
   KDA_ERR_ALIGNMENT = 5,   /* pointer not 16-byte aligned                  */
+  KDA_ERR_WORKSPACE = 6,   /* workspace missing or too small               */
   KDA_ERR_LAUNCH = 7       /* the HIP launch failed (see kda_last_error)   */
 } kda_status;
 
@@ -107,24 +108,47 @@ kda_status kda_gate(const void* x, kda_dtype x_dt, const void* b, kda_dtype b_dt
  *   cu_seqlens  [N+1] int32, device copy (read by the kernels)
  *   cu_seqlens_host [N+1] int32, host copy or NULL.  When given it is
  *               validated (cu[0]=0, non-decreasing, cu[N]=T_tot) and must
- *               equal the device copy.  The kernels clamp every sequence
- *               range into [0, T_tot], so no value can make them read or
- *               write out of bounds.
+ *               equal the device copy; it also sizes the work to the longest
+ *               sequence.  Without it every sequence is assumed to be up to
+ *               T_tot long.  The kernels clamp every sequence range into
+ *               [0, T_tot], so no value can make them read or write out of
+ *               bounds.
  *   initial_state [N, H, dk, dv] fp32 or NULL; final_state [N, H, dk, dv]
  *               fp32 or NULL; they may be the same buffer (in-place update).
  *   o           [T_tot, H, dv]   dtype o_dt (KDA_BF16 or KDA_F32)
+ *   workspace   device scratch of workspace_bytes bytes, 256-byte aligned,
+ *               owned by the caller, not read before it is written; it must
+ *               not overlap any other argument and must not be used by
+ *               anything else until the stream has finished this call.
+ *               kda_chunk_prefill_workspace_bytes(N, H, dk, dv, 1) is the
+ *               minimum (KDA_ERR_WORKSPACE below it).  The chunks of all
+ *               sequences are processed in passes of as many chunks per
+ *               sequence as the workspace holds (two launches per pass), so
+ *               a workspace for the longest sequence's chunk count runs the
+ *               whole batch in one pass.
  * Requires dk == dv == 128 (else KDA_ERR_UNSUPPORTED), N >= 1, H >= 1,
  * 16-byte aligned tensors.  Matrix products run as fp16 MFMA tiles with fp32
- * accumulation (bf16 inputs convert to fp16 exactly); the state and the
- * intermediate products are carried as hi+lo fp16 pairs, so results match a
- * full-precision recurrence to about 1e-4 of the state norm.
+ * accumulation (bf16 inputs convert to fp16 exactly); the state, X and Delta
+ * enter the products as hi+lo fp16 pairs.  Against an fp64 recurrence the
+ * final state agrees to a few 1e-4 of its Frobenius norm and o to a few 1e-3
+ * of its RMS (before any bf16 rounding of o).
  */
 kda_status kda_chunk_prefill(const void* q, const void* k, const void* v, kda_dtype qkv_dt,
                              const float* g, const float* beta, const int32_t* cu_seqlens,
                              const int32_t* cu_seqlens_host, int32_t N,
                              const float* initial_state, float* final_state, void* o,
                              kda_dtype o_dt, int64_t T_tot, int32_t H, int32_t dk,
-                             int32_t dv, float scale, void* stream);
+                             int32_t dv, float scale, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/*
+ * kda_chunk_prefill_workspace_bytes - workspace size for kda_chunk_prefill
+ * processing up to chunks_per_pass chunks (of 64 tokens) of every sequence per
+ * pass: a state carry of N*H*dk*dv*4 bytes plus N*H*chunks_per_pass images
+ * of 61,440 bytes.  Returns 0 for unsupported or non-positive arguments.
+ */
+size_t kda_chunk_prefill_workspace_bytes(int32_t N, int32_t H, int32_t dk, int32_t dv,
+                                         int32_t chunks_per_pass);
 
 /*
  * kda_recurrent_decode - one token per sequence, state updated in place.

@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol():
     L = _lib()
     names = _declared()
     assert set(names) == {"kda_last_error", "kda_version", "kda_gate", "kda_chunk_prefill",
-                          "kda_recurrent_decode"}
+                          "kda_chunk_prefill_workspace_bytes", "kda_recurrent_decode"}
     for n in names:
         assert hasattr(L, n), n
     assert L.kda_version().decode().startswith("kda-gfx950")
@@ -64,13 +64,14 @@ def test_gate_refuses_checkpoint_shaped_A_log():
 
 def _prefill(L, cu_host, **kw):
     a = dict(q=DEV[0], k=DEV[1], v=DEV[2], qkv_dt=1, g=DEV[3], beta=DEV[4], cu=DEV[5], N=2,
-             S0=None, Sf=DEV[6], o=DEV[7], o_dt=1, T=48, H=4, dk=128, dv=128, scale=1.0)
+             S0=None, Sf=DEV[6], o=DEV[7], o_dt=1, T=48, H=4, dk=128, dv=128, scale=1.0,
+             ws=DEV[8], ws_bytes=1 << 30)
     a.update(kw)
     hp = None if cu_host is None else np.ascontiguousarray(np.asarray(cu_host, dtype=np.int32))
     return L.kda_chunk_prefill(a["q"], a["k"], a["v"], a["qkv_dt"], a["g"], a["beta"], a["cu"],
                                None if hp is None else hp.ctypes.data, a["N"], a["S0"], a["Sf"],
                                a["o"], a["o_dt"], a["T"], a["H"], a["dk"], a["dv"], a["scale"],
-                               None)
+                               a["ws"], a["ws_bytes"], None)
 
 
 def test_prefill_refusals():
@@ -87,6 +88,22 @@ def test_prefill_refusals():
     assert _prefill(L, [0, 20, 48], scale=float("nan")) == 1
     assert _prefill(L, [0, 20, 48], o=DEV[7] + 2) == 5
     assert b"kda_chunk_prefill" in L.kda_last_error()
+
+
+def test_prefill_workspace_contract():
+    """Workspace size formula: state carry + one 61,440-byte image per
+    (sequence, head, chunk of a pass); a missing, short or misaligned
+    workspace is refused before launch."""
+    L = _lib()
+    f = L.kda_chunk_prefill_workspace_bytes
+    assert f(2, 4, 128, 128, 1) == 2 * 4 * (128 * 128 * 4 + 61440)
+    assert f(1, 96, 128, 128, 64) == 96 * 128 * 128 * 4 + 96 * 64 * 61440
+    assert f(1, 96, 64, 128, 1) == 0 and f(0, 96, 128, 128, 1) == 0 and f(1, 96, 128, 128, 0) == 0
+    need = f(2, 4, 128, 128, 1)
+    assert _prefill(L, [0, 20, 48], ws=None) == 6
+    assert _prefill(L, [0, 20, 48], ws_bytes=need - 1) == 6
+    assert b"workspace" in L.kda_last_error()
+    assert _prefill(L, [0, 20, 48], ws=DEV[8] + 16, ws_bytes=need) == 5
 
 
 def test_decode_refusals():

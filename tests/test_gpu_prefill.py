@@ -196,3 +196,36 @@ def test_strong_decay_heads():
     assert torch.isfinite(o).all() and torch.isfinite(S).all()
     assert_out(o, o_ref, "strong decay")
     assert_state(S, S_ref, "strong decay")
+
+
+def test_multi_pass_workspace():
+    """A workspace smaller than the longest sequence's chunk count runs the
+    chunk axis in passes (state carried through final_state, or through the
+    workspace when no final state is requested): results are bit-identical to
+    one pass."""
+    need_gpu()
+    dr = draw_prefill([200, 0, 64, 1, 77], H=3, dtype=torch.bfloat16, init_state=True, seed=51)
+    g, beta = oracle_gate_f32(dr)
+    say("multi-pass workspace")
+    q, k, v, gg, bb = (t.to(DEV) for t in (dr.q, dr.k, dr.v, g, beta))
+    cu_h = dr.cu_seqlens
+    cu = cu_h.to(DEV)
+    S0 = dr.initial_state.to(DEV)
+    o1, S1 = kda.chunk_prefill(q, k, v, gg, bb, cu, S0, cu_seqlens_host=cu_h, o_dtype=torch.float32)
+    for cpp in (1, 3):
+        nb = kda.chunk_prefill_workspace_bytes(5, 3, 128, 128, cpp)
+        ws = torch.empty(nb, dtype=torch.uint8, device=DEV)
+        o2, S2 = kda.chunk_prefill(q, k, v, gg, bb, cu, S0, cu_seqlens_host=cu_h,
+                                   o_dtype=torch.float32, workspace=ws)
+        o3, S3 = kda.chunk_prefill(q, k, v, gg, bb, cu, S0, cu_seqlens_host=cu_h,
+                                   o_dtype=torch.float32, workspace=ws, output_final_state=False)
+        st = S0.clone()
+        o4, _ = kda.chunk_prefill(q, k, v, gg, bb, cu, st, cu_seqlens_host=cu_h,
+                                  o_dtype=torch.float32, workspace=ws, final_state=st)
+        torch.cuda.synchronize()
+        assert S3 is None
+        assert torch.equal(o1, o2) and torch.equal(S1, S2), cpp
+        assert torch.equal(o1, o3) and torch.equal(o1, o4) and torch.equal(S1, st), cpp
+    o_ref, S_ref = oracle.prefill(dr.q, dr.k, dr.v, g, beta, cu_h, dr.initial_state)
+    assert_out(o1, o_ref, "multi-pass")
+    assert_state(S1, S_ref, "multi-pass")
