@@ -80,6 +80,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=96,
                     help="heads of the workload the CPU oracle runs (sample)")
+    ap.add_argument("--ws-chunks", type=int, default=T // C,
+                    help="chunks per pass the prefill workspace holds (T/64 = one pass)")
     ap.add_argument("--only", choices=["all", "prefill", "decode", "copy"], default="all",
                     help="profiling aid: run one part only (prints a diagnostic line, "
                          "not the bench line)")
@@ -118,8 +120,8 @@ def bench_prefill(args, torch, kda, synth):
     def gate():
         kda.gate(dr.x, dr.b, dr.A_log, dr.dt_bias, g_out=g, beta_out=beta)
 
-    ws = torch.empty(kda.chunk_prefill_workspace_bytes(1, H, D, D, T // C), dtype=torch.uint8,
-                     device=dev)
+    ws = torch.empty(kda.chunk_prefill_workspace_bytes(1, H, D, D, args.ws_chunks),
+                     dtype=torch.uint8, device=dev)
 
     def prefill():
         kda.chunk_prefill(dr.q, dr.k, dr.v, g, beta, cu_d, None, out=o, final_state=Sf,

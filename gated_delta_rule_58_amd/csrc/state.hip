@@ -16,15 +16,19 @@
 // image (pperm), so an accumulator tile pair is directly the next product's B
 // fragment.
 //
+// The output is computed transposed, O^T = S^T (Q e^gamma)^T + Delta^T P^T:
+// the same fragments with the operands swapped, so each lane ends up with four
+// consecutive columns of one token row.
+//
 // Wave 4 moves data.  While chunk c is computed it stores chunk c-1's output
 // tile from LDS to o and copies chunk c+1's image (60 KiB) and v tile into
 // the other LDS buffers with 16-byte buffer-to-LDS loads, so the compute
-// waves never wait on a memory instruction.  One workgroup barrier per chunk.
-// (fp32 v or o, used only off the benchmarked path, go through the compute
-// waves' registers instead.)
+// waves never wait on a memory instruction.  One workgroup barrier per chunk.  (fp32 v or o, used only
+// off the benchmarked path, go through the compute waves' registers instead.)
 //
-// Precision: operands are fp16 MFMA fragments with fp32 accumulation; S, X
-// and Delta enter the products as hi+lo fp16 pairs.
+// Precision: operands are fp16 MFMA fragments with fp32 accumulation; X and
+// Delta enter the products as hi+lo fp16 pairs, the state as one fp16 value
+// (its rounding is not carried: S itself stays fp32 in the accumulators).
 #include "chunk_common.hpp"
 #include "kda_internal.hpp"
 
@@ -45,12 +49,19 @@ struct StateLds {
 };
 static_assert(StateLds::total <= 160 * 1024, "LDS budget");
 
-// byte offset of (row r, column j < 64) in a bf16 v / o tile: 128-byte rows,
+// byte offset of (row r, column j < 64) in the bf16 v tile: 128-byte rows,
 // 16-byte chunk j>>3 swizzled so the four row groups 4lg+i of an accumulator
-// tile hit disjoint banks.
-__device__ __forceinline__ int tile_off(int r, int j) {
+// tile (read one element per lane) hit disjoint banks.
+__device__ __forceinline__ int vtile_off(int r, int j) {
   return r * 128 + ((((j >> 3) ^ (((r >> 2) & 3) << 1))) << 4) + ((j & 7) << 1);
 }
+__device__ __forceinline__ int vtile_swz(int r) { return ((r >> 2) & 3) << 1; }
+// byte offset of (row r, column j < 64) in the bf16 o tile, written 4 columns
+// of one row per lane with the 16 rows of a tile on distinct 16-byte slots.
+__device__ __forceinline__ int otile_off(int r, int j) {
+  return r * 128 + ((((j >> 3) ^ (r & 7))) << 4) + ((j & 7) << 1);
+}
+__device__ __forceinline__ int otile_swz(int r) { return r & 7; }
 
 template <bool QKV_BF16, bool O_BF16>
 __global__ void __launch_bounds__(NTHR_S, 1) state_kernel(
@@ -114,7 +125,7 @@ __global__ void __launch_bounds__(NTHR_S, 1) state_kernel(
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int r = 8 * u + (lane >> 3);
-        const int j = (lane & 7) ^ (((r >> 2) & 3) << 1);  // logical chunk for LDS slot lane&7
+        const int j = (lane & 7) ^ vtile_swz(r);  // logical chunk for LDS slot lane&7
         buf_to_lds16(rv, (lds_ptr_t)(vt + u * 1024), (lane >> 3) * HD * 2 + j * 16,
                      8 * u * HD * 2);
       }
@@ -127,7 +138,7 @@ __global__ void __launch_bounds__(NTHR_S, 1) state_kernel(
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int r = 8 * u + (lane >> 3);
-      const int j = (lane & 7) ^ (((r >> 2) & 3) << 1);  // logical chunk held by slot lane&7
+      const int j = (lane & 7) ^ otile_swz(r);  // logical chunk held by slot lane&7
       const u32x4 x = *reinterpret_cast<const u32x4*>(ot + r * 128 + (lane & 7) * 16);
       __builtin_amdgcn_raw_buffer_store_b128(x, ro, (lane >> 3) * HD * 2 + j * 16,
                                              8 * u * HD * 2, 0);
@@ -186,18 +197,23 @@ __global__ void __launch_bounds__(NTHR_S, 1) state_kernel(
 #pragma unroll
           for (int i = 0; i < 4; ++i)
             vcur[4 * rt + i] = bf16_bits_to_f32(
-                *reinterpret_cast<const uint16_t*>(vt + tile_off(16 * rt + 4 * lg + i, jl)));
+                *reinterpret_cast<const uint16_t*>(vt + vtile_off(16 * rt + 4 * lg + i, jl)));
       } else {
 #pragma unroll
         for (int i = 0; i < 16; ++i) vcur[i] = __uint_as_float(vraw[i]);
         if (more) load_v_regs(c + 1);
       }
 
-      // S as B fragments (hi/lo), contraction over key channels
-      f16x8 sbh[4], sbl[4];
+      // S as one fp16 fragment per k-step: it serves as the B operand of X
+      // (channels x value columns) and, unchanged, as the A operand of O^T
+      // (value columns x channels).
+      f16x8 sb[4];
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) bfrag_split(Sacc[2 * kk], Sacc[2 * kk + 1], sbh[kk], sbl[kk]);
-      // X = V - Ke S ;  O = Qe S   (8 independent accumulator chains)
+      for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          sb[kk][e] = static_cast<_Float16>(e < 4 ? Sacc[2 * kk][e] : Sacc[2 * kk + 1][e - 4]);
+      // X = V - Ke S (rows = tokens) ;  O^T = S^T Qe^T (rows = value columns)
       f32x4 Xacc[4], Oacc[4];
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) Xacc[rt] = Oacc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -208,10 +224,8 @@ __global__ void __launch_bounds__(NTHR_S, 1) state_kernel(
           const int po = ke_off(16 * rt + lr, 32 * kk + 8 * lg);
           const f16x8 ak = *reinterpret_cast<const f16x8*>(im + Ws::KE + po);
           const f16x8 aq = *reinterpret_cast<const f16x8*>(im + Ws::QE + po);
-          Xacc[rt] = mma_f16(ak, sbh[kk], Xacc[rt]);
-          Oacc[rt] = mma_f16(aq, sbh[kk], Oacc[rt]);
-          Xacc[rt] = mma_f16(ak, sbl[kk], Xacc[rt]);
-          Oacc[rt] = mma_f16(aq, sbl[kk], Oacc[rt]);
+          Xacc[rt] = mma_f16(ak, sb[kk], Xacc[rt]);
+          Oacc[rt] = mma_f16(sb[kk], aq, Oacc[rt]);
         }
       }
 #pragma unroll
@@ -245,8 +259,10 @@ __global__ void __launch_bounds__(NTHR_S, 1) state_kernel(
       f16x8 dbh[2], dbl[2];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) bfrag_split(Dacc[2 * ks], Dacc[2 * ks + 1], dbh[ks], dbl[ks]);
-      // -- O += P Delta ; bf16: into the LDS o tile (the data wave stores it);
-      // fp32: straight to o (rows past the chunk end are dropped)
+      // -- O^T += Delta^T P^T: lane (lr, lg) of tile rt then holds token row
+      // 16rt + lr, value columns 16w + 4lg .. +3.  bf16: into the LDS o tile
+      // (the data wave stores it); fp32: straight to o (rows past the chunk end
+      // are dropped).
       const auto ro = tok_buf(o, OS, c);
       char* ot = ot_of(c);
 #pragma unroll
@@ -257,18 +273,21 @@ __global__ void __launch_bounds__(NTHR_S, 1) state_kernel(
           if (ks > (rt >> 1)) continue;
           const f16x8 pm =
               *reinterpret_cast<const f16x8*>(im + Ws::PM + pm_off(16 * rt + lr, 32 * ks + 8 * lg));
-          ao = mma_f16(pm, dbh[ks], ao);
-          ao = mma_f16(pm, dbl[ks], ao);
+          ao = mma_f16(dbh[ks], pm, ao);
+          ao = mma_f16(dbl[ks], pm, ao);
         }
+        ao = ao * scale;
+        const int row = 16 * rt + lr;
+        const int j0 = 16 * w + 4 * lg;
+        if constexpr (O_BF16) {
+          bf16x4 ob;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = 16 * rt + 4 * lg + i;
-          const float val = scale * ao[i];
-          if constexpr (O_BF16)
-            *reinterpret_cast<__bf16*>(ot + tile_off(row, jl)) = static_cast<__bf16>(val);
-          else
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), ro, (4 * lg * HD + jl) * 4,
-                                                  (16 * rt + i) * HD * 4, 0);
+          for (int i = 0; i < 4; ++i) ob[i] = static_cast<__bf16>(ao[i]);
+          *reinterpret_cast<bf16x4*>(ot + otile_off(row, j0)) = ob;
+        } else {
+          typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, ao), ro, j0 * 4,
+                                                 row * HD * 4, 0);
         }
       }
       // -- S <- e^gamma_C S + Khat^T Delta
