@@ -7,13 +7,16 @@
 // inverses T_ii with the off-diagonal blocks -A_ij of the triangular system
 // (I + A) Delta = diag(beta) X, e^gamma_C and beta.
 //
-// Phases:
-//  P0  gamma = cumsum(g) per channel (lanes 2c, 2c+1 own channel c, rows
-//      0..31 and 32..63), the per-(block, channel) decay constants, and the
-//      transposed K e^(gamma_C - gamma) straight from that layout.
-//  P1  wave i owns chunk rows 16i..16i+15 (block i): decay factors, the
-//      row-major operands (written to the image), the diagonal tiles A_ii and
-//      P_ii, and T_ii = (I + A_ii)^-1 by repeated squaring.
+// Wave i owns chunk rows 16i..16i+15 (block i); lane (lr, lg) owns row
+// 16i + lr and, in k-step kk, the 8 consecutive channels 32kk + 8lg + e.
+// g, k and q are loaded straight into registers in that layout.
+//  S1  gamma = cumsum(g) down the rows: a 16-lane DPP scan inside each block,
+//      block sums exchanged through LDS.
+//  S2  per-(block, channel) decay constants from the block sums.
+//  P1  decay factors, K e^gamma and Q e^gamma (to the image), the decayed
+//      K^T (transposed by an MFMA against a 0/1 selector, to the image), the
+//      off-diagonal factors (LDS), the diagonal tiles A_ii and P_ii, and
+//      T_ii = (I + A_ii)^-1 by repeated squaring.
 //  P2  off-diagonal tiles (i, j < i) of A and P, two per wave at most.
 //
 // Decay factors.  gamma is kept in log2 units and every exponential is a
@@ -38,22 +41,19 @@ namespace {
 
 struct PrepLds {
   static constexpr int SC_LD = 17;  // fp32 [4][16][17] per-wave transpose scratch
-  static constexpr int off_gam = 0;                       // fp32 [64][128], gidx swizzle
-  static constexpr int off_R = off_gam + C * D * 4;       // fp16 [48][128], ke_off layout
+  static constexpr int off_R = 0;                         // fp16 [48][128], ke_off layout
   static constexpr int off_L3 = off_R + 48 * D * 2;       // fp16 [32][128], ke_off layout
   static constexpr int off_PM = off_L3 + 32 * D * 2;      // image of Ws::PM
   static constexpr int off_AT = off_PM + Ws::PM_BYTES;    // image of Ws::AT (follows PM)
   static constexpr int off_scr = off_AT + Ws::AT_BYTES;
-  static constexpr int off_cst = off_scr + 4 * 16 * SC_LD * 4;
-  static constexpr int off_beta = off_cst + 14 * D * 4;
+  static constexpr int off_btot = off_scr + 4 * 16 * SC_LD * 4;  // fp32 [4][128] block sums
+  static constexpr int off_bmid = off_btot + 4 * D * 4;   // fp32 [4][128] block sums to row 7
+  static constexpr int off_gm = off_bmid + 4 * D * 4;     // fp32 [4][128] gamma at mid rows
+  static constexpr int off_cst = off_gm + 4 * D * 4;      // fp32 [18][128]
+  static constexpr int off_beta = off_cst + 18 * D * 4;
   static constexpr int total = off_beta + C * 4;
 };
-static_assert(PrepLds::total <= 80 * 1024, "two prep workgroups per CU");
-
-// float index of element (row, c) of the swizzled gamma buffer
-__device__ __forceinline__ int gidx(int row, int c) {
-  return row * 128 + ((((c >> 2) ^ (row & 15))) << 2) + (c & 3);
-}
+static_assert(PrepLds::total <= 53 * 1024, "three prep workgroups per CU");
 
 // Per-channel constant slots (after exp2, all <= 1):
 //  0..3   em_i = 2^gamma_{m_i}
@@ -61,44 +61,46 @@ __device__ __forceinline__ int gidx(int row, int c) {
 //         (1,0),(2,1),(3,2) at 4,5,6; (2,0) 7; (3,1) 8; (3,0) 9
 //  10..12 eR_j = 2^(gamma_{b_{j+1}} - gamma_{m_j}), j = 0..2
 //  13     eC = 2^gamma_C
+//  14..17 eL_i = 2^(gamma_C - gamma_{m_i})
 __device__ __forceinline__ int cij_slot(int i, int j) {
   return (j == i - 1) ? 3 + i : (i == 2 ? 7 : (j == 1 ? 8 : 9));
 }
 
-template <bool BF16>
-struct QKRaw;  // raw q or k values of one lane: 4 k-steps x 2 halves x 4
-template <>
-struct QKRaw<true> {
-  u16x4 v[4][2];
-};
-template <>
-struct QKRaw<false> {
-  f32x4 v[4][2];
-};
-
-template <bool BF16>
-__device__ __forceinline__ void load_qk(QKRaw<BF16>& R, __amdgpu_buffer_rsrc_t rs, int off0) {
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-    for (int a = 0; a < 2; ++a) {
-      const int c = 32 * kk + 16 * a;  // plus 4lg, folded into off0
-      if constexpr (BF16) {
-        typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-        const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(rs, off0 + 2 * c, 0, 0);
-        R.v[kk][a] = __builtin_bit_cast(u16x4, x);
-      } else {
-        typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-        const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rs, off0 + 4 * c, 0, 0);
-        R.v[kk][a] = __builtin_bit_cast(f32x4, x);
-      }
-    }
+// v + (v of the lane K rows up, inside each 16-lane row; 0 above the row)
+template <int K>
+__device__ __forceinline__ float add_row_shr(float v) {
+  const int s = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x110 + K, 0xf, 0xf,
+                                            true);
+  return v + __builtin_bit_cast(float, s);
 }
 
 template <bool BF16>
-__device__ __forceinline__ float qk_at(const QKRaw<BF16>& R, int kk, int a, int e) {
-  if constexpr (BF16) return bf16_bits_to_f32(R.v[kk][a][e]);
-  else return R.v[kk][a][e];
+struct Row8;  // 8 consecutive channels per k-step, 4 k-steps
+template <>
+struct Row8<true> {
+  u16x8 v[4];
+  __device__ __forceinline__ float at(int kk, int e) const { return bf16_bits_to_f32(v[kk][e]); }
+};
+template <>
+struct Row8<false> {
+  f32x4 v[4][2];
+  __device__ __forceinline__ float at(int kk, int e) const { return v[kk][e >> 2][e & 3]; }
+};
+
+template <bool BF16>
+__device__ __forceinline__ void load_row8(Row8<BF16>& R, __amdgpu_buffer_rsrc_t rs, int off0) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    if constexpr (BF16) {
+      R.v[kk] = __builtin_bit_cast(u16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, off0 + 64 * kk, 0, 0));
+    } else {
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+        R.v[kk][a] = __builtin_bit_cast(
+            f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off0 + 128 * kk + 16 * a, 0, 0));
+    }
+  }
 }
 
 template <bool QKV_BF16>
@@ -107,11 +109,13 @@ __global__ void __launch_bounds__(NTHR, 2) prep_kernel(
     const float* __restrict__ beta, const int32_t* __restrict__ cu, int T_tot, int H, int Hp,
     int c_lo, int S_len, char* __restrict__ ws) {
   __shared__ __attribute__((aligned(16))) char lds[PrepLds::total];
-  float* gam = reinterpret_cast<float*>(lds + PrepLds::off_gam);
   char* Rb = lds + PrepLds::off_R;
   char* L3 = lds + PrepLds::off_L3;
   char* ATi = lds + PrepLds::off_AT;
   char* PMi = lds + PrepLds::off_PM;
+  float* btot = reinterpret_cast<float*>(lds + PrepLds::off_btot);
+  float* bmid = reinterpret_cast<float*>(lds + PrepLds::off_bmid);
+  float* gmv = reinterpret_cast<float*>(lds + PrepLds::off_gm);
   float* cst = reinterpret_cast<float*>(lds + PrepLds::off_cst);
   float* s_beta = reinterpret_cast<float*>(lds + PrepLds::off_beta);
 
@@ -141,6 +145,8 @@ __global__ void __launch_bounds__(NTHR, 2) prep_kernel(
   float* scr = reinterpret_cast<float*>(lds + PrepLds::off_scr) + w * 16 * PrepLds::SC_LD;
   const int HD = H * D;
   constexpr int QS = QKV_BF16 ? 2 : 4;
+  const int bi = w;
+  const int r = 16 * w + lr;  // chunk row of this lane
 
   // chunk buffers: rows [t0, t0 + Lc) of head h; loads past Lc return 0
   auto buf_tok = [&](const void* base, int esz) {
@@ -148,64 +154,63 @@ __global__ void __launch_bounds__(NTHR, 2) prep_kernel(
     return make_buf(b, (uint32_t)(Lc * HD * esz - h * D * esz));
   };
 
-  // ---- loads: g straight to LDS (16-byte rows chunks, swizzled), k and q in
-  // row layout (P1), k in column layout (P0), beta.
-  const int gc = tid >> 1, ghf = tid & 1;  // P0: channel, half
-  const int rA = 16 * w + lr;              // P1: chunk row of this lane
+  // ---- loads: row r, channels 32kk + 8lg .. +7
+  f32x4 graw[4][2];
   {
     const auto rg = buf_tok(g, 4);
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {  // rows 16w + 2j + (lane >> 5): lane writes chunk lane & 31
-      const int row0 = 16 * w + 2 * j;
-      const int hi = lane >> 5;
-      const int lchunk = (lane & 31) ^ ((2 * j + hi) & 15);
-      buf_to_lds16(rg, (lds_ptr_t)(gam + row0 * D), hi * HD * 4 + lchunk * 16, row0 * HD * 4);
-    }
-  }
-  QKRaw<QKV_BF16> kpf, qpf;
-  const auto rk = buf_tok(k, QS);
-  load_qk<QKV_BF16>(kpf, rk, rA * HD * QS + 4 * lg * QS);
-  load_qk<QKV_BF16>(qpf, buf_tok(q, QS), rA * HD * QS + 4 * lg * QS);
-  uint32_t kcol[32];  // k[32 ghf + i][gc]
+    for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    if constexpr (QKV_BF16)
-      kcol[i] = __builtin_amdgcn_raw_buffer_load_b16(rk, (32 * ghf * HD + gc) * QS, i * HD * QS, 0);
-    else
-      kcol[i] = __builtin_amdgcn_raw_buffer_load_b32(rk, (32 * ghf * HD + gc) * QS, i * HD * QS, 0);
+      for (int a = 0; a < 2; ++a)
+        graw[kk][a] = __builtin_bit_cast(
+            f32x4, __builtin_amdgcn_raw_buffer_load_b128(rg, r * HD * 4 + (32 * kk + 8 * lg + 4 * a) * 4, 0, 0));
   }
-  float bval = 0.0f;
-  if (tid < C) {
+  Row8<QKV_BF16> kv8, qv8;
+  load_row8<QKV_BF16>(kv8, buf_tok(k, QS), (r * HD + 8 * lg) * QS);
+  load_row8<QKV_BF16>(qv8, buf_tok(q, QS), (r * HD + 8 * lg) * QS);
+  float bval;
+  {
     const char* bb = reinterpret_cast<const char*>(beta) + ((int64_t)t0 * H + h) * 4;
-    bval = buf_f32(make_buf(bb, (uint32_t)(Lc * H * 4 - h * 4)), tid * H * 4);
+    bval = buf_f32(make_buf(bb, (uint32_t)(Lc * H * 4 - h * 4)), r * H * 4);
   }
-  wait_vmem();
+
+  // ================= S1: gamma (log2 units), in-block scan down the 16 rows
+  float gam[4][8];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float x = graw[kk][e >> 2][e & 3] * LOG2E;
+      x = add_row_shr<1>(x);
+      x = add_row_shr<2>(x);
+      x = add_row_shr<4>(x);
+      x = add_row_shr<8>(x);
+      gam[kk][e] = x;
+    }
+  if (lr == 15 || lr == 7) {
+    float* dst = (lr == 15 ? btot : bmid) + w * D;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+        *reinterpret_cast<f32x4*>(dst + 32 * kk + 8 * lg + 4 * a) =
+            f32x4{gam[kk][4 * a], gam[kk][4 * a + 1], gam[kk][4 * a + 2], gam[kk][4 * a + 3]};
+  }
+  if (lg == 0) s_beta[r] = bval;
   __syncthreads();
 
-  // ================= P0: gamma (cumsum of g, log2 units), decay constants,
-  // (K e^(gamma_C - gamma))^T.
+  // ================= S2: gamma at the block ends and mid rows, decay constants;
+  // every lane adds the sums of the blocks above its own.
   {
-    float gv[32];
-#pragma unroll
-    for (int i = 0; i < 32; ++i) gv[i] = gam[gidx(32 * ghf + i, gc)] * LOG2E;
-#pragma unroll
-    for (int i = 1; i < 32; ++i) gv[i] += gv[i - 1];
-    const float tot0 = __shfl_xor(gv[31], 1);
-    if (ghf) {
-#pragma unroll
-      for (int i = 0; i < 32; ++i) gv[i] += tot0;
-    }
-#pragma unroll
-    for (int i = 0; i < 32; ++i) gam[gidx(32 * ghf + i, gc)] = gv[i];
-    // key rows: block mids 7,23,39,55 and block ends 15,31,47,63
-    const float o7 = __shfl_xor(gv[7], 1), o15 = __shfl_xor(gv[15], 1);
-    const float o23 = __shfl_xor(gv[23], 1), o31 = __shfl_xor(gv[31], 1);
-    const float gm0 = ghf ? o7 : gv[7], gm1 = ghf ? o23 : gv[23];
-    const float gm2 = ghf ? gv[7] : o7, gm3 = ghf ? gv[23] : o23;
-    const float gb1 = ghf ? o15 : gv[15], gb2 = ghf ? o31 : gv[31];
-    const float gb3 = ghf ? gv[15] : o15, gl = ghf ? gv[31] : o31;
-    const int c = gc;
-    if (ghf == 0) {
+    const int c = tid & 127, half = tid >> 7;
+    const float t0v = btot[c], t1v = btot[D + c], t2v = btot[2 * D + c], t3v = btot[3 * D + c];
+    const float gb1 = t0v, gb2 = gb1 + t1v, gb3 = gb2 + t2v, gl = gb3 + t3v;
+    const float gm0 = bmid[c], gm1 = gb1 + bmid[D + c], gm2 = gb2 + bmid[2 * D + c],
+                gm3 = gb3 + bmid[3 * D + c];
+    if (half == 0) {
+      gmv[c] = gm0;
+      gmv[D + c] = gm1;
       cst[0 * D + c] = ex2(gm0);
       cst[1 * D + c] = ex2(gm1);
       cst[2 * D + c] = ex2(gm2);
@@ -213,7 +218,11 @@ __global__ void __launch_bounds__(NTHR, 2) prep_kernel(
       cst[4 * D + c] = ex2(gm1 - gb1);
       cst[5 * D + c] = ex2(gm2 - gb2);
       cst[6 * D + c] = ex2(gm3 - gb3);
+      cst[14 * D + c] = ex2(gl - gm0);
+      cst[15 * D + c] = ex2(gl - gm1);
     } else {
+      gmv[2 * D + c] = gm2;
+      gmv[3 * D + c] = gm3;
       cst[7 * D + c] = ex2(gm2 - gb1);
       cst[8 * D + c] = ex2(gm3 - gb2);
       cst[9 * D + c] = ex2(gm3 - gb1);
@@ -221,52 +230,48 @@ __global__ void __launch_bounds__(NTHR, 2) prep_kernel(
       cst[11 * D + c] = ex2(gb2 - gm1);
       cst[12 * D + c] = ex2(gb3 - gm2);
       cst[13 * D + c] = ex2(gl);
+      cst[16 * D + c] = ex2(gl - gm2);
+      cst[17 * D + c] = ex2(gl - gm3);
     }
-    if (tid < C) s_beta[tid] = bval;
-    // Khat^T row c, tokens 32 ghf + i at positions 32 ghf + pperm(i): chunk b
-    // of this half holds tokens 16(e>>2) + 4b + (e&3), e = 0..7.
+  }
+  // prefix of the blocks above (same summation order as gb_i above)
+  if (w > 0) {
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      f16x8 kd;
+    for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int i = 16 * (e >> 2) + 4 * b + (e & 3);
-        const float kv = QKV_BF16 ? __uint_as_float(kcol[i] << 16) : __uint_as_float(kcol[i]);
-        kd[e] = static_cast<_Float16>(kv * ex2(gl - gv[i]));
+      for (int a = 0; a < 2; ++a) {
+        const int c0 = 32 * kk + 8 * lg + 4 * a;
+        f32x4 pre = *reinterpret_cast<const f32x4*>(btot + c0);
+        for (int j = 1; j < w; ++j) pre += *reinterpret_cast<const f32x4*>(btot + j * D + c0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) gam[kk][4 * a + i] += pre[i];
       }
-      const int chunk = (4 * ghf + b) ^ ((c >> 1) & 7);
-      *reinterpret_cast<f16x8*>(img + Ws::KDT + c * 128 + chunk * 16) = kd;  // kdt_off layout
-    }
   }
   __syncthreads();
 
   // ================= P1: decay factors, operands, diagonal tiles and T_ii.
-  // Lane (lr, lg) of wave i handles chunk row r = 16i + lr and, in k-step kk,
-  // the 8 channels 32kk + 16a + 4lg + j (a < 2, j < 4), fragment element 4a + j.
-  const int bi = w;
-  const int r = rA;
   float kE[4][8], qE[4][8];
   {
-    const int mrow = 16 * bi + 7;
     float kF[4][8];
+    f16x8 kd8[4];
     float dgmax = 0.0f;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       f16x8 kt, qt, rr8, l3k, l3q;
 #pragma unroll
       for (int a = 0; a < 2; ++a) {
-        const int c = 32 * kk + 16 * a + 4 * lg;
-        const f32x4 gr = *reinterpret_cast<const f32x4*>(gam + gidx(r, c));
-        const f32x4 gm = *reinterpret_cast<const f32x4*>(gam + gidx(mrow, c));
+        const int c = 32 * kk + 8 * lg + 4 * a;
+        const f32x4 gm = *reinterpret_cast<const f32x4*>(gmv + bi * D + c);
         const f32x4 em = *reinterpret_cast<const f32x4*>(cst + bi * D + c);
         const f32x4 eR = *reinterpret_cast<const f32x4*>(cst + (10 + (bi < 3 ? bi : 0)) * D + c);
         const f32x4 c30 = *reinterpret_cast<const f32x4*>(cst + 9 * D + c);
+        const f32x4 eL = *reinterpret_cast<const f32x4*>(cst + (14 + bi) * D + c);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int e = 4 * a + j;
-          const float kv = qk_at<QKV_BF16>(kpf, kk, a, j);
-          const float qv = qk_at<QKV_BF16>(qpf, kk, a, j);
-          const float dg = gr[j] - gm[j];
+          const float kv = kv8.at(kk, e);
+          const float qv = qv8.at(kk, e);
+          const float dg = gam[kk][e] - gm[j];
           dgmax = fmaxf(dgmax, fabsf(dg));
           const float E = ex2(dg), F = ex2(-dg);
           const float ke = kv * E, qe = qv * E, kf = kv * F;
@@ -275,6 +280,7 @@ __global__ void __launch_bounds__(NTHR, 2) prep_kernel(
           kF[kk][e] = kf;
           kt[e] = static_cast<_Float16>(ke * em[j]);
           qt[e] = static_cast<_Float16>(qe * em[j]);
+          kd8[kk][e] = static_cast<_Float16>(kf * eL[j]);
           if (bi < 3) rr8[e] = static_cast<_Float16>(kf * eR[j]);
           if (bi == 3) {
             l3k[e] = static_cast<_Float16>(ke * c30[j]);
@@ -282,14 +288,42 @@ __global__ void __launch_bounds__(NTHR, 2) prep_kernel(
           }
         }
       }
-      const int po = ke_off(r, 32 * kk + 8 * lg);
-      *reinterpret_cast<f16x8*>(img + Ws::KE + po) = kt;
-      *reinterpret_cast<f16x8*>(img + Ws::QE + po) = qt;
+      // K e^gamma, Q e^gamma: channels 32kk + 8lg + e sit at image positions
+      // 32kk + pperm(8lg + e): two runs of four.
+      const int p0 = 32 * kk + 16 * (lg & 1) + 4 * (lg >> 1);
+      const f16x4 kt0 = {kt[0], kt[1], kt[2], kt[3]}, kt1 = {kt[4], kt[5], kt[6], kt[7]};
+      const f16x4 qt0 = {qt[0], qt[1], qt[2], qt[3]}, qt1 = {qt[4], qt[5], qt[6], qt[7]};
+      *reinterpret_cast<f16x4*>(img + Ws::KE + ke_off(r, p0)) = kt0;
+      *reinterpret_cast<f16x4*>(img + Ws::KE + ke_off(r, p0 + 8)) = kt1;
+      *reinterpret_cast<f16x4*>(img + Ws::QE + ke_off(r, p0)) = qt0;
+      *reinterpret_cast<f16x4*>(img + Ws::QE + ke_off(r, p0 + 8)) = qt1;
+      const int po = ke_off(r, 32 * kk + 8 * lg);  // natural channel order in LDS
       if (bi < 3) *reinterpret_cast<f16x8*>(Rb + po) = rr8;
       if (bi == 3) {  // left factors of tile (3,0), which wave 0 multiplies
         *reinterpret_cast<f16x8*>(L3 + ke_off(lr, 32 * kk + 8 * lg)) = l3k;
         *reinterpret_cast<f16x8*>(L3 + ke_off(16 + lr, 32 * kk + 8 * lg)) = l3q;
       }
+    }
+    // (K e^(gamma_C - gamma))^T: D = Kd x Sel_h with Sel_h[k][n] = (k == 16h + n)
+    // puts Kd[16bi + 4lg + i][32kk + 16h + lr] in lane (lr, lg): four tokens of
+    // one channel, i.e. four consecutive image positions.
+    {
+      f16x8 sel[2];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          sel[hh][e] = static_cast<_Float16>((8 * lg + e == 16 * hh + lr) ? 1.0f : 0.0f);
+      const int pos = 32 * (bi >> 1) + 8 * lg + 4 * (bi & 1);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const f32x4 dt = mma_f16(kd8[kk], sel[hh], f32x4{0.f, 0.f, 0.f, 0.f});
+          const f16x4 d4 = {static_cast<_Float16>(dt[0]), static_cast<_Float16>(dt[1]),
+                            static_cast<_Float16>(dt[2]), static_cast<_Float16>(dt[3])};
+          *reinterpret_cast<f16x4*>(img + Ws::KDT + kdt_off(32 * kk + 16 * hh + lr, pos)) = d4;
+        }
     }
     // Diagonal tiles A_ii = (k E)(k F)^T and P_ii = (q E)(k F)^T.
     f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
@@ -390,7 +424,7 @@ __global__ void __launch_bounds__(NTHR, 2) prep_kernel(
         if (ti == bi) {
 #pragma unroll
           for (int a = 0; a < 2; ++a) {
-            const f32x4 cc = *reinterpret_cast<const f32x4*>(cst + slotc * D + 32 * kk + 16 * a + 4 * lg);
+            const f32x4 cc = *reinterpret_cast<const f32x4*>(cst + slotc * D + 32 * kk + 8 * lg + 4 * a);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
               lk[4 * a + j] = static_cast<_Float16>(kE[kk][4 * a + j] * cc[j]);
