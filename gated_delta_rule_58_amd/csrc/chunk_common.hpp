@@ -46,16 +46,6 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Contraction-index permutation inside a group of 32.  For the 16x16x32 MFMA,
-// lane (lr, lg) supplies contraction elements 8lg..8lg+7; an accumulator tile
-// pair (t, t+1) holds rows 16t+4lg+i and 16(t+1)+4lg+i in lane (lr, lg).  So
-// logical index L = 16a + 4b + c (a<2, b<4, c<4) is stored at position
-// 8b + 4a + c, and fragment element e of lane group lg is logical
-// 16(e>>2) + 4lg + (e&3).  Operands whose partner is an accumulator store
-// their contraction index in this order.
-__device__ __forceinline__ int pperm(int L) { return ((L >> 2) & 3) * 8 + (L >> 4) * 4 + (L & 3); }
-__device__ __forceinline__ int ppos64(int s) { return (s & 32) + pperm(s & 31); }
-
 __device__ __forceinline__ void split_f16(float x, _Float16& hi, _Float16& lo) {
   hi = static_cast<_Float16>(x);
   lo = static_cast<_Float16>(x - static_cast<float>(hi));
@@ -65,7 +55,10 @@ __device__ __forceinline__ void split_bf16(float x, __bf16& hi, __bf16& lo) {
   lo = static_cast<__bf16>(x - static_cast<float>(hi));
 }
 
-// 16x16x32 B fragment (hi and lo fp16) from an accumulator tile pair.
+// 16x16x32 B fragment (hi and lo fp16) from an accumulator tile pair
+// (t0 = rows 4lg+i, t1 = rows 16+4lg+i): fragment element e of lane group lg
+// is contraction index 16(e>>2) + 4lg + (e&3) of the 32-wide step.  Every
+// A operand paired with it is read in that same order.
 __device__ __forceinline__ void bfrag_split(const f32x4& t0, const f32x4& t1, f16x8& hi,
                                             f16x8& lo) {
 #pragma unroll
@@ -110,20 +103,25 @@ __device__ __forceinline__ void buf_to_lds16(__amdgpu_buffer_rsrc_t r, lds_ptr_t
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0f70); }
 
 // ---- workspace image of one (chunk, head), all offsets in bytes.
-// The state kernel copies it 1 KiB at a time into LDS and reads MFMA operand
-// fragments from it; the swizzles below make those reads conflict-free.
-//   KE, QE  fp16 [64 rows][128]: K e^gamma, Q e^gamma.  Position p of a row
-//           holds key channel 32(p>>5) + pperm^-1(p&31); 16-byte chunk j of
-//           row r sits at chunk j ^ (r & 15).
-//   KDT     fp16 [128 channels][64]: (K e^(gamma_C - gamma))^T, token s at
-//           position ppos64(s); chunk j of row c sits at chunk j ^ ((c>>1)&7).
-//   PM      fp16: P with token-permuted columns, only the part the products
-//           read: rows 0..31 positions 0..31 (64-byte rows), then rows 32..63
-//           positions 0..63 (128-byte rows).
-//   AT      fp16: the ten 16x16 tiles (i, j <= i) of the triangular system,
-//           T_ii = (I + A_ii)^-1 on the diagonal and -A_ij (beta folded into
-//           the rows) below it; tile (i, j) at index i(i+1)/2 + j, 32-byte
-//           rows whose 8-byte units are swizzled by row.
+// The prep kernel writes each part straight from its registers (128 bytes to
+// 1 KiB contiguous per instruction); the state kernel copies the image 1 KiB
+// at a time into LDS and reads 8-byte operand pieces, ordered so that each
+// 16-lane group of a read covers 128 contiguous bytes (no bank conflicts).
+// Every part is a sequence of 8-byte units; lane (lr, lg) of a 16x16 operand
+// tile reads unit 16 lg + lr of that tile's 512 bytes.
+//   KE, QE  fp16 K e^gamma, Q e^gamma: per 16-row block rt and 32-channel
+//           step kk a 1 KiB block of 16-byte units; unit 16 lg + lr holds row
+//           16 rt + lr, channels 32kk + 4lg .. +3 then 32kk + 16 + 4lg .. +3
+//           (the channel order of a 16x16x32 fragment paired with an
+//           accumulator tile pair).
+//   KDT     fp16 (K e^(gamma_C - gamma))^T: per 32-token step ks and
+//           16-channel tile t a 1 KiB block; unit 16 lg + lr holds channel
+//           16t + lr, tokens 32ks + 4lg .. +3 then 32ks + 16 + 4lg .. +3.
+//   PM      fp16 P, ten 16x16 tiles (i, j <= i) at index i(i+1)/2 + j; unit
+//           16 lg + lr holds row lr, columns 4lg .. +3 of the tile.
+//   AT      fp16 the same ten tiles of the triangular system: T_ii =
+//           (I + A_ii)^-1 on the diagonal, -A_ij (beta folded into the rows)
+//           below it.
 //   EC      fp32 [128]: e^gamma_C per key channel.
 //   BETA    fp32 [64]: beta of the chunk rows (0 past the chunk end).
 struct Ws {
@@ -131,34 +129,33 @@ struct Ws {
   static constexpr int QE = KE + C * D * 2;
   static constexpr int KDT = QE + C * D * 2;
   static constexpr int PM = KDT + D * C * 2;
-  static constexpr int PM_BYTES = 32 * 64 + 32 * 128;
-  static constexpr int AT = PM + PM_BYTES;
-  static constexpr int AT_BYTES = 10 * 16 * 32;
-  static constexpr int EC = AT + AT_BYTES;
+  static constexpr int AT = PM + 10 * 512;
+  static constexpr int EC = AT + 10 * 512;
   static constexpr int BETA = EC + D * 4;
   static constexpr int used = BETA + C * 4;
   static constexpr int bytes = ((used + 1023) / 1024) * 1024;  // copied in 1 KiB rounds
 };
-static_assert(Ws::bytes == 60 * 1024, "workspace image size");
+static_assert(Ws::bytes == 59 * 1024, "workspace image size");
 
-// byte offset of (row r, position p) in KE / QE
-__device__ __forceinline__ int ke_off(int r, int p) {
-  return r * 256 + ((((p >> 3) ^ (r & 15))) << 4) + ((p & 7) << 1);
+// KE / QE: the 16-byte fragment of lane (lr, lg) for row block rt, step kk
+__device__ __forceinline__ int keqe_frag(int rt, int kk, int lr, int lg) {
+  return ((rt * 4 + kk) << 10) + ((((lg << 4) + lr)) << 4);
 }
-// byte offset of (channel row c, position p) in KDT
-__device__ __forceinline__ int kdt_off(int c, int p) {
-  return c * 128 + ((((p >> 3) ^ ((c >> 1) & 7))) << 4) + ((p & 7) << 1);
+// KE / QE: where row 16rt + lr, channels 32kk + x .. x+3 (x = 0, 4, .., 28) go
+__device__ __forceinline__ int keqe_at(int rt, int kk, int x, int lr) {
+  return keqe_frag(rt, kk, lr, (x >> 2) & 3) + ((x >> 4) << 3);
 }
-// byte offset of (row r, position p) in PM (p < 32 for r < 32)
-__device__ __forceinline__ int pm_off(int r, int p) {
-  return r < 32 ? r * 64 + ((((p >> 3) ^ ((r >> 1) & 3))) << 4) + ((p & 7) << 1)
-                : 2048 + (r - 32) * 128 + ((((p >> 3) ^ ((r >> 1) & 7))) << 4) + ((p & 7) << 1);
+// KDT: the 16-byte fragment of lane (lr, lg) for token step ks, channel tile t
+__device__ __forceinline__ int kdt_frag(int ks, int t, int lr, int lg) {
+  return ((ks * 8 + t) << 10) + ((((lg << 4) + lr)) << 4);
 }
-// byte offset of element (row, col) of the triangular system, col <= row's block
-__device__ __forceinline__ int at_off(int row, int col) {
-  const int i = row >> 4, j = col >> 4, r = row & 15, cc = col & 15;
-  return ((i * (i + 1)) / 2 + j) * 512 + r * 32 + ((((cc >> 2) ^ ((r >> 2) & 3))) << 3) +
-         ((cc & 3) << 1);
+// KDT: where channel 16t + lr, tokens 16b + 4lg .. +3 go
+__device__ __forceinline__ int kdt_at(int b, int t, int lr, int lg) {
+  return kdt_frag(b >> 1, t, lr, lg) + ((b & 1) << 3);
+}
+// PM / AT: tile (i, j <= i), row lr, columns 4lg .. +3
+__device__ __forceinline__ int tri_at(int i, int j, int lr, int lg) {
+  return ((((i * (i + 1)) >> 1) + j) << 9) + ((((lg << 4) + lr)) << 3);
 }
 
 // Longest-first rank -> sequence index for N <= 64 sequences (ties by index),

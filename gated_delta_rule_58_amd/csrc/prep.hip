@@ -41,11 +41,9 @@ namespace {
 
 struct PrepLds {
   static constexpr int SC_LD = 17;  // fp32 [4][16][17] per-wave transpose scratch
-  static constexpr int off_R = 0;                         // fp16 [48][128], ke_off layout
-  static constexpr int off_L3 = off_R + 48 * D * 2;       // fp16 [32][128], ke_off layout
-  static constexpr int off_PM = off_L3 + 32 * D * 2;      // image of Ws::PM
-  static constexpr int off_AT = off_PM + Ws::PM_BYTES;    // image of Ws::AT (follows PM)
-  static constexpr int off_scr = off_AT + Ws::AT_BYTES;
+  static constexpr int off_R = 0;                         // fp16 [48][128], rl_off layout
+  static constexpr int off_L3 = off_R + 48 * D * 2;       // fp16 [32][128], rl_off layout
+  static constexpr int off_scr = off_L3 + 32 * D * 2;
   static constexpr int off_btot = off_scr + 4 * 16 * SC_LD * 4;  // fp32 [4][128] block sums
   static constexpr int off_bmid = off_btot + 4 * D * 4;   // fp32 [4][128] block sums to row 7
   static constexpr int off_gm = off_bmid + 4 * D * 4;     // fp32 [4][128] gamma at mid rows
@@ -54,6 +52,12 @@ struct PrepLds {
   static constexpr int total = off_beta + C * 4;
 };
 static_assert(PrepLds::total <= 53 * 1024, "three prep workgroups per CU");
+
+// byte offset of (row r, channel c) in the fp16 [rows][128] factor buffers:
+// 16-byte chunks swizzled by row so a 16-lane column of rows is conflict-free
+__device__ __forceinline__ int rl_off(int r, int c) {
+  return r * 256 + ((((c >> 3) ^ (r & 15))) << 4) + ((c & 7) << 1);
+}
 
 // Per-channel constant slots (after exp2, all <= 1):
 //  0..3   em_i = 2^gamma_{m_i}
@@ -111,8 +115,6 @@ __global__ void __launch_bounds__(NTHR, 2) prep_kernel(
   __shared__ __attribute__((aligned(16))) char lds[PrepLds::total];
   char* Rb = lds + PrepLds::off_R;
   char* L3 = lds + PrepLds::off_L3;
-  char* ATi = lds + PrepLds::off_AT;
-  char* PMi = lds + PrepLds::off_PM;
   float* btot = reinterpret_cast<float*>(lds + PrepLds::off_btot);
   float* bmid = reinterpret_cast<float*>(lds + PrepLds::off_bmid);
   float* gmv = reinterpret_cast<float*>(lds + PrepLds::off_gm);
@@ -288,25 +290,24 @@ __global__ void __launch_bounds__(NTHR, 2) prep_kernel(
           }
         }
       }
-      // K e^gamma, Q e^gamma: channels 32kk + 8lg + e sit at image positions
-      // 32kk + pperm(8lg + e): two runs of four.
-      const int p0 = 32 * kk + 16 * (lg & 1) + 4 * (lg >> 1);
-      const f16x4 kt0 = {kt[0], kt[1], kt[2], kt[3]}, kt1 = {kt[4], kt[5], kt[6], kt[7]};
-      const f16x4 qt0 = {qt[0], qt[1], qt[2], qt[3]}, qt1 = {qt[4], qt[5], qt[6], qt[7]};
-      *reinterpret_cast<f16x4*>(img + Ws::KE + ke_off(r, p0)) = kt0;
-      *reinterpret_cast<f16x4*>(img + Ws::KE + ke_off(r, p0 + 8)) = kt1;
-      *reinterpret_cast<f16x4*>(img + Ws::QE + ke_off(r, p0)) = qt0;
-      *reinterpret_cast<f16x4*>(img + Ws::QE + ke_off(r, p0 + 8)) = qt1;
-      const int po = ke_off(r, 32 * kk + 8 * lg);  // natural channel order in LDS
-      if (bi < 3) *reinterpret_cast<f16x8*>(Rb + po) = rr8;
+      // K e^gamma, Q e^gamma: two 8-byte halves per lane
+      {
+        const f16x4 k0 = {kt[0], kt[1], kt[2], kt[3]}, k1 = {kt[4], kt[5], kt[6], kt[7]};
+        const f16x4 q0 = {qt[0], qt[1], qt[2], qt[3]}, q1 = {qt[4], qt[5], qt[6], qt[7]};
+        *reinterpret_cast<f16x4*>(img + Ws::KE + keqe_at(bi, kk, 8 * lg, lr)) = k0;
+        *reinterpret_cast<f16x4*>(img + Ws::KE + keqe_at(bi, kk, 8 * lg + 4, lr)) = k1;
+        *reinterpret_cast<f16x4*>(img + Ws::QE + keqe_at(bi, kk, 8 * lg, lr)) = q0;
+        *reinterpret_cast<f16x4*>(img + Ws::QE + keqe_at(bi, kk, 8 * lg + 4, lr)) = q1;
+      }
+      if (bi < 3) *reinterpret_cast<f16x8*>(Rb + rl_off(r, 32 * kk + 8 * lg)) = rr8;
       if (bi == 3) {  // left factors of tile (3,0), which wave 0 multiplies
-        *reinterpret_cast<f16x8*>(L3 + ke_off(lr, 32 * kk + 8 * lg)) = l3k;
-        *reinterpret_cast<f16x8*>(L3 + ke_off(16 + lr, 32 * kk + 8 * lg)) = l3q;
+        *reinterpret_cast<f16x8*>(L3 + rl_off(lr, 32 * kk + 8 * lg)) = l3k;
+        *reinterpret_cast<f16x8*>(L3 + rl_off(16 + lr, 32 * kk + 8 * lg)) = l3q;
       }
     }
     // (K e^(gamma_C - gamma))^T: D = Kd x Sel_h with Sel_h[k][n] = (k == 16h + n)
     // puts Kd[16bi + 4lg + i][32kk + 16h + lr] in lane (lr, lg): four tokens of
-    // one channel, i.e. four consecutive image positions.
+    // one channel (512 contiguous bytes per store).
     {
       f16x8 sel[2];
 #pragma unroll
@@ -314,7 +315,6 @@ __global__ void __launch_bounds__(NTHR, 2) prep_kernel(
 #pragma unroll
         for (int e = 0; e < 8; ++e)
           sel[hh][e] = static_cast<_Float16>((8 * lg + e == 16 * hh + lr) ? 1.0f : 0.0f);
-      const int pos = 32 * (bi >> 1) + 8 * lg + 4 * (bi & 1);
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
@@ -322,10 +322,12 @@ __global__ void __launch_bounds__(NTHR, 2) prep_kernel(
           const f32x4 dt = mma_f16(kd8[kk], sel[hh], f32x4{0.f, 0.f, 0.f, 0.f});
           const f16x4 d4 = {static_cast<_Float16>(dt[0]), static_cast<_Float16>(dt[1]),
                             static_cast<_Float16>(dt[2]), static_cast<_Float16>(dt[3])};
-          *reinterpret_cast<f16x4*>(img + Ws::KDT + kdt_off(32 * kk + 16 * hh + lr, pos)) = d4;
+          *reinterpret_cast<f16x4*>(img + Ws::KDT + kdt_at(bi, 2 * kk + hh, lr, lg)) = d4;
         }
     }
-    // Diagonal tiles A_ii = (k E)(k F)^T and P_ii = (q E)(k F)^T.
+    // Diagonal tiles A_ii = (k E)(k F)^T (accumulator layout: rows 4lg+i) and
+    // P_ii = (q E)(k F)^T computed as (k F)(q E)^T, so a lane holds row lr,
+    // columns 4lg .. +3 (the image's row-major tile).
     f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
     if (!__any(dgmax > 7.0f)) {
 #pragma unroll
@@ -338,7 +340,7 @@ __global__ void __launch_bounds__(NTHR, 2) prep_kernel(
           fk[e] = static_cast<_Float16>(kF[kk][e]);
         }
         accA = mma_f16(ek, fk, accA);
-        accP = mma_f16(eq, fk, accP);
+        accP = mma_f16(fk, eq, accP);
       }
     } else {
 #pragma unroll
@@ -354,24 +356,21 @@ __global__ void __launch_bounds__(NTHR, 2) prep_kernel(
         accA = mma_bf16(ekh, fkh, accA);
         accA = mma_bf16(ekh, fkl, accA);
         accA = mma_bf16(ekl, fkh, accA);
-        accP = mma_bf16(eqh, fkh, accP);
-        accP = mma_bf16(eqh, fkl, accP);
-        accP = mma_bf16(eql, fkh, accP);
+        accP = mma_bf16(fkh, eqh, accP);
+        accP = mma_bf16(fkl, eqh, accP);
+        accP = mma_bf16(fkh, eql, accP);
       }
     }
-    // -- diagonal tile (bi, bi): lane holds rows 16bi + 4lg + i, column s = 16bi + lr
-    const int sp = ppos64(16 * bi + lr);
+    // -- diagonal tile (bi, bi)
     f32x4 nB;  // N = A_ii (strictly lower, beta-scaled rows) in accumulator layout
+    f16x4 pd;  // P_ii row lr, columns 4lg + i (lower triangle kept)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int rr = 4 * lg + i, row = 16 * bi + rr;
       nB[i] = (lr < rr) ? accA[i] * s_beta[row] : 0.0f;
-      *reinterpret_cast<_Float16*>(PMi + pm_off(row, sp)) =
-          static_cast<_Float16>((lr <= rr) ? accP[i] : 0.0f);
-      if ((bi & 1) == 0)  // upper tile (bi, bi+1) of P lies inside a 32-wide k-step
-        *reinterpret_cast<_Float16*>(PMi + pm_off(row, ppos64(16 * bi + 16 + lr))) =
-            static_cast<_Float16>(0.0f);
+      pd[i] = static_cast<_Float16>((rr <= lr) ? accP[i] : 0.0f);
     }
+    *reinterpret_cast<f16x4*>(img + Ws::PM + tri_at(bi, bi, lr, lg)) = pd;
     // -- T_ii = (I + N)^-1 = (I - N)(I + N^2)(I + N^4)(I + N^8), exact since
     // N^16 = 0.  Products are 16x16x16 MFMAs: the left factor is read in operand
     // layout through a wave-private LDS transpose, the right factor is an
@@ -403,11 +402,10 @@ __global__ void __launch_bounds__(NTHR, 2) prep_kernel(
     const f32x4 n8B = mul(to_a(n4B), n4B);
     const f32x4 m2B = mul(eye - nA, eye + n2B);
     const f32x4 m3B = mul(to_a(m2B), eye + n4B);
-    const f32x4 tB = mul(to_a(m3B), eye + n8B);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<_Float16*>(ATi + at_off(16 * bi + 4 * lg + i, 16 * bi + lr)) =
-          static_cast<_Float16>(tB[i]);
+    const f32x4 tA = to_a(mul(to_a(m3B), eye + n8B));  // row lr, columns 4lg + e
+    const f16x4 td = {static_cast<_Float16>(tA[0]), static_cast<_Float16>(tA[1]),
+                      static_cast<_Float16>(tA[2]), static_cast<_Float16>(tA[3])};
+    *reinterpret_cast<f16x4*>(img + Ws::AT + tri_at(bi, bi, lr, lg)) = td;
   }
   __syncthreads();
 
@@ -432,21 +430,21 @@ __global__ void __launch_bounds__(NTHR, 2) prep_kernel(
             }
           }
         } else {
-          lk = *reinterpret_cast<const f16x8*>(L3 + ke_off(lr, 32 * kk + 8 * lg));
-          lq = *reinterpret_cast<const f16x8*>(L3 + ke_off(16 + lr, 32 * kk + 8 * lg));
+          lk = *reinterpret_cast<const f16x8*>(L3 + rl_off(lr, 32 * kk + 8 * lg));
+          lq = *reinterpret_cast<const f16x8*>(L3 + rl_off(16 + lr, 32 * kk + 8 * lg));
         }
-        const f16x8 rb = *reinterpret_cast<const f16x8*>(Rb + ke_off(16 * tj + lr, 32 * kk + 8 * lg));
-        accA = mma_f16(lk, rb, accA);
-        accP = mma_f16(lq, rb, accP);
+        const f16x8 rb = *reinterpret_cast<const f16x8*>(Rb + rl_off(16 * tj + lr, 32 * kk + 8 * lg));
+        // transposed products: lane (lr, lg) gets row lr, columns 4lg .. +3
+        accA = mma_f16(rb, lk, accA);
+        accP = mma_f16(rb, lq, accP);
       }
-      const int sp = ppos64(16 * tj + lr);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 16 * ti + 4 * lg + i;
-        *reinterpret_cast<_Float16*>(ATi + at_off(row, 16 * tj + lr)) =
-            static_cast<_Float16>(-accA[i] * s_beta[row]);
-        *reinterpret_cast<_Float16*>(PMi + pm_off(row, sp)) = static_cast<_Float16>(accP[i]);
-      }
+      const float nb = -s_beta[16 * ti + lr];
+      const f16x4 ad = {static_cast<_Float16>(nb * accA[0]), static_cast<_Float16>(nb * accA[1]),
+                        static_cast<_Float16>(nb * accA[2]), static_cast<_Float16>(nb * accA[3])};
+      const f16x4 pd = {static_cast<_Float16>(accP[0]), static_cast<_Float16>(accP[1]),
+                        static_cast<_Float16>(accP[2]), static_cast<_Float16>(accP[3])};
+      *reinterpret_cast<f16x4*>(img + Ws::AT + tri_at(ti, tj, lr, lg)) = ad;
+      *reinterpret_cast<f16x4*>(img + Ws::PM + tri_at(ti, tj, lr, lg)) = pd;
     };
     if (bi == 0) {
       offdiag(3, 0);
@@ -460,17 +458,10 @@ __global__ void __launch_bounds__(NTHR, 2) prep_kernel(
       offdiag(3, 2);
     }
   }
-  __syncthreads();
 
-  // ---- copy the LDS-built parts of the image: PM and AT (contiguous in both),
-  // EC, BETA
+  // ---- EC and BETA
   {
     typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-    constexpr int units = (Ws::PM_BYTES + Ws::AT_BYTES) / 16;
-    static_assert(Ws::AT == Ws::PM + Ws::PM_BYTES, "PM and AT adjacent");
-    for (int u = tid; u < units; u += NTHR)
-      *reinterpret_cast<u32x4*>(img + Ws::PM + 16 * u) =
-          *reinterpret_cast<const u32x4*>(lds + PrepLds::off_PM + 16 * u);
     if (tid < 32)
       *reinterpret_cast<u32x4*>(img + Ws::EC + 16 * tid) =
           *reinterpret_cast<const u32x4*>(cst + 13 * D + 4 * tid);

@@ -11,11 +11,12 @@
 // Waves 0..3 compute.  Every product is independent across value columns, so
 // compute wave w owns columns 16w..16w+15 of the tile and keeps its 128x16
 // slice of S, and its 64x16 slices of X, Delta and O, in MFMA accumulators:
-// no barriers inside a chunk.  The contraction index of every 16x16x32
-// product whose B operand comes from an accumulator is stored permuted in the
-// image (pperm), so an accumulator tile pair is directly the next product's B
-// fragment.
-//
+// no barriers inside a chunk.  An accumulator tile holds rows 4lg..4lg+3 of
+// column lr in lane (lr, lg); a pair of them is the B fragment of a 16x16x32
+// product (contraction index 16(e>>2) + 4lg + (e&3)) and, unchanged, the A
+// fragment of the transposed product, so S and Delta never leave their
+// registers.  The image operands are read in the matching order.  The block
+// forward substitution for Delta uses 16x16x16 products.
 // The output is computed transposed, O^T = S^T (Q e^gamma)^T + Delta^T P^T:
 // the same fragments with the operands swapped, so each lane ends up with four
 // consecutive columns of one token row.
@@ -204,28 +205,27 @@ __global__ void __launch_bounds__(NTHR_S, 1) state_kernel(
         if (more) load_v_regs(c + 1);
       }
 
-      // S as one fp16 fragment per k-step: it serves as the B operand of X
-      // (channels x value columns) and, unchanged, as the A operand of O^T
-      // (value columns x channels).
-      f16x8 sb[4];
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          sb[kk][e] = static_cast<_Float16>(e < 4 ? Sacc[2 * kk][e] : Sacc[2 * kk + 1][e - 4]);
-      // X = V - Ke S (rows = tokens) ;  O^T = S^T Qe^T (rows = value columns)
+      // X = V - Ke S (rows = tokens) and O^T = S^T Qe^T (rows = value columns),
+      // 16x16x32 products over the four 32-channel steps kk.  The S tile pair
+      // (2kk, 2kk+1) is the B fragment of the first and, unchanged, the A
+      // fragment of the second; the Ke / Qe fragment holds the matching
+      // channels 32kk + 4lg + e and 32kk + 16 + 4lg + e.
       f32x4 Xacc[4], Oacc[4];
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) Xacc[rt] = Oacc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
+        f16x8 sf;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          sf[e] = static_cast<_Float16>(e < 4 ? Sacc[2 * kk][e] : Sacc[2 * kk + 1][e - 4]);
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
-          const int po = ke_off(16 * rt + lr, 32 * kk + 8 * lg);
+          const int po = keqe_frag(rt, kk, lr, lg);
           const f16x8 ak = *reinterpret_cast<const f16x8*>(im + Ws::KE + po);
           const f16x8 aq = *reinterpret_cast<const f16x8*>(im + Ws::QE + po);
-          Xacc[rt] = mma_f16(ak, sb[kk], Xacc[rt]);
-          Oacc[rt] = mma_f16(sb[kk], aq, Oacc[rt]);
+          Xacc[rt] = mma_f16(ak, sf, Xacc[rt]);
+          Oacc[rt] = mma_f16(sf, aq, Oacc[rt]);
         }
       }
 #pragma unroll
@@ -242,21 +242,19 @@ __global__ void __launch_bounds__(NTHR_S, 1) state_kernel(
 #pragma unroll
         for (int bj4 = 0; bj4 < 3; ++bj4) {
           if (bj4 >= bi4) continue;
-          const f16x4 na =
-              *reinterpret_cast<const f16x4*>(im + Ws::AT + at_off(16 * bi4 + lr, 16 * bj4 + 4 * lg));
+          const f16x4 na = *reinterpret_cast<const f16x4*>(im + Ws::AT + tri_at(bi4, bj4, lr, lg));
           f16x4 dh, dl;
           bfrag16_split(Dacc[bj4], dh, dl);
           acc = mma_f16_k16(na, dh, acc);
           acc = mma_f16_k16(na, dl, acc);
         }
-        const f16x4 ti =
-            *reinterpret_cast<const f16x4*>(im + Ws::AT + at_off(16 * bi4 + lr, 16 * bi4 + 4 * lg));
+        const f16x4 ti = *reinterpret_cast<const f16x4*>(im + Ws::AT + tri_at(bi4, bi4, lr, lg));
         f16x4 xh, xl;
         bfrag16_split(acc, xh, xl);
         f32x4 d = mma_f16_k16(ti, xh, f32x4{0.f, 0.f, 0.f, 0.f});
         Dacc[bi4] = mma_f16_k16(ti, xl, d);
       }
-      f16x8 dbh[2], dbl[2];
+      f16x8 dbh[2], dbl[2];  // Delta block pairs as hi+lo fragments
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) bfrag_split(Dacc[2 * ks], Dacc[2 * ks + 1], dbh[ks], dbl[ks]);
       // -- O^T += Delta^T P^T: lane (lr, lg) of tile rt then holds token row
@@ -270,9 +268,14 @@ __global__ void __launch_bounds__(NTHR_S, 1) state_kernel(
         f32x4 ao = Oacc[rt];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          if (ks > (rt >> 1)) continue;
-          const f16x8 pm =
-              *reinterpret_cast<const f16x8*>(im + Ws::PM + pm_off(16 * rt + lr, 32 * ks + 8 * lg));
+          if (2 * ks > rt) continue;
+          // P row 16rt + lr, tokens 32ks + 4lg + e and 32ks + 16 + 4lg + e
+          // (tile (rt, 2ks+1) lies above the diagonal when 2ks + 1 > rt)
+          const f16x4 p0 = *reinterpret_cast<const f16x4*>(im + Ws::PM + tri_at(rt, 2 * ks, lr, lg));
+          f16x4 p1 = {0, 0, 0, 0};
+          if (2 * ks + 1 <= rt)
+            p1 = *reinterpret_cast<const f16x4*>(im + Ws::PM + tri_at(rt, 2 * ks + 1, lr, lg));
+          const f16x8 pm = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
           ao = mma_f16(dbh[ks], pm, ao);
           ao = mma_f16(dbl[ks], pm, ao);
         }
@@ -298,8 +301,7 @@ __global__ void __launch_bounds__(NTHR_S, 1) state_kernel(
         f32x4 s = Sacc[t] * dec;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          const f16x8 a =
-              *reinterpret_cast<const f16x8*>(im + Ws::KDT + kdt_off(16 * t + lr, 32 * ks + 8 * lg));
+          const f16x8 a = *reinterpret_cast<const f16x8*>(im + Ws::KDT + kdt_frag(ks, t, lr, lg));
           s = mma_f16(a, dbh[ks], s);
           s = mma_f16(a, dbl[ks], s);
         }
