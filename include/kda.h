@@ -145,7 +145,7 @@ kda_status kda_chunk_prefill(const void* q, const void* k, const void* v, kda_dt
  * kda_chunk_prefill_workspace_bytes - workspace size for kda_chunk_prefill
  * processing up to chunks_per_pass chunks (of 64 tokens) of every sequence per
  * pass: a state carry of N*H*dk*dv*4 bytes plus N*H*chunks_per_pass images
- * of 61,440 bytes.  Returns 0 for unsupported or non-positive arguments.
+ * of 60,416 bytes.  Returns 0 for unsupported or non-positive arguments.
  */
 size_t kda_chunk_prefill_workspace_bytes(int32_t N, int32_t H, int32_t dk, int32_t dv,
                                          int32_t chunks_per_pass);

@@ -91,13 +91,13 @@ def test_prefill_refusals():
 
 
 def test_prefill_workspace_contract():
-    """Workspace size formula: state carry + one 61,440-byte image per
+    """Workspace size formula: state carry + one 60,416-byte image per
     (sequence, head, chunk of a pass); a missing, short or misaligned
     workspace is refused before launch."""
     L = _lib()
     f = L.kda_chunk_prefill_workspace_bytes
-    assert f(2, 4, 128, 128, 1) == 2 * 4 * (128 * 128 * 4 + 61440)
-    assert f(1, 96, 128, 128, 64) == 96 * 128 * 128 * 4 + 96 * 64 * 61440
+    assert f(2, 4, 128, 128, 1) == 2 * 4 * (128 * 128 * 4 + 60416)
+    assert f(1, 96, 128, 128, 64) == 96 * 128 * 128 * 4 + 96 * 64 * 60416
     assert f(1, 96, 64, 128, 1) == 0 and f(0, 96, 128, 128, 1) == 0 and f(1, 96, 128, 128, 0) == 0
     need = f(2, 4, 128, 128, 1)
     assert _prefill(L, [0, 20, 48], ws=None) == 6
