@@ -41,17 +41,18 @@ namespace {
 
 struct PrepLds {
   static constexpr int SC_LD = 17;  // fp32 [4][16][17] per-wave transpose scratch
-  static constexpr int off_R = 0;                         // fp16 [48][128], rl_off layout
-  static constexpr int off_L3 = off_R + 48 * D * 2;       // fp16 [32][128], rl_off layout
+  static constexpr int off_R = 0;                         // fp16 6 x [16][128], rl_off layout
+  static constexpr int off_L3 = off_R + 96 * D * 2;       // fp16 [32][128], rl_off layout
   static constexpr int off_scr = off_L3 + 32 * D * 2;
   static constexpr int off_btot = off_scr + 4 * 16 * SC_LD * 4;  // fp32 [4][128] block sums
   static constexpr int off_bmid = off_btot + 4 * D * 4;   // fp32 [4][128] block sums to row 7
   static constexpr int off_gm = off_bmid + 4 * D * 4;     // fp32 [4][128] gamma at mid rows
   static constexpr int off_cst = off_gm + 4 * D * 4;      // fp32 [18][128]
   static constexpr int off_beta = off_cst + 18 * D * 4;
-  static constexpr int total = off_beta + C * 4;
+  static constexpr int off_flag = off_beta + C * 4;      // int [4]: block needs wide range
+  static constexpr int total = off_flag + 16;
 };
-static_assert(PrepLds::total <= 53 * 1024, "three prep workgroups per CU");
+static_assert(PrepLds::total <= 160 * 1024 / 3, "three prep workgroups per CU");
 
 // byte offset of (row r, channel c) in the fp16 [rows][128] factor buffers:
 // 16-byte chunks swizzled by row so a 16-lane column of rows is conflict-free
@@ -59,16 +60,18 @@ __device__ __forceinline__ int rl_off(int r, int c) {
   return r * 256 + ((((c >> 3) ^ (r & 15))) << 4) + ((c & 7) << 1);
 }
 
-// Per-channel constant slots (after exp2, all <= 1):
+// Per-channel constant slots (after exp2, all <= 1).  m_i = 16i + 7 is the
+// mid row of block i, b_i = 16i - 1 the row before it (gamma_{b_0} = 0):
 //  0..3   em_i = 2^gamma_{m_i}
-//  4..9   c(i,j) = 2^(gamma_{m_i} - gamma_{b_{j+1}}), b_{j+1} = last row of block j:
-//         (1,0),(2,1),(3,2) at 4,5,6; (2,0) 7; (3,1) 8; (3,0) 9
-//  10..12 eR_j = 2^(gamma_{b_{j+1}} - gamma_{m_j}), j = 0..2
+//  4..6   cL_i = 2^(gamma_{m_i} - gamma_{b_i}), i = 1..3
+//  7..12  cR(i,j) = 2^(gamma_{b_i} - gamma_{m_j}), pairs (i, j > ... ) in rset order
 //  13     eC = 2^gamma_C
 //  14..17 eL_i = 2^(gamma_C - gamma_{m_i})
-__device__ __forceinline__ int cij_slot(int i, int j) {
-  return (j == i - 1) ? 3 + i : (i == 2 ? 7 : (j == 1 ? 8 : 9));
-}
+// An off-diagonal tile (i, j < i) is then the product of the left factor
+// k_r 2^(gamma_r - gamma_{b_i}) = (k E)_r cL_i (one per row block) and the
+// right factor k_s 2^(gamma_{b_i} - gamma_s) = (k F)_s cR(i,j), both <= 1.
+// Right-factor set of tile (i, j): (1,0) (2,0) (3,0) (2,1) (3,1) (3,2).
+__device__ __forceinline__ int rset(int i, int j) { return j == 0 ? i - 1 : (j == 1 ? i + 1 : 5); }
 
 // v + (v of the lane K rows up, inside each 16-lane row; 0 above the row)
 template <int K>
@@ -108,7 +111,7 @@ __device__ __forceinline__ void load_row8(Row8<BF16>& R, __amdgpu_buffer_rsrc_t 
 }
 
 template <bool QKV_BF16>
-__global__ void __launch_bounds__(NTHR, 2) prep_kernel(
+__global__ void __launch_bounds__(NTHR, 3) prep_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const float* __restrict__ g,
     const float* __restrict__ beta, const int32_t* __restrict__ cu, int T_tot, int H, int Hp,
     int c_lo, int S_len, char* __restrict__ ws) {
@@ -120,6 +123,7 @@ __global__ void __launch_bounds__(NTHR, 2) prep_kernel(
   float* gmv = reinterpret_cast<float*>(lds + PrepLds::off_gm);
   float* cst = reinterpret_cast<float*>(lds + PrepLds::off_cst);
   float* s_beta = reinterpret_cast<float*>(lds + PrepLds::off_beta);
+  int* s_flag = reinterpret_cast<int*>(lds + PrepLds::off_flag);
 
   // ---- block -> (chunk slot, head); head % 8 == block % 8, so every chunk of
   // a head is prepared on the XCD that later runs that head's state walk.
@@ -200,6 +204,7 @@ __global__ void __launch_bounds__(NTHR, 2) prep_kernel(
             f32x4{gam[kk][4 * a], gam[kk][4 * a + 1], gam[kk][4 * a + 2], gam[kk][4 * a + 3]};
   }
   if (lg == 0) s_beta[r] = bval;
+  if (tid < 4) s_flag[tid] = 0;
   __syncthreads();
 
   // ================= S2: gamma at the block ends and mid rows, decay constants;
@@ -222,18 +227,23 @@ __global__ void __launch_bounds__(NTHR, 2) prep_kernel(
       cst[6 * D + c] = ex2(gm3 - gb3);
       cst[14 * D + c] = ex2(gl - gm0);
       cst[15 * D + c] = ex2(gl - gm1);
+      // gamma of block i spans [gamma_{b_{i+1}}, gamma_{b_i}] (non-increasing)
+      if (fmaxf(-gm0, gm0 - gb1) > 7.0f) s_flag[0] = 1;
+      if (fmaxf(gb1 - gm1, gm1 - gb2) > 7.0f) s_flag[1] = 1;
     } else {
       gmv[2 * D + c] = gm2;
       gmv[3 * D + c] = gm3;
-      cst[7 * D + c] = ex2(gm2 - gb1);
-      cst[8 * D + c] = ex2(gm3 - gb2);
-      cst[9 * D + c] = ex2(gm3 - gb1);
-      cst[10 * D + c] = ex2(gb1 - gm0);
-      cst[11 * D + c] = ex2(gb2 - gm1);
+      cst[7 * D + c] = ex2(gb1 - gm0);
+      cst[8 * D + c] = ex2(gb2 - gm0);
+      cst[9 * D + c] = ex2(gb3 - gm0);
+      cst[10 * D + c] = ex2(gb2 - gm1);
+      cst[11 * D + c] = ex2(gb3 - gm1);
       cst[12 * D + c] = ex2(gb3 - gm2);
       cst[13 * D + c] = ex2(gl);
       cst[16 * D + c] = ex2(gl - gm2);
       cst[17 * D + c] = ex2(gl - gm3);
+      if (fmaxf(gb2 - gm2, gm2 - gb3) > 7.0f) s_flag[2] = 1;
+      if (fmaxf(gb3 - gm3, gm3 - gl) > 7.0f) s_flag[3] = 1;
     }
   }
   // prefix of the blocks above (same summation order as gb_i above)
@@ -251,43 +261,61 @@ __global__ void __launch_bounds__(NTHR, 2) prep_kernel(
   }
   __syncthreads();
 
-  // ================= P1: decay factors, operands, diagonal tiles and T_ii.
-  float kE[4][8], qE[4][8];
+  // ================= P1: per 32-channel step kk: decay factors, the image's
+  // K e^gamma, Q e^gamma and transposed decayed K, the right factors of the
+  // tiles below this block (LDS), this block's left factors (registers; LDS
+  // for tile (3,0)), and the diagonal tiles A_ii, P_ii.  Only the left factors
+  // outlive a step.
+  // Diagonal tiles A_ii = (k E)(k F)^T (accumulator layout: rows 4lg+i) and
+  // P_ii = (q E)(k F)^T computed as (k F)(q E)^T, so a lane holds row lr,
+  // columns 4lg .. +3 (the image's row-major tile).  E and F span at most
+  // the block's decay: plain fp16 when that is <= 2^7, otherwise hi+lo bf16.
+  const bool wide = s_flag[bi] != 0;
+  f16x8 lk[4], lq[4];
+  f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
   {
-    float kF[4][8];
-    f16x8 kd8[4];
-    float dgmax = 0.0f;
+    // Kd x Sel_h with Sel_h[k][n] = (k == 16h + n) puts Kd[16bi + 4lg + i][32kk + 16h + lr]
+    // in lane (lr, lg): four tokens of one channel (512 contiguous bytes per store)
+    f16x8 sel[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        sel[hh][e] = static_cast<_Float16>((8 * lg + e == 16 * hh + lr) ? 1.0f : 0.0f);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      f16x8 kt, qt, rr8, l3k, l3q;
+      float ke8[8], qe8[8], kf8[8];
+      f16x8 kt, qt, kd, r0, r1, r2;
 #pragma unroll
       for (int a = 0; a < 2; ++a) {
         const int c = 32 * kk + 8 * lg + 4 * a;
         const f32x4 gm = *reinterpret_cast<const f32x4*>(gmv + bi * D + c);
         const f32x4 em = *reinterpret_cast<const f32x4*>(cst + bi * D + c);
-        const f32x4 eR = *reinterpret_cast<const f32x4*>(cst + (10 + (bi < 3 ? bi : 0)) * D + c);
-        const f32x4 c30 = *reinterpret_cast<const f32x4*>(cst + 9 * D + c);
         const f32x4 eL = *reinterpret_cast<const f32x4*>(cst + (14 + bi) * D + c);
+        const f32x4 cl = *reinterpret_cast<const f32x4*>(cst + (bi > 0 ? 3 + bi : 4) * D + c);
+        // right-factor scales of the tiles (i, bi), i > bi
+        const f32x4 s0 = *reinterpret_cast<const f32x4*>(cst + (7 + rset(bi < 3 ? bi + 1 : 3, bi < 3 ? bi : 2)) * D + c);
+        const f32x4 s1 = *reinterpret_cast<const f32x4*>(cst + (7 + rset(bi < 2 ? bi + 2 : 3, bi < 2 ? bi : 1)) * D + c);
+        const f32x4 s2 = *reinterpret_cast<const f32x4*>(cst + 7 * D + c + 2 * D);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int e = 4 * a + j;
           const float kv = kv8.at(kk, e);
           const float qv = qv8.at(kk, e);
           const float dg = gam[kk][e] - gm[j];
-          dgmax = fmaxf(dgmax, fabsf(dg));
           const float E = ex2(dg), F = ex2(-dg);
           const float ke = kv * E, qe = qv * E, kf = kv * F;
-          kE[kk][e] = ke;
-          qE[kk][e] = qe;
-          kF[kk][e] = kf;
+          ke8[e] = ke;
+          qe8[e] = qe;
+          kf8[e] = kf;
           kt[e] = static_cast<_Float16>(ke * em[j]);
           qt[e] = static_cast<_Float16>(qe * em[j]);
-          kd8[kk][e] = static_cast<_Float16>(kf * eL[j]);
-          if (bi < 3) rr8[e] = static_cast<_Float16>(kf * eR[j]);
-          if (bi == 3) {
-            l3k[e] = static_cast<_Float16>(ke * c30[j]);
-            l3q[e] = static_cast<_Float16>(qe * c30[j]);
-          }
+          kd[e] = static_cast<_Float16>(kf * eL[j]);
+          lk[kk][e] = static_cast<_Float16>(ke * cl[j]);
+          lq[kk][e] = static_cast<_Float16>(qe * cl[j]);
+          r0[e] = static_cast<_Float16>(kf * s0[j]);
+          r1[e] = static_cast<_Float16>(kf * s1[j]);
+          r2[e] = static_cast<_Float16>(kf * s2[j]);
         }
       }
       // K e^gamma, Q e^gamma: two 8-byte halves per lane
@@ -299,59 +327,42 @@ __global__ void __launch_bounds__(NTHR, 2) prep_kernel(
         *reinterpret_cast<f16x4*>(img + Ws::QE + keqe_at(bi, kk, 8 * lg, lr)) = q0;
         *reinterpret_cast<f16x4*>(img + Ws::QE + keqe_at(bi, kk, 8 * lg + 4, lr)) = q1;
       }
-      if (bi < 3) *reinterpret_cast<f16x8*>(Rb + rl_off(r, 32 * kk + 8 * lg)) = rr8;
-      if (bi == 3) {  // left factors of tile (3,0), which wave 0 multiplies
-        *reinterpret_cast<f16x8*>(L3 + rl_off(lr, 32 * kk + 8 * lg)) = l3k;
-        *reinterpret_cast<f16x8*>(L3 + rl_off(16 + lr, 32 * kk + 8 * lg)) = l3q;
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const f32x4 dt = mma_f16(kd, sel[hh], f32x4{0.f, 0.f, 0.f, 0.f});
+        const f16x4 d4 = {static_cast<_Float16>(dt[0]), static_cast<_Float16>(dt[1]),
+                          static_cast<_Float16>(dt[2]), static_cast<_Float16>(dt[3])};
+        *reinterpret_cast<f16x4*>(img + Ws::KDT + kdt_at(bi, 2 * kk + hh, lr, lg)) = d4;
       }
-    }
-    // (K e^(gamma_C - gamma))^T: D = Kd x Sel_h with Sel_h[k][n] = (k == 16h + n)
-    // puts Kd[16bi + 4lg + i][32kk + 16h + lr] in lane (lr, lg): four tokens of
-    // one channel (512 contiguous bytes per store).
-    {
-      f16x8 sel[2];
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          sel[hh][e] = static_cast<_Float16>((8 * lg + e == 16 * hh + lr) ? 1.0f : 0.0f);
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const f32x4 dt = mma_f16(kd8[kk], sel[hh], f32x4{0.f, 0.f, 0.f, 0.f});
-          const f16x4 d4 = {static_cast<_Float16>(dt[0]), static_cast<_Float16>(dt[1]),
-                            static_cast<_Float16>(dt[2]), static_cast<_Float16>(dt[3])};
-          *reinterpret_cast<f16x4*>(img + Ws::KDT + kdt_at(bi, 2 * kk + hh, lr, lg)) = d4;
-        }
-    }
-    // Diagonal tiles A_ii = (k E)(k F)^T (accumulator layout: rows 4lg+i) and
-    // P_ii = (q E)(k F)^T computed as (k F)(q E)^T, so a lane holds row lr,
-    // columns 4lg .. +3 (the image's row-major tile).
-    f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
-    if (!__any(dgmax > 7.0f)) {
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
+      // right factors of the tiles below: block 0 -> (1,0) (2,0) (3,0);
+      // block 1 -> (2,1) (3,1); block 2 -> (3,2)
+      const int co = 32 * kk + 8 * lg;
+      if (bi < 3) *reinterpret_cast<f16x8*>(Rb + rl_off(16 * rset(bi + 1, bi) + lr, co)) = r0;
+      if (bi < 2) *reinterpret_cast<f16x8*>(Rb + rl_off(16 * rset(bi + 2, bi) + lr, co)) = r1;
+      if (bi == 0) *reinterpret_cast<f16x8*>(Rb + rl_off(16 * rset(3, 0) + lr, co)) = r2;
+      if (bi == 3) {  // left factors of tile (3,0), which wave 0 multiplies
+        *reinterpret_cast<f16x8*>(L3 + rl_off(lr, co)) = lk[kk];
+        *reinterpret_cast<f16x8*>(L3 + rl_off(16 + lr, co)) = lq[kk];
+      }
+      // diagonal tiles, this step's 32 channels
+      if (!wide) {
         f16x8 ek, eq, fk;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          ek[e] = static_cast<_Float16>(kE[kk][e]);
-          eq[e] = static_cast<_Float16>(qE[kk][e]);
-          fk[e] = static_cast<_Float16>(kF[kk][e]);
+          ek[e] = static_cast<_Float16>(ke8[e]);
+          eq[e] = static_cast<_Float16>(qe8[e]);
+          fk[e] = static_cast<_Float16>(kf8[e]);
         }
         accA = mma_f16(ek, fk, accA);
         accP = mma_f16(fk, eq, accP);
-      }
-    } else {
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
+      } else {
         bf16x8 ekh, ekl, eqh, eql, fkh, fkl;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           __bf16 x0, x1;
-          split_bf16(kE[kk][e], x0, x1); ekh[e] = x0; ekl[e] = x1;
-          split_bf16(qE[kk][e], x0, x1); eqh[e] = x0; eql[e] = x1;
-          split_bf16(kF[kk][e], x0, x1); fkh[e] = x0; fkl[e] = x1;
+          split_bf16(ke8[e], x0, x1); ekh[e] = x0; ekl[e] = x1;
+          split_bf16(qe8[e], x0, x1); eqh[e] = x0; eql[e] = x1;
+          split_bf16(kf8[e], x0, x1); fkh[e] = x0; fkl[e] = x1;
         }
         accA = mma_bf16(ekh, fkh, accA);
         accA = mma_bf16(ekh, fkl, accA);
@@ -361,6 +372,8 @@ __global__ void __launch_bounds__(NTHR, 2) prep_kernel(
         accP = mma_bf16(fkh, eql, accP);
       }
     }
+  }
+  {
     // -- diagonal tile (bi, bi)
     f32x4 nB;  // N = A_ii (strictly lower, beta-scaled rows) in accumulator layout
     f16x4 pd;  // P_ii row lr, columns 4lg + i (lower triangle kept)
@@ -414,35 +427,28 @@ __global__ void __launch_bounds__(NTHR, 2) prep_kernel(
   // which takes tile (3,0) with the left factors wave 3 left in LDS.
   {
     auto offdiag = [&](int ti, int tj) {
-      f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
-      const int slotc = cij_slot(ti, tj);
+      f32x4 aA = {0.f, 0.f, 0.f, 0.f}, aP = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        f16x8 lk, lq;
+        const int co = 32 * kk + 8 * lg;
+        f16x8 lkk, lqk;
         if (ti == bi) {
-#pragma unroll
-          for (int a = 0; a < 2; ++a) {
-            const f32x4 cc = *reinterpret_cast<const f32x4*>(cst + slotc * D + 32 * kk + 8 * lg + 4 * a);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              lk[4 * a + j] = static_cast<_Float16>(kE[kk][4 * a + j] * cc[j]);
-              lq[4 * a + j] = static_cast<_Float16>(qE[kk][4 * a + j] * cc[j]);
-            }
-          }
+          lkk = lk[kk];
+          lqk = lq[kk];
         } else {
-          lk = *reinterpret_cast<const f16x8*>(L3 + rl_off(lr, 32 * kk + 8 * lg));
-          lq = *reinterpret_cast<const f16x8*>(L3 + rl_off(16 + lr, 32 * kk + 8 * lg));
+          lkk = *reinterpret_cast<const f16x8*>(L3 + rl_off(lr, co));
+          lqk = *reinterpret_cast<const f16x8*>(L3 + rl_off(16 + lr, co));
         }
-        const f16x8 rb = *reinterpret_cast<const f16x8*>(Rb + rl_off(16 * tj + lr, 32 * kk + 8 * lg));
+        const f16x8 rb = *reinterpret_cast<const f16x8*>(Rb + rl_off(16 * rset(ti, tj) + lr, co));
         // transposed products: lane (lr, lg) gets row lr, columns 4lg .. +3
-        accA = mma_f16(rb, lk, accA);
-        accP = mma_f16(rb, lq, accP);
+        aA = mma_f16(rb, lkk, aA);
+        aP = mma_f16(rb, lqk, aP);
       }
       const float nb = -s_beta[16 * ti + lr];
-      const f16x4 ad = {static_cast<_Float16>(nb * accA[0]), static_cast<_Float16>(nb * accA[1]),
-                        static_cast<_Float16>(nb * accA[2]), static_cast<_Float16>(nb * accA[3])};
-      const f16x4 pd = {static_cast<_Float16>(accP[0]), static_cast<_Float16>(accP[1]),
-                        static_cast<_Float16>(accP[2]), static_cast<_Float16>(accP[3])};
+      const f16x4 ad = {static_cast<_Float16>(nb * aA[0]), static_cast<_Float16>(nb * aA[1]),
+                        static_cast<_Float16>(nb * aA[2]), static_cast<_Float16>(nb * aA[3])};
+      const f16x4 pd = {static_cast<_Float16>(aP[0]), static_cast<_Float16>(aP[1]),
+                        static_cast<_Float16>(aP[2]), static_cast<_Float16>(aP[3])};
       *reinterpret_cast<f16x4*>(img + Ws::AT + tri_at(ti, tj, lr, lg)) = ad;
       *reinterpret_cast<f16x4*>(img + Ws::PM + tri_at(ti, tj, lr, lg)) = pd;
     };
