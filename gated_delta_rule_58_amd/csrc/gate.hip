@@ -45,6 +45,19 @@ __device__ __forceinline__ float softplus_tail(float az) {
   return d == 0.0f ? e : l;
 }
 
+// 4 consecutive logits as fp32, read once: non-temporal, so the stream of x
+// does not displace the cached lines of g that the prefill reads next.
+template <bool BF16>
+__device__ __forceinline__ f32x4 load4_stream(const void* base, int64_t idx) {
+  if constexpr (BF16) {
+    const u16x4 r = __builtin_nontemporal_load(reinterpret_cast<const u16x4*>(
+        static_cast<const uint16_t*>(base) + idx));
+    return f32x4{bf16_bits_to_f32(r[0]), bf16_bits_to_f32(r[1]), bf16_bits_to_f32(r[2]),
+                 bf16_bits_to_f32(r[3])};
+  }
+  return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(static_cast<const float*>(base) + idx));
+}
+
 template <bool XBF16, bool BBF16>
 __global__ void __launch_bounds__(kThreads) gate_kernel(
     const void* __restrict__ x, const void* __restrict__ b, const float* __restrict__ A_log,
@@ -67,7 +80,7 @@ __global__ void __launch_bounds__(kThreads) gate_kernel(
       f32x4 xv[kTokUnroll];
 #pragma unroll
       for (int u = 0; u < kTokUnroll; ++u)
-        if (t + u < ntk) xv[u] = load4(x, base + (t + u) * tok_stride, XBF16);
+        if (t + u < ntk) xv[u] = load4_stream<XBF16>(x, base + (t + u) * tok_stride);
 #pragma unroll
       for (int u = 0; u < kTokUnroll; ++u) {
         if (t + u < ntk) {
