@@ -1,16 +1,18 @@
 #!/usr/bin/env python3
 """KDA core benchmark on one MI355X.
 
-A step is one pass of the prefill hot path over one batch: kda_gate (raw
-gate/beta logits -> g, beta) then kda_chunk_prefill, on the K3-layer prefill
+A step is one pass of the prefill hot path over one batch, from the raw
+gate/beta logits to o and the final state: kda_chunk_prefill_gated (the gate
+formed in registers inside the chunked prefill), on the K3-layer prefill
 workload (one sequence, T=4096, H=96, d=128, bf16 q/k/v, fp32 gate logits,
 zero initial state, bf16 o, fp32 final state).  `value` is sequence tokens/s
-of that step, inputs already resident in HBM.
+of that step, inputs already resident in HBM.  The same step as two calls
+(kda_gate, then kda_chunk_prefill on g and beta) is timed beside it.
 
 The same JSON line carries
-  roofline      the chunk-prefill kernel: algorithmic HBM bytes per launch /
-                its average launch time (HIP events on the launch stream),
-                against 8 TB/s; plus its algorithmic MFMA rate
+  roofline      the gated prefill call: algorithmic HBM bytes per call / its
+                average time (HIP events on the launch stream), against
+                8 TB/s; plus its algorithmic MFMA rate
   decode        kda_recurrent_decode on 256 sequences x 96 heads (fp32 state
                 [256,96,128,128] updated in place), 64 steps: state-update GB/s
   cpu_baseline  the fp64 oracle (gate + token-by-token recurrence) on a
@@ -52,7 +54,8 @@ DEC_STEP_BYTES = DEC_N * H * DEC_PAIR_BYTES                           # 3,259,07
 # the value recorded with the counters.
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "chunk_prefill_T4096_H96_hbm_traffic.md")
 CHUNK_SOURCES = ["gated_delta_rule_58_amd/csrc/prep.hip", "gated_delta_rule_58_amd/csrc/state.hip",
-                 "gated_delta_rule_58_amd/csrc/chunk_common.hpp"]
+                 "gated_delta_rule_58_amd/csrc/chunk_common.hpp",
+                 "gated_delta_rule_58_amd/csrc/gate_math.hpp"]
 
 
 def measured_traffic():
@@ -120,6 +123,10 @@ def bench_prefill(args, torch, kda, synth):
     def gate():
         kda.gate(dr.x, dr.b, dr.A_log, dr.dt_bias, g_out=g, beta_out=beta)
 
+    def fused():
+        kda.chunk_prefill_gated(dr.q, dr.k, dr.v, dr.x, dr.b, dr.A_log, dr.dt_bias, cu_d, None,
+                                out=o, final_state=Sf, cu_seqlens_host=cu_h, workspace=ws)
+
     ws = torch.empty(kda.chunk_prefill_workspace_bytes(1, H, D, D, args.ws_chunks),
                      dtype=torch.uint8, device=dev)
 
@@ -127,31 +134,35 @@ def bench_prefill(args, torch, kda, synth):
         kda.chunk_prefill(dr.q, dr.k, dr.v, g, beta, cu_d, None, out=o, final_state=Sf,
                           cu_seqlens_host=cu_h, workspace=ws)
 
-    for _ in range(args.warmup):
-        gate()
-        prefill()
-    torch.cuda.synchronize()
-    step_ms, chunk_ms, gate_ms = [], [], []
-    for _ in range(args.repeats):
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3 * args.steps)]
+    def timed(fns):
+        """Per-step event times of the calls in fns (in order), over repeats x steps."""
+        for _ in range(args.warmup):
+            for f in fns:
+                f()
         torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(args.steps):
-            ev[3 * i].record()
-            gate()
-            ev[3 * i + 1].record()
-            prefill()
-            ev[3 * i + 2].record()
-        torch.cuda.synchronize()
-        wall = (time.perf_counter() - t0) * 1e3 / args.steps
-        for i in range(args.steps):
-            gate_ms.append(ev[3 * i].elapsed_time(ev[3 * i + 1]))
-            chunk_ms.append(ev[3 * i + 1].elapsed_time(ev[3 * i + 2]))
-            step_ms.append(ev[3 * i].elapsed_time(ev[3 * i + 2]))
-        step_ms_wall = wall
-    return dict(step_ms=sum(step_ms) / len(step_ms), chunk_ms=sum(chunk_ms) / len(chunk_ms),
-                gate_ms=sum(gate_ms) / len(gate_ms), wall_ms=step_ms_wall,
-                p95_step_ms=sorted(step_ms)[int(0.95 * (len(step_ms) - 1))])
+        per = [[] for _ in fns]
+        for _ in range(args.repeats):
+            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)]
+                  for _ in range(args.steps)]
+            torch.cuda.synchronize()
+            for i in range(args.steps):
+                ev[i][0].record()
+                for j, f in enumerate(fns):
+                    f()
+                    ev[i][j + 1].record()
+            torch.cuda.synchronize()
+            for i in range(args.steps):
+                for j in range(len(fns)):
+                    per[j].append(ev[i][j].elapsed_time(ev[i][j + 1]))
+        steps = [sum(x) for x in zip(*per)]
+        return per, steps
+
+    (fz,), fsteps = timed([fused])
+    (gt, ch), ssteps = timed([gate, prefill])
+    mean = lambda x: sum(x) / len(x)
+    p95 = lambda x: sorted(x)[int(0.95 * (len(x) - 1))]
+    return dict(step_ms=mean(fsteps), p95_step_ms=p95(fsteps), fused_ms=mean(fz),
+                sep_step_ms=mean(ssteps), chunk_ms=mean(ch), gate_ms=mean(gt))
 
 
 def bench_decode(args, torch, kda, synth):
@@ -228,15 +239,16 @@ def main():
         print(json.dumps({"diagnostic": args.only, **fn()}), flush=True)
         return
     pre = bench_prefill(args, torch, kda, synth)
-    print("prefill: step %.4f ms (gate %.4f, chunk %.4f), p95 %.4f ms" %
-          (pre["step_ms"], pre["gate_ms"], pre["chunk_ms"], pre["p95_step_ms"]),
+    print("prefill: step (gated prefill) %.4f ms, p95 %.4f ms; gate + prefill %.4f ms "
+          "(gate %.4f, chunk %.4f)" % (pre["step_ms"], pre["p95_step_ms"], pre["sep_step_ms"],
+                                      pre["gate_ms"], pre["chunk_ms"]),
           file=sys.stderr, flush=True)
     dec = bench_decode(args, torch, kda, synth)
     print("decode: %.4f ms/step, %.1f GB/s" % (dec["ms_per_step"], dec["GBps"]),
           file=sys.stderr, flush=True)
-    chunk_s = pre["chunk_ms"] * 1e-3
-    ach = PREFILL_BYTES / chunk_s / 1e9
-    mfma = PREFILL_FLOPS / chunk_s / 1e12
+    step_s = pre["fused_ms"] * 1e-3
+    ach = PREFILL_BYTES / step_s / 1e9
+    mfma = PREFILL_FLOPS / step_s / 1e12
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(args, synth)
@@ -253,15 +265,17 @@ def main():
         "vs_baseline": None,
         "dtype": "f16-mfma/f32-acc (bf16 q/k/v/o, f32 g/beta/state)",
         "data": "synthetic",
-        "config": {"workload": "k3-layer-prefill T=4096 H=96 d=128: kda_gate + kda_chunk_prefill",
+        "config": {"workload": "k3-layer-prefill T=4096 H=96 d=128: kda_chunk_prefill_gated "
+                               "(gate logits -> o and final state, one call)",
                    "T": T, "H": H, "d": D, "chunk": C, "qkv": "bf16", "o": "bf16",
                    "gate_logits": "f32", "initial_state": "zero", "repeats": args.repeats},
         "prefill": {"step_ms": pre["step_ms"], "p95_step_ms": pre["p95_step_ms"],
-                    "chunk_kernel_ms": pre["chunk_ms"], "gate_kernel_ms": pre["gate_ms"],
-                    "prefill_only_tokens_per_s": T / chunk_s},
+                    "gate_then_prefill_ms": pre["sep_step_ms"],
+                    "gate_kernel_ms": pre["gate_ms"], "chunk_prefill_ms": pre["chunk_ms"],
+                    "chunk_prefill_tokens_per_s": T / (pre["chunk_ms"] * 1e-3)},
         "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": ach / HBM_PEAK_GBS, "traffic": measured_traffic(),
-                     "kernel": "kda_chunk_prefill (prep_kernel + state_kernel, one pass)",
+                     "kernel": "kda_chunk_prefill_gated (prep_kernel + state_kernel, one pass)",
                      "alg_bytes_per_launch": PREFILL_BYTES},
         "roofline_mfma": {"achieved": mfma, "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                           "frac": mfma / MFMA_F16_PEAK_TFLOPS,

@@ -14,6 +14,7 @@ from .binding import (  # noqa: F401
     lib_path,
     gate,
     chunk_prefill,
+    chunk_prefill_gated,
     chunk_prefill_workspace_bytes,
     recurrent_decode,
     exported_symbols,

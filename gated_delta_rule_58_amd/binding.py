@@ -55,6 +55,11 @@ def lib():
         L.kda_chunk_prefill.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _vp, _i32,
                                         _vp, _vp, _vp, ctypes.c_int, _i64, _i32, _i32, _i32,
                                         ctypes.c_float, _vp, ctypes.c_size_t, _vp]
+        L.kda_chunk_prefill_gated.restype = ctypes.c_int
+        L.kda_chunk_prefill_gated.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, ctypes.c_int, _vp,
+                                              ctypes.c_int, _vp, _i64, _vp, _i64, _vp, _vp, _i32,
+                                              _vp, _vp, _vp, ctypes.c_int, _i64, _i32, _i32, _i32,
+                                              ctypes.c_float, _vp, ctypes.c_size_t, _vp]
         L.kda_chunk_prefill_workspace_bytes.restype = ctypes.c_size_t
         L.kda_chunk_prefill_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32, _i32]
         L.kda_recurrent_decode.restype = ctypes.c_int
@@ -67,7 +72,7 @@ def lib():
 
 def exported_symbols():
     return ["kda_last_error", "kda_version", "kda_gate", "kda_chunk_prefill",
-            "kda_chunk_prefill_workspace_bytes", "kda_recurrent_decode"]
+            "kda_chunk_prefill_gated", "kda_chunk_prefill_workspace_bytes", "kda_recurrent_decode"]
 
 
 def _check(status: int):
@@ -117,21 +122,8 @@ def chunk_prefill_workspace_bytes(N: int, H: int, dk: int = 128, dv: int = 128,
     return int(lib().kda_chunk_prefill_workspace_bytes(N, H, dk, dv, chunks_per_pass))
 
 
-def chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
-                  beta: torch.Tensor, cu_seqlens: Optional[torch.Tensor] = None,
-                  initial_state: Optional[torch.Tensor] = None, output_final_state: bool = True,
-                  scale: float = 1.0, o_dtype: Optional[torch.dtype] = None,
-                  out: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
-                  cu_seqlens_host: Optional[torch.Tensor] = None,
-                  workspace: Optional[torch.Tensor] = None,
-                  max_workspace_bytes: int = DEFAULT_WORKSPACE_BYTES):
-    """kda_chunk_prefill on packed [T_tot, H, d] tensors.
-
-    cu_seqlens: int32 [N+1] (device); None means one sequence of length T_tot.
-    workspace: uint8 device tensor; None allocates one that covers the longest
-    sequence in one pass, capped at max_workspace_bytes (at least the minimum).
-    Returns (o [T_tot,H,dv], final_state [N,H,dk,dv] or None).
-    """
+def _prefill_common(q, v, cu_seqlens, cu_seqlens_host, initial_state, output_final_state,
+                    o_dtype, out, final_state, workspace, max_workspace_bytes):
     T, H, dk = q.shape
     dv = v.shape[2]
     dev = q.device
@@ -157,8 +149,55 @@ def chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
         fit = max(1, (max_workspace_bytes - (one - per)) // per) if per > 0 else 1
         nbytes = chunk_prefill_workspace_bytes(N, H, dk, dv, int(min(max_chunks, fit)))
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    return T, H, dk, dv, dev, cu_seqlens, hp, N, out, final_state, workspace
+
+
+def chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                  beta: torch.Tensor, cu_seqlens: Optional[torch.Tensor] = None,
+                  initial_state: Optional[torch.Tensor] = None, output_final_state: bool = True,
+                  scale: float = 1.0, o_dtype: Optional[torch.dtype] = None,
+                  out: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
+                  cu_seqlens_host: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None,
+                  max_workspace_bytes: int = DEFAULT_WORKSPACE_BYTES):
+    """kda_chunk_prefill on packed [T_tot, H, d] tensors.
+
+    cu_seqlens: int32 [N+1] (device); None means one sequence of length T_tot.
+    workspace: uint8 device tensor; None allocates one that covers the longest
+    sequence in one pass, capped at max_workspace_bytes (at least the minimum).
+    Returns (o [T_tot,H,dv], final_state [N,H,dk,dv] or None).
+    """
+    T, H, dk, dv, dev, cu_seqlens, hp, N, out, final_state, workspace = _prefill_common(
+        q, v, cu_seqlens, cu_seqlens_host, initial_state, output_final_state, o_dtype, out,
+        final_state, workspace, max_workspace_bytes)
     st = lib().kda_chunk_prefill(
         _ptr(q), _ptr(k), _ptr(v), _dt(q), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
+        ctypes.cast(hp.data_ptr(), _vp), N, _ptr(initial_state), _ptr(final_state), _ptr(out),
+        _dt(out), T, H, dk, dv, float(scale), _ptr(workspace), workspace.numel(), _stream(dev))
+    _check(st)
+    return out, final_state
+
+
+def chunk_prefill_gated(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, x: torch.Tensor,
+                        b: torch.Tensor, A_log: torch.Tensor, dt_bias: torch.Tensor,
+                        cu_seqlens: Optional[torch.Tensor] = None,
+                        initial_state: Optional[torch.Tensor] = None,
+                        output_final_state: bool = True, scale: float = 1.0,
+                        o_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None,
+                        final_state: Optional[torch.Tensor] = None,
+                        cu_seqlens_host: Optional[torch.Tensor] = None,
+                        workspace: Optional[torch.Tensor] = None,
+                        max_workspace_bytes: int = DEFAULT_WORKSPACE_BYTES):
+    """kda_chunk_prefill_gated: the gate's raw inputs (x [T,H,dk] logits, b [T,H]
+    beta logits, A_log [H], dt_bias [H,dk]) instead of g and beta."""
+    T, H, dk, dv, dev, cu_seqlens, hp, N, out, final_state, workspace = _prefill_common(
+        q, v, cu_seqlens, cu_seqlens_host, initial_state, output_final_state, o_dtype, out,
+        final_state, workspace, max_workspace_bytes)
+    A_log = A_log.contiguous()
+    dt_bias = dt_bias.contiguous()
+    st = lib().kda_chunk_prefill_gated(
+        _ptr(q), _ptr(k), _ptr(v), _dt(q), _ptr(x), _dt(x), _ptr(b), _dt(b), _ptr(A_log),
+        A_log.numel(), _ptr(dt_bias), dt_bias.numel(), _ptr(cu_seqlens),
         ctypes.cast(hp.data_ptr(), _vp), N, _ptr(initial_state), _ptr(final_state), _ptr(out),
         _dt(out), T, H, dk, dv, float(scale), _ptr(workspace), workspace.numel(), _stream(dev))
     _check(st)

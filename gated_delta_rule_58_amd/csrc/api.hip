@@ -78,6 +78,65 @@ kda_status kda_gate(const void* x, kda_dtype x_dt, const void* b, kda_dtype b_dt
                   "kda_gate");
 }
 
+}  // extern "C"
+
+namespace {
+
+// Checks shared by both prefill entry points; `fn` names the caller.
+// decay / decay_al: g (or x) and its alignment; bb / bb_al: beta (or its logits).
+kda_status check_prefill(const char* fn, const void* q, const void* k, const void* v,
+                         kda_dtype qkv_dt, const void* decay, size_t decay_al, const void* bb,
+                         size_t bb_al, const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                         int32_t N, const float* initial_state, const float* final_state,
+                         const void* o, kda_dtype o_dt, int64_t T_tot, int32_t H, int32_t dk,
+                         int32_t dv, float scale, const void* workspace, size_t workspace_bytes) {
+  if (N <= 0 || H <= 0 || T_tot < 0)
+    return fail(KDA_ERR_INVALID_ARG, "%s: need N > 0, H > 0, T_tot >= 0 (got %d, %d, %lld)", fn,
+                N, H, (long long)T_tot);
+  if (!known_dtype(qkv_dt) || !known_dtype(o_dt))
+    return fail(KDA_ERR_DTYPE, "%s: qkv_dt and o_dt must be KDA_F32 or KDA_BF16", fn);
+  if (dk != 128 || dv != 128)
+    return fail(KDA_ERR_UNSUPPORTED, "%s: only dk = dv = 128 is implemented (got %d, %d)", fn,
+                dk, dv);
+  if (!(scale == scale) || scale > 3.0e38f || scale < -3.0e38f)
+    return fail(KDA_ERR_INVALID_ARG, "%s: scale must be finite", fn);
+  if (T_tot > ((int64_t)1 << 31) - 1)
+    return fail(KDA_ERR_UNSUPPORTED, "%s: T_tot must fit in int32", fn);
+  if (!cu_seqlens) return fail(KDA_ERR_INVALID_ARG, "%s: cu_seqlens is NULL", fn);
+  if (cu_seqlens_host) {
+    if (cu_seqlens_host[0] != 0 || cu_seqlens_host[N] != T_tot)
+      return fail(KDA_ERR_SHAPE, "%s: cu_seqlens must start at 0 and end at T_tot = %lld "
+                                 "(got %d .. %d)", fn, (long long)T_tot, cu_seqlens_host[0],
+                  cu_seqlens_host[N]);
+    for (int32_t n = 0; n < N; ++n)
+      if (cu_seqlens_host[n + 1] < cu_seqlens_host[n])
+        return fail(KDA_ERR_SHAPE, "%s: cu_seqlens decreases at index %d", fn, n);
+  }
+  if (T_tot > 0 && (!q || !k || !v || !decay || !bb || !o))
+    return fail(KDA_ERR_INVALID_ARG, "%s: q, k, v, the decay input, beta and o must be non-NULL",
+                fn);
+  const void* ptrs[] = {q, k, v, o, initial_state, final_state};
+  for (const void* p : ptrs)
+    if (p && !aligned(p, 16))
+      return fail(KDA_ERR_ALIGNMENT, "%s: tensors must be 16-byte aligned", fn);
+  if (!aligned(decay, decay_al) || !aligned(bb, bb_al) || !aligned(cu_seqlens, 4))
+    return fail(KDA_ERR_ALIGNMENT, "%s: the decay input must be %zu-byte aligned, beta %zu-byte, "
+                                   "cu_seqlens 4-byte", fn, decay_al, bb_al);
+  const size_t ws_min = kda::chunk_workspace_bytes(N, H, 1);
+  if (!workspace || workspace_bytes < ws_min)
+    return fail(KDA_ERR_WORKSPACE, "%s: need a workspace of at least %zu bytes (got %zu at %p)",
+                fn, ws_min, workspace_bytes, workspace);
+  if (!aligned(workspace, 256))
+    return fail(KDA_ERR_ALIGNMENT, "%s: workspace must be 256-byte aligned", fn);
+  if ((int64_t)N * H > ((int64_t)1 << 24) || H > 16384)
+    return fail(KDA_ERR_UNSUPPORTED, "%s: need H <= 16384 and N*H <= 2^24", fn);
+  return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 kda_status kda_chunk_prefill(const void* q, const void* k, const void* v, kda_dtype qkv_dt,
                              const float* g, const float* beta, const int32_t* cu_seqlens,
                              const int32_t* cu_seqlens_host, int32_t N,
@@ -85,49 +144,54 @@ kda_status kda_chunk_prefill(const void* q, const void* k, const void* v, kda_dt
                              kda_dtype o_dt, int64_t T_tot, int32_t H, int32_t dk,
                              int32_t dv, float scale, void* workspace, size_t workspace_bytes,
                              void* stream) {
-  if (N <= 0 || H <= 0 || T_tot < 0)
-    return fail(KDA_ERR_INVALID_ARG, "kda_chunk_prefill: need N > 0, H > 0, T_tot >= 0 "
-                                     "(got %d, %d, %lld)", N, H, (long long)T_tot);
-  if (!known_dtype(qkv_dt) || !known_dtype(o_dt))
-    return fail(KDA_ERR_DTYPE, "kda_chunk_prefill: qkv_dt and o_dt must be KDA_F32 or KDA_BF16");
-  if (dk != 128 || dv != 128)
-    return fail(KDA_ERR_UNSUPPORTED, "kda_chunk_prefill: only dk = dv = 128 is implemented "
-                                     "(got %d, %d)", dk, dv);
-  if (!(scale == scale) || scale > 3.0e38f || scale < -3.0e38f)
-    return fail(KDA_ERR_INVALID_ARG, "kda_chunk_prefill: scale must be finite");
-  if (T_tot > ((int64_t)1 << 31) - 1)
-    return fail(KDA_ERR_UNSUPPORTED, "kda_chunk_prefill: T_tot must fit in int32");
-  if (!cu_seqlens) return fail(KDA_ERR_INVALID_ARG, "kda_chunk_prefill: cu_seqlens is NULL");
-  if (cu_seqlens_host) {
-    if (cu_seqlens_host[0] != 0 || cu_seqlens_host[N] != T_tot)
-      return fail(KDA_ERR_SHAPE, "kda_chunk_prefill: cu_seqlens must start at 0 and end at "
-                                 "T_tot = %lld (got %d .. %d)", (long long)T_tot,
-                  cu_seqlens_host[0], cu_seqlens_host[N]);
-    for (int32_t n = 0; n < N; ++n)
-      if (cu_seqlens_host[n + 1] < cu_seqlens_host[n])
-        return fail(KDA_ERR_SHAPE, "kda_chunk_prefill: cu_seqlens decreases at index %d", n);
-  }
-  if (T_tot > 0 && (!q || !k || !v || !g || !beta || !o))
-    return fail(KDA_ERR_INVALID_ARG, "kda_chunk_prefill: q, k, v, g, beta and o must be non-NULL");
-  const void* ptrs[] = {q, k, v, g, beta, o, initial_state, final_state, cu_seqlens};
-  for (const void* p : ptrs)
-    if (p && !aligned(p, 16) && p != beta && p != cu_seqlens)
-      return fail(KDA_ERR_ALIGNMENT, "kda_chunk_prefill: tensors must be 16-byte aligned");
-  if (!aligned(beta, 4) || !aligned(cu_seqlens, 4))
-    return fail(KDA_ERR_ALIGNMENT, "kda_chunk_prefill: beta/cu_seqlens must be 4-byte aligned");
-  const size_t ws_min = kda::chunk_workspace_bytes(N, H, 1);
-  if (!workspace || workspace_bytes < ws_min)
-    return fail(KDA_ERR_WORKSPACE, "kda_chunk_prefill: need a workspace of at least %zu bytes "
-                                   "(got %zu at %p)", ws_min, workspace_bytes, workspace);
-  if (!aligned(workspace, 256))
-    return fail(KDA_ERR_ALIGNMENT, "kda_chunk_prefill: workspace must be 256-byte aligned");
-  if ((int64_t)N * H > ((int64_t)1 << 24) || H > 16384)
-    return fail(KDA_ERR_UNSUPPORTED, "kda_chunk_prefill: need H <= 16384 and N*H <= 2^24");
-  return launched(kda::launch_chunk_prefill(q, k, v, qkv_dt == KDA_BF16, g, beta, cu_seqlens,
-                                            cu_seqlens_host, N, initial_state, final_state, o,
-                                            o_dt == KDA_BF16, T_tot, H, scale, workspace,
-                                            workspace_bytes, static_cast<hipStream_t>(stream)),
+  const kda_status st = check_prefill("kda_chunk_prefill", q, k, v, qkv_dt, g, 16, beta, 4,
+                                      cu_seqlens, cu_seqlens_host, N, initial_state, final_state,
+                                      o, o_dt, T_tot, H, dk, dv, scale, workspace,
+                                      workspace_bytes);
+  if (st != KDA_OK) return st;
+  return launched(kda::launch_chunk_prefill(q, k, v, qkv_dt == KDA_BF16, g, 0, beta, false,
+                                            nullptr, nullptr, cu_seqlens, cu_seqlens_host, N,
+                                            initial_state, final_state, o, o_dt == KDA_BF16,
+                                            T_tot, H, scale, workspace, workspace_bytes,
+                                            static_cast<hipStream_t>(stream)),
                   "kda_chunk_prefill");
+}
+
+kda_status kda_chunk_prefill_gated(const void* q, const void* k, const void* v, kda_dtype qkv_dt,
+                                   const void* x, kda_dtype x_dt, const void* b, kda_dtype b_dt,
+                                   const float* A_log, int64_t A_log_len, const float* dt_bias,
+                                   int64_t dt_bias_len, const int32_t* cu_seqlens,
+                                   const int32_t* cu_seqlens_host, int32_t N,
+                                   const float* initial_state, float* final_state, void* o,
+                                   kda_dtype o_dt, int64_t T_tot, int32_t H, int32_t dk,
+                                   int32_t dv, float scale, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  const char* fn = "kda_chunk_prefill_gated";
+  if (!known_dtype(x_dt) || !known_dtype(b_dt))
+    return fail(KDA_ERR_DTYPE, "%s: x_dt and b_dt must be KDA_F32 or KDA_BF16", fn);
+  if (H > 0 && A_log_len != H)
+    return fail(KDA_ERR_SHAPE,
+                "%s: A_log has %lld values but H = %d; A_log must be one value per head "
+                "([H]); a per-channel or checkpoint-shaped A_log is refused, not reshaped",
+                fn, (long long)A_log_len, H);
+  if (H > 0 && dt_bias_len != (int64_t)H * dk)
+    return fail(KDA_ERR_SHAPE, "%s: dt_bias has %lld values, need H*dk = %lld", fn,
+                (long long)dt_bias_len, (long long)H * dk);
+  if (!A_log || !dt_bias) return fail(KDA_ERR_INVALID_ARG, "%s: A_log/dt_bias is NULL", fn);
+  if (!aligned(dt_bias, 16))
+    return fail(KDA_ERR_ALIGNMENT, "%s: dt_bias must be 16-byte aligned", fn);
+  const kda_status st = check_prefill(fn, q, k, v, qkv_dt, x, 16, b, b_dt == KDA_BF16 ? 2 : 4,
+                                      cu_seqlens, cu_seqlens_host, N, initial_state, final_state,
+                                      o, o_dt, T_tot, H, dk, dv, scale, workspace,
+                                      workspace_bytes);
+  if (st != KDA_OK) return st;
+  return launched(kda::launch_chunk_prefill(q, k, v, qkv_dt == KDA_BF16, x,
+                                            x_dt == KDA_BF16 ? 2 : 1, b, b_dt == KDA_BF16, A_log,
+                                            dt_bias, cu_seqlens, cu_seqlens_host, N,
+                                            initial_state, final_state, o, o_dt == KDA_BF16,
+                                            T_tot, H, scale, workspace, workspace_bytes,
+                                            static_cast<hipStream_t>(stream)),
+                  fn);
 }
 
 size_t kda_chunk_prefill_workspace_bytes(int32_t N, int32_t H, int32_t dk, int32_t dv,

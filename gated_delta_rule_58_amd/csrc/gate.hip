@@ -12,38 +12,17 @@
 // consecutive channels of one token: fully coalesced.  beta for the block's
 // (token, head) pairs is one extra pass by one lane per pair.
 //
-// Arithmetic: the softplus tail log1p(exp(-|z|)) uses the hardware exp2/log2
-// with two corrections that keep it within a few ulp of the exact value, where
-// a plain log2(1 + e) would lose up to all of the digits of a small e:
-//   e = 2^(-t) with t = |z| log2(e) rounded; the product's residual (an fma)
-//       and the fp32 constant's own error are folded back in to first order;
-//   log1p(e) = log(u) * e / (u - 1) with u = fl(1 + e) (exact when u = 1).
+// Arithmetic: gate_math.hpp.
+#include "gate_math.hpp"
 #include "kda_device.hpp"
 #include "kda_internal.hpp"
 
 namespace kda {
 namespace {
 
-constexpr float kLog2e = 1.4426950216293335f;     // fp32 nearest of log2(e)
-constexpr float kLog2eLo = 1.92596298909109e-08f;  // log2(e) - kLog2e
-constexpr float kLn2 = 0.6931471824645996f;
-
 constexpr int kThreads = 256;
 constexpr int kTokUnroll = 4;   // x loads in flight per thread
 constexpr int kTokPerBlock = 32;
-
-__device__ __forceinline__ float softplus_tail(float az) {
-  // log1p(exp(-az)) for az = |z| >= 0; beyond 200 the value is below fp32's
-  // range (and an infinite az must not reach the residual product).
-  az = fminf(az, 200.0f);
-  const float t = az * kLog2e;
-  const float r = fmaf(az, kLog2e, -t) + az * kLog2eLo;  // az*log2(e) - t
-  const float e = __builtin_amdgcn_exp2f(-t) * fmaf(-r, kLn2, 1.0f);
-  const float u = 1.0f + e;
-  const float d = u - 1.0f;
-  const float l = __builtin_amdgcn_logf(u) * kLn2 * (e * __builtin_amdgcn_rcpf(d));
-  return d == 0.0f ? e : l;
-}
 
 // 4 consecutive logits as fp32, read once: non-temporal, so the stream of x
 // does not displace the cached lines of g that the prefill reads next.
@@ -87,8 +66,8 @@ __global__ void __launch_bounds__(kThreads) gate_kernel(
           f32x4 out;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float z = xv[u][e] + db[e];
-            out[e] = a * (fmaxf(z, 0.0f) + softplus_tail(fabsf(z)));
+            const float z = gate_input(xv[u][e], db[e]);
+            out[e] = gate_log_decay(a, z);
           }
           *reinterpret_cast<f32x4*>(g + base + (t + u) * tok_stride) = out;
         }
@@ -103,7 +82,7 @@ __global__ void __launch_bounds__(kThreads) gate_kernel(
     const int tk = i / nh;
     const int64_t row = (int64_t)(tok0 + tk) * H + hbase + (i - tk * nh);
     const float bl = load1(b, row, BBF16);
-    beta[row] = 1.0f / (1.0f + expf(-bl));
+    beta[row] = gate_beta(bl);
   }
 }
 

@@ -18,8 +18,12 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, bool qkv_b
                          int N, int H, float scale, hipStream_t s);
 
 // Chunked prefill: prep + state kernel per pass over the chunks (prefill.hip).
+// The decay input is either g (g_mode 0, fp32) with post-sigmoid beta in b,
+// or raw gate logits x (g_mode 1 fp32, 2 bf16) with beta logits in b and the
+// gate parameters A_log [H], dt_bias [H, 128].
 hipError_t launch_chunk_prefill(const void* q, const void* k, const void* v, bool qkv_bf16,
-                                const float* g, const float* beta, const int32_t* cu,
+                                const void* g, int g_mode, const void* b, bool b_bf16,
+                                const float* A_log, const float* dt_bias, const int32_t* cu,
                                 const int32_t* cu_host, int N, const float* S0, float* S_final,
                                 void* o, bool o_bf16, int64_t T_tot, int H, float scale,
                                 void* ws, size_t ws_bytes, hipStream_t s);
@@ -27,9 +31,10 @@ size_t chunk_workspace_bytes(int N, int H, int chunks_per_pass);
 
 namespace chunk {
 // One pass: chunks [c_lo, c_lo + S_len) of every sequence (prep.hip, state.hip).
-hipError_t launch_prep(const void* q, const void* k, bool qkv_bf16, const float* g,
-                       const float* beta, const int32_t* cu, int N, int T_tot, int H, int c_lo,
-                       int S_len, char* ws, hipStream_t s);
+hipError_t launch_prep(const void* q, const void* k, bool qkv_bf16, const void* g, int g_mode,
+                       const void* b, bool b_bf16, const float* A_log, const float* dt_bias,
+                       const int32_t* cu, int N, int T_tot, int H, int c_lo, int S_len, char* ws,
+                       hipStream_t s);
 hipError_t launch_state(const void* v, bool qkv_bf16, const int32_t* cu, int N, int T_tot,
                         int H, const float* S_in, float* S_out, void* o, bool o_bf16,
                         float scale, int c_lo, int S_len, const char* ws, hipStream_t s);

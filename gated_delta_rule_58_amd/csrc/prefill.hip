@@ -19,7 +19,8 @@ size_t chunk_workspace_bytes(int N, int H, int chunks_per_pass) {
 }
 
 hipError_t launch_chunk_prefill(const void* q, const void* k, const void* v, bool qkv_bf16,
-                                const float* g, const float* beta, const int32_t* cu,
+                                const void* g, int g_mode, const void* b, bool b_bf16,
+                                const float* A_log, const float* dt_bias, const int32_t* cu,
                                 const int32_t* cu_host, int N, const float* S0, float* S_final,
                                 void* o, bool o_bf16, int64_t T_tot, int H, float scale,
                                 void* ws, size_t ws_bytes, hipStream_t s) {
@@ -41,8 +42,8 @@ hipError_t launch_chunk_prefill(const void* q, const void* k, const void* v, boo
   const int T = static_cast<int>(T_tot);
   for (int64_t c_lo = 0;; c_lo += S_len) {
     const bool last = c_lo + S_len >= max_nch;
-    hipError_t e = chunk::launch_prep(q, k, qkv_bf16, g, beta, cu, N, T, H, (int)c_lo,
-                                      (int)S_len, images, s);
+    hipError_t e = chunk::launch_prep(q, k, qkv_bf16, g, g_mode, b, b_bf16, A_log, dt_bias, cu,
+                                      N, T, H, (int)c_lo, (int)S_len, images, s);
     if (e != hipSuccess) return e;
     e = chunk::launch_state(v, qkv_bf16, cu, N, T, H, c_lo == 0 ? S0 : carry,
                             last ? S_final : carry, o, o_bf16, scale, (int)c_lo, (int)S_len,

@@ -33,6 +33,7 @@
 // pairs, which keep fp32 range.  Requirement: no channel decays by more than
 // 126 (log2 units) over 8 consecutive tokens.
 #include "chunk_common.hpp"
+#include "gate_math.hpp"
 #include "kda_internal.hpp"
 
 namespace kda {
@@ -76,6 +77,7 @@ __device__ __forceinline__ int rset(int i, int j) { return j == 0 ? i - 1 : (j =
 // v + (v of the lane K rows up, inside each 16-lane row; 0 above the row)
 template <int K>
 __device__ __forceinline__ float add_row_shr(float v) {
+#pragma clang fp contract(off)
   const int s = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x110 + K, 0xf, 0xf,
                                             true);
   return v + __builtin_bit_cast(float, s);
@@ -110,10 +112,20 @@ __device__ __forceinline__ void load_row8(Row8<BF16>& R, __amdgpu_buffer_rsrc_t 
   }
 }
 
-template <bool QKV_BF16>
+// The decay input: log-decay g (fp32), or the raw gate logits x (fp32 or
+// bf16) from which g and beta are formed in registers (gate_math.hpp).
+enum GateIn { kG = 0, kX32 = 1, kX16 = 2 };
+struct GateArgs {
+  const void* b;         // beta logits [T, H] (gated input) or post-sigmoid beta (fp32)
+  bool b_bf16;
+  const float* A_log;    // [H]
+  const float* dt_bias;  // [H, 128]
+};
+
+template <bool QKV_BF16, int GIN>
 __global__ void __launch_bounds__(NTHR, 3) prep_kernel(
-    const void* __restrict__ q, const void* __restrict__ k, const float* __restrict__ g,
-    const float* __restrict__ beta, const int32_t* __restrict__ cu, int T_tot, int H, int Hp,
+    const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ g,
+    GateArgs ga, const int32_t* __restrict__ cu, int T_tot, int H, int Hp,
     int c_lo, int S_len, char* __restrict__ ws) {
   __shared__ __attribute__((aligned(16))) char lds[PrepLds::total];
   char* Rb = lds + PrepLds::off_R;
@@ -163,22 +175,52 @@ __global__ void __launch_bounds__(NTHR, 3) prep_kernel(
   // ---- loads: row r, channels 32kk + 8lg .. +7
   f32x4 graw[4][2];
   {
-    const auto rg = buf_tok(g, 4);
     typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    if constexpr (GIN == kX16) {
+      const auto rg = buf_tok(g, 2);
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
+      for (int kk = 0; kk < 4; ++kk) {
+        const u16x8 x8 = __builtin_bit_cast(
+            u16x8, __builtin_amdgcn_raw_buffer_load_b128(rg, r * HD * 2 + (32 * kk + 8 * lg) * 2, 0, 0));
 #pragma unroll
-      for (int a = 0; a < 2; ++a)
-        graw[kk][a] = __builtin_bit_cast(
-            f32x4, __builtin_amdgcn_raw_buffer_load_b128(rg, r * HD * 4 + (32 * kk + 8 * lg + 4 * a) * 4, 0, 0));
+        for (int e = 0; e < 8; ++e) graw[kk][e >> 2][e & 3] = bf16_bits_to_f32(x8[e]);
+      }
+    } else {
+      const auto rg = buf_tok(g, 4);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+          graw[kk][a] = __builtin_bit_cast(
+              f32x4, __builtin_amdgcn_raw_buffer_load_b128(rg, r * HD * 4 + (32 * kk + 8 * lg + 4 * a) * 4, 0, 0));
+    }
   }
   Row8<QKV_BF16> kv8, qv8;
   load_row8<QKV_BF16>(kv8, buf_tok(k, QS), (r * HD + 8 * lg) * QS);
   load_row8<QKV_BF16>(qv8, buf_tok(q, QS), (r * HD + 8 * lg) * QS);
   float bval;
   {
-    const char* bb = reinterpret_cast<const char*>(beta) + ((int64_t)t0 * H + h) * 4;
-    bval = buf_f32(make_buf(bb, (uint32_t)(Lc * H * 4 - h * 4)), r * H * 4);
+    const int bs = (GIN != kG && ga.b_bf16) ? 2 : 4;
+    const char* bb = static_cast<const char*>(ga.b) + ((int64_t)t0 * H + h) * bs;
+    const auto rb = make_buf(bb, (uint32_t)(Lc * H * bs - h * bs));
+    if (bs == 2) bval = bf16_bits_to_f32((uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rb, r * H * 2, 0, 0));
+    else bval = buf_f32(rb, r * H * 4);
+  }
+  if constexpr (GIN != kG) {
+    // g = -exp(A_log[h]) softplus(x + dt_bias[h, c]), beta = sigmoid(b); rows
+    // past the chunk end get g = 0 and beta = 0, as the loaded inputs would
+    const float neg_a = -expf(ga.A_log[h]);
+    const bool live = r < Lc;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int a = 0; a < 2; ++a) {
+        const f32x4 db = *reinterpret_cast<const f32x4*>(ga.dt_bias + h * D + 32 * kk + 8 * lg + 4 * a);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          graw[kk][a][j] = live ? gate_log_decay(neg_a, gate_input(graw[kk][a][j], db[j])) : 0.0f;
+      }
+    bval = live ? gate_beta(bval) : 0.0f;
   }
 
   // ================= S1: gamma (log2 units), in-block scan down the 16 rows
@@ -187,6 +229,8 @@ __global__ void __launch_bounds__(NTHR, 3) prep_kernel(
   for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
+      // no multiply-add contraction: gamma must not depend on where g came from
+#pragma clang fp contract(off)
       float x = graw[kk][e >> 2][e & 3] * LOG2E;
       x = add_row_shr<1>(x);
       x = add_row_shr<2>(x);
@@ -479,19 +523,28 @@ __global__ void __launch_bounds__(NTHR, 3) prep_kernel(
 
 }  // namespace
 
-hipError_t launch_prep(const void* q, const void* k, bool qkv_bf16, const float* g,
-                       const float* beta, const int32_t* cu, int N, int T_tot, int H, int c_lo,
-                       int S_len, char* ws, hipStream_t s) {
+hipError_t launch_prep(const void* q, const void* k, bool qkv_bf16, const void* g, int g_mode,
+                       const void* b, bool b_bf16, const float* A_log, const float* dt_bias,
+                       const int32_t* cu, int N, int T_tot, int H, int c_lo, int S_len, char* ws,
+                       hipStream_t s) {
   const int Hp = (H + 7) & ~7;
   const int64_t blocks = (int64_t)N * S_len * Hp;
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  if (qkv_bf16)
-    prep_kernel<true><<<dim3((unsigned)blocks), NTHR, 0, s>>>(q, k, g, beta, cu, T_tot, H, Hp,
-                                                              c_lo, S_len, ws);
-  else
-    prep_kernel<false><<<dim3((unsigned)blocks), NTHR, 0, s>>>(q, k, g, beta, cu, T_tot, H, Hp,
-                                                               c_lo, S_len, ws);
+  const GateArgs ga{b, b_bf16, A_log, dt_bias};
+  const dim3 grid((unsigned)blocks);
+#define KDA_PREP(QB, GM) \
+  prep_kernel<QB, GM><<<grid, NTHR, 0, s>>>(q, k, g, ga, cu, T_tot, H, Hp, c_lo, S_len, ws)
+  if (qkv_bf16) {
+    if (g_mode == kG) KDA_PREP(true, kG);
+    else if (g_mode == kX32) KDA_PREP(true, kX32);
+    else KDA_PREP(true, kX16);
+  } else {
+    if (g_mode == kG) KDA_PREP(false, kG);
+    else if (g_mode == kX32) KDA_PREP(false, kX32);
+    else KDA_PREP(false, kX16);
+  }
+#undef KDA_PREP
   return hipGetLastError();
 }
 

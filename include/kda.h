@@ -142,6 +142,29 @@ kda_status kda_chunk_prefill(const void* q, const void* k, const void* v, kda_dt
                              void* stream);
 
 /*
+ * kda_chunk_prefill_gated - kda_gate fused into kda_chunk_prefill.
+ *
+ * The same recurrence, outputs, workspace and rules as kda_chunk_prefill,
+ * but the decay and beta come as the gate's raw inputs (the arguments of
+ * kda_gate): x [T_tot, H, dk] gate logits (x_dt KDA_F32 or KDA_BF16), b
+ * [T_tot, H] beta logits (b_dt), A_log [H], dt_bias [H, dk].  g and beta are
+ * formed in registers by the same arithmetic as kda_gate, so the result is
+ * bit-identical to kda_gate followed by kda_chunk_prefill; g never goes to
+ * memory.  FlashKDA's interface (Kimi K3 artifact audit, §7.1) likewise
+ * takes the gate's inputs.  Refusals: those of kda_gate for A_log /
+ * dt_bias, then those of kda_chunk_prefill; x must be 16-byte aligned.
+ */
+kda_status kda_chunk_prefill_gated(const void* q, const void* k, const void* v, kda_dtype qkv_dt,
+                                   const void* x, kda_dtype x_dt, const void* b, kda_dtype b_dt,
+                                   const float* A_log, int64_t A_log_len, const float* dt_bias,
+                                   int64_t dt_bias_len, const int32_t* cu_seqlens,
+                                   const int32_t* cu_seqlens_host, int32_t N,
+                                   const float* initial_state, float* final_state, void* o,
+                                   kda_dtype o_dt, int64_t T_tot, int32_t H, int32_t dk,
+                                   int32_t dv, float scale, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+/*
  * kda_chunk_prefill_workspace_bytes - workspace size for kda_chunk_prefill
  * processing up to chunks_per_pass chunks (of 64 tokens) of every sequence per
  * pass: a state carry of N*H*dk*dv*4 bytes plus N*H*chunks_per_pass images

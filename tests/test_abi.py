@@ -29,7 +29,8 @@ def test_exports_every_declared_symbol():
     L = _lib()
     names = _declared()
     assert set(names) == {"kda_last_error", "kda_version", "kda_gate", "kda_chunk_prefill",
-                          "kda_chunk_prefill_workspace_bytes", "kda_recurrent_decode"}
+                          "kda_chunk_prefill_gated", "kda_chunk_prefill_workspace_bytes",
+                          "kda_recurrent_decode"}
     for n in names:
         assert hasattr(L, n), n
     assert L.kda_version().decode().startswith("kda-gfx950")
@@ -104,6 +105,40 @@ def test_prefill_workspace_contract():
     assert _prefill(L, [0, 20, 48], ws_bytes=need - 1) == 6
     assert b"workspace" in L.kda_last_error()
     assert _prefill(L, [0, 20, 48], ws=DEV[8] + 16, ws_bytes=need) == 5
+
+
+def _prefill_gated(L, cu_host, **kw):
+    a = dict(q=DEV[0], k=DEV[1], v=DEV[2], qkv_dt=1, x=DEV[3], x_dt=0, b=DEV[4], b_dt=0,
+             A_log=DEV[9], A_log_len=4, dt_bias=DEV[10], dt_bias_len=4 * 128, cu=DEV[5], N=2,
+             S0=None, Sf=DEV[6], o=DEV[7], o_dt=1, T=48, H=4, dk=128, dv=128, scale=1.0,
+             ws=DEV[8], ws_bytes=1 << 30)
+    a.update(kw)
+    hp = None if cu_host is None else np.ascontiguousarray(np.asarray(cu_host, dtype=np.int32))
+    return L.kda_chunk_prefill_gated(
+        a["q"], a["k"], a["v"], a["qkv_dt"], a["x"], a["x_dt"], a["b"], a["b_dt"], a["A_log"],
+        a["A_log_len"], a["dt_bias"], a["dt_bias_len"], a["cu"],
+        None if hp is None else hp.ctypes.data, a["N"], a["S0"], a["Sf"], a["o"], a["o_dt"],
+        a["T"], a["H"], a["dk"], a["dv"], a["scale"], a["ws"], a["ws_bytes"], None)
+
+
+def test_prefill_gated_refusals():
+    """The gated prefill refuses what kda_gate refuses (checkpoint-shaped A_log,
+    dt_bias of the wrong size, unknown logit dtype) and what kda_chunk_prefill
+    refuses, before any HIP call."""
+    L = _lib()
+    cu = [0, 20, 48]
+    assert _prefill_gated(L, cu, A_log_len=128) == 2
+    assert b"A_log" in L.kda_last_error()
+    assert _prefill_gated(L, cu, dt_bias_len=4 * 128 + 1) == 2
+    assert _prefill_gated(L, cu, x_dt=7) == 3
+    assert _prefill_gated(L, cu, A_log=None) == 1
+    assert _prefill_gated(L, cu, x=DEV[3] + 8) == 5
+    assert _prefill_gated(L, cu, dt_bias=DEV[10] + 4) == 5
+    assert _prefill_gated(L, cu, b=DEV[4] + 2) == 5              # fp32 beta logits: 4-byte
+    assert _prefill_gated(L, cu, dk=64, dt_bias_len=4 * 64) == 4
+    assert _prefill_gated(L, [0, 30, 20], T=20) == 2
+    assert _prefill_gated(L, cu, ws=None) == 6
+    assert b"kda_chunk_prefill_gated" in L.kda_last_error()
 
 
 def test_decode_refusals():

@@ -229,3 +229,52 @@ def test_multi_pass_workspace():
     o_ref, S_ref = oracle.prefill(dr.q, dr.k, dr.v, g, beta, cu_h, dr.initial_state)
     assert_out(o1, o_ref, "multi-pass")
     assert_state(S1, S_ref, "multi-pass")
+
+
+@pytest.mark.parametrize("xdt", [torch.float32, torch.bfloat16])
+def test_gated_equals_gate_then_prefill(xdt):
+    """kda_chunk_prefill_gated is bit-identical to kda_gate followed by
+    kda_chunk_prefill (varlen with empty and one-token sequences, initial
+    state, scale), and matches the oracle gate followed by the oracle
+    recurrence."""
+    need_gpu()
+    dr = draw_prefill([200, 0, 64, 1, 77], H=3, dtype=torch.bfloat16, init_state=True, seed=61)
+    say("gated prefill vs gate + prefill", xdt)
+    x, b = dr.x.to(xdt), dr.b.to(xdt)
+    q, k, v = dr.q.to(DEV), dr.k.to(DEV), dr.v.to(DEV)
+    xd, bd, A, dtb = x.to(DEV), b.to(DEV), dr.A_log.to(DEV), dr.dt_bias.to(DEV)
+    cu_h = dr.cu_seqlens
+    cu = cu_h.to(DEV)
+    S0 = dr.initial_state.to(DEV)
+    g, beta = kda.gate(xd, bd, A, dtb)
+    o1, S1 = kda.chunk_prefill(q, k, v, g, beta, cu, S0, cu_seqlens_host=cu_h, scale=0.7,
+                               o_dtype=torch.float32)
+    o2, S2 = kda.chunk_prefill_gated(q, k, v, xd, bd, A, dtb, cu, S0, cu_seqlens_host=cu_h,
+                                     scale=0.7, o_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+    gr, br = oracle.gate(x.float(), b.float(), dr.A_log, dr.dt_bias)
+    o_ref, S_ref = oracle.prefill(dr.q, dr.k, dr.v, gr, br, cu_h, dr.initial_state, scale=0.7)
+    assert_out(o2, o_ref, "gated")
+    assert_state(S2, S_ref, "gated")
+
+
+def test_config1_gated_full_sampled_heads():
+    """The benchmarked call: K3-layer prefill T=4096 H=96 from the raw gate
+    logits, bf16 o, sampled heads against the oracle gate and recurrence."""
+    need_gpu()
+    c = CONFIGS[1]
+    say("full config 1 gated, sampled heads")
+    dr = draw_config(1, device=DEV)
+    cu_h = dr.cu_seqlens
+    o, S = kda.chunk_prefill_gated(dr.q, dr.k, dr.v, dr.x, dr.b, dr.A_log, dr.dt_bias,
+                                   cu_h.to(DEV), dr.initial_state, cu_seqlens_host=cu_h,
+                                   o_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    heads = sample_heads(c["H"], 6, 11)
+    gr, br = oracle_gate_f64(dr, heads)
+    o_ref, S_ref = oracle.prefill(dr.q[:, heads].cpu(), dr.k[:, heads].cpu(),
+                                  dr.v[:, heads].cpu(), gr, br, cu_h, None)
+    eo = assert_out_bf16(o[:, heads], o_ref, "config 1 gated")
+    es = assert_state(S[:, heads], S_ref, "config 1 gated")
+    say("  bf16-o err ratio %.3f  state err %.3e" % (eo, es))
