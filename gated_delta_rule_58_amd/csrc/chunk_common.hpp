@@ -10,7 +10,7 @@
 //   A[r,s] = b_r sum_c k_rc k_sc e^(gamma_rc - gamma_sc)   (s < r)
 //   P[r,s] =     sum_c q_rc k_sc e^(gamma_rc - gamma_sc)   (s <= r)
 //   X      = V - (K * e^gamma) S
-//   (I + A) Delta = diag(b) X
+//   Delta  = (I + A)^-1 diag(b) X
 //   O      = scale * ((Q * e^gamma) S + P Delta)
 //   S     <- Diag(e^gamma_C) S + (K * e^(gamma_C - gamma))^T Delta
 // Everything left of the state is fixed by the chunk's own inputs; the prep
@@ -119,11 +119,10 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0f70)
 //           16t + lr, tokens 32ks + 4lg .. +3 then 32ks + 16 + 4lg .. +3.
 //   PM      fp16 P, ten 16x16 tiles (i, j <= i) at index i(i+1)/2 + j; unit
 //           16 lg + lr holds row lr, columns 4lg .. +3 of the tile.
-//   AT      fp16 the same ten tiles of the triangular system: T_ii =
-//           (I + A_ii)^-1 on the diagonal, -A_ij (beta folded into the rows)
-//           below it.
+//   AT      fp16 the same ten tiles of (I + A)^-1 diag(b), the lower
+//           triangular matrix that maps X to Delta (columns past the chunk end
+//           are 0).
 //   EC      fp32 [128]: e^gamma_C per key channel.
-//   BETA    fp32 [64]: beta of the chunk rows (0 past the chunk end).
 struct Ws {
   static constexpr int KE = 0;
   static constexpr int QE = KE + C * D * 2;
@@ -131,8 +130,7 @@ struct Ws {
   static constexpr int PM = KDT + D * C * 2;
   static constexpr int AT = PM + 10 * 512;
   static constexpr int EC = AT + 10 * 512;
-  static constexpr int BETA = EC + D * 4;
-  static constexpr int used = BETA + C * 4;
+  static constexpr int used = EC + D * 4;
   static constexpr int bytes = ((used + 1023) / 1024) * 1024;  // copied in 1 KiB rounds
 };
 static_assert(Ws::bytes == 59 * 1024, "workspace image size");

@@ -3,9 +3,8 @@
 //
 // One workgroup (4 waves) per (chunk, head).  It writes that chunk's
 // workspace image (layout in chunk_common.hpp): K e^gamma, Q e^gamma,
-// (K e^(gamma_C - gamma))^T, the decay-weighted P, the diagonal-block
-// inverses T_ii with the off-diagonal blocks -A_ij of the triangular system
-// (I + A) Delta = diag(beta) X, e^gamma_C and beta.
+// (K e^(gamma_C - gamma))^T, the decay-weighted P, the lower triangular
+// (I + A)^-1 diag(beta) that maps X to Delta, and e^gamma_C.
 //
 // Wave i owns chunk rows 16i..16i+15 (block i); lane (lr, lg) owns row
 // 16i + lr and, in k-step kk, the 8 consecutive channels 32kk + 8lg + e.
@@ -18,6 +17,8 @@
 //      off-diagonal factors (LDS), the diagonal tiles A_ii and P_ii, and
 //      T_ii = (I + A_ii)^-1 by repeated squaring.
 //  P2  off-diagonal tiles (i, j < i) of A and P, two per wave at most.
+//  P3  the blocks of (I + A)^-1 below the diagonal, by forward substitution
+//      down each block column (one column per wave), from T_ii and -A_ij.
 //
 // Decay factors.  gamma is kept in log2 units and every exponential is a
 // hardware exp2.  Inside a chunk gamma can fall far below -126, so factors
@@ -32,6 +33,8 @@
 // when every |gamma_r - gamma_m| of the block is <= 7, otherwise hi+lo bf16
 // pairs, which keep fp32 range.  Requirement: no channel decays by more than
 // 126 (log2 units) over 8 consecutive tokens.
+#include <type_traits>
+
 #include "chunk_common.hpp"
 #include "gate_math.hpp"
 #include "kda_internal.hpp"
@@ -305,6 +308,39 @@ __global__ void __launch_bounds__(NTHR, 3) prep_kernel(
   }
   __syncthreads();
 
+  // 16x16 tile helpers (one wave): accumulator layout (rows 4lg+i, column lr)
+  // -> operand layout (row lr, columns 4lg+e) through the wave's LDS scratch,
+  // and the 16x16x16 product of an operand-layout left factor (one fp16) with
+  // an accumulator-layout right factor (hi+lo fp16), added to acc.
+  auto to_a = [&](const f32x4& xb) -> f32x4 {
+    wave_lds_sync();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) scr[(4 * lg + i) * PrepLds::SC_LD + lr] = xb[i];
+    wave_lds_sync();
+    f32x4 x;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = scr[lr * PrepLds::SC_LD + 4 * lg + e];
+    return x;
+  };
+  auto mac16 = [&](const f16x4& a, const f32x4& yb, f32x4 acc) -> f32x4 {
+    f16x4 bh, bl;
+    bfrag16_split(yb, bh, bl);
+    acc = mma_f16_k16(a, bh, acc);
+    return mma_f16_k16(a, bl, acc);
+  };
+  auto mul = [&](const f32x4& xa, const f32x4& yb) -> f32x4 {
+    f16x4 a;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) a[e] = static_cast<_Float16>(xa[e]);
+    return mac16(a, yb, f32x4{0.f, 0.f, 0.f, 0.f});
+  };
+  // P3 operands: fp32 T_ii tiles (row-major, over the block sums, dead since
+  // S2) and fp16 N_ij = -A_ij tiles (row-major, over constant slots 0..5, dead
+  // after P1)
+  float* Tt = btot;
+  _Float16* Nt = reinterpret_cast<_Float16*>(cst);
+  auto n_tile = [](int i, int j) { return ((i * (i - 1)) >> 1) + j; };
+
   // ================= P1: per 32-channel step kk: decay factors, the image's
   // K e^gamma, Q e^gamma and transposed decayed K, the right factors of the
   // tiles below this block (LDS), this block's left factors (registers; LDS
@@ -432,24 +468,6 @@ __global__ void __launch_bounds__(NTHR, 3) prep_kernel(
     // N^16 = 0.  Products are 16x16x16 MFMAs: the left factor is read in operand
     // layout through a wave-private LDS transpose, the right factor is an
     // accumulator (hi+lo fp16).
-    auto to_a = [&](const f32x4& xb) -> f32x4 {  // accumulator layout -> A-operand layout
-      wave_lds_sync();
-#pragma unroll
-      for (int i = 0; i < 4; ++i) scr[(4 * lg + i) * PrepLds::SC_LD + lr] = xb[i];
-      wave_lds_sync();
-      f32x4 x;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) x[e] = scr[lr * PrepLds::SC_LD + 4 * lg + e];
-      return x;
-    };
-    auto mul = [&](const f32x4& xa, const f32x4& yb) -> f32x4 {
-      f16x4 a, bh, bl;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) a[e] = static_cast<_Float16>(xa[e]);
-      bfrag16_split(yb, bh, bl);
-      f32x4 d = mma_f16_k16(a, bh, f32x4{0.f, 0.f, 0.f, 0.f});
-      return mma_f16_k16(a, bl, d);
-    };
     f32x4 eye;
 #pragma unroll
     for (int i = 0; i < 4; ++i) eye[i] = (4 * lg + i == lr) ? 1.0f : 0.0f;  // same in both layouts
@@ -460,8 +478,11 @@ __global__ void __launch_bounds__(NTHR, 3) prep_kernel(
     const f32x4 m2B = mul(eye - nA, eye + n2B);
     const f32x4 m3B = mul(to_a(m2B), eye + n4B);
     const f32x4 tA = to_a(mul(to_a(m3B), eye + n8B));  // row lr, columns 4lg + e
-    const f16x4 td = {static_cast<_Float16>(tA[0]), static_cast<_Float16>(tA[1]),
-                      static_cast<_Float16>(tA[2]), static_cast<_Float16>(tA[3])};
+    // fp32 T_ii for the blocks below the diagonal; the image gets T_ii diag(beta)
+    *reinterpret_cast<f32x4*>(Tt + bi * 256 + lr * 16 + 4 * lg) = tA;
+    const f32x4 bc = *reinterpret_cast<const f32x4*>(s_beta + 16 * bi + 4 * lg);
+    const f16x4 td = {static_cast<_Float16>(tA[0] * bc[0]), static_cast<_Float16>(tA[1] * bc[1]),
+                      static_cast<_Float16>(tA[2] * bc[2]), static_cast<_Float16>(tA[3] * bc[3])};
     *reinterpret_cast<f16x4*>(img + Ws::AT + tri_at(bi, bi, lr, lg)) = td;
   }
   __syncthreads();
@@ -493,7 +514,7 @@ __global__ void __launch_bounds__(NTHR, 3) prep_kernel(
                         static_cast<_Float16>(nb * aA[2]), static_cast<_Float16>(nb * aA[3])};
       const f16x4 pd = {static_cast<_Float16>(aP[0]), static_cast<_Float16>(aP[1]),
                         static_cast<_Float16>(aP[2]), static_cast<_Float16>(aP[3])};
-      *reinterpret_cast<f16x4*>(img + Ws::AT + tri_at(ti, tj, lr, lg)) = ad;
+      *reinterpret_cast<f16x4*>(Nt + n_tile(ti, tj) * 256 + lr * 16 + 4 * lg) = ad;
       *reinterpret_cast<f16x4*>(img + Ws::PM + tri_at(ti, tj, lr, lg)) = pd;
     };
     if (bi == 0) {
@@ -509,15 +530,42 @@ __global__ void __launch_bounds__(NTHR, 3) prep_kernel(
     }
   }
 
-  // ---- EC and BETA
+  __syncthreads();
+
+  // ================= P3: the blocks of T = (I + A)^-1 below the diagonal.  Column
+  // block j is a forward substitution down the column: T_ij = T_ii sum_{k=j}^{i-1}
+  // N_ik T_kj for i > j.  Wave j < 3 takes column j; the image gets T_ij
+  // diag(beta_j), so that the state kernel's Delta = (T diag(beta)) X needs no
+  // substitution of its own.
+  auto column = [&](auto J) {
+    constexpr int j = decltype(J)::value;
+    f32x4 X[4];  // X[k] = T_kj, accumulator layout
+#pragma unroll
+    for (int i = 0; i < 4; ++i) X[j][i] = Tt[j * 256 + (4 * lg + i) * 16 + lr];
+    const float bcol = s_beta[16 * j + lr];
+#pragma unroll
+    for (int i = j + 1; i < 4; ++i) {
+      f32x4 y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = j; kb < i; ++kb)
+        y = mac16(*reinterpret_cast<const f16x4*>(Nt + n_tile(i, kb) * 256 + lr * 16 + 4 * lg), X[kb], y);
+      X[i] = mul(*reinterpret_cast<const f32x4*>(Tt + i * 256 + lr * 16 + 4 * lg), y);
+      const f32x4 xa = to_a(X[i] * bcol);  // row lr, columns 4lg + e
+      const f16x4 td = {static_cast<_Float16>(xa[0]), static_cast<_Float16>(xa[1]),
+                        static_cast<_Float16>(xa[2]), static_cast<_Float16>(xa[3])};
+      *reinterpret_cast<f16x4*>(img + Ws::AT + tri_at(i, j, lr, lg)) = td;
+    }
+  };
+  if (w == 0) column(std::integral_constant<int, 0>{});
+  else if (w == 1) column(std::integral_constant<int, 1>{});
+  else if (w == 2) column(std::integral_constant<int, 2>{});
+
+  // ---- EC
   {
     typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-    if (tid < 32)
-      *reinterpret_cast<u32x4*>(img + Ws::EC + 16 * tid) =
-          *reinterpret_cast<const u32x4*>(cst + 13 * D + 4 * tid);
-    else if (tid < 48)
-      *reinterpret_cast<u32x4*>(img + Ws::BETA + 16 * (tid - 32)) =
-          *reinterpret_cast<const u32x4*>(s_beta + 4 * (tid - 32));
+    if (w == 3 && lane < 32)
+      *reinterpret_cast<u32x4*>(img + Ws::EC + 16 * lane) =
+          *reinterpret_cast<const u32x4*>(cst + 13 * D + 4 * lane);
   }
 }
 

@@ -4,7 +4,7 @@
 // chunks of its sequence in order.  Per chunk, with the chunk's workspace
 // image (written by the prep kernel) in LDS:
 //   X     = V - (K e^gamma) S                      (S the entry state)
-//   Delta_i = T_ii (b_i X_i - sum_{j<i} A_ij Delta_j)   16-row blocks i
+//   Delta = (I + A)^-1 diag(b) X                   (the prep kernel inverts)
 //   O     = scale ((Q e^gamma) S + P Delta)
 //   S    <- Diag(e^gamma_C) S + (K e^(gamma_C - gamma))^T Delta
 //
@@ -15,16 +15,18 @@
 // column lr in lane (lr, lg); a pair of them is the B fragment of a 16x16x32
 // product (contraction index 16(e>>2) + 4lg + (e&3)) and, unchanged, the A
 // fragment of the transposed product, so S and Delta never leave their
-// registers.  The image operands are read in the matching order.  The block
-// forward substitution for Delta uses 16x16x16 products.
+// registers.  The image operands are read in the matching order.
 // The output is computed transposed, O^T = S^T (Q e^gamma)^T + Delta^T P^T:
 // the same fragments with the operands swapped, so each lane ends up with four
 // consecutive columns of one token row.
 //
-// Wave 4 moves data.  While chunk c is computed it stores chunk c-1's output
-// tile from LDS to o and copies chunk c+1's image (60 KiB) and v tile into
-// the other LDS buffers with 16-byte buffer-to-LDS loads, so the compute
-// waves never wait on a memory instruction.  One workgroup barrier per chunk.  (fp32 v or o, used only
+// Waves 4 and 5 move data.  While chunk c is computed they store chunk c-1's
+// output tile from LDS to o and copy chunk c+1's image (59 KiB) and v tile
+// into the other LDS buffers with 16-byte buffer-to-LDS loads, so the compute
+// waves never wait on a memory instruction.  The copy is split over two waves
+// so that neither has more memory instructions in flight than its counter
+// holds (63): one wave issuing all 75 of them stalls on its own first loads.
+// One workgroup barrier per chunk.  (fp32 v or o, used only
 // off the benchmarked path, go through the compute waves' registers instead.)
 //
 // Precision: operands are fp16 MFMA fragments with fp32 accumulation; X and
@@ -39,7 +41,9 @@ namespace {
 
 constexpr int DV = 64;  // value columns per workgroup
 constexpr int NT = D / DV;
-constexpr int NTHR_S = NTHR + 64;  // 4 compute waves + 1 data wave
+constexpr int NTHR_S = NTHR + 128;  // 4 compute waves + 2 data waves
+constexpr int IMG_UNITS = Ws::bytes / 1024;
+constexpr int IMG_SPLIT = (IMG_UNITS + 1) / 2;  // image units copied by data wave 4
 constexpr int TILE_BYTES = C * DV * 2;  // bf16 v or o tile of one chunk
 
 struct StateLds {
@@ -77,7 +81,7 @@ __global__ void __launch_bounds__(NTHR_S, 1) state_kernel(
   const int lane = tid & 63;
   const int lr = lane & 15;
   const int lg = lane >> 4;
-  const bool mover = w == 4;
+  const bool mover = w >= 4;
 
   // ---- block -> (sequence rank, head, value tile); head % 8 == block % 8 so
   // both tiles of a head, and the prep blocks of its chunks, share one XCD.
@@ -112,14 +116,18 @@ __global__ void __launch_bounds__(NTHR_S, 1) state_kernel(
     return make_buf(b, (uint32_t)(rows_of(c) * HD * esz - (h * D + col0) * esz));
   };
 
-  // ---- data wave: image and v tile of chunk c into LDS; o tile of chunk c out
+  // ---- data waves: image and v tile of chunk c into LDS; o tile of chunk c
+  // out.  Wave 4 copies image units [0, IMG_SPLIT), wave 5 the rest of the
+  // image and the v tile; each stores half of the o tile.
   auto load_chunk = [&](int c) {
     const char* src = ws + ((int64_t)(n * S_len + (c - c_lo)) * H + h) * Ws::bytes;
     const auto rs = make_buf(src, Ws::bytes);
     char* dst = img_of(c);
-#pragma unroll 4
-    for (int u = 0; u < Ws::bytes / 1024; ++u)
+    const int u0 = w == 4 ? 0 : IMG_SPLIT, u1 = w == 4 ? IMG_SPLIT : IMG_UNITS;
+#pragma unroll 2
+    for (int u = u0; u < u1; ++u)
       buf_to_lds16(rs, (lds_ptr_t)(dst + u * 1024), lane * 16, u * 1024);
+    if (w == 4) return;
     if constexpr (QKV_BF16) {  // 8 rows of 128 bytes per round; lane writes slot lane&7
       const auto rv = tok_buf(v, 2, c);
       char* vt = vt_of(c);
@@ -132,12 +140,12 @@ __global__ void __launch_bounds__(NTHR_S, 1) state_kernel(
       }
     }
   };
-  auto store_o = [&](int c) {
+  auto store_o = [&](int c) {  // rows [32(w-4), 32(w-4) + 32) of the tile
     const auto ro = tok_buf(o, 2, c);
     const char* ot = ot_of(c);
     typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 4 * (w - 4); u < 4 * (w - 4) + 4; ++u) {
       const int r = 8 * u + (lane >> 3);
       const int j = (lane & 7) ^ otile_swz(r);  // logical chunk held by slot lane&7
       const u32x4 x = *reinterpret_cast<const u32x4*>(ot + r * 128 + (lane & 7) * 16);
@@ -183,10 +191,11 @@ __global__ void __launch_bounds__(NTHR_S, 1) state_kernel(
   for (int c = c_lo; c < c_end; ++c) {
     const bool more = c + 1 < c_end;
     if (mover) {
+      // loads first: the image has the whole chunk to arrive
+      if (more) load_chunk(c + 1);
       if constexpr (O_BF16) {
         if (c > c_lo) store_o(c - 1);
       }
-      if (more) load_chunk(c + 1);
       wait_vmem();
     } else {
       const char* im = img_of(c);
@@ -232,27 +241,28 @@ __global__ void __launch_bounds__(NTHR_S, 1) state_kernel(
       for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) Xacc[rt][i] = vcur[4 * rt + i] - Xacc[rt][i];
-      // -- Delta_i = T_ii (b_i X_i - sum_{j<i} A_ij Delta_j), 16-row blocks
-      const float* bet = reinterpret_cast<const float*>(im + Ws::BETA);
+      // -- Delta = (T diag(b)) X, T = (I + A)^-1 lower triangular: row block
+      // rt sums the X block pairs ks with 2ks <= rt (the tile (rt, 2ks+1) above
+      // the diagonal is 0); four independent chains of at most four products.
+      f16x8 xh[2], xl[2];  // X block pairs as hi+lo fragments
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) bfrag_split(Xacc[2 * ks], Xacc[2 * ks + 1], xh[ks], xl[ks]);
       f32x4 Dacc[4];
 #pragma unroll
-      for (int bi4 = 0; bi4 < 4; ++bi4) {
-        const f32x4 bb = *reinterpret_cast<const f32x4*>(bet + 16 * bi4 + 4 * lg);
-        f32x4 acc = bb * Xacc[bi4];
+      for (int rt = 0; rt < 4; ++rt) {
+        f32x4 d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int bj4 = 0; bj4 < 3; ++bj4) {
-          if (bj4 >= bi4) continue;
-          const f16x4 na = *reinterpret_cast<const f16x4*>(im + Ws::AT + tri_at(bi4, bj4, lr, lg));
-          f16x4 dh, dl;
-          bfrag16_split(Dacc[bj4], dh, dl);
-          acc = mma_f16_k16(na, dh, acc);
-          acc = mma_f16_k16(na, dl, acc);
+        for (int ks = 0; ks < 2; ++ks) {
+          if (2 * ks > rt) continue;
+          const f16x4 t0 = *reinterpret_cast<const f16x4*>(im + Ws::AT + tri_at(rt, 2 * ks, lr, lg));
+          f16x4 t1 = {0, 0, 0, 0};
+          if (2 * ks + 1 <= rt)
+            t1 = *reinterpret_cast<const f16x4*>(im + Ws::AT + tri_at(rt, 2 * ks + 1, lr, lg));
+          const f16x8 ta = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
+          d = mma_f16(ta, xh[ks], d);
+          d = mma_f16(ta, xl[ks], d);
         }
-        const f16x4 ti = *reinterpret_cast<const f16x4*>(im + Ws::AT + tri_at(bi4, bi4, lr, lg));
-        f16x4 xh, xl;
-        bfrag16_split(acc, xh, xl);
-        f32x4 d = mma_f16_k16(ti, xh, f32x4{0.f, 0.f, 0.f, 0.f});
-        Dacc[bi4] = mma_f16_k16(ti, xl, d);
+        Dacc[rt] = d;
       }
       f16x8 dbh[2], dbl[2];  // Delta block pairs as hi+lo fragments
 #pragma unroll
