@@ -80,7 +80,6 @@ __device__ __forceinline__ int rset(int i, int j) { return j == 0 ? i - 1 : (j =
 // v + (v of the lane K rows up, inside each 16-lane row; 0 above the row)
 template <int K>
 __device__ __forceinline__ float add_row_shr(float v) {
-#pragma clang fp contract(off)
   const int s = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x110 + K, 0xf, 0xf,
                                             true);
   return v + __builtin_bit_cast(float, s);
@@ -175,7 +174,16 @@ __global__ void __launch_bounds__(NTHR, 3) prep_kernel(
     return make_buf(b, (uint32_t)(Lc * HD * esz - h * D * esz));
   };
 
-  // ---- loads: row r, channels 32kk + 8lg .. +7
+  // ---- loads: row r, channels 32kk + 8lg .. +7 (dt_bias first: every gate
+  // element needs it)
+  f32x4 dtb[4][2];
+  if constexpr (GIN != kG) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+        dtb[kk][a] = *reinterpret_cast<const f32x4*>(ga.dt_bias + h * D + 32 * kk + 8 * lg + 4 * a);
+  }
   f32x4 graw[4][2];
   {
     typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -210,20 +218,20 @@ __global__ void __launch_bounds__(NTHR, 3) prep_kernel(
     else bval = buf_f32(rb, r * H * 4);
   }
   if constexpr (GIN != kG) {
-    // g = -exp(A_log[h]) softplus(x + dt_bias[h, c]), beta = sigmoid(b); rows
-    // past the chunk end get g = 0 and beta = 0, as the loaded inputs would
+    // g log2(e) = -exp(A_log[h]) softplus(x + dt_bias[h, c]) log2(e) straight in
+    // the scan's log2 units, beta = sigmoid(b).  Computed on every row and
+    // masked (rows past the chunk end read x = b = 0, finite): a select here
+    // becomes per-element branches that serialize the dt_bias loads.
     const float neg_a = -expf(ga.A_log[h]);
-    const bool live = r < Lc;
+    const float keep = r < Lc ? 1.0f : 0.0f;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-      for (int a = 0; a < 2; ++a) {
-        const f32x4 db = *reinterpret_cast<const f32x4*>(ga.dt_bias + h * D + 32 * kk + 8 * lg + 4 * a);
+      for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          graw[kk][a][j] = live ? gate_log_decay(neg_a, gate_input(graw[kk][a][j], db[j])) : 0.0f;
-      }
-    bval = live ? gate_beta(bval) : 0.0f;
+          graw[kk][a][j] = keep * gate_log2_decay_fast(neg_a, gate_input(graw[kk][a][j], dtb[kk][a][j]));
+    bval = keep * gate_beta(bval);
   }
 
   // ================= S1: gamma (log2 units), in-block scan down the 16 rows
@@ -232,9 +240,7 @@ __global__ void __launch_bounds__(NTHR, 3) prep_kernel(
   for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      // no multiply-add contraction: gamma must not depend on where g came from
-#pragma clang fp contract(off)
-      float x = graw[kk][e >> 2][e & 3] * LOG2E;
+      float x = GIN == kG ? graw[kk][e >> 2][e & 3] * LOG2E : graw[kk][e >> 2][e & 3];
       x = add_row_shr<1>(x);
       x = add_row_shr<2>(x);
       x = add_row_shr<4>(x);

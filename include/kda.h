@@ -148,9 +148,12 @@ kda_status kda_chunk_prefill(const void* q, const void* k, const void* v, kda_dt
  * but the decay and beta come as the gate's raw inputs (the arguments of
  * kda_gate): x [T_tot, H, dk] gate logits (x_dt KDA_F32 or KDA_BF16), b
  * [T_tot, H] beta logits (b_dt), A_log [H], dt_bias [H, dk].  g and beta are
- * formed in registers by the same arithmetic as kda_gate, so the result is
- * bit-identical to kda_gate followed by kda_chunk_prefill; g never goes to
- * memory.  FlashKDA's interface (Kimi K3 artifact audit, §7.1) likewise
+ * formed in registers and g never goes to memory.  g is summed into the
+ * cumulative decay straight in log2 units with the plain hardware exp2/log2
+ * (absolute error about exp(A_log) 2^-23 per token, against a few ulp for
+ * kda_gate), so results agree with kda_gate followed by kda_chunk_prefill to
+ * rounding, not bit for bit.  FlashKDA's interface (Kimi K3 artifact audit,
+ * §7.1) likewise
  * takes the gate's inputs.  Refusals: those of kda_gate for A_log /
  * dt_bias, then those of kda_chunk_prefill; x must be 16-byte aligned.
  */

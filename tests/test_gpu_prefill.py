@@ -12,7 +12,8 @@ import torch
 import oracle
 from synth import CONFIGS, draw_config, draw_prefill
 from tests.gpu_util import DEV, need_gpu, oracle_gate_f32, oracle_gate_f64, sample_heads, say
-from tests.parity import (assert_out, assert_out_bf16, assert_state, out_err, state_err, to64)
+from tests.parity import (O_TOL, S_TOL, assert_out, assert_out_bf16, assert_state, out_err,
+                          state_err, to64)
 import gated_delta_rule_58_amd as kda
 
 pytestmark = pytest.mark.gpu
@@ -232,11 +233,15 @@ def test_multi_pass_workspace():
 
 
 @pytest.mark.parametrize("xdt", [torch.float32, torch.bfloat16])
-def test_gated_equals_gate_then_prefill(xdt):
-    """kda_chunk_prefill_gated is bit-identical to kda_gate followed by
-    kda_chunk_prefill (varlen with empty and one-token sequences, initial
-    state, scale), and matches the oracle gate followed by the oracle
-    recurrence."""
+def test_gated_matches_gate_then_prefill(xdt):
+    """kda_chunk_prefill_gated matches the oracle gate followed by the oracle
+    recurrence, and kda_gate followed by kda_chunk_prefill within the same
+    tolerances, on varlen input with empty and one-token sequences, initial
+    state and scale.  The two GPU paths are not bit-identical: the in-register
+    gate skips kda_gate's last-ulp corrections (g differs by about
+    exp(A_log) 2^-23), which moves the fp16 rounding of some decayed
+    operands, so their difference is of the size of either path's own
+    rounding error (about 1e-3 x RMS(o) here)."""
     need_gpu()
     dr = draw_prefill([200, 0, 64, 1, 77], H=3, dtype=torch.bfloat16, init_state=True, seed=61)
     say("gated prefill vs gate + prefill", xdt)
@@ -252,7 +257,7 @@ def test_gated_equals_gate_then_prefill(xdt):
     o2, S2 = kda.chunk_prefill_gated(q, k, v, xd, bd, A, dtb, cu, S0, cu_seqlens_host=cu_h,
                                      scale=0.7, o_dtype=torch.float32)
     torch.cuda.synchronize()
-    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+    assert out_err(o2, o1) <= O_TOL and state_err(S2, S1) <= S_TOL
     gr, br = oracle.gate(x.float(), b.float(), dr.A_log, dr.dt_bias)
     o_ref, S_ref = oracle.prefill(dr.q, dr.k, dr.v, gr, br, cu_h, dr.initial_state, scale=0.7)
     assert_out(o2, o_ref, "gated")
