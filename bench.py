@@ -35,10 +35,11 @@ HBM_PEAK_GBS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0
 
 T, H, D, C = 4096, 96, 128, 64
-# algorithmic bytes of one chunk-prefill launch: per token q,k,v bf16 + g f32
-# + beta f32 + o bf16, plus the fp32 final state written once (zero initial state)
+# algorithmic bytes of one gated chunk-prefill call: per token q,k,v bf16 +
+# gate logits f32 + beta logit f32 + o bf16, plus the fp32 final state written
+# once (zero initial state) and the per-head A_log and dt_bias read once
 PREFILL_TOKEN_BYTES = H * (3 * D * 2 + D * 4 + 4 + D * 2)            # 147,840
-PREFILL_BYTES = T * PREFILL_TOKEN_BYTES + H * D * D * 4               # 611,844,096
+PREFILL_BYTES = T * PREFILL_TOKEN_BYTES + H * D * D * 4 + H * 4 + H * D * 4   # 611,893,632
 # algorithmic MACs per (chunk, head) at C=64: A 258,048, P 266,240, solve 41,664,
 # U 258,048, W 258,048, W.S / Qt.S / Khat^T.Delta 1,048,576 each, P.Delta 266,240
 MAC_PER_CHUNK_HEAD = 4_494_016
