@@ -197,6 +197,49 @@ def bench_decode(args, torch, kda, synth):
                 bytes_per_step=DEC_STEP_BYTES)
 
 
+def bench_decode_gated(args, torch, kda, synth, state_dtype):
+    """kda_recurrent_decode_gated on the decode workload's shape: fp32 gate and
+    beta logits in, a pool of 256 states (fp32 or bf16) addressed through a
+    permutation of the slots, updated in place."""
+    dev = "cuda:0"
+    c = synth.CONFIGS[4]
+    A_log, dt_bias, S0 = synth.draw_decode_params(DEC_N, H, seed=c["seed"], device=dev)
+    pool = S0.to(state_dtype).contiguous()
+    del S0
+    perm = torch.randperm(DEC_N, generator=torch.Generator().manual_seed(3))
+    ind = perm.to(torch.int32).to(dev)
+    steps = [synth.draw_decode_step(DEC_N, H, s, seed=c["seed"], device=dev)
+             for s in range(DEC_STEPS)]
+    steps = [(st.q, st.k, st.v, st.x.float(), st.b.float()) for st in steps]
+    o = torch.empty((DEC_N, H, D), dtype=torch.bfloat16, device=dev)
+
+    def step(s):
+        q, k, v, x, b = steps[s]
+        kda.recurrent_decode_gated(q, k, v, x, b, A_log, dt_bias, pool, state_indices=ind,
+                                   out=o)
+    for s in range(min(args.warmup, DEC_STEPS)):
+        step(s)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(args.repeats):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(DEC_STEPS + 1)]
+        ev[0].record()
+        for s in range(DEC_STEPS):
+            step(s)
+            ev[s + 1].record()
+        torch.cuda.synchronize()
+        times += [ev[s].elapsed_time(ev[s + 1]) for s in range(DEC_STEPS)]
+    ms = sum(times) / len(times)
+    es = 2 if state_dtype == torch.bfloat16 else 4
+    # per (sequence, head): state in + out, q/k/v bf16, x fp32, b fp32, o bf16;
+    # per step: the slot indices and the per-head A_log and dt_bias
+    pair = 2 * D * D * es + 3 * D * 2 + D * 4 + 4 + D * 2
+    nbytes = DEC_N * H * pair + DEC_N * 4 + H * 4 + H * D * 4
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return dict(ms_per_step=ms, GBps=gbs, frac=gbs / HBM_PEAK_GBS, bytes_per_step=nbytes,
+                tokens_per_s=DEC_N / (ms * 1e-3))
+
+
 def cpu_baseline(args, synth):
     """fp64 oracle on `cpu_heads` of the 96 heads of the same T=4096 workload."""
     import numpy as np
@@ -235,7 +278,11 @@ def main():
     kda.lib()
     if args.only != "all":
         fn = {"prefill": lambda: bench_prefill(args, torch, kda, synth),
-              "decode": lambda: bench_decode(args, torch, kda, synth),
+              "decode": lambda: dict(plain=bench_decode(args, torch, kda, synth),
+                                     gated_f32_pool=bench_decode_gated(args, torch, kda, synth,
+                                                                       torch.float32),
+                                     gated_bf16_pool=bench_decode_gated(args, torch, kda, synth,
+                                                                        torch.bfloat16)),
               "copy": lambda: bench_copy(args, torch)}[args.only]
         print(json.dumps({"diagnostic": args.only, **fn()}), flush=True)
         return
@@ -247,6 +294,12 @@ def main():
     dec = bench_decode(args, torch, kda, synth)
     print("decode: %.4f ms/step, %.1f GB/s" % (dec["ms_per_step"], dec["GBps"]),
           file=sys.stderr, flush=True)
+    dg = {}
+    for name, sdt in (("gated_f32_pool", torch.float32), ("gated_bf16_pool", torch.bfloat16)):
+        dg[name] = bench_decode_gated(args, torch, kda, synth, sdt)
+        print("decode %s: %.4f ms/step, %.1f GB/s" % (name, dg[name]["ms_per_step"],
+                                                     dg[name]["GBps"]),
+              file=sys.stderr, flush=True)
     step_s = pre["fused_ms"] * 1e-3
     ach = PREFILL_BYTES / step_s / 1e9
     mfma = PREFILL_FLOPS / step_s / 1e12
@@ -283,7 +336,12 @@ def main():
                           "alg_flops_per_launch": PREFILL_FLOPS},
         "decode": {"workload": "256 seqs x 96 heads x 1 token, 64 steps, fp32 state in place",
                    "ms_per_step": dec["ms_per_step"], "GBps": dec["GBps"], "frac": dec["frac"],
-                   "bytes_per_step": DEC_STEP_BYTES},
+                   "bytes_per_step": DEC_STEP_BYTES,
+                   "gated": {"workload": "kda_recurrent_decode_gated: fp32 gate/beta logits, "
+                                         "state pool of 256 slots addressed by a permutation",
+                             **{k: {kk: dg[k][kk] for kk in ("ms_per_step", "GBps", "frac",
+                                                             "tokens_per_s", "bytes_per_step")}
+                                for k in dg}}},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

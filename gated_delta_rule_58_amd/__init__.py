@@ -17,5 +17,6 @@ from .binding import (  # noqa: F401
     chunk_prefill_gated,
     chunk_prefill_workspace_bytes,
     recurrent_decode,
+    recurrent_decode_gated,
     exported_symbols,
 )

@@ -62,6 +62,11 @@ def lib():
                                               ctypes.c_float, _vp, ctypes.c_size_t, _vp]
         L.kda_chunk_prefill_workspace_bytes.restype = ctypes.c_size_t
         L.kda_chunk_prefill_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32, _i32]
+        L.kda_recurrent_decode_gated.restype = ctypes.c_int
+        L.kda_recurrent_decode_gated.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, ctypes.c_int,
+                                                 _vp, ctypes.c_int, _vp, _i64, _vp, _i64, _vp,
+                                                 ctypes.c_int, _i64, _vp, _vp, ctypes.c_int,
+                                                 _i32, _i32, _i32, _i32, ctypes.c_float, _vp]
         L.kda_recurrent_decode.restype = ctypes.c_int
         L.kda_recurrent_decode.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _vp,
                                            ctypes.c_int, _i32, _i32, _i32, _i32, ctypes.c_float,
@@ -72,7 +77,8 @@ def lib():
 
 def exported_symbols():
     return ["kda_last_error", "kda_version", "kda_gate", "kda_chunk_prefill",
-            "kda_chunk_prefill_gated", "kda_chunk_prefill_workspace_bytes", "kda_recurrent_decode"]
+            "kda_chunk_prefill_gated", "kda_chunk_prefill_workspace_bytes", "kda_recurrent_decode",
+            "kda_recurrent_decode_gated"]
 
 
 def _check(status: int):
@@ -215,5 +221,28 @@ def recurrent_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch
     st = lib().kda_recurrent_decode(_ptr(q), _ptr(k), _ptr(v), _dt(q), _ptr(g), _ptr(beta),
                                     _ptr(state), _ptr(out), _dt(out), N, H, dk, dv, float(scale),
                                     _stream(q.device))
+    _check(st)
+    return out
+
+
+def recurrent_decode_gated(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, x: torch.Tensor,
+                           b: torch.Tensor, A_log: torch.Tensor, dt_bias: torch.Tensor,
+                           state: torch.Tensor, state_indices: Optional[torch.Tensor] = None,
+                           scale: float = 1.0, o_dtype: Optional[torch.dtype] = None,
+                           out: Optional[torch.Tensor] = None):
+    """kda_recurrent_decode_gated: q/k/v/x [N,H,d], b [N,H], A_log [H], dt_bias [H,d];
+    state pool [num_slots,H,dk,dv] (float32 or bfloat16) updated in place;
+    state_indices [N] int32 on the device (None: sequence n uses slot n).
+    Returns o (zeros for sequences whose slot is outside the pool)."""
+    N, H, dk = q.shape
+    dv = v.shape[2]
+    if state_indices is not None and state_indices.dtype != torch.int32:
+        raise TypeError("state_indices must be int32")
+    if out is None:
+        out = torch.empty((N, H, dv), dtype=o_dtype or q.dtype, device=q.device)
+    st = lib().kda_recurrent_decode_gated(
+        _ptr(q), _ptr(k), _ptr(v), _dt(q), _ptr(x), _dt(x), _ptr(b), _dt(b), _ptr(A_log),
+        A_log.numel(), _ptr(dt_bias), dt_bias.numel(), _ptr(state), _dt(state), state.shape[0],
+        _ptr(state_indices), _ptr(out), _dt(out), N, H, dk, dv, float(scale), _stream(q.device))
     _check(st)
     return out

@@ -239,4 +239,73 @@ kda_status kda_recurrent_decode(const void* q, const void* k, const void* v, kda
                   "kda_recurrent_decode");
 }
 
+kda_status kda_recurrent_decode_gated(const void* q, const void* k, const void* v,
+                                      kda_dtype qkv_dt, const void* x, kda_dtype x_dt,
+                                      const void* b, kda_dtype b_dt, const float* A_log,
+                                      int64_t A_log_len, const float* dt_bias,
+                                      int64_t dt_bias_len, void* state, kda_dtype state_dt,
+                                      int64_t num_slots, const int32_t* state_indices, void* o,
+                                      kda_dtype o_dt, int32_t N, int32_t H, int32_t dk,
+                                      int32_t dv, float scale, void* stream) {
+  const char* fn = "kda_recurrent_decode_gated";
+  if (N < 0 || H <= 0)
+    return fail(KDA_ERR_INVALID_ARG, "%s: need N >= 0, H > 0 (got %d, %d)", fn, N, H);
+  if (!known_dtype(qkv_dt) || !known_dtype(x_dt) || !known_dtype(b_dt) ||
+      !known_dtype(state_dt) || !known_dtype(o_dt))
+    return fail(KDA_ERR_DTYPE, "%s: qkv_dt, x_dt, b_dt, state_dt and o_dt must be KDA_F32 or "
+                               "KDA_BF16", fn);
+  if (dk != 128 || dv != 128)
+    return fail(KDA_ERR_UNSUPPORTED, "%s: only dk = dv = 128 is implemented (got %d, %d)", fn,
+                dk, dv);
+  if (A_log_len != H)
+    return fail(KDA_ERR_SHAPE,
+                "%s: A_log has %lld values but H = %d; A_log must be one value per head "
+                "([H]); a per-channel or checkpoint-shaped A_log is refused, not reshaped",
+                fn, (long long)A_log_len, H);
+  if (dt_bias_len != (int64_t)H * dk)
+    return fail(KDA_ERR_SHAPE, "%s: dt_bias has %lld values, need H*dk = %lld", fn,
+                (long long)dt_bias_len, (long long)H * dk);
+  if (num_slots < 0)
+    return fail(KDA_ERR_INVALID_ARG, "%s: num_slots must be >= 0 (got %lld)", fn,
+                (long long)num_slots);
+  if (!state_indices && num_slots < N)
+    return fail(KDA_ERR_SHAPE, "%s: without state_indices sequence n uses slot n, so num_slots "
+                               "must be >= N (got %lld < %d)", fn, (long long)num_slots, N);
+  if (!(scale == scale) || scale > 3.0e38f || scale < -3.0e38f)
+    return fail(KDA_ERR_INVALID_ARG, "%s: scale must be finite", fn);
+  if (N == 0) return ok();
+  if (!q || !k || !v || !x || !b || !A_log || !dt_bias || !o || (num_slots > 0 && !state))
+    return fail(KDA_ERR_INVALID_ARG, "%s: all tensor pointers must be non-NULL", fn);
+  const void* ptrs[] = {q, k, v, x, o, state};
+  for (const void* p : ptrs)
+    if (p && !aligned(p, 16))
+      return fail(KDA_ERR_ALIGNMENT, "%s: q, k, v, x, o and state must be 16-byte aligned", fn);
+  if (!aligned(b, b_dt == KDA_BF16 ? 2 : 4) || !aligned(A_log, 4) || !aligned(dt_bias, 4) ||
+      !aligned(state_indices, 4))
+    return fail(KDA_ERR_ALIGNMENT, "%s: b, A_log, dt_bias and state_indices must be aligned to "
+                                   "their element size", fn);
+  const size_t s_es = state_dt == KDA_BF16 ? 2 : 4;
+  const char* sb = reinterpret_cast<const char*>(state);
+  const char* se = sb + (size_t)num_slots * H * dk * dv * s_es;
+  const size_t qkv_es = qkv_dt == KDA_BF16 ? 2 : 4;
+  const size_t x_es = x_dt == KDA_BF16 ? 2 : 4;
+  const size_t o_es = o_dt == KDA_BF16 ? 2 : 4;
+  struct { const void* p; size_t n; } others[] = {
+      {q, (size_t)N * H * dk * qkv_es},  {k, (size_t)N * H * dk * qkv_es},
+      {v, (size_t)N * H * dv * qkv_es},  {x, (size_t)N * H * dk * x_es},
+      {b, (size_t)N * H * (b_dt == KDA_BF16 ? 2 : 4)}, {o, (size_t)N * H * dv * o_es},
+      {state_indices, state_indices ? (size_t)N * 4 : 0}};
+  for (auto& r : others) {
+    const char* b0 = static_cast<const char*>(r.p);
+    if (r.n && b0 < se && sb < b0 + r.n)
+      return fail(KDA_ERR_INVALID_ARG, "%s: the state pool overlaps another tensor", fn);
+  }
+  return launched(kda::launch_decode_gated(q, k, v, qkv_dt == KDA_BF16, x, x_dt == KDA_BF16, b,
+                                           b_dt == KDA_BF16, A_log, dt_bias, state,
+                                           state_dt == KDA_BF16, num_slots, state_indices, o,
+                                           o_dt == KDA_BF16, N, H, scale,
+                                           static_cast<hipStream_t>(stream)),
+                  fn);
+}
+
 }  // extern "C"

@@ -17,6 +17,16 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, bool qkv_b
                          const float* g, const float* beta, float* state, void* o, bool o_bf16,
                          int N, int H, float scale, hipStream_t s);
 
+// One-token decode from the gate's raw inputs (x [N,H,128] fp32 or bf16, beta
+// logits b [N,H]) over a pool of num_slots x H states (fp32 or bf16); sequence
+// n uses slot slots[n] (n when slots is null), and a slot outside the pool
+// skips it (o = 0).
+hipError_t launch_decode_gated(const void* q, const void* k, const void* v, bool qkv_bf16,
+                               const void* gx, bool x_bf16, const void* b, bool b_bf16,
+                               const float* A_log, const float* dt_bias, void* pool,
+                               bool state_bf16, int64_t num_slots, const int32_t* slots, void* o,
+                               bool o_bf16, int N, int H, float scale, hipStream_t s);
+
 // Chunked prefill: prep + state kernel per pass over the chunks (prefill.hip).
 // The decay input is either g (g_mode 0, fp32) with post-sigmoid beta in b,
 // or raw gate logits x (g_mode 1 fp32, 2 bf16) with beta logits in b and the

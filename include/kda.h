@@ -191,6 +191,39 @@ kda_status kda_recurrent_decode(const void* q, const void* k, const void* v, kda
                                 kda_dtype o_dt, int32_t N, int32_t H, int32_t dk, int32_t dv,
                                 float scale, void* stream);
 
+/*
+ * kda_recurrent_decode_gated - the one-token step of kda_recurrent_decode for
+ * serving: the gate fused in, the states in a pool of slots, fp32 or bf16.
+ *
+ *   q, k  [N, H, dk], v [N, H, dv]   dtype qkv_dt
+ *   x     [N, H, dk] gate logits (x_dt), b [N, H] beta logits (b_dt),
+ *         A_log [H] fp32, dt_bias [H, dk] fp32: g and beta are formed per
+ *         key channel with kda_gate's arithmetic and never stored
+ *   state [num_slots, H, dk, dv] dtype state_dt, read and overwritten in place
+ *   state_indices [N] int32 device array: sequence n uses state slot
+ *         state_indices[n]; NULL means slot n (then num_slots >= N)
+ *   o     [N, H, dv] dtype o_dt
+ * A sequence whose slot lies outside [0, num_slots) (a padding entry, e.g.
+ * -1) is skipped: its o is written as zeros and no state is read or written.
+ * Two sequences of one call must not share a slot (their updates would race).
+ * With state_dt KDA_BF16 every step rounds the updated state to bf16 (round to
+ * nearest even); the arithmetic of the step is fp32 either way.  The gate's
+ * inputs are FlashKDA's (Kimi K3 artifact audit, §7.1: bf16 inputs, fp32
+ * A_log / dt_bias, a bf16 state mode, §7.4); the step is the code audit's fused
+ * recurrent decode regime.  Requires dk == dv == 128.  Refusals: A_log_len
+ * != H or dt_bias_len != H*dk (KDA_ERR_SHAPE), num_slots < N without
+ * indices (KDA_ERR_SHAPE), unaligned or overlapping tensors; the indices
+ * themselves are device data and are bounds-checked by the kernel.
+ */
+kda_status kda_recurrent_decode_gated(const void* q, const void* k, const void* v,
+                                      kda_dtype qkv_dt, const void* x, kda_dtype x_dt,
+                                      const void* b, kda_dtype b_dt, const float* A_log,
+                                      int64_t A_log_len, const float* dt_bias,
+                                      int64_t dt_bias_len, void* state, kda_dtype state_dt,
+                                      int64_t num_slots, const int32_t* state_indices, void* o,
+                                      kda_dtype o_dt, int32_t N, int32_t H, int32_t dk,
+                                      int32_t dv, float scale, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -30,7 +30,7 @@ def test_exports_every_declared_symbol():
     names = _declared()
     assert set(names) == {"kda_last_error", "kda_version", "kda_gate", "kda_chunk_prefill",
                           "kda_chunk_prefill_gated", "kda_chunk_prefill_workspace_bytes",
-                          "kda_recurrent_decode"}
+                          "kda_recurrent_decode", "kda_recurrent_decode_gated"}
     for n in names:
         assert hasattr(L, n), n
     assert L.kda_version().decode().startswith("kda-gfx950")
@@ -157,3 +157,38 @@ def test_decode_refusals():
     assert dec(S=DEV[5] + 8) == 5
     assert dec(o=DEV[5] + 4096) == 1   # o inside the state buffer: overlap refused
     assert dec(N=0, S=None) == 0       # empty batch is a no-op
+
+
+def _decode_gated(L, **kw):
+    a = dict(q=DEV[0], k=DEV[1], v=DEV[2], qkv_dt=1, x=DEV[3], x_dt=1, b=DEV[4], b_dt=1,
+             A_log=DEV[9], A_log_len=2, dt_bias=DEV[10], dt_bias_len=2 * 128, S=DEV[5], S_dt=1,
+             slots=8, idx=DEV[11], o=DEV[6], o_dt=1, N=4, H=2, dk=128, dv=128, scale=1.0)
+    a.update(kw)
+    return L.kda_recurrent_decode_gated(
+        a["q"], a["k"], a["v"], a["qkv_dt"], a["x"], a["x_dt"], a["b"], a["b_dt"], a["A_log"],
+        a["A_log_len"], a["dt_bias"], a["dt_bias_len"], a["S"], a["S_dt"], a["slots"], a["idx"],
+        a["o"], a["o_dt"], a["N"], a["H"], a["dk"], a["dv"], a["scale"], None)
+
+
+def test_decode_gated_refusals():
+    """The serving decode refuses what kda_gate refuses, a pool too small for
+    identity slots, unknown dtypes (the state's included), unaligned or
+    overlapping tensors, before any HIP call; empty batches are no-ops."""
+    L = _lib()
+    assert _decode_gated(L, A_log_len=128) == 2
+    assert b"A_log" in L.kda_last_error()
+    assert _decode_gated(L, dt_bias_len=2 * 128 - 1) == 2
+    assert _decode_gated(L, S_dt=2) == 3
+    assert _decode_gated(L, x_dt=9) == 3
+    assert _decode_gated(L, dk=64, dt_bias_len=2 * 64) == 4
+    assert _decode_gated(L, idx=None, slots=3) == 2           # slot n needs num_slots >= N
+    assert b"num_slots" in L.kda_last_error()
+    assert _decode_gated(L, slots=-1) == 1
+    assert _decode_gated(L, S=None) == 1
+    assert _decode_gated(L, S=DEV[5] + 8) == 5
+    assert _decode_gated(L, b=DEV[4] + 1) == 5                 # bf16 beta logits: 2-byte
+    assert _decode_gated(L, idx=DEV[11] + 2) == 5
+    assert _decode_gated(L, o=DEV[5] + 4096) == 1              # o inside the pool
+    assert _decode_gated(L, scale=float("nan")) == 1
+    assert _decode_gated(L, N=0, S=None, slots=0) == 0
+    assert b"kda_recurrent_decode_gated" in L.kda_last_error() or L.kda_last_error() == b""

@@ -6,7 +6,7 @@ import torch
 import oracle
 from synth import CONFIGS, draw_decode_params, draw_decode_step, draw_prefill
 from tests.gpu_util import DEV, need_gpu, oracle_gate_f32, say
-from tests.parity import assert_out, assert_state, to64
+from tests.parity import assert_out, assert_state, out_err, state_err, to64
 import gated_delta_rule_58_amd as kda
 
 pytestmark = pytest.mark.gpu
@@ -116,3 +116,111 @@ def test_decode_deterministic():
     o2 = kda.recurrent_decode(st.q, st.k, st.v, g, beta, S2)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+@pytest.mark.parametrize("xdt", [torch.float32, torch.bfloat16])
+def test_decode_gated_matches_gate_then_decode(xdt):
+    """kda_recurrent_decode_gated over an fp32 pool with slot n = sequence n
+    agrees with kda_gate followed by kda_recurrent_decode (the same gate
+    arithmetic, thread layout and summation order) to fp32 rounding, and both
+    match the oracle gate followed by the oracle step."""
+    need_gpu()
+    say("gated decode vs gate + decode", xdt)
+    N, H = 9, 5
+    A_log, dt_bias, S0 = draw_decode_params(N, H, seed=41)
+    S0 = S0 * 10
+    S1 = S0.to(DEV).contiguous()
+    S2 = S1.clone()
+    S_ref = to64(S0)
+    Ad, dbd = A_log.to(DEV), dt_bias.to(DEV)
+    for step in range(4):
+        st = draw_decode_step(N, H, step, seed=41, dtype=torch.bfloat16)
+        x, b = st.x.to(xdt), st.b.to(xdt)
+        q, k, v = st.q.to(DEV), st.k.to(DEV), st.v.to(DEV)
+        g, beta = kda.gate(x.to(DEV), b.to(DEV), Ad, dbd)
+        o1 = kda.recurrent_decode(q, k, v, g, beta, S1, scale=0.8, o_dtype=torch.float32)
+        o2 = kda.recurrent_decode_gated(q, k, v, x.to(DEV), b.to(DEV), Ad, dbd, S2, scale=0.8,
+                                        o_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert out_err(o2, o1) <= 1e-5 and state_err(S2, S1) <= 1e-6
+        gr, br = oracle.gate(x.float(), b.float(), A_log, dt_bias)
+        o_ref, S_ref = oracle.decode(st.q, st.k, st.v, gr, br, S_ref, scale=0.8)
+        assert_out(o2, o_ref, "gated decode step %d" % step)
+        assert_state(S2, S_ref, "gated decode step %d" % step)
+
+
+def _bf16_round(S):
+    """The bf16 state mode's rounding of an fp64 state: nearest even (torch)."""
+    return to64(torch.from_numpy(np.ascontiguousarray(S)).to(torch.bfloat16))
+
+
+@pytest.mark.parametrize("sdt", [torch.float32, torch.bfloat16])
+def test_decode_gated_state_pool(sdt):
+    """A pool of 7 slots; 4 sequences mapped to slots [5, -1, 0, 3] (-1 is a
+    padding entry); 6 steps against the oracle.  The padding sequence's o is
+    zero, the slots no sequence uses stay bit for bit unchanged, and in bf16
+    mode the oracle's state is rounded to bf16 after every step, which is what
+    that mode computes."""
+    need_gpu()
+    say("gated decode state pool", sdt)
+    N, H, NS = 4, 3, 7
+    idx = [5, -1, 0, 3]
+    live = [n for n in range(N) if idx[n] >= 0]
+    A_log, dt_bias, pool0 = draw_decode_params(NS, H, seed=43)
+    pool0 = (pool0 * 10).to(sdt)
+    pool = pool0.to(DEV).contiguous()
+    S_ref = {n: to64(pool0[idx[n]]) for n in live}
+    ind = torch.tensor(idx, dtype=torch.int32, device=DEV)
+    for step in range(6):
+        st = draw_decode_step(N, H, step, seed=43, dtype=torch.bfloat16)
+        o = kda.recurrent_decode_gated(st.q.to(DEV), st.k.to(DEV), st.v.to(DEV), st.x.to(DEV),
+                                       st.b.to(DEV), A_log.to(DEV), dt_bias.to(DEV), pool,
+                                       state_indices=ind, o_dtype=torch.float32)
+        torch.cuda.synchronize()
+        gr, br = oracle.gate(st.x, st.b, A_log, dt_bias)
+        o_ref, S_new = oracle.decode(st.q[live], st.k[live], st.v[live], gr[live], br[live],
+                                     np.stack([S_ref[n] for n in live]))
+        if sdt == torch.bfloat16:
+            S_new = _bf16_round(S_new)
+        for i, n in enumerate(live):
+            S_ref[n] = S_new[i]
+        assert_out(o[live], o_ref, "pool step %d" % step)
+        assert torch.all(o[1] == 0)
+    for s in range(NS):
+        if s not in idx:
+            assert torch.equal(pool[s].cpu(), pool0[s]), s
+    for n in live:
+        assert_state(pool[idx[n]], S_ref[n], "pool slot %d" % idx[n])
+
+
+def test_decode_gated_full_size_bf16_sampled():
+    """256 sequences x 96 heads, bf16 state pool of 256 slots addressed through
+    a permutation, bf16 logits, 8 steps; sampled (sequence, head) pairs against
+    the oracle gate and step with the state rounded to bf16 after each step."""
+    need_gpu()
+    c = CONFIGS[4]
+    N, H, seed, steps = c["N"], c["H"], c["seed"], 8
+    say("gated decode full size, bf16 pool, %d steps" % steps)
+    A_log, dt_bias, S0 = draw_decode_params(N, H, seed=seed, device=DEV)
+    pool = S0.to(torch.bfloat16)
+    perm = torch.randperm(N, generator=torch.Generator().manual_seed(7)).to(torch.int32)
+    ind = perm.to(DEV)
+    rng = np.random.default_rng(9)
+    pairs = [(int(a), int(b)) for a, b in zip(rng.integers(0, N, 24), rng.integers(0, H, 24))]
+    ni = torch.tensor([p[0] for p in pairs])
+    hi = torch.tensor([p[1] for p in pairs])
+    si = perm[ni].long()
+    S_ref = to64(pool[si, hi])                            # [24, 128, 128]
+    for step in range(steps):
+        st = draw_decode_step(N, H, step, seed=seed, dtype=torch.bfloat16, device=DEV)
+        x, b = st.x.to(torch.bfloat16), st.b.to(torch.bfloat16)
+        o = kda.recurrent_decode_gated(st.q, st.k, st.v, x, b, A_log, dt_bias, pool,
+                                       state_indices=ind, o_dtype=torch.float32)
+        gr, br = oracle.gate(x[ni, hi].cpu()[None].float(), b[ni, hi].cpu()[None].float(),
+                             A_log[hi].cpu(), dt_bias[hi].cpu())
+        o_ref, S_new = oracle.decode(st.q[ni, hi].cpu()[None], st.k[ni, hi].cpu()[None],
+                                     st.v[ni, hi].cpu()[None], gr, br, S_ref[None])
+        S_ref = _bf16_round(S_new[0])
+        assert_out(o[ni, hi], o_ref[0], "bf16 pool step %d" % step)
+    torch.cuda.synchronize()
+    assert_state(pool[si, hi], S_ref, "bf16 pool after %d steps" % steps)
