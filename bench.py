@@ -86,7 +86,8 @@ def parse():
                     help="heads of the workload the CPU oracle runs (sample)")
     ap.add_argument("--ws-chunks", type=int, default=T // C,
                     help="chunks per pass the prefill workspace holds (T/64 = one pass)")
-    ap.add_argument("--only", choices=["all", "prefill", "decode", "copy"], default="all",
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "prologue", "copy"],
+                    default="all",
                     help="profiling aid: run one part only (prints a diagnostic line, "
                          "not the bench line)")
     return ap.parse_args()
@@ -240,6 +241,38 @@ def bench_decode_gated(args, torch, kda, synth, state_dtype):
                 tokens_per_s=DEC_N / (ms * 1e-3))
 
 
+def bench_prologue(args, torch, kda):
+    """kda_shortconv_l2norm at the K3 layer's prefill shape: T=4096, H=96, bf16
+    q/k/v projections in and out, SiLU, conv state out."""
+    dev = "cuda:0"
+    g = torch.Generator(device=dev).manual_seed(5)
+    xs = [torch.randn((T, H, D), generator=g, device=dev).to(torch.bfloat16) for _ in range(3)]
+    ws = [torch.randn((H * D, 4), generator=g, device=dev) * 0.5 for _ in range(3)]
+    cu = torch.tensor([0, T], dtype=torch.int32)
+    cud = cu.to(dev)
+    st = torch.empty((1, 3, 3, H * D), dtype=torch.float32, device=dev)
+
+    def call():
+        kda.shortconv_l2norm(*xs, *ws, cu_seqlens=cud, cu_seqlens_host=cu, state_out=st)
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(args.repeats):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        ev[0].record()
+        for i in range(args.steps):
+            call()
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        times += [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
+    ms = sum(times) / len(times)
+    nbytes = 2 * 3 * T * H * D * 2 + 3 * H * D * 4 * 4 + 9 * H * D * 4
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return dict(ms=ms, GBps=gbs, frac=gbs / HBM_PEAK_GBS, bytes=nbytes,
+                tokens_per_s=T / (ms * 1e-3))
+
+
 def cpu_baseline(args, synth):
     """fp64 oracle on `cpu_heads` of the 96 heads of the same T=4096 workload."""
     import numpy as np
@@ -283,6 +316,7 @@ def main():
                                                                        torch.float32),
                                      gated_bf16_pool=bench_decode_gated(args, torch, kda, synth,
                                                                         torch.bfloat16)),
+              "prologue": lambda: bench_prologue(args, torch, kda),
               "copy": lambda: bench_copy(args, torch)}[args.only]
         print(json.dumps({"diagnostic": args.only, **fn()}), flush=True)
         return
@@ -300,6 +334,9 @@ def main():
         print("decode %s: %.4f ms/step, %.1f GB/s" % (name, dg[name]["ms_per_step"],
                                                      dg[name]["GBps"]),
               file=sys.stderr, flush=True)
+    pro = bench_prologue(args, torch, kda)
+    print("prologue (short conv + SiLU + q/k L2 norm): %.4f ms, %.1f GB/s"
+          % (pro["ms"], pro["GBps"]), file=sys.stderr, flush=True)
     step_s = pre["fused_ms"] * 1e-3
     ach = PREFILL_BYTES / step_s / 1e9
     mfma = PREFILL_FLOPS / step_s / 1e12
@@ -342,6 +379,10 @@ def main():
                              **{k: {kk: dg[k][kk] for kk in ("ms_per_step", "GBps", "frac",
                                                              "tokens_per_s", "bytes_per_step")}
                                 for k in dg}}},
+        "prologue": {"workload": "kda_shortconv_l2norm T=4096 H=96 bf16 q/k/v in and out, "
+                                 "SiLU, conv state out",
+                     "ms": pro["ms"], "GBps": pro["GBps"], "frac": pro["frac"],
+                     "bytes_per_call": pro["bytes"], "tokens_per_s": pro["tokens_per_s"]},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

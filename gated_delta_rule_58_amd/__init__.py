@@ -18,5 +18,6 @@ from .binding import (  # noqa: F401
     chunk_prefill_workspace_bytes,
     recurrent_decode,
     recurrent_decode_gated,
+    shortconv_l2norm,
     exported_symbols,
 )

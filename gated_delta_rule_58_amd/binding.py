@@ -16,6 +16,8 @@ _STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARG", 2: "KDA_ERR_SHAPE", 3: "KDA_ER
 # processed in passes when a batch needs more)
 DEFAULT_WORKSPACE_BYTES = 1 << 30
 CHUNK = 64
+KDA_ACT_NONE = 0
+KDA_ACT_SILU = 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -67,6 +69,10 @@ def lib():
                                                  _vp, ctypes.c_int, _vp, _i64, _vp, _i64, _vp,
                                                  ctypes.c_int, _i64, _vp, _vp, ctypes.c_int,
                                                  _i32, _i32, _i32, _i32, ctypes.c_float, _vp]
+        L.kda_shortconv_l2norm.restype = ctypes.c_int
+        L.kda_shortconv_l2norm.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _i64,
+                                           _i32, ctypes.c_float, _vp, _vp, _i32, _vp, _vp, _vp,
+                                           _vp, _vp, ctypes.c_int, _i64, _i32, _i32, _vp]
         L.kda_recurrent_decode.restype = ctypes.c_int
         L.kda_recurrent_decode.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _vp,
                                            ctypes.c_int, _i32, _i32, _i32, _i32, ctypes.c_float,
@@ -78,7 +84,7 @@ def lib():
 def exported_symbols():
     return ["kda_last_error", "kda_version", "kda_gate", "kda_chunk_prefill",
             "kda_chunk_prefill_gated", "kda_chunk_prefill_workspace_bytes", "kda_recurrent_decode",
-            "kda_recurrent_decode_gated"]
+            "kda_recurrent_decode_gated", "kda_shortconv_l2norm"]
 
 
 def _check(status: int):
@@ -246,3 +252,37 @@ def recurrent_decode_gated(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, x:
         _ptr(state_indices), _ptr(out), _dt(out), N, H, dk, dv, float(scale), _stream(q.device))
     _check(st)
     return out
+
+
+def shortconv_l2norm(xq: torch.Tensor, xk: torch.Tensor, xv: torch.Tensor, wq: torch.Tensor,
+                     wk: torch.Tensor, wv: torch.Tensor, cu_seqlens: Optional[torch.Tensor] = None,
+                     conv_state: Optional[torch.Tensor] = None, output_state: bool = True,
+                     activation: Optional[str] = "silu", eps: float = 1e-6,
+                     out_dtype: Optional[torch.dtype] = None,
+                     cu_seqlens_host: Optional[torch.Tensor] = None,
+                     state_out: Optional[torch.Tensor] = None):
+    """kda_shortconv_l2norm: xq/xk/xv [T,H,d] projections, conv weights [H*d,4]
+    (or the checkpoint's [H*d,1,4]) -> (yq, yk, yv, conv_state_out) with q and k
+    L2-normalised.  conv_state [N,3,3,H*d] fp32 or None (zeros); state_out may
+    be conv_state itself (in place) when no sequence exceeds 64 tokens."""
+    T, H, d = xq.shape
+    dev = xq.device
+    if cu_seqlens is None:
+        cu_seqlens = torch.tensor([0, T], dtype=torch.int32, device=dev)
+    if cu_seqlens_host is None:
+        cu_seqlens_host = cu_seqlens.detach().to("cpu", torch.int32)
+    cu_h = cu_seqlens_host.contiguous()
+    N = cu_h.numel() - 1
+    odt = out_dtype or xq.dtype
+    ys = [torch.empty((T, H, d), dtype=odt, device=dev) for _ in range(3)]
+    if output_state and state_out is None:
+        state_out = torch.empty((N, 3, 3, H * d), dtype=torch.float32, device=dev)
+    act = {None: KDA_ACT_NONE, "silu": KDA_ACT_SILU}[activation]
+    ws = [w.contiguous() for w in (wq, wk, wv)]
+    st = lib().kda_shortconv_l2norm(
+        _ptr(xq), _ptr(xk), _ptr(xv), _dt(xq), _ptr(ws[0]), _ptr(ws[1]), _ptr(ws[2]),
+        ws[0].numel(), act, float(eps), _ptr(cu_seqlens.to(dev, torch.int32).contiguous()),
+        cu_h.data_ptr(), N, _ptr(conv_state), _ptr(state_out if output_state else None),
+        _ptr(ys[0]), _ptr(ys[1]), _ptr(ys[2]), _dt(ys[0]), T, H, d, _stream(dev))
+    _check(st)
+    return ys[0], ys[1], ys[2], (state_out if output_state else None)

@@ -308,4 +308,86 @@ kda_status kda_recurrent_decode_gated(const void* q, const void* k, const void* 
                   fn);
 }
 
+kda_status kda_shortconv_l2norm(const void* xq, const void* xk, const void* xv, kda_dtype in_dt,
+                                const float* wq, const float* wk, const float* wv, int64_t w_len,
+                                int32_t activation, float eps, const int32_t* cu_seqlens,
+                                const int32_t* cu_seqlens_host, int32_t N,
+                                const float* conv_state_in, float* conv_state_out, void* yq,
+                                void* yk, void* yv, kda_dtype out_dt, int64_t T_tot, int32_t H,
+                                int32_t d, void* stream) {
+  const char* fn = "kda_shortconv_l2norm";
+  if (N < 0 || H <= 0 || T_tot < 0)
+    return fail(KDA_ERR_INVALID_ARG, "%s: need N >= 0, H > 0, T_tot >= 0 (got %d, %d, %lld)", fn,
+                N, H, (long long)T_tot);
+  if (!known_dtype(in_dt) || !known_dtype(out_dt))
+    return fail(KDA_ERR_DTYPE, "%s: in_dt and out_dt must be KDA_F32 or KDA_BF16", fn);
+  if (d != 128)
+    return fail(KDA_ERR_UNSUPPORTED, "%s: only d = 128 is implemented (got %d)", fn, d);
+  if (w_len != (int64_t)H * d * 4)
+    return fail(KDA_ERR_SHAPE, "%s: each conv weight has %lld values, need H*d*4 = %lld (the "
+                               "checkpoint's [H*d, 1, 4])", fn, (long long)w_len,
+                (long long)H * d * 4);
+  if (activation != KDA_ACT_NONE && activation != KDA_ACT_SILU)
+    return fail(KDA_ERR_INVALID_ARG, "%s: activation must be KDA_ACT_NONE or KDA_ACT_SILU", fn);
+  if (!(eps >= 0.0f) || eps > 3.0e38f)
+    return fail(KDA_ERR_INVALID_ARG, "%s: eps must be finite and >= 0", fn);
+  if (T_tot > ((int64_t)1 << 31) - 1 || H > 16384)
+    return fail(KDA_ERR_UNSUPPORTED, "%s: need T_tot < 2^31 and H <= 16384", fn);
+  if (N == 0) {
+    if (T_tot != 0) return fail(KDA_ERR_SHAPE, "%s: N = 0 needs T_tot = 0", fn);
+    return ok();
+  }
+  if (!cu_seqlens) return fail(KDA_ERR_INVALID_ARG, "%s: cu_seqlens is NULL", fn);
+  int64_t max_len = T_tot, min_len = 0;  // bounds when the lengths are unknown on the host
+  if (cu_seqlens_host) {
+    if (cu_seqlens_host[0] != 0 || cu_seqlens_host[N] != T_tot)
+      return fail(KDA_ERR_SHAPE, "%s: cu_seqlens must start at 0 and end at T_tot = %lld "
+                                 "(got %d .. %d)", fn, (long long)T_tot, cu_seqlens_host[0],
+                  cu_seqlens_host[N]);
+    max_len = 0;
+    min_len = T_tot;
+    for (int32_t n = 0; n < N; ++n) {
+      if (cu_seqlens_host[n + 1] < cu_seqlens_host[n])
+        return fail(KDA_ERR_SHAPE, "%s: cu_seqlens decreases at index %d", fn, n);
+      const int64_t l = (int64_t)cu_seqlens_host[n + 1] - cu_seqlens_host[n];
+      if (l > max_len) max_len = l;
+      if (l < min_len) min_len = l;
+    }
+  }
+  if (!wq || !wk || !wv || (T_tot > 0 && (!xq || !xk || !xv || !yq || !yk || !yv)))
+    return fail(KDA_ERR_INVALID_ARG, "%s: inputs, weights and outputs must be non-NULL", fn);
+  const void* ptrs[] = {xq, xk, xv, wq, wk, wv, conv_state_in, conv_state_out, yq, yk, yv};
+  for (const void* p : ptrs)
+    if (p && !aligned(p, 16))
+      return fail(KDA_ERR_ALIGNMENT, "%s: tensors must be 16-byte aligned", fn);
+  if (!aligned(cu_seqlens, 4)) return fail(KDA_ERR_ALIGNMENT, "%s: cu_seqlens must be 4-byte aligned", fn);
+  // outputs must not overlap inputs (runs read 3 rows of their neighbours);
+  // the state may be updated in place only when every sequence is one run
+  const size_t in_b = (size_t)T_tot * H * d * (in_dt == KDA_BF16 ? 2 : 4);
+  const size_t out_b = (size_t)T_tot * H * d * (out_dt == KDA_BF16 ? 2 : 4);
+  const void* ins[] = {xq, xk, xv};
+  const void* outs[] = {yq, yk, yv};
+  for (const void* a : ins)
+    for (const void* b : outs) {
+      const char* a0 = static_cast<const char*>(a);
+      const char* b0 = static_cast<const char*>(b);
+      if (in_b && out_b && a0 < b0 + out_b && b0 < a0 + in_b)
+        return fail(KDA_ERR_INVALID_ARG, "%s: an output overlaps an input", fn);
+    }
+  if (conv_state_in && conv_state_out) {
+    const size_t sb = (size_t)N * 9 * H * d * 4;
+    const char* a0 = reinterpret_cast<const char*>(conv_state_in);
+    const char* b0 = reinterpret_cast<const char*>(conv_state_out);
+    if (a0 < b0 + sb && b0 < a0 + sb && (a0 != b0 || max_len > 1))
+      return fail(KDA_ERR_INVALID_ARG, "%s: the conv state may be updated in place only when "
+                                       "every sequence has at most one token", fn);
+  }
+  return launched(kda::launch_shortconv(xq, xk, xv, in_dt == KDA_BF16, wq, wk, wv,
+                                        activation == KDA_ACT_SILU, eps, cu_seqlens, N, min_len,
+                                        max_len, T_tot, H, conv_state_in, conv_state_out, yq,
+                                        yk, yv,
+                                        out_dt == KDA_BF16, static_cast<hipStream_t>(stream)),
+                  fn);
+}
+
 }  // extern "C"

@@ -27,6 +27,17 @@ hipError_t launch_decode_gated(const void* q, const void* k, const void* v, bool
                                bool state_bf16, int64_t num_slots, const int32_t* slots, void* o,
                                bool o_bf16, int N, int H, float scale, hipStream_t s);
 
+// The layer's prologue: causal depthwise conv (kernel 4) of q, k, v, optional
+// SiLU, L2 norm of q and k per (token, head); conv state [N][3][3][H*128] fp32.
+// min_len / max_len: the shortest / longest sequence (0 / T_tot when unknown):
+// a zero-length sequence needs its state copied by a second launch.
+hipError_t launch_shortconv(const void* xq, const void* xk, const void* xv, bool in_bf16,
+                            const float* wq, const float* wk, const float* wv, bool silu,
+                            float eps, const int32_t* cu, int N, int64_t min_len,
+                            int64_t max_len, int64_t T_tot, int H, const float* state_in,
+                            float* state_out, void* yq, void* yk, void* yv, bool out_bf16,
+                            hipStream_t s);
+
 // Chunked prefill: prep + state kernel per pass over the chunks (prefill.hip).
 // The decay input is either g (g_mode 0, fp32) with post-sigmoid beta in b,
 // or raw gate logits x (g_mode 1 fp32, 2 bf16) with beta logits in b and the

@@ -224,6 +224,44 @@ kda_status kda_recurrent_decode_gated(const void* q, const void* k, const void* 
                                       kda_dtype o_dt, int32_t N, int32_t H, int32_t dk,
                                       int32_t dv, float scale, void* stream);
 
+/* activation after the short convolution */
+enum { KDA_ACT_NONE = 0, KDA_ACT_SILU = 1 };
+
+/*
+ * kda_shortconv_l2norm - the KDA layer's prologue to the core: for each of
+ * the q, k and v projections a causal depthwise convolution of kernel 4 per
+ * channel, then (optionally) SiLU, then for q and k an L2 normalisation over
+ * the d channels of every (token, head):
+ *
+ *   y[t, c] = sum_{i=0..3} w[c, i] x[t - 3 + i, c]
+ *   y       = silu(y) = y / (1 + exp(-y))       if activation == KDA_ACT_SILU
+ *   q, k    : y / sqrt(sum_c y[t, h, c]^2 + eps)
+ *
+ *   xq, xk, xv  [T_tot, H, d] dtype in_dt (packed varlen by cu_seqlens)
+ *   wq, wk, wv  [H*d, 4] fp32 each, w_len = H*d*4 values: the checkpoint's
+ *               q/k/v_conv1d.weight [H*d, 1, 4] (Kimi K3 artifact audit,
+ *               §4.1: 12288 = 96 x 128 channels, kernel size 4); no bias
+ *   yq, yk, yv  [T_tot, H, d] dtype out_dt
+ *   conv_state_in / conv_state_out  [N, 3 (q, k, v), 3 (taps, oldest first),
+ *               H*d] fp32: the 3 inputs before / the last 3 inputs of each
+ *               sequence (NULL in: zeros; NULL out: not written).  A sequence
+ *               shorter than 3 tokens carries the older state entries on, so
+ *               a prefill followed by one-token calls with the state equals
+ *               one longer prefill.  In place (in == out) is allowed only when
+ *               every sequence has at most one token (the decode step).
+ * The pages give the weight shapes only: the activation and eps are the
+ * caller's (SiLU and 1e-6 are the usual choices).  Requires d == 128.
+ * Refusals: w_len != H*d*4 (KDA_ERR_SHAPE), bad cu_seqlens_host,
+ * overlapping outputs and inputs, unaligned tensors.
+ */
+kda_status kda_shortconv_l2norm(const void* xq, const void* xk, const void* xv, kda_dtype in_dt,
+                                const float* wq, const float* wk, const float* wv, int64_t w_len,
+                                int32_t activation, float eps, const int32_t* cu_seqlens,
+                                const int32_t* cu_seqlens_host, int32_t N,
+                                const float* conv_state_in, float* conv_state_out, void* yq,
+                                void* yk, void* yv, kda_dtype out_dt, int64_t T_tot, int32_t H,
+                                int32_t d, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

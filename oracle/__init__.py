@@ -8,9 +8,12 @@ table or helper with the HIP path.
   (token by token, fp64).
 * `chunked.prefill_chunked` is an independent fp64 chunked form used only to
   pin the recurrence (the two must agree for every chunk size).
+* `prologue.shortconv_l2norm` is the layer's prologue (short causal conv,
+  SiLU, q/k L2 norm), plain numpy per sequence.
 
 Every function is pinned by a CPU test (closed forms, special cases, brute
 force, the audit page's printed exp(A_log) statistics); none is "parity
 unpinned".
 """
 from .api import gate, prefill, decode, build_oracle, oracle_lib_path  # noqa: F401
+from .prologue import shortconv_l2norm  # noqa: F401

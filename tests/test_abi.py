@@ -22,7 +22,7 @@ def _lib():
 def _declared():
     src = open(os.path.join(ROOT, "include", "kda.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(kda_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_exports_every_declared_symbol():
@@ -30,7 +30,8 @@ def test_exports_every_declared_symbol():
     names = _declared()
     assert set(names) == {"kda_last_error", "kda_version", "kda_gate", "kda_chunk_prefill",
                           "kda_chunk_prefill_gated", "kda_chunk_prefill_workspace_bytes",
-                          "kda_recurrent_decode", "kda_recurrent_decode_gated"}
+                          "kda_recurrent_decode", "kda_recurrent_decode_gated",
+                          "kda_shortconv_l2norm"}
     for n in names:
         assert hasattr(L, n), n
     assert L.kda_version().decode().startswith("kda-gfx950")
@@ -192,3 +193,38 @@ def test_decode_gated_refusals():
     assert _decode_gated(L, scale=float("nan")) == 1
     assert _decode_gated(L, N=0, S=None, slots=0) == 0
     assert b"kda_recurrent_decode_gated" in L.kda_last_error() or L.kda_last_error() == b""
+
+
+def _shortconv(L, cu_host, **kw):
+    a = dict(xq=DEV[0], xk=DEV[1], xv=DEV[2], in_dt=1, wq=DEV[3], wk=DEV[4], wv=DEV[5],
+             w_len=2 * 128 * 4, act=1, eps=1e-6, cu=DEV[6], N=2, s_in=None, s_out=DEV[7],
+             yq=DEV[8], yk=DEV[9], yv=DEV[10], out_dt=1, T=48, H=2, d=128)
+    a.update(kw)
+    hp = None if cu_host is None else np.ascontiguousarray(np.asarray(cu_host, dtype=np.int32))
+    return L.kda_shortconv_l2norm(
+        a["xq"], a["xk"], a["xv"], a["in_dt"], a["wq"], a["wk"], a["wv"], a["w_len"], a["act"],
+        a["eps"], a["cu"], None if hp is None else hp.ctypes.data, a["N"], a["s_in"], a["s_out"],
+        a["yq"], a["yk"], a["yv"], a["out_dt"], a["T"], a["H"], a["d"], None)
+
+
+def test_shortconv_refusals():
+    """The prologue refuses conv weights of the wrong size, unknown
+    activations and dtypes, a bad cu_seqlens, outputs overlapping inputs, an
+    in-place conv state over sequences of more than one token, and unaligned
+    tensors, before any HIP call."""
+    L = _lib()
+    cu = [0, 20, 48]
+    assert _shortconv(L, cu, w_len=2 * 128 * 3) == 2
+    assert b"H*d*4" in L.kda_last_error()
+    assert _shortconv(L, cu, act=2) == 1
+    assert _shortconv(L, cu, eps=-1.0) == 1
+    assert _shortconv(L, cu, in_dt=4) == 3
+    assert _shortconv(L, cu, d=64, w_len=2 * 64 * 4) == 4
+    assert _shortconv(L, [0, 30, 20], T=20) == 2
+    assert _shortconv(L, [1, 20, 48]) == 2
+    assert _shortconv(L, cu, yk=DEV[1]) == 1                      # output over an input
+    assert _shortconv(L, [0, 2, 3], T=3, s_in=DEV[7]) == 1        # in place, a 2-token sequence
+    assert b"in place" in L.kda_last_error()
+    assert _shortconv(L, cu, wq=DEV[3] + 4) == 5
+    assert _shortconv(L, cu, wk=None) == 1
+    assert _shortconv(L, [0], N=0, T=0) == 0

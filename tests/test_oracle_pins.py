@@ -259,3 +259,96 @@ def test_synthetic_recipe_statistics():
     assert abs(float(dr.dt_bias.mean()) + 4.6) < 0.15
     assert abs(float(dr.initial_state.std()) - 0.02) < 1e-3
     assert dr.cu_seqlens.tolist() == [0, 300, 512]
+
+
+# ---- the layer prologue (short causal conv, SiLU, q/k L2 norm)
+
+def _prologue_inputs(T, H, d=8, seed=3):
+    rng = np.random.default_rng(seed)
+    xs = [rng.standard_normal((T, H, d)) for _ in range(3)]
+    ws = [rng.standard_normal((H * d, 4)) for _ in range(3)]
+    return xs, ws
+
+
+def test_prologue_impulse_response():
+    """A one-hot input at token t0, channel c returns the conv weights in
+    reverse tap order on tokens t0..t0+3 (v has no norm; no activation)."""
+    from oracle.prologue import shortconv_l2norm
+    T, H, d = 10, 2, 8
+    xs, ws = _prologue_inputs(T, H, d)
+    xv = np.zeros((T, H, d))
+    xv[4, 1, 3] = 1.0
+    c = 1 * d + 3
+    _, _, yv, _ = shortconv_l2norm(xs[0], xs[1], xv, ws[0], ws[1], ws[2], [0, T], H, d,
+                                   activation=None)
+    got = yv.reshape(T, H * d)[:, c]
+    want = np.zeros(T)
+    for i in range(4):
+        want[4 + i] = ws[2][c, 3 - i]
+    assert np.array_equal(got, want)
+    assert np.count_nonzero(yv) == 4
+
+
+def test_prologue_conv_matches_numpy_convolve():
+    """Per channel the conv is numpy.convolve(x, w reversed) cut to the
+    sequence (zero state), for every channel of every packed sequence."""
+    from oracle.prologue import shortconv_l2norm
+    T, H, d = 23, 3, 8
+    xs, ws = _prologue_inputs(T, H, d, seed=5)
+    cu = [0, 9, 9, 11, 23]
+    _, _, yv, _ = shortconv_l2norm(xs[0], xs[1], xs[2], ws[0], ws[1], ws[2], cu, H, d,
+                                   activation=None)
+    x2 = xs[2].reshape(T, H * d)
+    y2 = yv.reshape(T, H * d)
+    for n in range(len(cu) - 1):
+        b, e = cu[n], cu[n + 1]
+        if e == b:
+            continue
+        for c in range(H * d):
+            ref = np.convolve(x2[b:e, c], ws[2][c, ::-1])[:e - b]
+            assert np.allclose(y2[b:e, c], ref, rtol=0, atol=1e-13)
+
+
+def test_prologue_norm_and_silu():
+    """q and k rows have unit norm (eps = 0) and point along the activated conv
+    output; SiLU matches x * expit(x) and its closed forms."""
+    from scipy.special import expit
+    from oracle.prologue import shortconv_l2norm, silu, causal_conv
+    T, H, d = 7, 2, 8
+    xs, ws = _prologue_inputs(T, H, d, seed=8)
+    yq, yk, yv, _ = shortconv_l2norm(*xs, *ws, [0, T], H, d, activation="silu", eps=0.0)
+    for y in (yq, yk):
+        assert np.allclose(np.linalg.norm(y, axis=2), 1.0, atol=1e-14)
+    raw = silu(causal_conv(xs[0].reshape(T, H * d), ws[0], np.zeros((3, H * d)))).reshape(T, H, d)
+    cos = np.sum(raw * yq, axis=2) / np.linalg.norm(raw, axis=2)
+    assert np.allclose(cos, 1.0, atol=1e-14)
+    z = np.linspace(-30, 30, 61)
+    assert np.allclose(silu(z), z * expit(z), rtol=1e-14, atol=1e-300)
+    assert silu(np.array([0.0]))[0] == 0.0
+    assert abs(silu(np.array([50.0]))[0] - 50.0) < 1e-15 * 50
+    assert abs(silu(np.array([-50.0]))[0]) < 1e-19
+
+
+def test_prologue_split_with_state_equals_one_shot():
+    """Running tokens [0, T1) and then [T1, T) with the conv state handed on
+    equals one run over [0, T); one-token steps too; a sequence shorter than 3
+    tokens carries the older state entries on."""
+    from oracle.prologue import shortconv_l2norm
+    T, H, d = 13, 2, 8
+    xs, ws = _prologue_inputs(T, H, d, seed=11)
+    full = shortconv_l2norm(*xs, *ws, [0, T], H, d)
+    T1 = 5
+    a = shortconv_l2norm(*[x[:T1] for x in xs], *ws, [0, T1], H, d)
+    st = a[3]
+    outs = [a[:3]]
+    for t in range(T1, T):                      # one-token steps
+        r = shortconv_l2norm(*[x[t:t + 1] for x in xs], *ws, [0, 1], H, d, state=st)
+        st = r[3]
+        outs.append(r[:3])
+    for z in range(3):
+        got = np.concatenate([o[z] for o in outs], axis=0)
+        assert np.allclose(got, full[z], rtol=0, atol=1e-13)
+    assert np.allclose(st, full[3], rtol=0, atol=0)
+    # a 2-token sequence keeps the last state entry
+    r = shortconv_l2norm(*[x[:2] for x in xs], *ws, [0, 2], H, d, state=full[3])
+    assert np.array_equal(r[3][0, :, 0], full[3][0, :, 2])
