@@ -86,7 +86,8 @@ def parse():
                     help="heads of the workload the CPU oracle runs (sample)")
     ap.add_argument("--ws-chunks", type=int, default=T // C,
                     help="chunks per pass the prefill workspace holds (T/64 = one pass)")
-    ap.add_argument("--only", choices=["all", "prefill", "decode", "prologue", "copy"],
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "prologue", "workloads",
+                                       "copy"],
                     default="all",
                     help="profiling aid: run one part only (prints a diagnostic line, "
                          "not the bench line)")
@@ -165,6 +166,50 @@ def bench_prefill(args, torch, kda, synth):
     p95 = lambda x: sorted(x)[int(0.95 * (len(x) - 1))]
     return dict(step_ms=mean(fsteps), p95_step_ms=p95(fsteps), fused_ms=mean(fz),
                 sep_step_ms=mean(ssteps), chunk_ms=mean(ch), gate_ms=mean(gt))
+
+
+def bench_prefill_workload(args, torch, kda, synth, idx):
+    """kda_chunk_prefill_gated on prefill workload idx at its full size (2: 8 packed
+    sequences of 32,768 tokens with initial states; 3: one sequence of 131,072
+    tokens), one pass (the workspace holds every chunk of the longest sequence)."""
+    dev = "cuda:0"
+    c = synth.CONFIGS[idx]
+    dr = synth.draw_config(idx, device=dev)
+    cu_h = dr.cu_seqlens
+    cu_d = cu_h.to(dev)
+    Tw = int(cu_h[-1])
+    Nw = cu_h.numel() - 1
+    max_len = int((cu_h[1:] - cu_h[:-1]).max())
+    ws = torch.empty(kda.chunk_prefill_workspace_bytes(Nw, H, D, D, (max_len + C - 1) // C),
+                     dtype=torch.uint8, device=dev)
+    o = torch.empty((Tw, H, D), dtype=torch.bfloat16, device=dev)
+    Sf = torch.empty((Nw, H, D, D), dtype=torch.float32, device=dev)
+
+    def call():
+        kda.chunk_prefill_gated(dr.q, dr.k, dr.v, dr.x, dr.b, dr.A_log, dr.dt_bias, cu_d,
+                                dr.initial_state, out=o, final_state=Sf, cu_seqlens_host=cu_h,
+                                workspace=ws)
+    reps = max(1, min(args.steps, 10))
+    for _ in range(2):
+        call()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(args.repeats):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ev[0].record()
+        for i in range(reps):
+            call()
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        times += [ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]
+    ms = sum(times) / len(times)
+    nbytes = (Tw * PREFILL_TOKEN_BYTES + Nw * H * D * D * 4 * (2 if dr.initial_state is not None else 1)
+              + H * 4 + H * D * 4)
+    del ws, dr
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return dict(workload=c["name"], tokens=Tw,
+                sequences=Nw, ms=ms, tokens_per_s=Tw / (ms * 1e-3), alg_GBps=gbs,
+                frac=gbs / HBM_PEAK_GBS)
 
 
 def bench_decode(args, torch, kda, synth):
@@ -317,6 +362,8 @@ def main():
                                      gated_bf16_pool=bench_decode_gated(args, torch, kda, synth,
                                                                         torch.bfloat16)),
               "prologue": lambda: bench_prologue(args, torch, kda),
+              "workloads": lambda: {str(i): bench_prefill_workload(args, torch, kda, synth, i)
+                                    for i in (2, 3)},
               "copy": lambda: bench_copy(args, torch)}[args.only]
         print(json.dumps({"diagnostic": args.only, **fn()}), flush=True)
         return
@@ -333,6 +380,12 @@ def main():
         dg[name] = bench_decode_gated(args, torch, kda, synth, sdt)
         print("decode %s: %.4f ms/step, %.1f GB/s" % (name, dg[name]["ms_per_step"],
                                                      dg[name]["GBps"]),
+              file=sys.stderr, flush=True)
+    wl = {}
+    for i, name in ((2, "varlen_8seq_32768"), (3, "long_131072")):
+        wl[name] = bench_prefill_workload(args, torch, kda, synth, i)
+        print("prefill workload %s: %.3f ms, %.2f M tokens/s" % (name, wl[name]["ms"],
+                                                                 wl[name]["tokens_per_s"] / 1e6),
               file=sys.stderr, flush=True)
     pro = bench_prologue(args, torch, kda)
     print("prologue (short conv + SiLU + q/k L2 norm): %.4f ms, %.1f GB/s"
@@ -379,6 +432,7 @@ def main():
                              **{k: {kk: dg[k][kk] for kk in ("ms_per_step", "GBps", "frac",
                                                              "tokens_per_s", "bytes_per_step")}
                                 for k in dg}}},
+        "prefill_workloads": wl,
         "prologue": {"workload": "kda_shortconv_l2norm T=4096 H=96 bf16 q/k/v in and out, "
                                  "SiLU, conv state out",
                      "ms": pro["ms"], "GBps": pro["GBps"], "frac": pro["frac"],
