@@ -71,6 +71,26 @@ def test_edge_shapes(lengths, H):
     _check_small(lengths, H, torch.bfloat16, True, seed=100 + sum(lengths) + H, scale=0.7)
 
 
+def test_edge_many_sequences():
+    """70 packed sequences of 0..39 tokens: more than the 64 that the state
+    kernel orders longest first, so workgroups map to sequences in order."""
+    need_gpu()
+    lengths = np.random.default_rng(5).integers(0, 40, 70).tolist()
+    _check_small(lengths, 2, torch.bfloat16, True, seed=170, scale=0.7)
+
+
+def test_edge_all_sequences_empty():
+    """T_tot = 0 with three zero-length sequences: no output rows, and every
+    final state is its initial state, bit for bit."""
+    need_gpu()
+    say("prefill all sequences empty")
+    dr = draw_prefill([0, 0, 0], H=2, dtype=torch.bfloat16, init_state=True, seed=171)
+    g, beta = oracle_gate_f32(dr)
+    o, Sf = _run_gpu(dr, g, beta, torch.float32, 1.0, dr.initial_state)
+    assert o.shape == (0, 2, 128)
+    assert torch.equal(Sf.cpu(), dr.initial_state)
+
+
 def test_edge_no_initial_state_fp32_inputs():
     need_gpu()
     _check_small([65, 130], 4, torch.float32, False, seed=7)
