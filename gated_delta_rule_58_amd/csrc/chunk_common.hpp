@@ -101,6 +101,17 @@ __device__ __forceinline__ void buf_to_lds16(__amdgpu_buffer_rsrc_t r, lds_ptr_t
 }
 // All of this wave's outstanding vector-memory operations have completed.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+// Workgroup barrier without the memory fence of __syncthreads, whose release
+// half makes every wave drain its outstanding vector-memory operations
+// (vmcnt 0) first.  Only the compiler is kept from moving memory operations
+// across it.  For code where each wave that writes data for others waits for
+// its own writes (counter waits on buffer-to-LDS copies) and every LDS read of
+// a buffer is consumed before the barrier after which that buffer is refilled.
+__device__ __forceinline__ void barrier_nofence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 // ---- workspace image of one (chunk, head), all offsets in bytes.
 // The prep kernel writes each part straight from its registers (128 bytes to

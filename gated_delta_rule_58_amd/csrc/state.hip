@@ -43,7 +43,6 @@ constexpr int DV = 64;  // value columns per workgroup
 constexpr int NT = D / DV;
 constexpr int NTHR_S = NTHR + 128;  // 4 compute waves + 2 data waves
 constexpr int IMG_UNITS = Ws::bytes / 1024;
-constexpr int IMG_SPLIT = (IMG_UNITS + 1) / 2;  // image units copied by data wave 4
 constexpr int TILE_BYTES = C * DV * 2;  // bf16 v or o tile of one chunk
 
 struct StateLds {
@@ -52,6 +51,24 @@ struct StateLds {
   static constexpr int off_o = off_v + 2 * TILE_BYTES;          // 2 bf16 o tiles
   static constexpr int total = off_o + 2 * TILE_BYTES;
 };
+// byte offset of (row r, column j < 64) in the bf16 o tile, written 4 columns
+// of one row per lane with the 16 rows of a tile on distinct 16-byte slots.
+__device__ __forceinline__ int otile_off(int r, int j) {
+  return r * 128 + ((((j >> 3) ^ (r & 7))) << 4) + ((j & 7) << 1);
+}
+__device__ __forceinline__ int otile_swz(int r) { return r & 7; }
+// Image halves: the front (K e^gamma, Q e^gamma) is what a chunk's first
+// products read, the back (the rest) what its later products read.
+constexpr int FRONT_UNITS = Ws::KDT / 1024;          // 32
+constexpr int BACK_UNITS = IMG_UNITS - FRONT_UNITS;  // 27
+static_assert(Ws::KE == 0 && Ws::QE + 16384 == Ws::KDT, "front = KE, QE");
+// s_waitcnt immediate that waits until at most N vector-memory operations of
+// this wave are outstanding (lgkm and export counts left unconstrained)
+template <int N>
+__device__ __forceinline__ void wait_vm_le() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
 static_assert(StateLds::total <= 160 * 1024, "LDS budget");
 
 // byte offset of (row r, column j < 64) in the bf16 v tile: 128-byte rows,
@@ -61,12 +78,6 @@ __device__ __forceinline__ int vtile_off(int r, int j) {
   return r * 128 + ((((j >> 3) ^ (((r >> 2) & 3) << 1))) << 4) + ((j & 7) << 1);
 }
 __device__ __forceinline__ int vtile_swz(int r) { return ((r >> 2) & 3) << 1; }
-// byte offset of (row r, column j < 64) in the bf16 o tile, written 4 columns
-// of one row per lane with the 16 rows of a tile on distinct 16-byte slots.
-__device__ __forceinline__ int otile_off(int r, int j) {
-  return r * 128 + ((((j >> 3) ^ (r & 7))) << 4) + ((j & 7) << 1);
-}
-__device__ __forceinline__ int otile_swz(int r) { return r & 7; }
 
 template <bool QKV_BF16, bool O_BF16>
 __global__ void __launch_bounds__(NTHR_S, 1) state_kernel(
@@ -116,18 +127,23 @@ __global__ void __launch_bounds__(NTHR_S, 1) state_kernel(
     return make_buf(b, (uint32_t)(rows_of(c) * HD * esz - (h * D + col0) * esz));
   };
 
-  // ---- data waves: image and v tile of chunk c into LDS; o tile of chunk c
-  // out.  Wave 4 copies image units [0, IMG_SPLIT), wave 5 the rest of the
-  // image and the v tile; each stores half of the o tile.
-  auto load_chunk = [&](int c) {
-    const char* src = ws + ((int64_t)(n * S_len + (c - c_lo)) * H + h) * Ws::bytes;
-    const auto rs = make_buf(src, Ws::bytes);
+  // ---- data waves: the front or the back of chunk c's image into LDS.  Each
+  // wave takes half of either part; wave 5 adds the v tile to the front.
+  const int mw = w - 4;
+  constexpr int F0 = FRONT_UNITS / 2, B0 = BACK_UNITS / 2;  // wave 4: 16 + 13 ops
+  constexpr int F1 = FRONT_UNITS - F0 + (QKV_BF16 ? 8 : 0);  // wave 5: 16 (+8 v) + 14 ops
+  constexpr int B1 = BACK_UNITS - B0;
+  auto img_src = [&](int c) {
+    return make_buf(ws + ((int64_t)(n * S_len + (c - c_lo)) * H + h) * Ws::bytes, Ws::bytes);
+  };
+  auto load_front = [&](int c) {
+    const auto rs = img_src(c);
     char* dst = img_of(c);
-    const int u0 = w == 4 ? 0 : IMG_SPLIT, u1 = w == 4 ? IMG_SPLIT : IMG_UNITS;
+    const int u0 = mw == 0 ? 0 : FRONT_UNITS / 2, u1 = mw == 0 ? FRONT_UNITS / 2 : FRONT_UNITS;
 #pragma unroll 2
     for (int u = u0; u < u1; ++u)
       buf_to_lds16(rs, (lds_ptr_t)(dst + u * 1024), lane * 16, u * 1024);
-    if (w == 4) return;
+    if (mw == 0) return;
     if constexpr (QKV_BF16) {  // 8 rows of 128 bytes per round; lane writes slot lane&7
       const auto rv = tok_buf(v, 2, c);
       char* vt = vt_of(c);
@@ -140,18 +156,26 @@ __global__ void __launch_bounds__(NTHR_S, 1) state_kernel(
       }
     }
   };
-  auto store_o = [&](int c) {  // rows [32(w-4), 32(w-4) + 32) of the tile
+  auto store_o = [&](int c) {  // rows [32 mw, 32 mw + 32) of chunk c's bf16 o tile
     const auto ro = tok_buf(o, 2, c);
     const char* ot = ot_of(c);
     typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
-    for (int u = 4 * (w - 4); u < 4 * (w - 4) + 4; ++u) {
+    for (int u = 4 * mw; u < 4 * mw + 4; ++u) {
       const int r = 8 * u + (lane >> 3);
       const int j = (lane & 7) ^ otile_swz(r);  // logical chunk held by slot lane&7
       const u32x4 x = *reinterpret_cast<const u32x4*>(ot + r * 128 + (lane & 7) * 16);
       __builtin_amdgcn_raw_buffer_store_b128(x, ro, (lane >> 3) * HD * 2 + j * 16,
                                              8 * u * HD * 2, 0);
     }
+  };
+  auto load_back = [&](int c) {
+    const auto rs = img_src(c);
+    char* dst = img_of(c);
+    const int u0 = FRONT_UNITS + (mw == 0 ? 0 : B0), u1 = mw == 0 ? FRONT_UNITS + B0 : IMG_UNITS;
+#pragma unroll 2
+    for (int u = u0; u < u1; ++u)
+      buf_to_lds16(rs, (lds_ptr_t)(dst + u * 1024), lane * 16, u * 1024);
   };
 
   // ---- state slice (compute waves): tile t holds key rows 16t + 4lg + i, column jcol.
@@ -181,23 +205,69 @@ __global__ void __launch_bounds__(NTHR_S, 1) state_kernel(
             rv, (4 * lg * HD + jl) * 4, (16 * rt + i) * HD * 4, 0);
   };
 
-  if (c_lo < c_end) {
-    if (mover) load_chunk(c_lo);
-    else if constexpr (!QKV_BF16) load_v_regs(c_lo);
-    wait_vmem();
-  }
-  __syncthreads();
-
-  for (int c = c_lo; c < c_end; ++c) {
-    const bool more = c + 1 < c_end;
-    if (mover) {
-      // loads first: the image has the whole chunk to arrive
-      if (more) load_chunk(c + 1);
+  // Two workgroup barriers per chunk c: A once its image front (and v tile)
+  // is in LDS, B once its back is.  The data waves keep the stream going:
+  // the front of c+1 is issued right after B(c-1) (the front of c-1 is read
+  // by then) and the back of c+1 right after A(c) (the back of c-1 likewise),
+  // and each wave waits with a counter bound that leaves the later part in
+  // flight.  The compute waves write o tiles into LDS (bf16 o), which the data
+  // waves store after the next A barrier, or straight to o (fp32 o).  The
+  // barriers carry no memory fence (a fence would drain the data waves'
+  // loads): the data waves wait for their own copies with counter bounds, and
+  // every LDS read of a buffer feeds a product before the barrier after which
+  // that buffer is refilled.
+  // (Separate loops for the two roles: the compiler's counter analysis then
+  // never sees a buffer-to-LDS copy pending on the compute waves' path, which
+  // would make every chunk's first LDS read wait for all their o stores.)
+  if (mover) {
+    if (c_lo < c_end) {
+      load_front(c_lo);
+      load_back(c_lo);
+    }
+    for (int c = c_lo; c < c_end; ++c) {
+      const bool more = c + 1 < c_end;
+      if (more) load_front(c + 1);
+      // front of c done: at most back(c) [+ front(c+1)] outstanding
+      if (mw == 0) {
+        if (more) wait_vm_le<B0 + F0>();
+        else wait_vm_le<B0>();
+      } else {
+        if (more) wait_vm_le<B1 + F1>();
+        else wait_vm_le<B1>();
+      }
+      barrier_nofence();  // A(c)
+      if (more) load_back(c + 1);
+      // chunk c-1's o tile is complete (its writers passed A(c)); the stores
+      // only add to the counter, which keeps the waits below conservative
       if constexpr (O_BF16) {
         if (c > c_lo) store_o(c - 1);
       }
-      wait_vmem();
-    } else {
+      // back of c done: at most front(c+1) + back(c+1) outstanding
+      if (more) {
+        if (mw == 0) wait_vm_le<F0 + B0>();
+        else wait_vm_le<F1 + B1>();
+      } else {
+        wait_vmem();
+      }
+      barrier_nofence();  // B(c)
+    }
+    if constexpr (O_BF16) {
+      if (c_lo < c_end) {
+        barrier_nofence();  // A(c_end): the last o tile is complete
+        store_o(c_end - 1);
+      }
+    }
+    return;
+  }
+
+  if constexpr (!QKV_BF16) {
+    if (c_lo < c_end) load_v_regs(c_lo);
+  }
+  for (int c = c_lo; c < c_end; ++c) {
+    const bool more = c + 1 < c_end;
+    if constexpr (!QKV_BF16) wait_vmem();  // this chunk's v registers
+    barrier_nofence();  // A(c)
+    {
       const char* im = img_of(c);
       float vcur[16];
       if constexpr (QKV_BF16) {
@@ -241,6 +311,7 @@ __global__ void __launch_bounds__(NTHR_S, 1) state_kernel(
       for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) Xacc[rt][i] = vcur[4 * rt + i] - Xacc[rt][i];
+      barrier_nofence();  // B(c): the image back is in LDS
       // -- Delta = (T diag(b)) X, T = (I + A)^-1 lower triangular: row block
       // rt sums the X block pairs ks with 2ks <= rt (the tile (rt, 2ks+1) above
       // the diagonal is 0); four independent chains of at most four products.
@@ -268,9 +339,8 @@ __global__ void __launch_bounds__(NTHR_S, 1) state_kernel(
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) bfrag_split(Dacc[2 * ks], Dacc[2 * ks + 1], dbh[ks], dbl[ks]);
       // -- O^T += Delta^T P^T: lane (lr, lg) of tile rt then holds token row
-      // 16rt + lr, value columns 16w + 4lg .. +3.  bf16: into the LDS o tile
-      // (the data wave stores it); fp32: straight to o (rows past the chunk end
-      // are dropped).
+      // 16rt + lr, value columns 16w + 4lg .. +3, stored straight to o (8 or
+      // 16 bytes per lane; rows past the chunk end are dropped)
       const auto ro = tok_buf(o, OS, c);
       char* ot = ot_of(c);
 #pragma unroll
@@ -299,8 +369,8 @@ __global__ void __launch_bounds__(NTHR_S, 1) state_kernel(
           *reinterpret_cast<bf16x4*>(ot + otile_off(row, j0)) = ob;
         } else {
           typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, ao), ro, j0 * 4,
-                                                 row * HD * 4, 0);
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, ao), ro,
+                                                 (row * HD + j0) * 4, 0, 0);
         }
       }
       // -- S <- e^gamma_C S + Khat^T Delta
@@ -317,16 +387,13 @@ __global__ void __launch_bounds__(NTHR_S, 1) state_kernel(
         }
         Sacc[t] = s;
       }
-      if constexpr (!QKV_BF16 || !O_BF16) wait_vmem();
     }
-    __syncthreads();
   }
 
-  if (mover) {
-    if constexpr (O_BF16) {
-      if (c_lo < c_end) store_o(c_end - 1);
-    }
-  } else if (S_out) {
+  if constexpr (O_BF16) {
+    if (c_lo < c_end) barrier_nofence();  // A(c_end): hands the last o tile to the data waves
+  }
+  if (S_out) {
 #pragma unroll
     for (int t = 0; t < 8; ++t)
 #pragma unroll
