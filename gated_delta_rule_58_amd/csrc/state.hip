@@ -26,8 +26,9 @@
 // waves never wait on a memory instruction.  The copy is split over two waves
 // so that neither has more memory instructions in flight than its counter
 // holds (63): one wave issuing all 75 of them stalls on its own first loads.
-// One workgroup barrier per chunk.  (fp32 v or o, used only
-// off the benchmarked path, go through the compute waves' registers instead.)
+// Two workgroup barriers per chunk (image front, image back), so the copy of
+// the next chunk streams without a gap.  (fp32 v or o, used only off the
+// benchmarked path, go through the compute waves' registers instead.)
 //
 // Precision: operands are fp16 MFMA fragments with fp32 accumulation; X and
 // Delta enter the products as hi+lo fp16 pairs, the state as one fp16 value
