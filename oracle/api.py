@@ -38,7 +38,7 @@ def _lib():
             build_oracle()
         lib = ctypes.CDLL(path)
         lib.kdao_gate.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _dp, _dp, _dp,
-                                  _dp, _dp, _dp]
+                                  ctypes.c_int32, _dp, _dp, _dp]
         lib.kdao_gate.restype = None
         lib.kdao_prefill.argtypes = [ctypes.c_int32, _ip, ctypes.c_int32, ctypes.c_int32,
                                      ctypes.c_int32, _dp, _dp, _dp, _dp, _dp, ctypes.c_double,
@@ -68,14 +68,19 @@ def _p(a: Optional[np.ndarray]):
 
 
 def gate(x, b, A_log, dt_bias):
-    """g = -exp(A_log[h]) softplus(x + dt_bias[h,c]); beta = sigmoid(b). fp64."""
+    """g = -exp(A_log) softplus(x + dt_bias[h,c]); beta = sigmoid(b). fp64.
+
+    A_log is per head, [H], or per (head, channel), [H, d]: the per-channel
+    form is the variant the Kimi K3 artifact audit (§5.2) leaves open for the
+    checkpoint's A_log; it is taken only when given explicitly as [H, d]."""
     x, b, A_log, dt_bias = f64(x), f64(b), f64(A_log), f64(dt_bias)
     T, H, d = x.shape
-    if b.shape != (T, H) or A_log.shape != (H,) or dt_bias.size != H * d:
+    if A_log.shape not in ((H,), (H, d)) or b.shape != (T, H) or dt_bias.size != H * d:
         raise ValueError("gate: shape mismatch")
     g = np.empty_like(x)
     beta = np.empty_like(b)
-    _lib().kdao_gate(T, H, d, _p(x), _p(b), _p(A_log), _p(dt_bias), _p(g), _p(beta))
+    _lib().kdao_gate(T, H, d, _p(x), _p(b), _p(A_log), int(A_log.ndim == 2), _p(dt_bias), _p(g),
+                     _p(beta))
     return g, beta
 
 

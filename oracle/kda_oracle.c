@@ -44,12 +44,14 @@
 static double softplus(double z) { return fmax(z, 0.0) + log1p(exp(-fabs(z))); }
 
 void kdao_gate(int64_t n_tok, int32_t H, int32_t d, const double* x, const double* b,
-               const double* A_log, const double* dt_bias, double* g, double* beta) {
+               const double* A_log, int32_t a_per_channel, const double* dt_bias, double* g,
+               double* beta) {
   for (int64_t t = 0; t < n_tok; ++t) {
     for (int32_t h = 0; h < H; ++h) {
-      const double a = exp(A_log[h]);
       for (int32_t c = 0; c < d; ++c) {
         const int64_t i = (t * H + h) * (int64_t)d + c;
+        /* A_log per head [H], or per (head, channel) [H, d] */
+        const double a = exp(a_per_channel ? A_log[(int64_t)h * d + c] : A_log[h]);
         g[i] = -a * softplus(x[i] + dt_bias[(int64_t)h * d + c]);
       }
       beta[t * H + h] = 1.0 / (1.0 + exp(-b[t * H + h]));

@@ -94,6 +94,33 @@ def test_gate_matches_library_softplus_and_expit():
     assert np.all(g <= 0)
 
 
+def test_gate_per_channel_alog():
+    """A_log given per (head, channel), [H, d] (the variant the audit page's
+    §5.2 leaves open, taken only when passed explicitly): channel c of every
+    head gets the per-head gate with A_log[:, c], against numpy.logaddexp,
+    and a constant row reproduces the per-head result exactly.  H != d with
+    distinct values, so a transposed or per-head-only index fails."""
+    r = rng(11)
+    T, H, d = 4, 3, 5
+    x = r.standard_normal((T, H, d)) * 4
+    b = r.standard_normal((T, H))
+    dt = r.normal(-4.6, 1.2, (H, d))
+    A = r.uniform(-0.75, 1.5, (H, d))
+    g, beta = oracle.gate(x, b, A, dt)
+    ref = -np.exp(A)[None] * np.logaddexp(0.0, x + dt[None])
+    assert np.allclose(g, ref, rtol=1e-14, atol=1e-300)
+    for c in range(d):
+        gc, bc = oracle.gate(x, b, A[:, c].copy(), dt)
+        assert np.array_equal(g[:, :, c], gc[:, :, c])
+        assert np.array_equal(beta, bc)
+    a_head = r.uniform(-0.75, 1.5, H)
+    g_pc, _ = oracle.gate(x, b, np.repeat(a_head[:, None], d, axis=1), dt)
+    g_ph, _ = oracle.gate(x, b, a_head, dt)
+    assert np.array_equal(g_pc, g_ph)
+    with pytest.raises(ValueError):
+        oracle.gate(x, b, np.zeros(d), dt)       # a bare [d] is not reshaped
+
+
 # ------------------------------------------------------------ recurrence pins
 
 def test_single_token_closed_form():
