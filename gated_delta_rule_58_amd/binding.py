@@ -108,6 +108,15 @@ def _ptr(t: Optional[torch.Tensor]):
     return t.data_ptr()
 
 
+def _alog(A_log: torch.Tensor, H: int, d: int) -> torch.Tensor:
+    """A_log as the library takes it: [H] per head, or [H, d] per (head, channel).
+    A 2-D tensor of another shape is refused here (its flat length could pass
+    for [H, d] with the axes swapped); 1-D lengths are checked by the library."""
+    if A_log.dim() == 2 and tuple(A_log.shape) != (H, d):
+        raise ValueError(f"A_log must be [H] or [H, d] = [{H}, {d}], got {tuple(A_log.shape)}")
+    return A_log.contiguous()
+
+
 def _stream(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
@@ -115,8 +124,10 @@ def _stream(device) -> int:
 def gate(x: torch.Tensor, b: torch.Tensor, A_log: torch.Tensor, dt_bias: torch.Tensor,
          g_out: Optional[torch.Tensor] = None, beta_out: Optional[torch.Tensor] = None
          ) -> Tuple[torch.Tensor, torch.Tensor]:
-    """kda_gate: x [T,H,d], b [T,H] -> g [T,H,d] fp32, beta [T,H] fp32."""
+    """kda_gate: x [T,H,d], b [T,H], A_log [H] or [H,d], dt_bias [H,d]
+    -> g [T,H,d] fp32, beta [T,H] fp32."""
     T, H, d = x.shape
+    A_log = _alog(A_log, H, d)
     if g_out is None:
         g_out = torch.empty((T, H, d), dtype=torch.float32, device=x.device)
     if beta_out is None:
@@ -201,11 +212,11 @@ def chunk_prefill_gated(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, x: to
                         workspace: Optional[torch.Tensor] = None,
                         max_workspace_bytes: int = DEFAULT_WORKSPACE_BYTES):
     """kda_chunk_prefill_gated: the gate's raw inputs (x [T,H,dk] logits, b [T,H]
-    beta logits, A_log [H], dt_bias [H,dk]) instead of g and beta."""
+    beta logits, A_log [H] or [H,dk], dt_bias [H,dk]) instead of g and beta."""
     T, H, dk, dv, dev, cu_seqlens, hp, N, out, final_state, workspace = _prefill_common(
         q, v, cu_seqlens, cu_seqlens_host, initial_state, output_final_state, o_dtype, out,
         final_state, workspace, max_workspace_bytes)
-    A_log = A_log.contiguous()
+    A_log = _alog(A_log, H, dk)
     dt_bias = dt_bias.contiguous()
     st = lib().kda_chunk_prefill_gated(
         _ptr(q), _ptr(k), _ptr(v), _dt(q), _ptr(x), _dt(x), _ptr(b), _dt(b), _ptr(A_log),
@@ -236,7 +247,7 @@ def recurrent_decode_gated(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, x:
                            state: torch.Tensor, state_indices: Optional[torch.Tensor] = None,
                            scale: float = 1.0, o_dtype: Optional[torch.dtype] = None,
                            out: Optional[torch.Tensor] = None):
-    """kda_recurrent_decode_gated: q/k/v/x [N,H,d], b [N,H], A_log [H], dt_bias [H,d];
+    """kda_recurrent_decode_gated: q/k/v/x [N,H,d], b [N,H], A_log [H] or [H,d], dt_bias [H,d];
     state pool [num_slots,H,dk,dv] (float32 or bfloat16) updated in place;
     state_indices [N] int32 on the device (None: sequence n uses slot n).
     Returns o (zeros for sequences whose slot is outside the pool)."""
@@ -244,6 +255,7 @@ def recurrent_decode_gated(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, x:
     dv = v.shape[2]
     if state_indices is not None and state_indices.dtype != torch.int32:
         raise TypeError("state_indices must be int32")
+    A_log = _alog(A_log, H, dk)
     if out is None:
         out = torch.empty((N, H, dv), dtype=o_dtype or q.dtype, device=q.device)
     st = lib().kda_recurrent_decode_gated(

@@ -31,6 +31,18 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 bool known_dtype(kda_dtype d) { return d == KDA_F32 || d == KDA_BF16; }
 
+// A_log is one value per head ([H]) or, given explicitly, one per (head,
+// channel) ([H, d]); any other length, the checkpoint's [128] among them, is
+// refused rather than reshaped (Kimi K3 artifact audit, §5.2).
+kda_status check_alog(const char* fn, int64_t len, int32_t H, int32_t d, bool* per_channel) {
+  *per_channel = len != H && len == (int64_t)H * d;
+  if (len == H || *per_channel) return KDA_OK;
+  return fail(KDA_ERR_SHAPE,
+              "%s: A_log has %lld values but H = %d, d = %d; A_log must be [H] (per head) or "
+              "[H, d] (per head and channel); other shapes are refused, not reshaped",
+              fn, (long long)len, H, d);
+}
+
 kda_status launched(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(KDA_ERR_LAUNCH, "%s: launch failed: %s", what, hipGetErrorString(e));
   return ok();
@@ -53,11 +65,8 @@ kda_status kda_gate(const void* x, kda_dtype x_dt, const void* b, kda_dtype b_dt
                 (long long)n_tok, H, d);
   if (!known_dtype(x_dt) || !known_dtype(b_dt))
     return fail(KDA_ERR_DTYPE, "kda_gate: x_dt and b_dt must be KDA_F32 or KDA_BF16");
-  if (A_log_len != H)
-    return fail(KDA_ERR_SHAPE,
-                "kda_gate: A_log has %lld values but H = %d; A_log must be one value per head "
-                "([H]); a per-channel or checkpoint-shaped A_log is refused, not reshaped",
-                (long long)A_log_len, H);
+  bool alog_pc = false;
+  if (const kda_status st = check_alog("kda_gate", A_log_len, H, d, &alog_pc)) return st;
   if (dt_bias_len != (int64_t)H * d)
     return fail(KDA_ERR_SHAPE, "kda_gate: dt_bias has %lld values, need H*d = %lld",
                 (long long)dt_bias_len, (long long)H * d);
@@ -73,8 +82,9 @@ kda_status kda_gate(const void* x, kda_dtype x_dt, const void* b, kda_dtype b_dt
   if (!aligned(x, x_dt == KDA_BF16 ? 8 : 16) || !aligned(g_out, 16) || !aligned(dt_bias, 16))
     return fail(KDA_ERR_ALIGNMENT, "kda_gate: x, g_out and dt_bias must be 16-byte aligned "
                                    "(8-byte for bf16 x)");
-  return launched(kda::launch_gate(x, x_dt == KDA_BF16, b, b_dt == KDA_BF16, A_log, dt_bias, g_out,
-                                   beta_out, n_tok, H, d, static_cast<hipStream_t>(stream)),
+  return launched(kda::launch_gate(x, x_dt == KDA_BF16, b, b_dt == KDA_BF16, A_log, alog_pc,
+                                   dt_bias, g_out, beta_out, n_tok, H, d,
+                                   static_cast<hipStream_t>(stream)),
                   "kda_gate");
 }
 
@@ -169,25 +179,24 @@ kda_status kda_chunk_prefill_gated(const void* q, const void* k, const void* v, 
   const char* fn = "kda_chunk_prefill_gated";
   if (!known_dtype(x_dt) || !known_dtype(b_dt))
     return fail(KDA_ERR_DTYPE, "%s: x_dt and b_dt must be KDA_F32 or KDA_BF16", fn);
-  if (H > 0 && A_log_len != H)
-    return fail(KDA_ERR_SHAPE,
-                "%s: A_log has %lld values but H = %d; A_log must be one value per head "
-                "([H]); a per-channel or checkpoint-shaped A_log is refused, not reshaped",
-                fn, (long long)A_log_len, H);
+  bool alog_pc = false;
+  if (H > 0)
+    if (const kda_status st = check_alog(fn, A_log_len, H, dk, &alog_pc)) return st;
   if (H > 0 && dt_bias_len != (int64_t)H * dk)
     return fail(KDA_ERR_SHAPE, "%s: dt_bias has %lld values, need H*dk = %lld", fn,
                 (long long)dt_bias_len, (long long)H * dk);
   if (!A_log || !dt_bias) return fail(KDA_ERR_INVALID_ARG, "%s: A_log/dt_bias is NULL", fn);
-  if (!aligned(dt_bias, 16))
-    return fail(KDA_ERR_ALIGNMENT, "%s: dt_bias must be 16-byte aligned", fn);
+  if (!aligned(dt_bias, 16) || (alog_pc && !aligned(A_log, 16)))
+    return fail(KDA_ERR_ALIGNMENT, "%s: dt_bias (and a per-channel A_log) must be 16-byte "
+                                   "aligned", fn);
   const kda_status st = check_prefill(fn, q, k, v, qkv_dt, x, 16, b, b_dt == KDA_BF16 ? 2 : 4,
                                       cu_seqlens, cu_seqlens_host, N, initial_state, final_state,
                                       o, o_dt, T_tot, H, dk, dv, scale, workspace,
                                       workspace_bytes);
   if (st != KDA_OK) return st;
-  return launched(kda::launch_chunk_prefill(q, k, v, qkv_dt == KDA_BF16, x,
-                                            x_dt == KDA_BF16 ? 2 : 1, b, b_dt == KDA_BF16, A_log,
-                                            dt_bias, cu_seqlens, cu_seqlens_host, N,
+  const int g_mode = (x_dt == KDA_BF16 ? 2 : 1) | (alog_pc ? 4 : 0);
+  return launched(kda::launch_chunk_prefill(q, k, v, qkv_dt == KDA_BF16, x, g_mode, b,
+                                            b_dt == KDA_BF16, A_log, dt_bias, cu_seqlens, cu_seqlens_host, N,
                                             initial_state, final_state, o, o_dt == KDA_BF16,
                                             T_tot, H, scale, workspace, workspace_bytes,
                                             static_cast<hipStream_t>(stream)),
@@ -257,11 +266,8 @@ kda_status kda_recurrent_decode_gated(const void* q, const void* k, const void* 
   if (dk != 128 || dv != 128)
     return fail(KDA_ERR_UNSUPPORTED, "%s: only dk = dv = 128 is implemented (got %d, %d)", fn,
                 dk, dv);
-  if (A_log_len != H)
-    return fail(KDA_ERR_SHAPE,
-                "%s: A_log has %lld values but H = %d; A_log must be one value per head "
-                "([H]); a per-channel or checkpoint-shaped A_log is refused, not reshaped",
-                fn, (long long)A_log_len, H);
+  bool alog_pc = false;
+  if (const kda_status st = check_alog(fn, A_log_len, H, dk, &alog_pc)) return st;
   if (dt_bias_len != (int64_t)H * dk)
     return fail(KDA_ERR_SHAPE, "%s: dt_bias has %lld values, need H*dk = %lld", fn,
                 (long long)dt_bias_len, (long long)H * dk);
@@ -301,7 +307,7 @@ kda_status kda_recurrent_decode_gated(const void* q, const void* k, const void* 
       return fail(KDA_ERR_INVALID_ARG, "%s: the state pool overlaps another tensor", fn);
   }
   return launched(kda::launch_decode_gated(q, k, v, qkv_dt == KDA_BF16, x, x_dt == KDA_BF16, b,
-                                           b_dt == KDA_BF16, A_log, dt_bias, state,
+                                           b_dt == KDA_BF16, A_log, alog_pc, dt_bias, state,
                                            state_dt == KDA_BF16, num_slots, state_indices, o,
                                            o_dt == KDA_BF16, N, H, scale,
                                            static_cast<hipStream_t>(stream)),

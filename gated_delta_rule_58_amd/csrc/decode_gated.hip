@@ -2,7 +2,8 @@
 // serving, with the gate fused in and the states kept in a slot pool.
 //
 // Per (sequence n, head h) with state S = pool[slot(n), h] (128 x 128, S[c][j]):
-//   g     = -exp(A_log[h]) softplus(x + dt_bias[h])   beta = sigmoid(b)
+//   g     = -exp(A_log) softplus(x + dt_bias[h])   beta = sigmoid(b)
+//           (A_log per head, or per (head, channel) when given as [H, 128])
 //           (the arithmetic of kda_gate, per key channel; g never goes to memory)
 //   S'    = Diag(exp(g)) S
 //   delta = beta (v - S'^T k),   o = scale (S'^T q + (q.k) delta),   S = S' + k delta^T
@@ -44,7 +45,7 @@ __global__ void __launch_bounds__(NTHR, 4) decode_gated_kernel(
     const void* __restrict__ gx, const void* __restrict__ bb, bool b_bf16,
     const float* __restrict__ A_log, const float* __restrict__ dt_bias, void* __restrict__ pool,
     const int32_t* __restrict__ slots, int64_t num_slots, void* __restrict__ o, float scale,
-    int64_t pairs, int H) {
+    int64_t pairs, int H, int alog_pc) {
   constexpr int CPT = S_BF16 ? 8 : 4;  // columns per thread
   constexpr int NCG = D / CPT;         // column groups
   constexpr int NRS = NTHR / NCG;      // row slots
@@ -80,7 +81,7 @@ __global__ void __launch_bounds__(NTHR, 4) decode_gated_kernel(
       sm.qq = load1(q, p * D + t, QKV_BF16);
       sm.xv = load1(gx, p * D + t, GIN == kDX16);
       sm.db = dt_bias[h * D + t];
-      sm.alog = A_log[h];
+      sm.alog = A_log[alog_pc ? h * D + t : h];
     }
 #pragma unroll
     for (int u = 0; u < NV; ++u) sm.vv[u] = load4(v, p * D + CPT * cg + 4 * u, QKV_BF16);
@@ -247,7 +248,7 @@ __global__ void __launch_bounds__(NTHR, 4) decode_gated_kernel(
 
 hipError_t launch_decode_gated(const void* q, const void* k, const void* v, bool qkv_bf16,
                                const void* gx, bool x_bf16, const void* b, bool b_bf16,
-                               const float* A_log, const float* dt_bias, void* pool,
+                               const float* A_log, bool alog_pc, const float* dt_bias, void* pool,
                                bool state_bf16, int64_t num_slots, const int32_t* slots, void* o,
                                bool o_bf16, int N, int H, float scale, hipStream_t s) {
   const int64_t pairs = (int64_t)N * H;
@@ -258,7 +259,7 @@ hipError_t launch_decode_gated(const void* q, const void* k, const void* v, bool
 #define KDA_DG(QB, OB, GM, SB)                                                              \
   decode_gated_kernel<QB, OB, GM, SB><<<grid, NTHR, 0, s>>>(q, k, v, gx, b, b_bf16, A_log, \
                                                             dt_bias, pool, slots, num_slots, \
-                                                            o, scale, pairs, H)
+                                                            o, scale, pairs, H, alog_pc ? 1 : 0)
 #define KDA_DG_S(QB, OB, GM) \
   do {                       \
     if (state_bf16)          \

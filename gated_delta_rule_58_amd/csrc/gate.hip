@@ -1,13 +1,14 @@
-// kda_gate: log-decay g = -exp(A_log[h]) * softplus(x + dt_bias[h,c]) and
+// kda_gate: log-decay g = -exp(A_log) * softplus(x + dt_bias[h,c]) and
 // beta = sigmoid(b), one elementwise HBM-bound pass.
 //
 // Shapes per the Kimi K3 artifact audit (§4.1 KDA tensor table; §5.2 shape
-// table): A_log one value per head, dt_bias one per (head, channel).  beta is
-// squashed here in fp32 (Model-Optimizer PR #2749 review, KDA beta fix).
+// table): A_log one value per head (or, explicitly, one per (head, channel)),
+// dt_bias one per (head, channel).  beta is squashed here in fp32
+// (Model-Optimizer PR #2749 review, KDA beta fix).
 //
 // Work split: blockIdx.y picks a group of R = 256 / (d/4) heads, blockIdx.x a
 // run of tokens.  A thread owns one (head, 4-channel) slot for the whole run,
-// so -exp(A_log[h]) and its dt_bias quad are loaded once and every token costs
+// so its -exp(A_log) and dt_bias quads are formed once and every token costs
 // one 16-byte load of x and one 16-byte store of g.  A wave covers 256
 // consecutive channels of one token: fully coalesced.  beta for the block's
 // (token, head) pairs is one extra pass by one lane per pair.
@@ -41,7 +42,7 @@ template <bool XBF16, bool BBF16>
 __global__ void __launch_bounds__(kThreads) gate_kernel(
     const void* __restrict__ x, const void* __restrict__ b, const float* __restrict__ A_log,
     const float* __restrict__ dt_bias, float* __restrict__ g, float* __restrict__ beta,
-    int n_tok, int H, int d, int rows_per_block) {
+    int n_tok, int H, int d, int rows_per_block, int alog_pc) {
   const int qpr = d >> 2;
   const int tid = threadIdx.x;
   const int hh = tid / qpr;
@@ -52,7 +53,9 @@ __global__ void __launch_bounds__(kThreads) gate_kernel(
   const int64_t tok_stride = (int64_t)H * d;
 
   if (hh < rows_per_block && h < H) {
-    const float a = -expf(A_log[h]);
+    f32x4 a;  // -exp(A_log) for the thread's 4 channels
+#pragma unroll
+    for (int e = 0; e < 4; ++e) a[e] = -expf(alog_pc ? A_log[(int64_t)h * d + c + e] : A_log[h]);
     const f32x4 db = *reinterpret_cast<const f32x4*>(dt_bias + (int64_t)h * d + c);
     const int64_t base = (int64_t)tok0 * tok_stride + (int64_t)h * d + c;
     for (int t = 0; t < ntk; t += kTokUnroll) {
@@ -67,7 +70,7 @@ __global__ void __launch_bounds__(kThreads) gate_kernel(
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const float z = gate_input(xv[u][e], db[e]);
-            out[e] = gate_log_decay(a, z);
+            out[e] = gate_log_decay(a[e], z);
           }
           *reinterpret_cast<f32x4*>(g + base + (t + u) * tok_stride) = out;
         }
@@ -89,8 +92,8 @@ __global__ void __launch_bounds__(kThreads) gate_kernel(
 }  // namespace
 
 hipError_t launch_gate(const void* x, bool x_bf16, const void* b, bool b_bf16, const float* A_log,
-                       const float* dt_bias, float* g, float* beta, int64_t n_tok, int H, int d,
-                       hipStream_t s) {
+                       bool alog_pc, const float* dt_bias, float* g, float* beta, int64_t n_tok,
+                       int H, int d, hipStream_t s) {
   if (n_tok == 0) return hipSuccess;
   // d is a multiple of 4 with d/4 <= 256 (checked by the caller).
   const int rows_per_block = kThreads / (d >> 2);
@@ -107,16 +110,16 @@ hipError_t launch_gate(const void* x, bool x_bf16, const void* b, bool b_bf16, c
     const dim3 grid((nt + kTokPerBlock - 1) / kTokPerBlock, head_groups);
     if (x_bf16 && b_bf16)
       gate_kernel<true, true><<<grid, kThreads, 0, s>>>(xs, bs, A_log, dt_bias, gs, betas, nt, H,
-                                                        d, rows_per_block);
+                                                        d, rows_per_block, alog_pc ? 1 : 0);
     else if (x_bf16)
       gate_kernel<true, false><<<grid, kThreads, 0, s>>>(xs, bs, A_log, dt_bias, gs, betas, nt, H,
-                                                         d, rows_per_block);
+                                                         d, rows_per_block, alog_pc ? 1 : 0);
     else if (b_bf16)
       gate_kernel<false, true><<<grid, kThreads, 0, s>>>(xs, bs, A_log, dt_bias, gs, betas, nt, H,
-                                                         d, rows_per_block);
+                                                         d, rows_per_block, alog_pc ? 1 : 0);
     else
       gate_kernel<false, false><<<grid, kThreads, 0, s>>>(xs, bs, A_log, dt_bias, gs, betas, nt,
-                                                          H, d, rows_per_block);
+                                                          H, d, rows_per_block, alog_pc ? 1 : 0);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -9,9 +9,10 @@
 namespace kda {
 
 // ---- launchers (one per kernel family); return hipSuccess or the launch error
+// A_log per head [H], or per (head, channel) [H, d] when alog_pc.
 hipError_t launch_gate(const void* x, bool x_bf16, const void* b, bool b_bf16, const float* A_log,
-                       const float* dt_bias, float* g, float* beta, int64_t n_tok, int H, int d,
-                       hipStream_t s);
+                       bool alog_pc, const float* dt_bias, float* g, float* beta, int64_t n_tok,
+                       int H, int d, hipStream_t s);
 
 hipError_t launch_decode(const void* q, const void* k, const void* v, bool qkv_bf16,
                          const float* g, const float* beta, float* state, void* o, bool o_bf16,
@@ -23,7 +24,7 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, bool qkv_b
 // skips it (o = 0).
 hipError_t launch_decode_gated(const void* q, const void* k, const void* v, bool qkv_bf16,
                                const void* gx, bool x_bf16, const void* b, bool b_bf16,
-                               const float* A_log, const float* dt_bias, void* pool,
+                               const float* A_log, bool alog_pc, const float* dt_bias, void* pool,
                                bool state_bf16, int64_t num_slots, const int32_t* slots, void* o,
                                bool o_bf16, int N, int H, float scale, hipStream_t s);
 
@@ -41,7 +42,7 @@ hipError_t launch_shortconv(const void* xq, const void* xk, const void* xv, bool
 // Chunked prefill: prep + state kernel per pass over the chunks (prefill.hip).
 // The decay input is either g (g_mode 0, fp32) with post-sigmoid beta in b,
 // or raw gate logits x (g_mode 1 fp32, 2 bf16) with beta logits in b and the
-// gate parameters A_log [H], dt_bias [H, 128].
+// gate parameters A_log [H], dt_bias [H, 128]; g_mode | 4: A_log [H, 128].
 hipError_t launch_chunk_prefill(const void* q, const void* k, const void* v, bool qkv_bf16,
                                 const void* g, int g_mode, const void* b, bool b_bf16,
                                 const float* A_log, const float* dt_bias, const int32_t* cu,

@@ -116,11 +116,12 @@ __device__ __forceinline__ void load_row8(Row8<BF16>& R, __amdgpu_buffer_rsrc_t 
 
 // The decay input: log-decay g (fp32), or the raw gate logits x (fp32 or
 // bf16) from which g and beta are formed in registers (gate_math.hpp).
-enum GateIn { kG = 0, kX32 = 1, kX16 = 2 };
+// kPC (or-ed into kX32 / kX16): A_log per (head, channel), [H, 128].
+enum GateIn { kG = 0, kX32 = 1, kX16 = 2, kPC = 4 };
 struct GateArgs {
   const void* b;         // beta logits [T, H] (gated input) or post-sigmoid beta (fp32)
   bool b_bf16;
-  const float* A_log;    // [H]
+  const float* A_log;    // [H], or [H, 128] with kPC
   const float* dt_bias;  // [H, 128]
 };
 
@@ -176,18 +177,21 @@ __global__ void __launch_bounds__(NTHR, 3) prep_kernel(
 
   // ---- loads: row r, channels 32kk + 8lg .. +7 (dt_bias first: every gate
   // element needs it)
-  f32x4 dtb[4][2];
+  f32x4 dtb[4][2], alc[4][2];
   if constexpr (GIN != kG) {
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-      for (int a = 0; a < 2; ++a)
+      for (int a = 0; a < 2; ++a) {
         dtb[kk][a] = *reinterpret_cast<const f32x4*>(ga.dt_bias + h * D + 32 * kk + 8 * lg + 4 * a);
+        if constexpr ((GIN & kPC) != 0)
+          alc[kk][a] = *reinterpret_cast<const f32x4*>(ga.A_log + h * D + 32 * kk + 8 * lg + 4 * a);
+      }
   }
   f32x4 graw[4][2];
   {
     typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-    if constexpr (GIN == kX16) {
+    if constexpr ((GIN & 3) == kX16) {
       const auto rg = buf_tok(g, 2);
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
@@ -222,15 +226,17 @@ __global__ void __launch_bounds__(NTHR, 3) prep_kernel(
     // the scan's log2 units, beta = sigmoid(b).  Computed on every row and
     // masked (rows past the chunk end read x = b = 0, finite): a select here
     // becomes per-element branches that serialize the dt_bias loads.
-    const float neg_a = -expf(ga.A_log[h]);
+    const float neg_a = (GIN & kPC) != 0 ? 0.0f : -expf(ga.A_log[h]);
     const float keep = r < Lc ? 1.0f : 0.0f;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          graw[kk][a][j] = keep * gate_log2_decay_fast(neg_a, gate_input(graw[kk][a][j], dtb[kk][a][j]));
+        for (int j = 0; j < 4; ++j) {
+          const float na = (GIN & kPC) != 0 ? -expf(alc[kk][a][j]) : neg_a;
+          graw[kk][a][j] = keep * gate_log2_decay_fast(na, gate_input(graw[kk][a][j], dtb[kk][a][j]));
+        }
     bval = keep * gate_beta(bval);
   }
 
@@ -592,11 +598,15 @@ hipError_t launch_prep(const void* q, const void* k, bool qkv_bf16, const void* 
   if (qkv_bf16) {
     if (g_mode == kG) KDA_PREP(true, kG);
     else if (g_mode == kX32) KDA_PREP(true, kX32);
-    else KDA_PREP(true, kX16);
+    else if (g_mode == kX16) KDA_PREP(true, kX16);
+    else if (g_mode == (kX32 | kPC)) KDA_PREP(true, kX32 | kPC);
+    else KDA_PREP(true, kX16 | kPC);
   } else {
     if (g_mode == kG) KDA_PREP(false, kG);
     else if (g_mode == kX32) KDA_PREP(false, kX32);
-    else KDA_PREP(false, kX16);
+    else if (g_mode == kX16) KDA_PREP(false, kX16);
+    else if (g_mode == (kX32 | kPC)) KDA_PREP(false, kX32 | kPC);
+    else KDA_PREP(false, kX16 | kPC);
   }
 #undef KDA_PREP
   return hipGetLastError();

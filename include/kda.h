@@ -45,7 +45,7 @@ extern "C" {
 typedef enum {
   KDA_OK = 0,
   KDA_ERR_INVALID_ARG = 1, /* null pointer, negative size, bad scale       */
-  KDA_ERR_SHAPE = 2,       /* inconsistent sizes (e.g. A_log length != H)  */
+  KDA_ERR_SHAPE = 2,       /* inconsistent sizes (e.g. A_log not [H] or [H,d]) */
   KDA_ERR_DTYPE = 3,       /* dtype code not supported for this argument   */
   KDA_ERR_UNSUPPORTED = 4, /* valid but not implemented (e.g. d != 128)    */
   KDA_ERR_ALIGNMENT = 5,   /* pointer not 16-byte aligned                  */
@@ -70,15 +70,19 @@ const char* kda_version(void);
  * A_log holds one value per head and dt_bias one per (head, channel): the
  * artifact audit's §5.2 shape table lists A_log as [H] in the model config,
  * remote code and FlashKDA's host check, and dt_bias [12288] = [96,128].
- * The checkpoint's own A_log is [128]; this library refuses any length but H
- * (KDA_ERR_SHAPE) rather than guess a reshape, as that section advises.
+ * The checkpoint's own A_log is [128]; that section leaves open whether it
+ * is a per-channel parameter and advises against guessing a reshape.  So
+ * the library takes A_log per head (A_log_len == H) or, given explicitly,
+ * per (head, channel) (A_log_len == H*d, [H, d] row-major, exp(A_log[h,c])
+ * in place of exp(A_log[h])), and refuses every other length, the bare
+ * [128] among them (KDA_ERR_SHAPE).
  * beta is squashed here, once, in fp32 (Model-Optimizer PR #2749 review,
  * the KDA beta fix); the prefill and decode calls take it post-sigmoid and
  * never apply a sigmoid themselves.
  *
  *   x        [n_tok, H, d]  gate logits, dtype x_dt (KDA_F32 or KDA_BF16)
  *   b        [n_tok, H]     beta logits, dtype b_dt (KDA_F32 or KDA_BF16)
- *   A_log    [A_log_len]    fp32, A_log_len must equal H
+ *   A_log    [A_log_len]    fp32, A_log_len == H, or H*d for [H, d]
  *   dt_bias  [dt_bias_len]  fp32, dt_bias_len must equal H*d
  *   g_out    [n_tok, H, d]  fp32 output
  *   beta_out [n_tok, H]     fp32 output
@@ -147,7 +151,8 @@ kda_status kda_chunk_prefill(const void* q, const void* k, const void* v, kda_dt
  * The same recurrence, outputs, workspace and rules as kda_chunk_prefill,
  * but the decay and beta come as the gate's raw inputs (the arguments of
  * kda_gate): x [T_tot, H, dk] gate logits (x_dt KDA_F32 or KDA_BF16), b
- * [T_tot, H] beta logits (b_dt), A_log [H], dt_bias [H, dk].  g and beta are
+ * [T_tot, H] beta logits (b_dt), A_log [H] or [H, dk] (16-byte aligned),
+ * dt_bias [H, dk].  g and beta are
  * formed in registers and g never goes to memory.  g is summed into the
  * cumulative decay straight in log2 units with the plain hardware exp2/log2
  * (absolute error about exp(A_log) 2^-23 per token, against a few ulp for
@@ -197,7 +202,7 @@ kda_status kda_recurrent_decode(const void* q, const void* k, const void* v, kda
  *
  *   q, k  [N, H, dk], v [N, H, dv]   dtype qkv_dt
  *   x     [N, H, dk] gate logits (x_dt), b [N, H] beta logits (b_dt),
- *         A_log [H] fp32, dt_bias [H, dk] fp32: g and beta are formed per
+ *         A_log [H] or [H, dk] fp32, dt_bias [H, dk] fp32: g and beta are formed per
  *         key channel with kda_gate's arithmetic and never stored
  *   state [num_slots, H, dk, dv] dtype state_dt, read and overwritten in place
  *   state_indices [N] int32 device array: sequence n uses state slot
@@ -211,7 +216,7 @@ kda_status kda_recurrent_decode(const void* q, const void* k, const void* v, kda
  * inputs are FlashKDA's (Kimi K3 artifact audit, §7.1: bf16 inputs, fp32
  * A_log / dt_bias, a bf16 state mode, §7.4); the step is the code audit's fused
  * recurrent decode regime.  Requires dk == dv == 128.  Refusals: A_log_len
- * != H or dt_bias_len != H*dk (KDA_ERR_SHAPE), num_slots < N without
+ * other than H or H*dk, or dt_bias_len != H*dk (KDA_ERR_SHAPE), num_slots < N without
  * indices (KDA_ERR_SHAPE), unaligned or overlapping tensors; the indices
  * themselves are device data and are bounds-checked by the kernel.
  */

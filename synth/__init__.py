@@ -12,6 +12,7 @@ from .inputs import (  # noqa: F401
     draw_config,
     draw_decode_params,
     draw_decode_step,
+    draw_alog_per_channel,
     varlen_lengths,
     orthonormal_keys_pm_quarter,
 )

@@ -4,6 +4,7 @@ Distributions follow the Kimi-K3 artifact audit ("Kimi K3 ç¬¬ä¸‰è½®ï¼šå¼€æ”¾å·¥ä
 å¯å¤çŽ°å®žéªŒå®¡è®¡", Â§5.1 KDA layer 1 parameter table): A_log has median about -0.15 and
 range -0.75..2.47, dt_bias median about -4.6.  The five workload recipes draw
   A_log   ~ U(-0.75, 0.5)            per head            [H]
+            (the per-channel variant: U(-0.75, 1.0) per (head, channel) [H, d])
   dt_bias ~ N(-4.6, 1.2)             per channel         [H, d]
   q, k    ~ N(0, 1), then L2-normalised over d per (token, head)
   v       ~ N(0, 1)
@@ -152,6 +153,15 @@ def draw_decode_step(N: int, H: int, step: int, seed: int, dtype=torch.bfloat16,
     g = _gen(seed * 1000 + 1 + step, device)
     q, k, v, x, b = _tokens(g, N, H, dtype, device)
     return DecodeDraw(q, k, v, x, b)
+
+
+def draw_alog_per_channel(H: int, seed: int, device="cpu", lo: float = -0.75,
+                          hi: float = 1.0) -> torch.Tensor:
+    """A_log per (head, channel), [H, d] fp32 ~ U(lo, hi): the channel-wise
+    variant of the gate (inside the audit's observed A_log range), from its own
+    generator seeded with seed * 1000 + 999."""
+    g = _gen(seed * 1000 + 999, device)
+    return torch.rand(H, D, generator=g, device=device, dtype=torch.float32) * (hi - lo) + lo
 
 
 def orthonormal_keys_pm_quarter(n: int, d: int = D) -> torch.Tensor:

@@ -56,6 +56,8 @@ def test_gate_refuses_checkpoint_shaped_A_log():
     L = _lib()
     assert _gate(L, A_log_len=128) == 2
     assert b"A_log" in L.kda_last_error()
+    assert _gate(L, A_log_len=96 * 128 - 1) == 2
+    assert _gate(L, A_log_len=96 * 128, x=None) == 1   # [H, d] passes the shape check
     assert _gate(L, dt_bias_len=12288 + 1) == 2
     assert _gate(L, x_dt=5) == 3
     assert _gate(L, d=126, dt_bias_len=96 * 126) == 4
@@ -140,6 +142,10 @@ def test_prefill_gated_refusals():
     assert _prefill_gated(L, [0, 30, 20], T=20) == 2
     assert _prefill_gated(L, cu, ws=None) == 6
     assert b"kda_chunk_prefill_gated" in L.kda_last_error()
+    # A_log per (head, channel), [H, dk]: accepted shape, 16-byte aligned
+    assert _prefill_gated(L, cu, A_log_len=4 * 128, ws=None) == 6
+    assert _prefill_gated(L, cu, A_log_len=4 * 128, A_log=DEV[9] + 4) == 5
+    assert _prefill_gated(L, cu, A_log_len=4 * 128 + 4) == 2
 
 
 def test_decode_refusals():
@@ -186,6 +192,7 @@ def test_decode_gated_refusals():
     assert b"num_slots" in L.kda_last_error()
     assert _decode_gated(L, slots=-1) == 1
     assert _decode_gated(L, S=None) == 1
+    assert _decode_gated(L, A_log_len=2 * 128, S=None) == 1    # [H, dk] A_log: shape accepted
     assert _decode_gated(L, S=DEV[5] + 8) == 5
     assert _decode_gated(L, b=DEV[4] + 1) == 5                 # bf16 beta logits: 2-byte
     assert _decode_gated(L, idx=DEV[11] + 2) == 5

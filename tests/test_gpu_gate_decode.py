@@ -4,7 +4,8 @@ import pytest
 import torch
 
 import oracle
-from synth import CONFIGS, draw_decode_params, draw_decode_step, draw_prefill
+from synth import (CONFIGS, draw_alog_per_channel, draw_decode_params, draw_decode_step,
+                   draw_prefill)
 from tests.gpu_util import DEV, need_gpu, oracle_gate_f32, say
 from tests.parity import assert_out, assert_state, out_err, state_err, to64
 import gated_delta_rule_58_amd as kda
@@ -44,6 +45,25 @@ def test_gate_extreme_logits():
     assert np.all(np.isfinite(g_gpu)) and np.all(np.isfinite(to64(beta)))
     assert np.all(np.abs(g_gpu - g_ref) <= 1e-5 * np.abs(g_ref) + 1e-37)
     assert np.max(np.abs(to64(beta) - b_ref)) <= 1e-6
+
+
+@pytest.mark.parametrize("xdt", [torch.float32, torch.bfloat16])
+def test_gate_per_channel_alog(xdt):
+    """A_log per (head, channel), [H, d]: kda_gate against the oracle gate, and
+    far from the per-head gate (so a per-head read of A_log would fail)."""
+    need_gpu()
+    say("gate per-channel A_log", xdt)
+    dr = draw_prefill([300], H=7, dtype=torch.bfloat16, seed=23)
+    A = draw_alog_per_channel(7, seed=23)
+    x, b = dr.x.to(xdt), dr.b.to(xdt)
+    g, beta = kda.gate(x.to(DEV), b.to(DEV), A.to(DEV), dr.dt_bias.to(DEV))
+    torch.cuda.synchronize()
+    g_ref, b_ref = oracle.gate(x, b, A, dr.dt_bias)
+    g_gpu = to64(g)
+    assert np.all(np.abs(g_gpu - g_ref) <= 1e-5 * np.abs(g_ref) + 1e-30)
+    assert np.max(np.abs(to64(beta) - b_ref)) <= 1e-6
+    g_ph, _ = oracle.gate(x, b, dr.A_log, dr.dt_bias)
+    assert np.max(np.abs(g_gpu - g_ph)) > 0.1 * np.max(np.abs(g_ph))
 
 
 @pytest.mark.parametrize("qdt,odt", [(torch.float32, torch.float32),
@@ -147,6 +167,33 @@ def test_decode_gated_matches_gate_then_decode(xdt):
         o_ref, S_ref = oracle.decode(st.q, st.k, st.v, gr, br, S_ref, scale=0.8)
         assert_out(o2, o_ref, "gated decode step %d" % step)
         assert_state(S2, S_ref, "gated decode step %d" % step)
+
+
+@pytest.mark.parametrize("sdt", [torch.float32, torch.bfloat16])
+def test_decode_gated_per_channel_alog(sdt):
+    """Gated decode with A_log per (head, channel), [H, d], over an fp32 or
+    bf16 pool: 4 steps against the oracle gate and step (the oracle's state
+    rounded to bf16 after each step in bf16 mode)."""
+    need_gpu()
+    say("gated decode per-channel A_log", sdt)
+    N, H = 6, 4
+    A_log, dt_bias, S0 = draw_decode_params(N, H, seed=47)
+    A = draw_alog_per_channel(H, seed=47)
+    S0 = (S0 * 10).to(sdt)
+    S = S0.to(DEV).contiguous()
+    S_ref = to64(S0)
+    for step in range(4):
+        st = draw_decode_step(N, H, step, seed=47, dtype=torch.bfloat16)
+        o = kda.recurrent_decode_gated(st.q.to(DEV), st.k.to(DEV), st.v.to(DEV), st.x.to(DEV),
+                                       st.b.to(DEV), A.to(DEV), dt_bias.to(DEV), S, scale=0.9,
+                                       o_dtype=torch.float32)
+        torch.cuda.synchronize()
+        gr, br = oracle.gate(st.x, st.b, A, dt_bias)
+        o_ref, S_ref = oracle.decode(st.q, st.k, st.v, gr, br, S_ref, scale=0.9)
+        if sdt == torch.bfloat16:
+            S_ref = _bf16_round(S_ref)
+        assert_out(o, o_ref, "per-channel A_log decode step %d" % step)
+    assert_state(S, S_ref, "per-channel A_log decode")
 
 
 def _bf16_round(S):

@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import oracle
-from synth import CONFIGS, draw_config, draw_prefill
+from synth import CONFIGS, draw_alog_per_channel, draw_config, draw_prefill
 from tests.gpu_util import DEV, need_gpu, oracle_gate_f32, oracle_gate_f64, sample_heads, say
 from tests.parity import (O_TOL, S_TOL, assert_out, assert_out_bf16, assert_state, out_err,
                           state_err, to64)
@@ -282,6 +282,28 @@ def test_gated_matches_gate_then_prefill(xdt):
     o_ref, S_ref = oracle.prefill(dr.q, dr.k, dr.v, gr, br, cu_h, dr.initial_state, scale=0.7)
     assert_out(o2, o_ref, "gated")
     assert_state(S2, S_ref, "gated")
+
+
+@pytest.mark.parametrize("xdt", [torch.float32, torch.bfloat16])
+def test_gated_per_channel_alog(xdt):
+    """kda_chunk_prefill_gated with A_log per (head, channel), [H, dk], on
+    varlen input with empty and one-token sequences and an initial state,
+    against the oracle gate (per-channel) followed by the oracle recurrence."""
+    need_gpu()
+    dr = draw_prefill([200, 0, 64, 1, 77], H=3, dtype=torch.bfloat16, init_state=True, seed=63)
+    A = draw_alog_per_channel(3, seed=63)
+    say("gated prefill per-channel A_log", xdt)
+    x, b = dr.x.to(xdt), dr.b.to(xdt)
+    cu_h = dr.cu_seqlens
+    o, S = kda.chunk_prefill_gated(dr.q.to(DEV), dr.k.to(DEV), dr.v.to(DEV), x.to(DEV),
+                                   b.to(DEV), A.to(DEV), dr.dt_bias.to(DEV), cu_h.to(DEV),
+                                   dr.initial_state.to(DEV), cu_seqlens_host=cu_h, scale=0.7,
+                                   o_dtype=torch.float32)
+    torch.cuda.synchronize()
+    gr, br = oracle.gate(x.float(), b.float(), A, dr.dt_bias)
+    o_ref, S_ref = oracle.prefill(dr.q, dr.k, dr.v, gr, br, cu_h, dr.initial_state, scale=0.7)
+    assert_out(o, o_ref, "gated per-channel A_log")
+    assert_state(S, S_ref, "gated per-channel A_log")
 
 
 def test_config1_gated_full_sampled_heads():
