@@ -40,6 +40,11 @@ def _lib():
         lib.kdao_gate.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _dp, _dp, _dp,
                                   ctypes.c_int32, _dp, _dp, _dp]
         lib.kdao_gate.restype = None
+        lib.kdao_prefill_backward.argtypes = [ctypes.c_int32, _ip, ctypes.c_int32, ctypes.c_int32,
+                                              ctypes.c_int32, _dp, _dp, _dp, _dp, _dp,
+                                              ctypes.c_double, _dp, _dp, _dp, _dp, _dp, _dp,
+                                              _dp, _dp, _dp, ctypes.c_int32]
+        lib.kdao_prefill_backward.restype = ctypes.c_int32
         lib.kdao_prefill.argtypes = [ctypes.c_int32, _ip, ctypes.c_int32, ctypes.c_int32,
                                      ctypes.c_int32, _dp, _dp, _dp, _dp, _dp, ctypes.c_double,
                                      _dp, _dp, _dp, ctypes.c_int32]
@@ -107,6 +112,37 @@ def prefill(q, k, v, g, beta, cu_seqlens, initial_state=None, scale=1.0, nthread
                                _p(g), _p(beta), float(scale), _p(S0), _p(o), _p(Sf),
                                int(nthreads))
     return (o, Sf, used) if return_threads else (o, Sf)
+
+
+def prefill_backward(q, k, v, g, beta, cu_seqlens, initial_state=None, scale=1.0, d_o=None,
+                     dS_final=None, nthreads=0):
+    """Gradients of prefill's outputs (o, final state) against d_o [T,H,dv] and
+    dS_final [N,H,dk,dv] (either may be None: zero), by reverse-mode through the
+    token recurrence in fp64 (kdao_prefill_backward).
+
+    Returns (dq, dk, dv, dg, dbeta, dS0) as fp64 numpy arrays; dS0 is the
+    gradient of the initial state (the zero state when none is given)."""
+    q, k, v, g, beta = f64(q), f64(k), f64(v), f64(g), f64(beta)
+    cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    N = cu.size - 1
+    if k.shape != (T, H, dk) or g.shape != (T, H, dk) or v.shape[:2] != (T, H) \
+            or beta.shape != (T, H) or cu[0] != 0 or cu[-1] != T or np.any(np.diff(cu) < 0):
+        raise ValueError("prefill_backward: bad shapes or cu_seqlens")
+    S0 = None if initial_state is None else f64(initial_state)
+    dO = None if d_o is None else f64(d_o)
+    dSf = None if dS_final is None else f64(dS_final)
+    if (S0 is not None and S0.shape != (N, H, dk, dv)) or \
+            (dSf is not None and dSf.shape != (N, H, dk, dv)) or \
+            (dO is not None and dO.shape != (T, H, dv)):
+        raise ValueError("prefill_backward: shape mismatch")
+    out = [np.zeros((T, H, dk)), np.zeros((T, H, dk)), np.zeros((T, H, dv)),
+           np.zeros((T, H, dk)), np.zeros((T, H)), np.zeros((N, H, dk, dv))]
+    _lib().kdao_prefill_backward(N, cu.ctypes.data_as(_ip), H, dk, dv, _p(q), _p(k), _p(v),
+                                 _p(g), _p(beta), float(scale), _p(S0), _p(dO), _p(dSf),
+                                 *[_p(a) for a in out], int(nthreads))
+    return tuple(out)
 
 
 def decode(q, k, v, g, beta, state, scale=1.0, nthreads=0, return_threads=False):

@@ -119,6 +119,151 @@ int32_t kdao_prefill(int32_t N, const int32_t* cu, int32_t H, int32_t dk, int32_
   return used;
 }
 
+/*
+ * Reverse-mode gradient of kdao_prefill (the same recurrence), written out
+ * step by step.  For one token, with S' = Diag(exp(g)) S_prev,
+ * e = v - S'^T k, S = S' + beta k e^T and o = scale S^T q, and dS the
+ * gradient arriving at S (from later tokens, or dS_final at the end):
+ *   dS     += scale q do^T;            dq  = scale S do
+ *   dbeta   = k^T dS e;                de  = beta dS^T k;     dv = de
+ *   dk      = beta dS e - S' de;       dS' = dS - k de^T
+ *   dg[c]   = sum_j dS'[c,j] S'[c,j];  dS_prev = Diag(exp(g)) dS'
+ * and dS after the first token is the gradient of the initial state.  The
+ * states are recomputed forward from checkpoints taken every 64 tokens.
+ * do, dS_final may be NULL (zero); dS0 may be NULL (not wanted).
+ */
+int32_t kdao_prefill_backward(int32_t N, const int32_t* cu, int32_t H, int32_t dk, int32_t dv,
+                              const double* q, const double* k, const double* v,
+                              const double* g, const double* beta, double scale,
+                              const double* S0, const double* d_o, const double* dS_final,
+                              double* dq, double* dk_out, double* dv_out, double* dg,
+                              double* dbeta, double* dS0, int32_t nthreads) {
+  enum { CK = 64 };
+  int32_t used = 1;
+  const int64_t pairs = (int64_t)N * H;
+  const size_t SS = (size_t)dk * dv;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+  (void)nthreads;
+#endif
+#pragma omp parallel
+  {
+#ifdef _OPENMP
+#pragma omp single
+    used = omp_get_num_threads();
+#endif
+    double* e = (double*)malloc(sizeof(double) * (size_t)dv);
+    double* de = (double*)malloc(sizeof(double) * (size_t)dv);
+    double* otmp = (double*)malloc(sizeof(double) * (size_t)dv);
+    double* dS = (double*)malloc(sizeof(double) * SS);
+    double* Sp = (double*)malloc(sizeof(double) * SS);
+    double* seg = (double*)malloc(sizeof(double) * SS * (CK + 1));
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t p = 0; p < pairs; ++p) {
+      const int32_t n = (int32_t)(p / H), h = (int32_t)(p % H);
+      const int64_t t0 = cu[n], L = cu[n + 1] - cu[n];
+      const int64_t nck = (L + CK - 1) / CK;
+      /* forward: the state before each segment of CK tokens */
+      double* ck = (double*)malloc(sizeof(double) * SS * (size_t)(nck > 0 ? nck : 1));
+      double* S = seg;
+      if (S0) memcpy(S, S0 + p * SS, sizeof(double) * SS);
+      else memset(S, 0, sizeof(double) * SS);
+      for (int64_t t = 0; t < L; ++t) {
+        if (t % CK == 0) memcpy(ck + (t / CK) * SS, S, sizeof(double) * SS);
+        const int64_t r = (t0 + t) * H + h;
+        step(dk, dv, S, e, q + r * dk, k + r * dk, v + r * dv, g + r * dk, beta[r], scale, otmp);
+      }
+      if (dS_final) memcpy(dS, dS_final + p * SS, sizeof(double) * SS);
+      else memset(dS, 0, sizeof(double) * SS);
+      for (int64_t b = nck - 1; b >= 0; --b) {
+        const int64_t ta = b * CK, tb = (ta + CK < L) ? ta + CK : L;
+        /* seg[i] = state before token ta + i, i = 0 .. tb - ta */
+        memcpy(seg, ck + b * SS, sizeof(double) * SS);
+        for (int64_t t = ta; t < tb; ++t) {
+          const int64_t r = (t0 + t) * H + h;
+          memcpy(seg + (t - ta + 1) * SS, seg + (t - ta) * SS, sizeof(double) * SS);
+          step(dk, dv, seg + (t - ta + 1) * SS, e, q + r * dk, k + r * dk, v + r * dv,
+               g + r * dk, beta[r], scale, otmp);
+        }
+        for (int64_t t = tb - 1; t >= ta; --t) {
+          const int64_t r = (t0 + t) * H + h;
+          const double* Sprev = seg + (t - ta) * SS;
+          const double* Snew = seg + (t - ta + 1) * SS;
+          const double* qt = q + r * dk;
+          const double* kt = k + r * dk;
+          const double* vt = v + r * dv;
+          const double* gt = g + r * dk;
+          const double bt = beta[r];
+          const double* dot = d_o ? d_o + r * dv : NULL;
+          /* o = scale S^T q */
+          for (int32_t c = 0; c < dk; ++c) {
+            double acc = 0.0;
+            if (dot)
+              for (int32_t j = 0; j < dv; ++j) acc += Snew[(int64_t)c * dv + j] * dot[j];
+            dq[r * dk + c] = scale * acc;
+            if (dot)
+              for (int32_t j = 0; j < dv; ++j) dS[(int64_t)c * dv + j] += scale * qt[c] * dot[j];
+          }
+          /* S' = Diag(exp(g)) S_prev and e = v - S'^T k, recomputed */
+          for (int32_t c = 0; c < dk; ++c) {
+            const double a = exp(gt[c]);
+            for (int32_t j = 0; j < dv; ++j) Sp[(int64_t)c * dv + j] = a * Sprev[(int64_t)c * dv + j];
+          }
+          for (int32_t j = 0; j < dv; ++j) {
+            double acc = vt[j];
+            for (int32_t c = 0; c < dk; ++c) acc -= kt[c] * Sp[(int64_t)c * dv + j];
+            e[j] = acc;
+          }
+          /* S = S' + beta k e^T */
+          double db = 0.0;
+          for (int32_t c = 0; c < dk; ++c) {
+            double dse = 0.0;
+            for (int32_t j = 0; j < dv; ++j) dse += dS[(int64_t)c * dv + j] * e[j];
+            db += kt[c] * dse;
+            dk_out[r * dk + c] = bt * dse;
+          }
+          dbeta[r] = db;
+          for (int32_t j = 0; j < dv; ++j) {
+            double acc = 0.0;
+            for (int32_t c = 0; c < dk; ++c) acc += dS[(int64_t)c * dv + j] * kt[c];
+            de[j] = bt * acc;
+            dv_out[r * dv + j] = de[j];
+          }
+          /* e = v - S'^T k:  dS' = dS - k de^T,  dk -= S' de */
+          for (int32_t c = 0; c < dk; ++c) {
+            double acc = 0.0;
+            for (int32_t j = 0; j < dv; ++j) {
+              acc += Sp[(int64_t)c * dv + j] * de[j];
+              dS[(int64_t)c * dv + j] -= kt[c] * de[j];
+            }
+            dk_out[r * dk + c] -= acc;
+          }
+          /* S' = Diag(exp(g)) S_prev */
+          for (int32_t c = 0; c < dk; ++c) {
+            const double a = exp(gt[c]);
+            double acc = 0.0;
+            for (int32_t j = 0; j < dv; ++j) {
+              acc += dS[(int64_t)c * dv + j] * Sp[(int64_t)c * dv + j];
+              dS[(int64_t)c * dv + j] *= a;
+            }
+            dg[r * dk + c] = acc;
+          }
+        }
+      }
+      if (dS0) memcpy(dS0 + p * SS, dS, sizeof(double) * SS);
+      free(ck);
+    }
+    free(e);
+    free(de);
+    free(otmp);
+    free(dS);
+    free(Sp);
+    free(seg);
+  }
+  return used;
+}
+
 /* One decode step: one token per sequence, state updated in place. */
 int32_t kdao_decode(int32_t N, int32_t H, int32_t dk, int32_t dv, const double* q,
                     const double* k, const double* v, const double* g, const double* beta,
