@@ -16,6 +16,8 @@ from .binding import (  # noqa: F401
     chunk_prefill,
     chunk_prefill_gated,
     chunk_prefill_workspace_bytes,
+    chunk_prefill_backward,
+    chunk_prefill_backward_workspace_bytes,
     recurrent_decode,
     recurrent_decode_gated,
     shortconv_l2norm,

@@ -73,6 +73,13 @@ def lib():
         L.kda_shortconv_l2norm.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _i64,
                                            _i32, ctypes.c_float, _vp, _vp, _i32, _vp, _vp, _vp,
                                            _vp, _vp, ctypes.c_int, _i64, _i32, _i32, _vp]
+        L.kda_chunk_prefill_backward.restype = ctypes.c_int
+        L.kda_chunk_prefill_backward.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _vp,
+                                                 _i32, _vp, _vp, ctypes.c_int, _vp, _vp, _vp,
+                                                 _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32,
+                                                 ctypes.c_float, _vp, ctypes.c_size_t, _vp]
+        L.kda_chunk_prefill_backward_workspace_bytes.restype = ctypes.c_size_t
+        L.kda_chunk_prefill_backward_workspace_bytes.argtypes = [_i64, _i32, _i32, _i32, _i32]
         L.kda_recurrent_decode.restype = ctypes.c_int
         L.kda_recurrent_decode.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _vp,
                                            ctypes.c_int, _i32, _i32, _i32, _i32, ctypes.c_float,
@@ -84,7 +91,8 @@ def lib():
 def exported_symbols():
     return ["kda_last_error", "kda_version", "kda_gate", "kda_chunk_prefill",
             "kda_chunk_prefill_gated", "kda_chunk_prefill_workspace_bytes", "kda_recurrent_decode",
-            "kda_recurrent_decode_gated", "kda_shortconv_l2norm"]
+            "kda_recurrent_decode_gated", "kda_shortconv_l2norm", "kda_chunk_prefill_backward",
+            "kda_chunk_prefill_backward_workspace_bytes"]
 
 
 def _check(status: int):
@@ -225,6 +233,57 @@ def chunk_prefill_gated(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, x: to
         _dt(out), T, H, dk, dv, float(scale), _ptr(workspace), workspace.numel(), _stream(dev))
     _check(st)
     return out, final_state
+
+
+def chunk_prefill_backward_workspace_bytes(T_tot: int, N: int, H: int, dk: int = 128,
+                                           dv: int = 128) -> int:
+    """kda_chunk_prefill_backward_workspace_bytes."""
+    return int(lib().kda_chunk_prefill_backward_workspace_bytes(T_tot, N, H, dk, dv))
+
+
+def chunk_prefill_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                           beta: torch.Tensor, d_o: Optional[torch.Tensor],
+                           cu_seqlens: Optional[torch.Tensor] = None,
+                           initial_state: Optional[torch.Tensor] = None,
+                           d_final_state: Optional[torch.Tensor] = None, scale: float = 1.0,
+                           want_d_initial_state: bool = True,
+                           cu_seqlens_host: Optional[torch.Tensor] = None,
+                           workspace: Optional[torch.Tensor] = None):
+    """kda_chunk_prefill_backward: gradients of chunk_prefill's (o, final_state)
+    against d_o [T,H,dv] (None: zero) and d_final_state [N,H,dk,dv] (None: zero).
+
+    Returns (dq, dk, dv, dg, dbeta, d_initial_state) as float32 tensors
+    (d_initial_state None unless want_d_initial_state)."""
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    dev = q.device
+    if cu_seqlens is None:
+        cu_seqlens_host = torch.tensor([0, T], dtype=torch.int32)
+        cu_seqlens = cu_seqlens_host.to(dev)
+    if cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    if cu_seqlens_host is None:
+        cu_seqlens_host = cu_seqlens.cpu()
+    hp = cu_seqlens_host.contiguous()
+    N = cu_seqlens.numel() - 1
+    f32 = dict(dtype=torch.float32, device=dev)
+    dq = torch.empty((T, H, dk), **f32)
+    dk_ = torch.empty((T, H, dk), **f32)
+    dv_ = torch.empty((T, H, dv), **f32)
+    dg = torch.empty((T, H, dk), **f32)
+    dbeta = torch.empty((T, H), **f32)
+    dS0 = torch.empty((N, H, dk, dv), **f32) if want_d_initial_state else None
+    if workspace is None:
+        nbytes = chunk_prefill_backward_workspace_bytes(T, N, H, dk, dv)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    st = lib().kda_chunk_prefill_backward(
+        _ptr(q), _ptr(k), _ptr(v), _dt(q), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
+        ctypes.cast(hp.data_ptr(), _vp), N, _ptr(initial_state), _ptr(d_o),
+        _dt(d_o) if d_o is not None else KDA_F32, _ptr(d_final_state), _ptr(dq), _ptr(dk_),
+        _ptr(dv_), _ptr(dg), _ptr(dbeta), _ptr(dS0), T, H, dk, dv, float(scale),
+        _ptr(workspace), workspace.numel(), _stream(dev))
+    _check(st)
+    return dq, dk_, dv_, dg, dbeta, dS0
 
 
 def recurrent_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,

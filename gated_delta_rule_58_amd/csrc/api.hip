@@ -99,7 +99,8 @@ kda_status check_prefill(const char* fn, const void* q, const void* k, const voi
                          size_t bb_al, const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
                          int32_t N, const float* initial_state, const float* final_state,
                          const void* o, kda_dtype o_dt, int64_t T_tot, int32_t H, int32_t dk,
-                         int32_t dv, float scale, const void* workspace, size_t workspace_bytes) {
+                         int32_t dv, float scale, const void* workspace, size_t workspace_bytes,
+                         bool backward = false) {
   if (N <= 0 || H <= 0 || T_tot < 0)
     return fail(KDA_ERR_INVALID_ARG, "%s: need N > 0, H > 0, T_tot >= 0 (got %d, %d, %lld)", fn,
                 N, H, (long long)T_tot);
@@ -132,7 +133,8 @@ kda_status check_prefill(const char* fn, const void* q, const void* k, const voi
   if (!aligned(decay, decay_al) || !aligned(bb, bb_al) || !aligned(cu_seqlens, 4))
     return fail(KDA_ERR_ALIGNMENT, "%s: the decay input must be %zu-byte aligned, beta %zu-byte, "
                                    "cu_seqlens 4-byte", fn, decay_al, bb_al);
-  const size_t ws_min = kda::chunk_workspace_bytes(N, H, 1);
+  const size_t ws_min = backward ? kda::bwd::workspace_bytes(T_tot, N, H)
+                                 : kda::chunk_workspace_bytes(N, H, 1);
   if (!workspace || workspace_bytes < ws_min)
     return fail(KDA_ERR_WORKSPACE, "%s: need a workspace of at least %zu bytes (got %zu at %p)",
                 fn, ws_min, workspace_bytes, workspace);
@@ -200,6 +202,42 @@ kda_status kda_chunk_prefill_gated(const void* q, const void* k, const void* v, 
                                             initial_state, final_state, o, o_dt == KDA_BF16,
                                             T_tot, H, scale, workspace, workspace_bytes,
                                             static_cast<hipStream_t>(stream)),
+                  fn);
+}
+
+size_t kda_chunk_prefill_backward_workspace_bytes(int64_t T_tot, int32_t N, int32_t H,
+                                                  int32_t dk, int32_t dv) {
+  if (dk != 128 || dv != 128 || T_tot < 0 || N <= 0 || H <= 0) return 0;
+  return kda::bwd::workspace_bytes(T_tot, N, H);
+}
+
+kda_status kda_chunk_prefill_backward(const void* q, const void* k, const void* v,
+                                      kda_dtype qkv_dt, const float* g, const float* beta,
+                                      const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                                      int32_t N, const float* initial_state, const void* d_o,
+                                      kda_dtype do_dt, const float* d_final_state, float* dq,
+                                      float* dk, float* dv, float* dg, float* dbeta,
+                                      float* d_initial_state, int64_t T_tot, int32_t H,
+                                      int32_t dk_dim, int32_t dv_dim, float scale,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "kda_chunk_prefill_backward";
+  const kda_status st = check_prefill(fn, q, k, v, qkv_dt, g, 16, beta, 4, cu_seqlens,
+                                      cu_seqlens_host, N, initial_state, d_final_state, dq, do_dt,
+                                      T_tot, H, dk_dim, dv_dim, scale, workspace, workspace_bytes,
+                                      true);
+  if (st != KDA_OK) return st;
+  if (T_tot > 0 && (!dk || !dv || !dg || !dbeta))
+    return fail(KDA_ERR_INVALID_ARG, "%s: dq, dk, dv, dg and dbeta must be non-NULL", fn);
+  const void* outs[] = {d_o, dk, dv, dg, d_initial_state};
+  for (const void* p : outs)
+    if (p && !aligned(p, 16))
+      return fail(KDA_ERR_ALIGNMENT, "%s: d_o and the gradients must be 16-byte aligned", fn);
+  if (!aligned(dbeta, 4))
+    return fail(KDA_ERR_ALIGNMENT, "%s: dbeta must be 4-byte aligned", fn);
+  return launched(kda::bwd::launch(q, k, v, qkv_dt == KDA_BF16, g, beta, cu_seqlens,
+                                   cu_seqlens_host, N, initial_state, d_o, do_dt == KDA_BF16,
+                                   d_final_state, dq, dk, dv, dg, dbeta, d_initial_state, T_tot,
+                                   H, scale, workspace, static_cast<hipStream_t>(stream)),
                   fn);
 }
 

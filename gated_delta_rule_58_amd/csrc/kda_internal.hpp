@@ -51,6 +51,17 @@ hipError_t launch_chunk_prefill(const void* q, const void* k, const void* v, boo
                                 void* ws, size_t ws_bytes, hipStream_t s);
 size_t chunk_workspace_bytes(int N, int H, int chunks_per_pass);
 
+// Chunked prefill backward (backward.hip): gradients of q, k, v, g, beta and
+// the initial state from d_o (bf16 or fp32, NULL = 0) and dS_final (NULL = 0).
+namespace bwd {
+size_t workspace_bytes(int64_t T_tot, int N, int H);
+hipError_t launch(const void* q, const void* k, const void* v, bool qkv_bf16, const float* g,
+                  const float* beta, const int32_t* cu, const int32_t* cu_host, int N,
+                  const float* S0, const void* d_o, bool do_bf16, const float* dS_final,
+                  float* dq, float* dk, float* dv, float* dg, float* dbeta, float* dS0,
+                  int64_t T_tot, int H, float scale, void* ws, hipStream_t s);
+}  // namespace bwd
+
 namespace chunk {
 // One pass: chunks [c_lo, c_lo + S_len) of every sequence (prep.hip, state.hip).
 hipError_t launch_prep(const void* q, const void* k, bool qkv_bf16, const void* g, int g_mode,

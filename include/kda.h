@@ -173,6 +173,44 @@ kda_status kda_chunk_prefill_gated(const void* q, const void* k, const void* v, 
                                    size_t workspace_bytes, void* stream);
 
 /*
+ * kda_chunk_prefill_backward - gradients of kda_chunk_prefill.
+ *
+ * For the forward of kda_chunk_prefill with the same q, k, v, g, beta,
+ * cu_seqlens, initial_state and scale, and the loss
+ *   sum(d_o * o) + sum(d_final_state * final_state),
+ * writes its gradients with respect to q, k, v, g, beta and the initial state:
+ *   dq, dk [T_tot, H, dk] fp32, dv [T_tot, H, dv] fp32, dg [T_tot, H, dk] fp32,
+ *   dbeta [T_tot, H] fp32, d_initial_state [N, H, dk, dv] fp32 (NULL: not wanted;
+ *   it is the gradient of the zero state when initial_state is NULL).
+ * d_o [T_tot, H, dv] has dtype do_dt (KDA_F32 or KDA_BF16); d_o and
+ * d_final_state may be NULL (zero).  The chunked form is the training path of
+ * the code audit's chunked KDA; this is the reverse-mode of the chunk
+ * identities (per chunk: the triangular inverse, the decay-weighted K K^T and
+ * Q K^T, the state products), in fp32: the forward states are recomputed
+ * chunk by chunk and the state gradient walks the chunks backwards.  The
+ * result equals the gradient of the fp64 recurrence up to fp32 rounding.
+ * The workspace (kda_chunk_prefill_backward_workspace_bytes) holds per (chunk,
+ * head) the chunk's intermediate matrices, the recomputed entry state and the
+ * state gradient, 573,952 bytes, for T_tot / 64 + N chunk slots per head; the
+ * call never allocates.  Requires dk == dv == 128; refusals as for
+ * kda_chunk_prefill (the workspace check uses the backward size), plus NULL
+ * or unaligned gradients (16-byte, dbeta 4-byte).  Asynchronous on stream.
+ */
+kda_status kda_chunk_prefill_backward(const void* q, const void* k, const void* v,
+                                      kda_dtype qkv_dt, const float* g, const float* beta,
+                                      const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                                      int32_t N, const float* initial_state, const void* d_o,
+                                      kda_dtype do_dt, const float* d_final_state, float* dq,
+                                      float* dk, float* dv, float* dg, float* dbeta,
+                                      float* d_initial_state, int64_t T_tot, int32_t H,
+                                      int32_t dk_dim, int32_t dv_dim, float scale,
+                                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes of kda_chunk_prefill_backward; 0 for unsupported arguments. */
+size_t kda_chunk_prefill_backward_workspace_bytes(int64_t T_tot, int32_t N, int32_t H,
+                                                  int32_t dk, int32_t dv);
+
+/*
  * kda_chunk_prefill_workspace_bytes - workspace size for kda_chunk_prefill
  * processing up to chunks_per_pass chunks (of 64 tokens) of every sequence per
  * pass: a state carry of N*H*dk*dv*4 bytes plus N*H*chunks_per_pass images

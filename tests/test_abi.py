@@ -31,7 +31,8 @@ def test_exports_every_declared_symbol():
     assert set(names) == {"kda_last_error", "kda_version", "kda_gate", "kda_chunk_prefill",
                           "kda_chunk_prefill_gated", "kda_chunk_prefill_workspace_bytes",
                           "kda_recurrent_decode", "kda_recurrent_decode_gated",
-                          "kda_shortconv_l2norm"}
+                          "kda_shortconv_l2norm", "kda_chunk_prefill_backward",
+                          "kda_chunk_prefill_backward_workspace_bytes"}
     for n in names:
         assert hasattr(L, n), n
     assert L.kda_version().decode().startswith("kda-gfx950")
@@ -235,3 +236,41 @@ def test_shortconv_refusals():
     assert _shortconv(L, cu, wq=DEV[3] + 4) == 5
     assert _shortconv(L, cu, wk=None) == 1
     assert _shortconv(L, [0], N=0, T=0) == 0
+
+
+def _backward(L, cu_host, **kw):
+    a = dict(q=DEV[0], k=DEV[1], v=DEV[2], qkv_dt=1, g=DEV[3], beta=DEV[4], cu=DEV[5], N=2,
+             S0=None, d_o=DEV[6], do_dt=1, dSf=None, dq=DEV[7], dk=DEV[8], dv=DEV[9],
+             dg=DEV[10], dbeta=DEV[11], dS0=None, T=48, H=4, dk_dim=128, dv_dim=128, scale=1.0,
+             ws=DEV[11] + (1 << 20), ws_bytes=1 << 40)
+    a.update(kw)
+    hp = None if cu_host is None else np.ascontiguousarray(np.asarray(cu_host, dtype=np.int32))
+    return L.kda_chunk_prefill_backward(
+        a["q"], a["k"], a["v"], a["qkv_dt"], a["g"], a["beta"], a["cu"],
+        None if hp is None else hp.ctypes.data, a["N"], a["S0"], a["d_o"], a["do_dt"], a["dSf"],
+        a["dq"], a["dk"], a["dv"], a["dg"], a["dbeta"], a["dS0"], a["T"], a["H"], a["dk_dim"],
+        a["dv_dim"], a["scale"], a["ws"], a["ws_bytes"], None)
+
+
+def test_backward_refusals():
+    """kda_chunk_prefill_backward refuses before any HIP call: unsupported
+    head size, bad cu_seqlens, a workspace below its own size, NULL or
+    unaligned gradients, unknown d_o dtype."""
+    L = _lib()
+    L.kda_chunk_prefill_backward_workspace_bytes.restype = ctypes.c_size_t
+    L.kda_chunk_prefill_backward_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int32,
+                                                             ctypes.c_int32, ctypes.c_int32,
+                                                             ctypes.c_int32]
+    need = L.kda_chunk_prefill_backward_workspace_bytes(48, 2, 4, 128, 128)
+    assert need == (48 // 64 + 2) * 4 * 573952
+    assert L.kda_chunk_prefill_backward_workspace_bytes(48, 2, 4, 64, 128) == 0
+    cu = [0, 20, 48]
+    assert _backward(L, cu, dk_dim=64) == 4
+    assert _backward(L, [0, 30, 20], T=20) == 2
+    assert _backward(L, cu, ws_bytes=need - 1) == 6
+    assert b"kda_chunk_prefill_backward" in L.kda_last_error()
+    assert _backward(L, cu, dq=None) == 1
+    assert _backward(L, cu, dg=None) == 1
+    assert _backward(L, cu, dbeta=DEV[11] + 2) == 5
+    assert _backward(L, cu, dk=DEV[8] + 4) == 5
+    assert _backward(L, cu, do_dt=7) == 3
