@@ -96,7 +96,7 @@ def parse():
     ap.add_argument("--ws-chunks", type=int, default=T // C,
                     help="chunks per pass the prefill workspace holds (T/64 = one pass)")
     ap.add_argument("--only", choices=["all", "prefill", "decode", "prologue", "workloads",
-                                       "copy"],
+                                       "backward", "copy"],
                     default="all",
                     help="profiling aid: run one part only (prints a diagnostic line, "
                          "not the bench line)")
@@ -327,6 +327,42 @@ def bench_prologue(args, torch, kda):
                 tokens_per_s=T / (ms * 1e-3))
 
 
+def bench_backward(args, torch, kda, synth):
+    """kda_chunk_prefill_backward at the benchmarked prefill shape: T=4096, H=96,
+    bf16 q/k/v and d_o, fp32 g/beta (from kda_gate), zero initial state,
+    gradients of q, k, v, g, beta (fp32 out)."""
+    dev = "cuda:0"
+    dr = synth.draw_config(1, device=dev)
+    cu_h = dr.cu_seqlens
+    cu_d = cu_h.to(dev)
+    g, beta = kda.gate(dr.x, dr.b, dr.A_log, dr.dt_bias)
+    d_o = torch.randn((T, H, D), generator=torch.Generator(device=dev).manual_seed(9),
+                      device=dev).to(torch.bfloat16)
+    ws = torch.empty(kda.chunk_prefill_backward_workspace_bytes(T, 1, H), dtype=torch.uint8,
+                     device=dev)
+
+    def call():
+        kda.chunk_prefill_backward(dr.q, dr.k, dr.v, g, beta, d_o, cu_d, None,
+                                   want_d_initial_state=False, cu_seqlens_host=cu_h,
+                                   workspace=ws)
+    for _ in range(max(1, args.warmup)):
+        call()
+    torch.cuda.synchronize()
+    nsteps = max(1, args.steps // 4)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(nsteps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / nsteps
+    # q, k, v, d_o bf16 + g fp32 + beta in; dq, dk, dv, dg fp32 + dbeta out
+    nbytes = T * H * (D * (3 * 2 + 2 + 4 + 4 * 4) + 4 + 4)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return dict(ms=ms, tokens_per_s=T / (ms * 1e-3), GBps=gbs, frac=gbs / HBM_PEAK_GBS,
+                bytes=nbytes, workspace_bytes=ws.numel())
+
+
 def cpu_baseline(args, synth):
     """fp64 oracle on `cpu_heads` of the 96 heads of the same T=4096 workload."""
     import numpy as np
@@ -371,6 +407,7 @@ def main():
                                      gated_bf16_pool=bench_decode_gated(args, torch, kda, synth,
                                                                         torch.bfloat16)),
               "prologue": lambda: bench_prologue(args, torch, kda),
+              "backward": lambda: bench_backward(args, torch, kda, synth),
               "workloads": lambda: {str(i): bench_prefill_workload(args, torch, kda, synth, i)
                                     for i in (2, 3)},
               "copy": lambda: bench_copy(args, torch)}[args.only]
@@ -399,6 +436,9 @@ def main():
     pro = bench_prologue(args, torch, kda)
     print("prologue (short conv + SiLU + q/k L2 norm): %.4f ms, %.1f GB/s"
           % (pro["ms"], pro["GBps"]), file=sys.stderr, flush=True)
+    bwd = bench_backward(args, torch, kda, synth)
+    print("prefill backward: %.3f ms, %.2f M tokens/s" % (bwd["ms"], bwd["tokens_per_s"] / 1e6),
+          file=sys.stderr, flush=True)
     step_s = pre["fused_ms"] * 1e-3
     ach = PREFILL_BYTES / step_s / 1e9
     mfma = PREFILL_FLOPS / step_s / 1e12
@@ -446,6 +486,9 @@ def main():
                                  "SiLU, conv state out",
                      "ms": pro["ms"], "GBps": pro["GBps"], "frac": pro["frac"],
                      "bytes_per_call": pro["bytes"], "tokens_per_s": pro["tokens_per_s"]},
+        "prefill_backward": {"workload": "kda_chunk_prefill_backward T=4096 H=96, bf16 "
+                                         "q/k/v and d_o, fp32 g/beta, zero initial state",
+                             **bwd},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

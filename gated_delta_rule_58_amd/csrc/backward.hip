@@ -73,6 +73,68 @@ __device__ __forceinline__ void gemm_acc(float (&acc)[TM][TN], int K, FA a, FB b
   }
 }
 
+// The same product with the operands staged through LDS in slabs of KT = 16
+// along the contraction (each element read once from memory instead of once
+// per thread that uses it).  A_KC: a(m, kk) is contiguous along kk in memory
+// (else along m); B_NC: b(kk, n) is contiguous along n (else along kk); the
+// slab fill follows the contiguous index.  sa: 16 x (16 TM + 1) floats, sb:
+// 16 x (16 TN + 1) floats.  Contains barriers: every thread of the block calls it.
+constexpr int KT = 16;
+template <int TM, int TN, bool A_KC, bool B_NC, typename FA, typename FB>
+__device__ __forceinline__ void gemm_staged(float (&acc)[TM][TN], int K, float* sa, float* sb,
+                                            FA a, FB b) {
+  constexpr int M = 16 * TM, N = 16 * TN, MS = M + 1, NS = N + 1;
+  constexpr int PA = M * KT / NT, PB = N * KT / NT;  // slab elements per thread
+  const int t = threadIdx.x, tr = t >> 4, tc = t & 15;
+  // the next slab is read into registers while the current one is in use
+  float ra[PA], rb[PB];
+  auto fetch = [&](int k0) {
+#pragma unroll
+    for (int u = 0; u < PA; ++u) {
+      const int e = t + NT * u;
+      const int m = A_KC ? e / KT : e % M, kt = A_KC ? e % KT : e / M;
+      ra[u] = a(m, k0 + kt);
+    }
+#pragma unroll
+    for (int u = 0; u < PB; ++u) {
+      const int e = t + NT * u;
+      const int n = B_NC ? e % N : e / KT, kt = B_NC ? e / N : e % KT;
+      rb[u] = b(k0 + kt, n);
+    }
+  };
+  fetch(0);
+  for (int k0 = 0; k0 < K; k0 += KT) {
+#pragma unroll
+    for (int u = 0; u < PA; ++u) {
+      const int e = t + NT * u;
+      const int m = A_KC ? e / KT : e % M, kt = A_KC ? e % KT : e / M;
+      sa[kt * MS + m] = ra[u];
+    }
+#pragma unroll
+    for (int u = 0; u < PB; ++u) {
+      const int e = t + NT * u;
+      const int n = B_NC ? e % N : e / KT, kt = B_NC ? e / N : e % KT;
+      sb[kt * NS + n] = rb[u];
+    }
+    __syncthreads();
+    if (k0 + KT < K) fetch(k0 + KT);
+#pragma unroll 4
+    for (int kt = 0; kt < KT; ++kt) {
+      float av[TM], bv[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) av[i] = sa[kt * MS + 16 * i + tr];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) bv[j] = sb[kt * NS + 16 * j + tc];
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+}
+constexpr int SA_FLOATS = KT * (64 + 1), SB_FLOATS = KT * (128 + 1);
+
 template <int TM, int TN>
 __device__ __forceinline__ void zero(float (&acc)[TM][TN]) {
 #pragma unroll
@@ -130,10 +192,15 @@ __global__ void __launch_bounds__(NT) bwd_prep_kernel(const void* __restrict__ q
     sQ[r][cc] = in ? load1(q, off, QB) : 0.0f;
   }
   if (t < C) sB[t] = t < p.Lc ? beta[(p.t0 + t) * H + p.h] : 0.0f;
-  if (t < D) {
+  for (int e = t; e < C * D; e += NT) {
+    const int r = e / D, cc = e % D;
+    sG[r][cc] = r < p.Lc ? g[(p.t0 + r) * HD + (int64_t)p.h * D + cc] : 0.0f;
+  }
+  __syncthreads();
+  if (t < D) {  // gamma: running sum down each channel
     float run = 0.0f;
     for (int r = 0; r < C; ++r) {
-      if (r < p.Lc) run += g[(p.t0 + r) * HD + (int64_t)p.h * D + t];
+      run += sG[r][t];
       sG[r][t] = run;
     }
   }
@@ -157,30 +224,30 @@ __global__ void __launch_bounds__(NT) bwd_prep_kernel(const void* __restrict__ q
     im[Rec::P + e] = pp;
   }
   __syncthreads();
-  // M = (I + diag(b) At)^-1, unit lower triangular: column s per thread
-  if (t < C) {
-    const int s = t;
+  // M = (I + diag(b) At)^-1, unit lower triangular, by forward substitution
+  // down each column: M[r][s] = -b_r sum_{s <= u < r} At[r][u] M[u][s].
+  // Column s belongs to lanes 4s .. 4s + 3 of one wave (a quarter of the
+  // sum each, combined by shuffles); rows go in order.
+  {
+    const int s = t >> 2, qd = t & 3;
     for (int r = 0; r < C; ++r) {
-      float m;
-      if (r < s) {
-        m = 0.0f;
-      } else if (r == s) {
-        m = 1.0f;
-      } else {
-        float acc = 0.0f;
-        for (int u = s; u < r; ++u) acc = fmaf(sA[r][u], sM[u][s], acc);
-        m = -sB[r] * acc;
-      }
-      sM[r][s] = m;
+      float acc = 0.0f;
+      for (int u = s + qd; u < r; u += 4) acc = fmaf(sA[r][u], sM[u][s], acc);
+      acc += __shfl_xor(acc, 1);
+      acc += __shfl_xor(acc, 2);
+      if (qd == 0) sM[r][s] = r < s ? 0.0f : (r == s ? 1.0f : -sB[r] * acc);
     }
   }
   __syncthreads();
   for (int e = t; e < C * C; e += NT) im[Rec::M + e] = sM[e / C][e % C];
   const int tr = t >> 4, tc = t & 15;
+  // At is no longer needed: its space holds the products' LDS slabs
+  float* sa = &sA[0][0];
+  float* sb = sa + SA_FLOATS;
   {  // W = M diag(b) K_E
     float acc[4][8];
     zero(acc);
-    gemm_acc(acc, C, [&](int r, int s) { return sM[r][s]; },
+    gemm_staged<4, 8, true, true>(acc, C, sa, sb, [&](int r, int s) { return sM[r][s]; },
              [&](int s, int cc) { return sB[s] * sK[s][cc] * __expf(sG[s][cc]); });
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -190,7 +257,7 @@ __global__ void __launch_bounds__(NT) bwd_prep_kernel(const void* __restrict__ q
   {  // U = M diag(b) V
     float acc[4][8];
     zero(acc);
-    gemm_acc(acc, C, [&](int r, int s) { return sM[r][s]; },
+    gemm_staged<4, 8, true, true>(acc, C, sa, sb, [&](int r, int s) { return sM[r][s]; },
              [&](int s, int j) {
                return s < p.Lc
                           ? sB[s] * load1(v, (p.t0 + s) * HD + (int64_t)p.h * D + j, QB)
@@ -205,7 +272,7 @@ __global__ void __launch_bounds__(NT) bwd_prep_kernel(const void* __restrict__ q
   {  // Qt = scale (Q_E - P W)
     float acc[4][8];
     zero(acc);
-    gemm_acc(acc, C, [&](int r, int s) { return sP[r][s]; },
+    gemm_staged<4, 8, true, true>(acc, C, sa, sb, [&](int r, int s) { return sP[r][s]; },
              [&](int s, int cc) { return im[Rec::W + s * D + cc]; });
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -235,6 +302,11 @@ __global__ void __launch_bounds__(NT) bwd_walk_kernel(const float* __restrict__ 
                                                       const float* __restrict__ R_init,
                                                       float* __restrict__ R_end,
                                                       float* __restrict__ rec) {
+  // the chunk's matrices (A1 and A2, then A3 in A1's place), its 64-column
+  // slice of B, the carried matrix and Z
+  __shared__ __attribute__((aligned(16))) float sM1[C * D];
+  __shared__ __attribute__((aligned(16))) float sM2[C * D];
+  __shared__ __attribute__((aligned(16))) float sBt[C][64 + 4];
   __shared__ float sR[D][64 + 1], sZ[C][64 + 1];
   const int64_t b = blockIdx.x;
   const int tile = static_cast<int>(b & 1);
@@ -259,6 +331,10 @@ __global__ void __launch_bounds__(NT) bwd_walk_kernel(const float* __restrict__ 
     for (int e = 0; e < 4; ++e)
       R[a][e] = R_init ? R_init[sbase + (int64_t)(row0 + a) * D + jg0 + e] : 0.0f;
   const int tr = t >> 4, tc = t & 15;
+  auto copy_mat = [&](float* dst, const float* src) {
+    for (int e = 4 * t; e < C * D; e += 4 * NT)
+      *reinterpret_cast<f32x4*>(dst + e) = *reinterpret_cast<const f32x4*>(src + e);
+  };
   for (int it = 0; it < nch; ++it) {
     const int c = FWD ? it : nch - 1 - it;
     const int64_t pair = (bos / C + n + c) * H + h;
@@ -266,6 +342,20 @@ __global__ void __launch_bounds__(NT) bwd_walk_kernel(const float* __restrict__ 
     const int Lc = static_cast<int>(L - (int64_t)c * C < C ? L - (int64_t)c * C : C);
     const int64_t t0 = bos + (int64_t)c * C;
     float* rc = rec + pair * (int64_t)(D * D);
+    copy_mat(sM1, im + (FWD ? Rec::W : Rec::KD));
+    copy_mat(sM2, im + (FWD ? Rec::KD : Rec::W));
+    for (int e = t; e < C * 16; e += NT) {  // B tile: 64 rows x 16 float4
+      const int r = e >> 4, q4 = (e & 15) * 4;
+      f32x4 bv;
+      if (FWD) {
+        bv = *reinterpret_cast<const f32x4*>(im + Rec::U + r * D + 64 * tile + q4);
+      } else {
+        bv = (d_o && r < Lc) ? load4(d_o, (t0 + r) * HD + (int64_t)h * D + 64 * tile + q4, DOB)
+                             : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) sBt[r][q4 + u] = bv[u];
+    }
 #pragma unroll
     for (int a = 0; a < 8; ++a)
 #pragma unroll
@@ -277,8 +367,7 @@ __global__ void __launch_bounds__(NT) bwd_walk_kernel(const float* __restrict__ 
     {  // Z = A1 R, A1 = W (forward) or K_D (backward)
       float z[4][4];
       zero(z);
-      const float* A1 = im + (FWD ? Rec::W : Rec::KD);
-      gemm_acc(z, D, [&](int r, int cc) { return A1[r * D + cc]; },
+      gemm_acc(z, D, [&](int r, int cc) { return sM1[r * D + cc]; },
                [&](int cc, int j) { return sR[cc][j]; });
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -286,34 +375,32 @@ __global__ void __launch_bounds__(NT) bwd_walk_kernel(const float* __restrict__ 
         for (int j = 0; j < 4; ++j) sZ[16 * i + tr][16 * j + tc] = z[i][j];
     }
     __syncthreads();
-    // R <- e^gamma_C R - A2^T Z + A3^T B
-    const float* A2 = im + (FWD ? Rec::KD : Rec::W);
-    const float* A3 = im + (FWD ? Rec::KD : Rec::QT);
+    if (!FWD) copy_mat(sM1, im + Rec::QT);  // A3 (A1 = K_D is done)
+    __syncthreads();
+    // R <- e^gamma_C R - A2^T Z + A3^T B, A2 = K_D / W, A3 = K_D / Qt
+    const float* A3 = FWD ? sM2 : sM1;
 #pragma unroll
     for (int a = 0; a < 8; ++a) {
       const float ec = im[Rec::EC + row0 + a];
 #pragma unroll
       for (int e = 0; e < 4; ++e) R[a][e] *= ec;
     }
+#pragma unroll 2
     for (int r = 0; r < C; ++r) {
-      float bb[4];
-      if (FWD) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) bb[e] = im[Rec::U + r * D + jg0 + e];
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          bb[e] = (d_o && r < Lc) ? load1(d_o, (t0 + r) * HD + (int64_t)h * D + jg0 + e, DOB)
-                                  : 0.0f;
-      }
+      const f32x4 z4 = f32x4{sZ[r][col0], sZ[r][col0 + 1], sZ[r][col0 + 2], sZ[r][col0 + 3]};
+      const f32x4 b4 = *reinterpret_cast<const f32x4*>(&sBt[r][col0]);
+      const f32x4 a2a = *reinterpret_cast<const f32x4*>(sM2 + r * D + row0);
+      const f32x4 a2b = *reinterpret_cast<const f32x4*>(sM2 + r * D + row0 + 4);
+      const f32x4 a3a = *reinterpret_cast<const f32x4*>(A3 + r * D + row0);
+      const f32x4 a3b = *reinterpret_cast<const f32x4*>(A3 + r * D + row0 + 4);
 #pragma unroll
       for (int a = 0; a < 8; ++a) {
-        const float a2 = A2[r * D + row0 + a], a3 = A3[r * D + row0 + a];
+        const float a2 = a < 4 ? a2a[a] : a2b[a - 4], a3 = a < 4 ? a3a[a] : a3b[a - 4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) R[a][e] = fmaf(a3, bb[e], fmaf(-a2, sZ[r][col0 + e], R[a][e]));
+        for (int e = 0; e < 4; ++e) R[a][e] = fmaf(a3, b4[e], fmaf(-a2, z4[e], R[a][e]));
       }
     }
-    __syncthreads();  // sR / sZ are rewritten by the next chunk
+    __syncthreads();  // the LDS buffers are refilled by the next chunk
   }
   if (R_end) {
 #pragma unroll
@@ -329,11 +416,15 @@ __global__ void __launch_bounds__(NT) bwd_grad_kernel(
     const void* __restrict__ d_o, const float* __restrict__ beta,
     const int32_t* __restrict__ cu, int N, int T_tot, int H, int maxnch, float scale,
     const float* __restrict__ img, const float* __restrict__ Srec,
-    const float* __restrict__ dSrec, float* scr, float* __restrict__ dq,
+    const float* __restrict__ dSrec, float* __restrict__ scr, float* __restrict__ dq,
     float* __restrict__ dk, float* __restrict__ dv, float* __restrict__ dg,
     float* __restrict__ dbeta) {
   __shared__ float sT[C][C + 1], sDA[C][C + 1], sDP[C][C + 1];
-  __shared__ float sAk[C][D], sAg[C][D], sB[C], sDB[C];
+  __shared__ float sB[C], sDB[C], sPart[D];
+  // the products' LDS slabs, then (pairwise phase) K, Q and gamma of the chunk
+  __shared__ float sU[3 * C * D];
+  float* sa = sU;
+  float* sb = sU + SA_FLOATS;
   ChunkPos p;
   if (!chunk_of_block(cu, N, T_tot, H, maxnch, p)) return;
   const int t = threadIdx.x;
@@ -352,6 +443,12 @@ __global__ void __launch_bounds__(NT) bwd_grad_kernel(
     return (d_o && r < Lc) ? load1(d_o, tok(r, cc), DOB) : 0.0f;
   };
   auto Gf = [&](int r, int cc) { return im[Rec::G + r * D + cc]; };
+  auto put8 = [&](float (&acc)[4][8], int off, float mul) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) sc[off + (16 * i + tr) * D + 16 * j + tc] = mul * acc[i][j];
+  };
   if (t < C) {
     sB[t] = t < Lc ? beta[(p.t0 + t) * H + p.h] : 0.0f;
     sDB[t] = 0.0f;
@@ -360,8 +457,9 @@ __global__ void __launch_bounds__(NT) bwd_grad_kernel(
   {  // X = V - K_E S
     float acc[4][8];
     zero(acc);
-    gemm_acc(acc, D, [&](int r, int cc) { return Kf(r, cc) * __expf(Gf(r, cc)); },
-             [&](int cc, int j) { return S[cc * D + j]; });
+    gemm_staged<4, 8, true, true>(acc, D, sa, sb,
+                                  [&](int r, int cc) { return Kf(r, cc) * __expf(Gf(r, cc)); },
+                                  [&](int cc, int j) { return S[cc * D + j]; });
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -374,31 +472,28 @@ __global__ void __launch_bounds__(NT) bwd_grad_kernel(
   {  // Delta = M diag(b) X
     float acc[4][8];
     zero(acc);
-    gemm_acc(acc, C, [&](int r, int s) { return im[Rec::M + r * C + s]; },
-             [&](int s, int j) { return sB[s] * sc[Scr::X + s * D + j]; });
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) sc[Scr::DL + (16 * i + tr) * D + 16 * j + tc] = acc[i][j];
+    gemm_staged<4, 8, true, true>(acc, C, sa, sb, [&](int r, int s) { return im[Rec::M + r * C + s]; },
+                                  [&](int s, int j) { return sB[s] * sc[Scr::X + s * D + j]; });
+    put8(acc, Scr::DL, 1.0f);
   }
   {  // dDelta = K_D dS_next + scale P^T dO
     float acc[4][8];
     zero(acc);
-    gemm_acc(acc, D, [&](int r, int cc) { return im[Rec::KD + r * D + cc]; },
-             [&](int cc, int j) { return dS[cc * D + j]; });
-    gemm_acc(acc, C, [&](int r, int s) { return scale * im[Rec::P + s * C + r]; },
-             [&](int s, int j) { return dOf(s, j); });
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) sc[Scr::DD + (16 * i + tr) * D + 16 * j + tc] = acc[i][j];
+    gemm_staged<4, 8, true, true>(acc, D, sa, sb,
+                                  [&](int r, int cc) { return im[Rec::KD + r * D + cc]; },
+                                  [&](int cc, int j) { return dS[cc * D + j]; });
+    gemm_staged<4, 8, false, true>(acc, C, sa, sb,
+                                   [&](int r, int s) { return scale * im[Rec::P + s * C + r]; },
+                                   [&](int s, int j) { return dOf(s, j); });
+    put8(acc, Scr::DD, 1.0f);
   }
   __syncthreads();
   {  // dY = M^T dDelta, dX = diag(b) dY (= dv), dbeta += rowsum(dY . X)
     float acc[4][8];
     zero(acc);
-    gemm_acc(acc, C, [&](int r, int s) { return im[Rec::M + s * C + r]; },
-             [&](int s, int j) { return sc[Scr::DD + s * D + j]; });
+    gemm_staged<4, 8, false, true>(acc, C, sa, sb,
+                                   [&](int r, int s) { return im[Rec::M + s * C + r]; },
+                                   [&](int s, int j) { return sc[Scr::DD + s * D + j]; });
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 16 * i + tr;
@@ -420,8 +515,9 @@ __global__ void __launch_bounds__(NT) bwd_grad_kernel(
   {  // dM = dDelta Y^T
     float a4[4][4];
     zero(a4);
-    gemm_acc(a4, D, [&](int r, int j) { return sc[Scr::DD + r * D + j]; },
-             [&](int j, int s) { return sB[s] * sc[Scr::X + s * D + j]; });
+    gemm_staged<4, 4, true, false>(a4, D, sa, sb,
+                                   [&](int r, int j) { return sc[Scr::DD + r * D + j]; },
+                                   [&](int j, int s) { return sB[s] * sc[Scr::X + s * D + j]; });
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -430,8 +526,8 @@ __global__ void __launch_bounds__(NT) bwd_grad_kernel(
   {  // dP = scale dO Delta^T on s <= r
     float a4[4][4];
     zero(a4);
-    gemm_acc(a4, D, [&](int r, int j) { return dOf(r, j); },
-             [&](int j, int s) { return sc[Scr::DL + s * D + j]; });
+    gemm_staged<4, 4, true, false>(a4, D, sa, sb, [&](int r, int j) { return dOf(r, j); },
+                                   [&](int j, int s) { return sc[Scr::DL + s * D + j]; });
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -444,8 +540,8 @@ __global__ void __launch_bounds__(NT) bwd_grad_kernel(
   {  // dM M^T
     float a4[4][4];
     zero(a4);
-    gemm_acc(a4, C, [&](int r, int u) { return sT[r][u]; },
-             [&](int u, int s) { return im[Rec::M + s * C + u]; });
+    gemm_staged<4, 4, true, false>(a4, C, sa, sb, [&](int r, int u) { return sT[r][u]; },
+                                   [&](int u, int s) { return im[Rec::M + s * C + u]; });
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -455,8 +551,9 @@ __global__ void __launch_bounds__(NT) bwd_grad_kernel(
   {  // dA = -M^T (dM M^T) on s < r
     float a4[4][4];
     zero(a4);
-    gemm_acc(a4, C, [&](int r, int u) { return im[Rec::M + u * C + r]; },
-             [&](int u, int s) { return sDA[u][s]; });
+    gemm_staged<4, 4, false, true>(a4, C, sa, sb,
+                                   [&](int r, int u) { return im[Rec::M + u * C + r]; },
+                                   [&](int u, int s) { return sDA[u][s]; });
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -465,83 +562,122 @@ __global__ void __launch_bounds__(NT) bwd_grad_kernel(
         sT[r][s] = (s < r && r < Lc) ? -a4[i][j] : 0.0f;
       }
   }
-  __syncthreads();
-  if (t < C) {  // dbeta += sum_s dA[r, s] At[r, s]
-    float a = 0.0f;
-    for (int s = 0; s < t; ++s) a = fmaf(sT[t][s], im[Rec::AT + t * C + s], a);
-    sDB[t] += a;
-  }
   {  // dK_E = -dX S^T
     float acc[4][8];
     zero(acc);
-    gemm_acc(acc, D, [&](int r, int j) { return sc[Scr::DX + r * D + j]; },
-             [&](int j, int cc) { return S[cc * D + j]; });
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) sc[Scr::DKE + (16 * i + tr) * D + 16 * j + tc] = -acc[i][j];
+    gemm_staged<4, 8, true, false>(acc, D, sa, sb,
+                                   [&](int r, int j) { return sc[Scr::DX + r * D + j]; },
+                                   [&](int j, int cc) { return S[cc * D + j]; });
+    put8(acc, Scr::DKE, -1.0f);
   }
   {  // dQ_E = scale dO S^T
     float acc[4][8];
     zero(acc);
-    gemm_acc(acc, D, [&](int r, int j) { return dOf(r, j); },
-             [&](int j, int cc) { return S[cc * D + j]; });
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        sc[Scr::DQE + (16 * i + tr) * D + 16 * j + tc] = scale * acc[i][j];
+    gemm_staged<4, 8, true, false>(acc, D, sa, sb, [&](int r, int j) { return dOf(r, j); },
+                                   [&](int j, int cc) { return S[cc * D + j]; });
+    put8(acc, Scr::DQE, scale);
   }
   {  // dK_D = Delta dS_next^T
     float acc[4][8];
     zero(acc);
-    gemm_acc(acc, D, [&](int r, int j) { return sc[Scr::DL + r * D + j]; },
-             [&](int j, int cc) { return dS[cc * D + j]; });
+    gemm_staged<4, 8, true, false>(acc, D, sa, sb,
+                                   [&](int r, int j) { return sc[Scr::DL + r * D + j]; },
+                                   [&](int j, int cc) { return dS[cc * D + j]; });
+    put8(acc, Scr::DKD, 1.0f);
+  }
+  {  // dbeta += sum_s dA[r, s] At[r, s]: row r on lanes 4r .. 4r + 3
+    const int r = t >> 2, qd = t & 3;
+    float a = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) sc[Scr::DKD + (16 * i + tr) * D + 16 * j + tc] = acc[i][j];
+    for (int u = 0; u < C / 4; ++u) {
+      const int s2 = 4 * u + qd;
+      a = fmaf(sT[r][s2], im[Rec::AT + r * C + s2], a);  // dA is 0 for s >= r
+    }
+    a += __shfl_xor(a, 1);
+    a += __shfl_xor(a, 2);
+    if (qd == 0) sDB[r] += a;
+  }
+  {  // d e^gamma_C[c] = sum_j dS_next[c, j] S[c, j]: channel c on threads c, c + 128
+    const int cc = t & (D - 1), half = t >> 7;
+    float d = 0.0f;
+#pragma unroll 16
+    for (int j = 64 * half; j < 64 * half + 64; ++j) d = fmaf(dS[cc * D + j], S[cc * D + j], d);
+    sPart[cc] = 0.0f;
+    __syncthreads();
+    if (half == 1) sPart[cc] = d;
+    __syncthreads();
+    if (half == 0) sPart[cc] += d;
+  }
+  // The chunk's K, Q and gamma into LDS for the pairwise terms
+  float* sK = sU;
+  float* sQ = sU + C * D;
+  float* sG = sU + 2 * C * D;
+  for (int e = t; e < C * D; e += NT) {
+    const int r = e / D, cc = e % D;
+    sK[e] = Kf(r, cc);
+    sQ[e] = Qf(r, cc);
+    sG[e] = Gf(r, cc);
   }
   __syncthreads();
-  if (t < D) {  // key channel cc: the decay factors and the pairwise terms of At and P
-    const int cc = t;
-    const float gC = Gf(C - 1, cc);
+  // Thread (channel cc, parity par) finishes the rows x = par, par + 2, ...:
+  // the decay-factor terms of K_E, Q_E, K_D, then the pairwise terms of At
+  // and P with x as the later token (s <= x) and as the earlier one (r >= x).
+  {
+    const int cc = t & (D - 1), par = t >> 7;
+    const float gC = sG[(C - 1) * D + cc];
+    const float dEC = sPart[cc];
     float dgC = 0.0f;
-    for (int j = 0; j < D; ++j) dgC = fmaf(dS[cc * D + j], S[cc * D + j], dgC);
-    dgC *= __expf(gC);
-    for (int r = 0; r < C; ++r) {
-      const float kr = Kf(r, cc), qr = Qf(r, cc), gr = Gf(r, cc);
-      const float E = __expf(gr), F = __expf(gC - gr);
-      const float dke = sc[Scr::DKE + r * D + cc], dqe = sc[Scr::DQE + r * D + cc];
-      const float dkd = sc[Scr::DKD + r * D + cc];
-      sAk[r][cc] = dke * E + dkd * F;
-      sAg[r][cc] = (dke * kr + dqe * qr) * E - dkd * kr * F;
-      dgC = fmaf(dkd * kr, F, dgC);
+    float nke = 0.0f, nqe = 0.0f, nkd = 0.0f;  // the next row's terms, read ahead
+    if (par < Lc) {
+      nke = sc[Scr::DKE + par * D + cc];
+      nqe = sc[Scr::DQE + par * D + cc];
+      nkd = sc[Scr::DKD + par * D + cc];
     }
-    for (int r = 0; r < Lc; ++r) {
-      const float kr = Kf(r, cc), qr = Qf(r, cc), gr = Gf(r, cc), br = sB[r];
-      float dkr = 0.0f, dqr = 0.0f, dgr = 0.0f;
-      for (int s = 0; s <= r; ++s) {
-        const float w = __expf(gr - Gf(s, cc));
-        const float u = w * Kf(s, cc);
-        const float al = s < r ? sT[r][s] * br : 0.0f;
-        const float pi = sDP[r][s];
-        const float phi = al * kr + pi * qr;
-        dkr = fmaf(al, u, dkr);
-        dqr = fmaf(pi, u, dqr);
-        dgr = fmaf(phi, u, dgr);
-        sAk[s][cc] = fmaf(phi, w, sAk[s][cc]);
-        sAg[s][cc] = fmaf(-phi, u, sAg[s][cc]);
+    for (int x = par; x < Lc; x += 2) {
+      const float kx = sK[x * D + cc], qx = sQ[x * D + cc], gx = sG[x * D + cc], bx = sB[x];
+      const float E = __expf(gx), F = __expf(gC - gx);
+      const float dke = nke, dqe = nqe, dkd = nkd;
+      if (x + 2 < Lc) {
+        nke = sc[Scr::DKE + (x + 2) * D + cc];
+        nqe = sc[Scr::DQE + (x + 2) * D + cc];
+        nkd = sc[Scr::DKD + (x + 2) * D + cc];
       }
-      sAk[r][cc] += dkr;
-      sAg[r][cc] += dgr;
-      dq[tok(r, cc)] = sc[Scr::DQE + r * D + cc] * __expf(gr) + dqr;
+      float dkx = dke * E + dkd * F;
+      float dgx = (dke * kx + dqe * qx) * E - dkd * kx * F;
+      float dqx = dqe * E;
+      dgC = fmaf(dkd * kx, F, dgC);
+      for (int s = 0; s <= x; ++s) {  // x later: pairs (x, s)
+        const float u = __expf(gx - sG[s * D + cc]) * sK[s * D + cc];
+        const float al = s < x ? sT[x][s] * bx : 0.0f;
+        const float pi = sDP[x][s];
+        dkx = fmaf(al, u, dkx);
+        dqx = fmaf(pi, u, dqx);
+        dgx = fmaf(al * kx + pi * qx, u, dgx);
+      }
+      for (int r = x; r < Lc; ++r) {  // x earlier: pairs (r, x)
+        const float w = __expf(sG[r * D + cc] - gx);
+        const float al = x < r ? sT[r][x] * sB[r] : 0.0f;
+        const float phi = al * sK[r * D + cc] + sDP[r][x] * sQ[r * D + cc];
+        dkx = fmaf(phi, w, dkx);
+        dgx = fmaf(-phi * w, kx, dgx);
+      }
+      dq[tok(x, cc)] = dqx;
+      dk[tok(x, cc)] = dkx;
+      sc[Scr::DX + x * D + cc] = dgx;  // dgamma, summed below
     }
-    float run = dgC;
-    for (int r = Lc - 1; r >= 0; --r) {
-      run += sAg[r][cc];
-      dg[tok(r, cc)] = run;
-      dk[tok(r, cc)] = sAk[r][cc];
+    __syncthreads();  // sPart (d e^gamma_C) read above by every thread
+    if (par == 1) sPart[cc] = dgC;
+    __syncthreads();
+    if (par == 0) {
+      float dgam[C];
+#pragma unroll
+      for (int x = 0; x < C; ++x) dgam[x] = x < Lc ? sc[Scr::DX + x * D + cc] : 0.0f;
+      float run = dgC + sPart[cc] + dEC * __expf(gC);
+#pragma unroll
+      for (int x = C - 1; x >= 0; --x) {
+        run += dgam[x];
+        if (x < Lc) dg[tok(x, cc)] = run;
+      }
     }
   }
   if (t < Lc) dbeta[(p.t0 + t) * H + p.h] = sDB[t];
