@@ -169,59 +169,79 @@ __device__ __forceinline__ bool chunk_of_block(const int32_t* cu, int N, int T_t
 }
 
 template <bool QB>
-__global__ void __launch_bounds__(NT) bwd_prep_kernel(const void* __restrict__ q,
-                                                      const void* __restrict__ k,
-                                                      const void* __restrict__ v,
-                                                      const float* __restrict__ g,
-                                                      const float* __restrict__ beta,
-                                                      const int32_t* __restrict__ cu, int N,
-                                                      int T_tot, int H, int maxnch, float scale,
-                                                      float* img) {
-  __shared__ float sK[C][D + 1], sQ[C][D + 1], sG[C][D + 1];
+__global__ void __launch_bounds__(NT, 2) bwd_prep_kernel(const void* __restrict__ q,
+                                                         const void* __restrict__ k,
+                                                         const void* __restrict__ v,
+                                                         const float* __restrict__ g,
+                                                         const float* __restrict__ beta,
+                                                         const int32_t* __restrict__ cu, int N,
+                                                         int T_tot, int H, int maxnch,
+                                                         float scale, float* __restrict__ img) {
+  constexpr int CS = 16;  // channels per slab of the At / P sums
   __shared__ float sA[C][C + 1], sP[C][C + 1], sM[C][C + 1], sB[C];
+  // slabs of K, Q, gamma (CS channels), later the products' LDS slabs
+  __shared__ float sS[3 * C * (CS + 1)];
   ChunkPos p;
   if (!chunk_of_block(cu, N, T_tot, H, maxnch, p)) return;
   const int t = threadIdx.x;
   const int64_t HD = (int64_t)H * D;
   float* im = img + p.pair * Rec::floats;
-  for (int e = t; e < C * D; e += NT) {
-    const int r = e / D, cc = e % D;
-    const bool in = r < p.Lc;
-    const int64_t off = (p.t0 + r) * HD + (int64_t)p.h * D + cc;
-    sK[r][cc] = in ? load1(k, off, QB) : 0.0f;
-    sQ[r][cc] = in ? load1(q, off, QB) : 0.0f;
-  }
+  auto tok = [&](int r, int cc) { return (p.t0 + r) * HD + (int64_t)p.h * D + cc; };
+  auto Kf = [&](int r, int cc) { return r < p.Lc ? load1(k, tok(r, cc), QB) : 0.0f; };
+  auto Qf = [&](int r, int cc) { return r < p.Lc ? load1(q, tok(r, cc), QB) : 0.0f; };
   if (t < C) sB[t] = t < p.Lc ? beta[(p.t0 + t) * H + p.h] : 0.0f;
-  for (int e = t; e < C * D; e += NT) {
-    const int r = e / D, cc = e % D;
-    sG[r][cc] = r < p.Lc ? g[(p.t0 + r) * HD + (int64_t)p.h * D + cc] : 0.0f;
-  }
-  __syncthreads();
-  if (t < D) {  // gamma: running sum down each channel
+  if (t < D) {  // gamma: running sum of g down channel t (rows past the end repeat the last)
+    float gv[C];
+#pragma unroll
+    for (int r = 0; r < C; ++r) gv[r] = r < p.Lc ? g[tok(r, t)] : 0.0f;
     float run = 0.0f;
+#pragma unroll
     for (int r = 0; r < C; ++r) {
-      run += sG[r][t];
-      sG[r][t] = run;
+      run += gv[r];
+      im[Rec::G + r * D + t] = run;
     }
   }
   __syncthreads();
-  for (int e = t; e < C * D; e += NT) im[Rec::G + e] = sG[e / D][e % D];
-  // At and P, one (r, s) pair per thread at a time
-  for (int e = t; e < C * C; e += NT) {
-    const int r = e / C, s = e % C;
-    float a = 0.0f, pp = 0.0f;
-    if (s <= r) {
-      for (int cc = 0; cc < D; ++cc) {
-        const float ks = sK[s][cc] * __expf(sG[r][cc] - sG[s][cc]);
-        a = fmaf(sK[r][cc], ks, a);
-        pp = fmaf(sQ[r][cc], ks, pp);
+  auto Gf = [&](int r, int cc) { return im[Rec::G + r * D + cc]; };
+  {  // At and P: thread t owns the pairs (r, s) = e / 64, e % 64 for e = t + 256 u
+    float* sK = sS;
+    float* sQ = sS + C * (CS + 1);
+    float* sG = sS + 2 * C * (CS + 1);
+    float a[16], pp[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) a[u] = pp[u] = 0.0f;
+    for (int c0 = 0; c0 < D; c0 += CS) {
+      for (int e = t; e < C * CS; e += NT) {
+        const int r = e / CS, ch = e % CS;
+        sK[r * (CS + 1) + ch] = Kf(r, c0 + ch);
+        sQ[r * (CS + 1) + ch] = Qf(r, c0 + ch);
+        sG[r * (CS + 1) + ch] = Gf(r, c0 + ch);
       }
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int e = t + NT * u, r = e / C, s2 = e % C;
+        if (s2 <= r) {
+#pragma unroll
+          for (int ch = 0; ch < CS; ++ch) {
+            const float ks = sK[s2 * (CS + 1) + ch] *
+                             __expf(sG[r * (CS + 1) + ch] - sG[s2 * (CS + 1) + ch]);
+            a[u] = fmaf(sK[r * (CS + 1) + ch], ks, a[u]);
+            pp[u] = fmaf(sQ[r * (CS + 1) + ch], ks, pp[u]);
+          }
+        }
+      }
+      __syncthreads();
     }
-    a = s < r ? a : 0.0f;
-    sA[r][s] = a;
-    sP[r][s] = pp;
-    im[Rec::AT + e] = a;
-    im[Rec::P + e] = pp;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int e = t + NT * u, r = e / C, s2 = e % C;
+      const float av = s2 < r ? a[u] : 0.0f, pv = s2 <= r ? pp[u] : 0.0f;
+      sA[r][s2] = av;
+      sP[r][s2] = pv;
+      im[Rec::AT + e] = av;
+      im[Rec::P + e] = pv;
+    }
   }
   __syncthreads();
   // M = (I + diag(b) At)^-1, unit lower triangular, by forward substitution
@@ -229,26 +249,27 @@ __global__ void __launch_bounds__(NT) bwd_prep_kernel(const void* __restrict__ q
   // Column s belongs to lanes 4s .. 4s + 3 of one wave (a quarter of the
   // sum each, combined by shuffles); rows go in order.
   {
-    const int s = t >> 2, qd = t & 3;
+    const int s2 = t >> 2, qd = t & 3;
     for (int r = 0; r < C; ++r) {
       float acc = 0.0f;
-      for (int u = s + qd; u < r; u += 4) acc = fmaf(sA[r][u], sM[u][s], acc);
+      for (int u = s2 + qd; u < r; u += 4) acc = fmaf(sA[r][u], sM[u][s2], acc);
       acc += __shfl_xor(acc, 1);
       acc += __shfl_xor(acc, 2);
-      if (qd == 0) sM[r][s] = r < s ? 0.0f : (r == s ? 1.0f : -sB[r] * acc);
+      if (qd == 0) sM[r][s2] = r < s2 ? 0.0f : (r == s2 ? 1.0f : -sB[r] * acc);
     }
   }
   __syncthreads();
   for (int e = t; e < C * C; e += NT) im[Rec::M + e] = sM[e / C][e % C];
   const int tr = t >> 4, tc = t & 15;
-  // At is no longer needed: its space holds the products' LDS slabs
-  float* sa = &sA[0][0];
-  float* sb = sa + SA_FLOATS;
+  float* sa = sS;
+  float* sb = sS + SA_FLOATS;
   {  // W = M diag(b) K_E
     float acc[4][8];
     zero(acc);
-    gemm_staged<4, 8, true, true>(acc, C, sa, sb, [&](int r, int s) { return sM[r][s]; },
-             [&](int s, int cc) { return sB[s] * sK[s][cc] * __expf(sG[s][cc]); });
+    gemm_staged<4, 8, true, true>(acc, C, sa, sb, [&](int r, int s2) { return sM[r][s2]; },
+                                  [&](int s2, int cc) {
+                                    return sB[s2] * Kf(s2, cc) * __expf(Gf(s2, cc));
+                                  });
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -257,12 +278,10 @@ __global__ void __launch_bounds__(NT) bwd_prep_kernel(const void* __restrict__ q
   {  // U = M diag(b) V
     float acc[4][8];
     zero(acc);
-    gemm_staged<4, 8, true, true>(acc, C, sa, sb, [&](int r, int s) { return sM[r][s]; },
-             [&](int s, int j) {
-               return s < p.Lc
-                          ? sB[s] * load1(v, (p.t0 + s) * HD + (int64_t)p.h * D + j, QB)
-                          : 0.0f;
-             });
+    gemm_staged<4, 8, true, true>(acc, C, sa, sb, [&](int r, int s2) { return sM[r][s2]; },
+                                  [&](int s2, int j) {
+                                    return s2 < p.Lc ? sB[s2] * load1(v, tok(s2, j), QB) : 0.0f;
+                                  });
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -272,21 +291,21 @@ __global__ void __launch_bounds__(NT) bwd_prep_kernel(const void* __restrict__ q
   {  // Qt = scale (Q_E - P W)
     float acc[4][8];
     zero(acc);
-    gemm_staged<4, 8, true, true>(acc, C, sa, sb, [&](int r, int s) { return sP[r][s]; },
-             [&](int s, int cc) { return im[Rec::W + s * D + cc]; });
+    gemm_staged<4, 8, true, true>(acc, C, sa, sb, [&](int r, int s2) { return sP[r][s2]; },
+                                  [&](int s2, int cc) { return im[Rec::W + s2 * D + cc]; });
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int r = 16 * i + tr, cc = 16 * j + tc;
-        im[Rec::QT + r * D + cc] = scale * (sQ[r][cc] * __expf(sG[r][cc]) - acc[i][j]);
+        im[Rec::QT + r * D + cc] = scale * (Qf(r, cc) * __expf(Gf(r, cc)) - acc[i][j]);
       }
   }
   for (int e = t; e < C * D; e += NT) {
     const int r = e / D, cc = e % D;
-    im[Rec::KD + e] = sK[r][cc] * __expf(sG[C - 1][cc] - sG[r][cc]);
+    im[Rec::KD + e] = Kf(r, cc) * __expf(Gf(C - 1, cc) - Gf(r, cc));
   }
-  if (t < D) im[Rec::EC + t] = __expf(sG[C - 1][t]);
+  if (t < D) im[Rec::EC + t] = __expf(Gf(C - 1, t));
 }
 
 // One (sequence, head, 64-column tile): thread t holds rows 8 (t / 16) .. +7
@@ -411,7 +430,7 @@ __global__ void __launch_bounds__(NT) bwd_walk_kernel(const float* __restrict__ 
 }
 
 template <bool QB, bool DOB>
-__global__ void __launch_bounds__(NT) bwd_grad_kernel(
+__global__ void __launch_bounds__(NT, 2) bwd_grad_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const void* __restrict__ d_o, const float* __restrict__ beta,
     const int32_t* __restrict__ cu, int N, int T_tot, int H, int maxnch, float scale,
@@ -419,10 +438,12 @@ __global__ void __launch_bounds__(NT) bwd_grad_kernel(
     const float* __restrict__ dSrec, float* __restrict__ scr, float* __restrict__ dq,
     float* __restrict__ dk, float* __restrict__ dv, float* __restrict__ dg,
     float* __restrict__ dbeta) {
-  __shared__ float sT[C][C + 1], sDA[C][C + 1], sDP[C][C + 1];
-  __shared__ float sB[C], sDB[C], sPart[D];
-  // the products' LDS slabs, then (pairwise phase) K, Q and gamma of the chunk
-  __shared__ float sU[3 * C * D];
+  __shared__ float sT[C][C + 1], sDP[C][C + 1];
+  __shared__ float sB[C], sDB[C], sGC[D];
+  // the products' LDS slabs, then (pairwise phase) K, Q and gamma of a
+  // quarter of the channels and the per-row-group partial sums
+  constexpr int QC = D / 4;
+  __shared__ float sU[3 * C * QC + 8 * QC];
   float* sa = sU;
   float* sb = sU + SA_FLOATS;
   ChunkPos p;
@@ -537,6 +558,7 @@ __global__ void __launch_bounds__(NT) bwd_grad_kernel(
       }
   }
   __syncthreads();
+  float* dMMt = sc + Scr::DKE;  // [C][C], until dK_E is written
   {  // dM M^T
     float a4[4][4];
     zero(a4);
@@ -545,7 +567,7 @@ __global__ void __launch_bounds__(NT) bwd_grad_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) sDA[16 * i + tr][16 * j + tc] = a4[i][j];
+      for (int j = 0; j < 4; ++j) dMMt[(16 * i + tr) * C + 16 * j + tc] = a4[i][j];
   }
   __syncthreads();
   {  // dA = -M^T (dM M^T) on s < r
@@ -553,7 +575,7 @@ __global__ void __launch_bounds__(NT) bwd_grad_kernel(
     zero(a4);
     gemm_staged<4, 4, false, true>(a4, C, sa, sb,
                                    [&](int r, int u) { return im[Rec::M + u * C + r]; },
-                                   [&](int u, int s) { return sDA[u][s]; });
+                                   [&](int u, int s) { return dMMt[u * C + s]; });
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -602,62 +624,53 @@ __global__ void __launch_bounds__(NT) bwd_grad_kernel(
     float d = 0.0f;
 #pragma unroll 16
     for (int j = 64 * half; j < 64 * half + 64; ++j) d = fmaf(dS[cc * D + j], S[cc * D + j], d);
-    sPart[cc] = 0.0f;
+    if (half == 1) sU[cc] = d;
     __syncthreads();
-    if (half == 1) sPart[cc] = d;
+    if (half == 0) sGC[cc] = (d + sU[cc]) * __expf(Gf(C - 1, cc));
     __syncthreads();
-    if (half == 0) sPart[cc] += d;
   }
-  // The chunk's K, Q and gamma into LDS for the pairwise terms
-  float* sK = sU;
-  float* sQ = sU + C * D;
-  float* sG = sU + 2 * C * D;
-  for (int e = t; e < C * D; e += NT) {
-    const int r = e / D, cc = e % D;
-    sK[e] = Kf(r, cc);
-    sQ[e] = Qf(r, cc);
-    sG[e] = Gf(r, cc);
-  }
-  __syncthreads();
-  // Thread (channel cc, parity par) finishes the rows x = par, par + 2, ...:
+  // The pairwise terms, a quarter of the channels at a time: thread (channel
+  // cc of the quarter, row group grp) finishes the rows x = grp, grp + 8, ...:
   // the decay-factor terms of K_E, Q_E, K_D, then the pairwise terms of At
   // and P with x as the later token (s <= x) and as the earlier one (r >= x).
-  {
-    const int cc = t & (D - 1), par = t >> 7;
-    const float gC = sG[(C - 1) * D + cc];
-    const float dEC = sPart[cc];
-    float dgC = 0.0f;
-    float nke = 0.0f, nqe = 0.0f, nkd = 0.0f;  // the next row's terms, read ahead
-    if (par < Lc) {
-      nke = sc[Scr::DKE + par * D + cc];
-      nqe = sc[Scr::DQE + par * D + cc];
-      nkd = sc[Scr::DKD + par * D + cc];
+  float* sK = sU;
+  float* sQ = sU + C * QC;
+  float* sG = sU + 2 * C * QC;
+  float* sPart = sU + 3 * C * QC;  // [8][QC]
+  const int cl = t & (QC - 1), grp = t >> 5;
+  for (int quarter = 0; quarter < 4; ++quarter) {
+    const int c0 = quarter * QC;
+    for (int e = t; e < C * QC; e += NT) {
+      const int r = e / QC, ch = c0 + e % QC;
+      sK[e] = Kf(r, ch);
+      sQ[e] = Qf(r, ch);
+      sG[e] = Gf(r, ch);
     }
-    for (int x = par; x < Lc; x += 2) {
-      const float kx = sK[x * D + cc], qx = sQ[x * D + cc], gx = sG[x * D + cc], bx = sB[x];
+    __syncthreads();
+    const int cc = c0 + cl;
+    const float gC = sG[(C - 1) * QC + cl];
+    float dgC = 0.0f;
+    for (int x = grp; x < Lc; x += 8) {
+      const float kx = sK[x * QC + cl], qx = sQ[x * QC + cl], gx = sG[x * QC + cl], bx = sB[x];
       const float E = __expf(gx), F = __expf(gC - gx);
-      const float dke = nke, dqe = nqe, dkd = nkd;
-      if (x + 2 < Lc) {
-        nke = sc[Scr::DKE + (x + 2) * D + cc];
-        nqe = sc[Scr::DQE + (x + 2) * D + cc];
-        nkd = sc[Scr::DKD + (x + 2) * D + cc];
-      }
+      const float dke = sc[Scr::DKE + x * D + cc], dqe = sc[Scr::DQE + x * D + cc];
+      const float dkd = sc[Scr::DKD + x * D + cc];
       float dkx = dke * E + dkd * F;
       float dgx = (dke * kx + dqe * qx) * E - dkd * kx * F;
       float dqx = dqe * E;
       dgC = fmaf(dkd * kx, F, dgC);
-      for (int s = 0; s <= x; ++s) {  // x later: pairs (x, s)
-        const float u = __expf(gx - sG[s * D + cc]) * sK[s * D + cc];
-        const float al = s < x ? sT[x][s] * bx : 0.0f;
-        const float pi = sDP[x][s];
+      for (int s2 = 0; s2 <= x; ++s2) {  // x later: pairs (x, s)
+        const float u = __expf(gx - sG[s2 * QC + cl]) * sK[s2 * QC + cl];
+        const float al = s2 < x ? sT[x][s2] * bx : 0.0f;
+        const float pi = sDP[x][s2];
         dkx = fmaf(al, u, dkx);
         dqx = fmaf(pi, u, dqx);
         dgx = fmaf(al * kx + pi * qx, u, dgx);
       }
       for (int r = x; r < Lc; ++r) {  // x earlier: pairs (r, x)
-        const float w = __expf(sG[r * D + cc] - gx);
+        const float w = __expf(sG[r * QC + cl] - gx);
         const float al = x < r ? sT[r][x] * sB[r] : 0.0f;
-        const float phi = al * sK[r * D + cc] + sDP[r][x] * sQ[r * D + cc];
+        const float phi = al * sK[r * QC + cl] + sDP[r][x] * sQ[r * QC + cl];
         dkx = fmaf(phi, w, dkx);
         dgx = fmaf(-phi * w, kx, dgx);
       }
@@ -665,19 +678,26 @@ __global__ void __launch_bounds__(NT) bwd_grad_kernel(
       dk[tok(x, cc)] = dkx;
       sc[Scr::DX + x * D + cc] = dgx;  // dgamma, summed below
     }
-    __syncthreads();  // sPart (d e^gamma_C) read above by every thread
-    if (par == 1) sPart[cc] = dgC;
+    sPart[grp * QC + cl] = dgC;
     __syncthreads();
-    if (par == 0) {
-      float dgam[C];
+    if (t < QC) {
+      float a = 0.0f;
 #pragma unroll
-      for (int x = 0; x < C; ++x) dgam[x] = x < Lc ? sc[Scr::DX + x * D + cc] : 0.0f;
-      float run = dgC + sPart[cc] + dEC * __expf(gC);
+      for (int g2 = 0; g2 < 8; ++g2) a += sPart[g2 * QC + t];
+      sGC[c0 + t] += a;
+    }
+    __syncthreads();  // sK / sQ / sG / sPart are refilled for the next quarter
+  }
+  if (t < D) {  // dg: reverse cumulative sum of dgamma, plus the gamma_C terms
+    const int cc = t;
+    float dgam[C];
 #pragma unroll
-      for (int x = C - 1; x >= 0; --x) {
-        run += dgam[x];
-        if (x < Lc) dg[tok(x, cc)] = run;
-      }
+    for (int x = 0; x < C; ++x) dgam[x] = x < Lc ? sc[Scr::DX + x * D + cc] : 0.0f;
+    float run = sGC[cc];
+#pragma unroll
+    for (int x = C - 1; x >= 0; --x) {
+      run += dgam[x];
+      if (x < Lc) dg[tok(x, cc)] = run;
     }
   }
   if (t < Lc) dbeta[(p.t0 + t) * H + p.h] = sDB[t];
