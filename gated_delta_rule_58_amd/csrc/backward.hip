@@ -308,26 +308,24 @@ __global__ void __launch_bounds__(NT, 2) bwd_prep_kernel(const void* __restrict_
   if (t < D) im[Rec::EC + t] = __expf(Gf(C - 1, t));
 }
 
-// One (sequence, head, 64-column tile): thread t holds rows 8 (t / 16) .. +7
-// and tile columns 4 (t % 16) .. +3 of the 128 x 64 carried matrix R.
-// FWD: R = S from the initial state; rec[chunk] = R at the chunk's entry.
-// Backward: R = dS from dS_final; rec[chunk] = R at the chunk's end; R_end
+// Both chunk walks in one launch: block b < nb walks forward (when both run),
+// the others backward; one (sequence, head, 64-column tile) each.  Thread t
+// holds R[16 i + t / 16][16 j + t % 16] of the tile, i < 8, j < 4.
+// Forward: R = S from the initial state; rec_f[chunk] = R at the chunk's entry.
+// Backward: R = dS from dS_final; rec_b[chunk] = R at the chunk's end; dS0
 // gets the gradient of the initial state.
-template <bool FWD, bool DOB>
-__global__ void __launch_bounds__(NT) bwd_walk_kernel(const float* __restrict__ img,
-                                                      const void* __restrict__ d_o,
-                                                      const int32_t* __restrict__ cu, int N,
-                                                      int T_tot, int H,
-                                                      const float* __restrict__ R_init,
-                                                      float* __restrict__ R_end,
-                                                      float* __restrict__ rec) {
-  // the chunk's matrices (A1 and A2, then A3 in A1's place), its 64-column
-  // slice of B, the carried matrix and Z
-  __shared__ __attribute__((aligned(16))) float sM1[C * D];
-  __shared__ __attribute__((aligned(16))) float sM2[C * D];
-  __shared__ __attribute__((aligned(16))) float sBt[C][64 + 4];
+template <bool DOB>
+__global__ void __launch_bounds__(NT, 2) bwd_walk_kernel(
+    const float* __restrict__ img, const void* __restrict__ d_o,
+    const int32_t* __restrict__ cu, int N, int T_tot, int H, int both,
+    const float* __restrict__ S0, float* __restrict__ rec_f, const float* __restrict__ dSf,
+    float* __restrict__ dS0, float* __restrict__ rec_b) {
   __shared__ float sR[D][64 + 1], sZ[C][64 + 1];
-  const int64_t b = blockIdx.x;
+  __shared__ float sS[SA_FLOATS + SB_FLOATS];
+  const int64_t nb = (int64_t)N * H * 2;
+  int64_t b = blockIdx.x;
+  const bool fwd = both && b < nb;
+  if (both && !fwd) b -= nb;
   const int tile = static_cast<int>(b & 1);
   const int h = static_cast<int>((b >> 1) % H);
   const int n = static_cast<int>((b >> 1) / H);
@@ -338,94 +336,72 @@ __global__ void __launch_bounds__(NT) bwd_walk_kernel(const float* __restrict__ 
   const int64_t L = eos - bos;
   const int nch = static_cast<int>((L + C - 1) / C);
   const int t = threadIdx.x;
-  const int rg = t >> 4, cg = t & 15;
-  const int row0 = 8 * rg, col0 = 4 * cg;  // col0 within the tile
-  const int jg0 = 64 * tile + col0;        // global value column
+  const int tr = t >> 4, tc = t & 15;
   const int64_t HD = (int64_t)H * D;
-  const int64_t sbase = ((int64_t)n * H + h) * D * D;
+  const int64_t sbase = ((int64_t)n * H + h) * D * D + 64 * tile;
+  const float* R_init = fwd ? S0 : dSf;
+  float* rec = fwd ? rec_f : rec_b;
   float R[8][4];
 #pragma unroll
-  for (int a = 0; a < 8; ++a)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      R[a][e] = R_init ? R_init[sbase + (int64_t)(row0 + a) * D + jg0 + e] : 0.0f;
-  const int tr = t >> 4, tc = t & 15;
-  auto copy_mat = [&](float* dst, const float* src) {
-    for (int e = 4 * t; e < C * D; e += 4 * NT)
-      *reinterpret_cast<f32x4*>(dst + e) = *reinterpret_cast<const f32x4*>(src + e);
-  };
+    for (int j = 0; j < 4; ++j)
+      R[i][j] = R_init ? R_init[sbase + (int64_t)(16 * i + tr) * D + 16 * j + tc] : 0.0f;
   for (int it = 0; it < nch; ++it) {
-    const int c = FWD ? it : nch - 1 - it;
+    const int c = fwd ? it : nch - 1 - it;
     const int64_t pair = (bos / C + n + c) * H + h;
     const float* im = img + pair * Rec::floats;
     const int Lc = static_cast<int>(L - (int64_t)c * C < C ? L - (int64_t)c * C : C);
     const int64_t t0 = bos + (int64_t)c * C;
-    float* rc = rec + pair * (int64_t)(D * D);
-    copy_mat(sM1, im + (FWD ? Rec::W : Rec::KD));
-    copy_mat(sM2, im + (FWD ? Rec::KD : Rec::W));
-    for (int e = t; e < C * 16; e += NT) {  // B tile: 64 rows x 16 float4
-      const int r = e >> 4, q4 = (e & 15) * 4;
-      f32x4 bv;
-      if (FWD) {
-        bv = *reinterpret_cast<const f32x4*>(im + Rec::U + r * D + 64 * tile + q4);
-      } else {
-        bv = (d_o && r < Lc) ? load4(d_o, (t0 + r) * HD + (int64_t)h * D + 64 * tile + q4, DOB)
-                             : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-      }
+    float* rc = rec + pair * (int64_t)(D * D) + 64 * tile;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) sBt[r][q4 + u] = bv[u];
-    }
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int a = 0; a < 8; ++a)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        rc[(row0 + a) * D + jg0 + e] = R[a][e];
-        sR[row0 + a][col0 + e] = R[a][e];
+      for (int j = 0; j < 4; ++j) {
+        rc[(16 * i + tr) * D + 16 * j + tc] = R[i][j];
+        sR[16 * i + tr][16 * j + tc] = R[i][j];
       }
     __syncthreads();
     {  // Z = A1 R, A1 = W (forward) or K_D (backward)
+      const float* A1 = im + (fwd ? Rec::W : Rec::KD);
       float z[4][4];
       zero(z);
-      gemm_acc(z, D, [&](int r, int cc) { return sM1[r * D + cc]; },
-               [&](int cc, int j) { return sR[cc][j]; });
+      gemm_staged<4, 4, true, true>(z, D, sS, sS + KT * (64 + 1),
+                                    [&](int r, int cc) { return A1[r * D + cc]; },
+                                    [&](int cc, int j) { return sR[cc][j]; });
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) sZ[16 * i + tr][16 * j + tc] = z[i][j];
     }
     __syncthreads();
-    if (!FWD) copy_mat(sM1, im + Rec::QT);  // A3 (A1 = K_D is done)
-    __syncthreads();
-    // R <- e^gamma_C R - A2^T Z + A3^T B, A2 = K_D / W, A3 = K_D / Qt
-    const float* A3 = FWD ? sM2 : sM1;
+    // R <- e^gamma_C R + [A2; A3]^T [-Z; B]: A2 = K_D / W, A3 = K_D / Qt,
+    // B = U (forward) or the d_o tile (backward)
 #pragma unroll
-    for (int a = 0; a < 8; ++a) {
-      const float ec = im[Rec::EC + row0 + a];
+    for (int i = 0; i < 8; ++i) {
+      const float ec = im[Rec::EC + 16 * i + tr];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) R[a][e] *= ec;
+      for (int j = 0; j < 4; ++j) R[i][j] *= ec;
     }
-#pragma unroll 2
-    for (int r = 0; r < C; ++r) {
-      const f32x4 z4 = f32x4{sZ[r][col0], sZ[r][col0 + 1], sZ[r][col0 + 2], sZ[r][col0 + 3]};
-      const f32x4 b4 = *reinterpret_cast<const f32x4*>(&sBt[r][col0]);
-      const f32x4 a2a = *reinterpret_cast<const f32x4*>(sM2 + r * D + row0);
-      const f32x4 a2b = *reinterpret_cast<const f32x4*>(sM2 + r * D + row0 + 4);
-      const f32x4 a3a = *reinterpret_cast<const f32x4*>(A3 + r * D + row0);
-      const f32x4 a3b = *reinterpret_cast<const f32x4*>(A3 + r * D + row0 + 4);
-#pragma unroll
-      for (int a = 0; a < 8; ++a) {
-        const float a2 = a < 4 ? a2a[a] : a2b[a - 4], a3 = a < 4 ? a3a[a] : a3b[a - 4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) R[a][e] = fmaf(a3, b4[e], fmaf(-a2, z4[e], R[a][e]));
-      }
-    }
-    __syncthreads();  // the LDS buffers are refilled by the next chunk
+    const float* A2 = im + (fwd ? Rec::KD : Rec::W);
+    const float* A3 = im + (fwd ? Rec::KD : Rec::QT);
+    gemm_staged<8, 4, false, true>(
+        R, 2 * C, sS, sS + KT * (128 + 1),
+        [&](int cr, int kk) { return kk < C ? A2[kk * D + cr] : A3[(kk - C) * D + cr]; },
+        [&](int kk, int j) {
+          if (kk < C) return -sZ[kk][j];
+          const int r = kk - C;
+          if (fwd) return im[Rec::U + r * D + 64 * tile + j];
+          return (d_o && r < Lc) ? load1(d_o, (t0 + r) * HD + (int64_t)h * D + 64 * tile + j, DOB)
+                                 : 0.0f;
+        });
   }
+  float* R_end = fwd ? nullptr : dS0;
   if (R_end) {
 #pragma unroll
-    for (int a = 0; a < 8; ++a)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) R_end[sbase + (int64_t)(row0 + a) * D + jg0 + e] = R[a][e];
+      for (int j = 0; j < 4; ++j) R_end[sbase + (int64_t)(16 * i + tr) * D + 16 * j + tc] = R[i][j];
   }
 }
 
@@ -731,7 +707,7 @@ hipError_t launch(const void* q, const void* k, const void* v, bool qkv_bf16, co
   const int T = static_cast<int>(T_tot);
   const int64_t chunk_blocks = (int64_t)N * maxnch * H;
   const int64_t walk_blocks = (int64_t)N * H * 2;
-  if (chunk_blocks > 0x7fffffff || walk_blocks > 0x7fffffff) return hipErrorInvalidValue;
+  if (chunk_blocks > 0x7fffffff || 2 * walk_blocks > 0x7fffffff) return hipErrorInvalidValue;
   if (chunk_blocks > 0) {
     if (qkv_bf16)
       bwd_prep_kernel<true><<<dim3((unsigned)chunk_blocks), NT, 0, s>>>(
@@ -739,15 +715,17 @@ hipError_t launch(const void* q, const void* k, const void* v, bool qkv_bf16, co
     else
       bwd_prep_kernel<false><<<dim3((unsigned)chunk_blocks), NT, 0, s>>>(
           q, k, v, g, beta, cu, N, T, H, (int)maxnch, scale, img);
-    bwd_walk_kernel<true, false><<<dim3((unsigned)walk_blocks), NT, 0, s>>>(
-        img, nullptr, cu, N, T, H, S0, nullptr, Srec);
   }
-  if (do_bf16)
-    bwd_walk_kernel<false, true><<<dim3((unsigned)walk_blocks), NT, 0, s>>>(
-        img, d_o, cu, N, T, H, dS_final, dS0, dSrec);
-  else
-    bwd_walk_kernel<false, false><<<dim3((unsigned)walk_blocks), NT, 0, s>>>(
-        img, d_o, cu, N, T, H, dS_final, dS0, dSrec);
+  {  // the forward and backward walks together (backward only when no chunk exists)
+    const int both = chunk_blocks > 0 ? 1 : 0;
+    const dim3 grid((unsigned)(walk_blocks * (both ? 2 : 1)));
+    if (do_bf16)
+      bwd_walk_kernel<true><<<grid, NT, 0, s>>>(img, d_o, cu, N, T, H, both, S0, Srec, dS_final,
+                                                dS0, dSrec);
+    else
+      bwd_walk_kernel<false><<<grid, NT, 0, s>>>(img, d_o, cu, N, T, H, both, S0, Srec,
+                                                 dS_final, dS0, dSrec);
+  }
   if (chunk_blocks > 0) {
 #define KDA_BG(QB, OB)                                                                        \
   bwd_grad_kernel<QB, OB><<<dim3((unsigned)chunk_blocks), NT, 0, s>>>(                        \
