@@ -6,7 +6,7 @@ table or helper with the HIP path.
 
 * `gate`, `prefill`, `decode` call the plain C recurrence in kda_oracle.c
   (token by token, fp64); `prefill_backward` is its reverse-mode gradient,
-  step by step through the same recurrence.
+  step by step through the same recurrence, and `gate_backward` the gate's.
 * `chunked.prefill_chunked` is an independent fp64 chunked form used only to
   pin the recurrence (the two must agree for every chunk size).
 * `prologue.shortconv_l2norm` is the layer's prologue (short causal conv,
@@ -17,6 +17,6 @@ force, the audit page's printed exp(A_log) statistics; the backward against
 central differences, torch autograd and a closed form); none is "parity
 unpinned".
 """
-from .api import (gate, prefill, prefill_backward, decode, build_oracle,  # noqa: F401
-                  oracle_lib_path)
+from .api import (gate, gate_backward, prefill, prefill_backward, decode,  # noqa: F401
+                  build_oracle, oracle_lib_path)
 from .prologue import shortconv_l2norm  # noqa: F401

@@ -40,6 +40,10 @@ def _lib():
         lib.kdao_gate.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _dp, _dp, _dp,
                                   ctypes.c_int32, _dp, _dp, _dp]
         lib.kdao_gate.restype = None
+        lib.kdao_gate_backward.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _dp,
+                                           _dp, _dp, ctypes.c_int32, _dp, _dp, _dp, _dp, _dp,
+                                           _dp, _dp]
+        lib.kdao_gate_backward.restype = None
         lib.kdao_prefill_backward.argtypes = [ctypes.c_int32, _ip, ctypes.c_int32, ctypes.c_int32,
                                               ctypes.c_int32, _dp, _dp, _dp, _dp, _dp,
                                               ctypes.c_double, _dp, _dp, _dp, _dp, _dp, _dp,
@@ -87,6 +91,25 @@ def gate(x, b, A_log, dt_bias):
     _lib().kdao_gate(T, H, d, _p(x), _p(b), _p(A_log), int(A_log.ndim == 2), _p(dt_bias), _p(g),
                      _p(beta))
     return g, beta
+
+
+def gate_backward(x, b, A_log, dt_bias, dg, dbeta):
+    """Gradient of gate() against dg [T,H,d] and dbeta [T,H], fp64.
+
+    Returns (dx [T,H,d], db [T,H], dA_log (A_log's shape), ddt_bias [H,d])."""
+    x, b, A_log, dt_bias = f64(x), f64(b), f64(A_log), f64(dt_bias)
+    dg, dbeta = f64(dg), f64(dbeta)
+    T, H, d = x.shape
+    if A_log.shape not in ((H,), (H, d)) or b.shape != (T, H) or dt_bias.size != H * d \
+            or dg.shape != (T, H, d) or dbeta.shape != (T, H):
+        raise ValueError("gate_backward: shape mismatch")
+    dx = np.empty_like(x)
+    db = np.empty_like(b)
+    dA = np.empty_like(A_log)
+    ddt = np.empty((H, d))
+    _lib().kdao_gate_backward(T, H, d, _p(x), _p(b), _p(A_log), int(A_log.ndim == 2),
+                              _p(dt_bias), _p(dg), _p(dbeta), _p(dx), _p(db), _p(dA), _p(ddt))
+    return dx, db, dA, ddt
 
 
 def prefill(q, k, v, g, beta, cu_seqlens, initial_state=None, scale=1.0, nthreads=0,

@@ -59,6 +59,39 @@ void kdao_gate(int64_t n_tok, int32_t H, int32_t d, const double* x, const doubl
   }
 }
 
+/*
+ * Gradient of kdao_gate.  With z = x + dt_bias, a = exp(A_log) (per head or
+ * per (head, channel)) and g = -a softplus(z), beta = sigmoid(b):
+ *   dx = dg * (-a sigmoid(z)),  ddt_bias[h,c] = sum_t dx[t,h,c],
+ *   dA_log = sum of dg * g over the entries that share the parameter,
+ *   db = dbeta * beta (1 - beta).
+ * dA_log has A_log's shape; ddt_bias is [H, d].
+ */
+void kdao_gate_backward(int64_t n_tok, int32_t H, int32_t d, const double* x, const double* b,
+                        const double* A_log, int32_t a_per_channel, const double* dt_bias,
+                        const double* dg, const double* dbeta, double* dx, double* db,
+                        double* dA_log, double* ddt_bias) {
+  memset(dA_log, 0, sizeof(double) * (size_t)(a_per_channel ? (int64_t)H * d : H));
+  memset(ddt_bias, 0, sizeof(double) * (size_t)((int64_t)H * d));
+  for (int64_t t = 0; t < n_tok; ++t) {
+    for (int32_t h = 0; h < H; ++h) {
+      for (int32_t c = 0; c < d; ++c) {
+        const int64_t i = (t * H + h) * (int64_t)d + c;
+        const int64_t ai = a_per_channel ? (int64_t)h * d + c : h;
+        const double a = exp(A_log[ai]);
+        const double z = x[i] + dt_bias[(int64_t)h * d + c];
+        const double sig = 1.0 / (1.0 + exp(-z));
+        const double g = -a * softplus(z);
+        dx[i] = dg[i] * (-a * sig);
+        ddt_bias[(int64_t)h * d + c] += dx[i];
+        dA_log[ai] += dg[i] * g;
+      }
+      const double be = 1.0 / (1.0 + exp(-b[t * H + h]));
+      db[t * H + h] = dbeta[t * H + h] * be * (1.0 - be);
+    }
+  }
+}
+
 /* One step of the recurrence on S (dk x dv) for one token of one head. */
 static void step(int32_t dk, int32_t dv, double* S, double* e, const double* q,
                  const double* k, const double* v, const double* g, double beta,

@@ -119,3 +119,51 @@ def test_backward_constant_state_closed_form():
         assert np.allclose(dg[t], np.sum(D * S, axis=2), atol=1e-12)
     assert np.allclose(dS0[0], D, atol=1e-12)
     assert np.all(dkk == 0) and np.all(dvv == 0)
+
+
+@pytest.mark.parametrize("per_channel", [False, True])
+def test_gate_backward_matches_central_differences(per_channel):
+    """oracle.gate_backward against central differences of oracle.gate for
+    the loss sum(dg * g) + sum(dbeta * beta), every element of x, b, A_log
+    (per head or per channel) and dt_bias."""
+    r = np.random.default_rng(21)
+    T, H, d = 3, 2, 3
+    x = r.standard_normal((T, H, d)) * 3
+    b = r.standard_normal((T, H)) * 2
+    A = r.uniform(-0.75, 1.0, (H, d) if per_channel else (H,))
+    dt = r.normal(-1.0, 1.0, (H, d))
+    dg = r.standard_normal((T, H, d))
+    dbeta = r.standard_normal((T, H))
+    got = oracle.gate_backward(x, b, A, dt, dg, dbeta)
+
+    def loss(xx, bb, AA, dd):
+        g, be = oracle.gate(xx, bb, AA, dd)
+        return float(np.sum(g * dg) + np.sum(be * dbeta))
+    ins = [x, b, A, dt]
+    h = 1e-6
+    for i, name in enumerate(["x", "b", "A_log", "dt_bias"]):
+        num = np.zeros_like(ins[i])
+        for idx in np.ndindex(ins[i].shape):
+            plus = [a.copy() for a in ins]
+            minus = [a.copy() for a in ins]
+            plus[i][idx] += h
+            minus[i][idx] -= h
+            num[idx] = (loss(*plus) - loss(*minus)) / (2 * h)
+        err = np.max(np.abs(got[i] - num)) / max(1.0, np.max(np.abs(num)))
+        assert err < 1e-7, (name, err)
+
+
+def test_gate_backward_closed_form_at_zero():
+    """x + dt_bias = 0 and b = 0: sigmoid = 1/2, so dx = -exp(A_log) dg / 2,
+    db = dbeta / 4 and dA_log = -ln 2 exp(A_log) sum(dg)."""
+    T, H, d = 4, 3, 2
+    A = np.array([0.0, 0.5, -0.75])
+    dt = np.arange(H * d, dtype=np.float64).reshape(H, d) * 0.3 - 0.5
+    x = np.broadcast_to(-dt, (T, H, d)).copy()
+    dg = np.random.default_rng(4).standard_normal((T, H, d))
+    dbeta = np.random.default_rng(5).standard_normal((T, H))
+    dx, db, dA, ddt = oracle.gate_backward(x, np.zeros((T, H)), A, dt, dg, dbeta)
+    assert np.allclose(dx, -np.exp(A)[None, :, None] * dg / 2, atol=1e-15)
+    assert np.allclose(db, dbeta / 4, atol=1e-15)
+    assert np.allclose(dA, -np.log(2.0) * np.exp(A) * dg.sum(axis=(0, 2)), atol=1e-13)
+    assert np.allclose(ddt, dx.sum(axis=0), atol=1e-14)
