@@ -13,6 +13,7 @@ from .binding import (  # noqa: F401
     lib,
     lib_path,
     gate,
+    gate_backward,
     chunk_prefill,
     chunk_prefill_gated,
     chunk_prefill_workspace_bytes,

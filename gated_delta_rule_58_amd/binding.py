@@ -73,6 +73,12 @@ def lib():
         L.kda_shortconv_l2norm.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _i64,
                                            _i32, ctypes.c_float, _vp, _vp, _i32, _vp, _vp, _vp,
                                            _vp, _vp, ctypes.c_int, _i64, _i32, _i32, _vp]
+        L.kda_gate_backward.restype = ctypes.c_int
+        L.kda_gate_backward.argtypes = [_vp, ctypes.c_int, _vp, ctypes.c_int, _vp, _i64, _vp,
+                                        _i64, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32,
+                                        _vp, ctypes.c_size_t, _vp]
+        L.kda_gate_backward_workspace_bytes.restype = ctypes.c_size_t
+        L.kda_gate_backward_workspace_bytes.argtypes = [_i64, _i32, _i32]
         L.kda_chunk_prefill_backward.restype = ctypes.c_int
         L.kda_chunk_prefill_backward.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _vp,
                                                  _i32, _vp, _vp, ctypes.c_int, _vp, _vp, _vp,
@@ -92,7 +98,8 @@ def exported_symbols():
     return ["kda_last_error", "kda_version", "kda_gate", "kda_chunk_prefill",
             "kda_chunk_prefill_gated", "kda_chunk_prefill_workspace_bytes", "kda_recurrent_decode",
             "kda_recurrent_decode_gated", "kda_shortconv_l2norm", "kda_chunk_prefill_backward",
-            "kda_chunk_prefill_backward_workspace_bytes"]
+            "kda_chunk_prefill_backward_workspace_bytes", "kda_gate_backward",
+            "kda_gate_backward_workspace_bytes"]
 
 
 def _check(status: int):
@@ -233,6 +240,29 @@ def chunk_prefill_gated(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, x: to
         _dt(out), T, H, dk, dv, float(scale), _ptr(workspace), workspace.numel(), _stream(dev))
     _check(st)
     return out, final_state
+
+
+def gate_backward(x: torch.Tensor, b: torch.Tensor, A_log: torch.Tensor, dt_bias: torch.Tensor,
+                  dg: torch.Tensor, dbeta: torch.Tensor):
+    """kda_gate_backward: gradients of gate() against dg [T,H,d] and dbeta [T,H].
+
+    Returns (dx [T,H,d], db [T,H], dA_log (A_log's shape), ddt_bias [H,d]), float32."""
+    T, H, d = x.shape
+    A_log = _alog(A_log, H, d)
+    dev = x.device
+    f32 = dict(dtype=torch.float32, device=dev)
+    dx = torch.empty((T, H, d), **f32)
+    db = torch.empty((T, H), **f32)
+    dA = torch.empty(tuple(A_log.shape), **f32)
+    ddt = torch.empty((H, d), **f32)
+    nbytes = int(lib().kda_gate_backward_workspace_bytes(T, H, d))
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    st = lib().kda_gate_backward(_ptr(x), _dt(x), _ptr(b), _dt(b), _ptr(A_log), A_log.numel(),
+                                 _ptr(dt_bias.contiguous()), dt_bias.numel(), _ptr(dg),
+                                 _ptr(dbeta), _ptr(dx), _ptr(db), _ptr(dA), _ptr(ddt), T, H, d,
+                                 _ptr(ws), ws.numel(), _stream(dev))
+    _check(st)
+    return dx, db, dA, ddt
 
 
 def chunk_prefill_backward_workspace_bytes(T_tot: int, N: int, H: int, dk: int = 128,

@@ -88,6 +88,57 @@ kda_status kda_gate(const void* x, kda_dtype x_dt, const void* b, kda_dtype b_dt
                   "kda_gate");
 }
 
+size_t kda_gate_backward_workspace_bytes(int64_t n_tok, int32_t H, int32_t d) {
+  if (n_tok < 0 || H <= 0 || d <= 0) return 0;
+  return kda::gate_bwd_workspace_bytes(n_tok, H, d);
+}
+
+kda_status kda_gate_backward(const void* x, kda_dtype x_dt, const void* b, kda_dtype b_dt,
+                             const float* A_log, int64_t A_log_len, const float* dt_bias,
+                             int64_t dt_bias_len, const float* dg, const float* dbeta, float* dx,
+                             float* db, float* dA_log, float* ddt_bias, int64_t n_tok,
+                             int32_t H, int32_t d, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  const char* fn = "kda_gate_backward";
+  if (n_tok < 0 || H <= 0 || d <= 0)
+    return fail(KDA_ERR_INVALID_ARG, "%s: need n_tok >= 0, H > 0, d > 0 (got %lld, %d, %d)", fn,
+                (long long)n_tok, H, d);
+  if (!known_dtype(x_dt) || !known_dtype(b_dt))
+    return fail(KDA_ERR_DTYPE, "%s: x_dt and b_dt must be KDA_F32 or KDA_BF16", fn);
+  bool alog_pc = false;
+  if (const kda_status st = check_alog(fn, A_log_len, H, d, &alog_pc)) return st;
+  if (dt_bias_len != (int64_t)H * d)
+    return fail(KDA_ERR_SHAPE, "%s: dt_bias has %lld values, need H*d = %lld", fn,
+                (long long)dt_bias_len, (long long)H * d);
+  if (d % 4 != 0 || d > 1024)
+    return fail(KDA_ERR_UNSUPPORTED, "%s: d must be a multiple of 4 and at most 1024 (got %d)", fn,
+                d);
+  if ((H + 256 / (d / 4) - 1) / (256 / (d / 4)) > 65535 || n_tok > ((int64_t)1 << 31) - 1)
+    return fail(KDA_ERR_UNSUPPORTED, "%s: H = %d or n_tok = %lld is too large", fn, H,
+                (long long)n_tok);
+  if (!A_log || !dt_bias || !dA_log || !ddt_bias)
+    return fail(KDA_ERR_INVALID_ARG, "%s: A_log, dt_bias, dA_log and ddt_bias must be non-NULL",
+                fn);
+  if (n_tok > 0 && (!x || !b || !dg || !dbeta || !dx || !db))
+    return fail(KDA_ERR_INVALID_ARG, "%s: x, b, dg, dbeta, dx and db must be non-NULL", fn);
+  if (!aligned(x, x_dt == KDA_BF16 ? 8 : 16) || !aligned(dg, 16) || !aligned(dx, 16) ||
+      !aligned(dt_bias, 16) || !aligned(A_log, 4) || !aligned(b, b_dt == KDA_BF16 ? 2 : 4) ||
+      !aligned(dbeta, 4) || !aligned(db, 4) || !aligned(dA_log, 4) || !aligned(ddt_bias, 4))
+    return fail(KDA_ERR_ALIGNMENT, "%s: x, dg, dx and dt_bias must be 16-byte aligned (8 for "
+                                   "bf16 x), the rest aligned to their element size", fn);
+  const size_t need = kda::gate_bwd_workspace_bytes(n_tok, H, d);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(KDA_ERR_WORKSPACE, "%s: need a workspace of at least %zu bytes (got %zu)", fn,
+                need, workspace_bytes);
+  if (!aligned(workspace, 16))
+    return fail(KDA_ERR_ALIGNMENT, "%s: workspace must be 16-byte aligned", fn);
+  return launched(kda::launch_gate_backward(x, x_dt == KDA_BF16, b, b_dt == KDA_BF16, A_log,
+                                            alog_pc, dt_bias, dg, dbeta, dx, db, dA_log,
+                                            ddt_bias, n_tok, H, d, workspace,
+                                            static_cast<hipStream_t>(stream)),
+                  fn);
+}
+
 }  // extern "C"
 
 namespace {

@@ -89,7 +89,124 @@ __global__ void __launch_bounds__(kThreads) gate_kernel(
   }
 }
 
+// Gradient of the gate, per token run (same thread layout as gate_kernel):
+//   dx = dg (-exp(A_log) sigmoid(z)),  db = dbeta beta (1 - beta),
+// plus, per thread, the run's partial sums of dx (for dt_bias) and dg g (for
+// A_log) into part[0 / 1][run][h][c]; gate_bwd_reduce adds the runs.
+template <bool XBF16, bool BBF16>
+__global__ void __launch_bounds__(kThreads) gate_bwd_kernel(
+    const void* __restrict__ x, const void* __restrict__ b, const float* __restrict__ A_log,
+    const float* __restrict__ dt_bias, const float* __restrict__ dg,
+    const float* __restrict__ dbeta, float* __restrict__ dx, float* __restrict__ db,
+    float* __restrict__ part, int n_tok, int H, int d, int rows_per_block, int alog_pc) {
+  const int qpr = d >> 2;
+  const int tid = threadIdx.x;
+  const int hh = tid / qpr;
+  const int h = blockIdx.y * rows_per_block + hh;
+  const int c = (tid - hh * qpr) << 2;
+  const int tok0 = blockIdx.x * kTokPerBlock;
+  const int ntk = min(kTokPerBlock, n_tok - tok0);
+  const int64_t tok_stride = (int64_t)H * d;
+  if (hh < rows_per_block && h < H) {
+    f32x4 a;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) a[e] = -expf(alog_pc ? A_log[(int64_t)h * d + c + e] : A_log[h]);
+    const f32x4 dtb = *reinterpret_cast<const f32x4*>(dt_bias + (int64_t)h * d + c);
+    const int64_t base = (int64_t)tok0 * tok_stride + (int64_t)h * d + c;
+    f32x4 sdx = {0.0f, 0.0f, 0.0f, 0.0f}, sda = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int t = 0; t < ntk; ++t) {
+      const int64_t i = base + t * tok_stride;
+      const f32x4 xv = load4(x, i, XBF16);
+      const f32x4 gv = *reinterpret_cast<const f32x4*>(dg + i);
+      f32x4 out;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float z = gate_input(xv[e], dtb[e]);
+        out[e] = gv[e] * (a[e] * gate_beta(z));
+        sdx[e] += out[e];
+        sda[e] = fmaf(gv[e], gate_log_decay(a[e], z), sda[e]);
+      }
+      *reinterpret_cast<f32x4*>(dx + i) = out;
+    }
+    const int64_t pbase = ((int64_t)blockIdx.x * H + h) * d + c;
+    const int64_t half = (int64_t)gridDim.x * H * d;
+    *reinterpret_cast<f32x4*>(part + pbase) = sdx;
+    *reinterpret_cast<f32x4*>(part + half + pbase) = sda;
+  }
+  const int hbase = blockIdx.y * rows_per_block;
+  const int nh = min(rows_per_block, H - hbase);
+  for (int i = tid; i < ntk * nh; i += kThreads) {
+    const int tk = i / nh;
+    const int64_t row = (int64_t)(tok0 + tk) * H + hbase + (i - tk * nh);
+    const float be = gate_beta(load1(b, row, BBF16));
+    db[row] = dbeta[row] * be * (1.0f - be);
+  }
+}
+
+// ddt_bias[h][c] and dA_log (per channel, or summed over the head's
+// channels) from the runs' partial sums; one workgroup per head.
+__global__ void __launch_bounds__(1024) gate_bwd_reduce(const float* __restrict__ part, int nrun,
+                                                        int H, int d, int alog_pc,
+                                                        float* __restrict__ ddt_bias,
+                                                        float* __restrict__ dA_log) {
+  __shared__ float red[32];
+  const int h = blockIdx.x, c = threadIdx.x;
+  const int64_t half = (int64_t)nrun * H * d;
+  float sdt = 0.0f, sda = 0.0f;
+  if (c < d) {
+    for (int r = 0; r < nrun; ++r) {
+      sdt += part[((int64_t)r * H + h) * d + c];
+      sda += part[half + ((int64_t)r * H + h) * d + c];
+    }
+    ddt_bias[(int64_t)h * d + c] = sdt;
+    if (alog_pc) dA_log[(int64_t)h * d + c] = sda;
+  }
+  if (alog_pc) return;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) sda += __shfl_xor(sda, off);
+  if ((c & 63) == 0) red[c >> 6] = sda;
+  __syncthreads();
+  if (c == 0) {
+    float s2 = 0.0f;
+    for (int w = 0; w < (int)((blockDim.x + 63) / 64); ++w) s2 += red[w];
+    dA_log[h] = s2;
+  }
+}
+
 }  // namespace
+
+size_t gate_bwd_workspace_bytes(int64_t n_tok, int H, int d) {
+  return (size_t)2 * (size_t)((n_tok + kTokPerBlock - 1) / kTokPerBlock) * (size_t)H *
+         (size_t)d * sizeof(float);
+}
+
+hipError_t launch_gate_backward(const void* x, bool x_bf16, const void* b, bool b_bf16,
+                                const float* A_log, bool alog_pc, const float* dt_bias,
+                                const float* dg, const float* dbeta, float* dx, float* db,
+                                float* dA_log, float* ddt_bias, int64_t n_tok, int H, int d,
+                                void* ws, hipStream_t s) {
+  const int rows_per_block = kThreads / (d >> 2);
+  const int head_groups = (H + rows_per_block - 1) / rows_per_block;
+  const int64_t nrun = (n_tok + kTokPerBlock - 1) / kTokPerBlock;
+  float* part = static_cast<float*>(ws);
+  if (nrun > 0) {
+    const dim3 grid((unsigned)nrun, head_groups);
+    const int nt = static_cast<int>(n_tok);
+    const int pc = alog_pc ? 1 : 0;
+#define KDA_GB(XB, BB)                                                                        \
+  gate_bwd_kernel<XB, BB><<<grid, kThreads, 0, s>>>(x, b, A_log, dt_bias, dg, dbeta, dx, db, \
+                                                    part, nt, H, d, rows_per_block, pc)
+    if (x_bf16 && b_bf16) KDA_GB(true, true);
+    else if (x_bf16) KDA_GB(true, false);
+    else if (b_bf16) KDA_GB(false, true);
+    else KDA_GB(false, false);
+#undef KDA_GB
+  }
+  const int rthreads = ((d + 63) / 64) * 64;
+  gate_bwd_reduce<<<dim3((unsigned)H), rthreads, 0, s>>>(part, (int)nrun, H, d, alog_pc ? 1 : 0,
+                                                          ddt_bias, dA_log);
+  return hipGetLastError();
+}
 
 hipError_t launch_gate(const void* x, bool x_bf16, const void* b, bool b_bf16, const float* A_log,
                        bool alog_pc, const float* dt_bias, float* g, float* beta, int64_t n_tok,

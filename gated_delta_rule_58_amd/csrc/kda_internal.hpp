@@ -14,6 +14,15 @@ hipError_t launch_gate(const void* x, bool x_bf16, const void* b, bool b_bf16, c
                        bool alog_pc, const float* dt_bias, float* g, float* beta, int64_t n_tok,
                        int H, int d, hipStream_t s);
 
+// Gradient of the gate: dx, db elementwise; dA_log and ddt_bias summed over
+// the tokens through ws (gate_bwd_workspace_bytes) in a fixed order.
+size_t gate_bwd_workspace_bytes(int64_t n_tok, int H, int d);
+hipError_t launch_gate_backward(const void* x, bool x_bf16, const void* b, bool b_bf16,
+                                const float* A_log, bool alog_pc, const float* dt_bias,
+                                const float* dg, const float* dbeta, float* dx, float* db,
+                                float* dA_log, float* ddt_bias, int64_t n_tok, int H, int d,
+                                void* ws, hipStream_t s);
+
 hipError_t launch_decode(const void* q, const void* k, const void* v, bool qkv_bf16,
                          const float* g, const float* beta, float* state, void* o, bool o_bf16,
                          int N, int H, float scale, hipStream_t s);

@@ -95,6 +95,35 @@ kda_status kda_gate(const void* x, kda_dtype x_dt, const void* b, kda_dtype b_dt
                     int32_t H, int32_t d, void* stream);
 
 /*
+ * kda_gate_backward - gradient of kda_gate.
+ *
+ * For the loss sum(dg * g) + sum(dbeta * beta) with g, beta as kda_gate
+ * forms them from the same x, b, A_log and dt_bias (A_log [H] or [H, d]):
+ *   dx[t,h,c]    = dg * (-exp(A_log) sigmoid(x + dt_bias))        fp32 [n_tok, H, d]
+ *   db[t,h]      = dbeta * beta (1 - beta)                        fp32 [n_tok, H]
+ *   ddt_bias[h,c] = sum_t dx[t,h,c]                               fp32 [H, d]
+ *   dA_log       = sum of dg * g over the entries sharing the parameter
+ *                  (A_log's shape: [H] or [H, d])                 fp32
+ * This is the chain rule through the gate of the artifact audit's §4.1 /
+ * §5.2 parameters, so that kda_chunk_prefill_backward's dg and dbeta reach
+ * the gated call's raw inputs.  The token sums go through the workspace
+ * (kda_gate_backward_workspace_bytes: two fp32 partial sums per 32-token run,
+ * head and channel) in a fixed order, so the result is deterministic.
+ * Requires d % 4 == 0, d <= 1024; 16-byte aligned x (8 for bf16), dg, dx,
+ * dt_bias; the rest aligned to their element size.  Refusals as kda_gate,
+ * plus a NULL or short workspace (KDA_ERR_WORKSPACE).
+ */
+kda_status kda_gate_backward(const void* x, kda_dtype x_dt, const void* b, kda_dtype b_dt,
+                             const float* A_log, int64_t A_log_len, const float* dt_bias,
+                             int64_t dt_bias_len, const float* dg, const float* dbeta, float* dx,
+                             float* db, float* dA_log, float* ddt_bias, int64_t n_tok,
+                             int32_t H, int32_t d, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/* Workspace bytes of kda_gate_backward; 0 for invalid arguments. */
+size_t kda_gate_backward_workspace_bytes(int64_t n_tok, int32_t H, int32_t d);
+
+/*
  * kda_chunk_prefill - chunked KDA over a packed variable-length batch.
  *
  * Sequence n owns tokens cu_seqlens[n] .. cu_seqlens[n+1]-1 of the packed

@@ -32,7 +32,8 @@ def test_exports_every_declared_symbol():
                           "kda_chunk_prefill_gated", "kda_chunk_prefill_workspace_bytes",
                           "kda_recurrent_decode", "kda_recurrent_decode_gated",
                           "kda_shortconv_l2norm", "kda_chunk_prefill_backward",
-                          "kda_chunk_prefill_backward_workspace_bytes"}
+                          "kda_chunk_prefill_backward_workspace_bytes", "kda_gate_backward",
+                          "kda_gate_backward_workspace_bytes"}
     for n in names:
         assert hasattr(L, n), n
     assert L.kda_version().decode().startswith("kda-gfx950")
@@ -274,3 +275,30 @@ def test_backward_refusals():
     assert _backward(L, cu, dbeta=DEV[11] + 2) == 5
     assert _backward(L, cu, dk=DEV[8] + 4) == 5
     assert _backward(L, cu, do_dt=7) == 3
+
+
+def test_gate_backward_refusals():
+    """kda_gate_backward refuses before any HIP call."""
+    L = _lib()
+
+    def gb(**kw):
+        a = dict(x=DEV[0], x_dt=0, b=DEV[1], b_dt=0, A=DEV[2], A_len=4, dt=DEV[3],
+                 dt_len=4 * 128, dg=DEV[4], dbeta=DEV[5], dx=DEV[6], db=DEV[7], dA=DEV[8],
+                 ddt=DEV[9], n=40, H=4, d=128, ws=DEV[10], ws_bytes=1 << 30)
+        a.update(kw)
+        return L.kda_gate_backward(a["x"], a["x_dt"], a["b"], a["b_dt"], a["A"], a["A_len"],
+                                   a["dt"], a["dt_len"], a["dg"], a["dbeta"], a["dx"], a["db"],
+                                   a["dA"], a["ddt"], a["n"], a["H"], a["d"], a["ws"],
+                                   a["ws_bytes"], None)
+    need = L.kda_gate_backward_workspace_bytes(40, 4, 128)
+    assert need == 2 * 2 * 4 * 128 * 4
+    assert gb(A_len=128) == 2
+    assert gb(A_len=4 * 128, dx=None) == 1      # [H, d] A_log passes the shape check
+    assert gb(dt_len=4 * 128 - 1) == 2
+    assert gb(x_dt=3) == 3
+    assert gb(d=126, dt_len=4 * 126) == 4
+    assert gb(dA=None) == 1
+    assert gb(dg=DEV[4] + 4) == 5
+    assert gb(ws=None) == 6
+    assert gb(ws_bytes=need - 1) == 6
+    assert b"kda_gate_backward" in L.kda_last_error()

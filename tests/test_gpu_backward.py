@@ -26,9 +26,9 @@ GRAD_TOL = 1e-4
 NAMES = ["dq", "dk", "dv", "dg", "dbeta", "dS0"]
 
 
-def grad_errs(got, ref):
+def grad_errs(got, ref, names=NAMES):
     out = {}
-    for name, a, b in zip(NAMES, got, ref):
+    for name, a, b in zip(names, got, ref):
         if a is None:
             continue
         a, b = to64(a), to64(b)
@@ -123,3 +123,62 @@ def test_backward_config1_sampled_heads():
                                   dr.cu_seqlens, S0, d_o=d_o[:, heads].float())
     sub = [None if a is None else a[:, heads] for a in got]
     check(sub, ref, "config 1 heads %s" % heads)
+
+
+@pytest.mark.parametrize("per_channel,xdt", [(False, torch.float32), (True, torch.bfloat16)])
+def test_gate_backward_parity(per_channel, xdt):
+    """kda_gate_backward against oracle.gate_backward: dx and db elementwise
+    within 1e-5 relative; the token sums ddt_bias and dA_log within 1e-5 of
+    the sum of the absolute values of their terms (fp32 sums of at most a few
+    hundred terms: about 1e-6)."""
+    need_gpu()
+    say("gate backward", per_channel, xdt)
+    from synth import draw_alog_per_channel
+    dr = draw_prefill([300, 0, 77], H=5, dtype=torch.bfloat16, seed=81)
+    A = draw_alog_per_channel(5, seed=81) if per_channel else dr.A_log
+    x, b = dr.x.to(xdt), dr.b.to(xdt)
+    r = torch.Generator().manual_seed(82)
+    dg = torch.randn(x.shape, generator=r)
+    dbeta = torch.randn(b.shape, generator=r)
+    dx, db, dA, ddt = kda.gate_backward(x.to(DEV), b.to(DEV), A.to(DEV), dr.dt_bias.to(DEV),
+                                        dg.to(DEV), dbeta.to(DEV))
+    torch.cuda.synchronize()
+    rdx, rdb, rdA, rddt = oracle.gate_backward(x, b, A, dr.dt_bias, dg, dbeta)
+    assert np.all(np.abs(to64(dx) - rdx) <= 1e-5 * np.abs(rdx) + 1e-30)
+    assert np.all(np.abs(to64(db) - rdb) <= 1e-5 * np.abs(rdb) + 1e-30)
+    assert np.all(np.abs(to64(ddt) - rddt) <= 1e-5 * np.abs(rdx).sum(axis=0) + 1e-30)
+    g_ref, _ = oracle.gate(x, b, A, dr.dt_bias)
+    terms = np.abs(to64(dg) * g_ref)
+    bound = terms.sum(axis=0) if per_channel else terms.sum(axis=(0, 2))
+    assert np.all(np.abs(to64(dA) - rdA) <= 1e-5 * bound + 1e-30)
+
+
+def test_gated_training_path():
+    """The gated prefill's full backward, as a training step would chain it:
+    kda_gate -> kda_chunk_prefill_backward -> kda_gate_backward, against the
+    oracle's gate, recurrence gradient and gate gradient (per-head A_log,
+    varlen, initial state, bf16 d_o)."""
+    need_gpu()
+    say("gated training path")
+    dr = draw_prefill([150, 64, 1], H=3, dtype=torch.bfloat16, init_state=True, seed=83)
+    xd, bd = dr.x.to(DEV), dr.b.to(DEV)
+    Ad, dtd = dr.A_log.to(DEV), dr.dt_bias.to(DEV)
+    g, beta = kda.gate(xd, bd, Ad, dtd)
+    r = torch.Generator().manual_seed(84)
+    d_o = torch.randn(dr.q.shape[0], 3, 128, generator=r).to(torch.bfloat16)
+    cu_h = dr.cu_seqlens
+    dq, dk, dv, dgg, dbeta, dS0 = kda.chunk_prefill_backward(
+        dr.q.to(DEV), dr.k.to(DEV), dr.v.to(DEV), g, beta, d_o.to(DEV), cu_h.to(DEV),
+        dr.initial_state.to(DEV), scale=0.9, cu_seqlens_host=cu_h)
+    dx, db, dA, ddt = kda.gate_backward(xd, bd, Ad, dtd, dgg, dbeta)
+    torch.cuda.synchronize()
+    gr, br = oracle.gate(dr.x, dr.b, dr.A_log, dr.dt_bias)
+    ref = oracle.prefill_backward(dr.q, dr.k, dr.v, gr, br, cu_h, dr.initial_state, scale=0.9,
+                                  d_o=d_o.float())
+    check([dq, dk, dv, dgg, dbeta, dS0], ref, "training path core")
+    rdx, rdb, rdA, rddt = oracle.gate_backward(dr.x, dr.b, dr.A_log, dr.dt_bias, ref[3], ref[4])
+    errs = grad_errs([dx, db, dA.reshape(-1), ddt], [rdx, rdb, rdA.reshape(-1), rddt],
+                     ["dx", "db", "dA_log", "ddt_bias"])
+    say("training path gate", errs)
+    for name, e in errs.items():
+        assert e <= GRAD_TOL, name
