@@ -150,8 +150,7 @@ struct ChunkPos {
   int64_t t0, pair;
 };
 __device__ __forceinline__ bool chunk_of_block(const int32_t* cu, int N, int T_tot, int H,
-                                               int maxnch, ChunkPos& p) {
-  const int64_t b = blockIdx.x;
+                                               int maxnch, ChunkPos& p, int64_t b) {
   p.h = static_cast<int>(b % H);
   const int64_t rest = b / H;
   p.c = static_cast<int>(rest % maxnch);
@@ -182,7 +181,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_prep_kernel(const void* __restrict_
   // slabs of K, Q, gamma (CS channels), later the products' LDS slabs
   __shared__ float sS[3 * C * (CS + 1)];
   ChunkPos p;
-  if (!chunk_of_block(cu, N, T_tot, H, maxnch, p)) return;
+  if (!chunk_of_block(cu, N, T_tot, H, maxnch, p, blockIdx.x)) return;
   const int t = threadIdx.x;
   const int64_t HD = (int64_t)H * D;
   float* im = img + p.pair * Rec::floats;
@@ -413,7 +412,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_grad_kernel(
     const float* __restrict__ img, const float* __restrict__ Srec,
     const float* __restrict__ dSrec, float* __restrict__ scr, float* __restrict__ dq,
     float* __restrict__ dk, float* __restrict__ dv, float* __restrict__ dg,
-    float* __restrict__ dbeta) {
+    float* __restrict__ dbeta, int64_t item0) {
   __shared__ float sT[C][C + 1], sDP[C][C + 1];
   __shared__ float sB[C], sDB[C], sGC[D];
   // the products' LDS slabs, then (pairwise phase) K, Q and gamma of a
@@ -423,14 +422,15 @@ __global__ void __launch_bounds__(NT, 2) bwd_grad_kernel(
   float* sa = sU;
   float* sb = sU + SA_FLOATS;
   ChunkPos p;
-  if (!chunk_of_block(cu, N, T_tot, H, maxnch, p)) return;
+  if (!chunk_of_block(cu, N, T_tot, H, maxnch, p, item0 + blockIdx.x)) return;
   const int t = threadIdx.x;
   const int tr = t >> 4, tc = t & 15;
   const int64_t HD = (int64_t)H * D;
   const float* im = img + p.pair * Rec::floats;
   const float* S = Srec + p.pair * (int64_t)(D * D);
   const float* dS = dSrec + p.pair * (int64_t)(D * D);
-  float* sc = scr + p.pair * Scr::floats;
+  // one scratch slot per workgroup of a launch (a launch has at most GRAD_SLOTS)
+  float* sc = scr + (int64_t)blockIdx.x * Scr::floats;
   const int Lc = p.Lc;
   auto tok = [&](int r, int cc) { return (p.t0 + r) * HD + (int64_t)p.h * D + cc; };
   auto Kf = [&](int r, int cc) { return r < Lc ? load1(k, tok(r, cc), QB) : 0.0f; };
@@ -681,9 +681,15 @@ __global__ void __launch_bounds__(NT, 2) bwd_grad_kernel(
 
 }  // namespace
 
+// The gradient kernel runs in launches of at most GRAD_SLOTS workgroups (two
+// per CU), each with a scratch slot of its own, so the scratch does not grow
+// with the sequence length.
+constexpr int64_t GRAD_SLOTS = 512;
+
 size_t workspace_bytes(int64_t T_tot, int N, int H) {
   const size_t pairs = (size_t)(T_tot / C + N) * (size_t)H;
-  return pairs * (size_t)(Rec::floats + 2 * D * D + Scr::floats) * sizeof(float);
+  return (pairs * (size_t)(Rec::floats + 2 * D * D) + (size_t)GRAD_SLOTS * Scr::floats) *
+         sizeof(float);
 }
 
 hipError_t launch(const void* q, const void* k, const void* v, bool qkv_bf16, const float* g,
@@ -726,11 +732,12 @@ hipError_t launch(const void* q, const void* k, const void* v, bool qkv_bf16, co
       bwd_walk_kernel<false><<<grid, NT, 0, s>>>(img, d_o, cu, N, T, H, both, S0, Srec,
                                                  dS_final, dS0, dSrec);
   }
-  if (chunk_blocks > 0) {
+  for (int64_t item0 = 0; item0 < chunk_blocks; item0 += GRAD_SLOTS) {
+    const int64_t nb = chunk_blocks - item0 < GRAD_SLOTS ? chunk_blocks - item0 : GRAD_SLOTS;
 #define KDA_BG(QB, OB)                                                                        \
-  bwd_grad_kernel<QB, OB><<<dim3((unsigned)chunk_blocks), NT, 0, s>>>(                        \
+  bwd_grad_kernel<QB, OB><<<dim3((unsigned)nb), NT, 0, s>>>(                                  \
       q, k, v, d_o, beta, cu, N, T, H, (int)maxnch, scale, img, Srec, dSrec, scr, dq, dk, dv, \
-      dg, dbeta)
+      dg, dbeta, item0)
     if (qkv_bf16 && do_bf16) KDA_BG(true, true);
     else if (qkv_bf16) KDA_BG(true, false);
     else if (do_bf16) KDA_BG(false, true);

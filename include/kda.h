@@ -220,8 +220,9 @@ kda_status kda_chunk_prefill_gated(const void* q, const void* k, const void* v, 
  * result equals the gradient of the fp64 recurrence up to fp32 rounding.
  * The workspace (kda_chunk_prefill_backward_workspace_bytes) holds per (chunk,
  * head) the chunk's intermediate matrices, the recomputed entry state and the
- * state gradient, 573,952 bytes, for T_tot / 64 + N chunk slots per head; the
- * call never allocates.  Requires dk == dv == 128; refusals as for
+ * state gradient, 344,576 bytes, for T_tot / 64 + N chunk slots per head, plus
+ * 512 scratch slots of 229,376 bytes for the gradient kernel; the call never
+ * allocates.  Requires dk == dv == 128; refusals as for
  * kda_chunk_prefill (the workspace check uses the backward size), plus NULL
  * or unaligned gradients (16-byte, dbeta 4-byte).  Asynchronous on stream.
  */

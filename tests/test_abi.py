@@ -263,7 +263,7 @@ def test_backward_refusals():
                                                              ctypes.c_int32, ctypes.c_int32,
                                                              ctypes.c_int32]
     need = L.kda_chunk_prefill_backward_workspace_bytes(48, 2, 4, 128, 128)
-    assert need == (48 // 64 + 2) * 4 * 573952
+    assert need == (48 // 64 + 2) * 4 * 344576 + 512 * 229376
     assert L.kda_chunk_prefill_backward_workspace_bytes(48, 2, 4, 64, 128) == 0
     cu = [0, 20, 48]
     assert _backward(L, cu, dk_dim=64) == 4
