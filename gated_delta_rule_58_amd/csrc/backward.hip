@@ -55,27 +55,10 @@ struct Scr {
                        DQE = 5 * C * D, DKD = 6 * C * D, floats = 7 * C * D;
 };
 
-// acc[i][j] += sum_{kk < K} a(16 i + tr, kk) b(kk, 16 j + tc) with tr = tid / 16,
-// tc = tid % 16: a (16 TM) x (16 TN) output over the 256 threads.
-template <int TM, int TN, typename FA, typename FB>
-__device__ __forceinline__ void gemm_acc(float (&acc)[TM][TN], int K, FA a, FB b) {
-  const int tr = threadIdx.x >> 4, tc = threadIdx.x & 15;
-  for (int kk = 0; kk < K; ++kk) {
-    float av[TM], bv[TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i) av[i] = a(16 * i + tr, kk);
-#pragma unroll
-    for (int j = 0; j < TN; ++j) bv[j] = b(kk, 16 * j + tc);
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
-  }
-}
-
-// The same product with the operands staged through LDS in slabs of KT = 16
-// along the contraction (each element read once from memory instead of once
-// per thread that uses it).  A_KC: a(m, kk) is contiguous along kk in memory
+// acc += a b for a (16 TM) x (16 TN) output over the 256 threads, on fp32
+// MFMA, with the operands staged through LDS in slabs of KT = 16 along the
+// contraction (each element read once from memory instead of once per thread
+// that uses it).  acc[i][j] is element (orow<TM>(i), ocol(j)).  A_KC: a(m, kk) is contiguous along kk in memory
 // (else along m); B_NC: b(kk, n) is contiguous along n (else along kk); the
 // slab fill follows the contiguous index.  sa: 16 x (16 TM + 1) floats, sb:
 // 16 x (16 TN + 1) floats.  Contains barriers: every thread of the block calls it.
@@ -85,7 +68,8 @@ __device__ __forceinline__ void gemm_staged(float (&acc)[TM][TN], int K, float* 
                                             FA a, FB b) {
   constexpr int M = 16 * TM, N = 16 * TN, MS = M + 1, NS = N + 1;
   constexpr int PA = M * KT / NT, PB = N * KT / NT;  // slab elements per thread
-  const int t = threadIdx.x, tr = t >> 4, tc = t & 15;
+  static_assert(TM % 4 == 0, "whole 16-row tiles per wave");
+  const int t = threadIdx.x;
   // the next slab is read into registers while the current one is in use
   float ra[PA], rb[PB];
   auto fetch = [&](int k0) {
@@ -102,6 +86,15 @@ __device__ __forceinline__ void gemm_staged(float (&acc)[TM][TN], int K, float* 
       rb[u] = b(k0 + kt, n);
     }
   };
+  // the accumulators as MFMA tiles for the whole product (4 consecutive
+  // registers each), converted from and to acc once
+  constexpr int TR = TM / 4;
+  f32x4 ct[TR][TN];
+#pragma unroll
+  for (int i = 0; i < TR; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+      ct[i][j] = f32x4{acc[4 * i][j], acc[4 * i + 1][j], acc[4 * i + 2][j], acc[4 * i + 3][j]};
   fetch(0);
   for (int k0 = 0; k0 < K; k0 += KT) {
 #pragma unroll
@@ -118,22 +111,43 @@ __device__ __forceinline__ void gemm_staged(float (&acc)[TM][TN], int K, float* 
     }
     __syncthreads();
     if (k0 + KT < K) fetch(k0 + KT);
-#pragma unroll 4
-    for (int kt = 0; kt < KT; ++kt) {
-      float av[TM], bv[TN];
+    // fp32 16x16x4 MFMA: lane l supplies A[l % 16][l / 16] and B[l / 16][l % 16]
+    // and holds D[4 (l / 16) + v][l % 16]; wave w owns the output tile rows
+    // TR w .. TR w + TR - 1 and every tile column.
+    const int lane = t & 63, w = t >> 6, lr = lane & 15, lq = lane >> 4;
 #pragma unroll
-      for (int i = 0; i < TM; ++i) av[i] = sa[kt * MS + 16 * i + tr];
+    for (int kg = 0; kg < KT / 4; ++kg) {
+      const int kk = 4 * kg + lq;
+      float av[TR], bv[TN];
 #pragma unroll
-      for (int j = 0; j < TN; ++j) bv[j] = sb[kt * NS + 16 * j + tc];
+      for (int i = 0; i < TR; ++i) av[i] = sa[kk * MS + 16 * (TR * w + i) + lr];
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+      for (int j = 0; j < TN; ++j) bv[j] = sb[kk * NS + 16 * j + lr];
 #pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
+      for (int i = 0; i < TR; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          ct[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[i], bv[j], ct[i][j], 0, 0, 0);
     }
     __syncthreads();
   }
+#pragma unroll
+  for (int i = 0; i < TR; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[4 * i + v][j] = ct[i][j][v];
 }
 constexpr int SA_FLOATS = KT * (64 + 1), SB_FLOATS = KT * (128 + 1);
+
+// Output element of acc[i][j] after gemm_staged<TM, TN>: row orow<TM>(i),
+// column ocol(j).
+template <int TM>
+__device__ __forceinline__ int orow(int i) {
+  const int t = threadIdx.x;
+  return 16 * ((TM / 4) * (t >> 6) + (i >> 2)) + 4 * ((t & 63) >> 4) + (i & 3);
+}
+__device__ __forceinline__ int ocol(int j) { return 16 * j + (threadIdx.x & 15); }
 
 template <int TM, int TN>
 __device__ __forceinline__ void zero(float (&acc)[TM][TN]) {
@@ -259,7 +273,6 @@ __global__ void __launch_bounds__(NT, 2) bwd_prep_kernel(const void* __restrict_
   }
   __syncthreads();
   for (int e = t; e < C * C; e += NT) im[Rec::M + e] = sM[e / C][e % C];
-  const int tr = t >> 4, tc = t & 15;
   float* sa = sS;
   float* sb = sS + SA_FLOATS;
   {  // W = M diag(b) K_E
@@ -272,7 +285,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_prep_kernel(const void* __restrict_
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) im[Rec::W + (16 * i + tr) * D + 16 * j + tc] = acc[i][j];
+      for (int j = 0; j < 8; ++j) im[Rec::W + orow<4>(i) * D + ocol(j)] = acc[i][j];
   }
   {  // U = M diag(b) V
     float acc[4][8];
@@ -284,7 +297,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_prep_kernel(const void* __restrict_
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) im[Rec::U + (16 * i + tr) * D + 16 * j + tc] = acc[i][j];
+      for (int j = 0; j < 8; ++j) im[Rec::U + orow<4>(i) * D + ocol(j)] = acc[i][j];
   }
   __syncthreads();  // W complete
   {  // Qt = scale (Q_E - P W)
@@ -296,7 +309,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_prep_kernel(const void* __restrict_
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const int r = 16 * i + tr, cc = 16 * j + tc;
+        const int r = orow<4>(i), cc = ocol(j);
         im[Rec::QT + r * D + cc] = scale * (Qf(r, cc) * __expf(Gf(r, cc)) - acc[i][j]);
       }
   }
@@ -335,7 +348,6 @@ __global__ void __launch_bounds__(NT, 2) bwd_walk_kernel(
   const int64_t L = eos - bos;
   const int nch = static_cast<int>((L + C - 1) / C);
   const int t = threadIdx.x;
-  const int tr = t >> 4, tc = t & 15;
   const int64_t HD = (int64_t)H * D;
   const int64_t sbase = ((int64_t)n * H + h) * D * D + 64 * tile;
   const float* R_init = fwd ? S0 : dSf;
@@ -345,7 +357,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_walk_kernel(
   for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      R[i][j] = R_init ? R_init[sbase + (int64_t)(16 * i + tr) * D + 16 * j + tc] : 0.0f;
+      R[i][j] = R_init ? R_init[sbase + (int64_t)orow<8>(i) * D + ocol(j)] : 0.0f;
   for (int it = 0; it < nch; ++it) {
     const int c = fwd ? it : nch - 1 - it;
     const int64_t pair = (bos / C + n + c) * H + h;
@@ -357,8 +369,8 @@ __global__ void __launch_bounds__(NT, 2) bwd_walk_kernel(
     for (int i = 0; i < 8; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        rc[(16 * i + tr) * D + 16 * j + tc] = R[i][j];
-        sR[16 * i + tr][16 * j + tc] = R[i][j];
+        rc[orow<8>(i) * D + ocol(j)] = R[i][j];
+        sR[orow<8>(i)][ocol(j)] = R[i][j];
       }
     __syncthreads();
     {  // Z = A1 R, A1 = W (forward) or K_D (backward)
@@ -371,14 +383,14 @@ __global__ void __launch_bounds__(NT, 2) bwd_walk_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) sZ[16 * i + tr][16 * j + tc] = z[i][j];
+        for (int j = 0; j < 4; ++j) sZ[orow<4>(i)][ocol(j)] = z[i][j];
     }
     __syncthreads();
     // R <- e^gamma_C R + [A2; A3]^T [-Z; B]: A2 = K_D / W, A3 = K_D / Qt,
     // B = U (forward) or the d_o tile (backward)
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float ec = im[Rec::EC + 16 * i + tr];
+      const float ec = im[Rec::EC + orow<8>(i)];
 #pragma unroll
       for (int j = 0; j < 4; ++j) R[i][j] *= ec;
     }
@@ -400,7 +412,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_walk_kernel(
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) R_end[sbase + (int64_t)(16 * i + tr) * D + 16 * j + tc] = R[i][j];
+      for (int j = 0; j < 4; ++j) R_end[sbase + (int64_t)orow<8>(i) * D + ocol(j)] = R[i][j];
   }
 }
 
@@ -424,7 +436,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_grad_kernel(
   ChunkPos p;
   if (!chunk_of_block(cu, N, T_tot, H, maxnch, p, item0 + blockIdx.x)) return;
   const int t = threadIdx.x;
-  const int tr = t >> 4, tc = t & 15;
+  const int tc = t & 15;
   const int64_t HD = (int64_t)H * D;
   const float* im = img + p.pair * Rec::floats;
   const float* S = Srec + p.pair * (int64_t)(D * D);
@@ -444,7 +456,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_grad_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) sc[off + (16 * i + tr) * D + 16 * j + tc] = mul * acc[i][j];
+      for (int j = 0; j < 8; ++j) sc[off + orow<4>(i) * D + ocol(j)] = mul * acc[i][j];
   };
   if (t < C) {
     sB[t] = t < Lc ? beta[(p.t0 + t) * H + p.h] : 0.0f;
@@ -461,7 +473,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_grad_kernel(
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const int r = 16 * i + tr, col = 16 * j + tc;
+        const int r = orow<4>(i), col = ocol(j);
         sc[Scr::X + r * D + col] = Vf(r, col) - acc[i][j];
       }
   }
@@ -493,11 +505,11 @@ __global__ void __launch_bounds__(NT, 2) bwd_grad_kernel(
                                    [&](int s, int j) { return sc[Scr::DD + s * D + j]; });
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r = 16 * i + tr;
+      const int r = orow<4>(i);
       float part = 0.0f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const int col = 16 * j + tc;
+        const int col = ocol(j);
         const float dX = sB[r] * acc[i][j];
         sc[Scr::DX + r * D + col] = dX;
         if (r < Lc) dv[tok(r, col)] = dX;
@@ -505,7 +517,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_grad_kernel(
       }
 #pragma unroll
       for (int off = 1; off < 16; off <<= 1) part += __shfl_xor(part, off);
-      if (tc == 0) sDB[r] += part;
+      if (tc == 0) sDB[r] += part;  // the 16 lanes holding row r
     }
   }
   __syncthreads();
@@ -518,7 +530,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_grad_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) sT[16 * i + tr][16 * j + tc] = a4[i][j];
+      for (int j = 0; j < 4; ++j) sT[orow<4>(i)][ocol(j)] = a4[i][j];
   }
   {  // dP = scale dO Delta^T on s <= r
     float a4[4][4];
@@ -529,7 +541,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_grad_kernel(
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int r = 16 * i + tr, s = 16 * j + tc;
+        const int r = orow<4>(i), s = ocol(j);
         sDP[r][s] = (s <= r && r < Lc) ? scale * a4[i][j] : 0.0f;
       }
   }
@@ -543,7 +555,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_grad_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) dMMt[(16 * i + tr) * C + 16 * j + tc] = a4[i][j];
+      for (int j = 0; j < 4; ++j) dMMt[orow<4>(i) * C + ocol(j)] = a4[i][j];
   }
   __syncthreads();
   {  // dA = -M^T (dM M^T) on s < r
@@ -556,7 +568,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_grad_kernel(
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int r = 16 * i + tr, s = 16 * j + tc;
+        const int r = orow<4>(i), s = ocol(j);
         sT[r][s] = (s < r && r < Lc) ? -a4[i][j] : 0.0f;
       }
   }
