@@ -102,6 +102,55 @@ def test_backward_final_state_only():
     check(got, ref, "final state only")
 
 
+def test_backward_strong_decay_heads():
+    """Heads whose channels decay by several nats per token (A_log up to 1.5,
+    dt_bias 0 on a whole head, a few fast channels on another): the pairwise
+    decay weights and e^gamma underflow to 0 where they should, never
+    overflow."""
+    need_gpu()
+    say("backward strong decay")
+    dr = draw_prefill([200, 77], H=4, dtype=torch.bfloat16, init_state=True, seed=85)
+    dr.A_log = torch.tensor([1.5, -0.75, 1.0, 0.0])
+    dt = dr.dt_bias.clone()
+    dt[0] = 0.0
+    dt[2, :16] = 1.0
+    dr.dt_bias = dt
+    g, beta = oracle_gate_f32(dr)
+    r = torch.Generator().manual_seed(86)
+    d_o = torch.randn(dr.q.shape[0], 4, 128, generator=r)
+    dSf = torch.randn(2, 4, 128, 128, generator=r) * 0.1
+    got = _run(dr, g, beta, d_o, dSf, 1.0)
+    for a in got:
+        assert torch.isfinite(a).all()
+    ref = oracle.prefill_backward(dr.q, dr.k, dr.v, g, beta, dr.cu_seqlens, dr.initial_state,
+                                  d_o=d_o, dS_final=dSf)
+    check(got, ref, "strong decay")
+
+
+def test_backward_config2_varlen_sampled_heads():
+    """8 sequences, 32,768 tokens, initial states (the varlen prefill
+    workload): the whole backward on the GPU, sampled heads against the
+    oracle."""
+    need_gpu()
+    say("backward config 2 sampled heads")
+    dr = draw_config(2, device=DEV)
+    g, beta = oracle_gate_f32(dr)
+    H = CONFIGS[2]["H"]
+    d_o = torch.randn(dr.q.shape[0], H, 128, generator=torch.Generator().manual_seed(87)).to(
+        torch.bfloat16)
+    got = kda.chunk_prefill_backward(dr.q, dr.k, dr.v, g.to(DEV), beta.to(DEV), d_o.to(DEV),
+                                     dr.cu_seqlens.to(DEV), dr.initial_state,
+                                     cu_seqlens_host=dr.cu_seqlens)
+    torch.cuda.synchronize()
+    heads = sample_heads(H, 2, 88)
+    S0 = None if dr.initial_state is None else dr.initial_state[:, heads].cpu()
+    ref = oracle.prefill_backward(dr.q[:, heads].cpu(), dr.k[:, heads].cpu(),
+                                  dr.v[:, heads].cpu(), g[:, heads], beta[:, heads],
+                                  dr.cu_seqlens, S0, d_o=d_o[:, heads].float())
+    sub = [None if a is None else a[:, heads] for a in got]
+    check(sub, ref, "config 2 heads %s" % heads)
+
+
 def test_backward_config1_sampled_heads():
     """T=4096, H=96 (the benchmarked prefill shape), bf16 q/k/v, bf16 d_o:
     the whole backward on the GPU, sampled heads against the oracle."""
