@@ -64,9 +64,14 @@ struct Scr {
 // 16 x (16 TN + 1) floats.  Contains barriers: every thread of the block calls it.
 constexpr int KT = 16;
 template <int TM, int TN, bool A_KC, bool B_NC, typename FA, typename FB>
-__device__ __forceinline__ void gemm_staged(float (&acc)[TM][TN], int K, float* sa, float* sb,
-                                            FA a, FB b) {
-  constexpr int M = 16 * TM, N = 16 * TN, MS = M + 1, NS = N + 1;
+__device__ __forceinline__ void gemm_staged(float (&acc)[TM][TN], int K, float* stage, FA a,
+                                            FB b) {
+  // slab rows 17 floats past a multiple of 32 apart: the MFMA reads (16
+  // consecutive elements of 4 consecutive rows) and the kk-fastest fills
+  // both spread over the banks
+  constexpr int M = 16 * TM, N = 16 * TN, MS = M + 17, NS = N + 17;
+  float* sa = stage;
+  float* sb = stage + KT * MS;
   constexpr int PA = M * KT / NT, PB = N * KT / NT;  // slab elements per thread
   static_assert(TM % 4 == 0, "whole 16-row tiles per wave");
   const int t = threadIdx.x;
@@ -138,7 +143,7 @@ __device__ __forceinline__ void gemm_staged(float (&acc)[TM][TN], int K, float* 
 #pragma unroll
       for (int v = 0; v < 4; ++v) acc[4 * i + v][j] = ct[i][j][v];
 }
-constexpr int SA_FLOATS = KT * (64 + 1), SB_FLOATS = KT * (128 + 1);
+constexpr int STAGE_FLOATS = KT * (64 + 17) + KT * (128 + 17);  // the largest product's slabs
 
 // Output element of acc[i][j] after gemm_staged<TM, TN>: row orow<TM>(i),
 // column ocol(j).
@@ -193,7 +198,8 @@ __global__ void __launch_bounds__(NT, 2) bwd_prep_kernel(const void* __restrict_
   constexpr int CS = 16;  // channels per slab of the At / P sums
   __shared__ float sA[C][C + 1], sP[C][C + 1], sM[C][C + 1], sB[C];
   // slabs of K, Q, gamma (CS channels), later the products' LDS slabs
-  __shared__ float sS[3 * C * (CS + 1)];
+  constexpr int SLAB = C * (CS + 1);
+  __shared__ float sS[(3 * SLAB > STAGE_FLOATS ? 3 * SLAB : STAGE_FLOATS)];
   ChunkPos p;
   if (!chunk_of_block(cu, N, T_tot, H, maxnch, p, blockIdx.x)) return;
   const int t = threadIdx.x;
@@ -223,14 +229,29 @@ __global__ void __launch_bounds__(NT, 2) bwd_prep_kernel(const void* __restrict_
     float a[16], pp[16];
 #pragma unroll
     for (int u = 0; u < 16; ++u) a[u] = pp[u] = 0.0f;
+    // slab c0 is read into registers while the previous one is in use
+    constexpr int PS = C * CS / NT;
+    float rk[PS], rq[PS], rg[PS];
+    auto fetch_slab = [&](int c0) {
+#pragma unroll
+      for (int u = 0; u < PS; ++u) {
+        const int e = t + NT * u, r = e / CS, ch = e % CS;
+        rk[u] = Kf(r, c0 + ch);
+        rq[u] = Qf(r, c0 + ch);
+        rg[u] = Gf(r, c0 + ch);
+      }
+    };
+    fetch_slab(0);
     for (int c0 = 0; c0 < D; c0 += CS) {
-      for (int e = t; e < C * CS; e += NT) {
-        const int r = e / CS, ch = e % CS;
-        sK[r * (CS + 1) + ch] = Kf(r, c0 + ch);
-        sQ[r * (CS + 1) + ch] = Qf(r, c0 + ch);
-        sG[r * (CS + 1) + ch] = Gf(r, c0 + ch);
+#pragma unroll
+      for (int u = 0; u < PS; ++u) {
+        const int e = t + NT * u, r = e / CS, ch = e % CS;
+        sK[r * (CS + 1) + ch] = rk[u];
+        sQ[r * (CS + 1) + ch] = rq[u];
+        sG[r * (CS + 1) + ch] = rg[u];
       }
       __syncthreads();
+      if (c0 + CS < D) fetch_slab(c0 + CS);
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
         const int e = t + NT * u, r = e / C, s2 = e % C;
@@ -274,11 +295,10 @@ __global__ void __launch_bounds__(NT, 2) bwd_prep_kernel(const void* __restrict_
   __syncthreads();
   for (int e = t; e < C * C; e += NT) im[Rec::M + e] = sM[e / C][e % C];
   float* sa = sS;
-  float* sb = sS + SA_FLOATS;
   {  // W = M diag(b) K_E
     float acc[4][8];
     zero(acc);
-    gemm_staged<4, 8, true, true>(acc, C, sa, sb, [&](int r, int s2) { return sM[r][s2]; },
+    gemm_staged<4, 8, true, true>(acc, C, sa, [&](int r, int s2) { return sM[r][s2]; },
                                   [&](int s2, int cc) {
                                     return sB[s2] * Kf(s2, cc) * __expf(Gf(s2, cc));
                                   });
@@ -290,7 +310,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_prep_kernel(const void* __restrict_
   {  // U = M diag(b) V
     float acc[4][8];
     zero(acc);
-    gemm_staged<4, 8, true, true>(acc, C, sa, sb, [&](int r, int s2) { return sM[r][s2]; },
+    gemm_staged<4, 8, true, true>(acc, C, sa, [&](int r, int s2) { return sM[r][s2]; },
                                   [&](int s2, int j) {
                                     return s2 < p.Lc ? sB[s2] * load1(v, tok(s2, j), QB) : 0.0f;
                                   });
@@ -303,7 +323,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_prep_kernel(const void* __restrict_
   {  // Qt = scale (Q_E - P W)
     float acc[4][8];
     zero(acc);
-    gemm_staged<4, 8, true, true>(acc, C, sa, sb, [&](int r, int s2) { return sP[r][s2]; },
+    gemm_staged<4, 8, true, true>(acc, C, sa, [&](int r, int s2) { return sP[r][s2]; },
                                   [&](int s2, int cc) { return im[Rec::W + s2 * D + cc]; });
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -333,7 +353,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_walk_kernel(
     const float* __restrict__ S0, float* __restrict__ rec_f, const float* __restrict__ dSf,
     float* __restrict__ dS0, float* __restrict__ rec_b) {
   __shared__ float sR[D][64 + 1], sZ[C][64 + 1];
-  __shared__ float sS[SA_FLOATS + SB_FLOATS];
+  __shared__ float sS[STAGE_FLOATS];
   const int64_t nb = (int64_t)N * H * 2;
   int64_t b = blockIdx.x;
   const bool fwd = both && b < nb;
@@ -377,7 +397,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_walk_kernel(
       const float* A1 = im + (fwd ? Rec::W : Rec::KD);
       float z[4][4];
       zero(z);
-      gemm_staged<4, 4, true, true>(z, D, sS, sS + KT * (64 + 1),
+      gemm_staged<4, 4, true, true>(z, D, sS,
                                     [&](int r, int cc) { return A1[r * D + cc]; },
                                     [&](int cc, int j) { return sR[cc][j]; });
 #pragma unroll
@@ -397,7 +417,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_walk_kernel(
     const float* A2 = im + (fwd ? Rec::KD : Rec::W);
     const float* A3 = im + (fwd ? Rec::KD : Rec::QT);
     gemm_staged<8, 4, false, true>(
-        R, 2 * C, sS, sS + KT * (128 + 1),
+        R, 2 * C, sS,
         [&](int cr, int kk) { return kk < C ? A2[kk * D + cr] : A3[(kk - C) * D + cr]; },
         [&](int kk, int j) {
           if (kk < C) return -sZ[kk][j];
@@ -432,7 +452,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_grad_kernel(
   constexpr int QC = D / 4;
   __shared__ float sU[3 * C * QC + 8 * QC];
   float* sa = sU;
-  float* sb = sU + SA_FLOATS;
+  static_assert(STAGE_FLOATS <= 3 * C * (D / 4) + 8 * (D / 4), "stage fits the union");
   ChunkPos p;
   if (!chunk_of_block(cu, N, T_tot, H, maxnch, p, item0 + blockIdx.x)) return;
   const int t = threadIdx.x;
@@ -466,7 +486,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_grad_kernel(
   {  // X = V - K_E S
     float acc[4][8];
     zero(acc);
-    gemm_staged<4, 8, true, true>(acc, D, sa, sb,
+    gemm_staged<4, 8, true, true>(acc, D, sa,
                                   [&](int r, int cc) { return Kf(r, cc) * __expf(Gf(r, cc)); },
                                   [&](int cc, int j) { return S[cc * D + j]; });
 #pragma unroll
@@ -481,17 +501,17 @@ __global__ void __launch_bounds__(NT, 2) bwd_grad_kernel(
   {  // Delta = M diag(b) X
     float acc[4][8];
     zero(acc);
-    gemm_staged<4, 8, true, true>(acc, C, sa, sb, [&](int r, int s) { return im[Rec::M + r * C + s]; },
+    gemm_staged<4, 8, true, true>(acc, C, sa, [&](int r, int s) { return im[Rec::M + r * C + s]; },
                                   [&](int s, int j) { return sB[s] * sc[Scr::X + s * D + j]; });
     put8(acc, Scr::DL, 1.0f);
   }
   {  // dDelta = K_D dS_next + scale P^T dO
     float acc[4][8];
     zero(acc);
-    gemm_staged<4, 8, true, true>(acc, D, sa, sb,
+    gemm_staged<4, 8, true, true>(acc, D, sa,
                                   [&](int r, int cc) { return im[Rec::KD + r * D + cc]; },
                                   [&](int cc, int j) { return dS[cc * D + j]; });
-    gemm_staged<4, 8, false, true>(acc, C, sa, sb,
+    gemm_staged<4, 8, false, true>(acc, C, sa,
                                    [&](int r, int s) { return scale * im[Rec::P + s * C + r]; },
                                    [&](int s, int j) { return dOf(s, j); });
     put8(acc, Scr::DD, 1.0f);
@@ -500,7 +520,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_grad_kernel(
   {  // dY = M^T dDelta, dX = diag(b) dY (= dv), dbeta += rowsum(dY . X)
     float acc[4][8];
     zero(acc);
-    gemm_staged<4, 8, false, true>(acc, C, sa, sb,
+    gemm_staged<4, 8, false, true>(acc, C, sa,
                                    [&](int r, int s) { return im[Rec::M + s * C + r]; },
                                    [&](int s, int j) { return sc[Scr::DD + s * D + j]; });
 #pragma unroll
@@ -524,7 +544,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_grad_kernel(
   {  // dM = dDelta Y^T
     float a4[4][4];
     zero(a4);
-    gemm_staged<4, 4, true, false>(a4, D, sa, sb,
+    gemm_staged<4, 4, true, false>(a4, D, sa,
                                    [&](int r, int j) { return sc[Scr::DD + r * D + j]; },
                                    [&](int j, int s) { return sB[s] * sc[Scr::X + s * D + j]; });
 #pragma unroll
@@ -535,7 +555,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_grad_kernel(
   {  // dP = scale dO Delta^T on s <= r
     float a4[4][4];
     zero(a4);
-    gemm_staged<4, 4, true, false>(a4, D, sa, sb, [&](int r, int j) { return dOf(r, j); },
+    gemm_staged<4, 4, true, false>(a4, D, sa, [&](int r, int j) { return dOf(r, j); },
                                    [&](int j, int s) { return sc[Scr::DL + s * D + j]; });
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -550,7 +570,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_grad_kernel(
   {  // dM M^T
     float a4[4][4];
     zero(a4);
-    gemm_staged<4, 4, true, false>(a4, C, sa, sb, [&](int r, int u) { return sT[r][u]; },
+    gemm_staged<4, 4, true, false>(a4, C, sa, [&](int r, int u) { return sT[r][u]; },
                                    [&](int u, int s) { return im[Rec::M + s * C + u]; });
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -561,7 +581,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_grad_kernel(
   {  // dA = -M^T (dM M^T) on s < r
     float a4[4][4];
     zero(a4);
-    gemm_staged<4, 4, false, true>(a4, C, sa, sb,
+    gemm_staged<4, 4, false, true>(a4, C, sa,
                                    [&](int r, int u) { return im[Rec::M + u * C + r]; },
                                    [&](int u, int s) { return dMMt[u * C + s]; });
 #pragma unroll
@@ -575,7 +595,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_grad_kernel(
   {  // dK_E = -dX S^T
     float acc[4][8];
     zero(acc);
-    gemm_staged<4, 8, true, false>(acc, D, sa, sb,
+    gemm_staged<4, 8, true, false>(acc, D, sa,
                                    [&](int r, int j) { return sc[Scr::DX + r * D + j]; },
                                    [&](int j, int cc) { return S[cc * D + j]; });
     put8(acc, Scr::DKE, -1.0f);
@@ -583,14 +603,14 @@ __global__ void __launch_bounds__(NT, 2) bwd_grad_kernel(
   {  // dQ_E = scale dO S^T
     float acc[4][8];
     zero(acc);
-    gemm_staged<4, 8, true, false>(acc, D, sa, sb, [&](int r, int j) { return dOf(r, j); },
+    gemm_staged<4, 8, true, false>(acc, D, sa, [&](int r, int j) { return dOf(r, j); },
                                    [&](int j, int cc) { return S[cc * D + j]; });
     put8(acc, Scr::DQE, scale);
   }
   {  // dK_D = Delta dS_next^T
     float acc[4][8];
     zero(acc);
-    gemm_staged<4, 8, true, false>(acc, D, sa, sb,
+    gemm_staged<4, 8, true, false>(acc, D, sa,
                                    [&](int r, int j) { return sc[Scr::DL + r * D + j]; },
                                    [&](int j, int cc) { return dS[cc * D + j]; });
     put8(acc, Scr::DKD, 1.0f);
@@ -638,11 +658,21 @@ __global__ void __launch_bounds__(NT, 2) bwd_grad_kernel(
     const int cc = c0 + cl;
     const float gC = sG[(C - 1) * QC + cl];
     float dgC = 0.0f;
+    float nke = 0.0f, nqe = 0.0f, nkd = 0.0f;  // the next row's terms, read ahead
+    if (grp < Lc) {
+      nke = sc[Scr::DKE + grp * D + cc];
+      nqe = sc[Scr::DQE + grp * D + cc];
+      nkd = sc[Scr::DKD + grp * D + cc];
+    }
     for (int x = grp; x < Lc; x += 8) {
       const float kx = sK[x * QC + cl], qx = sQ[x * QC + cl], gx = sG[x * QC + cl], bx = sB[x];
       const float E = __expf(gx), F = __expf(gC - gx);
-      const float dke = sc[Scr::DKE + x * D + cc], dqe = sc[Scr::DQE + x * D + cc];
-      const float dkd = sc[Scr::DKD + x * D + cc];
+      const float dke = nke, dqe = nqe, dkd = nkd;
+      if (x + 8 < Lc) {
+        nke = sc[Scr::DKE + (x + 8) * D + cc];
+        nqe = sc[Scr::DQE + (x + 8) * D + cc];
+        nkd = sc[Scr::DKD + (x + 8) * D + cc];
+      }
       float dkx = dke * E + dkd * F;
       float dgx = (dke * kx + dqe * qx) * E - dkd * kx * F;
       float dqx = dqe * E;
