@@ -231,3 +231,28 @@ def test_gated_training_path():
     say("training path gate", errs)
     for name, e in errs.items():
         assert e <= GRAD_TOL, name
+
+
+def test_backward_empty_batch():
+    """Every sequence empty (T_tot = 0): no gradient tensor has elements, the
+    initial state's gradient is d_final_state unchanged, and the gate's
+    parameter gradients over zero tokens are zero."""
+    need_gpu()
+    say("backward empty batch")
+    H = 2
+    z3 = torch.empty((0, H, 128), dtype=torch.bfloat16, device=DEV)
+    g = torch.empty((0, H, 128), dtype=torch.float32, device=DEV)
+    beta = torch.empty((0, H), dtype=torch.float32, device=DEV)
+    cu_h = torch.tensor([0, 0, 0], dtype=torch.int32)
+    S0 = torch.randn(2, H, 128, 128, device=DEV)
+    dSf = torch.randn(2, H, 128, 128, device=DEV)
+    dq, dk, dv, dgg, db, dS0 = kda.chunk_prefill_backward(
+        z3, z3, z3, g, beta, None, cu_h.to(DEV), S0, dSf, cu_seqlens_host=cu_h)
+    torch.cuda.synchronize()
+    assert dq.numel() == 0 and dgg.numel() == 0 and db.numel() == 0
+    assert torch.equal(dS0, dSf)
+    A = torch.zeros(H, device=DEV)
+    dt = torch.zeros(H, 128, device=DEV)
+    dx, dbl, dA, ddt = kda.gate_backward(g, beta, A, dt, g, beta)
+    torch.cuda.synchronize()
+    assert dx.numel() == 0 and torch.all(dA == 0) and torch.all(ddt == 0)
