@@ -677,6 +677,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_grad_kernel(
       float dgx = (dke * kx + dqe * qx) * E - dkd * kx * F;
       float dqx = dqe * E;
       dgC = fmaf(dkd * kx, F, dgC);
+#pragma unroll 4
       for (int s2 = 0; s2 <= x; ++s2) {  // x later: pairs (x, s)
         const float u = __expf(gx - sG[s2 * QC + cl]) * sK[s2 * QC + cl];
         const float al = s2 < x ? sT[x][s2] * bx : 0.0f;
@@ -685,6 +686,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_grad_kernel(
         dqx = fmaf(pi, u, dqx);
         dgx = fmaf(al * kx + pi * qx, u, dgx);
       }
+#pragma unroll 4
       for (int r = x; r < Lc; ++r) {  // x earlier: pairs (r, x)
         const float w = __expf(sG[r * QC + cl] - gx);
         const float al = x < r ? sT[r][x] * sB[r] : 0.0f;
