@@ -436,6 +436,9 @@ def main():
     pro = bench_prologue(args, torch, kda)
     print("prologue (short conv + SiLU + q/k L2 norm): %.4f ms, %.1f GB/s"
           % (pro["ms"], pro["GBps"]), file=sys.stderr, flush=True)
+    cp = bench_copy(argparse.Namespace(steps=8, warmup=2), torch)
+    print("copy (1 GiB read + 1 GiB written): %.1f GB/s" % cp["GBps"], file=sys.stderr,
+          flush=True)
     bwd = bench_backward(args, torch, kda, synth)
     print("prefill backward: %.3f ms, %.2f M tokens/s" % (bwd["ms"], bwd["tokens_per_s"] / 1e6),
           file=sys.stderr, flush=True)
@@ -468,6 +471,7 @@ def main():
                     "chunk_prefill_tokens_per_s": T / (pre["chunk_ms"] * 1e-3)},
         "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": ach / HBM_PEAK_GBS, "traffic": measured_traffic(),
+                     "frac_of_measured_copy": ach / cp["GBps"],
                      "kernel": "kda_chunk_prefill_gated (prep_kernel + state_kernel, one pass)",
                      "alg_bytes_per_launch": PREFILL_BYTES},
         "roofline_mfma": {"achieved": mfma, "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -475,6 +479,7 @@ def main():
                           "alg_flops_per_launch": PREFILL_FLOPS},
         "decode": {"workload": "256 seqs x 96 heads x 1 token, 64 steps, fp32 state in place",
                    "ms_per_step": dec["ms_per_step"], "GBps": dec["GBps"], "frac": dec["frac"],
+                   "frac_of_measured_copy": dec["GBps"] / cp["GBps"],
                    "bytes_per_step": DEC_STEP_BYTES,
                    "gated": {"workload": "kda_recurrent_decode_gated: fp32 gate/beta logits, "
                                          "state pool of 256 slots addressed by a permutation",
@@ -486,6 +491,9 @@ def main():
                                  "SiLU, conv state out",
                      "ms": pro["ms"], "GBps": pro["GBps"], "frac": pro["frac"],
                      "bytes_per_call": pro["bytes"], "tokens_per_s": pro["tokens_per_s"]},
+        "copy": {"workload": "device copy of 1 GiB (read + write), the measured bandwidth "
+                             "ceiling the fractions of_measured_copy use",
+                 "GBps": cp["GBps"], "ms": cp["ms"]},
         "prefill_backward": {"workload": "kda_chunk_prefill_backward T=4096 H=96, bf16 "
                                          "q/k/v and d_o, fp32 g/beta, zero initial state",
                              **bwd},
