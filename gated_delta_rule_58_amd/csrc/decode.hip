@@ -41,21 +41,39 @@ __global__ void __launch_bounds__(NTHR) decode_kernel(
   __shared__ f32x4 s_red[NTHR / 64][32][2];
   __shared__ float s_qk[2][2];
 
-  // q, k, decay and q.k of pair p into LDS buffer buf; this thread's v and beta
-  auto load_small = [&](int64_t p, int buf, f32x4& vv, float& b) {
+  // Small inputs of a pair in two halves: fetch issues the loads (before the
+  // previous pair's stores) and keeps the raw bits, commit widens and uses
+  // them (after those stores): q, k, decay and q.k into LDS buffer buf; v and
+  // beta stay in registers.  Every thread loads (threads past the 128
+  // channels repeat the first ones), so no load sits inside a branch.
+  struct Small {
+    typename Raw<QKV_BF16>::T1 kk, qq;
+    float gg, b;
+    typename Raw<QKV_BF16>::T4 vv;
+  };
+  auto fetch_small = [&](int64_t p, Small& sm) {
+    const int c = t & (D - 1);
+    sm.kk = load1_raw<QKV_BF16>(k, p * D + c);
+    sm.qq = load1_raw<QKV_BF16>(q, p * D + c);
+    sm.gg = g[p * D + c];
+    sm.vv = load4_raw<QKV_BF16>(v, p * D + 4 * cg);
+    sm.b = beta[p];
+  };
+  auto commit_small = [&](int buf, Small& sm) {
+    hold(sm.kk);
+    hold(sm.qq);
+    hold(sm.gg);
+    hold(sm.vv);
     if (t < D) {
-      const float kk = load1(k, p * D + t, QKV_BF16);
-      const float qq = load1(q, p * D + t, QKV_BF16);
+      const float kk = widen1<QKV_BF16>(sm.kk), qq = widen1<QKV_BF16>(sm.qq);
       s_k[buf][t] = kk;
       s_q[buf][t] = qq;
-      s_a[buf][t] = expf(g[p * D + t]);
+      s_a[buf][t] = expf(sm.gg);
       float pr = kk * qq;
 #pragma unroll
       for (int off = 32; off > 0; off >>= 1) pr += __shfl_xor(pr, off);
       if ((t & 63) == 0) s_qk[buf][t >> 6] = pr;
     }
-    vv = load4(v, p * D + 4 * cg, QKV_BF16);
-    b = beta[p];
   };
   auto load_state = [&](int64_t p, f32x4* st) {
     const float* S = state + p * (D * D);
@@ -66,14 +84,14 @@ __global__ void __launch_bounds__(NTHR) decode_kernel(
 
   int64_t pair = (int64_t)blockIdx.x * PAIRS_PER_BLOCK;
   f32x4 st[8], nx[8];
-  f32x4 vv;
-  float b;
-  load_small(pair, 0, vv, b);
+  Small cur, nxt;
+  fetch_small(pair, cur);
   load_state(pair, st);
+  commit_small(0, cur);
 #pragma unroll
   for (int j = 0; j < PAIRS_PER_BLOCK; ++j, ++pair) {
     const int buf = j & 1;
-    __syncthreads();
+    barrier_lds();
     f32x4 pk = {0.f, 0.f, 0.f, 0.f}, pq = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -91,7 +109,7 @@ __global__ void __launch_bounds__(NTHR) decode_kernel(
       s_red[w][cg][0] = pk;
       s_red[w][cg][1] = pq;
     }
-    __syncthreads();
+    barrier_lds();
     f32x4 kS = s_red[0][cg][0], qS = s_red[0][cg][1];
 #pragma unroll
     for (int jj = 1; jj < NTHR / 64; ++jj) {
@@ -99,13 +117,11 @@ __global__ void __launch_bounds__(NTHR) decode_kernel(
       qS += s_red[jj][cg][1];
     }
     const float qk = s_qk[buf][0] + s_qk[buf][1];
-    const f32x4 delta = b * (vv - kS);
+    const f32x4 delta = cur.b * (widen4<QKV_BF16>(cur.vv) - kS);
     // next pair's loads go out before this pair's stores
     const bool more = j + 1 < PAIRS_PER_BLOCK && pair + 1 < pairs;
-    f32x4 vn = vv;
-    float bn = b;
     if (more) {
-      load_small(pair + 1, buf ^ 1, vn, bn);
+      fetch_small(pair + 1, nxt);
       load_state(pair + 1, nx);
     }
     float* S = state + pair * (D * D);
@@ -117,10 +133,10 @@ __global__ void __launch_bounds__(NTHR) decode_kernel(
     }
     if (rs == 0) store4(o, pair * D + 4 * cg, scale * (qS + qk * delta), O_BF16);
     if (!more) break;
+    commit_small(buf ^ 1, nxt);
+    cur = nxt;
 #pragma unroll
     for (int i = 0; i < 8; ++i) st[i] = nx[i];
-    vv = vn;
-    b = bn;
   }
 }
 
