@@ -111,7 +111,11 @@ __global__ void __launch_bounds__(NTHR) shortconv_kernel(
   const int64_t c0 = (int64_t)h * D + 8 * oct;
   // conv state layout [N][3 tensors][3 taps, oldest first][H*128] fp32
   const int64_t sbase = ((int64_t)n * 3 + z) * 3 * HD + c0;
-  // window row j = token t0 - 3 + j of the sequence; all loads issued first
+  // the conv weights first (the first token needs them all), then the window:
+  // row j = token t0 - 3 + j of the sequence; all loads issued up front
+  f32x4 wc[8];  // wc[e][i] = w[c0 + e, i]
+#pragma unroll
+  for (int e = 0; e < 8; ++e) wc[e] = *reinterpret_cast<const f32x4*>(w + (c0 + e) * 4);
   RawRow<IN_BF16> win[NW];
 #pragma unroll
   for (int j = 0; j < NW; ++j) {
@@ -148,9 +152,6 @@ __global__ void __launch_bounds__(NTHR) shortconv_kernel(
   auto val = [&](int j, int e) -> float {  // window row j, channel e (fp32)
     return (j < 3 && t0 - 3 + j < 0) ? pre[j][e] : win[j].at(e);
   };
-  f32x4 wc[8];  // wc[e][i] = w[c0 + e, i]
-#pragma unroll
-  for (int e = 0; e < 8; ++e) wc[e] = *reinterpret_cast<const f32x4*>(w + (c0 + e) * 4);
 #pragma unroll
   for (int k = 0; k < TPT; ++k) {
     if (t0 + k >= L) break;
