@@ -128,15 +128,15 @@ __global__ void __launch_bounds__(NTHR, 4) decode_gated_kernel(
   };
   // state rows as loaded (fp32 float4 or 8 bf16), widened to fp32 only when
   // used, so the next pair's loads stay in flight across this pair's stores
-  typedef typename std::conditional<S_BF16, u16x8, f32x4>::type Raw;
-  auto load_state = [&](const Tile& tl, Raw* raw) {
+  typedef typename std::conditional<S_BF16, u16x8, f32x4>::type StateRaw;
+  auto load_state = [&](const Tile& tl, StateRaw* raw) {
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       const int off = ((rs + NRS * i) * D + CPT * cg) * ES;
-      raw[i] = __builtin_bit_cast(Raw, __builtin_amdgcn_raw_buffer_load_b128(tl.r, off, 0, kBufNT));
+      raw[i] = __builtin_bit_cast(StateRaw, __builtin_amdgcn_raw_buffer_load_b128(tl.r, off, 0, kBufNT));
     }
   };
-  auto widen = [&](const Raw* raw, f32x4 (*st)[NV]) {
+  auto widen = [&](const StateRaw* raw, f32x4 (*st)[NV]) {
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       if constexpr (S_BF16) {
@@ -172,7 +172,7 @@ __global__ void __launch_bounds__(NTHR, 4) decode_gated_kernel(
   // in flight across them.
   int64_t pair = (int64_t)blockIdx.x * PAIRS;
   f32x4 st[RPT][NV];
-  Raw raw[RPT];
+  StateRaw raw[RPT];
   Small sm;
   float b;
   Tile cur = state_of(pair), nxt = cur;
