@@ -186,6 +186,29 @@ __device__ __forceinline__ bool chunk_of_block(const int32_t* cu, int N, int T_t
   return true;
 }
 
+// The chunk's rows of one head of a token-major [T, H, 128] tensor as a
+// buffer resource: rows at or past the chunk's end (and every row when the
+// tensor is absent) read as 0.  Loads through it carry no branch: with a
+// branch per element (r < Lc ? load : 0) every load waited alone, and the
+// staged products' operand fetches ran one memory round trip per element.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t chunk_rows(const void* base, int esz,
+                                                             const ChunkPos& p, int64_t HD) {
+  const char* b = base ? static_cast<const char*>(base) +
+                             ((int64_t)p.t0 * HD + (int64_t)p.h * D) * esz
+                       : nullptr;
+  const int64_t n = (base && p.Lc > 0) ? ((int64_t)(p.Lc - 1) * HD + D) * esz : 0;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(b), (short)0, (int)n, 0x00020000);
+}
+// element (row r < 64, channel cc) through chunk_rows; HDi = H * 128
+template <bool BF16>
+__device__ __forceinline__ float row_at(__amdgpu_buffer_rsrc_t rs, int HDi, int r, int cc) {
+  if constexpr (BF16)
+    return bf16_bits_to_f32(static_cast<uint16_t>(
+        __builtin_amdgcn_raw_buffer_load_b16(rs, (r * HDi + cc) * 2, 0, 0)));
+  else
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (r * HDi + cc) * 4, 0, 0));
+}
+
 template <bool QB>
 __global__ void __launch_bounds__(NT, 2) bwd_prep_kernel(const void* __restrict__ q,
                                                          const void* __restrict__ k,
@@ -205,14 +228,16 @@ __global__ void __launch_bounds__(NT, 2) bwd_prep_kernel(const void* __restrict_
   const int t = threadIdx.x;
   const int64_t HD = (int64_t)H * D;
   float* im = img + p.pair * Rec::floats;
-  auto tok = [&](int r, int cc) { return (p.t0 + r) * HD + (int64_t)p.h * D + cc; };
-  auto Kf = [&](int r, int cc) { return r < p.Lc ? load1(k, tok(r, cc), QB) : 0.0f; };
-  auto Qf = [&](int r, int cc) { return r < p.Lc ? load1(q, tok(r, cc), QB) : 0.0f; };
+  const int HDi = static_cast<int>(HD);
+  const auto rk = chunk_rows(k, QB ? 2 : 4, p, HD), rq = chunk_rows(q, QB ? 2 : 4, p, HD),
+             rv = chunk_rows(v, QB ? 2 : 4, p, HD), rg = chunk_rows(g, 4, p, HD);
+  auto Kf = [&](int r, int cc) { return row_at<QB>(rk, HDi, r, cc); };
+  auto Qf = [&](int r, int cc) { return row_at<QB>(rq, HDi, r, cc); };
   if (t < C) sB[t] = t < p.Lc ? beta[(p.t0 + t) * H + p.h] : 0.0f;
   if (t < D) {  // gamma: running sum of g down channel t (rows past the end repeat the last)
     float gv[C];
 #pragma unroll
-    for (int r = 0; r < C; ++r) gv[r] = r < p.Lc ? g[tok(r, t)] : 0.0f;
+    for (int r = 0; r < C; ++r) gv[r] = row_at<false>(rg, HDi, r, t);
     float run = 0.0f;
 #pragma unroll
     for (int r = 0; r < C; ++r) {
@@ -312,7 +337,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_prep_kernel(const void* __restrict_
     zero(acc);
     gemm_staged<4, 8, true, true>(acc, C, sa, [&](int r, int s2) { return sM[r][s2]; },
                                   [&](int s2, int j) {
-                                    return s2 < p.Lc ? sB[s2] * load1(v, tok(s2, j), QB) : 0.0f;
+                                    return sB[s2] * row_at<QB>(rv, HDi, s2, j);
                                   });
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -369,6 +394,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_walk_kernel(
   const int nch = static_cast<int>((L + C - 1) / C);
   const int t = threadIdx.x;
   const int64_t HD = (int64_t)H * D;
+  const int HDi = static_cast<int>(HD);
   const int64_t sbase = ((int64_t)n * H + h) * D * D + 64 * tile;
   const float* R_init = fwd ? S0 : dSf;
   float* rec = fwd ? rec_f : rec_b;
@@ -384,6 +410,11 @@ __global__ void __launch_bounds__(NT, 2) bwd_walk_kernel(
     const float* im = img + pair * Rec::floats;
     const int Lc = static_cast<int>(L - (int64_t)c * C < C ? L - (int64_t)c * C : C);
     const int64_t t0 = bos + (int64_t)c * C;
+    ChunkPos cp;
+    cp.t0 = t0;
+    cp.h = h;
+    cp.Lc = Lc;
+    const auto rdo = chunk_rows(d_o, DOB ? 2 : 4, cp, HD);
     float* rc = rec + pair * (int64_t)(D * D) + 64 * tile;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
@@ -423,8 +454,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_walk_kernel(
           if (kk < C) return -sZ[kk][j];
           const int r = kk - C;
           if (fwd) return im[Rec::U + r * D + 64 * tile + j];
-          return (d_o && r < Lc) ? load1(d_o, (t0 + r) * HD + (int64_t)h * D + 64 * tile + j, DOB)
-                                 : 0.0f;
+          return row_at<DOB>(rdo, HDi, r, 64 * tile + j);
         });
   }
   float* R_end = fwd ? nullptr : dS0;
@@ -465,12 +495,13 @@ __global__ void __launch_bounds__(NT, 2) bwd_grad_kernel(
   float* sc = scr + (int64_t)blockIdx.x * Scr::floats;
   const int Lc = p.Lc;
   auto tok = [&](int r, int cc) { return (p.t0 + r) * HD + (int64_t)p.h * D + cc; };
-  auto Kf = [&](int r, int cc) { return r < Lc ? load1(k, tok(r, cc), QB) : 0.0f; };
-  auto Qf = [&](int r, int cc) { return r < Lc ? load1(q, tok(r, cc), QB) : 0.0f; };
-  auto Vf = [&](int r, int cc) { return r < Lc ? load1(v, tok(r, cc), QB) : 0.0f; };
-  auto dOf = [&](int r, int cc) {
-    return (d_o && r < Lc) ? load1(d_o, tok(r, cc), DOB) : 0.0f;
-  };
+  const int HDi = static_cast<int>(HD);
+  const auto rk = chunk_rows(k, QB ? 2 : 4, p, HD), rq = chunk_rows(q, QB ? 2 : 4, p, HD),
+             rv = chunk_rows(v, QB ? 2 : 4, p, HD), ro = chunk_rows(d_o, DOB ? 2 : 4, p, HD);
+  auto Kf = [&](int r, int cc) { return row_at<QB>(rk, HDi, r, cc); };
+  auto Qf = [&](int r, int cc) { return row_at<QB>(rq, HDi, r, cc); };
+  auto Vf = [&](int r, int cc) { return row_at<QB>(rv, HDi, r, cc); };
+  auto dOf = [&](int r, int cc) { return row_at<DOB>(ro, HDi, r, cc); };
   auto Gf = [&](int r, int cc) { return im[Rec::G + r * D + cc]; };
   auto put8 = [&](float (&acc)[4][8], int off, float mul) {
 #pragma unroll
