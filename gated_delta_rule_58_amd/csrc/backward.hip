@@ -646,13 +646,18 @@ __global__ void __launch_bounds__(NT, 2) bwd_grad_kernel(
                                    [&](int j, int cc) { return dS[cc * D + j]; });
     put8(acc, Scr::DKD, 1.0f);
   }
-  {  // dbeta += sum_s dA[r, s] At[r, s]: row r on lanes 4r .. 4r + 3
+  {  // dbeta += sum_s dA[r, s] At[r, s]: row r on lanes 4r .. 4r + 3; each lane
+     // then scales the dA entries it read by beta_r, the factor the pairwise
+     // terms below take them with (the barriers of the next block order it)
     const int r = t >> 2, qd = t & 3;
+    const float br = sB[r];
     float a = 0.0f;
 #pragma unroll
     for (int u = 0; u < C / 4; ++u) {
       const int s2 = 4 * u + qd;
-      a = fmaf(sT[r][s2], im[Rec::AT + r * C + s2], a);  // dA is 0 for s >= r
+      const float da = sT[r][s2];
+      a = fmaf(da, im[Rec::AT + r * C + s2], a);  // dA is 0 for s >= r
+      sT[r][s2] = da * br;
     }
     a += __shfl_xor(a, 1);
     a += __shfl_xor(a, 2);
@@ -696,7 +701,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_grad_kernel(
       nkd = sc[Scr::DKD + grp * D + cc];
     }
     for (int x = grp; x < Lc; x += 8) {
-      const float kx = sK[x * QC + cl], qx = sQ[x * QC + cl], gx = sG[x * QC + cl], bx = sB[x];
+      const float kx = sK[x * QC + cl], qx = sQ[x * QC + cl], gx = sG[x * QC + cl];
       const float E = __expf(gx), F = __expf(gC - gx);
       const float dke = nke, dqe = nqe, dkd = nkd;
       if (x + 8 < Lc) {
@@ -708,23 +713,27 @@ __global__ void __launch_bounds__(NT, 2) bwd_grad_kernel(
       float dgx = (dke * kx + dqe * qx) * E - dkd * kx * F;
       float dqx = dqe * E;
       dgC = fmaf(dkd * kx, F, dgC);
+      // sT rows carry beta of the row and are 0 on and above the diagonal;
+      // the row's factors (kx, qx) multiply the two sums once at the end
+      float sum_at = 0.0f, sum_p = 0.0f;
 #pragma unroll 4
       for (int s2 = 0; s2 <= x; ++s2) {  // x later: pairs (x, s)
         const float u = __expf(gx - sG[s2 * QC + cl]) * sK[s2 * QC + cl];
-        const float al = s2 < x ? sT[x][s2] * bx : 0.0f;
-        const float pi = sDP[x][s2];
-        dkx = fmaf(al, u, dkx);
-        dqx = fmaf(pi, u, dqx);
-        dgx = fmaf(al * kx + pi * qx, u, dgx);
+        sum_at = fmaf(sT[x][s2], u, sum_at);
+        sum_p = fmaf(sDP[x][s2], u, sum_p);
       }
+      dkx += sum_at;
+      dqx += sum_p;
+      dgx += sum_at * kx + sum_p * qx;
+      float sum_e = 0.0f;
 #pragma unroll 4
       for (int r = x; r < Lc; ++r) {  // x earlier: pairs (r, x)
         const float w = __expf(sG[r * QC + cl] - gx);
-        const float al = x < r ? sT[r][x] * sB[r] : 0.0f;
-        const float phi = al * sK[r * QC + cl] + sDP[r][x] * sQ[r * QC + cl];
-        dkx = fmaf(phi, w, dkx);
-        dgx = fmaf(-phi * w, kx, dgx);
+        const float phi = sT[r][x] * sK[r * QC + cl] + sDP[r][x] * sQ[r * QC + cl];
+        sum_e = fmaf(phi, w, sum_e);
       }
+      dkx += sum_e;
+      dgx -= sum_e * kx;
       dq[tok(x, cc)] = dqx;
       dk[tok(x, cc)] = dkx;
       sc[Scr::DX + x * D + cc] = dgx;  // dgamma, summed below
