@@ -247,13 +247,19 @@ __global__ void __launch_bounds__(NT, 2) bwd_prep_kernel(const void* __restrict_
   }
   __syncthreads();
   auto Gf = [&](int r, int cc) { return im[Rec::G + r * D + cc]; };
-  {  // At and P: thread t owns the pairs (r, s) = e / 64, e % 64 for e = t + 256 u
+  {  // At and P over the strictly lower pairs, folded so that no lane idles:
+     // wave w, step u takes the rows lo = w + 4u and hi = 63 - lo (lo + hi = 63
+     // pairs s < r between them); lane l < lo takes (lo, l), lanes lo .. 62
+     // take (hi, l - lo), and lane 63 the two diagonal entries of P (q_r . k_r,
+     // the decay over zero tokens being 1; At is 0 on the diagonal).
     float* sK = sS;
     float* sQ = sS + C * (CS + 1);
     float* sG = sS + 2 * C * (CS + 1);
-    float a[16], pp[16];
+    constexpr int NU = C / 2 / (NT / 64);  // row pairs per wave
+    const int l = t & 63, w = t >> 6;
+    float a[NU], pp[NU];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) a[u] = pp[u] = 0.0f;
+    for (int u = 0; u < NU; ++u) a[u] = pp[u] = 0.0f;
     // slab c0 is read into registers while the previous one is in use
     constexpr int PS = C * CS / NT;
     float rk[PS], rq[PS], rg[PS];
@@ -278,9 +284,10 @@ __global__ void __launch_bounds__(NT, 2) bwd_prep_kernel(const void* __restrict_
       __syncthreads();
       if (c0 + CS < D) fetch_slab(c0 + CS);
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const int e = t + NT * u, r = e / C, s2 = e % C;
-        if (s2 <= r) {
+      for (int u = 0; u < NU; ++u) {
+        const int lo = w + 4 * u, hi = C - 1 - lo;
+        if (l < C - 1) {
+          const int r = l < lo ? lo : hi, s2 = l < lo ? l : l - lo;
 #pragma unroll
           for (int ch = 0; ch < CS; ++ch) {
             const float ks = sK[s2 * (CS + 1) + ch] *
@@ -288,18 +295,38 @@ __global__ void __launch_bounds__(NT, 2) bwd_prep_kernel(const void* __restrict_
             a[u] = fmaf(sK[r * (CS + 1) + ch], ks, a[u]);
             pp[u] = fmaf(sQ[r * (CS + 1) + ch], ks, pp[u]);
           }
+        } else {
+#pragma unroll
+          for (int ch = 0; ch < CS; ++ch) {
+            a[u] = fmaf(sQ[lo * (CS + 1) + ch], sK[lo * (CS + 1) + ch], a[u]);
+            pp[u] = fmaf(sQ[hi * (CS + 1) + ch], sK[hi * (CS + 1) + ch], pp[u]);
+          }
         }
       }
       __syncthreads();
     }
+    // each lower pair (r, s) also writes the zero of its mirror (s, r)
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int e = t + NT * u, r = e / C, s2 = e % C;
-      const float av = s2 < r ? a[u] : 0.0f, pv = s2 <= r ? pp[u] : 0.0f;
-      sA[r][s2] = av;
-      sP[r][s2] = pv;
-      im[Rec::AT + e] = av;
-      im[Rec::P + e] = pv;
+    for (int u = 0; u < NU; ++u) {
+      const int lo = w + 4 * u, hi = C - 1 - lo;
+      if (l < C - 1) {
+        const int r = l < lo ? lo : hi, s2 = l < lo ? l : l - lo;
+        sA[r][s2] = a[u];
+        sP[r][s2] = pp[u];
+        sA[s2][r] = 0.0f;
+        sP[s2][r] = 0.0f;
+        im[Rec::AT + r * C + s2] = a[u];
+        im[Rec::P + r * C + s2] = pp[u];
+        im[Rec::AT + s2 * C + r] = 0.0f;
+        im[Rec::P + s2 * C + r] = 0.0f;
+      } else {
+        sA[lo][lo] = sA[hi][hi] = 0.0f;
+        sP[lo][lo] = a[u];
+        sP[hi][hi] = pp[u];
+        im[Rec::AT + lo * C + lo] = im[Rec::AT + hi * C + hi] = 0.0f;
+        im[Rec::P + lo * C + lo] = a[u];
+        im[Rec::P + hi * C + hi] = pp[u];
+      }
     }
   }
   __syncthreads();
