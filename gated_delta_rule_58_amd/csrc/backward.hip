@@ -472,17 +472,22 @@ __global__ void __launch_bounds__(NT, 2) bwd_walk_kernel(
 #pragma unroll
       for (int j = 0; j < 4; ++j) R[i][j] *= ec;
     }
+    // as three products whose operand reads have no branch of their own (a
+    // branch per element made every operand load wait alone)
     const float* A2 = im + (fwd ? Rec::KD : Rec::W);
     const float* A3 = im + (fwd ? Rec::KD : Rec::QT);
     gemm_staged<8, 4, false, true>(
-        R, 2 * C, sS,
-        [&](int cr, int kk) { return kk < C ? A2[kk * D + cr] : A3[(kk - C) * D + cr]; },
-        [&](int kk, int j) {
-          if (kk < C) return -sZ[kk][j];
-          const int r = kk - C;
-          if (fwd) return im[Rec::U + r * D + 64 * tile + j];
-          return row_at<DOB>(rdo, HDi, r, 64 * tile + j);
-        });
+        R, C, sS, [&](int cr, int kk) { return A2[kk * D + cr]; },
+        [&](int kk, int j) { return -sZ[kk][j]; });
+    if (fwd) {
+      gemm_staged<8, 4, false, true>(
+          R, C, sS, [&](int cr, int kk) { return A3[kk * D + cr]; },
+          [&](int kk, int j) { return im[Rec::U + kk * D + 64 * tile + j]; });
+    } else {
+      gemm_staged<8, 4, false, true>(
+          R, C, sS, [&](int cr, int kk) { return A3[kk * D + cr]; },
+          [&](int kk, int j) { return row_at<DOB>(rdo, HDi, kk, 64 * tile + j); });
+    }
   }
   float* R_end = fwd ? nullptr : dS0;
   if (R_end) {
