@@ -7,7 +7,7 @@ The library computes the gradient in fp32 through the chunk identities: sums
 of at most 256 products per element (unit roundoff 2^-24 = 6e-8, so about
 1e-6 for a length-256 sum of terms of like size) and a walk of up to 64
 chunk steps at T=4096 in which each step contracts the carried gradient;
-the observed error is 2e-6 .. 7e-6 x RMS, and 1e-4 leaves a margin of 15x
+the observed error is 1e-6 .. 8e-6 x RMS, and 1e-4 leaves a margin of 12x
 while still failing any dropped term (which shows up at O(1e-2) or more).
 """
 import numpy as np
