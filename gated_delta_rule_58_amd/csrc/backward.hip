@@ -144,6 +144,89 @@ __device__ __forceinline__ void gemm_staged(float (&acc)[TM][TN], int K, float* 
       for (int v = 0; v < 4; ++v) acc[4 * i + v][j] = ct[i][j][v];
 }
 constexpr int STAGE_FLOATS = KT * (64 + 17) + KT * (128 + 17);  // the largest product's slabs
+// gemm_staged with two slabs in flight, for kernels with the registers to
+// spare: slab k0 + 2 KT is read into registers while slab k0 is used, and
+// the barriers order LDS only, so those loads stay in flight across them (a
+// __syncthreads fence would wait for them at every slab).  With one slab in
+// flight each slab costs about one memory latency, the products being short.
+// K, always 64 or 128, is a multiple of 2 KT; a caller orders any global
+// data it wrote before the call itself.
+template <int TM, int TN, bool A_KC, bool B_NC, typename FA, typename FB>
+__device__ __forceinline__ void gemm_staged2(float (&acc)[TM][TN], int K, float* stage, FA a,
+                                             FB b) {
+  constexpr int M = 16 * TM, N = 16 * TN, MS = M + 17, NS = N + 17;
+  float* sa = stage;
+  float* sb = stage + KT * MS;
+  constexpr int PA = M * KT / NT, PB = N * KT / NT;
+  static_assert(TM % 4 == 0, "whole 16-row tiles per wave");
+  const int t = threadIdx.x;
+  float ra[2][PA], rb[2][PB];
+  auto fetch = [&](int k0, int sl) {
+#pragma unroll
+    for (int u = 0; u < PA; ++u) {
+      const int e = t + NT * u;
+      const int m = A_KC ? e / KT : e % M, kt = A_KC ? e % KT : e / M;
+      ra[sl][u] = a(m, k0 + kt);
+    }
+#pragma unroll
+    for (int u = 0; u < PB; ++u) {
+      const int e = t + NT * u;
+      const int n = B_NC ? e % N : e / KT, kt = B_NC ? e / N : e % KT;
+      rb[sl][u] = b(k0 + kt, n);
+    }
+  };
+  constexpr int TR = TM / 4;
+  f32x4 ct[TR][TN];
+#pragma unroll
+  for (int i = 0; i < TR; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+      ct[i][j] = f32x4{acc[4 * i][j], acc[4 * i + 1][j], acc[4 * i + 2][j], acc[4 * i + 3][j]};
+  fetch(0, 0);
+  fetch(KT, 1);
+  for (int k0 = 0; k0 < K; k0 += 2 * KT) {
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl) {
+#pragma unroll
+      for (int u = 0; u < PA; ++u) {
+        const int e = t + NT * u;
+        const int m = A_KC ? e / KT : e % M, kt = A_KC ? e % KT : e / M;
+        sa[kt * MS + m] = ra[sl][u];
+      }
+#pragma unroll
+      for (int u = 0; u < PB; ++u) {
+        const int e = t + NT * u;
+        const int n = B_NC ? e % N : e / KT, kt = B_NC ? e / N : e % KT;
+        sb[kt * NS + n] = rb[sl][u];
+      }
+      barrier_lds();
+      if (k0 + (2 + sl) * KT < K) fetch(k0 + (2 + sl) * KT, sl);
+      // the fp32 16x16x4 MFMA fragments of gemm_staged
+      const int lane = t & 63, w = t >> 6, lr = lane & 15, lq = lane >> 4;
+#pragma unroll
+      for (int kg = 0; kg < KT / 4; ++kg) {
+        const int kk = 4 * kg + lq;
+        float av[TR], bv[TN];
+#pragma unroll
+        for (int i = 0; i < TR; ++i) av[i] = sa[kk * MS + 16 * (TR * w + i) + lr];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) bv[j] = sb[kk * NS + 16 * j + lr];
+#pragma unroll
+        for (int i = 0; i < TR; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            ct[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[i], bv[j], ct[i][j], 0, 0, 0);
+      }
+      barrier_lds();
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < TR; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[4 * i + v][j] = ct[i][j][v];
+}
 
 // Output element of acc[i][j] after gemm_staged<TM, TN>: row orow<TM>(i),
 // column ocol(j).
@@ -455,7 +538,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_walk_kernel(
       const float* A1 = im + (fwd ? Rec::W : Rec::KD);
       float z[4][4];
       zero(z);
-      gemm_staged<4, 4, true, true>(z, D, sS,
+      gemm_staged2<4, 4, true, true>(z, D, sS,
                                     [&](int r, int cc) { return A1[r * D + cc]; },
                                     [&](int cc, int j) { return sR[cc][j]; });
 #pragma unroll
@@ -476,15 +559,15 @@ __global__ void __launch_bounds__(NT, 2) bwd_walk_kernel(
     // branch per element made every operand load wait alone)
     const float* A2 = im + (fwd ? Rec::KD : Rec::W);
     const float* A3 = im + (fwd ? Rec::KD : Rec::QT);
-    gemm_staged<8, 4, false, true>(
+    gemm_staged2<8, 4, false, true>(
         R, C, sS, [&](int cr, int kk) { return A2[kk * D + cr]; },
         [&](int kk, int j) { return -sZ[kk][j]; });
     if (fwd) {
-      gemm_staged<8, 4, false, true>(
+      gemm_staged2<8, 4, false, true>(
           R, C, sS, [&](int cr, int kk) { return A3[kk * D + cr]; },
           [&](int kk, int j) { return im[Rec::U + kk * D + 64 * tile + j]; });
     } else {
-      gemm_staged<8, 4, false, true>(
+      gemm_staged2<8, 4, false, true>(
           R, C, sS, [&](int cr, int kk) { return A3[kk * D + cr]; },
           [&](int kk, int j) { return row_at<DOB>(rdo, HDi, kk, 64 * tile + j); });
     }
