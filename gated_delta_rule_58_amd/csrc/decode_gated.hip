@@ -16,10 +16,12 @@
 // indices are given; a slot outside [0, num_slots) skips the sequence: its o
 // is written as zeros and no state is touched.
 //
-// HBM-bound like decode.hip: one 512-thread workgroup handles consecutive
-// (sequence, head) pairs, two with fp32 states, four with bf16 states; the
-// next pair's loads are issued before a pair's stores, and every wave-wide
-// state access is 1 KiB contiguous.
+// HBM-bound like decode.hip: one 512-thread workgroup handles two
+// consecutive (sequence, head) pairs with fp32 states (the second pair's
+// loads are issued before the first pair's stores) and one pair with bf16
+// states (two workgroups per CU then keep more pairs in flight than the
+// in-workgroup pipeline did); every wave-wide state access is 1 KiB
+// contiguous.
 // fp32 states: thread t holds 4 columns (4*(t%32)..) of the 8 key rows
 // t/32 + 16 i; bf16 states: 8 columns (8*(t%16)..) of the 4 rows t/16 + 32 i.
 // The column sums kS = S'^T k and qS = S'^T q run over a thread's rows, the
@@ -46,7 +48,8 @@ __global__ void __launch_bounds__(NTHR, 4) decode_gated_kernel(
     const float* __restrict__ A_log, const float* __restrict__ dt_bias, void* __restrict__ pool,
     const int32_t* __restrict__ slots, int64_t num_slots, void* __restrict__ o, float scale,
     int64_t pairs, int H, int alog_pc) {
-  constexpr int PAIRS = S_BF16 ? 4 : 2;  // pairs per workgroup
+  // pairs per workgroup (bf16: 2 -> 1 took the 256 x 96 step 0.287 -> 0.266 ms)
+  constexpr int PAIRS = S_BF16 ? 1 : 2;
   constexpr int CPT = S_BF16 ? 8 : 4;  // columns per thread
   constexpr int NCG = D / CPT;         // column groups
   constexpr int NRS = NTHR / NCG;      // row slots
@@ -270,7 +273,7 @@ hipError_t launch_decode_gated(const void* q, const void* k, const void* v, bool
                                bool o_bf16, int N, int H, float scale, hipStream_t s) {
   const int64_t pairs = (int64_t)N * H;
   if (pairs == 0) return hipSuccess;
-  const int64_t per_block = state_bf16 ? 4 : 2;  // the kernel's PAIRS
+  const int64_t per_block = state_bf16 ? 1 : 2;  // the kernel's PAIRS
   const int64_t blocks = (pairs + per_block - 1) / per_block;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(blocks));
