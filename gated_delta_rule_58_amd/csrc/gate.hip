@@ -7,7 +7,7 @@
 // (Model-Optimizer PR #2749 review, KDA beta fix).
 //
 // Work split: blockIdx.y picks a group of R = 256 / (d/4) heads, blockIdx.x a
-// run of tokens.  A thread owns one (head, 4-channel) slot for the whole run,
+// run of 32 tokens.  A thread owns one (head, 4-channel) slot for the whole run,
 // so its -exp(A_log) and dt_bias quads are formed once and every token costs
 // one 16-byte load of x and one 16-byte store of g.  A wave covers 256
 // consecutive channels of one token: fully coalesced.  beta for the block's
@@ -22,20 +22,21 @@ namespace kda {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kTokUnroll = 4;   // x loads in flight per thread
+constexpr int kTokUnroll = 8;   // x loads per group; two groups in flight per thread
 constexpr int kTokPerBlock = 32;
 
-// 4 consecutive logits as fp32, read once: non-temporal, so the stream of x
-// does not displace the cached lines of g that the prefill reads next.
+// 4 consecutive logits of token t of the run through the run's buffer (rows
+// past the run read 0), as raw bits: widened only where used.
 template <bool BF16>
-__device__ __forceinline__ f32x4 load4_stream(const void* base, int64_t idx) {
-  if constexpr (BF16) {
-    const u16x4 r = __builtin_nontemporal_load(reinterpret_cast<const u16x4*>(
-        static_cast<const uint16_t*>(base) + idx));
-    return f32x4{bf16_bits_to_f32(r[0]), bf16_bits_to_f32(r[1]), bf16_bits_to_f32(r[2]),
-                 bf16_bits_to_f32(r[3])};
-  }
-  return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(static_cast<const float*>(base) + idx));
+struct X4 {
+  typedef typename Raw<BF16>::T4 T;
+};
+template <bool BF16>
+__device__ __forceinline__ typename X4<BF16>::T load_x4(__amdgpu_buffer_rsrc_t r, int off) {
+  if constexpr (BF16)
+    return __builtin_bit_cast(u16x4, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kBufNT));
+  else
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kBufNT));
 }
 
 template <bool XBF16, bool BBF16>
@@ -57,24 +58,44 @@ __global__ void __launch_bounds__(kThreads) gate_kernel(
 #pragma unroll
     for (int e = 0; e < 4; ++e) a[e] = -expf(alog_pc ? A_log[(int64_t)h * d + c + e] : A_log[h]);
     const f32x4 db = *reinterpret_cast<const f32x4*>(dt_bias + (int64_t)h * d + c);
-    const int64_t base = (int64_t)tok0 * tok_stride + (int64_t)h * d + c;
-    for (int t = 0; t < ntk; t += kTokUnroll) {
-      f32x4 xv[kTokUnroll];
+    // The run's x and g as buffers over its ntk tokens: every load and store
+    // runs on every path (x past the run reads 0, g past it is dropped), so
+    // the loads of a group stay in flight together and the next group's go
+    // out before this group's arithmetic (a branch per token made each load
+    // wait for the one before it).  x is read once: non-temporal.
+    // (the buffers start at the run's first token, the same for every lane, so
+    // the resource stays in scalar registers; a lane's channels are an offset)
+    constexpr int XS = XBF16 ? 2 : 4;
+    const int stride_b = static_cast<int>(tok_stride);  // elements per token
+    const int lane_off = h * d + c;
+    const uint32_t span = static_cast<uint32_t>((int64_t)ntk * tok_stride);
+    const auto rx = buffer_over(static_cast<const char*>(x) + (int64_t)tok0 * tok_stride * XS,
+                                span * XS);
+    const auto rg = buffer_over(g + (int64_t)tok0 * tok_stride, span * 4);
+    typename X4<XBF16>::T xa[kTokUnroll], xb[kTokUnroll];
+    auto load_group = [&](int t0, typename X4<XBF16>::T* xv) {
 #pragma unroll
       for (int u = 0; u < kTokUnroll; ++u)
-        if (t + u < ntk) xv[u] = load4_stream<XBF16>(x, base + (t + u) * tok_stride);
+        xv[u] = load_x4<XBF16>(rx, ((t0 + u) * stride_b + lane_off) * XS);
+    };
+    auto run_group = [&](int t0, typename X4<XBF16>::T* xv) {
 #pragma unroll
       for (int u = 0; u < kTokUnroll; ++u) {
-        if (t + u < ntk) {
-          f32x4 out;
+        const f32x4 xf = widen4<XBF16>(xv[u]);
+        f32x4 out;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float z = gate_input(xv[u][e], db[e]);
-            out[e] = gate_log_decay(a[e], z);
-          }
-          *reinterpret_cast<f32x4*>(g + base + (t + u) * tok_stride) = out;
-        }
+        for (int e = 0; e < 4; ++e) out[e] = gate_log_decay(a[e], gate_input(xf[e], db[e]));
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, out), rg,
+                                               ((t0 + u) * stride_b + lane_off) * 4, 0, 0);
       }
+    };
+    load_group(0, xa);
+#pragma unroll
+    for (int t = 0; t < kTokPerBlock; t += 2 * kTokUnroll) {
+      load_group(t + kTokUnroll, xb);
+      run_group(t, xa);
+      if (t + 2 * kTokUnroll < kTokPerBlock) load_group(t + 2 * kTokUnroll, xa);
+      run_group(t + kTokUnroll, xb);
     }
   }
 
