@@ -29,6 +29,26 @@ def test_gate_parity(xdt):
     assert np.all(g_gpu <= 0)
 
 
+def test_gate_writes_stop_at_the_last_token():
+    """A partial last token run (777 = 24 * 32 + 9) writes g and beta for its
+    9 tokens only: the memory after them keeps its contents."""
+    need_gpu()
+    say("gate bounds")
+    dr = draw_prefill([777], H=96, dtype=torch.bfloat16, seed=29)
+    T, H, d = dr.x.shape
+    n, nb = T * H * d, T * H
+    sentinel = 7.0
+    gbuf = torch.full((n + 2 * H * d,), sentinel, dtype=torch.float32, device=DEV)
+    bbuf = torch.full((nb + 2 * H,), sentinel, dtype=torch.float32, device=DEV)
+    g, beta = kda.gate(dr.x.to(DEV), dr.b.to(DEV), dr.A_log.to(DEV), dr.dt_bias.to(DEV),
+                       g_out=gbuf[:n].view(T, H, d), beta_out=bbuf[:nb].view(T, H))
+    torch.cuda.synchronize()
+    assert torch.all(gbuf[n:] == sentinel) and torch.all(bbuf[nb:] == sentinel)
+    g_ref, b_ref = oracle.gate(dr.x, dr.b, dr.A_log, dr.dt_bias)
+    assert np.all(np.abs(to64(g) - g_ref) <= 1e-5 * np.abs(g_ref) + 1e-30)
+    assert np.max(np.abs(to64(beta) - b_ref)) <= 1e-6
+
+
 def test_gate_extreme_logits():
     """Large |x + dt_bias| and |b| stay finite and match the asymptotes."""
     need_gpu()
