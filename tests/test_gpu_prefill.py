@@ -1,9 +1,11 @@
 """GPU parity of kda_chunk_prefill against the fp64 oracle.
 
 Small cases feed both sides the same fp32 g/beta (from the oracle gate).  The
-full-size workloads run the HIP gate then the HIP prefill in the launch
-configuration the bench times, and compare sampled heads (heads are
-independent) against the oracle gate then the oracle recurrence.
+full-size workloads run the gated prefill in the one-pass launch
+configuration the bench times, and kda_gate then kda_chunk_prefill through
+the binding's capped workspace, both with an fp32 output held to the stated
+bound, and compare sampled heads (heads are independent) against the oracle
+gate then the oracle recurrence.
 """
 import numpy as np
 import pytest
@@ -40,6 +42,7 @@ def _check_small(lengths, H, qdt, init, seed, scale=1.0):
     es = assert_state(S32, S_ref, str(lengths))
     ob, Sb = _run_gpu(dr, g, beta, torch.bfloat16, scale, dr.initial_state)
     assert_out_bf16(ob, o_ref, str(lengths))
+    assert torch.equal(ob, o32.to(torch.bfloat16)), "bf16 o is not RNE(fp32 o)"
     assert torch.equal(Sb, S32)
     return eo, es
 
@@ -164,24 +167,62 @@ def test_in_place_state_and_determinism():
     assert torch.equal(o1, o3) and torch.equal(S1, st)
 
 
+def _one_pass_workspace(cu_h, H):
+    """Workspace that holds every chunk of the longest sequence: one pass, the
+    launch configuration the bench times."""
+    lens = (cu_h[1:] - cu_h[:-1]).clamp(min=0)
+    chunks = max(1, (int(lens.max()) + 63) // 64)
+    nb = kda.chunk_prefill_workspace_bytes(cu_h.numel() - 1, H, 128, 128, chunks)
+    return torch.empty(nb, dtype=torch.uint8, device=DEV)
+
+
 def _full_config(idx, n_heads, seed):
+    """Workload idx at full size, on sampled heads against the oracle gate and
+    recurrence, at the stated tolerances on an fp32 output:
+      (1) kda_chunk_prefill_gated in one pass with the whole workspace (the
+          call the bench times), o fp32;
+      (2) the same call with o bf16: bit-for-bit the round-to-nearest-even
+          rounding of (1), and the same final state;
+      (3) kda_gate then kda_chunk_prefill through the binding's default
+          workspace (1 GiB cap: several passes at this size), o fp32."""
     c = CONFIGS[idx]
     say("full config %d (%s), sampled heads" % (idx, c["name"]))
     dr = draw_config(idx, device=DEV)
     cu_h = dr.cu_seqlens
-    g, beta = kda.gate(dr.x, dr.b, dr.A_log, dr.dt_bias)
-    o, S = kda.chunk_prefill(dr.q, dr.k, dr.v, g, beta, cu_h.to(DEV), dr.initial_state,
-                             cu_seqlens_host=cu_h, o_dtype=torch.bfloat16)
+    cu = cu_h.to(DEV)
+    H = c["H"]
+    ws = _one_pass_workspace(cu_h, H)
+    say("  gated one pass, fp32 o, workspace %d bytes" % ws.numel())
+    o32, S32 = kda.chunk_prefill_gated(dr.q, dr.k, dr.v, dr.x, dr.b, dr.A_log, dr.dt_bias, cu,
+                                       dr.initial_state, cu_seqlens_host=cu_h,
+                                       o_dtype=torch.float32, workspace=ws)
+    say("  gated one pass, bf16 o")
+    o16, S16 = kda.chunk_prefill_gated(dr.q, dr.k, dr.v, dr.x, dr.b, dr.A_log, dr.dt_bias, cu,
+                                       dr.initial_state, cu_seqlens_host=cu_h,
+                                       o_dtype=torch.bfloat16, workspace=ws)
     torch.cuda.synchronize()
-    heads = sample_heads(c["H"], n_heads, seed)
+    del ws
+    assert torch.equal(o16, o32.to(torch.bfloat16)), "bf16 o is not RNE(fp32 o)"
+    assert torch.equal(S16, S32)
+    del o16, S16
+    say("  kda_gate + kda_chunk_prefill (binding workspace), fp32 o")
+    g, beta = kda.gate(dr.x, dr.b, dr.A_log, dr.dt_bias)
+    o2, S2 = kda.chunk_prefill(dr.q, dr.k, dr.v, g, beta, cu, dr.initial_state,
+                               cu_seqlens_host=cu_h, o_dtype=torch.float32)
+    torch.cuda.synchronize()
+    del g, beta
+    heads = sample_heads(H, n_heads, seed)
     say("  oracle on heads", heads)
     gr, br = oracle_gate_f64(dr, heads)
     S0 = None if dr.initial_state is None else dr.initial_state[:, heads].cpu()
     o_ref, S_ref = oracle.prefill(dr.q[:, heads].cpu(), dr.k[:, heads].cpu(),
                                   dr.v[:, heads].cpu(), gr, br, cu_h, S0)
-    eo = assert_out_bf16(o[:, heads], o_ref, "config %d" % idx)
-    es = assert_state(S[:, heads], S_ref, "config %d" % idx)
-    say("  bf16-o err ratio %.3f  state err %.3e" % (eo, es))
+    e1 = assert_out(o32[:, heads], o_ref, "config %d gated one pass" % idx)
+    s1 = assert_state(S32[:, heads], S_ref, "config %d gated one pass" % idx)
+    e3 = assert_out(o2[:, heads], o_ref, "config %d gate + prefill" % idx)
+    s3 = assert_state(S2[:, heads], S_ref, "config %d gate + prefill" % idx)
+    say("  fp32-o err / RMS: gated %.3e, gate+prefill %.3e (bound 5e-3); state rel-F: "
+        "gated %.3e, gate+prefill %.3e (bound 1e-3)" % (e1, e3, s1, s3))
 
 
 def test_config1_full_sampled_heads():
@@ -304,24 +345,3 @@ def test_gated_per_channel_alog(xdt):
     o_ref, S_ref = oracle.prefill(dr.q, dr.k, dr.v, gr, br, cu_h, dr.initial_state, scale=0.7)
     assert_out(o, o_ref, "gated per-channel A_log")
     assert_state(S, S_ref, "gated per-channel A_log")
-
-
-def test_config1_gated_full_sampled_heads():
-    """The benchmarked call: K3-layer prefill T=4096 H=96 from the raw gate
-    logits, bf16 o, sampled heads against the oracle gate and recurrence."""
-    need_gpu()
-    c = CONFIGS[1]
-    say("full config 1 gated, sampled heads")
-    dr = draw_config(1, device=DEV)
-    cu_h = dr.cu_seqlens
-    o, S = kda.chunk_prefill_gated(dr.q, dr.k, dr.v, dr.x, dr.b, dr.A_log, dr.dt_bias,
-                                   cu_h.to(DEV), dr.initial_state, cu_seqlens_host=cu_h,
-                                   o_dtype=torch.bfloat16)
-    torch.cuda.synchronize()
-    heads = sample_heads(c["H"], 6, 11)
-    gr, br = oracle_gate_f64(dr, heads)
-    o_ref, S_ref = oracle.prefill(dr.q[:, heads].cpu(), dr.k[:, heads].cpu(),
-                                  dr.v[:, heads].cpu(), gr, br, cu_h, None)
-    eo = assert_out_bf16(o[:, heads], o_ref, "config 1 gated")
-    es = assert_state(S[:, heads], S_ref, "config 1 gated")
-    say("  bf16-o err ratio %.3f  state err %.3e" % (eo, es))
