@@ -27,6 +27,13 @@ constexpr int C = 64;     // chunk length
 constexpr int D = 128;    // dk = dv
 constexpr int NTHR = 256; // 4 waves per workgroup
 constexpr float LOG2E = 1.4426950408889634f;
+// Floor of the per-token log2 decay in the prefill's cumulative sum.  The
+// decay factors are built from references at most 8 tokens away, and 8 x 15.5
+// = 124 keeps every such factor inside fp32 range for any g <= 0.  A floored
+// decay factor is 2^-15.5 (2.2e-5) where the exact one is smaller, so o and
+// the state move by far less than their rounding error (the audit's printed
+// A_log maximum, 2.47, reaches tens of log2 units per token).
+constexpr float DECAY_FLOOR_LOG2 = 15.5f;
 
 __device__ __forceinline__ f32x4 mma_f16(f16x8 a, f16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);

@@ -31,8 +31,10 @@
 // k_s 2^(gamma_b - gamma_s), b = last row of block j: both <= 1 (fp16).  The
 // diagonal tiles multiply E and F, bounded by 8 tokens of decay: plain fp16
 // when every |gamma_r - gamma_m| of the block is <= 7, otherwise hi+lo bf16
-// pairs, which keep fp32 range.  Requirement: no channel decays by more than
-// 126 (log2 units) over 8 consecutive tokens.
+// pairs, which keep fp32 range.  fp32 range needs every 8-token span of one
+// channel's decay below 126 (log2 units): the per-token decay is floored at
+// -DECAY_FLOOR_LOG2 (15.5) before the scan, which keeps the spans at 124 or
+// less for any g <= 0 (NaN passes through unchanged).
 #include <type_traits>
 
 #include "chunk_common.hpp"
@@ -247,6 +249,7 @@ __global__ void __launch_bounds__(NTHR, 3) prep_kernel(
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       float x = GIN == kG ? graw[kk][e >> 2][e & 3] * LOG2E : graw[kk][e >> 2][e & 3];
+      x = x < -DECAY_FLOOR_LOG2 ? -DECAY_FLOOR_LOG2 : x;
       x = add_row_shr<1>(x);
       x = add_row_shr<2>(x);
       x = add_row_shr<4>(x);

@@ -260,6 +260,49 @@ def test_strong_decay_heads():
     assert_state(S, S_ref, "strong decay")
 
 
+A_LOG_MAX, DT_BIAS_MAX = 2.4661, 0.1792   # artifact audit §5.1, the printed maxima
+
+
+@pytest.mark.parametrize("mode", ["g", "gated", "gated_per_channel"])
+def test_printed_extreme_decay(mode):
+    """Decay at the artifact audit's printed parameter extremes (§5.1: A_log up
+    to 2.4661, dt_bias up to 0.1792), where a single token can decay a channel
+    by tens of log2 units: every channel of head 0 and half the channels of
+    head 1 at both maxima, head 3 at A_log 1.0, head 2 at the median; or, per
+    channel, A_log [H, d] ~ U(-0.75, 2.4661) with dt_bias at its maximum on
+    every other channel.  Varlen with an initial state; fp32 o at the stated
+    bounds, every value finite."""
+    need_gpu()
+    dr = draw_prefill([300, 77, 129], H=4, dtype=torch.bfloat16, init_state=True, seed=43)
+    dt = dr.dt_bias.clone()
+    if mode == "gated_per_channel":
+        A = torch.rand(4, 128, generator=torch.Generator().manual_seed(44)) * (A_LOG_MAX + 0.75) - 0.75
+        A[:, 0] = A_LOG_MAX
+        dt[:, ::2] = DT_BIAS_MAX
+    else:
+        A = torch.tensor([A_LOG_MAX, A_LOG_MAX, -0.1533, 1.0])
+        dt[0] = DT_BIAS_MAX
+        dt[1, :64] = DT_BIAS_MAX
+    dr.A_log, dr.dt_bias = A, dt
+    say("printed extreme decay", mode)
+    gr, br = oracle.gate(dr.x, dr.b, A, dt)
+    o_ref, S_ref = oracle.prefill(dr.q, dr.k, dr.v, gr, br, dr.cu_seqlens, dr.initial_state)
+    cu_h = dr.cu_seqlens
+    if mode == "g":
+        g, beta = oracle_gate_f32(dr)
+        o, S = _run_gpu(dr, g, beta, torch.float32, S0=dr.initial_state)
+    else:
+        o, S = kda.chunk_prefill_gated(dr.q.to(DEV), dr.k.to(DEV), dr.v.to(DEV), dr.x.to(DEV),
+                                       dr.b.to(DEV), A.to(DEV), dt.to(DEV), cu_h.to(DEV),
+                                       dr.initial_state.to(DEV), cu_seqlens_host=cu_h,
+                                       o_dtype=torch.float32)
+        torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and torch.isfinite(S).all()
+    eo = assert_out(o, o_ref, "extreme decay " + mode)
+    es = assert_state(S, S_ref, "extreme decay " + mode)
+    say("  o err / RMS %.3e, state rel-F %.3e" % (eo, es))
+
+
 def test_multi_pass_workspace():
     """A workspace smaller than the longest sequence's chunk count runs the
     chunk axis in passes (state carried through final_state, or through the
