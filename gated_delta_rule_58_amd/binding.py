@@ -11,7 +11,7 @@ KDA_F32 = 0
 KDA_BF16 = 1
 _STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARG", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_DTYPE",
            4: "KDA_ERR_UNSUPPORTED", 5: "KDA_ERR_ALIGNMENT", 6: "KDA_ERR_WORKSPACE",
-           7: "KDA_ERR_LAUNCH"}
+           7: "KDA_ERR_LAUNCH", 8: "KDA_ERR_DOMAIN", 9: "KDA_ERR_NONFINITE"}
 # default cap on the prefill workspace the binding allocates (the chunk axis is
 # processed in passes when a batch needs more)
 DEFAULT_WORKSPACE_BYTES = 1 << 30
@@ -60,8 +60,9 @@ def lib():
         L.kda_chunk_prefill_gated.restype = ctypes.c_int
         L.kda_chunk_prefill_gated.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, ctypes.c_int, _vp,
                                               ctypes.c_int, _vp, _i64, _vp, _i64, _vp, _vp, _i32,
-                                              _vp, _vp, _vp, ctypes.c_int, _i64, _i32, _i32, _i32,
-                                              ctypes.c_float, _vp, ctypes.c_size_t, _vp]
+                                              _vp, _vp, ctypes.c_int, _i64, _vp, _vp, ctypes.c_int,
+                                              _i64, _i32, _i32, _i32, ctypes.c_float, _vp,
+                                              ctypes.c_size_t, _vp]
         L.kda_chunk_prefill_workspace_bytes.restype = ctypes.c_size_t
         L.kda_chunk_prefill_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32, _i32]
         L.kda_recurrent_decode_gated.restype = ctypes.c_int
@@ -161,7 +162,8 @@ def chunk_prefill_workspace_bytes(N: int, H: int, dk: int = 128, dv: int = 128,
 
 
 def _prefill_common(q, v, cu_seqlens, cu_seqlens_host, initial_state, output_final_state,
-                    o_dtype, out, final_state, workspace, max_workspace_bytes):
+                    o_dtype, out, final_state, workspace, max_workspace_bytes,
+                    state_dtype=torch.float32):
     T, H, dk = q.shape
     dv = v.shape[2]
     dev = q.device
@@ -177,7 +179,7 @@ def _prefill_common(q, v, cu_seqlens, cu_seqlens_host, initial_state, output_fin
     if out is None:
         out = torch.empty((T, H, dv), dtype=o_dtype, device=dev)
     if final_state is None and output_final_state:
-        final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+        final_state = torch.empty((N, H, dk, dv), dtype=state_dtype, device=dev)
     hp = cu_seqlens_host.contiguous()
     if workspace is None:
         lens = (hp[1:] - hp[:-1]).clamp(min=0)
@@ -225,19 +227,46 @@ def chunk_prefill_gated(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, x: to
                         final_state: Optional[torch.Tensor] = None,
                         cu_seqlens_host: Optional[torch.Tensor] = None,
                         workspace: Optional[torch.Tensor] = None,
-                        max_workspace_bytes: int = DEFAULT_WORKSPACE_BYTES):
+                        max_workspace_bytes: int = DEFAULT_WORKSPACE_BYTES,
+                        state_indices: Optional[torch.Tensor] = None,
+                        state_dtype: Optional[torch.dtype] = None):
     """kda_chunk_prefill_gated: the gate's raw inputs (x [T,H,dk] logits, b [T,H]
-    beta logits, A_log [H] or [H,dk], dt_bias [H,dk]) instead of g and beta."""
+    beta logits, A_log [H] or [H,dk], dt_bias [H,dk]) instead of g and beta.
+
+    States are float32 or bfloat16 (state_dtype; default: initial_state's dtype,
+    else float32).  Without state_indices they are [N,H,dk,dv] per sequence and a
+    final state is allocated when output_final_state is set and none is given.
+    With state_indices ([N] int32 on the device) initial_state and final_state
+    are pools [num_slots,H,dk,dv] (final_state may be initial_state: an in-place
+    update; it is written only when passed), and sequence n uses slot
+    state_indices[n]; a slot outside the pool starts from zeros and is not
+    written."""
+    if state_dtype is None:
+        state_dtype = initial_state.dtype if initial_state is not None else (
+            final_state.dtype if final_state is not None else torch.float32)
+    if state_indices is not None:
+        if state_indices.dtype != torch.int32:
+            raise TypeError("state_indices must be int32")
+        output_final_state = False  # a pool is written only when passed as final_state
     T, H, dk, dv, dev, cu_seqlens, hp, N, out, final_state, workspace = _prefill_common(
         q, v, cu_seqlens, cu_seqlens_host, initial_state, output_final_state, o_dtype, out,
-        final_state, workspace, max_workspace_bytes)
+        final_state, workspace, max_workspace_bytes, state_dtype)
+    for t in (initial_state, final_state):
+        if t is not None and t.dtype != state_dtype:
+            raise TypeError("initial_state and final_state must both be %s" % state_dtype)
+    pools = [t for t in (initial_state, final_state) if t is not None]
+    num_slots = pools[0].shape[0] if pools else N
+    if any(t.shape[0] != num_slots for t in pools):
+        raise ValueError("initial_state and final_state must have the same number of slots")
     A_log = _alog(A_log, H, dk)
     dt_bias = dt_bias.contiguous()
     st = lib().kda_chunk_prefill_gated(
         _ptr(q), _ptr(k), _ptr(v), _dt(q), _ptr(x), _dt(x), _ptr(b), _dt(b), _ptr(A_log),
         A_log.numel(), _ptr(dt_bias), dt_bias.numel(), _ptr(cu_seqlens),
-        ctypes.cast(hp.data_ptr(), _vp), N, _ptr(initial_state), _ptr(final_state), _ptr(out),
-        _dt(out), T, H, dk, dv, float(scale), _ptr(workspace), workspace.numel(), _stream(dev))
+        ctypes.cast(hp.data_ptr(), _vp), N, _ptr(initial_state), _ptr(final_state),
+        KDA_BF16 if state_dtype == torch.bfloat16 else KDA_F32, num_slots, _ptr(state_indices),
+        _ptr(out), _dt(out), T, H, dk, dv, float(scale), _ptr(workspace), workspace.numel(),
+        _stream(dev))
     _check(st)
     return out, final_state
 

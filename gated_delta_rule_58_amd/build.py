@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkda.so")
-SOURCES = ["api.hip", "gate.hip", "decode.hip", "decode_gated.hip", "prefill.hip", "prep.hip",
+SOURCES = ["api.hip", "debug.hip", "gate.hip", "decode.hip", "decode_gated.hip", "prefill.hip", "prep.hip",
            "state.hip", "shortconv.hip", "backward.hip"]
 ARCH = os.environ.get("KDA_OFFLOAD_ARCH", "gfx950")
 

@@ -48,6 +48,44 @@ kda_status launched(hipError_t e, const char* what) {
   return ok();
 }
 
+// Runs a call's launches (`run`).  With KDA_DEBUG=1 `pre` first adds the scans
+// of its inputs (a failure returns KDA_ERR_DOMAIN before `run`), and `post`
+// the scans of its outputs after it (KDA_ERR_NONFINITE); the call then waits
+// for its stream.
+template <class Pre, class Run, class Post>
+kda_status run_checked(const char* fn, hipStream_t s, Pre pre, Run run, Post post) {
+  if (!kda::dbg::enabled()) return launched(run(), fn);
+  std::lock_guard<std::mutex> lock(kda::dbg::mutex());
+  kda::dbg::Session ses(s);
+  std::string rep;
+  hipError_t e = ses.begin();
+  if (e == hipSuccess) {
+    pre(ses);
+    e = ses.finish(&rep);
+  }
+  if (e != hipSuccess)
+    return fail(KDA_ERR_LAUNCH, "%s (KDA_DEBUG): input scan failed: %s", fn, hipGetErrorString(e));
+  if (!rep.empty())
+    return fail(KDA_ERR_DOMAIN, "%s (KDA_DEBUG): %s; nothing was launched", fn, rep.c_str());
+  e = run();
+  if (e != hipSuccess) return launched(e, fn);
+  e = ses.begin();
+  if (e == hipSuccess) {
+    post(ses);
+    e = ses.finish(&rep);
+  }
+  if (e != hipSuccess)
+    return fail(KDA_ERR_LAUNCH, "%s (KDA_DEBUG): output scan failed: %s", fn,
+                hipGetErrorString(e));
+  if (!rep.empty()) return fail(KDA_ERR_NONFINITE, "%s (KDA_DEBUG): %s", fn, rep.c_str());
+  return ok();
+}
+
+using kda::dbg::kFinite;
+using kda::dbg::kNonPositive;
+using kda::dbg::kNotNaN;
+using kda::dbg::kUnit;
+
 }  // namespace
 
 extern "C" {
@@ -82,10 +120,25 @@ kda_status kda_gate(const void* x, kda_dtype x_dt, const void* b, kda_dtype b_dt
   if (!aligned(x, x_dt == KDA_BF16 ? 8 : 16) || !aligned(g_out, 16) || !aligned(dt_bias, 16))
     return fail(KDA_ERR_ALIGNMENT, "kda_gate: x, g_out and dt_bias must be 16-byte aligned "
                                    "(8-byte for bf16 x)");
-  return launched(kda::launch_gate(x, x_dt == KDA_BF16, b, b_dt == KDA_BF16, A_log, alog_pc,
-                                   dt_bias, g_out, beta_out, n_tok, H, d,
-                                   static_cast<hipStream_t>(stream)),
-                  "kda_gate");
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t nx = n_tok * H * d, nb = n_tok * H;
+  const int64_t na = alog_pc ? (int64_t)H * d : H;
+  return run_checked(
+      "kda_gate", s,
+      [&](kda::dbg::Session& c) {
+        c.add("x", x, nx, x_dt == KDA_BF16, kNotNaN);
+        c.add("b", b, nb, b_dt == KDA_BF16, kNotNaN);
+        c.add("A_log", A_log, na, false, kFinite);
+        c.add("dt_bias", dt_bias, (int64_t)H * d, false, kFinite);
+      },
+      [&] {
+        return kda::launch_gate(x, x_dt == KDA_BF16, b, b_dt == KDA_BF16, A_log, alog_pc,
+                                dt_bias, g_out, beta_out, n_tok, H, d, s);
+      },
+      [&](kda::dbg::Session& c) {
+        c.add("g", g_out, nx, false, kNotNaN);
+        c.add("beta", beta_out, nb, false, kNotNaN);
+      });
 }
 
 size_t kda_gate_backward_workspace_bytes(int64_t n_tok, int32_t H, int32_t d) {
@@ -132,11 +185,30 @@ kda_status kda_gate_backward(const void* x, kda_dtype x_dt, const void* b, kda_d
                 need, workspace_bytes);
   if (!aligned(workspace, 16))
     return fail(KDA_ERR_ALIGNMENT, "%s: workspace must be 16-byte aligned", fn);
-  return launched(kda::launch_gate_backward(x, x_dt == KDA_BF16, b, b_dt == KDA_BF16, A_log,
-                                            alog_pc, dt_bias, dg, dbeta, dx, db, dA_log,
-                                            ddt_bias, n_tok, H, d, workspace,
-                                            static_cast<hipStream_t>(stream)),
-                  fn);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t nx = n_tok * H * d, nb = n_tok * H;
+  const int64_t na = alog_pc ? (int64_t)H * d : H;
+  return run_checked(
+      fn, s,
+      [&](kda::dbg::Session& c) {
+        c.add("x", x, nx, x_dt == KDA_BF16, kNotNaN);
+        c.add("b", b, nb, b_dt == KDA_BF16, kNotNaN);
+        c.add("A_log", A_log, na, false, kFinite);
+        c.add("dt_bias", dt_bias, (int64_t)H * d, false, kFinite);
+        c.add("dg", dg, nx, false, kFinite);
+        c.add("dbeta", dbeta, nb, false, kFinite);
+      },
+      [&] {
+        return kda::launch_gate_backward(x, x_dt == KDA_BF16, b, b_dt == KDA_BF16, A_log,
+                                         alog_pc, dt_bias, dg, dbeta, dx, db, dA_log, ddt_bias,
+                                         n_tok, H, d, workspace, s);
+      },
+      [&](kda::dbg::Session& c) {
+        c.add("dx", dx, nx, false, kFinite);
+        c.add("db", db, nb, false, kFinite);
+        c.add("dA_log", dA_log, na, false, kFinite);
+        c.add("ddt_bias", ddt_bias, (int64_t)H * d, false, kFinite);
+      });
 }
 
 }  // extern "C"
@@ -148,7 +220,7 @@ namespace {
 kda_status check_prefill(const char* fn, const void* q, const void* k, const void* v,
                          kda_dtype qkv_dt, const void* decay, size_t decay_al, const void* bb,
                          size_t bb_al, const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
-                         int32_t N, const float* initial_state, const float* final_state,
+                         int32_t N, const void* initial_state, const void* final_state,
                          const void* o, kda_dtype o_dt, int64_t T_tot, int32_t H, int32_t dk,
                          int32_t dv, float scale, const void* workspace, size_t workspace_bytes,
                          bool backward = false) {
@@ -212,12 +284,33 @@ kda_status kda_chunk_prefill(const void* q, const void* k, const void* v, kda_dt
                                       o, o_dt, T_tot, H, dk, dv, scale, workspace,
                                       workspace_bytes);
   if (st != KDA_OK) return st;
-  return launched(kda::launch_chunk_prefill(q, k, v, qkv_dt == KDA_BF16, g, 0, beta, false,
-                                            nullptr, nullptr, cu_seqlens, cu_seqlens_host, N,
-                                            initial_state, final_state, o, o_dt == KDA_BF16,
-                                            T_tot, H, scale, workspace, workspace_bytes,
-                                            static_cast<hipStream_t>(stream)),
-                  "kda_chunk_prefill");
+  kda::StatePool pool;
+  pool.in = initial_state;
+  pool.out = final_state;
+  pool.slots = N;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool qb = qkv_dt == KDA_BF16;
+  const int64_t nt = T_tot * H * 128;
+  return run_checked(
+      "kda_chunk_prefill", s,
+      [&](kda::dbg::Session& c) {
+        c.add("q", q, nt, qb, kFinite);
+        c.add("k", k, nt, qb, kFinite);
+        c.add("v", v, nt, qb, kFinite);
+        c.add("g", g, nt, false, kNonPositive);
+        c.add("beta", beta, T_tot * H, false, kUnit);
+        c.add_states("initial_state", initial_state, false, nullptr, N, N, H);
+      },
+      [&] {
+        return kda::launch_chunk_prefill(q, k, v, qb, g, 0, beta, false, nullptr, nullptr,
+                                         cu_seqlens, cu_seqlens_host, N, pool, o,
+                                         o_dt == KDA_BF16, T_tot, H, scale, workspace,
+                                         workspace_bytes, s);
+      },
+      [&](kda::dbg::Session& c) {
+        c.add("o", o, nt, o_dt == KDA_BF16, kFinite);
+        c.add_states("final_state", final_state, false, nullptr, N, N, H);
+      });
 }
 
 kda_status kda_chunk_prefill_gated(const void* q, const void* k, const void* v, kda_dtype qkv_dt,
@@ -225,13 +318,22 @@ kda_status kda_chunk_prefill_gated(const void* q, const void* k, const void* v, 
                                    const float* A_log, int64_t A_log_len, const float* dt_bias,
                                    int64_t dt_bias_len, const int32_t* cu_seqlens,
                                    const int32_t* cu_seqlens_host, int32_t N,
-                                   const float* initial_state, float* final_state, void* o,
-                                   kda_dtype o_dt, int64_t T_tot, int32_t H, int32_t dk,
-                                   int32_t dv, float scale, void* workspace,
-                                   size_t workspace_bytes, void* stream) {
+                                   const void* initial_state, void* final_state,
+                                   kda_dtype state_dt, int64_t num_slots,
+                                   const int32_t* state_indices, void* o, kda_dtype o_dt,
+                                   int64_t T_tot, int32_t H, int32_t dk, int32_t dv, float scale,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
   const char* fn = "kda_chunk_prefill_gated";
-  if (!known_dtype(x_dt) || !known_dtype(b_dt))
-    return fail(KDA_ERR_DTYPE, "%s: x_dt and b_dt must be KDA_F32 or KDA_BF16", fn);
+  if (!known_dtype(x_dt) || !known_dtype(b_dt) || !known_dtype(state_dt))
+    return fail(KDA_ERR_DTYPE, "%s: x_dt, b_dt and state_dt must be KDA_F32 or KDA_BF16", fn);
+  if (num_slots < 0)
+    return fail(KDA_ERR_INVALID_ARG, "%s: num_slots must be >= 0 (got %lld)", fn,
+                (long long)num_slots);
+  if ((initial_state || final_state) && !state_indices && num_slots < N)
+    return fail(KDA_ERR_SHAPE, "%s: without state_indices sequence n uses slot n, so num_slots "
+                               "must be >= N (got %lld < %d)", fn, (long long)num_slots, N);
+  if (!aligned(state_indices, 4))
+    return fail(KDA_ERR_ALIGNMENT, "%s: state_indices must be 4-byte aligned", fn);
   bool alog_pc = false;
   if (H > 0)
     if (const kda_status st = check_alog(fn, A_log_len, H, dk, &alog_pc)) return st;
@@ -247,13 +349,55 @@ kda_status kda_chunk_prefill_gated(const void* q, const void* k, const void* v, 
                                       o, o_dt, T_tot, H, dk, dv, scale, workspace,
                                       workspace_bytes);
   if (st != KDA_OK) return st;
+  // the final-state pool must not overlap what the call reads or writes besides
+  // the initial-state pool (which it may equal: an in-place update)
+  if (final_state) {
+    const size_t s_es = state_dt == KDA_BF16 ? 2 : 4;
+    const char* sb = static_cast<const char*>(final_state);
+    const char* se = sb + (size_t)num_slots * H * dk * dv * s_es;
+    const size_t qkv_es = qkv_dt == KDA_BF16 ? 2 : 4;
+    struct { const void* p; size_t n; } others[] = {
+        {q, (size_t)T_tot * H * dk * qkv_es}, {k, (size_t)T_tot * H * dk * qkv_es},
+        {v, (size_t)T_tot * H * dv * qkv_es}, {o, (size_t)T_tot * H * dv * (o_dt == KDA_BF16 ? 2 : 4)},
+        {workspace, workspace_bytes}, {state_indices, state_indices ? (size_t)N * 4 : 0}};
+    for (auto& r : others) {
+      const char* b0 = static_cast<const char*>(r.p);
+      if (r.n && b0 && b0 < se && sb < b0 + r.n)
+        return fail(KDA_ERR_INVALID_ARG, "%s: the final-state pool overlaps another tensor", fn);
+    }
+  }
   const int g_mode = (x_dt == KDA_BF16 ? 2 : 1) | (alog_pc ? 4 : 0);
-  return launched(kda::launch_chunk_prefill(q, k, v, qkv_dt == KDA_BF16, x, g_mode, b,
-                                            b_dt == KDA_BF16, A_log, dt_bias, cu_seqlens, cu_seqlens_host, N,
-                                            initial_state, final_state, o, o_dt == KDA_BF16,
-                                            T_tot, H, scale, workspace, workspace_bytes,
-                                            static_cast<hipStream_t>(stream)),
-                  fn);
+  kda::StatePool pool;
+  pool.in = initial_state;
+  pool.out = final_state;
+  pool.idx = state_indices;
+  pool.slots = state_indices ? num_slots : (num_slots < N ? num_slots : N);
+  pool.bf16 = state_dt == KDA_BF16;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool qb = qkv_dt == KDA_BF16;
+  const int64_t nt = T_tot * H * 128;
+  return run_checked(
+      fn, s,
+      [&](kda::dbg::Session& c) {
+        c.add("q", q, nt, qb, kFinite);
+        c.add("k", k, nt, qb, kFinite);
+        c.add("v", v, nt, qb, kFinite);
+        c.add("x", x, nt, x_dt == KDA_BF16, kNotNaN);
+        c.add("b", b, T_tot * H, b_dt == KDA_BF16, kNotNaN);
+        c.add("A_log", A_log, alog_pc ? (int64_t)H * 128 : H, false, kFinite);
+        c.add("dt_bias", dt_bias, (int64_t)H * 128, false, kFinite);
+        c.add_states("initial_state", initial_state, pool.bf16, state_indices, pool.slots, N, H);
+      },
+      [&] {
+        return kda::launch_chunk_prefill(q, k, v, qb, x, g_mode, b, b_dt == KDA_BF16, A_log,
+                                         dt_bias, cu_seqlens, cu_seqlens_host, N, pool, o,
+                                         o_dt == KDA_BF16, T_tot, H, scale, workspace,
+                                         workspace_bytes, s);
+      },
+      [&](kda::dbg::Session& c) {
+        c.add("o", o, nt, o_dt == KDA_BF16, kFinite);
+        c.add_states("final_state", final_state, pool.bf16, state_indices, pool.slots, N, H);
+      });
 }
 
 size_t kda_chunk_prefill_backward_workspace_bytes(int64_t T_tot, int32_t N, int32_t H,
@@ -285,11 +429,34 @@ kda_status kda_chunk_prefill_backward(const void* q, const void* k, const void* 
       return fail(KDA_ERR_ALIGNMENT, "%s: d_o and the gradients must be 16-byte aligned", fn);
   if (!aligned(dbeta, 4))
     return fail(KDA_ERR_ALIGNMENT, "%s: dbeta must be 4-byte aligned", fn);
-  return launched(kda::bwd::launch(q, k, v, qkv_dt == KDA_BF16, g, beta, cu_seqlens,
-                                   cu_seqlens_host, N, initial_state, d_o, do_dt == KDA_BF16,
-                                   d_final_state, dq, dk, dv, dg, dbeta, d_initial_state, T_tot,
-                                   H, scale, workspace, static_cast<hipStream_t>(stream)),
-                  fn);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool qb = qkv_dt == KDA_BF16;
+  const int64_t nt = T_tot * H * 128;
+  return run_checked(
+      fn, s,
+      [&](kda::dbg::Session& c) {
+        c.add("q", q, nt, qb, kFinite);
+        c.add("k", k, nt, qb, kFinite);
+        c.add("v", v, nt, qb, kFinite);
+        c.add("g", g, nt, false, kNonPositive);
+        c.add("beta", beta, T_tot * H, false, kUnit);
+        c.add("d_o", d_o, nt, do_dt == KDA_BF16, kFinite);
+        c.add_states("initial_state", initial_state, false, nullptr, N, N, H);
+        c.add_states("d_final_state", d_final_state, false, nullptr, N, N, H);
+      },
+      [&] {
+        return kda::bwd::launch(q, k, v, qb, g, beta, cu_seqlens, cu_seqlens_host, N,
+                                initial_state, d_o, do_dt == KDA_BF16, d_final_state, dq, dk,
+                                dv, dg, dbeta, d_initial_state, T_tot, H, scale, workspace, s);
+      },
+      [&](kda::dbg::Session& c) {
+        c.add("dq", dq, nt, false, kFinite);
+        c.add("dk", dk, nt, false, kFinite);
+        c.add("dv", dv, nt, false, kFinite);
+        c.add("dg", dg, nt, false, kFinite);
+        c.add("dbeta", dbeta, T_tot * H, false, kFinite);
+        c.add_states("d_initial_state", d_initial_state, false, nullptr, N, N, H);
+      });
 }
 
 size_t kda_chunk_prefill_workspace_bytes(int32_t N, int32_t H, int32_t dk, int32_t dv,
@@ -331,10 +498,27 @@ kda_status kda_recurrent_decode(const void* q, const void* k, const void* v, kda
     if (b0 < se && sb < b0 + r.n)
       return fail(KDA_ERR_INVALID_ARG, "kda_recurrent_decode: state overlaps another tensor");
   }
-  return launched(kda::launch_decode(q, k, v, qkv_dt == KDA_BF16, g, beta, state, o,
-                                     o_dt == KDA_BF16, N, H, scale,
-                                     static_cast<hipStream_t>(stream)),
-                  "kda_recurrent_decode");
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool qb = qkv_dt == KDA_BF16;
+  const int64_t nt = (int64_t)N * H * 128;
+  return run_checked(
+      "kda_recurrent_decode", s,
+      [&](kda::dbg::Session& c) {
+        c.add("q", q, nt, qb, kFinite);
+        c.add("k", k, nt, qb, kFinite);
+        c.add("v", v, nt, qb, kFinite);
+        c.add("g", g, nt, false, kNonPositive);
+        c.add("beta", beta, (int64_t)N * H, false, kUnit);
+        c.add_states("state", state, false, nullptr, N, N, H);
+      },
+      [&] {
+        return kda::launch_decode(q, k, v, qb, g, beta, state, o, o_dt == KDA_BF16, N, H, scale,
+                                  s);
+      },
+      [&](kda::dbg::Session& c) {
+        c.add("o", o, nt, o_dt == KDA_BF16, kFinite);
+        c.add_states("state", state, false, nullptr, N, N, H);
+      });
 }
 
 kda_status kda_recurrent_decode_gated(const void* q, const void* k, const void* v,
@@ -395,12 +579,30 @@ kda_status kda_recurrent_decode_gated(const void* q, const void* k, const void* 
     if (r.n && b0 < se && sb < b0 + r.n)
       return fail(KDA_ERR_INVALID_ARG, "%s: the state pool overlaps another tensor", fn);
   }
-  return launched(kda::launch_decode_gated(q, k, v, qkv_dt == KDA_BF16, x, x_dt == KDA_BF16, b,
-                                           b_dt == KDA_BF16, A_log, alog_pc, dt_bias, state,
-                                           state_dt == KDA_BF16, num_slots, state_indices, o,
-                                           o_dt == KDA_BF16, N, H, scale,
-                                           static_cast<hipStream_t>(stream)),
-                  fn);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool qb = qkv_dt == KDA_BF16, sb16 = state_dt == KDA_BF16;
+  const int64_t nt = (int64_t)N * H * 128;
+  return run_checked(
+      fn, s,
+      [&](kda::dbg::Session& c) {
+        c.add("q", q, nt, qb, kFinite);
+        c.add("k", k, nt, qb, kFinite);
+        c.add("v", v, nt, qb, kFinite);
+        c.add("x", x, nt, x_dt == KDA_BF16, kNotNaN);
+        c.add("b", b, (int64_t)N * H, b_dt == KDA_BF16, kNotNaN);
+        c.add("A_log", A_log, alog_pc ? (int64_t)H * 128 : H, false, kFinite);
+        c.add("dt_bias", dt_bias, (int64_t)H * 128, false, kFinite);
+        c.add_states("state", state, sb16, state_indices, num_slots, N, H);
+      },
+      [&] {
+        return kda::launch_decode_gated(q, k, v, qb, x, x_dt == KDA_BF16, b, b_dt == KDA_BF16,
+                                        A_log, alog_pc, dt_bias, state, sb16, num_slots,
+                                        state_indices, o, o_dt == KDA_BF16, N, H, scale, s);
+      },
+      [&](kda::dbg::Session& c) {
+        c.add("o", o, nt, o_dt == KDA_BF16, kFinite);
+        c.add_states("state", state, sb16, state_indices, num_slots, N, H);
+      });
 }
 
 kda_status kda_shortconv_l2norm(const void* xq, const void* xk, const void* xv, kda_dtype in_dt,
@@ -477,12 +679,31 @@ kda_status kda_shortconv_l2norm(const void* xq, const void* xk, const void* xv, 
       return fail(KDA_ERR_INVALID_ARG, "%s: the conv state may be updated in place only when "
                                        "every sequence has at most one token", fn);
   }
-  return launched(kda::launch_shortconv(xq, xk, xv, in_dt == KDA_BF16, wq, wk, wv,
-                                        activation == KDA_ACT_SILU, eps, cu_seqlens, N, min_len,
-                                        max_len, T_tot, H, conv_state_in, conv_state_out, yq,
-                                        yk, yv,
-                                        out_dt == KDA_BF16, static_cast<hipStream_t>(stream)),
-                  fn);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool ib = in_dt == KDA_BF16, ob = out_dt == KDA_BF16;
+  const int64_t nt = T_tot * H * d, ns = (int64_t)N * 9 * H * d;
+  return run_checked(
+      fn, s,
+      [&](kda::dbg::Session& c) {
+        c.add("xq", xq, nt, ib, kFinite);
+        c.add("xk", xk, nt, ib, kFinite);
+        c.add("xv", xv, nt, ib, kFinite);
+        c.add("wq", wq, w_len, false, kFinite);
+        c.add("wk", wk, w_len, false, kFinite);
+        c.add("wv", wv, w_len, false, kFinite);
+        c.add("conv_state_in", conv_state_in, ns, false, kFinite);
+      },
+      [&] {
+        return kda::launch_shortconv(xq, xk, xv, ib, wq, wk, wv, activation == KDA_ACT_SILU, eps,
+                                     cu_seqlens, N, min_len, max_len, T_tot, H, conv_state_in,
+                                     conv_state_out, yq, yk, yv, ob, s);
+      },
+      [&](kda::dbg::Session& c) {
+        c.add("yq", yq, nt, ob, kFinite);
+        c.add("yk", yk, nt, ob, kFinite);
+        c.add("yv", yv, nt, ob, kFinite);
+        c.add("conv_state_out", conv_state_out, ns, false, kFinite);
+      });
 }
 
 }  // extern "C"

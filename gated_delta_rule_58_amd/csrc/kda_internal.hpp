@@ -4,9 +4,41 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+#include <string>
+
 #include "kda.h"
 
 namespace kda {
+
+// KDA_DEBUG=1 scans (debug.hip): input-domain scans before a call's kernels,
+// non-finite scans of its outputs after them.
+namespace dbg {
+enum Rule { kFinite = 0, kNotNaN = 1, kNonPositive = 2, kUnit = 3 };
+bool enabled();          // KDA_DEBUG is "1" (read on every call)
+std::mutex& mutex();     // held for a whole debug call
+class Session {
+ public:
+  explicit Session(hipStream_t s);
+  hipError_t begin();    // clears the counters (a kernel on the stream)
+  // count the values of p[0 .. n) (fp32 or bf16) that break `rule`
+  void add(const char* what, const void* p, int64_t n, bool bf16, int rule);
+  // count non-finite values of the 128 x 128 states of slot idx[n] (n when idx is
+  // null) for every (sequence n < N, head), skipping slots outside [0, slots)
+  void add_states(const char* what, const void* p, bool bf16, const int32_t* idx, int64_t slots,
+                  int N, int H);
+  // waits for the stream; report lists every scan that found values ("" if none)
+  hipError_t finish(std::string* report);
+
+ private:
+  hipStream_t stream_;
+  uint32_t* words_ = nullptr;
+  int count_ = 0;
+  const char* what_[16];
+  int rule_[16];
+  int64_t n_[16];
+};
+}  // namespace dbg
 
 // ---- launchers (one per kernel family); return hipSuccess or the launch error
 // A_log per head [H], or per (head, channel) [H, d] when alog_pc.
@@ -48,6 +80,17 @@ hipError_t launch_shortconv(const void* xq, const void* xk, const void* xv, bool
                             float* state_out, void* yq, void* yk, void* yv, bool out_bf16,
                             hipStream_t s);
 
+// Entry or exit states of the chunked prefill: fp32 or bf16 [slots, H, 128, 128];
+// sequence n uses slot idx[n] (n when idx is null).  A slot outside
+// [0, slots) means a zero entry state / no exit state.
+struct StatePool {
+  const void* in = nullptr;       // null: zero entry states
+  void* out = nullptr;            // null: no exit states written
+  const int32_t* idx = nullptr;   // slot per sequence, or null
+  int64_t slots = 0;
+  bool bf16 = false;
+};
+
 // Chunked prefill: prep + state kernel per pass over the chunks (prefill.hip).
 // The decay input is either g (g_mode 0, fp32) with post-sigmoid beta in b,
 // or raw gate logits x (g_mode 1 fp32, 2 bf16) with beta logits in b and the
@@ -55,7 +98,7 @@ hipError_t launch_shortconv(const void* xq, const void* xk, const void* xv, bool
 hipError_t launch_chunk_prefill(const void* q, const void* k, const void* v, bool qkv_bf16,
                                 const void* g, int g_mode, const void* b, bool b_bf16,
                                 const float* A_log, const float* dt_bias, const int32_t* cu,
-                                const int32_t* cu_host, int N, const float* S0, float* S_final,
+                                const int32_t* cu_host, int N, const StatePool& st,
                                 void* o, bool o_bf16, int64_t T_tot, int H, float scale,
                                 void* ws, size_t ws_bytes, hipStream_t s);
 size_t chunk_workspace_bytes(int N, int H, int chunks_per_pass);
@@ -72,13 +115,24 @@ hipError_t launch(const void* q, const void* k, const void* v, bool qkv_bf16, co
 }  // namespace bwd
 
 namespace chunk {
+// Entry and exit states of one state-kernel pass (each fp32 or bf16, each
+// addressed by slot index or by sequence): the pool, or the workspace's fp32
+// carry between passes.  A slot outside [0, slots) reads zeros / is not written.
+struct StateIO {
+  const void* in;
+  const int32_t* in_idx;
+  void* out;
+  const int32_t* out_idx;
+  int64_t in_slots, out_slots;
+  bool in_bf16, out_bf16;
+};
 // One pass: chunks [c_lo, c_lo + S_len) of every sequence (prep.hip, state.hip).
 hipError_t launch_prep(const void* q, const void* k, bool qkv_bf16, const void* g, int g_mode,
                        const void* b, bool b_bf16, const float* A_log, const float* dt_bias,
                        const int32_t* cu, int N, int T_tot, int H, int c_lo, int S_len, char* ws,
                        hipStream_t s);
 hipError_t launch_state(const void* v, bool qkv_bf16, const int32_t* cu, int N, int T_tot,
-                        int H, const float* S_in, float* S_out, void* o, bool o_bf16,
+                        int H, const StateIO& sio, void* o, bool o_bf16,
                         float scale, int c_lo, int S_len, const char* ws, hipStream_t s);
 }  // namespace chunk
 

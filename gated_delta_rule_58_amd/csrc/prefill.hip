@@ -21,7 +21,7 @@ size_t chunk_workspace_bytes(int N, int H, int chunks_per_pass) {
 hipError_t launch_chunk_prefill(const void* q, const void* k, const void* v, bool qkv_bf16,
                                 const void* g, int g_mode, const void* b, bool b_bf16,
                                 const float* A_log, const float* dt_bias, const int32_t* cu,
-                                const int32_t* cu_host, int N, const float* S0, float* S_final,
+                                const int32_t* cu_host, int N, const StatePool& st,
                                 void* o, bool o_bf16, int64_t T_tot, int H, float scale,
                                 void* ws, size_t ws_bytes, hipStream_t s) {
   using namespace chunk;
@@ -37,7 +37,11 @@ hipError_t launch_chunk_prefill(const void* q, const void* k, const void* v, boo
   const size_t carry_bytes = pairs * D * D * sizeof(float);
   int64_t S_len = (int64_t)((ws_bytes - carry_bytes) / (pairs * Ws::bytes));  // >= 1 (checked)
   if (S_len > max_nch) S_len = max_nch > 0 ? max_nch : 1;
-  float* carry = S_final ? S_final : static_cast<float*>(ws);
+  // The state carried between passes stays fp32 and is addressed by sequence:
+  // in the final-state buffer when that is an fp32 [N, H, 128, 128] array,
+  // else in the workspace.
+  const bool out_plain = st.out && !st.bf16 && !st.idx;
+  float* carry = out_plain ? static_cast<float*>(st.out) : static_cast<float*>(ws);
   char* images = static_cast<char*>(ws) + carry_bytes;
   const int T = static_cast<int>(T_tot);
   for (int64_t c_lo = 0;; c_lo += S_len) {
@@ -45,9 +49,31 @@ hipError_t launch_chunk_prefill(const void* q, const void* k, const void* v, boo
     hipError_t e = chunk::launch_prep(q, k, qkv_bf16, g, g_mode, b, b_bf16, A_log, dt_bias, cu,
                                       N, T, H, (int)c_lo, (int)S_len, images, s);
     if (e != hipSuccess) return e;
-    e = chunk::launch_state(v, qkv_bf16, cu, N, T, H, c_lo == 0 ? S0 : carry,
-                            last ? S_final : carry, o, o_bf16, scale, (int)c_lo, (int)S_len,
-                            images, s);
+    chunk::StateIO sio;
+    if (c_lo == 0) {
+      sio.in = st.in;
+      sio.in_idx = st.idx;
+      sio.in_slots = st.slots;
+      sio.in_bf16 = st.bf16;
+    } else {
+      sio.in = carry;
+      sio.in_idx = nullptr;
+      sio.in_slots = N;
+      sio.in_bf16 = false;
+    }
+    if (last) {
+      sio.out = st.out;
+      sio.out_idx = st.idx;
+      sio.out_slots = st.slots;
+      sio.out_bf16 = st.bf16;
+    } else {
+      sio.out = carry;
+      sio.out_idx = nullptr;
+      sio.out_slots = N;
+      sio.out_bf16 = false;
+    }
+    e = chunk::launch_state(v, qkv_bf16, cu, N, T, H, sio, o, o_bf16, scale, (int)c_lo,
+                            (int)S_len, images, s);
     if (e != hipSuccess) return e;
     if (last) return hipSuccess;
   }

@@ -83,7 +83,7 @@ __device__ __forceinline__ int vtile_swz(int r) { return ((r >> 2) & 3) << 1; }
 template <bool QKV_BF16, bool O_BF16>
 __global__ void __launch_bounds__(NTHR_S, 1) state_kernel(
     const void* __restrict__ v, const int32_t* __restrict__ cu, int N, int T_tot, int H, int Hp,
-    const float* S_in, float* S_out, void* __restrict__ o, float scale, int c_lo, int S_len,
+    StateIO sio, void* __restrict__ o, float scale, int c_lo, int S_len,
     const char* __restrict__ ws) {
   __shared__ __attribute__((aligned(16))) char lds[StateLds::total];
   __shared__ int s_seq[1];
@@ -181,14 +181,18 @@ __global__ void __launch_bounds__(NTHR_S, 1) state_kernel(
 
   // ---- state slice (compute waves): tile t holds key rows 16t + 4lg + i, column jcol.
   f32x4 Sacc[8];
-  const int64_t sbase = ((int64_t)n * H + h) * D * D;
   if (!mover) {
-    if (S_in) {
+    const int64_t si = sio.in_idx ? static_cast<int64_t>(sio.in_idx[n]) : n;
+    if (sio.in && si >= 0 && si < sio.in_slots) {
+      const int64_t sbase = (si * H + h) * D * D;
 #pragma unroll
       for (int t = 0; t < 8; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          Sacc[t][i] = S_in[sbase + (int64_t)(16 * t + 4 * lg + i) * D + jcol];
+        for (int i = 0; i < 4; ++i) {
+          const int64_t e = sbase + (int64_t)(16 * t + 4 * lg + i) * D + jcol;
+          Sacc[t][i] = sio.in_bf16 ? bf16_bits_to_f32(static_cast<const uint16_t*>(sio.in)[e])
+                                   : static_cast<const float*>(sio.in)[e];
+        }
     } else {
 #pragma unroll
       for (int t = 0; t < 8; ++t) Sacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -394,26 +398,31 @@ __global__ void __launch_bounds__(NTHR_S, 1) state_kernel(
   if constexpr (O_BF16) {
     if (c_lo < c_end) barrier_nofence();  // A(c_end): hands the last o tile to the data waves
   }
-  if (S_out) {
+  const int64_t so = sio.out_idx ? static_cast<int64_t>(sio.out_idx[n]) : n;
+  if (sio.out && so >= 0 && so < sio.out_slots) {
+    const int64_t sbase = (so * H + h) * D * D;
 #pragma unroll
     for (int t = 0; t < 8; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        S_out[sbase + (int64_t)(16 * t + 4 * lg + i) * D + jcol] = Sacc[t][i];
+      for (int i = 0; i < 4; ++i) {
+        const int64_t e = sbase + (int64_t)(16 * t + 4 * lg + i) * D + jcol;
+        if (sio.out_bf16) static_cast<uint16_t*>(sio.out)[e] = f32_to_bf16_bits(Sacc[t][i]);
+        else static_cast<float*>(sio.out)[e] = Sacc[t][i];
+      }
   }
 }
 
 }  // namespace
 
 hipError_t launch_state(const void* v, bool qkv_bf16, const int32_t* cu, int N, int T_tot,
-                        int H, const float* S_in, float* S_out, void* o, bool o_bf16,
+                        int H, const StateIO& sio, void* o, bool o_bf16,
                         float scale, int c_lo, int S_len, const char* ws, hipStream_t s) {
   const int Hp = (H + 7) & ~7;
   const int64_t blocks = (int64_t)N * Hp * NT;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   dim3 grid(static_cast<unsigned>(blocks));
 #define KDA_LAUNCH(QB, OB)                                                                      \
-  state_kernel<QB, OB><<<grid, NTHR_S, 0, s>>>(v, cu, N, T_tot, H, Hp, S_in, S_out, o, scale, \
+  state_kernel<QB, OB><<<grid, NTHR_S, 0, s>>>(v, cu, N, T_tot, H, Hp, sio, o, scale,       \
                                                c_lo, S_len, ws)
   if (qkv_bf16 && o_bf16) KDA_LAUNCH(true, true);
   else if (qkv_bf16) KDA_LAUNCH(true, false);

@@ -21,16 +21,37 @@
  * Conventions for every entry point:
  *   - Tensors are dense, row-major (last index fastest), on the current HIP
  *     device, and must not overlap unless stated.  The library never
- *     allocates, frees or copies memory and never synchronises the stream.
+ *     allocates, frees or copies memory and never synchronises the stream
+ *     (outside the KDA_DEBUG mode below).
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = legacy default
  *     stream) and runs asynchronously; outputs are ready when the stream is.
  *   - Each call validates all arguments first.  On any status other than
  *     KDA_OK returned before launch, nothing was launched and no output was
  *     written.  KDA_ERR_LAUNCH means the kernel launch itself failed.
  *   - kda_last_error() returns a thread-local message for the last failure.
- *   - Inputs to the recurrence are assumed finite with g <= 0 and beta in
- *     [0,1] (the gate produces exactly these); other values are not
- *     checked and propagate into the outputs.
+ *   - The recurrence's domain: g <= 0 and beta in [0, 1] (the gate produces
+ *     exactly these), q, k, v and states finite.  The chunked prefill computes
+ *     its matrix products on fp16 operands, so q, k, v and state entries must
+ *     stay well inside fp16 range (|x| < 2^15); with unit-norm q and k that
+ *     holds for any realistic v and state.  Any g <= 0 is accepted: the
+ *     chunked prefill floors the per-token decay factor exp(g) at 2^-15.5
+ *     (2.2e-5), which keeps every factor it forms in fp32 range for decays
+ *     as strong as the Kimi K3 artifact audit's printed parameter maxima
+ *     produce (§5.1: A_log up to 2.47, dt_bias up to 0.18), and moves o and
+ *     the state by far less than their rounding error.
+ *   - Values outside that domain are not checked and propagate into the
+ *     outputs, unless the environment variable KDA_DEBUG is "1" (read on
+ *     every call).  Then every call first scans its inputs (q, k, v and
+ *     states finite, g <= 0, beta in [0, 1], gate logits not NaN, A_log and
+ *     dt_bias finite) and returns KDA_ERR_DOMAIN, launching nothing and
+ *     writing nothing, if any value breaks its rule; after its kernels it
+ *     scans every output and returns KDA_ERR_NONFINITE if any value is NaN
+ *     or infinite (a g of -inf, the gate's limit for an infinite logit, is
+ *     allowed).  kda_last_error() names each offending tensor and the count.
+ *     Debug calls wait for their stream and are serialised by a process-wide
+ *     lock.  The Model-Optimizer PR #2749 review (the KDA beta fix) describes
+ *     the failure this makes visible: a recurrence fed unsquashed beta
+ *     diverges, and the only symptom downstream is a NaN.
  */
 #ifndef KDA_H_
 #define KDA_H_
@@ -50,7 +71,9 @@ typedef enum {
   KDA_ERR_UNSUPPORTED = 4, /* valid but not implemented (e.g. d != 128)    */
   KDA_ERR_ALIGNMENT = 5,   /* pointer not 16-byte aligned                  */
   KDA_ERR_WORKSPACE = 6,   /* workspace missing or too small               */
-  KDA_ERR_LAUNCH = 7       /* the HIP launch failed (see kda_last_error)   */
+  KDA_ERR_LAUNCH = 7,      /* the HIP launch failed (see kda_last_error)   */
+  KDA_ERR_DOMAIN = 8,      /* KDA_DEBUG=1: an input outside the domain; nothing launched */
+  KDA_ERR_NONFINITE = 9    /* KDA_DEBUG=1: a NaN or inf in an output (outputs written)   */
 } kda_status;
 
 typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
@@ -161,10 +184,13 @@ size_t kda_gate_backward_workspace_bytes(int64_t n_tok, int32_t H, int32_t d);
  *               whole batch in one pass.
  * Requires dk == dv == 128 (else KDA_ERR_UNSUPPORTED), N >= 1, H >= 1,
  * 16-byte aligned tensors.  Matrix products run as fp16 MFMA tiles with fp32
- * accumulation (bf16 inputs convert to fp16 exactly); the state, X and Delta
- * enter the products as hi+lo fp16 pairs.  Against an fp64 recurrence the
- * final state agrees to a few 1e-4 of its Frobenius norm and o to a few 1e-3
- * of its RMS (before any bf16 rounding of o).
+ * accumulation (bf16 inputs convert to fp16 exactly inside fp16's range); X
+ * and Delta enter the products as hi+lo fp16 pairs, the state as one fp16
+ * value (it stays fp32 in the accumulators).  Against an fp64 recurrence
+ * the final state agrees to about 3.4e-4 of its Frobenius norm and o to
+ * about 3.4e-3 of its RMS (measured on the full-size workloads; the stated
+ * bounds are 1e-3 and 5e-3).  A bf16 o is the round-to-nearest-even
+ * rounding of the fp32 o, bit for bit.
  */
 kda_status kda_chunk_prefill(const void* q, const void* k, const void* v, kda_dtype qkv_dt,
                              const float* g, const float* beta, const int32_t* cu_seqlens,
@@ -175,31 +201,54 @@ kda_status kda_chunk_prefill(const void* q, const void* k, const void* v, kda_dt
                              void* stream);
 
 /*
- * kda_chunk_prefill_gated - kda_gate fused into kda_chunk_prefill.
+ * kda_chunk_prefill_gated - kda_gate fused into kda_chunk_prefill, with the
+ * states in a pool of slots (fp32 or bf16) shared with
+ * kda_recurrent_decode_gated.
  *
  * The same recurrence, outputs, workspace and rules as kda_chunk_prefill,
  * but the decay and beta come as the gate's raw inputs (the arguments of
  * kda_gate): x [T_tot, H, dk] gate logits (x_dt KDA_F32 or KDA_BF16), b
  * [T_tot, H] beta logits (b_dt), A_log [H] or [H, dk] (16-byte aligned),
  * dt_bias [H, dk].  g and beta are
- * formed in registers and g never goes to memory.  g is summed into the
+ * formed in registers and g never goes to memory.
+ *
+ * States: initial_state and final_state are pools [num_slots, H, dk, dv] of
+ * state_dt (KDA_F32 or KDA_BF16), either NULL (zero entry states / no exit
+ * states), possibly the same pool (an in-place update).  Sequence n reads and
+ * writes slot state_indices[n] (int32, device), or slot n when state_indices
+ * is NULL (then num_slots >= N).  A sequence whose slot lies outside
+ * [0, num_slots) (a padding entry such as -1) starts from a zero state and
+ * writes no final state; its o is computed.  Two sequences must not share a
+ * slot that is written.  A bf16 entry state is widened exactly; the walk
+ * keeps the state in fp32 (also between passes) and rounds the exit state
+ * to bf16 once, to nearest even.  The artifact audit's §7.4 times FlashKDA's
+ * prefill with BF16, no and FP32 state modes; the code audit's
+ * repeated-cache-concatenation finding recommends indexed writes into
+ * preallocated storage, which the slots provide, so a prefill hands its
+ * states to the gated decode without copies or conversions.  g is summed into the
  * cumulative decay straight in log2 units with the plain hardware exp2/log2
  * (absolute error about exp(A_log) 2^-23 per token, against a few ulp for
  * kda_gate), so results agree with kda_gate followed by kda_chunk_prefill to
  * rounding, not bit for bit.  FlashKDA's interface (Kimi K3 artifact audit,
  * §7.1) likewise
  * takes the gate's inputs.  Refusals: those of kda_gate for A_log /
- * dt_bias, then those of kda_chunk_prefill; x must be 16-byte aligned.
+ * dt_bias, then those of kda_chunk_prefill; x must be 16-byte aligned;
+ * state_dt not KDA_F32 / KDA_BF16 (KDA_ERR_DTYPE), num_slots < 0
+ * (KDA_ERR_INVALID_ARG), num_slots < N with states but no indices
+ * (KDA_ERR_SHAPE), a final-state pool overlapping q, k, v, o, the workspace
+ * or the indices (KDA_ERR_INVALID_ARG).  The indices themselves are device
+ * data and are bounds-checked by the kernel.
  */
 kda_status kda_chunk_prefill_gated(const void* q, const void* k, const void* v, kda_dtype qkv_dt,
                                    const void* x, kda_dtype x_dt, const void* b, kda_dtype b_dt,
                                    const float* A_log, int64_t A_log_len, const float* dt_bias,
                                    int64_t dt_bias_len, const int32_t* cu_seqlens,
                                    const int32_t* cu_seqlens_host, int32_t N,
-                                   const float* initial_state, float* final_state, void* o,
-                                   kda_dtype o_dt, int64_t T_tot, int32_t H, int32_t dk,
-                                   int32_t dv, float scale, void* workspace,
-                                   size_t workspace_bytes, void* stream);
+                                   const void* initial_state, void* final_state,
+                                   kda_dtype state_dt, int64_t num_slots,
+                                   const int32_t* state_indices, void* o, kda_dtype o_dt,
+                                   int64_t T_tot, int32_t H, int32_t dk, int32_t dv, float scale,
+                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * kda_chunk_prefill_backward - gradients of kda_chunk_prefill.

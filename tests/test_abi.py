@@ -115,15 +115,16 @@ def test_prefill_workspace_contract():
 def _prefill_gated(L, cu_host, **kw):
     a = dict(q=DEV[0], k=DEV[1], v=DEV[2], qkv_dt=1, x=DEV[3], x_dt=0, b=DEV[4], b_dt=0,
              A_log=DEV[9], A_log_len=4, dt_bias=DEV[10], dt_bias_len=4 * 128, cu=DEV[5], N=2,
-             S0=None, Sf=DEV[6], o=DEV[7], o_dt=1, T=48, H=4, dk=128, dv=128, scale=1.0,
-             ws=DEV[8], ws_bytes=1 << 30)
+             S0=None, Sf=DEV[6], S_dt=0, slots=2, idx=None, o=DEV[7], o_dt=1, T=48, H=4,
+             dk=128, dv=128, scale=1.0, ws=DEV[8], ws_bytes=1 << 30)
     a.update(kw)
     hp = None if cu_host is None else np.ascontiguousarray(np.asarray(cu_host, dtype=np.int32))
     return L.kda_chunk_prefill_gated(
         a["q"], a["k"], a["v"], a["qkv_dt"], a["x"], a["x_dt"], a["b"], a["b_dt"], a["A_log"],
         a["A_log_len"], a["dt_bias"], a["dt_bias_len"], a["cu"],
-        None if hp is None else hp.ctypes.data, a["N"], a["S0"], a["Sf"], a["o"], a["o_dt"],
-        a["T"], a["H"], a["dk"], a["dv"], a["scale"], a["ws"], a["ws_bytes"], None)
+        None if hp is None else hp.ctypes.data, a["N"], a["S0"], a["Sf"], a["S_dt"], a["slots"],
+        a["idx"], a["o"], a["o_dt"], a["T"], a["H"], a["dk"], a["dv"], a["scale"], a["ws"],
+        a["ws_bytes"], None)
 
 
 def test_prefill_gated_refusals():
@@ -148,6 +149,25 @@ def test_prefill_gated_refusals():
     assert _prefill_gated(L, cu, A_log_len=4 * 128, ws=None) == 6
     assert _prefill_gated(L, cu, A_log_len=4 * 128, A_log=DEV[9] + 4) == 5
     assert _prefill_gated(L, cu, A_log_len=4 * 128 + 4) == 2
+
+
+def test_prefill_gated_state_pool_refusals():
+    """State dtype, slot count, index alignment and pool overlap are checked on
+    the host before any HIP call."""
+    L = _lib()
+    cu = [0, 20, 48]
+    assert _prefill_gated(L, cu, S_dt=5) == 3                     # unknown state dtype
+    assert _prefill_gated(L, cu, slots=-1) == 1
+    assert _prefill_gated(L, cu, slots=1) == 2                    # N = 2 slots, no indices
+    assert b"num_slots" in L.kda_last_error()
+    assert _prefill_gated(L, cu, slots=1, idx=DEV[11], ws=None) == 6   # indices: any pool size
+    assert _prefill_gated(L, cu, slots=0, S0=None, Sf=None, ws=None) == 6  # no states: no slots
+    assert _prefill_gated(L, cu, idx=DEV[11] + 2) == 5            # indices 4-byte aligned
+    assert _prefill_gated(L, cu, Sf=DEV[6] + 8) == 5              # pool 16-byte aligned
+    # a final-state pool of 64 slots x 4 heads x 64 KiB reaches into o at DEV[7]
+    assert _prefill_gated(L, cu, slots=64, idx=DEV[11]) == 1
+    assert b"overlaps" in L.kda_last_error()
+    assert _prefill_gated(L, cu, S_dt=1, S0=DEV[6], Sf=DEV[6], ws=None) == 6  # bf16, in place
 
 
 def test_decode_refusals():
