@@ -16,6 +16,7 @@ from .binding import (  # noqa: F401
     gate_backward,
     chunk_prefill,
     chunk_prefill_gated,
+    chunk_prefill_gated_static,
     chunk_prefill_workspace_bytes,
     chunk_prefill_backward,
     chunk_prefill_backward_workspace_bytes,

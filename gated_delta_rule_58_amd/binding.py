@@ -63,6 +63,12 @@ def lib():
                                               _vp, _vp, ctypes.c_int, _i64, _vp, _vp, ctypes.c_int,
                                               _i64, _i32, _i32, _i32, ctypes.c_float, _vp,
                                               ctypes.c_size_t, _vp]
+        L.kda_chunk_prefill_gated_static.restype = ctypes.c_int
+        L.kda_chunk_prefill_gated_static.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp,
+                                                     ctypes.c_int, _vp, ctypes.c_int, _vp, _i64,
+                                                     _vp, _i64, _vp, _vp, _i32, _vp, _vp,
+                                                     ctypes.c_int, _i64, _vp, _vp, ctypes.c_int,
+                                                     _i64, _i32, _i32, _i32, ctypes.c_float, _vp]
         L.kda_chunk_prefill_workspace_bytes.restype = ctypes.c_size_t
         L.kda_chunk_prefill_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32, _i32]
         L.kda_recurrent_decode_gated.restype = ctypes.c_int
@@ -97,7 +103,8 @@ def lib():
 
 def exported_symbols():
     return ["kda_last_error", "kda_version", "kda_gate", "kda_chunk_prefill",
-            "kda_chunk_prefill_gated", "kda_chunk_prefill_workspace_bytes", "kda_recurrent_decode",
+            "kda_chunk_prefill_gated", "kda_chunk_prefill_gated_static",
+            "kda_chunk_prefill_workspace_bytes", "kda_recurrent_decode",
             "kda_recurrent_decode_gated", "kda_shortconv_l2norm", "kda_chunk_prefill_backward",
             "kda_chunk_prefill_backward_workspace_bytes", "kda_gate_backward",
             "kda_gate_backward_workspace_bytes"]
@@ -267,6 +274,44 @@ def chunk_prefill_gated(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, x: to
         KDA_BF16 if state_dtype == torch.bfloat16 else KDA_F32, num_slots, _ptr(state_indices),
         _ptr(out), _dt(out), T, H, dk, dv, float(scale), _ptr(workspace), workspace.numel(),
         _stream(dev))
+    _check(st)
+    return out, final_state
+
+
+def chunk_prefill_gated_static(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                               x: torch.Tensor, b: torch.Tensor, A_log: torch.Tensor,
+                               dt_bias: torch.Tensor, cu_seqlens: Optional[torch.Tensor] = None,
+                               initial_state: Optional[torch.Tensor] = None,
+                               final_state: Optional[torch.Tensor] = None,
+                               out: Optional[torch.Tensor] = None, scale: float = 1.0,
+                               cu_seqlens_host: Optional[torch.Tensor] = None,
+                               state_indices: Optional[torch.Tensor] = None,
+                               state_dtype: Optional[torch.dtype] = None):
+    """kda_chunk_prefill_gated_static: chunk_prefill_gated over the library's own
+    device scratch (no workspace).  The caller passes every output: o as `out`
+    and, if wanted, final_state; nothing is allocated.  Returns (out, final_state)."""
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    if out is None:
+        raise ValueError("chunk_prefill_gated_static allocates nothing: pass out")
+    if cu_seqlens is None or cu_seqlens_host is None:
+        raise ValueError("chunk_prefill_gated_static needs cu_seqlens and cu_seqlens_host")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens_host.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    hp = cu_seqlens_host.contiguous()
+    N = cu_seqlens.numel() - 1
+    if state_dtype is None:
+        state_dtype = initial_state.dtype if initial_state is not None else (
+            final_state.dtype if final_state is not None else torch.float32)
+    pools = [t for t in (initial_state, final_state) if t is not None]
+    num_slots = pools[0].shape[0] if pools else N
+    A_log = _alog(A_log, H, dk)
+    st = lib().kda_chunk_prefill_gated_static(
+        _ptr(q), _ptr(k), _ptr(v), _dt(q), _ptr(x), _dt(x), _ptr(b), _dt(b), _ptr(A_log),
+        A_log.numel(), _ptr(dt_bias), dt_bias.numel(), _ptr(cu_seqlens),
+        ctypes.cast(hp.data_ptr(), _vp), N, _ptr(initial_state), _ptr(final_state),
+        KDA_BF16 if state_dtype == torch.bfloat16 else KDA_F32, num_slots, _ptr(state_indices),
+        _ptr(out), _dt(out), T, H, dk, dv, float(scale), _stream(q.device))
     _check(st)
     return out, final_state
 

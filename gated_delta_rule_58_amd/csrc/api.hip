@@ -268,6 +268,123 @@ kda_status check_prefill(const char* fn, const void* q, const void* k, const voi
   return KDA_OK;
 }
 
+// The gated prefill's arguments (kda_chunk_prefill_gated without the
+// workspace and stream).
+struct GatedPrefill {
+  const void *q, *k, *v;
+  kda_dtype qkv_dt;
+  const void* x;
+  kda_dtype x_dt;
+  const void* b;
+  kda_dtype b_dt;
+  const float* A_log;
+  int64_t A_log_len;
+  const float* dt_bias;
+  int64_t dt_bias_len;
+  const int32_t *cu_seqlens, *cu_seqlens_host;
+  int32_t N;
+  const void* initial_state;
+  void* final_state;
+  kda_dtype state_dt;
+  int64_t num_slots;
+  const int32_t* state_indices;
+  void* o;
+  kda_dtype o_dt;
+  int64_t T_tot;
+  int32_t H, dk, dv;
+  float scale;
+};
+
+// Host-side validation of a gated prefill; `user_ws` says whether the
+// workspace is the caller's (then a final-state pool must not overlap it).
+kda_status check_gated(const char* fn, const GatedPrefill& a, const void* workspace,
+                       size_t workspace_bytes, bool user_ws, bool* alog_pc) {
+  if (!known_dtype(a.x_dt) || !known_dtype(a.b_dt) || !known_dtype(a.state_dt))
+    return fail(KDA_ERR_DTYPE, "%s: x_dt, b_dt and state_dt must be KDA_F32 or KDA_BF16", fn);
+  if (a.num_slots < 0)
+    return fail(KDA_ERR_INVALID_ARG, "%s: num_slots must be >= 0 (got %lld)", fn,
+                (long long)a.num_slots);
+  if ((a.initial_state || a.final_state) && !a.state_indices && a.num_slots < a.N)
+    return fail(KDA_ERR_SHAPE, "%s: without state_indices sequence n uses slot n, so num_slots "
+                               "must be >= N (got %lld < %d)", fn, (long long)a.num_slots, a.N);
+  if (!aligned(a.state_indices, 4))
+    return fail(KDA_ERR_ALIGNMENT, "%s: state_indices must be 4-byte aligned", fn);
+  *alog_pc = false;
+  if (a.H > 0)
+    if (const kda_status st = check_alog(fn, a.A_log_len, a.H, a.dk, alog_pc)) return st;
+  if (a.H > 0 && a.dt_bias_len != (int64_t)a.H * a.dk)
+    return fail(KDA_ERR_SHAPE, "%s: dt_bias has %lld values, need H*dk = %lld", fn,
+                (long long)a.dt_bias_len, (long long)a.H * a.dk);
+  if (!a.A_log || !a.dt_bias) return fail(KDA_ERR_INVALID_ARG, "%s: A_log/dt_bias is NULL", fn);
+  if (!aligned(a.dt_bias, 16) || (*alog_pc && !aligned(a.A_log, 16)))
+    return fail(KDA_ERR_ALIGNMENT, "%s: dt_bias (and a per-channel A_log) must be 16-byte "
+                                   "aligned", fn);
+  const kda_status st = check_prefill(fn, a.q, a.k, a.v, a.qkv_dt, a.x, 16, a.b,
+                                      a.b_dt == KDA_BF16 ? 2 : 4, a.cu_seqlens,
+                                      a.cu_seqlens_host, a.N, a.initial_state, a.final_state,
+                                      a.o, a.o_dt, a.T_tot, a.H, a.dk, a.dv, a.scale, workspace,
+                                      workspace_bytes);
+  if (st != KDA_OK) return st;
+  // the final-state pool must not overlap what the call reads or writes besides
+  // the initial-state pool (which it may equal: an in-place update)
+  if (a.final_state) {
+    const size_t s_es = a.state_dt == KDA_BF16 ? 2 : 4;
+    const char* sb = static_cast<const char*>(a.final_state);
+    const char* se = sb + (size_t)a.num_slots * a.H * a.dk * a.dv * s_es;
+    const size_t qkv_es = a.qkv_dt == KDA_BF16 ? 2 : 4;
+    const size_t T = (size_t)a.T_tot;
+    struct { const void* p; size_t n; } others[] = {
+        {a.q, T * a.H * a.dk * qkv_es}, {a.k, T * a.H * a.dk * qkv_es},
+        {a.v, T * a.H * a.dv * qkv_es}, {a.o, T * a.H * a.dv * (a.o_dt == KDA_BF16 ? 2 : 4)},
+        {workspace, user_ws ? workspace_bytes : 0},
+        {a.state_indices, a.state_indices ? (size_t)a.N * 4 : 0}};
+    for (auto& r : others) {
+      const char* b0 = static_cast<const char*>(r.p);
+      if (r.n && b0 && b0 < se && sb < b0 + r.n)
+        return fail(KDA_ERR_INVALID_ARG, "%s: the final-state pool overlaps another tensor", fn);
+    }
+  }
+  return KDA_OK;
+}
+
+// Launches a validated gated prefill (under KDA_DEBUG's scans when that is on).
+kda_status run_gated(const char* fn, const GatedPrefill& a, bool alog_pc, void* workspace,
+                     size_t workspace_bytes, hipStream_t s) {
+  const int g_mode = (a.x_dt == KDA_BF16 ? 2 : 1) | (alog_pc ? 4 : 0);
+  kda::StatePool pool;
+  pool.in = a.initial_state;
+  pool.out = a.final_state;
+  pool.idx = a.state_indices;
+  pool.slots = a.state_indices ? a.num_slots : (a.num_slots < a.N ? a.num_slots : a.N);
+  pool.bf16 = a.state_dt == KDA_BF16;
+  const bool qb = a.qkv_dt == KDA_BF16;
+  const int64_t nt = a.T_tot * a.H * 128;
+  const int N = a.N, H = a.H;
+  return run_checked(
+      fn, s,
+      [&](kda::dbg::Session& c) {
+        c.add("q", a.q, nt, qb, kFinite);
+        c.add("k", a.k, nt, qb, kFinite);
+        c.add("v", a.v, nt, qb, kFinite);
+        c.add("x", a.x, nt, a.x_dt == KDA_BF16, kNotNaN);
+        c.add("b", a.b, a.T_tot * H, a.b_dt == KDA_BF16, kNotNaN);
+        c.add("A_log", a.A_log, alog_pc ? (int64_t)H * 128 : H, false, kFinite);
+        c.add("dt_bias", a.dt_bias, (int64_t)H * 128, false, kFinite);
+        c.add_states("initial_state", a.initial_state, pool.bf16, a.state_indices, pool.slots,
+                     N, H);
+      },
+      [&] {
+        return kda::launch_chunk_prefill(a.q, a.k, a.v, qb, a.x, g_mode, a.b, a.b_dt == KDA_BF16,
+                                         a.A_log, a.dt_bias, a.cu_seqlens, a.cu_seqlens_host, N,
+                                         pool, a.o, a.o_dt == KDA_BF16, a.T_tot, H, a.scale,
+                                         workspace, workspace_bytes, s);
+      },
+      [&](kda::dbg::Session& c) {
+        c.add("o", a.o, nt, a.o_dt == KDA_BF16, kFinite);
+        c.add_states("final_state", a.final_state, pool.bf16, a.state_indices, pool.slots, N, H);
+      });
+}
+
 }  // namespace
 
 extern "C" {
@@ -324,80 +441,87 @@ kda_status kda_chunk_prefill_gated(const void* q, const void* k, const void* v, 
                                    int64_t T_tot, int32_t H, int32_t dk, int32_t dv, float scale,
                                    void* workspace, size_t workspace_bytes, void* stream) {
   const char* fn = "kda_chunk_prefill_gated";
-  if (!known_dtype(x_dt) || !known_dtype(b_dt) || !known_dtype(state_dt))
-    return fail(KDA_ERR_DTYPE, "%s: x_dt, b_dt and state_dt must be KDA_F32 or KDA_BF16", fn);
-  if (num_slots < 0)
-    return fail(KDA_ERR_INVALID_ARG, "%s: num_slots must be >= 0 (got %lld)", fn,
-                (long long)num_slots);
-  if ((initial_state || final_state) && !state_indices && num_slots < N)
-    return fail(KDA_ERR_SHAPE, "%s: without state_indices sequence n uses slot n, so num_slots "
-                               "must be >= N (got %lld < %d)", fn, (long long)num_slots, N);
-  if (!aligned(state_indices, 4))
-    return fail(KDA_ERR_ALIGNMENT, "%s: state_indices must be 4-byte aligned", fn);
+  const GatedPrefill a{q, k, v, qkv_dt, x, x_dt, b, b_dt, A_log, A_log_len, dt_bias,
+                       dt_bias_len, cu_seqlens, cu_seqlens_host, N, initial_state, final_state,
+                       state_dt, num_slots, state_indices, o, o_dt, T_tot, H, dk, dv, scale};
   bool alog_pc = false;
-  if (H > 0)
-    if (const kda_status st = check_alog(fn, A_log_len, H, dk, &alog_pc)) return st;
-  if (H > 0 && dt_bias_len != (int64_t)H * dk)
-    return fail(KDA_ERR_SHAPE, "%s: dt_bias has %lld values, need H*dk = %lld", fn,
-                (long long)dt_bias_len, (long long)H * dk);
-  if (!A_log || !dt_bias) return fail(KDA_ERR_INVALID_ARG, "%s: A_log/dt_bias is NULL", fn);
-  if (!aligned(dt_bias, 16) || (alog_pc && !aligned(A_log, 16)))
-    return fail(KDA_ERR_ALIGNMENT, "%s: dt_bias (and a per-channel A_log) must be 16-byte "
-                                   "aligned", fn);
-  const kda_status st = check_prefill(fn, q, k, v, qkv_dt, x, 16, b, b_dt == KDA_BF16 ? 2 : 4,
-                                      cu_seqlens, cu_seqlens_host, N, initial_state, final_state,
-                                      o, o_dt, T_tot, H, dk, dv, scale, workspace,
-                                      workspace_bytes);
-  if (st != KDA_OK) return st;
-  // the final-state pool must not overlap what the call reads or writes besides
-  // the initial-state pool (which it may equal: an in-place update)
-  if (final_state) {
-    const size_t s_es = state_dt == KDA_BF16 ? 2 : 4;
-    const char* sb = static_cast<const char*>(final_state);
-    const char* se = sb + (size_t)num_slots * H * dk * dv * s_es;
-    const size_t qkv_es = qkv_dt == KDA_BF16 ? 2 : 4;
-    struct { const void* p; size_t n; } others[] = {
-        {q, (size_t)T_tot * H * dk * qkv_es}, {k, (size_t)T_tot * H * dk * qkv_es},
-        {v, (size_t)T_tot * H * dv * qkv_es}, {o, (size_t)T_tot * H * dv * (o_dt == KDA_BF16 ? 2 : 4)},
-        {workspace, workspace_bytes}, {state_indices, state_indices ? (size_t)N * 4 : 0}};
-    for (auto& r : others) {
-      const char* b0 = static_cast<const char*>(r.p);
-      if (r.n && b0 && b0 < se && sb < b0 + r.n)
-        return fail(KDA_ERR_INVALID_ARG, "%s: the final-state pool overlaps another tensor", fn);
-    }
+  if (const kda_status st = check_gated(fn, a, workspace, workspace_bytes, true, &alog_pc))
+    return st;
+  return run_gated(fn, a, alog_pc, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"
+
+// ---- kda_chunk_prefill_gated_static: the gated prefill over a workspace that
+// lives in this file as a device array, for callers that cannot allocate.
+namespace {
+
+constexpr size_t kStaticScratchBytes = size_t(KDA_PREFILL_STATIC_SCRATCH_BYTES);
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxScratchDevices];  // per device: device address of `scratch`
+
+// The device address of this device's `scratch` (looked up once per device,
+// with that device current).  Host code uses only this address: the array's
+// own name in host code is a host-side stand-in, not device memory.
+kda_status scratch_for_current_device(const char* fn, void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess)
+    return fail(KDA_ERR_LAUNCH, "%s: hipGetDevice failed: %s", fn, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxScratchDevices)
+    return fail(KDA_ERR_UNSUPPORTED, "%s: device %d is beyond the %d the library tracks", fn, dev,
+                kMaxScratchDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(KDA_ERR_LAUNCH, "%s: hipGetSymbolAddress(scratch) failed: %s", fn,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
   }
-  const int g_mode = (x_dt == KDA_BF16 ? 2 : 1) | (alog_pc ? 4 : 0);
-  kda::StatePool pool;
-  pool.in = initial_state;
-  pool.out = final_state;
-  pool.idx = state_indices;
-  pool.slots = state_indices ? num_slots : (num_slots < N ? num_slots : N);
-  pool.bf16 = state_dt == KDA_BF16;
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool qb = qkv_dt == KDA_BF16;
-  const int64_t nt = T_tot * H * 128;
-  return run_checked(
-      fn, s,
-      [&](kda::dbg::Session& c) {
-        c.add("q", q, nt, qb, kFinite);
-        c.add("k", k, nt, qb, kFinite);
-        c.add("v", v, nt, qb, kFinite);
-        c.add("x", x, nt, x_dt == KDA_BF16, kNotNaN);
-        c.add("b", b, T_tot * H, b_dt == KDA_BF16, kNotNaN);
-        c.add("A_log", A_log, alog_pc ? (int64_t)H * 128 : H, false, kFinite);
-        c.add("dt_bias", dt_bias, (int64_t)H * 128, false, kFinite);
-        c.add_states("initial_state", initial_state, pool.bf16, state_indices, pool.slots, N, H);
-      },
-      [&] {
-        return kda::launch_chunk_prefill(q, k, v, qb, x, g_mode, b, b_dt == KDA_BF16, A_log,
-                                         dt_bias, cu_seqlens, cu_seqlens_host, N, pool, o,
-                                         o_dt == KDA_BF16, T_tot, H, scale, workspace,
-                                         workspace_bytes, s);
-      },
-      [&](kda::dbg::Session& c) {
-        c.add("o", o, nt, o_dt == KDA_BF16, kFinite);
-        c.add_states("final_state", final_state, pool.bf16, state_indices, pool.slots, N, H);
-      });
+  *out = g_scratch_ptr[dev];
+  return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_chunk_prefill_gated_static(
+    const void* q, const void* k, const void* v, kda_dtype qkv_dt, const void* x, kda_dtype x_dt,
+    const void* b, kda_dtype b_dt, const float* A_log, int64_t A_log_len, const float* dt_bias,
+    int64_t dt_bias_len, const int32_t* cu_seqlens, const int32_t* cu_seqlens_host, int32_t N,
+    const void* initial_state, void* final_state, kda_dtype state_dt, int64_t num_slots,
+    const int32_t* state_indices, void* o, kda_dtype o_dt, int64_t T_tot, int32_t H, int32_t dk,
+    int32_t dv, float scale, void* stream) {
+  const char* fn = "kda_chunk_prefill_gated_static";
+  if (N > 0 && H > 0 && dk == 128 && dv == 128 && (int64_t)N * H <= ((int64_t)1 << 24)) {
+    const size_t need = kda::chunk_workspace_bytes(N, H, 1);
+    if (need > kStaticScratchBytes)
+      return fail(KDA_ERR_WORKSPACE,
+                  "%s: N * H = %lld (sequence, head) pairs need %zu bytes of scratch for one "
+                  "chunk per pass, more than the static scratch's %zu (at most %zu pairs); use "
+                  "kda_chunk_prefill_gated with a workspace",
+                  fn, (long long)N * H, need, kStaticScratchBytes,
+                  kStaticScratchBytes / kda::chunk_workspace_bytes(1, 1, 1));
+  }
+  const GatedPrefill a{q, k, v, qkv_dt, x, x_dt, b, b_dt, A_log, A_log_len, dt_bias,
+                       dt_bias_len, cu_seqlens, cu_seqlens_host, N, initial_state, final_state,
+                       state_dt, num_slots, state_indices, o, o_dt, T_tot, H, dk, dv, scale};
+  // every check before the first HIP call: the workspace argument is a
+  // non-null, aligned stand-in of the scratch's size (the scratch is the
+  // library's own memory, so it overlaps no argument)
+  bool alog_pc = false;
+  if (const kda_status st = check_gated(fn, a, reinterpret_cast<const void*>(uintptr_t(256)),
+                                        kStaticScratchBytes, false, &alog_pc))
+    return st;
+  void* ws = nullptr;
+  if (const kda_status st = scratch_for_current_device(fn, &ws)) return st;
+  return run_gated(fn, a, alog_pc, ws, kStaticScratchBytes, static_cast<hipStream_t>(stream));
 }
 
 size_t kda_chunk_prefill_backward_workspace_bytes(int64_t T_tot, int32_t N, int32_t H,

@@ -251,6 +251,34 @@ kda_status kda_chunk_prefill_gated(const void* q, const void* k, const void* v, 
                                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * kda_chunk_prefill_gated_static - kda_chunk_prefill_gated with no workspace
+ * argument, for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * Arguments, results and refusals are those of kda_chunk_prefill_gated.  The
+ * workspace is a device array inside the library of
+ * KDA_PREFILL_STATIC_SCRATCH_BYTES (256 MiB) per GPU, created when the library
+ * is loaded and held until the process ends; the call allocates and frees
+ * nothing.  A batch needs kda_chunk_prefill_workspace_bytes(N, H, 128, 128, 1)
+ * bytes for one chunk per pass (N * H <= 2,131 (sequence, head) pairs): a
+ * larger one is refused with KDA_ERR_WORKSPACE before any HIP call.  Smaller
+ * batches run the chunk axis in as few passes as the array allows (45 chunks
+ * of 64 tokens per pass at N = 1, H = 96; 4 at N = 8).  Every call on one
+ * GPU uses that GPU's one
+ * array: calls that overlap in time on one GPU (two streams, two host threads)
+ * race and must be serialised by the caller.  Nothing in the array is read
+ * before the same call writes it.
+ */
+#define KDA_PREFILL_STATIC_SCRATCH_BYTES (256u << 20)
+kda_status kda_chunk_prefill_gated_static(
+    const void* q, const void* k, const void* v, kda_dtype qkv_dt, const void* x, kda_dtype x_dt,
+    const void* b, kda_dtype b_dt, const float* A_log, int64_t A_log_len, const float* dt_bias,
+    int64_t dt_bias_len, const int32_t* cu_seqlens, const int32_t* cu_seqlens_host, int32_t N,
+    const void* initial_state, void* final_state, kda_dtype state_dt, int64_t num_slots,
+    const int32_t* state_indices, void* o, kda_dtype o_dt, int64_t T_tot, int32_t H, int32_t dk,
+    int32_t dv, float scale, void* stream);
+
+/*
  * kda_chunk_prefill_backward - gradients of kda_chunk_prefill.
  *
  * For the forward of kda_chunk_prefill with the same q, k, v, g, beta,

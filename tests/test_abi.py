@@ -29,7 +29,8 @@ def test_exports_every_declared_symbol():
     L = _lib()
     names = _declared()
     assert set(names) == {"kda_last_error", "kda_version", "kda_gate", "kda_chunk_prefill",
-                          "kda_chunk_prefill_gated", "kda_chunk_prefill_workspace_bytes",
+                          "kda_chunk_prefill_gated", "kda_chunk_prefill_gated_static",
+                          "kda_chunk_prefill_workspace_bytes",
                           "kda_recurrent_decode", "kda_recurrent_decode_gated",
                           "kda_shortconv_l2norm", "kda_chunk_prefill_backward",
                           "kda_chunk_prefill_backward_workspace_bytes", "kda_gate_backward",
@@ -168,6 +169,25 @@ def test_prefill_gated_state_pool_refusals():
     assert _prefill_gated(L, cu, slots=64, idx=DEV[11]) == 1
     assert b"overlaps" in L.kda_last_error()
     assert _prefill_gated(L, cu, S_dt=1, S0=DEV[6], Sf=DEV[6], ws=None) == 6  # bf16, in place
+
+
+def test_prefill_gated_static_refusals():
+    """The no-allocation variant refuses, before any HIP call, a batch with more
+    (sequence, head) pairs than its static scratch holds at one chunk per pass,
+    and everything the gated prefill refuses."""
+    L = _lib()
+
+    def call(N=2, H=4, T=48, A_log_len=None, cu_host=(0, 20, 48)):
+        hp = np.ascontiguousarray(np.asarray(cu_host, dtype=np.int32))
+        return L.kda_chunk_prefill_gated_static(
+            DEV[0], DEV[1], DEV[2], 1, DEV[3], 0, DEV[4], 0, DEV[9],
+            H if A_log_len is None else A_log_len, DEV[10], H * 128, DEV[5], hp.ctypes.data, N,
+            None, DEV[6], 0, N, None, DEV[7], 1, T, H, 128, 128, 1.0, None)
+    cu23 = list(range(24))
+    assert call(N=23, H=96, T=23, cu_host=cu23) == 6          # 2,208 pairs > 2,131
+    assert b"static scratch" in L.kda_last_error()
+    assert call(A_log_len=128) == 2                             # checkpoint-shaped A_log
+    assert call(cu_host=(0, 30, 20), T=20) == 2                 # decreasing cu_seqlens
 
 
 def test_decode_refusals():
