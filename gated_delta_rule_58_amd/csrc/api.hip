@@ -487,6 +487,13 @@ kda_status scratch_for_current_device(const char* fn, void** out) {
   return KDA_OK;
 }
 
+// (sequence, head) pairs the static scratch holds at one chunk per pass
+size_t static_scratch_max_pairs() {
+  const size_t per_pair = kda::chunk_workspace_bytes(2, 1, 1) - kda::chunk_workspace_bytes(1, 1, 1);
+  const size_t fixed = kda::chunk_workspace_bytes(1, 1, 1) - per_pair;
+  return (kStaticScratchBytes - fixed) / per_pair;
+}
+
 }  // namespace
 
 extern "C" {
@@ -506,8 +513,7 @@ kda_status kda_chunk_prefill_gated_static(
                   "%s: N * H = %lld (sequence, head) pairs need %zu bytes of scratch for one "
                   "chunk per pass, more than the static scratch's %zu (at most %zu pairs); use "
                   "kda_chunk_prefill_gated with a workspace",
-                  fn, (long long)N * H, need, kStaticScratchBytes,
-                  kStaticScratchBytes / kda::chunk_workspace_bytes(1, 1, 1));
+                  fn, (long long)N * H, need, kStaticScratchBytes, static_scratch_max_pairs());
   }
   const GatedPrefill a{q, k, v, qkv_dt, x, x_dt, b, b_dt, A_log, A_log_len, dt_bias,
                        dt_bias_len, cu_seqlens, cu_seqlens_host, N, initial_state, final_state,

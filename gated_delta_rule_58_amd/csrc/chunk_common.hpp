@@ -46,6 +46,15 @@ __device__ __forceinline__ f32x4 mma_f16_k16(f16x4 a, f16x4 b, f32x4 c) {
 }
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+// fp32 -> fp16 rounding to nearest even, two values per instruction
+// (v_cvt_pk_f16_f32) where a per-element cast costs a conversion and a pack.
+__device__ __forceinline__ f16x8 cvt_f16(f32x8 x) { return __builtin_convertvector(x, f16x8); }
+__device__ __forceinline__ f16x4 cvt_f16(f32x4 x) { return __builtin_convertvector(x, f16x4); }
+__device__ __forceinline__ f32x8 f32x8_of(const float (&x)[8]) {
+  return f32x8{x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]};
+}
+
 // Orders this wave's LDS writes before its later LDS reads (no workgroup barrier).
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -68,23 +77,14 @@ __device__ __forceinline__ void split_bf16(float x, __bf16& hi, __bf16& lo) {
 // A operand paired with it is read in that same order.
 __device__ __forceinline__ void bfrag_split(const f32x4& t0, const f32x4& t1, f16x8& hi,
                                             f16x8& lo) {
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    _Float16 a, b;
-    split_f16(e < 4 ? t0[e] : t1[e - 4], a, b);
-    hi[e] = a;
-    lo[e] = b;
-  }
+  const f32x8 t = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
+  hi = cvt_f16(t);
+  lo = cvt_f16(t - __builtin_convertvector(hi, f32x8));
 }
 // 16x16x16 B fragment (hi and lo fp16) from one accumulator tile.
 __device__ __forceinline__ void bfrag16_split(const f32x4& t, f16x4& hi, f16x4& lo) {
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    _Float16 a, b;
-    split_f16(t[e], a, b);
-    hi[e] = a;
-    lo[e] = b;
-  }
+  hi = cvt_f16(t);
+  lo = cvt_f16(t - __builtin_convertvector(hi, f32x4));
 }
 
 // Raw buffer resource over [base, base + nbytes): loads past the end return 0

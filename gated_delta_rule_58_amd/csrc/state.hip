@@ -299,10 +299,8 @@ __global__ void __launch_bounds__(NTHR_S, 1) state_kernel(
       for (int rt = 0; rt < 4; ++rt) Xacc[rt] = Oacc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        f16x8 sf;
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          sf[e] = static_cast<_Float16>(e < 4 ? Sacc[2 * kk][e] : Sacc[2 * kk + 1][e - 4]);
+        const f32x4 s0 = Sacc[2 * kk], s1 = Sacc[2 * kk + 1];
+        const f16x8 sf = cvt_f16(f32x8{s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]});
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
           const int po = keqe_frag(rt, kk, lr, lg);
