@@ -27,6 +27,7 @@
 //             chunk's gradients dq, dk, dv, dg, dbeta by the chain rule
 //             through the identities above (the pairwise decay terms of At
 //             and P per key channel, then a reverse cumulative sum for dg).
+#include "chunk_common.hpp"
 #include "kda_device.hpp"
 #include "kda_internal.hpp"
 
@@ -37,6 +38,18 @@ namespace {
 constexpr int C = 64;
 constexpr int D = 128;
 constexpr int NT = 256;
+
+// The per-token decay floor of the forward prefill, in natural-log units: g
+// enters as max(g, -15.5 / log2 e) (the test taken in log2 units, as the
+// forward takes it; NaN passes through), so the backward differentiates the
+// function the forward computes and its decay factors keep their range
+// bounds.  The gradient of a floored g is 0.
+__device__ __forceinline__ bool decay_floored(float g) {
+  return g * chunk::LOG2E < -chunk::DECAY_FLOOR_LOG2;
+}
+__device__ __forceinline__ float floor_decay(float g) {
+  return decay_floored(g) ? -chunk::DECAY_FLOOR_LOG2 / chunk::LOG2E : g;
+}
 
 // Per-(chunk, head) record written by bwd_prep (offsets in floats).
 struct Rec {
@@ -294,6 +307,89 @@ __device__ __forceinline__ float row_at(__amdgpu_buffer_rsrc_t rs, int HDi, int 
     return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (r * HDi + cc) * 4, 0, 0));
 }
 
+// At[r, s] = sum_c k_rc k_sc e^(gamma_rc - gamma_sc) (s < r) and P[r, s] =
+// sum_c q_rc k_sc e^(...) (s <= r) as fp32 16x16x4 MFMA products over 16-row
+// tiles, with the decay split into two factors taken relative to an anchor
+// row a: (k_r e^(gamma_r - gamma_a)) (k_s e^(gamma_a - gamma_s)).
+//  * Tile (i, j < i): a = 16 i - 1, the row before block i; both factors <= 1.
+//  * Diagonal tile (i, i), by quadrants of 8 rows: the top-left and the
+//    bottom-right ones take a = 16 i + 3 and 16 i + 11 (one product, each row
+//    and column with the anchor of its own half), the bottom-left one
+//    a = 16 i + 7 (factors <= 1, a second product); the top-right one lies
+//    above the diagonal.  A factor then spans at most 4 tokens of decay,
+//    below e^43 with the per-token decay floored (DECAY_FLOOR_NAT).  The
+//    first product's mixed-anchor quadrants may overflow; they are dropped.
+// MFMA lanes: lane (ln, lq) supplies A[ln][lq] (row ln of the tile, channel
+// ch) and B[lq][ln] (channel ch, column ln), and holds D[4 lq + v][ln].
+struct AtpDiag {
+  f32x4 a1, p1, a3, p3;  // first product (same-half quadrants), second (bottom-left)
+};
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+constexpr int ATP_LD = 17;  // row stride of the K / Q / gamma slabs (16 channels + 1)
+__device__ __forceinline__ void atp_diag(AtpDiag& d, int i, const float* sK, const float* sQ,
+                                         const float* sG, int ch, int ln) {
+  const int r = 16 * i + ln;
+  const float kr = sK[r * ATP_LD + ch], qr = sQ[r * ATP_LD + ch], gr = sG[r * ATP_LD + ch];
+  const float ga = sG[(16 * i + (ln < 8 ? 3 : 11)) * ATP_LD + ch];
+  const float e1 = __expf(gr - ga), b1 = kr * __expf(ga - gr);
+  d.a1 = mfma4(kr * e1, b1, d.a1);
+  d.p1 = mfma4(qr * e1, b1, d.p1);
+  const float g7 = sG[(16 * i + 7) * ATP_LD + ch];
+  const bool lower = ln >= 8;  // row of the bottom half (A) / column of the top half (B)
+  const float e3 = __expf(lower ? gr - g7 : g7 - gr);
+  const float ka = lower ? kr * e3 : 0.0f, qa = lower ? qr * e3 : 0.0f;
+  const float kb = lower ? 0.0f : kr * e3;
+  d.a3 = mfma4(ka, kb, d.a3);
+  d.p3 = mfma4(qa, kb, d.p3);
+}
+// tiles (i, j) for j < n into slots SLOT0 + j (n <= 3 - SLOT0)
+template <int SLOT0>
+__device__ __forceinline__ void atp_off(f32x4 (&oa)[3], f32x4 (&op)[3], int i, int n,
+                                        const float* sK, const float* sQ, const float* sG,
+                                        int ch, int ln) {
+  if (i == 0) return;
+  const int r = 16 * i + ln;
+  const float gb = sG[(16 * i - 1) * ATP_LD + ch];
+  const float eo = __expf(sG[r * ATP_LD + ch] - gb);
+  const float ka = sK[r * ATP_LD + ch] * eo, qa = sQ[r * ATP_LD + ch] * eo;
+#pragma unroll
+  for (int j = 0; j < 3 - SLOT0; ++j) {
+    if (j < n) {
+      const int s = 16 * j + ln;
+      const float kb = sK[s * ATP_LD + ch] * __expf(gb - sG[s * ATP_LD + ch]);
+      oa[SLOT0 + j] = mfma4(ka, kb, oa[SLOT0 + j]);
+      op[SLOT0 + j] = mfma4(qa, kb, op[SLOT0 + j]);
+    }
+  }
+}
+// store (add = false) or add and finish (add = true) one wave's share of a tile
+__device__ __forceinline__ void atp_put_diag(const AtpDiag& d, int i, float (*sA)[C + 1],
+                                             float (*sP)[C + 1], int ln, int lq, bool add) {
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int rr = 4 * lq + v, r = 16 * i + rr, s = 16 * i + ln;
+    const bool bl = rr >= 8 && ln < 8;
+    float a = bl ? d.a3[v] : d.a1[v], p = bl ? d.p3[v] : d.p1[v];
+    if (add) {
+      a = ln < rr ? a + sA[r][s] : 0.0f;
+      p = ln <= rr ? p + sP[r][s] : 0.0f;
+    }
+    sA[r][s] = a;
+    sP[r][s] = p;
+  }
+}
+__device__ __forceinline__ void atp_put_off(f32x4 a, f32x4 p, int i, int j, float (*sA)[C + 1],
+                                            float (*sP)[C + 1], int ln, int lq, bool add) {
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int r = 16 * i + 4 * lq + v, s = 16 * j + ln;
+    sA[r][s] = add ? a[v] + sA[r][s] : a[v];
+    sP[r][s] = add ? p[v] + sP[r][s] : p[v];
+  }
+}
+
 template <bool QB>
 __global__ void __launch_bounds__(NT, 2) bwd_prep_kernel(const void* __restrict__ q,
                                                          const void* __restrict__ k,
@@ -319,46 +415,48 @@ __global__ void __launch_bounds__(NT, 2) bwd_prep_kernel(const void* __restrict_
   auto Kf = [&](int r, int cc) { return row_at<QB>(rk, HDi, r, cc); };
   auto Qf = [&](int r, int cc) { return row_at<QB>(rq, HDi, r, cc); };
   if (t < C) sB[t] = t < p.Lc ? beta[(p.t0 + t) * H + p.h] : 0.0f;
-  if (t < D) {  // gamma: running sum of g down channel t (rows past the end repeat the last)
+  if (t < D) {  // gamma: running sum of the floored g down channel t (rows past the end repeat the last)
     float gv[C];
 #pragma unroll
     for (int r = 0; r < C; ++r) gv[r] = row_at<false>(rg, HDi, r, t);
     float run = 0.0f;
 #pragma unroll
     for (int r = 0; r < C; ++r) {
-      run += gv[r];
+      run += floor_decay(gv[r]);
       im[Rec::G + r * D + t] = run;
     }
   }
   __syncthreads();
   auto Gf = [&](int r, int cc) { return im[Rec::G + r * D + cc]; };
-  {  // At and P over the strictly lower pairs, folded so that no lane idles:
-     // wave w, step u takes the rows lo = w + 4u and hi = 63 - lo (lo + hi = 63
-     // pairs s < r between them); lane l < lo takes (lo, l), lanes lo .. 62
-     // take (hi, l - lo), and lane 63 the two diagonal entries of P (q_r . k_r,
-     // the decay over zero tokens being 1; At is 0 on the diagonal).
+  {  // At and P (see atp_diag / atp_off): wave w sums the channels of half
+     // w >> 1 for the row blocks {0, 3} (w even) or {1, 2} (w odd), 14
+     // products per 4 channels either way.  Slab sl holds the channels
+     // 8 sl .. 8 sl + 7 (columns 0..7) and 64 + 8 sl .. 64 + 8 sl + 7 (8..15).
     float* sK = sS;
-    float* sQ = sS + C * (CS + 1);
-    float* sG = sS + 2 * C * (CS + 1);
-    constexpr int NU = C / 2 / (NT / 64);  // row pairs per wave
-    const int l = t & 63, w = t >> 6;
-    float a[NU], pp[NU];
-#pragma unroll
-    for (int u = 0; u < NU; ++u) a[u] = pp[u] = 0.0f;
-    // slab c0 is read into registers while the previous one is in use
+    float* sQ = sS + SLAB;
+    float* sG = sS + 2 * SLAB;
+    const int l = t & 63, w = t >> 6, ln = l & 15, lq = l >> 4, hf = w >> 1;
+    const int bA = w & 1, bB = 3 - bA;
+    for (int e = t; e < C * (C + 1); e += NT) {
+      (&sA[0][0])[e] = 0.0f;
+      (&sP[0][0])[e] = 0.0f;
+    }
+    AtpDiag dA{}, dB{};
+    f32x4 oa[3] = {}, op[3] = {};
     constexpr int PS = C * CS / NT;
     float rk[PS], rq[PS], rg[PS];
-    auto fetch_slab = [&](int c0) {
+    auto fetch_slab = [&](int sl) {
 #pragma unroll
       for (int u = 0; u < PS; ++u) {
         const int e = t + NT * u, r = e / CS, ch = e % CS;
-        rk[u] = Kf(r, c0 + ch);
-        rq[u] = Qf(r, c0 + ch);
-        rg[u] = Gf(r, c0 + ch);
+        const int cc = ch < 8 ? 8 * sl + ch : 64 + 8 * sl + ch - 8;
+        rk[u] = Kf(r, cc);
+        rq[u] = Qf(r, cc);
+        rg[u] = Gf(r, cc);
       }
     };
     fetch_slab(0);
-    for (int c0 = 0; c0 < D; c0 += CS) {
+    for (int sl = 0; sl < D / CS; ++sl) {
 #pragma unroll
       for (int u = 0; u < PS; ++u) {
         const int e = t + NT * u, r = e / CS, ch = e % CS;
@@ -366,52 +464,36 @@ __global__ void __launch_bounds__(NT, 2) bwd_prep_kernel(const void* __restrict_
         sQ[r * (CS + 1) + ch] = rq[u];
         sG[r * (CS + 1) + ch] = rg[u];
       }
-      __syncthreads();
-      if (c0 + CS < D) fetch_slab(c0 + CS);
+      barrier_lds();
+      if (sl + 1 < D / CS) fetch_slab(sl + 1);
 #pragma unroll
-      for (int u = 0; u < NU; ++u) {
-        const int lo = w + 4 * u, hi = C - 1 - lo;
-        if (l < C - 1) {
-          const int r = l < lo ? lo : hi, s2 = l < lo ? l : l - lo;
+      for (int kk = 0; kk < 2; ++kk) {
+        const int ch = 8 * hf + 4 * kk + lq;
+        atp_diag(dA, bA, sK, sQ, sG, ch, ln);
+        atp_diag(dB, bB, sK, sQ, sG, ch, ln);
+        // tiles (bB, j < bB) in slots j; tile (1, 0) of the pair {1, 2} in slot 2
+        atp_off<0>(oa, op, bB, bB, sK, sQ, sG, ch, ln);
+        if (bA == 1) atp_off<2>(oa, op, 1, 1, sK, sQ, sG, ch, ln);
+      }
+      barrier_lds();
+    }
+    // the second channel half stores its sums, the first adds its own and
+    // masks the diagonal tiles
+    for (int pass = 1; pass >= 0; --pass) {
+      if (hf == pass) {
+        atp_put_diag(dA, bA, sA, sP, ln, lq, pass == 0);
+        atp_put_diag(dB, bB, sA, sP, ln, lq, pass == 0);
 #pragma unroll
-          for (int ch = 0; ch < CS; ++ch) {
-            const float ks = sK[s2 * (CS + 1) + ch] *
-                             __expf(sG[r * (CS + 1) + ch] - sG[s2 * (CS + 1) + ch]);
-            a[u] = fmaf(sK[r * (CS + 1) + ch], ks, a[u]);
-            pp[u] = fmaf(sQ[r * (CS + 1) + ch], ks, pp[u]);
-          }
-        } else {
-#pragma unroll
-          for (int ch = 0; ch < CS; ++ch) {
-            a[u] = fmaf(sQ[lo * (CS + 1) + ch], sK[lo * (CS + 1) + ch], a[u]);
-            pp[u] = fmaf(sQ[hi * (CS + 1) + ch], sK[hi * (CS + 1) + ch], pp[u]);
-          }
+        for (int j = 0; j < 3; ++j) {
+          const int ti = j < bB ? bB : 1, tj = j < bB ? j : 0;
+          if (j < bB || bA == 1) atp_put_off(oa[j], op[j], ti, tj, sA, sP, ln, lq, pass == 0);
         }
       }
-      __syncthreads();
+      barrier_lds();
     }
-    // each lower pair (r, s) also writes the zero of its mirror (s, r)
-#pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      const int lo = w + 4 * u, hi = C - 1 - lo;
-      if (l < C - 1) {
-        const int r = l < lo ? lo : hi, s2 = l < lo ? l : l - lo;
-        sA[r][s2] = a[u];
-        sP[r][s2] = pp[u];
-        sA[s2][r] = 0.0f;
-        sP[s2][r] = 0.0f;
-        im[Rec::AT + r * C + s2] = a[u];
-        im[Rec::P + r * C + s2] = pp[u];
-        im[Rec::AT + s2 * C + r] = 0.0f;
-        im[Rec::P + s2 * C + r] = 0.0f;
-      } else {
-        sA[lo][lo] = sA[hi][hi] = 0.0f;
-        sP[lo][lo] = a[u];
-        sP[hi][hi] = pp[u];
-        im[Rec::AT + lo * C + lo] = im[Rec::AT + hi * C + hi] = 0.0f;
-        im[Rec::P + lo * C + lo] = a[u];
-        im[Rec::P + hi * C + hi] = pp[u];
-      }
+    for (int e = t; e < C * C; e += NT) {
+      im[Rec::AT + e] = sA[e / C][e % C];
+      im[Rec::P + e] = sP[e / C][e % C];
     }
   }
   __syncthreads();
@@ -435,7 +517,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_prep_kernel(const void* __restrict_
   {  // W = M diag(b) K_E
     float acc[4][8];
     zero(acc);
-    gemm_staged<4, 8, true, true>(acc, C, sa, [&](int r, int s2) { return sM[r][s2]; },
+    gemm_staged2<4, 8, true, true>(acc, C, sa, [&](int r, int s2) { return sM[r][s2]; },
                                   [&](int s2, int cc) {
                                     return sB[s2] * Kf(s2, cc) * __expf(Gf(s2, cc));
                                   });
@@ -447,7 +529,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_prep_kernel(const void* __restrict_
   {  // U = M diag(b) V
     float acc[4][8];
     zero(acc);
-    gemm_staged<4, 8, true, true>(acc, C, sa, [&](int r, int s2) { return sM[r][s2]; },
+    gemm_staged2<4, 8, true, true>(acc, C, sa, [&](int r, int s2) { return sM[r][s2]; },
                                   [&](int s2, int j) {
                                     return sB[s2] * row_at<QB>(rv, HDi, s2, j);
                                   });
@@ -460,7 +542,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_prep_kernel(const void* __restrict_
   {  // Qt = scale (Q_E - P W)
     float acc[4][8];
     zero(acc);
-    gemm_staged<4, 8, true, true>(acc, C, sa, [&](int r, int s2) { return sP[r][s2]; },
+    gemm_staged2<4, 8, true, true>(acc, C, sa, [&](int r, int s2) { return sP[r][s2]; },
                                   [&](int s2, int cc) { return im[Rec::W + s2 * D + cc]; });
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -586,7 +668,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_walk_kernel(
 template <bool QB, bool DOB>
 __global__ void __launch_bounds__(NT, 2) bwd_grad_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
-    const void* __restrict__ d_o, const float* __restrict__ beta,
+    const void* __restrict__ d_o, const float* __restrict__ g, const float* __restrict__ beta,
     const int32_t* __restrict__ cu, int N, int T_tot, int H, int maxnch, float scale,
     const float* __restrict__ img, const float* __restrict__ Srec,
     const float* __restrict__ dSrec, float* __restrict__ scr, float* __restrict__ dq,
@@ -594,12 +676,13 @@ __global__ void __launch_bounds__(NT, 2) bwd_grad_kernel(
     float* __restrict__ dbeta, int64_t item0) {
   __shared__ float sT[C][C + 1], sDP[C][C + 1];
   __shared__ float sB[C], sDB[C], sGC[D];
-  // the products' LDS slabs, then (pairwise phase) K, Q and gamma of a
-  // quarter of the channels and the per-row-group partial sums
-  constexpr int QC = D / 4;
-  __shared__ float sU[3 * C * QC + 8 * QC];
+  __shared__ uint32_t sFl[C][D / 32];  // bit c % 32 of word c / 32: g of (row, c) floored
+  // the products' LDS slabs, then (pairwise phase) K, Q, gamma and the three
+  // accumulators of a 16-channel slab, and the per-wave partial sums
+  constexpr int SC = 16, SS = SC + 1;
+  constexpr int PAIR_FLOATS = 6 * C * SS + 4 * SC;
+  __shared__ float sU[PAIR_FLOATS > STAGE_FLOATS ? PAIR_FLOATS : STAGE_FLOATS];
   float* sa = sU;
-  static_assert(STAGE_FLOATS <= 3 * C * (D / 4) + 8 * (D / 4), "stage fits the union");
   ChunkPos p;
   if (!chunk_of_block(cu, N, T_tot, H, maxnch, p, item0 + blockIdx.x)) return;
   const int t = threadIdx.x;
@@ -630,11 +713,13 @@ __global__ void __launch_bounds__(NT, 2) bwd_grad_kernel(
     sB[t] = t < Lc ? beta[(p.t0 + t) * H + p.h] : 0.0f;
     sDB[t] = 0.0f;
   }
+  (&sFl[0][0])[t] = 0u;
+  static_assert(C * (D / 32) == NT, "one flag word per thread");
   __syncthreads();
   {  // X = V - K_E S
     float acc[4][8];
     zero(acc);
-    gemm_staged<4, 8, true, true>(acc, D, sa,
+    gemm_staged2<4, 8, true, true>(acc, D, sa,
                                   [&](int r, int cc) { return Kf(r, cc) * __expf(Gf(r, cc)); },
                                   [&](int cc, int j) { return S[cc * D + j]; });
 #pragma unroll
@@ -649,17 +734,17 @@ __global__ void __launch_bounds__(NT, 2) bwd_grad_kernel(
   {  // Delta = M diag(b) X
     float acc[4][8];
     zero(acc);
-    gemm_staged<4, 8, true, true>(acc, C, sa, [&](int r, int s) { return im[Rec::M + r * C + s]; },
+    gemm_staged2<4, 8, true, true>(acc, C, sa, [&](int r, int s) { return im[Rec::M + r * C + s]; },
                                   [&](int s, int j) { return sB[s] * sc[Scr::X + s * D + j]; });
     put8(acc, Scr::DL, 1.0f);
   }
   {  // dDelta = K_D dS_next + scale P^T dO
     float acc[4][8];
     zero(acc);
-    gemm_staged<4, 8, true, true>(acc, D, sa,
+    gemm_staged2<4, 8, true, true>(acc, D, sa,
                                   [&](int r, int cc) { return im[Rec::KD + r * D + cc]; },
                                   [&](int cc, int j) { return dS[cc * D + j]; });
-    gemm_staged<4, 8, false, true>(acc, C, sa,
+    gemm_staged2<4, 8, false, true>(acc, C, sa,
                                    [&](int r, int s) { return scale * im[Rec::P + s * C + r]; },
                                    [&](int s, int j) { return dOf(s, j); });
     put8(acc, Scr::DD, 1.0f);
@@ -668,7 +753,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_grad_kernel(
   {  // dY = M^T dDelta, dX = diag(b) dY (= dv), dbeta += rowsum(dY . X)
     float acc[4][8];
     zero(acc);
-    gemm_staged<4, 8, false, true>(acc, C, sa,
+    gemm_staged2<4, 8, false, true>(acc, C, sa,
                                    [&](int r, int s) { return im[Rec::M + s * C + r]; },
                                    [&](int s, int j) { return sc[Scr::DD + s * D + j]; });
 #pragma unroll
@@ -692,7 +777,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_grad_kernel(
   {  // dM = dDelta Y^T
     float a4[4][4];
     zero(a4);
-    gemm_staged<4, 4, true, false>(a4, D, sa,
+    gemm_staged2<4, 4, true, false>(a4, D, sa,
                                    [&](int r, int j) { return sc[Scr::DD + r * D + j]; },
                                    [&](int j, int s) { return sB[s] * sc[Scr::X + s * D + j]; });
 #pragma unroll
@@ -703,7 +788,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_grad_kernel(
   {  // dP = scale dO Delta^T on s <= r
     float a4[4][4];
     zero(a4);
-    gemm_staged<4, 4, true, false>(a4, D, sa, [&](int r, int j) { return dOf(r, j); },
+    gemm_staged2<4, 4, true, false>(a4, D, sa, [&](int r, int j) { return dOf(r, j); },
                                    [&](int j, int s) { return sc[Scr::DL + s * D + j]; });
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -718,7 +803,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_grad_kernel(
   {  // dM M^T
     float a4[4][4];
     zero(a4);
-    gemm_staged<4, 4, true, false>(a4, C, sa, [&](int r, int u) { return sT[r][u]; },
+    gemm_staged2<4, 4, true, false>(a4, C, sa, [&](int r, int u) { return sT[r][u]; },
                                    [&](int u, int s) { return im[Rec::M + s * C + u]; });
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -729,7 +814,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_grad_kernel(
   {  // dA = -M^T (dM M^T) on s < r
     float a4[4][4];
     zero(a4);
-    gemm_staged<4, 4, false, true>(a4, C, sa,
+    gemm_staged2<4, 4, false, true>(a4, C, sa,
                                    [&](int r, int u) { return im[Rec::M + u * C + r]; },
                                    [&](int u, int s) { return dMMt[u * C + s]; });
 #pragma unroll
@@ -743,7 +828,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_grad_kernel(
   {  // dK_E = -dX S^T
     float acc[4][8];
     zero(acc);
-    gemm_staged<4, 8, true, false>(acc, D, sa,
+    gemm_staged2<4, 8, true, false>(acc, D, sa,
                                    [&](int r, int j) { return sc[Scr::DX + r * D + j]; },
                                    [&](int j, int cc) { return S[cc * D + j]; });
     put8(acc, Scr::DKE, -1.0f);
@@ -751,14 +836,14 @@ __global__ void __launch_bounds__(NT, 2) bwd_grad_kernel(
   {  // dQ_E = scale dO S^T
     float acc[4][8];
     zero(acc);
-    gemm_staged<4, 8, true, false>(acc, D, sa, [&](int r, int j) { return dOf(r, j); },
+    gemm_staged2<4, 8, true, false>(acc, D, sa, [&](int r, int j) { return dOf(r, j); },
                                    [&](int j, int cc) { return S[cc * D + j]; });
     put8(acc, Scr::DQE, scale);
   }
   {  // dK_D = Delta dS_next^T
     float acc[4][8];
     zero(acc);
-    gemm_staged<4, 8, true, false>(acc, D, sa,
+    gemm_staged2<4, 8, true, false>(acc, D, sa,
                                    [&](int r, int j) { return sc[Scr::DL + r * D + j]; },
                                    [&](int j, int cc) { return dS[cc * D + j]; });
     put8(acc, Scr::DKD, 1.0f);
@@ -790,81 +875,158 @@ __global__ void __launch_bounds__(NT, 2) bwd_grad_kernel(
     if (half == 0) sGC[cc] = (d + sU[cc]) * __expf(Gf(C - 1, cc));
     __syncthreads();
   }
-  // The pairwise terms, a quarter of the channels at a time: thread (channel
-  // cc of the quarter, row group grp) finishes the rows x = grp, grp + 8, ...:
-  // the decay-factor terms of K_E, Q_E, K_D, then the pairwise terms of At
-  // and P with x as the later token (s <= x) and as the earlier one (r >= x).
-  float* sK = sU;
-  float* sQ = sU + C * QC;
-  float* sG = sU + 2 * C * QC;
-  float* sPart = sU + 3 * C * QC;  // [8][QC]
-  const int cl = t & (QC - 1), grp = t >> 5;
-  for (int quarter = 0; quarter < 4; ++quarter) {
-    const int c0 = quarter * QC;
-    for (int e = t; e < C * QC; e += NT) {
-      const int r = e / QC, ch = c0 + e % QC;
-      sK[e] = Kf(r, ch);
-      sQ[e] = Qf(r, ch);
-      sG[e] = Gf(r, ch);
-    }
-    __syncthreads();
-    const int cc = c0 + cl;
-    const float gC = sG[(C - 1) * QC + cl];
-    float dgC = 0.0f;
-    float nke = 0.0f, nqe = 0.0f, nkd = 0.0f;  // the next row's terms, read ahead
-    if (grp < Lc) {
-      nke = sc[Scr::DKE + grp * D + cc];
-      nqe = sc[Scr::DQE + grp * D + cc];
-      nkd = sc[Scr::DKD + grp * D + cc];
-    }
-    for (int x = grp; x < Lc; x += 8) {
-      const float kx = sK[x * QC + cl], qx = sQ[x * QC + cl], gx = sG[x * QC + cl];
-      const float E = __expf(gx), F = __expf(gC - gx);
-      const float dke = nke, dqe = nqe, dkd = nkd;
-      if (x + 8 < Lc) {
-        nke = sc[Scr::DKE + (x + 8) * D + cc];
-        nqe = sc[Scr::DQE + (x + 8) * D + cc];
-        nkd = sc[Scr::DKD + (x + 8) * D + cc];
-      }
-      float dkx = dke * E + dkd * F;
-      float dgx = (dke * kx + dqe * qx) * E - dkd * kx * F;
-      float dqx = dqe * E;
-      dgC = fmaf(dkd * kx, F, dgC);
-      // sT rows carry beta of the row and are 0 on and above the diagonal;
-      // the row's factors (kx, qx) multiply the two sums once at the end
-      float sum_at = 0.0f, sum_p = 0.0f;
-#pragma unroll 4
-      for (int s2 = 0; s2 <= x; ++s2) {  // x later: pairs (x, s)
-        const float u = __expf(gx - sG[s2 * QC + cl]) * sK[s2 * QC + cl];
-        sum_at = fmaf(sT[x][s2], u, sum_at);
-        sum_p = fmaf(sDP[x][s2], u, sum_p);
-      }
-      dkx += sum_at;
-      dqx += sum_p;
-      dgx += sum_at * kx + sum_p * qx;
-      float sum_e = 0.0f;
-#pragma unroll 4
-      for (int r = x; r < Lc; ++r) {  // x earlier: pairs (r, x)
-        const float w = __expf(sG[r * QC + cl] - gx);
-        const float phi = sT[r][x] * sK[r * QC + cl] + sDP[r][x] * sQ[r * QC + cl];
-        sum_e = fmaf(phi, w, sum_e);
-      }
-      dkx += sum_e;
-      dgx -= sum_e * kx;
-      dq[tok(x, cc)] = dqx;
-      dk[tok(x, cc)] = dkx;
-      sc[Scr::DX + x * D + cc] = dgx;  // dgamma, summed below
-    }
-    sPart[grp * QC + cl] = dgC;
-    __syncthreads();
-    if (t < QC) {
-      float a = 0.0f;
+  // The terms of the decay factors and the pairwise terms of At and P, 16
+  // channels at a time.  For a row x and channel c (w(a, b) = e^(gamma_a -
+  // gamma_b) <= 1 for a >= b):
+  //   L1[x] = sum_{s < x} dA~[x, s] k_s w(x, s)     (dA~: dA with beta_x folded in)
+  //   L2[x] = sum_{s <= x} dP[x, s] k_s w(x, s)
+  //   R[x]  = sum_{r >= x} (dA~[r, x] k_r + dP[r, x] q_r) w(r, x)
+  //   dk += L1 + R,  dq += L2,  dgamma += k L1 + q L2 - k R.
+  // For x in 16-row block i and s in an earlier block, w(x, s) = w(x, b)
+  // w(b, s) with b the row before block i, both <= 1: L1 and L2 of block i are
+  // products of the dA~ / dP rows with the right factors k_s w(b, s) over all
+  // earlier rows, scaled by w(x, b) (fp32 MFMA).  Likewise R of block j uses
+  // e, the block's last row: (dA~ / dP columns)^T times k_r w(r, e) and
+  // q_r w(r, e) over all later rows, scaled by w(e, x).  Pairs inside one
+  // block take w directly (a pair's factors could both be huge there).
+  float* sK = sU;                  // [C][SS] k of the slab's channels
+  float* sQ = sK + C * SS;         // q
+  float* sG = sQ + C * SS;         // gamma
+  float* aK = sG + C * SS;         // dk, dq and dgamma of the slab, accumulated
+  float* aQ = aK + C * SS;
+  float* aG = aQ + C * SS;
+  float* sPart = aG + C * SS;      // [4][SC] partial sums of the gamma_C term
+  const int lane = t & 63, w = t >> 6, ln = lane & 15, lq = lane >> 4;
+  // Thread t holds rows x = t / 16 + 16 m (m < 4) of channel t % 16 of the
+  // slab: k, q, gamma and the three decay-factor gradients, read one slab
+  // ahead so that the reads stay in flight across the slab's barriers (which
+  // order LDS only).
+  const int n16 = t & 15, x16 = t >> 4;
+  float pk[4], pq[4], pg[4], pke[4], pqe[4], pkd[4], pgc;
+  bool pfl[4];
+  auto fetch_slab = [&](int c0) {
+    pgc = Gf(C - 1, c0 + n16);
 #pragma unroll
-      for (int g2 = 0; g2 < 8; ++g2) a += sPart[g2 * QC + t];
-      sGC[c0 + t] += a;
+    for (int m = 0; m < 4; ++m) {
+      const int x = x16 + 16 * m, cc = c0 + n16;
+      pk[m] = Kf(x, cc);
+      pq[m] = Qf(x, cc);
+      pg[m] = Gf(x, cc);
+      pke[m] = sc[Scr::DKE + x * D + cc];
+      pqe[m] = sc[Scr::DQE + x * D + cc];
+      pkd[m] = sc[Scr::DKD + x * D + cc];
+      pfl[m] = x < Lc && decay_floored(g[tok(x, cc)]);
     }
-    __syncthreads();  // sK / sQ / sG / sPart are refilled for the next quarter
+  };
+  fetch_slab(0);
+  for (int c0 = 0; c0 < D; c0 += SC) {
+    {  // the slab to LDS, and the decay-factor terms of K_E, Q_E, K_D
+      float dgC = 0.0f;
+      const float gC = pgc;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int x = x16 + 16 * m;
+        const float kx = pk[m], qx = pq[m], gx = pg[m];
+        sK[x * SS + n16] = kx;
+        sQ[x * SS + n16] = qx;
+        sG[x * SS + n16] = gx;
+        float vk = 0.0f, vq = 0.0f, vg = 0.0f;
+        if (x < Lc) {
+          const float dke = pke[m], dqe = pqe[m], dkd = pkd[m];
+          const float E = __expf(gx), F = __expf(gC - gx);
+          vk = dke * E + dkd * F;
+          vq = dqe * E;
+          vg = (dke * kx + dqe * qx) * E - dkd * kx * F;
+          dgC = fmaf(dkd * kx, F, dgC);
+        }
+        aK[x * SS + n16] = vk;
+        aQ[x * SS + n16] = vq;
+        aG[x * SS + n16] = vg;
+        if (pfl[m]) atomicOr(&sFl[x][(c0 + n16) >> 5], 1u << ((c0 + n16) & 31));
+      }
+      dgC += __shfl_xor(dgC, 16);
+      dgC += __shfl_xor(dgC, 32);
+      if (lane < 16) sPart[w * SC + lane] = dgC;
+    }
+    barrier_lds();
+    if (c0 + SC < D) fetch_slab(c0 + SC);
+    {  // pairs across blocks on fp32 MFMA: wave w owns the rows of block w.
+       // Lane l supplies A[l % 16][l / 16] and B[l / 16][l % 16] and holds
+       // D[4 (l / 16) + v][l % 16]; n = l % 16 is the channel of B and D.
+      f32x4 L1 = {0.f, 0.f, 0.f, 0.f}, L2 = L1, R = L1;
+      if (w >= 1) {  // s < 16 w, reference b = 16 w - 1
+        const int b = 16 * w - 1;
+        const float gb = sG[b * SS + ln];
+        for (int ks = 0; ks < 4 * w; ++ks) {
+          const int s2 = 4 * ks + lq;
+          const float bv = sK[s2 * SS + ln] * __expf(gb - sG[s2 * SS + ln]);
+          L1 = __builtin_amdgcn_mfma_f32_16x16x4f32(sT[16 * w + ln][s2], bv, L1, 0, 0, 0);
+          L2 = __builtin_amdgcn_mfma_f32_16x16x4f32(sDP[16 * w + ln][s2], bv, L2, 0, 0, 0);
+        }
+      }
+      if (w <= 2) {  // r >= 16 (w + 1), reference e = 16 w + 15
+        const int e = 16 * w + 15;
+        const float ge = sG[e * SS + ln];
+        for (int ks = 4 * (w + 1); ks < C / 4; ++ks) {
+          const int r = 4 * ks + lq;
+          const float wr = __expf(sG[r * SS + ln] - ge);
+          R = __builtin_amdgcn_mfma_f32_16x16x4f32(sT[r][16 * w + ln], sK[r * SS + ln] * wr, R,
+                                                   0, 0, 0);
+          R = __builtin_amdgcn_mfma_f32_16x16x4f32(sDP[r][16 * w + ln], sQ[r * SS + ln] * wr, R,
+                                                   0, 0, 0);
+        }
+      }
+      const float gb = w >= 1 ? sG[(16 * w - 1) * SS + ln] : 0.0f;
+      const float ge = sG[(16 * w + 15) * SS + ln];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int x = 16 * w + 4 * lq + v;
+        const float gx = sG[x * SS + ln];
+        const float l1 = w >= 1 ? L1[v] * __expf(gx - gb) : 0.0f;
+        const float l2 = w >= 1 ? L2[v] * __expf(gx - gb) : 0.0f;
+        const float rr = w <= 2 ? R[v] * __expf(ge - gx) : 0.0f;
+        const float kx = sK[x * SS + ln], qx = sQ[x * SS + ln];
+        aK[x * SS + ln] += l1 + rr;
+        aQ[x * SS + ln] += l2;
+        aG[x * SS + ln] += kx * l1 + qx * l2 - kx * rr;
+      }
+    }
+    barrier_lds();
+    {  // pairs inside a block, w taken directly: thread (block i, channel n)
+       // of combo t / 4 takes the 4 rows 16 i + 4 (t % 4) + 0..3 (68 pairs a thread)
+      const int combo = t >> 2, i = combo >> 4, n = combo & 15, x0 = 16 * i + 4 * (t & 3);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int x = x0 + v;
+        const float gx = sG[x * SS + n], kx = sK[x * SS + n], qx = sQ[x * SS + n];
+        float l1 = 0.0f, l2 = 0.0f, rr = 0.0f;
+        for (int s2 = 16 * i; s2 <= x; ++s2) {
+          const float u = __expf(gx - sG[s2 * SS + n]) * sK[s2 * SS + n];
+          l1 = fmaf(sT[x][s2], u, l1);  // 0 on the diagonal
+          l2 = fmaf(sDP[x][s2], u, l2);
+        }
+        for (int r = x; r < 16 * i + 16; ++r) {
+          const float wr = __expf(sG[r * SS + n] - gx);
+          rr = fmaf(fmaf(sT[r][x], sK[r * SS + n], sDP[r][x] * sQ[r * SS + n]), wr, rr);
+        }
+        aK[x * SS + n] += l1 + rr;
+        aQ[x * SS + n] += l2;
+        aG[x * SS + n] += kx * l1 + qx * l2 - kx * rr;
+      }
+    }
+    barrier_lds();
+    for (int e = t; e < C * SC; e += NT) {
+      const int x = e / SC, ch = e % SC;
+      if (x < Lc) {
+        dq[tok(x, c0 + ch)] = aQ[x * SS + ch];
+        dk[tok(x, c0 + ch)] = aK[x * SS + ch];
+        sc[Scr::DX + x * D + c0 + ch] = aG[x * SS + ch];  // dgamma, summed below
+      }
+    }
+    if (t < SC) sGC[c0 + t] += sPart[t] + sPart[SC + t] + sPart[2 * SC + t] + sPart[3 * SC + t];
+    barrier_lds();  // the slab's arrays are refilled for the next 16 channels
   }
+  __syncthreads();  // dgamma (scratch) complete
   if (t < D) {  // dg: reverse cumulative sum of dgamma, plus the gamma_C terms
     const int cc = t;
     float dgam[C];
@@ -874,7 +1036,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_grad_kernel(
 #pragma unroll
     for (int x = C - 1; x >= 0; --x) {
       run += dgam[x];
-      if (x < Lc) dg[tok(x, cc)] = run;
+      if (x < Lc) dg[tok(x, cc)] = (sFl[x][cc >> 5] >> (cc & 31)) & 1u ? 0.0f : run;
     }
   }
   if (t < Lc) dbeta[(p.t0 + t) * H + p.h] = sDB[t];
@@ -937,7 +1099,7 @@ hipError_t launch(const void* q, const void* k, const void* v, bool qkv_bf16, co
     const int64_t nb = chunk_blocks - item0 < GRAD_SLOTS ? chunk_blocks - item0 : GRAD_SLOTS;
 #define KDA_BG(QB, OB)                                                                        \
   bwd_grad_kernel<QB, OB><<<dim3((unsigned)nb), NT, 0, s>>>(                                  \
-      q, k, v, d_o, beta, cu, N, T, H, (int)maxnch, scale, img, Srec, dSrec, scr, dq, dk, dv, \
+      q, k, v, d_o, g, beta, cu, N, T, H, (int)maxnch, scale, img, Srec, dSrec, scr, dq, dk, dv, \
       dg, dbeta, item0)
     if (qkv_bf16 && do_bf16) KDA_BG(true, true);
     else if (qkv_bf16) KDA_BG(true, false);

@@ -127,6 +127,36 @@ def test_backward_strong_decay_heads():
     check(got, ref, "strong decay")
 
 
+def test_backward_below_decay_floor():
+    """Per-token decays below the forward prefill's floor (g < -15.5 / log2 e,
+    about -10.74 nats; the floor test taken in fp32 on g * log2 e, as the
+    kernels take it) on a tenth of the (token, channel) entries, down to -41:
+    the backward differentiates the floored recurrence that the forward
+    computes, so it matches the oracle's gradient at the floored g, with dg = 0
+    where the floor is active (the derivative of max(g, floor) there)."""
+    need_gpu()
+    say("backward below the decay floor")
+    dr = draw_prefill([150, 77], H=2, dtype=torch.bfloat16, init_state=True, seed=89)
+    g, beta = oracle_gate_f32(dr)
+    r = torch.Generator().manual_seed(90)
+    hit = torch.rand(g.shape, generator=r) < 0.1
+    g = torch.where(hit, -11.0 - 30.0 * torch.rand(g.shape, generator=r), g).float()
+    log2e = torch.tensor(1.4426950408889634, dtype=torch.float32)
+    floored = g * log2e < -15.5
+    gf = torch.where(floored, torch.tensor(-15.5, dtype=torch.float32) / log2e, g)
+    assert floored.float().mean() > 0.05
+    d_o = torch.randn(dr.q.shape[0], 2, 128, generator=r)
+    dSf = torch.randn(2, 2, 128, 128, generator=r) * 0.1
+    got = _run(dr, g, beta, d_o, dSf, 1.0)
+    for a in got:
+        assert torch.isfinite(a).all()
+    ref = list(oracle.prefill_backward(dr.q, dr.k, dr.v, gf, beta, dr.cu_seqlens,
+                                       dr.initial_state, d_o=d_o, dS_final=dSf))
+    ref[3] = np.where(floored.numpy(), 0.0, ref[3])
+    check(got, ref, "below the decay floor")
+    assert torch.all(got[3].cpu()[floored] == 0)
+
+
 def test_backward_config2_varlen_sampled_heads():
     """8 sequences, 32,768 tokens, initial states (the varlen prefill
     workload): the whole backward on the GPU, sampled heads against the
