@@ -976,42 +976,71 @@ __global__ void __launch_bounds__(NT, 2) bwd_grad_kernel(
                                                    0, 0, 0);
         }
       }
+      // Pairs inside block w, by 8-row halves as in the prep's diagonal At / P
+      // tiles: same-half pairs relative to the half's anchor a (rows 3 and 11
+      // of the block: at most 4 tokens from any row of the half), pairs across
+      // the halves relative to row 7 (factors <= 1).  Each product's operand
+      // A is masked to its pairs; with L the later row:
+      //   Ls / Lx: rows x, columns s <= x, B = k_s e^(gamma_a(s) - gamma_s) /
+      //            k_s e^(gamma_7 - gamma_s), scaled by e^(gamma_x - gamma_a(x)) /
+      //            e^(gamma_x - gamma_7);
+      //   Rs / Rx: rows x, columns r >= x (A transposed), B = (k_r, q_r)
+      //            e^(gamma_r - gamma_a(r)) / e^(gamma_r - gamma_7), scaled by
+      //            e^(gamma_a(x) - gamma_x) / e^(gamma_7 - gamma_x).
+      f32x4 L1s = {0.f, 0.f, 0.f, 0.f}, L2s = L1s, L1x = L1s, L2x = L1s, Rs = L1s, Rx = L1s;
+      {
+        const int x = 16 * w + ln;
+        const float g7 = sG[(16 * w + 7) * SS + ln];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const int sl = 4 * ks + lq, s2 = 16 * w + sl;  // k index of A, row of B
+          const bool same = (ln < 8) == (sl < 8);
+          const bool cl = ln >= 8 && sl < 8, cr = ln < 8 && sl >= 8;
+          const float gs = sG[s2 * SS + ln], ks2 = sK[s2 * SS + ln], qs2 = sQ[s2 * SS + ln];
+          const float ga = sG[(16 * w + (sl < 8 ? 3 : 11)) * SS + ln];
+          const float fa = __expf(ga - gs), ea = __expf(gs - ga);
+          const float e7 = __expf(sl < 8 ? g7 - gs : gs - g7);
+          const float ta = sT[x][s2], tp = sDP[x][s2];      // A of L: (x, s)
+          const float ua = sT[s2][x], up = sDP[s2][x];      // A of R: (r, x)
+          const float b1 = ks2 * fa, b3 = sl < 8 ? ks2 * e7 : 0.0f;
+          L1s = __builtin_amdgcn_mfma_f32_16x16x4f32(same ? ta : 0.0f, b1, L1s, 0, 0, 0);
+          L2s = __builtin_amdgcn_mfma_f32_16x16x4f32(same ? tp : 0.0f, b1, L2s, 0, 0, 0);
+          L1x = __builtin_amdgcn_mfma_f32_16x16x4f32(cl ? ta : 0.0f, b3, L1x, 0, 0, 0);
+          L2x = __builtin_amdgcn_mfma_f32_16x16x4f32(cl ? tp : 0.0f, b3, L2x, 0, 0, 0);
+          Rs = __builtin_amdgcn_mfma_f32_16x16x4f32(same ? ua : 0.0f, ks2 * ea, Rs, 0, 0, 0);
+          Rs = __builtin_amdgcn_mfma_f32_16x16x4f32(same ? up : 0.0f, qs2 * ea, Rs, 0, 0, 0);
+          const float rk = sl >= 8 ? ks2 * e7 : 0.0f, rq = sl >= 8 ? qs2 * e7 : 0.0f;
+          Rx = __builtin_amdgcn_mfma_f32_16x16x4f32(cr ? ua : 0.0f, rk, Rx, 0, 0, 0);
+          Rx = __builtin_amdgcn_mfma_f32_16x16x4f32(cr ? up : 0.0f, rq, Rx, 0, 0, 0);
+        }
+      }
       const float gb = w >= 1 ? sG[(16 * w - 1) * SS + ln] : 0.0f;
       const float ge = sG[(16 * w + 15) * SS + ln];
+      const float g7 = sG[(16 * w + 7) * SS + ln];
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int x = 16 * w + 4 * lq + v;
+        const int xl = 4 * lq + v, x = 16 * w + xl;
         const float gx = sG[x * SS + ln];
-        const float l1 = w >= 1 ? L1[v] * __expf(gx - gb) : 0.0f;
-        const float l2 = w >= 1 ? L2[v] * __expf(gx - gb) : 0.0f;
-        const float rr = w <= 2 ? R[v] * __expf(ge - gx) : 0.0f;
+        const float gax = sG[(16 * w + (xl < 8 ? 3 : 11)) * SS + ln];
+        const float ex = __expf(gx - gax), fx = __expf(gax - gx);
+        const float e7 = __expf(xl < 8 ? g7 - gx : gx - g7);  // <= 1 either way
+        float l1 = L1s[v] * ex, l2 = L2s[v] * ex, rr = Rs[v] * fx;
+        if (xl >= 8) {
+          l1 += L1x[v] * e7;
+          l2 += L2x[v] * e7;
+        } else {
+          rr += Rx[v] * e7;
+        }
+        if (w >= 1) {
+          const float eb = __expf(gx - gb);
+          l1 += L1[v] * eb;
+          l2 += L2[v] * eb;
+        }
+        if (w <= 2) rr += R[v] * __expf(ge - gx);
         const float kx = sK[x * SS + ln], qx = sQ[x * SS + ln];
         aK[x * SS + ln] += l1 + rr;
         aQ[x * SS + ln] += l2;
         aG[x * SS + ln] += kx * l1 + qx * l2 - kx * rr;
-      }
-    }
-    barrier_lds();
-    {  // pairs inside a block, w taken directly: thread (block i, channel n)
-       // of combo t / 4 takes the 4 rows 16 i + 4 (t % 4) + 0..3 (68 pairs a thread)
-      const int combo = t >> 2, i = combo >> 4, n = combo & 15, x0 = 16 * i + 4 * (t & 3);
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int x = x0 + v;
-        const float gx = sG[x * SS + n], kx = sK[x * SS + n], qx = sQ[x * SS + n];
-        float l1 = 0.0f, l2 = 0.0f, rr = 0.0f;
-        for (int s2 = 16 * i; s2 <= x; ++s2) {
-          const float u = __expf(gx - sG[s2 * SS + n]) * sK[s2 * SS + n];
-          l1 = fmaf(sT[x][s2], u, l1);  // 0 on the diagonal
-          l2 = fmaf(sDP[x][s2], u, l2);
-        }
-        for (int r = x; r < 16 * i + 16; ++r) {
-          const float wr = __expf(sG[r * SS + n] - gx);
-          rr = fmaf(fmaf(sT[r][x], sK[r * SS + n], sDP[r][x] * sQ[r * SS + n]), wr, rr);
-        }
-        aK[x * SS + n] += l1 + rr;
-        aQ[x * SS + n] += l2;
-        aG[x * SS + n] += kx * l1 + qx * l2 - kx * rr;
       }
     }
     barrier_lds();
