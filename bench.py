@@ -44,6 +44,16 @@ PREFILL_BYTES = T * PREFILL_TOKEN_BYTES + H * D * D * 4 + H * 4 + H * D * 4   # 
 # U 258,048, W 258,048, W.S / Qt.S / Khat^T.Delta 1,048,576 each, P.Delta 266,240
 MAC_PER_CHUNK_HEAD = 4_494_016
 PREFILL_FLOPS = 2 * MAC_PER_CHUNK_HEAD * (T // C) * H                 # 5.52e10
+# backward, algorithmic MACs per (chunk, head) at C=64 (triangular factors
+# counted by their nonzeros, products the kernels form densely counted dense):
+#   prep   At 258,048, P 266,240, (I + A)^-1 41,664, W / U / Qt 266,240 each
+#   walks  forward and backward, 3 products of 1,048,576 each per direction
+#   grad   X, K_D dS, dK_E, dQ_E, dK_D 1,048,576 each; Delta, P^T dO, dY, dM, dP
+#          266,240 each; dM M^T, dA 262,144 each; the pairwise At / P terms
+#          (4 sums over the lower pairs x 128 channels) 1,048,576
+BWD_MAC_PER_CHUNK_HEAD = 1_364_672 + 6_291_456 + 8_146_944            # 15,803,072
+BWD_FLOPS = 2 * BWD_MAC_PER_CHUNK_HEAD * (T // C) * H                 # 1.94e11
+MFMA_F32_PEAK_TFLOPS = 157.3
 # decode: per (sequence, head, step) state read + write, q/k/v bf16, g f32, beta, o bf16
 DEC_N, DEC_STEPS = 256, 64
 DEC_PAIR_BYTES = 2 * D * D * 4 + 3 * D * 2 + D * 4 + 4 + D * 2       # 132,612
@@ -98,7 +108,7 @@ def parse():
     ap.add_argument("--ws-chunks", type=int, default=T // C,
                     help="chunks per pass the prefill workspace holds (T/64 = one pass)")
     ap.add_argument("--only", choices=["all", "prefill", "decode", "prologue", "workloads",
-                                       "backward", "copy"],
+                                       "backward", "copy", "states"],
                     default="all",
                     help="profiling aid: run one part only (prints a diagnostic line, "
                          "not the bench line)")
@@ -177,6 +187,49 @@ def bench_prefill(args, torch, kda, synth):
     p95 = lambda x: sorted(x)[int(0.95 * (len(x) - 1))]
     return dict(step_ms=mean(fsteps), p95_step_ms=p95(fsteps), fused_ms=mean(fz),
                 sep_step_ms=mean(ssteps), chunk_ms=mean(ch), gate_ms=mean(gt))
+
+
+def bench_prefill_states(args, torch, kda, synth):
+    """kda_chunk_prefill_gated on the T=4096, H=96 workload with the three state
+    modes a serving stack uses: no state (neither initial nor final), fp32
+    initial and final states, bf16 initial and final states (the initial ones
+    drawn N(0, 0.02) per sequence and head)."""
+    dev = "cuda:0"
+    dr = synth.draw_config(1, device=dev)
+    cu_h = dr.cu_seqlens
+    cu_d = cu_h.to(dev)
+    ws = torch.empty(kda.chunk_prefill_workspace_bytes(1, H, D, D, args.ws_chunks),
+                     dtype=torch.uint8, device=dev)
+    o = torch.empty((T, H, D), dtype=torch.bfloat16, device=dev)
+    S0 = torch.randn((1, H, D, D), generator=torch.Generator(device=dev).manual_seed(11),
+                     device=dev) * 0.02
+    modes = {"none": (None, None),
+             "fp32": (S0, torch.empty_like(S0)),
+             "bf16": (S0.to(torch.bfloat16), torch.empty_like(S0, dtype=torch.bfloat16))}
+    out = {}
+    for name, (si, sf) in modes.items():
+        def call():
+            kda.chunk_prefill_gated(dr.q, dr.k, dr.v, dr.x, dr.b, dr.A_log, dr.dt_bias, cu_d, si,
+                                    output_final_state=sf is not None, out=o, final_state=sf,
+                                    cu_seqlens_host=cu_h, workspace=ws)
+        for _ in range(args.warmup):
+            call()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(args.repeats):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+            ev[0].record()
+            for i in range(args.steps):
+                call()
+                ev[i + 1].record()
+            torch.cuda.synchronize()
+            times += [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
+        ms = sum(times) / len(times)
+        es = 0 if si is None else si.element_size()
+        nbytes = T * PREFILL_TOKEN_BYTES + 2 * H * D * D * es + H * 4 + H * D * 4
+        out[name] = dict(ms=ms, tokens_per_s=T / (ms * 1e-3), alg_bytes=nbytes,
+                         alg_GBps=nbytes / (ms * 1e-3) / 1e9)
+    return out
 
 
 def bench_prefill_workload(args, torch, kda, synth, idx):
@@ -361,8 +414,14 @@ def bench_backward(args, torch, kda, synth):
     # q, k, v, d_o bf16 + g fp32 + beta in; dq, dk, dv, dg fp32 + dbeta out
     nbytes = T * H * (D * (3 * 2 + 2 + 4 + 4 * 4) + 4 + 4)
     gbs = nbytes / (ms * 1e-3) / 1e9
+    tf = BWD_FLOPS / (ms * 1e-3) / 1e12
     return dict(ms=ms, tokens_per_s=T / (ms * 1e-3), GBps=gbs, frac=gbs / HBM_PEAK_GBS,
-                bytes=nbytes, workspace_bytes=ws.numel())
+                bytes=nbytes, workspace_bytes=ws.numel(),
+                roofline={"bound": "mfma", "achieved": tf, "peak": MFMA_F32_PEAK_TFLOPS,
+                          "unit": "TFLOP/s", "frac": tf / MFMA_F32_PEAK_TFLOPS,
+                          "alg_flops_per_call": BWD_FLOPS,
+                          "alg_mac_per_chunk_head": BWD_MAC_PER_CHUNK_HEAD,
+                          "precision": "fp32 products on fp32 16x16x4 MFMA"})
 
 
 def cpu_baseline(args, synth):
@@ -414,6 +473,7 @@ def main():
                                      gated_bf16_pool=bench_decode_gated(args, torch, kda, synth,
                                                                         torch.bfloat16)),
               "prologue": lambda: bench_prologue(args, torch, kda),
+              "states": lambda: bench_prefill_states(args, torch, kda, synth),
               "backward": lambda: bench_backward(args, torch, kda, synth),
               "workloads": lambda: {str(i): bench_prefill_workload(args, torch, kda, synth, i)
                                     for i in (2, 3)},
@@ -424,6 +484,9 @@ def main():
     print("prefill: step (gated prefill) %.4f ms, p95 %.4f ms; gate + prefill %.4f ms "
           "(gate %.4f, chunk %.4f)" % (pre["step_ms"], pre["p95_step_ms"], pre["sep_step_ms"],
                                       pre["gate_ms"], pre["chunk_ms"]),
+          file=sys.stderr, flush=True)
+    stm = bench_prefill_states(args, torch, kda, synth)
+    print("prefill state modes: " + ", ".join("%s %.4f ms" % (k, v["ms"]) for k, v in stm.items()),
           file=sys.stderr, flush=True)
     dec = bench_decode(args, torch, kda, synth)
     print("decode: %.4f ms/step, %.1f GB/s" % (dec["ms_per_step"], dec["GBps"]),
@@ -493,6 +556,9 @@ def main():
                              **{k: {kk: dg[k][kk] for kk in ("ms_per_step", "GBps", "frac",
                                                              "tokens_per_s", "bytes_per_step")}
                                 for k in dg}}},
+        "prefill_state_modes": {"workload": "kda_chunk_prefill_gated T=4096 H=96: no state / "
+                                            "fp32 initial+final / bf16 initial+final",
+                                **stm},
         "prefill_workloads": wl,
         "prologue": {"workload": "kda_shortconv_l2norm T=4096 H=96 bf16 q/k/v in and out, "
                                  "SiLU, conv state out",
