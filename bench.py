@@ -64,7 +64,8 @@ DEC_STEP_BYTES = DEC_N * H * DEC_PAIR_BYTES                           # 3,259,07
 # FETCH_SIZE / WRITE_SIZE summary; valid only while the kernel sources hash to
 # the value recorded with the counters.
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "chunk_prefill_T4096_H96_hbm_traffic.md")
-CHUNK_SOURCES = ["gated_delta_rule_58_amd/csrc/prep.hip", "gated_delta_rule_58_amd/csrc/state.hip",
+CHUNK_SOURCES = ["gated_delta_rule_58_amd/csrc/prep.hip", "gated_delta_rule_58_amd/csrc/prep_chunk.hpp",
+                 "gated_delta_rule_58_amd/csrc/state.hip",
                  "gated_delta_rule_58_amd/csrc/chunk_common.hpp",
                  "gated_delta_rule_58_amd/csrc/gate_math.hpp"]
 
