@@ -294,7 +294,10 @@ kda_status kda_chunk_prefill_gated_static(
  * identities (per chunk: the triangular inverse, the decay-weighted K K^T and
  * Q K^T, the state products), in fp32: the forward states are recomputed
  * chunk by chunk and the state gradient walks the chunks backwards.  The
- * result equals the gradient of the fp64 recurrence up to fp32 rounding.
+ * result equals the gradient of the fp64 recurrence up to fp32 rounding.  g
+ * enters with the forward's per-token floor (exp(g) >= 2^-15.5; see the
+ * conventions above), so the gradient is that of the floored recurrence the
+ * forward computes: dg is 0 for a token and channel where the floor acts.
  * The workspace (kda_chunk_prefill_backward_workspace_bytes) holds per (chunk,
  * head) the chunk's intermediate matrices, the recomputed entry state and the
  * state gradient, 344,576 bytes, for T_tot / 64 + N chunk slots per head, plus
