@@ -391,7 +391,7 @@ __device__ __forceinline__ void atp_put_off(f32x4 a, f32x4 p, int i, int j, floa
 }
 
 template <bool QB>
-__global__ void __launch_bounds__(NT, 2) bwd_prep_kernel(const void* __restrict__ q,
+__global__ void __launch_bounds__(NT, 3) bwd_prep_kernel(const void* __restrict__ q,
                                                          const void* __restrict__ k,
                                                          const void* __restrict__ v,
                                                          const float* __restrict__ g,
@@ -400,10 +400,17 @@ __global__ void __launch_bounds__(NT, 2) bwd_prep_kernel(const void* __restrict_
                                                          int T_tot, int H, int maxnch,
                                                          float scale, float* __restrict__ img) {
   constexpr int CS = 16;  // channels per slab of the At / P sums
-  __shared__ float sA[C][C + 1], sP[C][C + 1], sM[C][C + 1], sB[C];
-  // slabs of K, Q, gamma (CS channels), later the products' LDS slabs
+  // At, P and M (three workgroups per CU); the At / P phase keeps its slabs of
+  // K, Q and gamma where M goes later, the products after M stage through At's
+  // place
   constexpr int SLAB = C * (CS + 1);
-  __shared__ float sS[(3 * SLAB > STAGE_FLOATS ? 3 * SLAB : STAGE_FLOATS)];
+  __shared__ float sPool[3 * C * (C + 1)];
+  __shared__ float sB[C];
+  static_assert(3 * SLAB <= C * (C + 1) && STAGE_FLOATS <= C * (C + 1), "slabs fit");
+  float(*sA)[C + 1] = reinterpret_cast<float(*)[C + 1]>(sPool);
+  float(*sP)[C + 1] = reinterpret_cast<float(*)[C + 1]>(sPool + C * (C + 1));
+  float(*sM)[C + 1] = reinterpret_cast<float(*)[C + 1]>(sPool + 2 * C * (C + 1));
+  float* sS = sPool + 2 * C * (C + 1);  // the At / P slabs (over M)
   ChunkPos p;
   if (!chunk_of_block(cu, N, T_tot, H, maxnch, p, blockIdx.x)) return;
   const int t = threadIdx.x;
@@ -513,7 +520,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_prep_kernel(const void* __restrict_
   }
   __syncthreads();
   for (int e = t; e < C * C; e += NT) im[Rec::M + e] = sM[e / C][e % C];
-  float* sa = sS;
+  float* sa = sPool;  // the products' slabs, over At (read for the last time above)
   {  // W = M diag(b) K_E
     float acc[4][8];
     zero(acc);
