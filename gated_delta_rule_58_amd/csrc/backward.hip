@@ -908,6 +908,9 @@ __global__ void __launch_bounds__(NT, 2) bwd_grad_kernel(
   // slab: k, q, gamma and the three decay-factor gradients, read one slab
   // ahead so that the reads stay in flight across the slab's barriers (which
   // order LDS only).
+  // (16 channels per slab: the MFMA tiles below use the 16 lanes of a row
+  // as the slab's channels too)
+  static_assert(SC == 16, "one slab channel per lane of a 16-lane row");
   const int n16 = t & 15, x16 = t >> 4;
   float pk[4], pq[4], pg[4], pke[4], pqe[4], pkd[4], pgc;
   bool pfl[4];
