@@ -298,6 +298,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t chunk_rows(const void* base, i
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(b), (short)0, (int)n, 0x00020000);
 }
 // element (row r < 64, channel cc) through chunk_rows; HDi = H * 128
+// elements (row r, channels cc .. cc + 3) through chunk_rows, cc a multiple of 4
+template <bool BF16>
+__device__ __forceinline__ f32x4 row4_at(__amdgpu_buffer_rsrc_t rs, int HDi, int r, int cc) {
+  if constexpr (BF16) {
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 w = __builtin_bit_cast(
+        u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, (r * HDi + cc) * 2, 0, 0));
+    return f32x4{__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xffff0000u),
+                 __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xffff0000u)};
+  } else {
+    return __builtin_bit_cast(f32x4,
+                              __builtin_amdgcn_raw_buffer_load_b128(rs, (r * HDi + cc) * 4, 0, 0));
+  }
+}
 template <bool BF16>
 __device__ __forceinline__ float row_at(__amdgpu_buffer_rsrc_t rs, int HDi, int r, int cc) {
   if constexpr (BF16)
@@ -904,59 +918,71 @@ __global__ void __launch_bounds__(NT, 2) bwd_grad_kernel(
   float* aG = aQ + C * SS;
   float* sPart = aG + C * SS;      // [4][SC] partial sums of the gamma_C term
   const int lane = t & 63, w = t >> 6, ln = lane & 15, lq = lane >> 4;
-  // Thread t holds rows x = t / 16 + 16 m (m < 4) of channel t % 16 of the
-  // slab: k, q, gamma and the three decay-factor gradients, read one slab
-  // ahead so that the reads stay in flight across the slab's barriers (which
-  // order LDS only).
+  // Thread t holds row x = t / 4, channels 4 (t % 4) .. 4 (t % 4) + 3 of the
+  // slab: k, q, gamma, the three decay-factor gradients and g (for the
+  // floor), read one slab ahead (4-wide loads) so that the reads stay in
+  // flight across the slab's barriers (which order LDS only).
   // (16 channels per slab: the MFMA tiles below use the 16 lanes of a row
-  // as the slab's channels too)
+  // as the slab's channels)
   static_assert(SC == 16, "one slab channel per lane of a 16-lane row");
-  const int n16 = t & 15, x16 = t >> 4;
-  float pk[4], pq[4], pg[4], pke[4], pqe[4], pkd[4], pgc;
-  bool pfl[4];
+  const int xr = t >> 2, n4 = 4 * (t & 3);
+  const auto rgf = chunk_rows(g, 4, p, HD);
+  f32x4 pk, pq, pg, pke, pqe, pkd, pgc, pgv;
   auto fetch_slab = [&](int c0) {
-    pgc = Gf(C - 1, c0 + n16);
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int x = x16 + 16 * m, cc = c0 + n16;
-      pk[m] = Kf(x, cc);
-      pq[m] = Qf(x, cc);
-      pg[m] = Gf(x, cc);
-      pke[m] = sc[Scr::DKE + x * D + cc];
-      pqe[m] = sc[Scr::DQE + x * D + cc];
-      pkd[m] = sc[Scr::DKD + x * D + cc];
-      pfl[m] = x < Lc && decay_floored(g[tok(x, cc)]);
-    }
+    const int cc = c0 + n4;
+    pgc = *reinterpret_cast<const f32x4*>(im + Rec::G + (C - 1) * D + cc);
+    pk = row4_at<QB>(rk, HDi, xr, cc);
+    pq = row4_at<QB>(rq, HDi, xr, cc);
+    pg = *reinterpret_cast<const f32x4*>(im + Rec::G + xr * D + cc);
+    pke = *reinterpret_cast<const f32x4*>(sc + Scr::DKE + xr * D + cc);
+    pqe = *reinterpret_cast<const f32x4*>(sc + Scr::DQE + xr * D + cc);
+    pkd = *reinterpret_cast<const f32x4*>(sc + Scr::DKD + xr * D + cc);
+    pgv = row4_at<false>(rgf, HDi, xr, cc);  // rows past the chunk end read 0
   };
   fetch_slab(0);
   for (int c0 = 0; c0 < D; c0 += SC) {
     {  // the slab to LDS, and the decay-factor terms of K_E, Q_E, K_D
-      float dgC = 0.0f;
-      const float gC = pgc;
+      const int x = xr;
+      float dgc[4];
+      uint32_t fl = 0;
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int x = x16 + 16 * m;
-        const float kx = pk[m], qx = pq[m], gx = pg[m];
-        sK[x * SS + n16] = kx;
-        sQ[x * SS + n16] = qx;
-        sG[x * SS + n16] = gx;
-        float vk = 0.0f, vq = 0.0f, vg = 0.0f;
+      for (int i = 0; i < 4; ++i) {
+        const int n = n4 + i;
+        const float kx = pk[i], qx = pq[i], gx = pg[i];
+        sK[x * SS + n] = kx;
+        sQ[x * SS + n] = qx;
+        sG[x * SS + n] = gx;
+        float vk = 0.0f, vq = 0.0f, vg = 0.0f, dc = 0.0f;
         if (x < Lc) {
-          const float dke = pke[m], dqe = pqe[m], dkd = pkd[m];
-          const float E = __expf(gx), F = __expf(gC - gx);
+          const float dke = pke[i], dqe = pqe[i], dkd = pkd[i];
+          const float E = __expf(gx), F = __expf(pgc[i] - gx);
           vk = dke * E + dkd * F;
           vq = dqe * E;
           vg = (dke * kx + dqe * qx) * E - dkd * kx * F;
-          dgC = fmaf(dkd * kx, F, dgC);
+          dc = dkd * kx * F;
+          if (decay_floored(pgv[i])) fl |= 1u << ((c0 + n) & 31);
         }
-        aK[x * SS + n16] = vk;
-        aQ[x * SS + n16] = vq;
-        aG[x * SS + n16] = vg;
-        if (pfl[m]) atomicOr(&sFl[x][(c0 + n16) >> 5], 1u << ((c0 + n16) & 31));
+        aK[x * SS + n] = vk;
+        aQ[x * SS + n] = vq;
+        aG[x * SS + n] = vg;
+        dgc[i] = dc;
       }
-      dgC += __shfl_xor(dgC, 16);
-      dgC += __shfl_xor(dgC, 32);
-      if (lane < 16) sPart[w * SC + lane] = dgC;
+      if (fl) atomicOr(&sFl[x][c0 >> 5], fl);
+      // the gamma_C terms of each channel summed over the wave's 16 rows (the
+      // lanes sharing t % 4)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float v = dgc[i];
+        v += __shfl_xor(v, 4);
+        v += __shfl_xor(v, 8);
+        v += __shfl_xor(v, 16);
+        v += __shfl_xor(v, 32);
+        dgc[i] = v;
+      }
+      if (lane < 4) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sPart[w * SC + n4 + i] = dgc[i];
+      }
     }
     barrier_lds();
     if (c0 + SC < D) fetch_slab(c0 + SC);
