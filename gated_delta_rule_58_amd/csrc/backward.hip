@@ -518,18 +518,69 @@ __global__ void __launch_bounds__(NT, 3) bwd_prep_kernel(const void* __restrict_
     }
   }
   __syncthreads();
-  // M = (I + diag(b) At)^-1, unit lower triangular, by forward substitution
-  // down each column: M[r][s] = -b_r sum_{s <= u < r} At[r][u] M[u][s].
-  // Column s belongs to lanes 4s .. 4s + 3 of one wave (a quarter of the
-  // sum each, combined by shuffles); rows go in order.
+  // M = (I + A)^-1, A = diag(b) At strictly lower, by 16-row blocks on fp32
+  // MFMA: the diagonal blocks M_ii = (I - N)(I + N^2)(I + N^4)(I + N^8) with
+  // N = A_ii (nilpotent, N^16 = 0), then block column j on wave j by forward
+  // substitution, M_ij = -M_ii sum_{k=j}^{i-1} A_ik M_kj.  P's LDS copy is
+  // free from here (the Qt product reads P from the record): it holds each
+  // wave's 16 x 16 intermediates.
   {
-    const int s2 = t >> 2, qd = t & 3;
-    for (int r = 0; r < C; ++r) {
-      float acc = 0.0f;
-      for (int u = s2 + qd; u < r; u += 4) acc = fmaf(sA[r][u], sM[u][s2], acc);
-      acc += __shfl_xor(acc, 1);
-      acc += __shfl_xor(acc, 2);
-      if (qd == 0) sM[r][s2] = r < s2 ? 0.0f : (r == s2 ? 1.0f : -sB[r] * acc);
+    const int l = t & 63, w = t >> 6, lr = l & 15, lq = l >> 4;
+    float* scr = &sP[0][0] + w * 1024;  // four 16 x 16 matrices per wave
+    float* X2 = scr;
+    float* X4 = scr + 256;
+    float* X8 = scr + 512;
+    float* Q = scr + 768;
+    // acc += X Y over 16 x 16 x 16; X (m, k) at x[m xs + k] times xrow[m],
+    // Y (k, n) at y[k ys + n] times yrow[k] (1 when the pointers are null)
+    auto mm16 = [&](const float* x, int xs, const float* xrow, const float* y, int ys,
+                    const float* yrow, f32x4 acc) {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int k = 4 * kk + lq;
+        const float a = x[lr * xs + k] * (xrow ? xrow[lr] : 1.0f);
+        const float b = y[k * ys + lr] * (yrow ? yrow[k] : 1.0f);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
+      }
+      return acc;
+    };
+    auto put16 = [&](float* d, int ds, f32x4 v, float sgn) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) d[(4 * lq + i) * ds + lr] = sgn * v[i];
+    };
+    const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+    {  // the diagonal block of row block w
+      const int b0 = 16 * w;
+      const float* N = &sA[b0][b0];
+      const float* bw = sB + b0;
+      put16(X2, 16, mm16(N, C + 1, bw, N, C + 1, bw, z4), 1.0f);
+      put16(X4, 16, mm16(X2, 16, nullptr, X2, 16, nullptr, z4), 1.0f);
+      put16(X8, 16, mm16(X4, 16, nullptr, X4, 16, nullptr, z4), 1.0f);
+      f32x4 q;  // I - N in the accumulator layout: element (4 lq + i, lr)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * lq + i;
+        q[i] = (r == lr ? 1.0f : 0.0f) - bw[r] * N[r * (C + 1) + lr];
+      }
+      put16(Q, 16, q, 1.0f);
+      q = mm16(Q, 16, nullptr, X2, 16, nullptr, q);  // (I - N)(I + N^2)
+      put16(Q, 16, q, 1.0f);
+      q = mm16(Q, 16, nullptr, X4, 16, nullptr, q);  // ... (I + N^4)
+      put16(Q, 16, q, 1.0f);
+      q = mm16(Q, 16, nullptr, X8, 16, nullptr, q);  // ... (I + N^8)
+      put16(&sM[b0][b0], C + 1, q, 1.0f);
+      for (int j = w + 1; j < 4; ++j) put16(&sM[b0][16 * j], C + 1, z4, 1.0f);
+    }
+    __syncthreads();
+    // block column j = w: rows i = j + 1 .. 3 in order
+    for (int i = w + 1; i < 4; ++i) {
+      f32x4 acc = z4;
+      for (int k = w; k < i; ++k)
+        acc = mm16(&sA[16 * i][16 * k], C + 1, sB + 16 * i, &sM[16 * k][16 * w], C + 1, nullptr,
+                   acc);
+      put16(Q, 16, acc, 1.0f);
+      put16(&sM[16 * i][16 * w], C + 1,
+            mm16(&sM[16 * i][16 * i], C + 1, nullptr, Q, 16, nullptr, z4), -1.0f);
     }
   }
   __syncthreads();
@@ -563,8 +614,9 @@ __global__ void __launch_bounds__(NT, 3) bwd_prep_kernel(const void* __restrict_
   {  // Qt = scale (Q_E - P W)
     float acc[4][8];
     zero(acc);
-    gemm_staged2<4, 8, true, true>(acc, C, sa, [&](int r, int s2) { return sP[r][s2]; },
-                                  [&](int s2, int cc) { return im[Rec::W + s2 * D + cc]; });
+    gemm_staged2<4, 8, true, true>(acc, C, sa,
+                                   [&](int r, int s2) { return im[Rec::P + r * C + s2]; },
+                                   [&](int s2, int cc) { return im[Rec::W + s2 * D + cc]; });
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
