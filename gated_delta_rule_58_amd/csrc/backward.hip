@@ -243,6 +243,100 @@ __device__ __forceinline__ void gemm_staged2(float (&acc)[TM][TN], int K, float*
       for (int v = 0; v < 4; ++v) acc[4 * i + v][j] = ct[i][j][v];
 }
 
+// gemm_staged2 with operands read 4 at a time: a4(m, k) returns a(m, k .. k+3)
+// when A_KC (contiguous along k), else a(m .. m+3, k); b4(k, n) returns
+// b(k, n .. n+3) when B_NC, else b(k .. k+3, n).  Index arguments are
+// multiples of 4 along the vector's direction.
+template <int TM, int TN, bool A_KC, bool B_NC, typename FA4, typename FB4>
+__device__ __forceinline__ void gemm_staged2v(float (&acc)[TM][TN], int K, float* stage, FA4 a4,
+                                              FB4 b4) {
+  constexpr int M = 16 * TM, N = 16 * TN, MS = M + 17, NS = N + 17;
+  float* sa = stage;
+  float* sb = stage + KT * MS;
+  constexpr int PA4 = M * KT / NT / 4, PB4 = N * KT / NT / 4;
+  static_assert(TM % 4 == 0 && PA4 >= 1 && PB4 >= 1 && (M * KT) % (4 * NT) == 0 &&
+                    (N * KT) % (4 * NT) == 0,
+                "whole 16-row tiles per wave, whole 4-vectors per thread");
+  const int t = threadIdx.x;
+  f32x4 ra[2][PA4], rb[2][PB4];
+  auto a_pos = [&](int u, int& m, int& kt) {
+    const int e = t + NT * u;
+    m = A_KC ? e / (KT / 4) : 4 * (e % (M / 4));
+    kt = A_KC ? 4 * (e % (KT / 4)) : e / (M / 4);
+  };
+  auto b_pos = [&](int u, int& n, int& kt) {
+    const int e = t + NT * u;
+    n = B_NC ? 4 * (e % (N / 4)) : e / (KT / 4);
+    kt = B_NC ? e / (N / 4) : 4 * (e % (KT / 4));
+  };
+  auto fetch = [&](int k0, int sl) {
+#pragma unroll
+    for (int u = 0; u < PA4; ++u) {
+      int m, kt;
+      a_pos(u, m, kt);
+      ra[sl][u] = a4(m, k0 + kt);
+    }
+#pragma unroll
+    for (int u = 0; u < PB4; ++u) {
+      int n, kt;
+      b_pos(u, n, kt);
+      rb[sl][u] = b4(k0 + kt, n);
+    }
+  };
+  constexpr int TR = TM / 4;
+  f32x4 ct[TR][TN];
+#pragma unroll
+  for (int i = 0; i < TR; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+      ct[i][j] = f32x4{acc[4 * i][j], acc[4 * i + 1][j], acc[4 * i + 2][j], acc[4 * i + 3][j]};
+  fetch(0, 0);
+  fetch(KT, 1);
+  for (int k0 = 0; k0 < K; k0 += 2 * KT) {
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl) {
+#pragma unroll
+      for (int u = 0; u < PA4; ++u) {
+        int m, kt;
+        a_pos(u, m, kt);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sa[(A_KC ? (kt + i) * MS + m : kt * MS + m + i)] = ra[sl][u][i];
+      }
+#pragma unroll
+      for (int u = 0; u < PB4; ++u) {
+        int n, kt;
+        b_pos(u, n, kt);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sb[(B_NC ? kt * NS + n + i : (kt + i) * NS + n)] = rb[sl][u][i];
+      }
+      barrier_lds();
+      if (k0 + (2 + sl) * KT < K) fetch(k0 + (2 + sl) * KT, sl);
+      const int lane = t & 63, w = t >> 6, lr = lane & 15, lq = lane >> 4;
+#pragma unroll
+      for (int kg = 0; kg < KT / 4; ++kg) {
+        const int kk = 4 * kg + lq;
+        float av[TR], bv[TN];
+#pragma unroll
+        for (int i = 0; i < TR; ++i) av[i] = sa[kk * MS + 16 * (TR * w + i) + lr];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) bv[j] = sb[kk * NS + 16 * j + lr];
+#pragma unroll
+        for (int i = 0; i < TR; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            ct[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[i], bv[j], ct[i][j], 0, 0, 0);
+      }
+      barrier_lds();
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < TR; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[4 * i + v][j] = ct[i][j][v];
+}
+
 // Output element of acc[i][j] after gemm_staged<TM, TN>: row orow<TM>(i),
 // column ocol(j).
 template <int TM>
@@ -297,8 +391,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t chunk_rows(const void* base, i
   const int64_t n = (base && p.Lc > 0) ? ((int64_t)(p.Lc - 1) * HD + D) * esz : 0;
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(b), (short)0, (int)n, 0x00020000);
 }
-// element (row r < 64, channel cc) through chunk_rows; HDi = H * 128
-// elements (row r, channels cc .. cc + 3) through chunk_rows, cc a multiple of 4
+// elements (row r < 64, channels cc .. cc + 3) through chunk_rows, cc a
+// multiple of 4; HDi = H * 128
 template <bool BF16>
 __device__ __forceinline__ f32x4 row4_at(__amdgpu_buffer_rsrc_t rs, int HDi, int r, int cc) {
   if constexpr (BF16) {
@@ -312,6 +406,7 @@ __device__ __forceinline__ f32x4 row4_at(__amdgpu_buffer_rsrc_t rs, int HDi, int
                               __builtin_amdgcn_raw_buffer_load_b128(rs, (r * HDi + cc) * 4, 0, 0));
   }
 }
+// element (row r < 64, channel cc) through chunk_rows
 template <bool BF16>
 __device__ __forceinline__ float row_at(__amdgpu_buffer_rsrc_t rs, int HDi, int r, int cc) {
   if constexpr (BF16)
@@ -589,10 +684,16 @@ __global__ void __launch_bounds__(NT, 3) bwd_prep_kernel(const void* __restrict_
   {  // W = M diag(b) K_E
     float acc[4][8];
     zero(acc);
-    gemm_staged2<4, 8, true, true>(acc, C, sa, [&](int r, int s2) { return sM[r][s2]; },
-                                  [&](int s2, int cc) {
-                                    return sB[s2] * Kf(s2, cc) * __expf(Gf(s2, cc));
-                                  });
+    gemm_staged2v<4, 8, true, true>(
+        acc, C, sa,
+        [&](int r, int s2) { return f32x4{sM[r][s2], sM[r][s2 + 1], sM[r][s2 + 2], sM[r][s2 + 3]}; },
+        [&](int s2, int cc) {
+          const f32x4 kv = row4_at<QB>(rk, HDi, s2, cc);
+          const f32x4 gv = *reinterpret_cast<const f32x4*>(im + Rec::G + s2 * D + cc);
+          const float b = sB[s2];
+          return f32x4{b * kv[0] * __expf(gv[0]), b * kv[1] * __expf(gv[1]),
+                       b * kv[2] * __expf(gv[2]), b * kv[3] * __expf(gv[3])};
+        });
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -601,10 +702,10 @@ __global__ void __launch_bounds__(NT, 3) bwd_prep_kernel(const void* __restrict_
   {  // U = M diag(b) V
     float acc[4][8];
     zero(acc);
-    gemm_staged2<4, 8, true, true>(acc, C, sa, [&](int r, int s2) { return sM[r][s2]; },
-                                  [&](int s2, int j) {
-                                    return sB[s2] * row_at<QB>(rv, HDi, s2, j);
-                                  });
+    gemm_staged2v<4, 8, true, true>(
+        acc, C, sa,
+        [&](int r, int s2) { return f32x4{sM[r][s2], sM[r][s2 + 1], sM[r][s2 + 2], sM[r][s2 + 3]}; },
+        [&](int s2, int j) { return sB[s2] * row4_at<QB>(rv, HDi, s2, j); });
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -614,9 +715,10 @@ __global__ void __launch_bounds__(NT, 3) bwd_prep_kernel(const void* __restrict_
   {  // Qt = scale (Q_E - P W)
     float acc[4][8];
     zero(acc);
-    gemm_staged2<4, 8, true, true>(acc, C, sa,
-                                   [&](int r, int s2) { return im[Rec::P + r * C + s2]; },
-                                   [&](int s2, int cc) { return im[Rec::W + s2 * D + cc]; });
+    gemm_staged2v<4, 8, true, true>(
+        acc, C, sa,
+        [&](int r, int s2) { return *reinterpret_cast<const f32x4*>(im + Rec::P + r * C + s2); },
+        [&](int s2, int cc) { return *reinterpret_cast<const f32x4*>(im + Rec::W + s2 * D + cc); });
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
