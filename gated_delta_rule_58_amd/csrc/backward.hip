@@ -793,7 +793,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_walk_kernel(
         sR[orow<8>(i)][ocol(j)] = R[i][j];
       }
     __syncthreads();
-    {  // Z = A1 R, A1 = W (forward) or K_D (backward)
+    {  // Z = A1 R, A1 = W (forward) or K_D (backward); forward keeps U - Z
       const float* A1 = im + (fwd ? Rec::W : Rec::KD);
       float z[4][4];
       zero(z);
@@ -803,29 +803,33 @@ __global__ void __launch_bounds__(NT, 2) bwd_walk_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) sZ[orow<4>(i)][ocol(j)] = z[i][j];
+        for (int j = 0; j < 4; ++j) {
+          const int r = orow<4>(i), c2 = ocol(j);
+          sZ[r][c2] = fwd ? im[Rec::U + r * D + 64 * tile + c2] - z[i][j] : z[i][j];
+        }
     }
     __syncthreads();
-    // R <- e^gamma_C R + [A2; A3]^T [-Z; B]: A2 = K_D / W, A3 = K_D / Qt,
-    // B = U (forward) or the d_o tile (backward)
+    // R <- e^gamma_C R + K_D^T (U - Z) (forward) or e^gamma_C R - W^T Z +
+    // Qt^T dO (backward, dO the tile's columns of d_o)
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const float ec = im[Rec::EC + orow<8>(i)];
 #pragma unroll
       for (int j = 0; j < 4; ++j) R[i][j] *= ec;
     }
-    // as three products whose operand reads have no branch of their own (a
-    // branch per element made every operand load wait alone)
-    const float* A2 = im + (fwd ? Rec::KD : Rec::W);
-    const float* A3 = im + (fwd ? Rec::KD : Rec::QT);
-    gemm_staged2<8, 4, false, true>(
-        R, C, sS, [&](int cr, int kk) { return A2[kk * D + cr]; },
-        [&](int kk, int j) { return -sZ[kk][j]; });
+    // as products whose operand reads have no branch of their own (a branch
+    // per element made every operand load wait alone)
     if (fwd) {
+      const float* A2 = im + Rec::KD;
       gemm_staged2<8, 4, false, true>(
-          R, C, sS, [&](int cr, int kk) { return A3[kk * D + cr]; },
-          [&](int kk, int j) { return im[Rec::U + kk * D + 64 * tile + j]; });
+          R, C, sS, [&](int cr, int kk) { return A2[kk * D + cr]; },
+          [&](int kk, int j) { return sZ[kk][j]; });
     } else {
+      const float* A2 = im + Rec::W;
+      const float* A3 = im + Rec::QT;
+      gemm_staged2<8, 4, false, true>(
+          R, C, sS, [&](int cr, int kk) { return A2[kk * D + cr]; },
+          [&](int kk, int j) { return -sZ[kk][j]; });
       gemm_staged2<8, 4, false, true>(
           R, C, sS, [&](int cr, int kk) { return A3[kk * D + cr]; },
           [&](int kk, int j) { return row_at<DOB>(rdo, HDi, kk, 64 * tile + j); });
