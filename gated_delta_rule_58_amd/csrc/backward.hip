@@ -734,20 +734,196 @@ __global__ void __launch_bounds__(NT, 3) bwd_prep_kernel(const void* __restrict_
   if (t < D) im[Rec::EC + t] = __expf(Gf(C - 1, t));
 }
 
+// One chunk walk of a (sequence, head, 64-column tile).  Lane (lr, lq) of
+// wave w holds R[32 w + 16 i + 4 lq + v][16 j + lr] of the tile in R[i][j][v]
+// (i < 2, j < 4), the fp32 16x16x4 MFMA accumulator layout.
+// Forward (FWD): R = S from the initial state; rec[chunk] = R at the chunk's
+// entry.  Backward: R = dS from dS_final; rec[chunk] = R at the chunk's end,
+// R_end gets the gradient of the initial state.
+// A chunk step is Z = A1 R (A1 = W forward, K_D backward; 16 rows of Z per
+// wave), then R <- e^gamma_C R + K_D^T (U - Z) forward, or e^gamma_C R +
+// [W; Qt]^T [-Z; dO] backward (dO the tile's columns of d_o).  The MFMA A
+// operands come straight from the chunk record into registers, one product
+// ahead of their use: rows of A1 16 bytes a lane (lane group lq, sub-step s
+// of group u takes contraction index 16 u + 4 lq + s, and the B operand is
+// read in that order), the transposed operands one float a lane (16 lanes on
+// 64 contiguous bytes).  The B operands R and [Z; dO] sit transposed in LDS,
+// so the four contraction indices of a lane's four MFMAs are one 16-byte
+// read.  Two barriers per chunk step.
+constexpr int WTS = 2 * C + 4;  // row stride of the transposed LDS tiles: 4 WTS = 16 (mod 64 banks)
+template <bool FWD, bool DOB>
+__device__ __forceinline__ void walk_dir(const float* __restrict__ img, const void* d_o,
+                                         int64_t bos, int64_t L, int n, int h, int tile, int H,
+                                         const float* __restrict__ R_init,
+                                         float* __restrict__ rec, float* __restrict__ R_end,
+                                         float (*sRt)[WTS], float (*sZt)[WTS]) {
+  const int nch = static_cast<int>((L + C - 1) / C);
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, lr = lane & 15, lq = lane >> 4;
+  const int64_t HD = (int64_t)H * D;
+  const int HDi = static_cast<int>(HD);
+  const int64_t sbase = ((int64_t)n * H + h) * D * D + 64 * tile;
+  auto rrow = [&](int i, int v) { return 32 * w + 16 * i + 4 * lq + v; };
+  f32x4 R[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        R[i][j][v] = R_init ? R_init[sbase + (int64_t)rrow(i, v) * D + 16 * j + lr] : 0.0f;
+  auto pair_of = [&](int it) {
+    const int c = FWD ? it : nch - 1 - it;
+    return (bos / C + n + c) * H + h;
+  };
+  // Record reads through a buffer resource: the lane's part of the offset in
+  // one register, the rest a constant, so the many operand loads share it.
+  auto rec_buf = [&](int64_t pair) { return chunk::make_buf(img + pair * Rec::floats, Rec::floats * 4); };
+  auto ld1 = [](__amdgpu_buffer_rsrc_t rs, int vo, int so) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, vo, so, 0));
+  };
+  constexpr int A1 = FWD ? Rec::W : Rec::KD;
+  f32x4 zA[8];  // A1 rows 16 w + lr, contraction 16 u + 4 lq .. + 3
+  const int vo_zA = ((16 * w + lr) * D + 4 * lq) * 4;
+  auto load_zA = [&](__amdgpu_buffer_rsrc_t rs) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      zA[u] = __builtin_bit_cast(
+          f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, vo_zA, (A1 + 16 * u) * 4, 0));
+  };
+  if (nch > 0) load_zA(rec_buf(pair_of(0)));
+  for (int it = 0; it < nch; ++it) {
+    const int c = FWD ? it : nch - 1 - it;
+    const int64_t pair = pair_of(it);
+    const auto rs = rec_buf(pair);
+    float* rc = rec + pair * (int64_t)(D * D) + 64 * tile;
+    // (1) R into the record and, transposed, into LDS
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) rc[rrow(i, v) * D + 16 * j + lr] = R[i][j][v];
+        *reinterpret_cast<f32x4*>(&sRt[16 * j + lr][rrow(i, 0)]) = R[i][j];
+      }
+    // the state update's operands, in flight during Z = A1 R
+    constexpr int KU = FWD ? 4 : 8;  // 16-deep contraction groups of the update
+    float a2[KU][4][2];
+    const int vo_a2 = (4 * lq * D + 32 * w + lr) * 4;
+#pragma unroll
+    for (int u = 0; u < KU; ++u)
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int part = FWD ? Rec::KD : (u < 4 ? Rec::W : Rec::QT);
+          a2[u][s][i] = ld1(rs, vo_a2, (part + (16 * (u & 3) + s) * D + 16 * i) * 4);
+        }
+    float ec[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) ec[i][v] = ld1(rs, (32 * w + 4 * lq) * 4, (Rec::EC + 16 * i + v) * 4);
+    f32x4 ext[4];  // forward: U at Z's elements; backward: d_o row `lane`, columns 16 w .. + 15
+    if constexpr (FWD) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          ext[j][v] = ld1(rs, ((16 * w + 4 * lq) * D + 64 * tile + lr) * 4,
+                          (Rec::U + v * D + 16 * j) * 4);
+    } else {
+      ChunkPos cp;
+      cp.t0 = bos + (int64_t)c * C;
+      cp.h = h;
+      cp.Lc = static_cast<int>(L - (int64_t)c * C < C ? L - (int64_t)c * C : C);
+      const auto rdo = chunk_rows(d_o, DOB ? 2 : 4, cp, HD);
+      const int off = lane * HDi + 64 * tile + 16 * w;
+      if constexpr (DOB) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+          const u32x4 x = __builtin_bit_cast(
+              u32x4, __builtin_amdgcn_raw_buffer_load_b128(rdo, (off + 8 * hh) * 2, 0, 0));
+#pragma unroll
+          for (int e = 0; e < 2; ++e)
+            ext[2 * hh + e] = f32x4{__uint_as_float(x[2 * e] << 16),
+                                    __uint_as_float(x[2 * e] & 0xffff0000u),
+                                    __uint_as_float(x[2 * e + 1] << 16),
+                                    __uint_as_float(x[2 * e + 1] & 0xffff0000u)};
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          ext[e] = __builtin_bit_cast(
+              f32x4, __builtin_amdgcn_raw_buffer_load_b128(rdo, (off + 4 * e) * 4, 0, 0));
+      }
+    }
+    barrier_lds();
+    // (2) Z = A1 R, rows 16 w .. + 15 of the chunk
+    f32x4 z[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) z[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 b = *reinterpret_cast<const f32x4*>(&sRt[16 * j + lr][16 * u + 4 * lq]);
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          z[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(zA[u][s], b[s], z[j], 0, 0, 0);
+      }
+    if (it + 1 < nch) load_zA(rec_buf(pair_of(it + 1)));
+    // (3) U - Z (forward) or [-Z; dO] (backward), transposed, into LDS
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      *reinterpret_cast<f32x4*>(&sZt[16 * j + lr][16 * w + 4 * lq]) = FWD ? ext[j] - z[j] : -z[j];
+    if constexpr (!FWD) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sZt[16 * w + e][C + lane] = ext[e >> 2][e & 3];
+    }
+    barrier_lds();
+    // (4) the state update
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) R[i][j][v] *= ec[i][v];
+#pragma unroll
+    for (int u = 0; u < KU; ++u)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 b = *reinterpret_cast<const f32x4*>(&sZt[16 * j + lr][16 * u + 4 * lq]);
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+            R[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a2[u][s][i], b[s], R[i][j], 0, 0, 0);
+      }
+  }
+  if (R_end) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          R_end[sbase + (int64_t)rrow(i, v) * D + 16 * j + lr] = R[i][j][v];
+  }
+}
+
 // Both chunk walks in one launch: block b < nb walks forward (when both run),
-// the others backward; one (sequence, head, 64-column tile) each.  Thread t
-// holds R[16 i + t / 16][16 j + t % 16] of the tile, i < 8, j < 4.
-// Forward: R = S from the initial state; rec_f[chunk] = R at the chunk's entry.
-// Backward: R = dS from dS_final; rec_b[chunk] = R at the chunk's end; dS0
-// gets the gradient of the initial state.
+// the others backward; one (sequence, head, 64-column tile) each.  Forward:
+// rec_f[chunk] = S at the chunk's entry; backward: rec_b[chunk] = dS at the
+// chunk's end, dS0 = the initial state's gradient.
 template <bool DOB>
 __global__ void __launch_bounds__(NT, 2) bwd_walk_kernel(
     const float* __restrict__ img, const void* __restrict__ d_o,
     const int32_t* __restrict__ cu, int N, int T_tot, int H, int both,
     const float* __restrict__ S0, float* __restrict__ rec_f, const float* __restrict__ dSf,
     float* __restrict__ dS0, float* __restrict__ rec_b) {
-  __shared__ float sR[D][64 + 1], sZ[C][64 + 1];
-  __shared__ float sS[STAGE_FLOATS];
+  __shared__ __attribute__((aligned(16))) float sRt[64][WTS];  // sRt[j][cc] = R[cc][j]
+  __shared__ __attribute__((aligned(16))) float sZt[64][WTS];  // sZt[j][kk]: the update's B operand
   const int64_t nb = (int64_t)N * H * 2;
   int64_t b = blockIdx.x;
   const bool fwd = both && b < nb;
@@ -760,88 +936,10 @@ __global__ void __launch_bounds__(NT, 2) bwd_walk_kernel(
   bos = bos < 0 ? 0 : (bos > T_tot ? T_tot : bos);
   eos = eos < bos ? bos : (eos > T_tot ? T_tot : eos);
   const int64_t L = eos - bos;
-  const int nch = static_cast<int>((L + C - 1) / C);
-  const int t = threadIdx.x;
-  const int64_t HD = (int64_t)H * D;
-  const int HDi = static_cast<int>(HD);
-  const int64_t sbase = ((int64_t)n * H + h) * D * D + 64 * tile;
-  const float* R_init = fwd ? S0 : dSf;
-  float* rec = fwd ? rec_f : rec_b;
-  float R[8][4];
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      R[i][j] = R_init ? R_init[sbase + (int64_t)orow<8>(i) * D + ocol(j)] : 0.0f;
-  for (int it = 0; it < nch; ++it) {
-    const int c = fwd ? it : nch - 1 - it;
-    const int64_t pair = (bos / C + n + c) * H + h;
-    const float* im = img + pair * Rec::floats;
-    const int Lc = static_cast<int>(L - (int64_t)c * C < C ? L - (int64_t)c * C : C);
-    const int64_t t0 = bos + (int64_t)c * C;
-    ChunkPos cp;
-    cp.t0 = t0;
-    cp.h = h;
-    cp.Lc = Lc;
-    const auto rdo = chunk_rows(d_o, DOB ? 2 : 4, cp, HD);
-    float* rc = rec + pair * (int64_t)(D * D) + 64 * tile;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        rc[orow<8>(i) * D + ocol(j)] = R[i][j];
-        sR[orow<8>(i)][ocol(j)] = R[i][j];
-      }
-    __syncthreads();
-    {  // Z = A1 R, A1 = W (forward) or K_D (backward); forward keeps U - Z
-      const float* A1 = im + (fwd ? Rec::W : Rec::KD);
-      float z[4][4];
-      zero(z);
-      gemm_staged2<4, 4, true, true>(z, D, sS,
-                                    [&](int r, int cc) { return A1[r * D + cc]; },
-                                    [&](int cc, int j) { return sR[cc][j]; });
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int r = orow<4>(i), c2 = ocol(j);
-          sZ[r][c2] = fwd ? im[Rec::U + r * D + 64 * tile + c2] - z[i][j] : z[i][j];
-        }
-    }
-    __syncthreads();
-    // R <- e^gamma_C R + K_D^T (U - Z) (forward) or e^gamma_C R - W^T Z +
-    // Qt^T dO (backward, dO the tile's columns of d_o)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float ec = im[Rec::EC + orow<8>(i)];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) R[i][j] *= ec;
-    }
-    // as products whose operand reads have no branch of their own (a branch
-    // per element made every operand load wait alone)
-    if (fwd) {
-      const float* A2 = im + Rec::KD;
-      gemm_staged2<8, 4, false, true>(
-          R, C, sS, [&](int cr, int kk) { return A2[kk * D + cr]; },
-          [&](int kk, int j) { return sZ[kk][j]; });
-    } else {
-      const float* A2 = im + Rec::W;
-      const float* A3 = im + Rec::QT;
-      gemm_staged2<8, 4, false, true>(
-          R, C, sS, [&](int cr, int kk) { return A2[kk * D + cr]; },
-          [&](int kk, int j) { return -sZ[kk][j]; });
-      gemm_staged2<8, 4, false, true>(
-          R, C, sS, [&](int cr, int kk) { return A3[kk * D + cr]; },
-          [&](int kk, int j) { return row_at<DOB>(rdo, HDi, kk, 64 * tile + j); });
-    }
-  }
-  float* R_end = fwd ? nullptr : dS0;
-  if (R_end) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) R_end[sbase + (int64_t)orow<8>(i) * D + ocol(j)] = R[i][j];
-  }
+  if (fwd)
+    walk_dir<true, DOB>(img, d_o, bos, L, n, h, tile, H, S0, rec_f, nullptr, sRt, sZt);
+  else
+    walk_dir<false, DOB>(img, d_o, bos, L, n, h, tile, H, dSf, rec_b, dS0, sRt, sZt);
 }
 
 template <bool QB, bool DOB>
