@@ -749,14 +749,19 @@ __global__ void __launch_bounds__(NT, 3) bwd_prep_kernel(const void* __restrict_
 // read in that order), the transposed operands one float a lane (16 lanes on
 // 64 contiguous bytes).  The B operands R and [Z; dO] sit transposed in LDS,
 // so the four contraction indices of a lane's four MFMAs are one 16-byte
-// read.  Two barriers per chunk step.
+// read.  Two barriers per chunk step.  With bf16 d_o, Qt^T dO runs on the
+// bf16 16x16x32 MFMA instead: dO exactly, Qt as three bf16 terms (hi + mid +
+// lo hold its 24 bits; products of bf16 pairs are exact in the fp32
+// accumulator), a sixth of the fp32 MFMA cycles.
 constexpr int WTS = 2 * C + 4;  // row stride of the transposed LDS tiles: 4 WTS = 16 (mod 64 banks)
+constexpr int DTS = C + 8;      // the bf16 d_o tile's: 16-lane reads of 16 bytes land on distinct banks
 template <bool FWD, bool DOB>
 __device__ __forceinline__ void walk_dir(const float* __restrict__ img, const void* d_o,
                                          int64_t bos, int64_t L, int n, int h, int tile, int H,
                                          const float* __restrict__ R_init,
                                          float* __restrict__ rec, float* __restrict__ R_end,
-                                         float (*sRt)[WTS], float (*sZt)[WTS]) {
+                                         float (*sRt)[WTS], float (*sZt)[WTS],
+                                         uint16_t (*sDt)[DTS]) {
   const int nch = static_cast<int>((L + C - 1) / C);
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, lr = lane & 15, lq = lane >> 4;
   const int64_t HD = (int64_t)H * D;
@@ -806,7 +811,8 @@ __device__ __forceinline__ void walk_dir(const float* __restrict__ img, const vo
         *reinterpret_cast<f32x4*>(&sRt[16 * j + lr][rrow(i, 0)]) = R[i][j];
       }
     // the state update's operands, in flight during Z = A1 R
-    constexpr int KU = FWD ? 4 : 8;  // 16-deep contraction groups of the update
+    constexpr bool QT16 = !FWD && DOB;  // Qt^T dO on the bf16 MFMA
+    constexpr int KU = FWD || QT16 ? 4 : 8;  // 16-deep fp32 contraction groups of the update
     float a2[KU][4][2];
     const int vo_a2 = (4 * lq * D + 32 * w + lr) * 4;
 #pragma unroll
@@ -818,11 +824,23 @@ __device__ __forceinline__ void walk_dir(const float* __restrict__ img, const vo
           const int part = FWD ? Rec::KD : (u < 4 ? Rec::W : Rec::QT);
           a2[u][s][i] = ld1(rs, vo_a2, (part + (16 * (u & 3) + s) * D + 16 * i) * 4);
         }
+    float qa[2][2][8];  // QT16: Qt[32 g + 8 lq + e][32 w + 16 i + lr] in qa[g][i][e]
+    if constexpr (QT16) {
+      const int vo_q = (8 * lq * D + 32 * w + lr) * 4;
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            qa[g][i][e] = ld1(rs, vo_q, (Rec::QT + (32 * g + e) * D + 16 * i) * 4);
+    }
     float ec[2][4];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int v = 0; v < 4; ++v) ec[i][v] = ld1(rs, (32 * w + 4 * lq) * 4, (Rec::EC + 16 * i + v) * 4);
+    u32x4 draw[2];  // QT16: d_o row `lane`, columns 16 w .. + 15, as stored
     f32x4 ext[4];  // forward: U at Z's elements; backward: d_o row `lane`, columns 16 w .. + 15
     if constexpr (FWD) {
 #pragma unroll
@@ -840,17 +858,9 @@ __device__ __forceinline__ void walk_dir(const float* __restrict__ img, const vo
       const int off = lane * HDi + 64 * tile + 16 * w;
       if constexpr (DOB) {
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-          const u32x4 x = __builtin_bit_cast(
+        for (int hh = 0; hh < 2; ++hh)
+          draw[hh] = __builtin_bit_cast(
               u32x4, __builtin_amdgcn_raw_buffer_load_b128(rdo, (off + 8 * hh) * 2, 0, 0));
-#pragma unroll
-          for (int e = 0; e < 2; ++e)
-            ext[2 * hh + e] = f32x4{__uint_as_float(x[2 * e] << 16),
-                                    __uint_as_float(x[2 * e] & 0xffff0000u),
-                                    __uint_as_float(x[2 * e + 1] << 16),
-                                    __uint_as_float(x[2 * e + 1] & 0xffff0000u)};
-        }
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
@@ -877,7 +887,11 @@ __device__ __forceinline__ void walk_dir(const float* __restrict__ img, const vo
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       *reinterpret_cast<f32x4*>(&sZt[16 * j + lr][16 * w + 4 * lq]) = FWD ? ext[j] - z[j] : -z[j];
-    if constexpr (!FWD) {
+    if constexpr (QT16) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        sDt[16 * w + e][lane] = static_cast<uint16_t>(draw[e >> 3][(e & 7) >> 1] >> (16 * (e & 1)));
+    } else if constexpr (!FWD) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) sZt[16 * w + e][C + lane] = ext[e >> 2][e & 3];
     }
@@ -900,6 +914,30 @@ __device__ __forceinline__ void walk_dir(const float* __restrict__ img, const vo
           for (int i = 0; i < 2; ++i)
             R[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a2[u][s][i], b[s], R[i][j], 0, 0, 0);
       }
+    if constexpr (QT16) {  // + Qt^T dO, contraction index 32 g + 8 lq + e
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        bf16x8 bo[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          bo[j] = *reinterpret_cast<const bf16x8*>(&sDt[16 * j + lr][32 * g + 8 * lq]);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const chunk::f32x8 x = chunk::f32x8_of(qa[g][i]);
+          const bf16x8 hi = __builtin_convertvector(x, bf16x8);
+          const chunk::f32x8 r1 = x - __builtin_convertvector(hi, chunk::f32x8);
+          const bf16x8 mi = __builtin_convertvector(r1, bf16x8);
+          const bf16x8 lo =
+              __builtin_convertvector(r1 - __builtin_convertvector(mi, chunk::f32x8), bf16x8);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            R[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, bo[j], R[i][j], 0, 0, 0);
+            R[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mi, bo[j], R[i][j], 0, 0, 0);
+            R[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, bo[j], R[i][j], 0, 0, 0);
+          }
+        }
+      }
+    }
   }
   if (R_end) {
 #pragma unroll
@@ -924,6 +962,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_walk_kernel(
     float* __restrict__ dS0, float* __restrict__ rec_b) {
   __shared__ __attribute__((aligned(16))) float sRt[64][WTS];  // sRt[j][cc] = R[cc][j]
   __shared__ __attribute__((aligned(16))) float sZt[64][WTS];  // sZt[j][kk]: the update's B operand
+  __shared__ __attribute__((aligned(16))) uint16_t sDt[64][DTS];  // bf16 d_o, transposed
   const int64_t nb = (int64_t)N * H * 2;
   int64_t b = blockIdx.x;
   const bool fwd = both && b < nb;
@@ -937,9 +976,9 @@ __global__ void __launch_bounds__(NT, 2) bwd_walk_kernel(
   eos = eos < bos ? bos : (eos > T_tot ? T_tot : eos);
   const int64_t L = eos - bos;
   if (fwd)
-    walk_dir<true, DOB>(img, d_o, bos, L, n, h, tile, H, S0, rec_f, nullptr, sRt, sZt);
+    walk_dir<true, DOB>(img, d_o, bos, L, n, h, tile, H, S0, rec_f, nullptr, sRt, sZt, sDt);
   else
-    walk_dir<false, DOB>(img, d_o, bos, L, n, h, tile, H, dSf, rec_b, dS0, sRt, sZt);
+    walk_dir<false, DOB>(img, d_o, bos, L, n, h, tile, H, dSf, rec_b, dS0, sRt, sZt, sDt);
 }
 
 template <bool QB, bool DOB>
