@@ -528,8 +528,6 @@ __global__ void __launch_bounds__(NT, 3) bwd_prep_kernel(const void* __restrict_
   const int HDi = static_cast<int>(HD);
   const auto rk = chunk_rows(k, QB ? 2 : 4, p, HD), rq = chunk_rows(q, QB ? 2 : 4, p, HD),
              rv = chunk_rows(v, QB ? 2 : 4, p, HD), rg = chunk_rows(g, 4, p, HD);
-  auto Kf = [&](int r, int cc) { return row_at<QB>(rk, HDi, r, cc); };
-  auto Qf = [&](int r, int cc) { return row_at<QB>(rq, HDi, r, cc); };
   if (t < C) sB[t] = t < p.Lc ? beta[(p.t0 + t) * H + p.h] : 0.0f;
   if (t < D) {  // gamma: running sum of the floored g down channel t (rows past the end repeat the last)
     float gv[C];
@@ -559,26 +557,23 @@ __global__ void __launch_bounds__(NT, 3) bwd_prep_kernel(const void* __restrict_
     }
     AtpDiag dA{}, dB{};
     f32x4 oa[3] = {}, op[3] = {};
-    constexpr int PS = C * CS / NT;
-    float rk[PS], rq[PS], rg[PS];
+    // thread t reads row t / 4, slab columns 4 (t % 4) .. + 3 (4 contiguous channels)
+    static_assert(C * CS == 4 * NT, "one 4-channel group a thread");
+    const int fr = t >> 2, fc = 4 * (t & 3);
+    f32x4 rk4, rq4, rg4;
     auto fetch_slab = [&](int sl) {
-#pragma unroll
-      for (int u = 0; u < PS; ++u) {
-        const int e = t + NT * u, r = e / CS, ch = e % CS;
-        const int cc = ch < 8 ? 8 * sl + ch : 64 + 8 * sl + ch - 8;
-        rk[u] = Kf(r, cc);
-        rq[u] = Qf(r, cc);
-        rg[u] = Gf(r, cc);
-      }
+      const int cc = fc < 8 ? 8 * sl + fc : 64 + 8 * sl + fc - 8;
+      rk4 = row4_at<QB>(rk, HDi, fr, cc);
+      rq4 = row4_at<QB>(rq, HDi, fr, cc);
+      rg4 = *reinterpret_cast<const f32x4*>(im + Rec::G + fr * D + cc);
     };
     fetch_slab(0);
     for (int sl = 0; sl < D / CS; ++sl) {
 #pragma unroll
-      for (int u = 0; u < PS; ++u) {
-        const int e = t + NT * u, r = e / CS, ch = e % CS;
-        sK[r * (CS + 1) + ch] = rk[u];
-        sQ[r * (CS + 1) + ch] = rq[u];
-        sG[r * (CS + 1) + ch] = rg[u];
+      for (int i = 0; i < 4; ++i) {
+        sK[fr * (CS + 1) + fc + i] = rk4[i];
+        sQ[fr * (CS + 1) + fc + i] = rq4[i];
+        sG[fr * (CS + 1) + fc + i] = rg4[i];
       }
       barrier_lds();
       if (sl + 1 < D / CS) fetch_slab(sl + 1);
@@ -607,9 +602,12 @@ __global__ void __launch_bounds__(NT, 3) bwd_prep_kernel(const void* __restrict_
       }
       barrier_lds();
     }
-    for (int e = t; e < C * C; e += NT) {
-      im[Rec::AT + e] = sA[e / C][e % C];
-      im[Rec::P + e] = sP[e / C][e % C];
+    for (int e = t; e < C * C / 4; e += NT) {  // 4 columns a thread
+      const int r = e / (C / 4), s4 = 4 * (e % (C / 4));
+      *reinterpret_cast<f32x4*>(im + Rec::AT + r * C + s4) =
+          f32x4{sA[r][s4], sA[r][s4 + 1], sA[r][s4 + 2], sA[r][s4 + 3]};
+      *reinterpret_cast<f32x4*>(im + Rec::P + r * C + s4) =
+          f32x4{sP[r][s4], sP[r][s4 + 1], sP[r][s4 + 2], sP[r][s4 + 3]};
     }
   }
   __syncthreads();
@@ -679,9 +677,14 @@ __global__ void __launch_bounds__(NT, 3) bwd_prep_kernel(const void* __restrict_
     }
   }
   __syncthreads();
-  for (int e = t; e < C * C; e += NT) im[Rec::M + e] = sM[e / C][e % C];
+  for (int e = t; e < C * C / 4; e += NT) {
+    const int r = e / (C / 4), s4 = 4 * (e % (C / 4));
+    *reinterpret_cast<f32x4*>(im + Rec::M + r * C + s4) =
+        f32x4{sM[r][s4], sM[r][s4 + 1], sM[r][s4 + 2], sM[r][s4 + 3]};
+  }
   float* sa = sPool;  // the products' slabs, over At (read for the last time above)
-  {  // W = M diag(b) K_E
+  {  // W = M diag(b) K_E; the operand fetch, which reads each K and gamma
+     // element once, also writes K_D = K e^(gamma_C - gamma) to the record
     float acc[4][8];
     zero(acc);
     gemm_staged2v<4, 8, true, true>(
@@ -690,6 +693,10 @@ __global__ void __launch_bounds__(NT, 3) bwd_prep_kernel(const void* __restrict_
         [&](int s2, int cc) {
           const f32x4 kv = row4_at<QB>(rk, HDi, s2, cc);
           const f32x4 gv = *reinterpret_cast<const f32x4*>(im + Rec::G + s2 * D + cc);
+          const f32x4 gl = *reinterpret_cast<const f32x4*>(im + Rec::G + (C - 1) * D + cc);
+          *reinterpret_cast<f32x4*>(im + Rec::KD + s2 * D + cc) =
+              f32x4{kv[0] * __expf(gl[0] - gv[0]), kv[1] * __expf(gl[1] - gv[1]),
+                    kv[2] * __expf(gl[2] - gv[2]), kv[3] * __expf(gl[3] - gv[3])};
           const float b = sB[s2];
           return f32x4{b * kv[0] * __expf(gv[0]), b * kv[1] * __expf(gv[1]),
                        b * kv[2] * __expf(gv[2]), b * kv[3] * __expf(gv[3])};
@@ -712,9 +719,15 @@ __global__ void __launch_bounds__(NT, 3) bwd_prep_kernel(const void* __restrict_
       for (int j = 0; j < 8; ++j) im[Rec::U + orow<4>(i) * D + ocol(j)] = acc[i][j];
   }
   __syncthreads();  // W complete
-  {  // Qt = scale (Q_E - P W)
+  {  // Qt = scale (Q_E - P W): acc starts at -Q_E (its reads overlap the product's)
     float acc[4][8];
-    zero(acc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int r = orow<4>(i), cc = ocol(j);
+        acc[i][j] = -row_at<QB>(rq, HDi, r, cc) * __expf(Gf(r, cc));
+      }
     gemm_staged2v<4, 8, true, true>(
         acc, C, sa,
         [&](int r, int s2) { return *reinterpret_cast<const f32x4*>(im + Rec::P + r * C + s2); },
@@ -722,14 +735,7 @@ __global__ void __launch_bounds__(NT, 3) bwd_prep_kernel(const void* __restrict_
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int r = orow<4>(i), cc = ocol(j);
-        im[Rec::QT + r * D + cc] = scale * (Qf(r, cc) * __expf(Gf(r, cc)) - acc[i][j]);
-      }
-  }
-  for (int e = t; e < C * D; e += NT) {
-    const int r = e / D, cc = e % D;
-    im[Rec::KD + e] = Kf(r, cc) * __expf(Gf(C - 1, cc) - Gf(r, cc));
+      for (int j = 0; j < 8; ++j) im[Rec::QT + orow<4>(i) * D + ocol(j)] = -scale * acc[i][j];
   }
   if (t < D) im[Rec::EC + t] = __expf(Gf(C - 1, t));
 }
