@@ -22,7 +22,7 @@
 //             direction, both directions in one launch: forward, the entry
 //             state of every chunk; backward, the state gradient at every
 //             chunk's end and the initial state's gradient;
-//   bwd_grad  in launches of at most GRAD_SLOTS workgroups, one per (chunk,
+//   bwd_grad  in launches of at most grad_slots workgroups, one per (chunk,
 //             head), each with a scratch slot of its own: with S and dS_next known, the
 //             chunk's gradients dq, dk, dv, dg, dbeta by the chain rule
 //             through the identities above (the pairwise decay terms of At
@@ -1013,7 +1013,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_grad_kernel(
   const float* im = img + p.pair * Rec::floats;
   const float* S = Srec + p.pair * (int64_t)(D * D);
   const float* dS = dSrec + p.pair * (int64_t)(D * D);
-  // one scratch slot per workgroup of a launch (a launch has at most GRAD_SLOTS)
+  // one scratch slot per workgroup of a launch (a launch has at most grad_slots)
   float* sc = scr + (int64_t)blockIdx.x * Scr::floats;
   const int Lc = p.Lc;
   auto tok = [&](int r, int cc) { return (p.t0 + r) * HD + (int64_t)p.h * D + cc; };
@@ -1410,14 +1410,20 @@ __global__ void __launch_bounds__(NT, 2) bwd_grad_kernel(
 
 }  // namespace
 
-// The gradient kernel runs in launches of at most GRAD_SLOTS workgroups (two
-// per CU), each with a scratch slot of its own, so the scratch does not grow
-// with the sequence length.
-constexpr int64_t GRAD_SLOTS = 512;
+// The gradient kernel runs in launches of at most grad_slots workgroups, each
+// with a scratch slot of its own: one slot per (chunk, head) up to
+// GRAD_SLOTS_MAX (1.9 GB of scratch), so that up to that size one launch
+// covers every chunk and the GPU's dispatcher refills each CU as its
+// workgroups finish (a launch per 512 workgroups cost 4 % at T = 4096,
+// H = 96 in drained launch tails).
+constexpr int64_t GRAD_SLOTS_MAX = 8192;
+int64_t grad_slots(size_t pairs) {
+  return pairs == 0 ? 1 : (pairs < (size_t)GRAD_SLOTS_MAX ? (int64_t)pairs : GRAD_SLOTS_MAX);
+}
 
 size_t workspace_bytes(int64_t T_tot, int N, int H) {
   const size_t pairs = (size_t)(T_tot / C + N) * (size_t)H;
-  return (pairs * (size_t)(Rec::floats + 2 * D * D) + (size_t)GRAD_SLOTS * Scr::floats) *
+  return (pairs * (size_t)(Rec::floats + 2 * D * D) + (size_t)grad_slots(pairs) * Scr::floats) *
          sizeof(float);
 }
 
@@ -1461,8 +1467,9 @@ hipError_t launch(const void* q, const void* k, const void* v, bool qkv_bf16, co
       bwd_walk_kernel<false><<<grid, NT, 0, s>>>(img, d_o, cu, N, T, H, both, S0, Srec,
                                                  dS_final, dS0, dSrec);
   }
-  for (int64_t item0 = 0; item0 < chunk_blocks; item0 += GRAD_SLOTS) {
-    const int64_t nb = chunk_blocks - item0 < GRAD_SLOTS ? chunk_blocks - item0 : GRAD_SLOTS;
+  const int64_t slots = grad_slots(pairs);
+  for (int64_t item0 = 0; item0 < chunk_blocks; item0 += slots) {
+    const int64_t nb = chunk_blocks - item0 < slots ? chunk_blocks - item0 : slots;
 #define KDA_BG(QB, OB)                                                                        \
   bwd_grad_kernel<QB, OB><<<dim3((unsigned)nb), NT, 0, s>>>(                                  \
       q, k, v, d_o, g, beta, cu, N, T, H, (int)maxnch, scale, img, Srec, dSrec, scr, dq, dk, dv, \
