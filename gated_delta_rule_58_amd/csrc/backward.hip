@@ -742,32 +742,53 @@ __global__ void __launch_bounds__(NT, 3) bwd_prep_kernel(const void* __restrict_
 
 // One chunk walk of a (sequence, head, 64-column tile).  Lane (lr, lq) of
 // wave w holds R[32 w + 16 i + 4 lq + v][16 j + lr] of the tile in R[i][j][v]
-// (i < 2, j < 4), the fp32 16x16x4 MFMA accumulator layout.
+// (i < 2, j < 4), the 16x16 MFMA accumulator layout.
 // Forward (FWD): R = S from the initial state; rec[chunk] = R at the chunk's
 // entry.  Backward: R = dS from dS_final; rec[chunk] = R at the chunk's end,
 // R_end gets the gradient of the initial state.
 // A chunk step is Z = A1 R (A1 = W forward, K_D backward; 16 rows of Z per
-// wave), then R <- e^gamma_C R + K_D^T (U - Z) forward, or e^gamma_C R +
-// [W; Qt]^T [-Z; dO] backward (dO the tile's columns of d_o).  The MFMA A
+// wave), then R <- e^gamma_C R + K_D^T (U - Z) forward, or e^gamma_C R -
+// W^T Z + Qt^T dO backward (dO the tile's columns of d_o).  The MFMA A
 // operands come straight from the chunk record into registers, one product
 // ahead of their use: rows of A1 16 bytes a lane (lane group lq, sub-step s
 // of group u takes contraction index 16 u + 4 lq + s, and the B operand is
 // read in that order), the transposed operands one float a lane (16 lanes on
-// 64 contiguous bytes).  The B operands R and [Z; dO] sit transposed in LDS,
-// so the four contraction indices of a lane's four MFMAs are one 16-byte
-// read.  Two barriers per chunk step.  With bf16 d_o, Qt^T dO runs on the
-// bf16 16x16x32 MFMA instead: dO exactly, Qt as three bf16 terms (hi + mid +
-// lo hold its 24 bits; products of bf16 pairs are exact in the fp32
-// accumulator), a sixth of the fp32 MFMA cycles.
-constexpr int WTS = 2 * C + 4;  // row stride of the transposed LDS tiles: 4 WTS = 16 (mod 64 banks)
-constexpr int DTS = C + 8;      // the bf16 d_o tile's: 16-lane reads of 16 bytes land on distinct banks
+// 64 contiguous bytes).  The B operands sit transposed in LDS, so the
+// contraction indices a lane needs are one 16-byte read.  Two barriers per
+// chunk step.
+// Z = A1 R runs on the fp32 16x16x4 MFMA.  The update's products run on the
+// bf16 16x16x32 MFMA with three-term splits: x = hi + mid + lo in bf16
+// carries the 24 bits of an fp32 x, a product of two such sums is the six
+// bf16 products whose terms reach 2^-16 of the leading one (the three left
+// out are below 2^-24 of it), and bf16 products are exact in the fp32
+// accumulator, so the result is the fp32 product up to fp32 rounding at a
+// third of the fp32 MFMA cycles.  With bf16 d_o, Qt^T dO takes dO as is
+// (three products); with fp32 d_o it stays on the fp32 MFMA.
+constexpr int WTS = 2 * C + 4;  // row stride of the transposed fp32 tile: 4 WTS = 16 (mod 64 banks)
+constexpr int DTS = C + 8;      // the bf16 tiles': 16-lane reads of 16 bytes land on distinct banks
+constexpr int FTS = C + 4;      // the fp32 d_o tile's
+__device__ __forceinline__ void split3(const chunk::f32x8& x, bf16x8& hi, bf16x8& mi, bf16x8& lo) {
+  hi = __builtin_convertvector(x, bf16x8);
+  const chunk::f32x8 r = x - __builtin_convertvector(hi, chunk::f32x8);
+  mi = __builtin_convertvector(r, bf16x8);
+  lo = __builtin_convertvector(r - __builtin_convertvector(mi, chunk::f32x8), bf16x8);
+}
+__device__ __forceinline__ void split3(const f32x4& x, bf16x4& hi, bf16x4& mi, bf16x4& lo) {
+  hi = __builtin_convertvector(x, bf16x4);
+  const f32x4 r = x - __builtin_convertvector(hi, f32x4);
+  mi = __builtin_convertvector(r, bf16x4);
+  lo = __builtin_convertvector(r - __builtin_convertvector(mi, f32x4), bf16x4);
+}
+__device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
 template <bool FWD, bool DOB>
 __device__ __forceinline__ void walk_dir(const float* __restrict__ img, const void* d_o,
                                          int64_t bos, int64_t L, int n, int h, int tile, int H,
                                          const float* __restrict__ R_init,
                                          float* __restrict__ rec, float* __restrict__ R_end,
-                                         float (*sRt)[WTS], float (*sZt)[WTS],
-                                         uint16_t (*sDt)[DTS]) {
+                                         float (*sRt)[WTS], uint16_t (*sZp)[64][DTS],
+                                         void* sDo) {
   const int nch = static_cast<int>((L + C - 1) / C);
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, lr = lane & 15, lq = lane >> 4;
   const int64_t HD = (int64_t)H * D;
@@ -788,7 +809,9 @@ __device__ __forceinline__ void walk_dir(const float* __restrict__ img, const vo
   };
   // Record reads through a buffer resource: the lane's part of the offset in
   // one register, the rest a constant, so the many operand loads share it.
-  auto rec_buf = [&](int64_t pair) { return chunk::make_buf(img + pair * Rec::floats, Rec::floats * 4); };
+  auto rec_buf = [&](int64_t pair) {
+    return chunk::make_buf(img + pair * Rec::floats, Rec::floats * 4);
+  };
   auto ld1 = [](__amdgpu_buffer_rsrc_t rs, int vo, int so) {
     return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, vo, so, 0));
   };
@@ -802,6 +825,10 @@ __device__ __forceinline__ void walk_dir(const float* __restrict__ img, const vo
           f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, vo_zA, (A1 + 16 * u) * 4, 0));
   };
   if (nch > 0) load_zA(rec_buf(pair_of(0)));
+  // the transposed update operand: K_D forward, W backward, as bf16 A
+  // fragments (row 32 w + 16 i + lr, contraction 32 g + 8 lq + e)
+  constexpr int A2 = FWD ? Rec::KD : Rec::W;
+  const int vo_a = (8 * lq * D + 32 * w + lr) * 4;
   for (int it = 0; it < nch; ++it) {
     const int c = FWD ? it : nch - 1 - it;
     const int64_t pair = pair_of(it);
@@ -817,37 +844,45 @@ __device__ __forceinline__ void walk_dir(const float* __restrict__ img, const vo
         *reinterpret_cast<f32x4*>(&sRt[16 * j + lr][rrow(i, 0)]) = R[i][j];
       }
     // the state update's operands, in flight during Z = A1 R
-    constexpr bool QT16 = !FWD && DOB;  // Qt^T dO on the bf16 MFMA
-    constexpr int KU = FWD || QT16 ? 4 : 8;  // 16-deep fp32 contraction groups of the update
-    float a2[KU][4][2];
-    const int vo_a2 = (4 * lq * D + 32 * w + lr) * 4;
+    float a2[2][2][8];  // [g][i][e]
 #pragma unroll
-    for (int u = 0; u < KU; ++u)
+    for (int g = 0; g < 2; ++g)
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const int part = FWD ? Rec::KD : (u < 4 ? Rec::W : Rec::QT);
-          a2[u][s][i] = ld1(rs, vo_a2, (part + (16 * (u & 3) + s) * D + 16 * i) * 4);
-        }
-    float qa[2][2][8];  // QT16: Qt[32 g + 8 lq + e][32 w + 16 i + lr] in qa[g][i][e]
-    if constexpr (QT16) {
-      const int vo_q = (8 * lq * D + 32 * w + lr) * 4;
+        for (int e = 0; e < 8; ++e) a2[g][i][e] = ld1(rs, vo_a, (A2 + (32 * g + e) * D + 16 * i) * 4);
+    // Qt^T dO: bf16 A fragments (like a2) with bf16 d_o, fp32 16x16x4 ones
+    // (contraction 16 u + 4 lq + s) with fp32 d_o
+    float qa[2][2][8];
+    float qf[4][4][2];
+    if constexpr (!FWD) {
+      if constexpr (DOB) {
 #pragma unroll
-      for (int g = 0; g < 2; ++g)
+        for (int g = 0; g < 2; ++g)
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+          for (int i = 0; i < 2; ++i)
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            qa[g][i][e] = ld1(rs, vo_q, (Rec::QT + (32 * g + e) * D + 16 * i) * 4);
+            for (int e = 0; e < 8; ++e)
+              qa[g][i][e] = ld1(rs, vo_a, (Rec::QT + (32 * g + e) * D + 16 * i) * 4);
+      } else {
+        const int vo_q = (4 * lq * D + 32 * w + lr) * 4;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+              qf[u][s][i] = ld1(rs, vo_q, (Rec::QT + (16 * u + s) * D + 16 * i) * 4);
+      }
     }
     float ec[2][4];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) ec[i][v] = ld1(rs, (32 * w + 4 * lq) * 4, (Rec::EC + 16 * i + v) * 4);
-    u32x4 draw[2];  // QT16: d_o row `lane`, columns 16 w .. + 15, as stored
-    f32x4 ext[4];  // forward: U at Z's elements; backward: d_o row `lane`, columns 16 w .. + 15
+      for (int v = 0; v < 4; ++v)
+        ec[i][v] = ld1(rs, (32 * w + 4 * lq) * 4, (Rec::EC + 16 * i + v) * 4);
+    u32x4 draw[2];  // bf16 d_o row `lane`, columns 16 w .. + 15, as stored
+    f32x4 ext[4];   // forward: U at Z's elements; fp32 d_o: that row segment
     if constexpr (FWD) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
@@ -889,17 +924,27 @@ __device__ __forceinline__ void walk_dir(const float* __restrict__ img, const vo
           z[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(zA[u][s], b[s], z[j], 0, 0, 0);
       }
     if (it + 1 < nch) load_zA(rec_buf(pair_of(it + 1)));
-    // (3) U - Z (forward) or [-Z; dO] (backward), transposed, into LDS
+    // (3) U - Z (forward) or -Z (backward) as three bf16 planes, transposed,
+    // and d_o, into LDS
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      *reinterpret_cast<f32x4*>(&sZt[16 * j + lr][16 * w + 4 * lq]) = FWD ? ext[j] - z[j] : -z[j];
-    if constexpr (QT16) {
+    for (int j = 0; j < 4; ++j) {
+      bf16x4 ph, pm, pl;
+      split3(FWD ? ext[j] - z[j] : -z[j], ph, pm, pl);
+      *reinterpret_cast<bf16x4*>(&sZp[0][16 * j + lr][16 * w + 4 * lq]) = ph;
+      *reinterpret_cast<bf16x4*>(&sZp[1][16 * j + lr][16 * w + 4 * lq]) = pm;
+      *reinterpret_cast<bf16x4*>(&sZp[2][16 * j + lr][16 * w + 4 * lq]) = pl;
+    }
+    if constexpr (!FWD) {
+      if constexpr (DOB) {
+        uint16_t(*sDt)[DTS] = reinterpret_cast<uint16_t(*)[DTS]>(sDo);
 #pragma unroll
-      for (int e = 0; e < 16; ++e)
-        sDt[16 * w + e][lane] = static_cast<uint16_t>(draw[e >> 3][(e & 7) >> 1] >> (16 * (e & 1)));
-    } else if constexpr (!FWD) {
+        for (int e = 0; e < 16; ++e)
+          sDt[16 * w + e][lane] = static_cast<uint16_t>(draw[e >> 3][(e & 7) >> 1] >> (16 * (e & 1)));
+      } else {
+        float(*sDf)[FTS] = reinterpret_cast<float(*)[FTS]>(sDo);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) sZt[16 * w + e][C + lane] = ext[e >> 2][e & 3];
+        for (int e = 0; e < 16; ++e) sDf[16 * w + e][lane] = ext[e >> 2][e & 3];
+      }
     }
     barrier_lds();
     // (4) the state update
@@ -910,17 +955,33 @@ __device__ __forceinline__ void walk_dir(const float* __restrict__ img, const vo
 #pragma unroll
         for (int v = 0; v < 4; ++v) R[i][j][v] *= ec[i][v];
 #pragma unroll
-    for (int u = 0; u < KU; ++u)
+    for (int g = 0; g < 2; ++g) {  // + A2^T (U - Z) or A2^T (-Z), contraction 32 g + 8 lq + e
+      bf16x8 bz[3][4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f32x4 b = *reinterpret_cast<const f32x4*>(&sZt[16 * j + lr][16 * u + 4 * lq]);
+      for (int p = 0; p < 3; ++p)
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
+        for (int j = 0; j < 4; ++j)
+          bz[p][j] = *reinterpret_cast<const bf16x8*>(&sZp[p][16 * j + lr][32 * g + 8 * lq]);
 #pragma unroll
-          for (int i = 0; i < 2; ++i)
-            R[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a2[u][s][i], b[s], R[i][j], 0, 0, 0);
+      for (int i = 0; i < 2; ++i) {
+        bf16x8 ah, am, al;
+        split3(chunk::f32x8_of(a2[g][i]), ah, am, al);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) R[i][j] = mfma_bf16(am, bz[1][j], R[i][j]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) R[i][j] = mfma_bf16(al, bz[0][j], R[i][j]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) R[i][j] = mfma_bf16(ah, bz[2][j], R[i][j]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) R[i][j] = mfma_bf16(am, bz[0][j], R[i][j]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) R[i][j] = mfma_bf16(ah, bz[1][j], R[i][j]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) R[i][j] = mfma_bf16(ah, bz[0][j], R[i][j]);
       }
-    if constexpr (QT16) {  // + Qt^T dO, contraction index 32 g + 8 lq + e
+    }
+    if constexpr (!FWD && DOB) {  // + Qt^T dO, dO exact in bf16
+      uint16_t(*sDt)[DTS] = reinterpret_cast<uint16_t(*)[DTS]>(sDo);
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
         bf16x8 bo[4];
@@ -929,20 +990,29 @@ __device__ __forceinline__ void walk_dir(const float* __restrict__ img, const vo
           bo[j] = *reinterpret_cast<const bf16x8*>(&sDt[16 * j + lr][32 * g + 8 * lq]);
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-          const chunk::f32x8 x = chunk::f32x8_of(qa[g][i]);
-          const bf16x8 hi = __builtin_convertvector(x, bf16x8);
-          const chunk::f32x8 r1 = x - __builtin_convertvector(hi, chunk::f32x8);
-          const bf16x8 mi = __builtin_convertvector(r1, bf16x8);
-          const bf16x8 lo =
-              __builtin_convertvector(r1 - __builtin_convertvector(mi, chunk::f32x8), bf16x8);
+          bf16x8 qh, qm, ql;
+          split3(chunk::f32x8_of(qa[g][i]), qh, qm, ql);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            R[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, bo[j], R[i][j], 0, 0, 0);
-            R[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mi, bo[j], R[i][j], 0, 0, 0);
-            R[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, bo[j], R[i][j], 0, 0, 0);
-          }
+          for (int j = 0; j < 4; ++j) R[i][j] = mfma_bf16(ql, bo[j], R[i][j]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) R[i][j] = mfma_bf16(qm, bo[j], R[i][j]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) R[i][j] = mfma_bf16(qh, bo[j], R[i][j]);
         }
       }
+    } else if constexpr (!FWD) {  // + Qt^T dO on the fp32 MFMA
+      float(*sDf)[FTS] = reinterpret_cast<float(*)[FTS]>(sDo);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const f32x4 b = *reinterpret_cast<const f32x4*>(&sDf[16 * j + lr][16 * u + 4 * lq]);
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+              R[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(qf[u][s][i], b[s], R[i][j], 0, 0, 0);
+        }
     }
   }
   if (R_end) {
@@ -967,8 +1037,10 @@ __global__ void __launch_bounds__(NT, 2) bwd_walk_kernel(
     const float* __restrict__ S0, float* __restrict__ rec_f, const float* __restrict__ dSf,
     float* __restrict__ dS0, float* __restrict__ rec_b) {
   __shared__ __attribute__((aligned(16))) float sRt[64][WTS];  // sRt[j][cc] = R[cc][j]
-  __shared__ __attribute__((aligned(16))) float sZt[64][WTS];  // sZt[j][kk]: the update's B operand
-  __shared__ __attribute__((aligned(16))) uint16_t sDt[64][DTS];  // bf16 d_o, transposed
+  __shared__ __attribute__((aligned(16))) uint16_t sZp[3][64][DTS];  // the update's B planes
+  // d_o of the chunk's tile, transposed: bf16 [64][DTS] or fp32 [64][FTS]
+  constexpr int DO_BYTES = DOB ? 64 * DTS * 2 : 64 * FTS * 4;
+  __shared__ __attribute__((aligned(16))) unsigned char sDo[DO_BYTES];
   const int64_t nb = (int64_t)N * H * 2;
   int64_t b = blockIdx.x;
   const bool fwd = both && b < nb;
@@ -982,9 +1054,9 @@ __global__ void __launch_bounds__(NT, 2) bwd_walk_kernel(
   eos = eos < bos ? bos : (eos > T_tot ? T_tot : eos);
   const int64_t L = eos - bos;
   if (fwd)
-    walk_dir<true, DOB>(img, d_o, bos, L, n, h, tile, H, S0, rec_f, nullptr, sRt, sZt, sDt);
+    walk_dir<true, DOB>(img, d_o, bos, L, n, h, tile, H, S0, rec_f, nullptr, sRt, sZp, sDo);
   else
-    walk_dir<false, DOB>(img, d_o, bos, L, n, h, tile, H, dSf, rec_b, dS0, sRt, sZt, sDt);
+    walk_dir<false, DOB>(img, d_o, bos, L, n, h, tile, H, dSf, rec_b, dS0, sRt, sZp, sDo);
 }
 
 template <bool QB, bool DOB>
