@@ -70,104 +70,27 @@ struct Scr {
                        DQE = 5 * C * D, DKD = 6 * C * D, floats = 7 * C * D;
 };
 
-// acc += a b for a (16 TM) x (16 TN) output over the 256 threads, on fp32
-// MFMA, with the operands staged through LDS in slabs of KT = 16 along the
-// contraction (each element read once from memory instead of once per thread
-// that uses it).  acc[i][j] is element (orow<TM>(i), ocol(j)).  A_KC: a(m, kk) is contiguous along kk in memory
-// (else along m); B_NC: b(kk, n) is contiguous along n (else along kk); the
-// slab fill follows the contiguous index.  sa: 16 x (16 TM + 1) floats, sb:
-// 16 x (16 TN + 1) floats.  Contains barriers: every thread of the block calls it.
 constexpr int KT = 16;
-template <int TM, int TN, bool A_KC, bool B_NC, typename FA, typename FB>
-__device__ __forceinline__ void gemm_staged(float (&acc)[TM][TN], int K, float* stage, FA a,
-                                            FB b) {
-  // slab rows 17 floats past a multiple of 32 apart: the MFMA reads (16
-  // consecutive elements of 4 consecutive rows) and the kk-fastest fills
-  // both spread over the banks
-  constexpr int M = 16 * TM, N = 16 * TN, MS = M + 17, NS = N + 17;
-  float* sa = stage;
-  float* sb = stage + KT * MS;
-  constexpr int PA = M * KT / NT, PB = N * KT / NT;  // slab elements per thread
-  static_assert(TM % 4 == 0, "whole 16-row tiles per wave");
-  const int t = threadIdx.x;
-  // the next slab is read into registers while the current one is in use
-  float ra[PA], rb[PB];
-  auto fetch = [&](int k0) {
-#pragma unroll
-    for (int u = 0; u < PA; ++u) {
-      const int e = t + NT * u;
-      const int m = A_KC ? e / KT : e % M, kt = A_KC ? e % KT : e / M;
-      ra[u] = a(m, k0 + kt);
-    }
-#pragma unroll
-    for (int u = 0; u < PB; ++u) {
-      const int e = t + NT * u;
-      const int n = B_NC ? e % N : e / KT, kt = B_NC ? e / N : e % KT;
-      rb[u] = b(k0 + kt, n);
-    }
-  };
-  // the accumulators as MFMA tiles for the whole product (4 consecutive
-  // registers each), converted from and to acc once
-  constexpr int TR = TM / 4;
-  f32x4 ct[TR][TN];
-#pragma unroll
-  for (int i = 0; i < TR; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-      ct[i][j] = f32x4{acc[4 * i][j], acc[4 * i + 1][j], acc[4 * i + 2][j], acc[4 * i + 3][j]};
-  fetch(0);
-  for (int k0 = 0; k0 < K; k0 += KT) {
-#pragma unroll
-    for (int u = 0; u < PA; ++u) {
-      const int e = t + NT * u;
-      const int m = A_KC ? e / KT : e % M, kt = A_KC ? e % KT : e / M;
-      sa[kt * MS + m] = ra[u];
-    }
-#pragma unroll
-    for (int u = 0; u < PB; ++u) {
-      const int e = t + NT * u;
-      const int n = B_NC ? e % N : e / KT, kt = B_NC ? e / N : e % KT;
-      sb[kt * NS + n] = rb[u];
-    }
-    __syncthreads();
-    if (k0 + KT < K) fetch(k0 + KT);
-    // fp32 16x16x4 MFMA: lane l supplies A[l % 16][l / 16] and B[l / 16][l % 16]
-    // and holds D[4 (l / 16) + v][l % 16]; wave w owns the output tile rows
-    // TR w .. TR w + TR - 1 and every tile column.
-    const int lane = t & 63, w = t >> 6, lr = lane & 15, lq = lane >> 4;
-#pragma unroll
-    for (int kg = 0; kg < KT / 4; ++kg) {
-      const int kk = 4 * kg + lq;
-      float av[TR], bv[TN];
-#pragma unroll
-      for (int i = 0; i < TR; ++i) av[i] = sa[kk * MS + 16 * (TR * w + i) + lr];
-#pragma unroll
-      for (int j = 0; j < TN; ++j) bv[j] = sb[kk * NS + 16 * j + lr];
-#pragma unroll
-      for (int i = 0; i < TR; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          ct[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[i], bv[j], ct[i][j], 0, 0, 0);
-    }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int i = 0; i < TR; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) acc[4 * i + v][j] = ct[i][j][v];
-}
 constexpr int STAGE_FLOATS = KT * (64 + 17) + KT * (128 + 17);  // the largest product's slabs
-// gemm_staged with two slabs in flight, for kernels with the registers to
-// spare: slab k0 + 2 KT is read into registers while slab k0 is used, and
-// the barriers order LDS only, so those loads stay in flight across them (a
-// __syncthreads fence would wait for them at every slab).  With one slab in
-// flight each slab costs about one memory latency, the products being short.
-// K, always 64 or 128, is a multiple of 2 KT; a caller orders any global
-// data it wrote before the call itself.
+// acc += a b for a (16 TM / 4 x 4 waves) x (16 TN) output over the 256
+// threads, on fp32 MFMA, with the operands staged through LDS in slabs of
+// KT = 16 along the contraction (each element read once from memory instead
+// of once per thread that uses it).  acc[0][j][i][v] is element
+// (orow<TM>(4 i + v), ocol(j)): wave w owns whole 16-row output tiles and
+// keeps them in MFMA accumulator registers for the whole product.  A_KC:
+// a(m, kk) is contiguous along kk in memory (else along m); B_NC: b(kk, n)
+// is contiguous along n (else along kk); the slab fill follows the
+// contiguous index.  Slab rows are 17 floats past a multiple of 32 apart, so
+// the MFMA reads (16 consecutive elements of 4 consecutive rows) and the
+// kk-fastest fills both spread over the banks.  Two slabs are in flight:
+// slab k0 + 2 KT is read into registers while slab k0 is used, and the
+// barriers order LDS only, so those loads stay in flight across them (a
+// __syncthreads fence would wait for them at every slab).  K, always 64 or
+// 128, is a multiple of 2 KT; a caller orders any global data it wrote
+// before the call itself.  Contains barriers: every thread of the block
+// calls it.
 template <int TM, int TN, bool A_KC, bool B_NC, typename FA, typename FB>
-__device__ __forceinline__ void gemm_staged2(float (&acc)[TM][TN], int K, float* stage, FA a,
+__device__ __forceinline__ void gemm_staged2(f32x4 (&ct)[TM / 4][TN], int K, float* stage, FA a,
                                              FB b) {
   constexpr int M = 16 * TM, N = 16 * TN, MS = M + 17, NS = N + 17;
   float* sa = stage;
@@ -191,12 +114,6 @@ __device__ __forceinline__ void gemm_staged2(float (&acc)[TM][TN], int K, float*
     }
   };
   constexpr int TR = TM / 4;
-  f32x4 ct[TR][TN];
-#pragma unroll
-  for (int i = 0; i < TR; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-      ct[i][j] = f32x4{acc[4 * i][j], acc[4 * i + 1][j], acc[4 * i + 2][j], acc[4 * i + 3][j]};
   fetch(0, 0);
   fetch(KT, 1);
   for (int k0 = 0; k0 < K; k0 += 2 * KT) {
@@ -235,12 +152,6 @@ __device__ __forceinline__ void gemm_staged2(float (&acc)[TM][TN], int K, float*
       barrier_lds();
     }
   }
-#pragma unroll
-  for (int i = 0; i < TR; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) acc[4 * i + v][j] = ct[i][j][v];
 }
 
 // gemm_staged2 with operands read 4 at a time: a4(m, k) returns a(m, k .. k+3)
@@ -248,7 +159,7 @@ __device__ __forceinline__ void gemm_staged2(float (&acc)[TM][TN], int K, float*
 // b(k, n .. n+3) when B_NC, else b(k .. k+3, n).  Index arguments are
 // multiples of 4 along the vector's direction.
 template <int TM, int TN, bool A_KC, bool B_NC, typename FA4, typename FB4>
-__device__ __forceinline__ void gemm_staged2v(float (&acc)[TM][TN], int K, float* stage, FA4 a4,
+__device__ __forceinline__ void gemm_staged2v(f32x4 (&ct)[TM / 4][TN], int K, float* stage, FA4 a4,
                                               FB4 b4) {
   constexpr int M = 16 * TM, N = 16 * TN, MS = M + 17, NS = N + 17;
   float* sa = stage;
@@ -284,12 +195,6 @@ __device__ __forceinline__ void gemm_staged2v(float (&acc)[TM][TN], int K, float
     }
   };
   constexpr int TR = TM / 4;
-  f32x4 ct[TR][TN];
-#pragma unroll
-  for (int i = 0; i < TR; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-      ct[i][j] = f32x4{acc[4 * i][j], acc[4 * i + 1][j], acc[4 * i + 2][j], acc[4 * i + 3][j]};
   fetch(0, 0);
   fetch(KT, 1);
   for (int k0 = 0; k0 < K; k0 += 2 * KT) {
@@ -329,16 +234,10 @@ __device__ __forceinline__ void gemm_staged2v(float (&acc)[TM][TN], int K, float
       barrier_lds();
     }
   }
-#pragma unroll
-  for (int i = 0; i < TR; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) acc[4 * i + v][j] = ct[i][j][v];
 }
 
-// Output element of acc[i][j] after gemm_staged<TM, TN>: row orow<TM>(i),
-// column ocol(j).
+// Output element of acc[0][j][i][v] after gemm_staged2<TM, TN>: row
+// orow<TM>(4 i + v), column ocol(j).
 template <int TM>
 __device__ __forceinline__ int orow(int i) {
   const int t = threadIdx.x;
@@ -346,12 +245,12 @@ __device__ __forceinline__ int orow(int i) {
 }
 __device__ __forceinline__ int ocol(int j) { return 16 * j + (threadIdx.x & 15); }
 
-template <int TM, int TN>
-__device__ __forceinline__ void zero(float (&acc)[TM][TN]) {
+template <int TR, int TN>
+__device__ __forceinline__ void zero(f32x4 (&acc)[TR][TN]) {
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+  for (int i = 0; i < TR; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = 0.0f;
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 }
 
 // Chunk c of sequence n: its packed index (bos / 64 + n + c) is unique and
@@ -685,7 +584,7 @@ __global__ void __launch_bounds__(NT, 3) bwd_prep_kernel(const void* __restrict_
   float* sa = sPool;  // the products' slabs, over At (read for the last time above)
   {  // W = M diag(b) K_E; the operand fetch, which reads each K and gamma
      // element once, also writes K_D = K e^(gamma_C - gamma) to the record
-    float acc[4][8];
+    f32x4 acc[1][8];
     zero(acc);
     gemm_staged2v<4, 8, true, true>(
         acc, C, sa,
@@ -704,10 +603,10 @@ __global__ void __launch_bounds__(NT, 3) bwd_prep_kernel(const void* __restrict_
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) im[Rec::W + orow<4>(i) * D + ocol(j)] = acc[i][j];
+      for (int j = 0; j < 8; ++j) im[Rec::W + orow<4>(i) * D + ocol(j)] = acc[0][j][i];
   }
   {  // U = M diag(b) V
-    float acc[4][8];
+    f32x4 acc[1][8];
     zero(acc);
     gemm_staged2v<4, 8, true, true>(
         acc, C, sa,
@@ -716,17 +615,17 @@ __global__ void __launch_bounds__(NT, 3) bwd_prep_kernel(const void* __restrict_
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) im[Rec::U + orow<4>(i) * D + ocol(j)] = acc[i][j];
+      for (int j = 0; j < 8; ++j) im[Rec::U + orow<4>(i) * D + ocol(j)] = acc[0][j][i];
   }
   __syncthreads();  // W complete
   {  // Qt = scale (Q_E - P W): acc starts at -Q_E (its reads overlap the product's)
-    float acc[4][8];
+    f32x4 acc[1][8];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int r = orow<4>(i), cc = ocol(j);
-        acc[i][j] = -row_at<QB>(rq, HDi, r, cc) * __expf(Gf(r, cc));
+        acc[0][j][i] = -row_at<QB>(rq, HDi, r, cc) * __expf(Gf(r, cc));
       }
     gemm_staged2v<4, 8, true, true>(
         acc, C, sa,
@@ -735,7 +634,7 @@ __global__ void __launch_bounds__(NT, 3) bwd_prep_kernel(const void* __restrict_
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) im[Rec::QT + orow<4>(i) * D + ocol(j)] = -scale * acc[i][j];
+      for (int j = 0; j < 8; ++j) im[Rec::QT + orow<4>(i) * D + ocol(j)] = -scale * acc[0][j][i];
   }
   if (t < D) im[Rec::EC + t] = __expf(Gf(C - 1, t));
 }
@@ -1097,11 +996,11 @@ __global__ void __launch_bounds__(NT, 2) bwd_grad_kernel(
   auto Vf = [&](int r, int cc) { return row_at<QB>(rv, HDi, r, cc); };
   auto dOf = [&](int r, int cc) { return row_at<DOB>(ro, HDi, r, cc); };
   auto Gf = [&](int r, int cc) { return im[Rec::G + r * D + cc]; };
-  auto put8 = [&](float (&acc)[4][8], int off, float mul) {
+  auto put8 = [&](f32x4 (&acc)[1][8], int off, float mul) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) sc[off + orow<4>(i) * D + ocol(j)] = mul * acc[i][j];
+      for (int j = 0; j < 8; ++j) sc[off + orow<4>(i) * D + ocol(j)] = mul * acc[0][j][i];
   };
   if (t < C) {
     sB[t] = t < Lc ? beta[(p.t0 + t) * H + p.h] : 0.0f;
@@ -1111,7 +1010,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_grad_kernel(
   static_assert(C * (D / 32) == NT, "one flag word per thread");
   __syncthreads();
   {  // X = V - K_E S
-    float acc[4][8];
+    f32x4 acc[1][8];
     zero(acc);
     gemm_staged2<4, 8, true, true>(acc, D, sa,
                                   [&](int r, int cc) { return Kf(r, cc) * __expf(Gf(r, cc)); },
@@ -1121,19 +1020,19 @@ __global__ void __launch_bounds__(NT, 2) bwd_grad_kernel(
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int r = orow<4>(i), col = ocol(j);
-        sc[Scr::X + r * D + col] = Vf(r, col) - acc[i][j];
+        sc[Scr::X + r * D + col] = Vf(r, col) - acc[0][j][i];
       }
   }
   __syncthreads();
   {  // Delta = M diag(b) X
-    float acc[4][8];
+    f32x4 acc[1][8];
     zero(acc);
     gemm_staged2<4, 8, true, true>(acc, C, sa, [&](int r, int s) { return im[Rec::M + r * C + s]; },
                                   [&](int s, int j) { return sB[s] * sc[Scr::X + s * D + j]; });
     put8(acc, Scr::DL, 1.0f);
   }
   {  // dDelta = K_D dS_next + scale P^T dO
-    float acc[4][8];
+    f32x4 acc[1][8];
     zero(acc);
     gemm_staged2<4, 8, true, true>(acc, D, sa,
                                   [&](int r, int cc) { return im[Rec::KD + r * D + cc]; },
@@ -1145,7 +1044,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_grad_kernel(
   }
   __syncthreads();
   {  // dY = M^T dDelta, dX = diag(b) dY (= dv), dbeta += rowsum(dY . X)
-    float acc[4][8];
+    f32x4 acc[1][8];
     zero(acc);
     gemm_staged2<4, 8, false, true>(acc, C, sa,
                                    [&](int r, int s) { return im[Rec::M + s * C + r]; },
@@ -1157,10 +1056,10 @@ __global__ void __launch_bounds__(NT, 2) bwd_grad_kernel(
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int col = ocol(j);
-        const float dX = sB[r] * acc[i][j];
+        const float dX = sB[r] * acc[0][j][i];
         sc[Scr::DX + r * D + col] = dX;
         if (r < Lc) dv[tok(r, col)] = dX;
-        part = fmaf(acc[i][j], sc[Scr::X + r * D + col], part);
+        part = fmaf(acc[0][j][i], sc[Scr::X + r * D + col], part);
       }
 #pragma unroll
       for (int off = 1; off < 16; off <<= 1) part += __shfl_xor(part, off);
@@ -1169,7 +1068,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_grad_kernel(
   }
   __syncthreads();
   {  // dM = dDelta Y^T
-    float a4[4][4];
+    f32x4 a4[1][4];
     zero(a4);
     gemm_staged2<4, 4, true, false>(a4, D, sa,
                                    [&](int r, int j) { return sc[Scr::DD + r * D + j]; },
@@ -1177,10 +1076,10 @@ __global__ void __launch_bounds__(NT, 2) bwd_grad_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) sT[orow<4>(i)][ocol(j)] = a4[i][j];
+      for (int j = 0; j < 4; ++j) sT[orow<4>(i)][ocol(j)] = a4[0][j][i];
   }
   {  // dP = scale dO Delta^T on s <= r
-    float a4[4][4];
+    f32x4 a4[1][4];
     zero(a4);
     gemm_staged2<4, 4, true, false>(a4, D, sa, [&](int r, int j) { return dOf(r, j); },
                                    [&](int j, int s) { return sc[Scr::DL + s * D + j]; });
@@ -1189,24 +1088,24 @@ __global__ void __launch_bounds__(NT, 2) bwd_grad_kernel(
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int r = orow<4>(i), s = ocol(j);
-        sDP[r][s] = (s <= r && r < Lc) ? scale * a4[i][j] : 0.0f;
+        sDP[r][s] = (s <= r && r < Lc) ? scale * a4[0][j][i] : 0.0f;
       }
   }
   __syncthreads();
   float* dMMt = sc + Scr::DKE;  // [C][C], until dK_E is written
   {  // dM M^T
-    float a4[4][4];
+    f32x4 a4[1][4];
     zero(a4);
     gemm_staged2<4, 4, true, false>(a4, C, sa, [&](int r, int u) { return sT[r][u]; },
                                    [&](int u, int s) { return im[Rec::M + s * C + u]; });
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) dMMt[orow<4>(i) * C + ocol(j)] = a4[i][j];
+      for (int j = 0; j < 4; ++j) dMMt[orow<4>(i) * C + ocol(j)] = a4[0][j][i];
   }
   __syncthreads();
   {  // dA = -M^T (dM M^T) on s < r
-    float a4[4][4];
+    f32x4 a4[1][4];
     zero(a4);
     gemm_staged2<4, 4, false, true>(a4, C, sa,
                                    [&](int r, int u) { return im[Rec::M + u * C + r]; },
@@ -1216,11 +1115,11 @@ __global__ void __launch_bounds__(NT, 2) bwd_grad_kernel(
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int r = orow<4>(i), s = ocol(j);
-        sT[r][s] = (s < r && r < Lc) ? -a4[i][j] : 0.0f;
+        sT[r][s] = (s < r && r < Lc) ? -a4[0][j][i] : 0.0f;
       }
   }
   {  // dK_E = -dX S^T
-    float acc[4][8];
+    f32x4 acc[1][8];
     zero(acc);
     gemm_staged2<4, 8, true, false>(acc, D, sa,
                                    [&](int r, int j) { return sc[Scr::DX + r * D + j]; },
@@ -1228,14 +1127,14 @@ __global__ void __launch_bounds__(NT, 2) bwd_grad_kernel(
     put8(acc, Scr::DKE, -1.0f);
   }
   {  // dQ_E = scale dO S^T
-    float acc[4][8];
+    f32x4 acc[1][8];
     zero(acc);
     gemm_staged2<4, 8, true, false>(acc, D, sa, [&](int r, int j) { return dOf(r, j); },
                                    [&](int j, int cc) { return S[cc * D + j]; });
     put8(acc, Scr::DQE, scale);
   }
   {  // dK_D = Delta dS_next^T
-    float acc[4][8];
+    f32x4 acc[1][8];
     zero(acc);
     gemm_staged2<4, 8, true, false>(acc, D, sa,
                                    [&](int r, int j) { return sc[Scr::DL + r * D + j]; },
