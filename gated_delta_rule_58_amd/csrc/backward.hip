@@ -71,11 +71,15 @@ struct Scr {
 };
 
 constexpr int KT = 16;
-constexpr int STAGE_FLOATS = KT * (64 + 17) + KT * (128 + 17);  // the largest product's slabs
+// Slab rows of the staged products: the contraction index contiguous, rows
+// 4 x odd floats apart, so the 16-byte fills and reads of 16 lanes land on
+// distinct banks.
+constexpr int SKP = KT + 4;
+constexpr int STAGE_FLOATS = (64 + 128) * SKP;  // the largest product's slabs
 // acc += a b for a (16 TM / 4 x 4 waves) x (16 TN) output over the 256
 // threads, on fp32 MFMA, with the operands staged through LDS in slabs of
 // KT = 16 along the contraction (each element read once from memory instead
-// of once per thread that uses it).  acc[0][j][i][v] is element
+// of once per thread that uses it).  acc[i][j][v] is element
 // (orow<TM>(4 i + v), ocol(j)): wave w owns whole 16-row output tiles and
 // keeps them in MFMA accumulator registers for the whole product.  A_KC:
 // a(m, kk) is contiguous along kk in memory (else along m); B_NC: b(kk, n)
@@ -92,25 +96,41 @@ constexpr int STAGE_FLOATS = KT * (64 + 17) + KT * (128 + 17);  // the largest p
 template <int TM, int TN, bool A_KC, bool B_NC, typename FA, typename FB>
 __device__ __forceinline__ void gemm_staged2(f32x4 (&ct)[TM / 4][TN], int K, float* stage, FA a,
                                              FB b) {
-  constexpr int M = 16 * TM, N = 16 * TN, MS = M + 17, NS = N + 17;
-  float* sa = stage;
-  float* sb = stage + KT * MS;
-  constexpr int PA = M * KT / NT, PB = N * KT / NT;
-  static_assert(TM % 4 == 0, "whole 16-row tiles per wave");
+  constexpr int M = 16 * TM, N = 16 * TN;
+  float* sa = stage;           // [M][SKP]
+  float* sb = stage + M * SKP;  // [N][SKP]
+  constexpr int QA = M * KT / 4 / NT, QB = N * KT / 4 / NT;  // quads a thread fills
+  static_assert(TM % 4 == 0 && QA >= 1 && QB >= 1 && (M * KT) % (4 * NT) == 0 &&
+                    (N * KT) % (4 * NT) == 0,
+                "whole 16-row tiles per wave, whole quads per thread");
   const int t = threadIdx.x;
-  float ra[2][PA], rb[2][PB];
+  // quad u of thread t: row m (column n) and contraction indices 4 q .. 4 q + 3,
+  // the lanes running along the index that is contiguous in memory
+  auto a_pos = [&](int u, int& m, int& q) {
+    const int e = t + NT * u;
+    m = A_KC ? e / (KT / 4) : e % M;
+    q = A_KC ? e % (KT / 4) : e / M;
+  };
+  auto b_pos = [&](int u, int& n, int& q) {
+    const int e = t + NT * u;
+    n = B_NC ? e % N : e / (KT / 4);
+    q = B_NC ? e / N : e % (KT / 4);
+  };
+  f32x4 ra[2][QA], rb[2][QB];
   auto fetch = [&](int k0, int sl) {
 #pragma unroll
-    for (int u = 0; u < PA; ++u) {
-      const int e = t + NT * u;
-      const int m = A_KC ? e / KT : e % M, kt = A_KC ? e % KT : e / M;
-      ra[sl][u] = a(m, k0 + kt);
+    for (int u = 0; u < QA; ++u) {
+      int m, q;
+      a_pos(u, m, q);
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2) ra[sl][u][s2] = a(m, k0 + 4 * q + s2);
     }
 #pragma unroll
-    for (int u = 0; u < PB; ++u) {
-      const int e = t + NT * u;
-      const int n = B_NC ? e % N : e / KT, kt = B_NC ? e / N : e % KT;
-      rb[sl][u] = b(k0 + kt, n);
+    for (int u = 0; u < QB; ++u) {
+      int n, q;
+      b_pos(u, n, q);
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2) rb[sl][u][s2] = b(k0 + 4 * q + s2, n);
     }
   };
   constexpr int TR = TM / 4;
@@ -120,35 +140,36 @@ __device__ __forceinline__ void gemm_staged2(f32x4 (&ct)[TM / 4][TN], int K, flo
 #pragma unroll
     for (int sl = 0; sl < 2; ++sl) {
 #pragma unroll
-      for (int u = 0; u < PA; ++u) {
-        const int e = t + NT * u;
-        const int m = A_KC ? e / KT : e % M, kt = A_KC ? e % KT : e / M;
-        sa[kt * MS + m] = ra[sl][u];
+      for (int u = 0; u < QA; ++u) {
+        int m, q;
+        a_pos(u, m, q);
+        *reinterpret_cast<f32x4*>(sa + m * SKP + 4 * q) = ra[sl][u];
       }
 #pragma unroll
-      for (int u = 0; u < PB; ++u) {
-        const int e = t + NT * u;
-        const int n = B_NC ? e % N : e / KT, kt = B_NC ? e / N : e % KT;
-        sb[kt * NS + n] = rb[sl][u];
+      for (int u = 0; u < QB; ++u) {
+        int n, q;
+        b_pos(u, n, q);
+        *reinterpret_cast<f32x4*>(sb + n * SKP + 4 * q) = rb[sl][u];
       }
       barrier_lds();
       if (k0 + (2 + sl) * KT < K) fetch(k0 + (2 + sl) * KT, sl);
-      // the fp32 16x16x4 MFMA fragments of gemm_staged
+      // sub-step s of lane group lq takes contraction index 4 lq + s: a
+      // lane's four are one 16-byte read of each operand
       const int lane = t & 63, w = t >> 6, lr = lane & 15, lq = lane >> 4;
+      f32x4 av[TR], bv[TN];
 #pragma unroll
-      for (int kg = 0; kg < KT / 4; ++kg) {
-        const int kk = 4 * kg + lq;
-        float av[TR], bv[TN];
+      for (int i = 0; i < TR; ++i)
+        av[i] = *reinterpret_cast<const f32x4*>(sa + (16 * (TR * w + i) + lr) * SKP + 4 * lq);
 #pragma unroll
-        for (int i = 0; i < TR; ++i) av[i] = sa[kk * MS + 16 * (TR * w + i) + lr];
+      for (int j = 0; j < TN; ++j)
+        bv[j] = *reinterpret_cast<const f32x4*>(sb + (16 * j + lr) * SKP + 4 * lq);
 #pragma unroll
-        for (int j = 0; j < TN; ++j) bv[j] = sb[kk * NS + 16 * j + lr];
+      for (int s2 = 0; s2 < 4; ++s2)
 #pragma unroll
         for (int i = 0; i < TR; ++i)
 #pragma unroll
           for (int j = 0; j < TN; ++j)
-            ct[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[i], bv[j], ct[i][j], 0, 0, 0);
-      }
+            ct[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[i][s2], bv[j][s2], ct[i][j], 0, 0, 0);
       barrier_lds();
     }
   }
