@@ -979,8 +979,12 @@ __global__ void __launch_bounds__(NT, 2) bwd_walk_kernel(
     walk_dir<false, DOB>(img, d_o, bos, L, n, h, tile, H, dSf, rec_b, dS0, sRt, sZp, sDo);
 }
 
+// Three workgroups per CU (50 KB of LDS, at most 168 VGPRs): the kernel is
+// bound by latency, and a third workgroup hides it better than the few
+// registers the compiler spills to fit (one workgroup per CU measured 35 %
+// slower than two, three 7 % faster).
 template <bool QB, bool DOB>
-__global__ void __launch_bounds__(NT, 2) bwd_grad_kernel(
+__global__ void __launch_bounds__(NT, 3) bwd_grad_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const void* __restrict__ d_o, const float* __restrict__ g, const float* __restrict__ beta,
     const int32_t* __restrict__ cu, int N, int T_tot, int H, int maxnch, float scale,
@@ -991,10 +995,10 @@ __global__ void __launch_bounds__(NT, 2) bwd_grad_kernel(
   __shared__ float sT[C][C + 1], sDP[C][C + 1];
   __shared__ float sB[C], sDB[C], sGC[D];
   __shared__ uint32_t sFl[C][D / 32];  // bit c % 32 of word c / 32: g of (row, c) floored
-  // the products' LDS slabs, then (pairwise phase) K, Q, gamma and the three
-  // accumulators of a 16-channel slab, and the per-wave partial sums
+  // the products' LDS slabs, then (pairwise phase) K, Q and gamma of a
+  // 16-channel slab and the per-wave partial sums
   constexpr int SC = 16, SS = SC + 1;
-  constexpr int PAIR_FLOATS = 6 * C * SS + 4 * SC;
+  constexpr int PAIR_FLOATS = 3 * C * SS + 4 * SC;
   __shared__ float sU[PAIR_FLOATS > STAGE_FLOATS ? PAIR_FLOATS : STAGE_FLOATS];
   float* sa = sU;
   ChunkPos p;
@@ -1206,77 +1210,46 @@ __global__ void __launch_bounds__(NT, 2) bwd_grad_kernel(
   float* sK = sU;                  // [C][SS] k of the slab's channels
   float* sQ = sK + C * SS;         // q
   float* sG = sQ + C * SS;         // gamma
-  float* aK = sG + C * SS;         // dk, dq and dgamma of the slab, accumulated
-  float* aQ = aK + C * SS;
-  float* aG = aQ + C * SS;
-  float* sPart = aG + C * SS;      // [4][SC] partial sums of the gamma_C term
+  float* sPart = sG + C * SS;      // [4][SC] partial sums of the gamma_C term
   const int lane = t & 63, w = t >> 6, ln = lane & 15, lq = lane >> 4;
-  // Thread t holds row x = t / 4, channels 4 (t % 4) .. 4 (t % 4) + 3 of the
-  // slab: k, q, gamma, the three decay-factor gradients and g (for the
-  // floor), read one slab ahead (4-wide loads) so that the reads stay in
-  // flight across the slab's barriers (which order LDS only).
+  // Thread t reads row t / 4, channels 4 (t % 4) .. + 3 of the slab's k, q
+  // and gamma into LDS (4-wide loads, one slab ahead so that the reads stay
+  // in flight across the slab's barriers, which order LDS only).  Lane
+  // (ln, lq) of wave w then owns rows 16 w + 4 lq + v (v < 4) of channel
+  // c0 + ln: it reads those elements' decay-factor gradients and g (for the
+  // floor) itself, one slab ahead as well, adds the pairwise terms and writes
+  // dq, dk and dgamma.
   // (16 channels per slab: the MFMA tiles below use the 16 lanes of a row
   // as the slab's channels)
   static_assert(SC == 16, "one slab channel per lane of a 16-lane row");
   const int xr = t >> 2, n4 = 4 * (t & 3);
   const auto rgf = chunk_rows(g, 4, p, HD);
-  f32x4 pk, pq, pg, pke, pqe, pkd, pgc, pgv;
+  const auto rsc = chunk::make_buf(sc, Scr::floats * 4);
+  f32x4 pk, pq, pg;          // the LDS fill
+  f32x4 eke, eqe, ekd, egv;  // the lane's own elements, rows 16 w + 4 lq + v
   auto fetch_slab = [&](int c0) {
     const int cc = c0 + n4;
-    pgc = *reinterpret_cast<const f32x4*>(im + Rec::G + (C - 1) * D + cc);
     pk = row4_at<QB>(rk, HDi, xr, cc);
     pq = row4_at<QB>(rq, HDi, xr, cc);
     pg = *reinterpret_cast<const f32x4*>(im + Rec::G + xr * D + cc);
-    pke = *reinterpret_cast<const f32x4*>(sc + Scr::DKE + xr * D + cc);
-    pqe = *reinterpret_cast<const f32x4*>(sc + Scr::DQE + xr * D + cc);
-    pkd = *reinterpret_cast<const f32x4*>(sc + Scr::DKD + xr * D + cc);
-    pgv = row4_at<false>(rgf, HDi, xr, cc);  // rows past the chunk end read 0
+    const int x0 = 16 * w + 4 * lq, vo = (x0 * D + c0 + ln) * 4;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      eke[v] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsc, vo, (Scr::DKE + v * D) * 4, 0));
+      eqe[v] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsc, vo, (Scr::DQE + v * D) * 4, 0));
+      ekd[v] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsc, vo, (Scr::DKD + v * D) * 4, 0));
+      egv[v] = row_at<false>(rgf, HDi, x0 + v, c0 + ln);  // rows past the chunk end read 0
+    }
   };
   fetch_slab(0);
   for (int c0 = 0; c0 < D; c0 += SC) {
-    {  // the slab to LDS, and the decay-factor terms of K_E, Q_E, K_D
-      const int x = xr;
-      float dgc[4];
-      uint32_t fl = 0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int n = n4 + i;
-        const float kx = pk[i], qx = pq[i], gx = pg[i];
-        sK[x * SS + n] = kx;
-        sQ[x * SS + n] = qx;
-        sG[x * SS + n] = gx;
-        float vk = 0.0f, vq = 0.0f, vg = 0.0f, dc = 0.0f;
-        if (x < Lc) {
-          const float dke = pke[i], dqe = pqe[i], dkd = pkd[i];
-          const float E = __expf(gx), F = __expf(pgc[i] - gx);
-          vk = dke * E + dkd * F;
-          vq = dqe * E;
-          vg = (dke * kx + dqe * qx) * E - dkd * kx * F;
-          dc = dkd * kx * F;
-          if (decay_floored(pgv[i])) fl |= 1u << ((c0 + n) & 31);
-        }
-        aK[x * SS + n] = vk;
-        aQ[x * SS + n] = vq;
-        aG[x * SS + n] = vg;
-        dgc[i] = dc;
-      }
-      if (fl) atomicOr(&sFl[x][c0 >> 5], fl);
-      // the gamma_C terms of each channel summed over the wave's 16 rows (the
-      // lanes sharing t % 4)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float v = dgc[i];
-        v += __shfl_xor(v, 4);
-        v += __shfl_xor(v, 8);
-        v += __shfl_xor(v, 16);
-        v += __shfl_xor(v, 32);
-        dgc[i] = v;
-      }
-      if (lane < 4) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sPart[w * SC + n4 + i] = dgc[i];
-      }
+    for (int i = 0; i < 4; ++i) {
+      sK[xr * SS + n4 + i] = pk[i];
+      sQ[xr * SS + n4 + i] = pq[i];
+      sG[xr * SS + n4 + i] = pg[i];
     }
+    const f32x4 dke = eke, dqe = eqe, dkd = ekd, gv = egv;  // this slab's
     barrier_lds();
     if (c0 + SC < D) fetch_slab(c0 + SC);
     {  // pairs across blocks on fp32 MFMA: wave w owns the rows of block w.
@@ -1346,6 +1319,8 @@ __global__ void __launch_bounds__(NT, 2) bwd_grad_kernel(
       const float gb = w >= 1 ? sG[(16 * w - 1) * SS + ln] : 0.0f;
       const float ge = sG[(16 * w + 15) * SS + ln];
       const float g7 = sG[(16 * w + 7) * SS + ln];
+      const float gc = sG[(C - 1) * SS + ln];  // gamma_C of channel c0 + ln
+      float dcs = 0.0f;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int xl = 4 * lq + v, x = 16 * w + xl;
@@ -1366,23 +1341,27 @@ __global__ void __launch_bounds__(NT, 2) bwd_grad_kernel(
           l2 += L2[v] * eb;
         }
         if (w <= 2) rr += R[v] * __expf(ge - gx);
+        // plus the terms of the decay factors of K_E = K e^gamma, Q_E = Q
+        // e^gamma and K_D = K e^(gamma_C - gamma)
         const float kx = sK[x * SS + ln], qx = sQ[x * SS + ln];
-        aK[x * SS + ln] += l1 + rr;
-        aQ[x * SS + ln] += l2;
-        aG[x * SS + ln] += kx * l1 + qx * l2 - kx * rr;
+        if (x < Lc) {
+          const float E = __expf(gx), F = __expf(gc - gx);
+          const int cc = c0 + ln;
+          dk[tok(x, cc)] = dke[v] * E + dkd[v] * F + l1 + rr;
+          dq[tok(x, cc)] = dqe[v] * E + l2;
+          sc[Scr::DX + x * D + cc] =  // dgamma, summed below
+              (dke[v] * kx + dqe[v] * qx) * E - dkd[v] * kx * F + kx * l1 + qx * l2 - kx * rr;
+          dcs += dkd[v] * kx * F;
+          if (decay_floored(gv[v])) atomicOr(&sFl[x][cc >> 5], 1u << (cc & 31));
+        }
       }
+      // the gamma_C terms of channel c0 + ln summed over the wave's 16 rows
+      dcs += __shfl_xor(dcs, 16);
+      dcs += __shfl_xor(dcs, 32);
+      if (lq == 0) sPart[w * SC + ln] = dcs;
     }
-    barrier_lds();
-    for (int e = t; e < C * SC; e += NT) {
-      const int x = e / SC, ch = e % SC;
-      if (x < Lc) {
-        dq[tok(x, c0 + ch)] = aQ[x * SS + ch];
-        dk[tok(x, c0 + ch)] = aK[x * SS + ch];
-        sc[Scr::DX + x * D + c0 + ch] = aG[x * SS + ch];  // dgamma, summed below
-      }
-    }
+    barrier_lds();  // sPart complete; the slab's arrays are refilled next
     if (t < SC) sGC[c0 + t] += sPart[t] + sPart[SC + t] + sPart[2 * SC + t] + sPart[3 * SC + t];
-    barrier_lds();  // the slab's arrays are refilled for the next 16 channels
   }
   __syncthreads();  // dgamma (scratch) complete
   if (t < D) {  // dg: reverse cumulative sum of dgamma, plus the gamma_C terms
