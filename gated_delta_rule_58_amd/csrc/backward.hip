@@ -257,7 +257,7 @@ __device__ __forceinline__ void gemm_staged2v(f32x4 (&ct)[TM / 4][TN], int K, fl
   }
 }
 
-// Output element of acc[0][j][i][v] after gemm_staged2<TM, TN>: row
+// Output element of acc[i][j][v] after gemm_staged2<TM, TN>: row
 // orow<TM>(4 i + v), column ocol(j).
 template <int TM>
 __device__ __forceinline__ int orow(int i) {
