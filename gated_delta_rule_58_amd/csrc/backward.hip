@@ -15,18 +15,21 @@
 //   dS     = Diag(e^gamma_C) dS_next - W^T (K_D dS_next) + Qt^T dO     (backward)
 // Both walks have one shape: Z = A1 R; R <- e^gamma_C R - A2^T Z + A3^T B.
 //
-// Three kernels, all in fp32 (the products on fp32 MFMA):
+// Three kernels, all to fp32 accuracy: the products on fp32 MFMA, except the
+// walk's state update, whose products run on bf16 MFMA as three-term splits
+// that carry fp32's 24 bits (walk_dir):
 //   bwd_prep  one workgroup per (chunk, head): gamma, At, P, M, W, U, Qt, K_D
 //             and e^gamma_C into a per-(chunk, head) record;
 //   bwd_walk  one workgroup per (sequence, head, 64-column tile) and
 //             direction, both directions in one launch: forward, the entry
 //             state of every chunk; backward, the state gradient at every
 //             chunk's end and the initial state's gradient;
-//   bwd_grad  in launches of at most grad_slots workgroups, one per (chunk,
-//             head), each with a scratch slot of its own: with S and dS_next known, the
-//             chunk's gradients dq, dk, dv, dg, dbeta by the chain rule
-//             through the identities above (the pairwise decay terms of At
-//             and P per key channel, then a reverse cumulative sum for dg).
+//   bwd_grad  one workgroup per (chunk, head), each with a scratch slot of
+//             its own, in launches of at most grad_slots workgroups: with S
+//             and dS_next known, the chunk's gradients dq, dk, dv, dg, dbeta
+//             by the chain rule through the identities above (the pairwise
+//             decay terms of At and P per key channel, then a reverse
+//             cumulative sum for dg).
 #include "chunk_common.hpp"
 #include "kda_device.hpp"
 #include "kda_internal.hpp"
