@@ -1186,14 +1186,28 @@ __global__ void __launch_bounds__(NT, 3) bwd_grad_kernel(
     a += __shfl_xor(a, 2);
     if (qd == 0) sDB[r] += a;
   }
-  {  // d e^gamma_C[c] = sum_j dS_next[c, j] S[c, j]: channel c on threads c, c + 128
-    const int cc = t & (D - 1), half = t >> 7;
-    float d = 0.0f;
-#pragma unroll 16
-    for (int j = 64 * half; j < 64 * half + 64; ++j) d = fmaf(dS[cc * D + j], S[cc * D + j], d);
-    if (half == 1) sU[cc] = d;
+  {  // d e^gamma_C[c] = sum_j dS_next[c, j] S[c, j]: each group of 32 lanes
+     // reads rows c = t / 32 + 8 p (p < 16) 16 bytes a lane, so that a load
+     // covers whole rows, and sums each row over its lanes
+    const int j4 = 4 * (t & 31), r0 = t >> 5;
+    float part[16];
+#pragma unroll
+    for (int p2 = 0; p2 < 16; ++p2) {
+      const int c = r0 + 8 * p2;
+      const f32x4 a = *reinterpret_cast<const f32x4*>(dS + c * D + j4);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(S + c * D + j4);
+      part[p2] = fmaf(a[0], b[0], fmaf(a[1], b[1], fmaf(a[2], b[2], a[3] * b[3])));
+    }
+#pragma unroll
+    for (int p2 = 0; p2 < 16; ++p2)
+#pragma unroll
+      for (int off = 1; off < 32; off <<= 1) part[p2] += __shfl_xor(part[p2], off);
+    if ((t & 31) == 0) {
+#pragma unroll
+      for (int p2 = 0; p2 < 16; ++p2) sU[r0 + 8 * p2] = part[p2];
+    }
     __syncthreads();
-    if (half == 0) sGC[cc] = (d + sU[cc]) * __expf(Gf(C - 1, cc));
+    if (t < D) sGC[t] = sU[t] * __expf(Gf(C - 1, t));
     __syncthreads();
   }
   // The terms of the decay factors and the pairwise terms of At and P, 16
