@@ -30,6 +30,8 @@
 //             by the chain rule through the identities above (the pairwise
 //             decay terms of At and P per key channel, then a reverse
 //             cumulative sum for dg).
+#include <type_traits>
+
 #include "chunk_common.hpp"
 #include "kda_device.hpp"
 #include "kda_internal.hpp"
@@ -119,21 +121,33 @@ __device__ __forceinline__ void gemm_staged2(f32x4 (&ct)[TM / 4][TN], int K, flo
     n = B_NC ? e % N : e / (KT / 4);
     q = B_NC ? e / N : e % (KT / 4);
   };
+  // A lambda that returns an f32x4 gives a whole quad at once: a(m, k) the
+  // contraction indices k .. k + 3 of row m (b(k, n) those of column n).
+  constexpr bool AQ = std::is_same_v<decltype(a(0, 0)), f32x4>;
+  constexpr bool BQ = std::is_same_v<decltype(b(0, 0)), f32x4>;
   f32x4 ra[2][QA], rb[2][QB];
   auto fetch = [&](int k0, int sl) {
 #pragma unroll
     for (int u = 0; u < QA; ++u) {
       int m, q;
       a_pos(u, m, q);
+      if constexpr (AQ) {
+        ra[sl][u] = a(m, k0 + 4 * q);
+      } else {
 #pragma unroll
-      for (int s2 = 0; s2 < 4; ++s2) ra[sl][u][s2] = a(m, k0 + 4 * q + s2);
+        for (int s2 = 0; s2 < 4; ++s2) ra[sl][u][s2] = a(m, k0 + 4 * q + s2);
+      }
     }
 #pragma unroll
     for (int u = 0; u < QB; ++u) {
       int n, q;
       b_pos(u, n, q);
+      if constexpr (BQ) {
+        rb[sl][u] = b(k0 + 4 * q, n);
+      } else {
 #pragma unroll
-      for (int s2 = 0; s2 < 4; ++s2) rb[sl][u][s2] = b(k0 + 4 * q + s2, n);
+        for (int s2 = 0; s2 < 4; ++s2) rb[sl][u][s2] = b(k0 + 4 * q + s2, n);
+      }
     }
   };
   constexpr int TR = TM / 4;
@@ -1024,6 +1038,9 @@ __global__ void __launch_bounds__(NT, 3) bwd_grad_kernel(
   auto Vf = [&](int r, int cc) { return row_at<QB>(rv, HDi, r, cc); };
   auto dOf = [&](int r, int cc) { return row_at<DOB>(ro, HDi, r, cc); };
   auto Gf = [&](int r, int cc) { return im[Rec::G + r * D + cc]; };
+  // quads (4 consecutive contraction indices) for the staged products
+  auto ld4 = [](const float* x) { return *reinterpret_cast<const f32x4*>(x); };
+  auto dO4 = [&](int r, int cc) { return row4_at<DOB>(ro, HDi, r, cc); };
   auto put8 = [&](f32x4 (&acc)[1][8], int off, float mul) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -1041,7 +1058,12 @@ __global__ void __launch_bounds__(NT, 3) bwd_grad_kernel(
     f32x4 acc[1][8];
     zero(acc);
     gemm_staged2<4, 8, true, true>(acc, D, sa,
-                                  [&](int r, int cc) { return Kf(r, cc) * __expf(Gf(r, cc)); },
+                                  [&](int r, int cc) {
+                                    const f32x4 kv = row4_at<QB>(rk, HDi, r, cc);
+                                    const f32x4 gv = ld4(im + Rec::G + r * D + cc);
+                                    return f32x4{kv[0] * __expf(gv[0]), kv[1] * __expf(gv[1]),
+                                                 kv[2] * __expf(gv[2]), kv[3] * __expf(gv[3])};
+                                  },
                                   [&](int cc, int j) { return S[cc * D + j]; });
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -1055,7 +1077,7 @@ __global__ void __launch_bounds__(NT, 3) bwd_grad_kernel(
   {  // Delta = M diag(b) X
     f32x4 acc[1][8];
     zero(acc);
-    gemm_staged2<4, 8, true, true>(acc, C, sa, [&](int r, int s) { return im[Rec::M + r * C + s]; },
+    gemm_staged2<4, 8, true, true>(acc, C, sa, [&](int r, int s) { return ld4(im + Rec::M + r * C + s); },
                                   [&](int s, int j) { return sB[s] * sc[Scr::X + s * D + j]; });
     put8(acc, Scr::DL, 1.0f);
   }
@@ -1063,7 +1085,7 @@ __global__ void __launch_bounds__(NT, 3) bwd_grad_kernel(
     f32x4 acc[1][8];
     zero(acc);
     gemm_staged2<4, 8, true, true>(acc, D, sa,
-                                  [&](int r, int cc) { return im[Rec::KD + r * D + cc]; },
+                                  [&](int r, int cc) { return ld4(im + Rec::KD + r * D + cc); },
                                   [&](int cc, int j) { return dS[cc * D + j]; });
     gemm_staged2<4, 8, false, true>(acc, C, sa,
                                    [&](int r, int s) { return scale * im[Rec::P + s * C + r]; },
@@ -1099,8 +1121,8 @@ __global__ void __launch_bounds__(NT, 3) bwd_grad_kernel(
     f32x4 a4[1][4];
     zero(a4);
     gemm_staged2<4, 4, true, false>(a4, D, sa,
-                                   [&](int r, int j) { return sc[Scr::DD + r * D + j]; },
-                                   [&](int j, int s) { return sB[s] * sc[Scr::X + s * D + j]; });
+                                   [&](int r, int j) { return ld4(sc + Scr::DD + r * D + j); },
+                                   [&](int j, int s) { return sB[s] * ld4(sc + Scr::X + s * D + j); });
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -1109,8 +1131,8 @@ __global__ void __launch_bounds__(NT, 3) bwd_grad_kernel(
   {  // dP = scale dO Delta^T on s <= r
     f32x4 a4[1][4];
     zero(a4);
-    gemm_staged2<4, 4, true, false>(a4, D, sa, [&](int r, int j) { return dOf(r, j); },
-                                   [&](int j, int s) { return sc[Scr::DL + s * D + j]; });
+    gemm_staged2<4, 4, true, false>(a4, D, sa, dO4,
+                                   [&](int j, int s) { return ld4(sc + Scr::DL + s * D + j); });
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -1125,7 +1147,7 @@ __global__ void __launch_bounds__(NT, 3) bwd_grad_kernel(
     f32x4 a4[1][4];
     zero(a4);
     gemm_staged2<4, 4, true, false>(a4, C, sa, [&](int r, int u) { return sT[r][u]; },
-                                   [&](int u, int s) { return im[Rec::M + s * C + u]; });
+                                   [&](int u, int s) { return ld4(im + Rec::M + s * C + u); });
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -1150,23 +1172,23 @@ __global__ void __launch_bounds__(NT, 3) bwd_grad_kernel(
     f32x4 acc[1][8];
     zero(acc);
     gemm_staged2<4, 8, true, false>(acc, D, sa,
-                                   [&](int r, int j) { return sc[Scr::DX + r * D + j]; },
-                                   [&](int j, int cc) { return S[cc * D + j]; });
+                                   [&](int r, int j) { return ld4(sc + Scr::DX + r * D + j); },
+                                   [&](int j, int cc) { return ld4(S + cc * D + j); });
     put8(acc, Scr::DKE, -1.0f);
   }
   {  // dQ_E = scale dO S^T
     f32x4 acc[1][8];
     zero(acc);
-    gemm_staged2<4, 8, true, false>(acc, D, sa, [&](int r, int j) { return dOf(r, j); },
-                                   [&](int j, int cc) { return S[cc * D + j]; });
+    gemm_staged2<4, 8, true, false>(acc, D, sa, dO4,
+                                   [&](int j, int cc) { return ld4(S + cc * D + j); });
     put8(acc, Scr::DQE, scale);
   }
   {  // dK_D = Delta dS_next^T
     f32x4 acc[1][8];
     zero(acc);
     gemm_staged2<4, 8, true, false>(acc, D, sa,
-                                   [&](int r, int j) { return sc[Scr::DL + r * D + j]; },
-                                   [&](int j, int cc) { return dS[cc * D + j]; });
+                                   [&](int r, int j) { return ld4(sc + Scr::DL + r * D + j); },
+                                   [&](int j, int cc) { return ld4(dS + cc * D + j); });
     put8(acc, Scr::DKD, 1.0f);
   }
   {  // dbeta += sum_s dA[r, s] At[r, s]: row r on lanes 4r .. 4r + 3; each lane
