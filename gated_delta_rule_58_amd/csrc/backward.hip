@@ -1033,8 +1033,6 @@ __global__ void __launch_bounds__(NT, 3) bwd_grad_kernel(
   const int HDi = static_cast<int>(HD);
   const auto rk = chunk_rows(k, QB ? 2 : 4, p, HD), rq = chunk_rows(q, QB ? 2 : 4, p, HD),
              rv = chunk_rows(v, QB ? 2 : 4, p, HD), ro = chunk_rows(d_o, DOB ? 2 : 4, p, HD);
-  auto Kf = [&](int r, int cc) { return row_at<QB>(rk, HDi, r, cc); };
-  auto Qf = [&](int r, int cc) { return row_at<QB>(rq, HDi, r, cc); };
   auto Vf = [&](int r, int cc) { return row_at<QB>(rv, HDi, r, cc); };
   auto dOf = [&](int r, int cc) { return row_at<DOB>(ro, HDi, r, cc); };
   auto Gf = [&](int r, int cc) { return im[Rec::G + r * D + cc]; };
