@@ -98,9 +98,14 @@ constexpr int STAGE_FLOATS = (64 + 128) * SKP;  // the largest product's slabs
 // 128, is a multiple of 2 KT; a caller orders any global data it wrote
 // before the call itself.  Contains barriers: every thread of the block
 // calls it.
-template <int TM, int TN, bool A_KC, bool B_NC, typename FA, typename FB>
-__device__ __forceinline__ void gemm_staged2(f32x4 (&ct)[TM / 4][TN], int K, float* stage, FA a,
-                                             FB b) {
+// NP products of one shape in a row through one slab pipeline: a(p, m, k)
+// and b(p, k, n) give product p's operands, and after product p < NP - 1
+// epi(p, ct) takes its result and ct starts again from zero (the last one is
+// left in ct).  The two slabs in flight run on across product boundaries, so
+// a product's first slabs are read while the previous one finishes.
+template <int NP, int TM, int TN, bool A_KC, bool B_NC, typename FA, typename FB, typename FE>
+__device__ __forceinline__ void gemm_staged2_seq(f32x4 (&ct)[TM / 4][TN], int K, float* stage,
+                                                 FA a, FB b, FE epi) {
   constexpr int M = 16 * TM, N = 16 * TN;
   float* sa = stage;           // [M][SKP]
   float* sb = stage + M * SKP;  // [N][SKP]
@@ -121,21 +126,22 @@ __device__ __forceinline__ void gemm_staged2(f32x4 (&ct)[TM / 4][TN], int K, flo
     n = B_NC ? e % N : e / (KT / 4);
     q = B_NC ? e / N : e % (KT / 4);
   };
-  // A lambda that returns an f32x4 gives a whole quad at once: a(m, k) the
-  // contraction indices k .. k + 3 of row m (b(k, n) those of column n).
-  constexpr bool AQ = std::is_same_v<decltype(a(0, 0)), f32x4>;
-  constexpr bool BQ = std::is_same_v<decltype(b(0, 0)), f32x4>;
+  // A lambda that returns an f32x4 gives a whole quad at once: a(p, m, k) the
+  // contraction indices k .. k + 3 of row m (b(p, k, n) those of column n).
+  constexpr bool AQ = std::is_same_v<decltype(a(0, 0, 0)), f32x4>;
+  constexpr bool BQ = std::is_same_v<decltype(b(0, 0, 0)), f32x4>;
   f32x4 ra[2][QA], rb[2][QB];
-  auto fetch = [&](int k0, int sl) {
+  auto fetch = [&](int g0, int sl) {  // slab at g0 of the products' joint contraction
+    const int p = g0 / K, k0 = g0 - p * K;
 #pragma unroll
     for (int u = 0; u < QA; ++u) {
       int m, q;
       a_pos(u, m, q);
       if constexpr (AQ) {
-        ra[sl][u] = a(m, k0 + 4 * q);
+        ra[sl][u] = a(p, m, k0 + 4 * q);
       } else {
 #pragma unroll
-        for (int s2 = 0; s2 < 4; ++s2) ra[sl][u][s2] = a(m, k0 + 4 * q + s2);
+        for (int s2 = 0; s2 < 4; ++s2) ra[sl][u][s2] = a(p, m, k0 + 4 * q + s2);
       }
     }
 #pragma unroll
@@ -143,17 +149,18 @@ __device__ __forceinline__ void gemm_staged2(f32x4 (&ct)[TM / 4][TN], int K, flo
       int n, q;
       b_pos(u, n, q);
       if constexpr (BQ) {
-        rb[sl][u] = b(k0 + 4 * q, n);
+        rb[sl][u] = b(p, k0 + 4 * q, n);
       } else {
 #pragma unroll
-        for (int s2 = 0; s2 < 4; ++s2) rb[sl][u][s2] = b(k0 + 4 * q + s2, n);
+        for (int s2 = 0; s2 < 4; ++s2) rb[sl][u][s2] = b(p, k0 + 4 * q + s2, n);
       }
     }
   };
   constexpr int TR = TM / 4;
+  const int KA = NP * K;
   fetch(0, 0);
   fetch(KT, 1);
-  for (int k0 = 0; k0 < K; k0 += 2 * KT) {
+  for (int g0 = 0; g0 < KA; g0 += 2 * KT) {
 #pragma unroll
     for (int sl = 0; sl < 2; ++sl) {
 #pragma unroll
@@ -169,7 +176,7 @@ __device__ __forceinline__ void gemm_staged2(f32x4 (&ct)[TM / 4][TN], int K, flo
         *reinterpret_cast<f32x4*>(sb + n * SKP + 4 * q) = rb[sl][u];
       }
       barrier_lds();
-      if (k0 + (2 + sl) * KT < K) fetch(k0 + (2 + sl) * KT, sl);
+      if (g0 + (2 + sl) * KT < KA) fetch(g0 + (2 + sl) * KT, sl);
       // sub-step s of lane group lq takes contraction index 4 lq + s: a
       // lane's four are one 16-byte read of each operand
       const int lane = t & 63, w = t >> 6, lr = lane & 15, lq = lane >> 4;
@@ -189,7 +196,24 @@ __device__ __forceinline__ void gemm_staged2(f32x4 (&ct)[TM / 4][TN], int K, flo
             ct[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[i][s2], bv[j][s2], ct[i][j], 0, 0, 0);
       barrier_lds();
     }
+    if constexpr (NP > 1) {
+      const int g1 = g0 + 2 * KT;
+      if (g1 < KA && g1 % K == 0) {
+        epi(g1 / K - 1, ct);
+#pragma unroll
+        for (int i = 0; i < TR; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j) ct[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      }
+    }
   }
+}
+template <int TM, int TN, bool A_KC, bool B_NC, typename FA, typename FB>
+__device__ __forceinline__ void gemm_staged2(f32x4 (&ct)[TM / 4][TN], int K, float* stage, FA a,
+                                             FB b) {
+  gemm_staged2_seq<1, TM, TN, A_KC, B_NC>(
+      ct, K, stage, [&](int, int m, int k) { return a(m, k); },
+      [&](int, int k, int n) { return b(k, n); }, [](int, f32x4(&)[TM / 4][TN]) {});
 }
 
 // gemm_staged2 with operands read 4 at a time: a4(m, k) returns a(m, k .. k+3)
@@ -1115,22 +1139,21 @@ __global__ void __launch_bounds__(NT, 3) bwd_grad_kernel(
     }
   }
   __syncthreads();
-  {  // dM = dDelta Y^T
+  {  // dM = dDelta Y^T, then dP = scale dO Delta^T on s <= r, in one pipeline
     f32x4 a4[1][4];
     zero(a4);
-    gemm_staged2<4, 4, true, false>(a4, D, sa,
-                                   [&](int r, int j) { return ld4(sc + Scr::DD + r * D + j); },
-                                   [&](int j, int s) { return sB[s] * ld4(sc + Scr::X + s * D + j); });
+    gemm_staged2_seq<2, 4, 4, true, false>(
+        a4, D, sa,
+        [&](int p2, int r, int j) { return p2 == 0 ? ld4(sc + Scr::DD + r * D + j) : dO4(r, j); },
+        [&](int p2, int j, int s) {
+          return p2 == 0 ? sB[s] * ld4(sc + Scr::X + s * D + j) : ld4(sc + Scr::DL + s * D + j);
+        },
+        [&](int, f32x4(&c)[1][4]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+          for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) sT[orow<4>(i)][ocol(j)] = a4[0][j][i];
-  }
-  {  // dP = scale dO Delta^T on s <= r
-    f32x4 a4[1][4];
-    zero(a4);
-    gemm_staged2<4, 4, true, false>(a4, D, sa, dO4,
-                                   [&](int j, int s) { return ld4(sc + Scr::DL + s * D + j); });
+            for (int j = 0; j < 4; ++j) sT[orow<4>(i)][ocol(j)] = c[0][j][i];
+        });
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -1166,27 +1189,21 @@ __global__ void __launch_bounds__(NT, 3) bwd_grad_kernel(
         sT[r][s] = (s < r && r < Lc) ? -a4[0][j][i] : 0.0f;
       }
   }
-  {  // dK_E = -dX S^T
+  {  // dK_E = -dX S^T, dQ_E = scale dO S^T, dK_D = Delta dS_next^T in one pipeline
     f32x4 acc[1][8];
     zero(acc);
-    gemm_staged2<4, 8, true, false>(acc, D, sa,
-                                   [&](int r, int j) { return ld4(sc + Scr::DX + r * D + j); },
-                                   [&](int j, int cc) { return ld4(S + cc * D + j); });
-    put8(acc, Scr::DKE, -1.0f);
-  }
-  {  // dQ_E = scale dO S^T
-    f32x4 acc[1][8];
-    zero(acc);
-    gemm_staged2<4, 8, true, false>(acc, D, sa, dO4,
-                                   [&](int j, int cc) { return ld4(S + cc * D + j); });
-    put8(acc, Scr::DQE, scale);
-  }
-  {  // dK_D = Delta dS_next^T
-    f32x4 acc[1][8];
-    zero(acc);
-    gemm_staged2<4, 8, true, false>(acc, D, sa,
-                                   [&](int r, int j) { return ld4(sc + Scr::DL + r * D + j); },
-                                   [&](int j, int cc) { return ld4(dS + cc * D + j); });
+    gemm_staged2_seq<3, 4, 8, true, false>(
+        acc, D, sa,
+        [&](int p2, int r, int j) {
+          return p2 == 1 ? dO4(r, j) : ld4(sc + (p2 == 0 ? Scr::DX : Scr::DL) + r * D + j);
+        },
+        [&](int p2, int j, int cc) { return ld4((p2 == 2 ? dS : S) + cc * D + j); },
+        [&](int p2, f32x4(&c)[1][8]) {
+          if (p2 == 0)
+            put8(c, Scr::DKE, -1.0f);
+          else
+            put8(c, Scr::DQE, scale);
+        });
     put8(acc, Scr::DKD, 1.0f);
   }
   {  // dbeta += sum_s dA[r, s] At[r, s]: row r on lanes 4r .. 4r + 3; each lane
