@@ -670,10 +670,10 @@ __global__ void __launch_bounds__(NT, 3) bwd_prep_kernel(const void* __restrict_
   {  // U = M diag(b) V
     f32x4 acc[1][8];
     zero(acc);
-    gemm_staged2v<4, 8, true, true>(
+    gemm_staged2<4, 8, true, true>(
         acc, C, sa,
         [&](int r, int s2) { return f32x4{sM[r][s2], sM[r][s2 + 1], sM[r][s2 + 2], sM[r][s2 + 3]}; },
-        [&](int s2, int j) { return sB[s2] * row4_at<QB>(rv, HDi, s2, j); });
+        [&](int s2, int j) { return sB[s2] * row_at<QB>(rv, HDi, s2, j); });
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -689,10 +689,10 @@ __global__ void __launch_bounds__(NT, 3) bwd_prep_kernel(const void* __restrict_
         const int r = orow<4>(i), cc = ocol(j);
         acc[0][j][i] = -row_at<QB>(rq, HDi, r, cc) * __expf(Gf(r, cc));
       }
-    gemm_staged2v<4, 8, true, true>(
+    gemm_staged2<4, 8, true, true>(
         acc, C, sa,
         [&](int r, int s2) { return *reinterpret_cast<const f32x4*>(im + Rec::P + r * C + s2); },
-        [&](int s2, int cc) { return *reinterpret_cast<const f32x4*>(im + Rec::W + s2 * D + cc); });
+        [&](int s2, int cc) { return im[Rec::W + s2 * D + cc]; });
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
