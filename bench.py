@@ -422,9 +422,10 @@ def bench_backward(args, torch, kda, synth):
                           "unit": "TFLOP/s", "frac": tf / MFMA_F32_PEAK_TFLOPS,
                           "alg_flops_per_call": BWD_FLOPS,
                           "alg_mac_per_chunk_head": BWD_MAC_PER_CHUNK_HEAD,
-                          "precision": "fp32 products on fp32 16x16x4 MFMA; with bf16 d_o the "
-                                       "walk's Qt^T dO on bf16 16x16x32 MFMA with Qt as three "
-                                       "bf16 terms (fp32-exact), priced at the fp32 peak"})
+                          "precision": "fp32 products on fp32 16x16x4 MFMA, except the walk's "
+                                       "state update: bf16 16x16x32 MFMA on three-term bf16 "
+                                       "splits (fp32-exact; with bf16 d_o, Qt^T dO takes d_o "
+                                       "as is), priced at the fp32 peak"})
 
 
 def cpu_baseline(args, synth):
