@@ -157,6 +157,39 @@ def test_backward_below_decay_floor():
     assert torch.all(got[3].cpu()[floored] == 0)
 
 
+@pytest.mark.parametrize("seed", [101, 102, 103, 104, 105, 106])
+def test_backward_random_shapes(seed):
+    """Random varlen batches (empty, one-token and chunk-boundary lengths among
+    them), head counts, q/k/v and d_o dtypes, state terms and scales against
+    the oracle."""
+    need_gpu()
+    rng = np.random.default_rng(seed)
+    nseq = int(rng.integers(1, 6))
+    pool = [0, 1, 63, 64, 65, 127, 128, 129]
+    lengths = [int(rng.choice(pool)) if rng.random() < 0.4 else int(rng.integers(2, 260))
+               for _ in range(nseq)]
+    if sum(lengths) == 0:
+        lengths[0] = 97
+    H = int(rng.choice([1, 3, 5]))
+    qdt = torch.bfloat16 if rng.random() < 0.5 else torch.float32
+    dodt = torch.bfloat16 if rng.random() < 0.5 else torch.float32
+    init = bool(rng.random() < 0.5)
+    scale = float(rng.uniform(0.3, 1.5))
+    with_do = bool(rng.random() < 0.8)
+    with_dsf = (not with_do) or bool(rng.random() < 0.5)
+    say("backward random", seed, lengths, H, qdt, dodt, init, with_do, with_dsf, "%.3f" % scale)
+    dr = draw_prefill(lengths, H=H, dtype=qdt, init_state=init, seed=seed)
+    g, beta = oracle_gate_f32(dr)
+    r = torch.Generator().manual_seed(seed + 1000)
+    d_o = torch.randn(dr.q.shape[0], H, 128, generator=r).to(dodt) if with_do else None
+    dSf = torch.randn(nseq, H, 128, 128, generator=r) * 0.1 if with_dsf else None
+    got = _run(dr, g, beta, d_o, dSf, scale)
+    ref = oracle.prefill_backward(dr.q, dr.k, dr.v, g, beta, dr.cu_seqlens, dr.initial_state,
+                                  scale=scale, d_o=None if d_o is None else d_o.float(),
+                                  dS_final=dSf)
+    check(got, ref, "random %d" % seed)
+
+
 def test_backward_config2_varlen_sampled_heads():
     """8 sequences, 32,768 tokens, initial states (the varlen prefill
     workload): the whole backward on the GPU, sampled heads against the
