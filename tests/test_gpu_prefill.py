@@ -74,6 +74,26 @@ def test_edge_shapes(lengths, H):
     _check_small(lengths, H, torch.bfloat16, True, seed=100 + sum(lengths) + H, scale=0.7)
 
 
+@pytest.mark.parametrize("seed", [201, 202, 203, 204, 205, 206])
+def test_random_shapes(seed):
+    """Random varlen batches (empty, one-token and chunk-boundary lengths among
+    them), head counts, q/k/v dtypes, initial states and scales: fp32 o within
+    the stated bound, bf16 o the rounding of it, the state within its bound."""
+    need_gpu()
+    rng = np.random.default_rng(seed)
+    nseq = int(rng.integers(1, 7))
+    pool = [0, 1, 16, 17, 63, 64, 65, 127, 128, 129]
+    lengths = [int(rng.choice(pool)) if rng.random() < 0.4 else int(rng.integers(2, 400))
+               for _ in range(nseq)]
+    if sum(lengths) == 0:
+        lengths[0] = 97
+    H = int(rng.choice([1, 2, 3, 5, 8]))
+    qdt = torch.bfloat16 if rng.random() < 0.6 else torch.float32
+    init = bool(rng.random() < 0.5)
+    scale = float(rng.uniform(0.3, 1.5))
+    _check_small(lengths, H, qdt, init, seed, scale)
+
+
 def test_edge_many_sequences():
     """70 packed sequences of 0..39 tokens: more than the 64 that the state
     kernel orders longest first, so workgroups map to sequences in order."""
