@@ -216,6 +216,91 @@ __device__ __forceinline__ void gemm_staged2(f32x4 (&ct)[TM / 4][TN], int K, flo
       [&](int, int k, int n) { return b(k, n); }, [](int, f32x4(&)[TM / 4][TN]) {});
 }
 
+// Two products of one shape over one contraction, c_p += a(p) b(p) for p < 2,
+// through one slab pipeline (the gemm_staged2 scheme with both products'
+// slabs filled and read each step): each slab step does twice the MFMA work
+// per barrier.  a(p, m, k) returns the quad k .. k + 3 of row m (A_KC), b(p,
+// k, n) one element (B_NC).  hook(k0, sb0, sb1) runs once per slab, while
+// the B slabs of contraction indices k0 .. k0 + KT - 1 are in LDS: element
+// (k0 + kk, n) of operand p at sb_p[n SKP + kk].  Stage: 2 (M + N) SKP floats.
+template <int TM, int TN, typename FA, typename FB, typename FH>
+__device__ __forceinline__ void gemm_staged2_pair(f32x4 (&c0)[TM / 4][TN], f32x4 (&c1)[TM / 4][TN],
+                                                  int K, float* stage, FA a, FB b, FH hook) {
+  constexpr int M = 16 * TM, N = 16 * TN;
+  float* sa0 = stage;
+  float* sa1 = sa0 + M * SKP;
+  float* sb0 = sa1 + M * SKP;
+  float* sb1 = sb0 + N * SKP;
+  constexpr int QA = M * KT / 4 / NT, QB = N * KT / 4 / NT;
+  static_assert(TM % 4 == 0 && QA >= 1 && QB >= 1 && (M * KT) % (4 * NT) == 0 &&
+                    (N * KT) % (4 * NT) == 0,
+                "whole 16-row tiles per wave, whole quads per thread");
+  const int t = threadIdx.x;
+  // one slab in flight: a slab step is both products' MFMA work, as long as
+  // two steps of a single product
+  f32x4 ra[2][QA], rb[2][QB];
+  auto fetch = [&](int k0) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+#pragma unroll
+      for (int u = 0; u < QA; ++u) {
+        const int e = t + NT * u;
+        ra[p][u] = a(p, e / (KT / 4), k0 + 4 * (e % (KT / 4)));
+      }
+#pragma unroll
+      for (int u = 0; u < QB; ++u) {
+        const int e = t + NT * u, n = e % N, q = e / N;
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) rb[p][u][s2] = b(p, k0 + 4 * q + s2, n);
+      }
+    }
+  };
+  constexpr int TR = TM / 4;
+  fetch(0);
+  for (int k0 = 0; k0 < K; k0 += KT) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+#pragma unroll
+      for (int u = 0; u < QA; ++u) {
+        const int e = t + NT * u;
+        *reinterpret_cast<f32x4*>((p ? sa1 : sa0) + (e / (KT / 4)) * SKP + 4 * (e % (KT / 4))) =
+            ra[p][u];
+      }
+#pragma unroll
+      for (int u = 0; u < QB; ++u) {
+        const int e = t + NT * u;
+        *reinterpret_cast<f32x4*>((p ? sb1 : sb0) + (e % N) * SKP + 4 * (e / N)) = rb[p][u];
+      }
+    }
+    barrier_lds();
+    if (k0 + KT < K) fetch(k0 + KT);
+    const int lane = t & 63, w = t >> 6, lr = lane & 15, lq = lane >> 4;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const float* xa = p ? sa1 : sa0;
+      const float* xb = p ? sb1 : sb0;
+      f32x4 av[TR], bv[TN];
+#pragma unroll
+      for (int i = 0; i < TR; ++i)
+        av[i] = *reinterpret_cast<const f32x4*>(xa + (16 * (TR * w + i) + lr) * SKP + 4 * lq);
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        bv[j] = *reinterpret_cast<const f32x4*>(xb + (16 * j + lr) * SKP + 4 * lq);
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2)
+#pragma unroll
+        for (int i = 0; i < TR; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j) {
+            f32x4& c = p ? c1[i][j] : c0[i][j];
+            c = __builtin_amdgcn_mfma_f32_16x16x4f32(av[i][s2], bv[j][s2], c, 0, 0, 0);
+          }
+    }
+    hook(k0, static_cast<const float*>(sb0), static_cast<const float*>(sb1));
+    barrier_lds();
+  }
+}
+
 // gemm_staged2 with operands read 4 at a time: a4(m, k) returns a(m, k .. k+3)
 // when A_KC (contiguous along k), else a(m .. m+3, k); b4(k, n) returns
 // b(k, n .. n+3) when B_NC, else b(k .. k+3, n).  Index arguments are
@@ -1033,14 +1118,21 @@ __global__ void __launch_bounds__(NT, 3) bwd_grad_kernel(
     const float* __restrict__ dSrec, float* __restrict__ scr, float* __restrict__ dq,
     float* __restrict__ dk, float* __restrict__ dv, float* __restrict__ dg,
     float* __restrict__ dbeta, int64_t item0) {
-  __shared__ float sT[C][C + 1], sDP[C][C + 1];
-  __shared__ float sB[C], sDB[C], sGC[D];
-  __shared__ uint32_t sFl[C][D / 32];  // bit c % 32 of word c / 32: g of (row, c) floored
-  // the products' LDS slabs, then (pairwise phase) K, Q and gamma of a
-  // 16-channel slab and the per-wave partial sums
+  // sT, sDP: [C][C + 1] each, written from dM on; before that the first
+  // products' slabs (gemm_staged2_pair) and their per-wave row sums sit there.
+  // sU: the other products' LDS slabs, then (pairwise phase) K, Q and gamma of
+  // a 16-channel slab and the per-wave partial sums.
   constexpr int SC = 16, SS = SC + 1;
-  constexpr int PAIR_FLOATS = 3 * C * SS + 4 * SC;
-  __shared__ float sU[PAIR_FLOATS > STAGE_FLOATS ? PAIR_FLOATS : STAGE_FLOATS];
+  constexpr int PAIR_FLOATS = 3 * C * SS + 8 * SC;
+  constexpr int TP = C * (C + 1);
+  constexpr int STAGE_PAIR = 2 * (C + D) * SKP;
+  static_assert(STAGE_PAIR + 4 * D <= 2 * TP, "paired slabs and row sums fit in sT, sDP");
+  __shared__ float sPool[2 * TP + (PAIR_FLOATS > STAGE_FLOATS ? PAIR_FLOATS : STAGE_FLOATS)];
+  __shared__ float sB[C], sDB[C], sGC[D];
+  float(*sT)[C + 1] = reinterpret_cast<float(*)[C + 1]>(sPool);
+  float(*sDP)[C + 1] = reinterpret_cast<float(*)[C + 1]>(sPool + TP);
+  float* sU = sPool + 2 * TP;
+  float* sRed = sPool + STAGE_PAIR;  // [4][D]
   float* sa = sU;
   ChunkPos p;
   if (!chunk_of_block(cu, N, T_tot, H, maxnch, p, item0 + blockIdx.x)) return;
@@ -1073,20 +1165,38 @@ __global__ void __launch_bounds__(NT, 3) bwd_grad_kernel(
     sB[t] = t < Lc ? beta[(p.t0 + t) * H + p.h] : 0.0f;
     sDB[t] = 0.0f;
   }
-  (&sFl[0][0])[t] = 0u;
-  static_assert(C * (D / 32) == NT, "one flag word per thread");
   __syncthreads();
-  {  // X = V - K_E S
+  f32x4 accD[1][8];  // dDelta
+  {  // X = V - K_E S and K_D dS_next in one pipeline.  While a slab of rows
+     // of S and dS_next is in LDS, thread t sums row t % 16 of S . dS_next over
+     // the columns 4 lq + w + 16 i (i < 8; the 16-lane groups of a wave read
+     // distinct banks); summed over the wave's lane groups, then over the waves
+     // below, this is d e^gamma_C[c] = sum_j dS_next[c, j] S[c, j].
     f32x4 acc[1][8];
     zero(acc);
-    gemm_staged2<4, 8, true, true>(acc, D, sa,
-                                  [&](int r, int cc) {
-                                    const f32x4 kv = row4_at<QB>(rk, HDi, r, cc);
-                                    const f32x4 gv = ld4(im + Rec::G + r * D + cc);
-                                    return f32x4{kv[0] * __expf(gv[0]), kv[1] * __expf(gv[1]),
-                                                 kv[2] * __expf(gv[2]), kv[3] * __expf(gv[3])};
-                                  },
-                                  [&](int cc, int j) { return S[cc * D + j]; });
+    zero(accD);
+    const int w = t >> 6, lq = (t & 63) >> 4, kk = t & 15;
+    gemm_staged2_pair<4, 8>(
+        acc, accD, D, sPool,
+        [&](int p2, int r, int cc) {
+          if (p2 == 1) return ld4(im + Rec::KD + r * D + cc);
+          const f32x4 kv = row4_at<QB>(rk, HDi, r, cc);
+          const f32x4 gv = ld4(im + Rec::G + r * D + cc);
+          return f32x4{kv[0] * __expf(gv[0]), kv[1] * __expf(gv[1]), kv[2] * __expf(gv[2]),
+                       kv[3] * __expf(gv[3])};
+        },
+        [&](int p2, int cc, int j) { return (p2 == 0 ? S : dS)[cc * D + j]; },
+        [&](int k0, const float* b0, const float* b1) {
+          float part = 0.0f;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int o = (4 * lq + w + 16 * i) * SKP + kk;
+            part = fmaf(b0[o], b1[o], part);
+          }
+          part += __shfl_xor(part, 16);
+          part += __shfl_xor(part, 32);
+          if (lq == 0) sRed[w * D + k0 + kk] = part;
+        });
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -1095,7 +1205,14 @@ __global__ void __launch_bounds__(NT, 3) bwd_grad_kernel(
         sc[Scr::X + r * D + col] = Vf(r, col) - acc[0][j][i];
       }
   }
+  // dDelta += scale P^T dO
+  gemm_staged2<4, 8, false, true>(accD, C, sa,
+                                 [&](int r, int s) { return scale * im[Rec::P + s * C + r]; },
+                                 [&](int s, int j) { return dOf(s, j); });
+  put8(accD, Scr::DD, 1.0f);
   __syncthreads();
+  if (t < D)  // the gradient of gamma_C through e^gamma_C (the pairwise phase adds the rest)
+    sGC[t] = (sRed[t] + sRed[D + t] + sRed[2 * D + t] + sRed[3 * D + t]) * __expf(Gf(C - 1, t));
   {  // Delta = M diag(b) X
     f32x4 acc[1][8];
     zero(acc);
@@ -1103,18 +1220,6 @@ __global__ void __launch_bounds__(NT, 3) bwd_grad_kernel(
                                   [&](int s, int j) { return sB[s] * sc[Scr::X + s * D + j]; });
     put8(acc, Scr::DL, 1.0f);
   }
-  {  // dDelta = K_D dS_next + scale P^T dO
-    f32x4 acc[1][8];
-    zero(acc);
-    gemm_staged2<4, 8, true, true>(acc, D, sa,
-                                  [&](int r, int cc) { return ld4(im + Rec::KD + r * D + cc); },
-                                  [&](int cc, int j) { return dS[cc * D + j]; });
-    gemm_staged2<4, 8, false, true>(acc, C, sa,
-                                   [&](int r, int s) { return scale * im[Rec::P + s * C + r]; },
-                                   [&](int s, int j) { return dOf(s, j); });
-    put8(acc, Scr::DD, 1.0f);
-  }
-  __syncthreads();
   {  // dY = M^T dDelta, dX = diag(b) dY (= dv), dbeta += rowsum(dY . X)
     f32x4 acc[1][8];
     zero(acc);
@@ -1208,7 +1313,7 @@ __global__ void __launch_bounds__(NT, 3) bwd_grad_kernel(
   }
   {  // dbeta += sum_s dA[r, s] At[r, s]: row r on lanes 4r .. 4r + 3; each lane
      // then scales the dA entries it read by beta_r, the factor the pairwise
-     // terms below take them with (the barriers of the next block order it)
+     // terms below take them with (the barrier after it orders it)
     const int r = t >> 2, qd = t & 3;
     const float br = sB[r];
     float a = 0.0f;
@@ -1223,30 +1328,7 @@ __global__ void __launch_bounds__(NT, 3) bwd_grad_kernel(
     a += __shfl_xor(a, 2);
     if (qd == 0) sDB[r] += a;
   }
-  {  // d e^gamma_C[c] = sum_j dS_next[c, j] S[c, j]: each group of 32 lanes
-     // reads rows c = t / 32 + 8 p (p < 16) 16 bytes a lane, so that a load
-     // covers whole rows, and sums each row over its lanes
-    const int j4 = 4 * (t & 31), r0 = t >> 5;
-    float part[16];
-#pragma unroll
-    for (int p2 = 0; p2 < 16; ++p2) {
-      const int c = r0 + 8 * p2;
-      const f32x4 a = *reinterpret_cast<const f32x4*>(dS + c * D + j4);
-      const f32x4 b = *reinterpret_cast<const f32x4*>(S + c * D + j4);
-      part[p2] = fmaf(a[0], b[0], fmaf(a[1], b[1], fmaf(a[2], b[2], a[3] * b[3])));
-    }
-#pragma unroll
-    for (int p2 = 0; p2 < 16; ++p2)
-#pragma unroll
-      for (int off = 1; off < 32; off <<= 1) part[p2] += __shfl_xor(part[p2], off);
-    if ((t & 31) == 0) {
-#pragma unroll
-      for (int p2 = 0; p2 < 16; ++p2) sU[r0 + 8 * p2] = part[p2];
-    }
-    __syncthreads();
-    if (t < D) sGC[t] = sU[t] * __expf(Gf(C - 1, t));
-    __syncthreads();
-  }
+  __syncthreads();  // dK_E, dQ_E, dK_D (scratch) and the scaled dA complete
   // The terms of the decay factors and the pairwise terms of At and P, 16
   // channels at a time.  For a row x and channel c (w(a, b) = e^(gamma_a -
   // gamma_b) <= 1 for a >= b):
@@ -1265,6 +1347,7 @@ __global__ void __launch_bounds__(NT, 3) bwd_grad_kernel(
   float* sQ = sK + C * SS;         // q
   float* sG = sQ + C * SS;         // gamma
   float* sPart = sG + C * SS;      // [4][SC] partial sums of the gamma_C term
+  float* sBlk = sPart + 4 * SC;    // [4][SC] dgamma summed over each wave's rows
   const int lane = t & 63, w = t >> 6, ln = lane & 15, lq = lane >> 4;
   // Thread t reads row t / 4, channels 4 (t % 4) .. + 3 of the slab's k, q
   // and gamma into LDS (4-wide loads, one slab ahead so that the reads stay
@@ -1304,6 +1387,7 @@ __global__ void __launch_bounds__(NT, 3) bwd_grad_kernel(
       sG[xr * SS + n4 + i] = pg[i];
     }
     const f32x4 dke = eke, dqe = eqe, dkd = ekd, gv = egv;  // this slab's
+    float dgs[4];  // dgamma of the lane's rows (0 past the chunk end)
     barrier_lds();
     if (c0 + SC < D) fetch_slab(c0 + SC);
     {  // pairs across blocks on fp32 MFMA: wave w owns the rows of block w.
@@ -1378,6 +1462,7 @@ __global__ void __launch_bounds__(NT, 3) bwd_grad_kernel(
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int xl = 4 * lq + v, x = 16 * w + xl;
+        dgs[v] = 0.0f;
         const float gx = sG[x * SS + ln];
         const float gax = sG[(16 * w + (xl < 8 ? 3 : 11)) * SS + ln];
         const float ex = __expf(gx - gax), fx = __expf(gax - gx);
@@ -1403,10 +1488,8 @@ __global__ void __launch_bounds__(NT, 3) bwd_grad_kernel(
           const int cc = c0 + ln;
           dk[tok(x, cc)] = dke[v] * E + dkd[v] * F + l1 + rr;
           dq[tok(x, cc)] = dqe[v] * E + l2;
-          sc[Scr::DX + x * D + cc] =  // dgamma, summed below
-              (dke[v] * kx + dqe[v] * qx) * E - dkd[v] * kx * F + kx * l1 + qx * l2 - kx * rr;
+          dgs[v] = (dke[v] * kx + dqe[v] * qx) * E - dkd[v] * kx * F + kx * l1 + qx * l2 - kx * rr;
           dcs += dkd[v] * kx * F;
-          if (decay_floored(gv[v])) atomicOr(&sFl[x][cc >> 5], 1u << (cc & 31));
         }
       }
       // the gamma_C terms of channel c0 + ln summed over the wave's 16 rows
@@ -1414,20 +1497,26 @@ __global__ void __launch_bounds__(NT, 3) bwd_grad_kernel(
       dcs += __shfl_xor(dcs, 32);
       if (lq == 0) sPart[w * SC + ln] = dcs;
     }
-    barrier_lds();  // sPart complete; the slab's arrays are refilled next
-    if (t < SC) sGC[c0 + t] += sPart[t] + sPart[SC + t] + sPart[2 * SC + t] + sPart[3 * SC + t];
-  }
-  __syncthreads();  // dgamma (scratch) complete
-  if (t < D) {  // dg: reverse cumulative sum of dgamma, plus the gamma_C terms
-    const int cc = t;
-    float dgam[C];
+    // dg = the reverse cumulative sum of dgamma down the rows plus the gamma_C
+    // terms.  The lane's rows 16 w + 4 lq + v, summed from the last: within
+    // the lane, then the later lane groups of the wave, then (after the
+    // barrier) the later waves and the gamma_C terms of the channel.
 #pragma unroll
-    for (int x = 0; x < C; ++x) dgam[x] = x < Lc ? sc[Scr::DX + x * D + cc] : 0.0f;
-    float run = sGC[cc];
+    for (int v = 2; v >= 0; --v) dgs[v] += dgs[v + 1];
+    const float o1 = __shfl(dgs[0], (lane + 16) & 63), o2 = __shfl(dgs[0], (lane + 32) & 63),
+                o3 = __shfl(dgs[0], (lane + 48) & 63);
+    const float later = (lq < 3 ? o1 : 0.0f) + (lq < 2 ? o2 : 0.0f) + (lq < 1 ? o3 : 0.0f);
+    if (lq == 0) sBlk[w * SC + ln] = dgs[0] + o1 + o2 + o3;
+    barrier_lds();  // sPart, sBlk complete; the slab's arrays are refilled next
+    {
+      float run = sGC[c0 + ln] + sPart[ln] + sPart[SC + ln] + sPart[2 * SC + ln] +
+                  sPart[3 * SC + ln] + later;
+      for (int w2 = w + 1; w2 < 4; ++w2) run += sBlk[w2 * SC + ln];
 #pragma unroll
-    for (int x = C - 1; x >= 0; --x) {
-      run += dgam[x];
-      if (x < Lc) dg[tok(x, cc)] = (sFl[x][cc >> 5] >> (cc & 31)) & 1u ? 0.0f : run;
+      for (int v = 0; v < 4; ++v) {
+        const int x = 16 * w + 4 * lq + v;
+        if (x < Lc) dg[tok(x, c0 + ln)] = decay_floored(gv[v]) ? 0.0f : run + dgs[v];
+      }
     }
   }
   if (t < Lc) dbeta[(p.t0 + t) * H + p.h] = sDB[t];
