@@ -423,9 +423,10 @@ def bench_backward(args, torch, kda, synth):
                           "alg_flops_per_call": BWD_FLOPS,
                           "alg_mac_per_chunk_head": BWD_MAC_PER_CHUNK_HEAD,
                           "precision": "fp32 products on fp32 16x16x4 MFMA, except the walk's "
-                                       "state update: bf16 16x16x32 MFMA on three-term bf16 "
-                                       "splits (fp32-exact; with bf16 d_o, Qt^T dO takes d_o "
-                                       "as is), priced at the fp32 peak"})
+                                       "(its state update, and Z = A1 R with bf16 d_o): bf16 "
+                                       "16x16x32 MFMA on three-term bf16 splits (fp32-exact; "
+                                       "with bf16 d_o, Qt^T dO takes d_o as is), priced at "
+                                       "the fp32 peak"})
 
 
 def cpu_baseline(args, synth):

@@ -16,8 +16,8 @@
 // Both walks have one shape: Z = A1 R; R <- e^gamma_C R - A2^T Z + A3^T B.
 //
 // Three kernels, all to fp32 accuracy: the products on fp32 MFMA, except the
-// walk's state update, whose products run on bf16 MFMA as three-term splits
-// that carry fp32's 24 bits (walk_dir):
+// walk's (its state update, and Z = A1 R with bf16 d_o), which run on bf16
+// MFMA as three-term splits that carry fp32's 24 bits (walk_dir):
 //   bwd_prep  one workgroup per (chunk, head): gamma, At, P, M, W, U, Qt, K_D
 //             and e^gamma_C into a per-(chunk, head) record;
 //   bwd_walk  one workgroup per (sequence, head, 64-column tile) and
@@ -796,23 +796,38 @@ __global__ void __launch_bounds__(NT, 3) bwd_prep_kernel(const void* __restrict_
 // wave), then R <- e^gamma_C R + K_D^T (U - Z) forward, or e^gamma_C R -
 // W^T Z + Qt^T dO backward (dO the tile's columns of d_o).  The MFMA A
 // operands come straight from the chunk record into registers, one product
-// ahead of their use: rows of A1 16 bytes a lane (lane group lq, sub-step s
-// of group u takes contraction index 16 u + 4 lq + s, and the B operand is
-// read in that order), the transposed operands one float a lane (16 lanes on
-// 64 contiguous bytes).  The B operands sit transposed in LDS, so the
-// contraction indices a lane needs are one 16-byte read.  Two barriers per
-// chunk step.
-// Z = A1 R runs on the fp32 16x16x4 MFMA.  The update's products run on the
-// bf16 16x16x32 MFMA with three-term splits: x = hi + mid + lo in bf16
-// carries the 24 bits of an fp32 x, a product of two such sums is the six
-// bf16 products whose terms reach 2^-16 of the leading one (the three left
-// out are below 2^-24 of it), and bf16 products are exact in the fp32
-// accumulator, so the result is the fp32 product up to fp32 rounding at a
-// third of the fp32 MFMA cycles.  With bf16 d_o, Qt^T dO takes dO as is
-// (three products); with fp32 d_o it stays on the fp32 MFMA.
+// ahead of their use: rows of A1 16 or 32 bytes a lane (the contraction
+// index of lane group lq and sub-step s is 16 u + 4 lq + s on the fp32 MFMA,
+// 32 g + 8 lq + s on the bf16 one, and the B operand is read in that order),
+// the transposed operands one float a lane (16 lanes on 64 contiguous
+// bytes).  The B operands sit transposed in LDS, so the contraction indices
+// a lane needs are one 16-byte read.  Two barriers per chunk step.
+// The products run on the bf16 16x16x32 MFMA with three-term splits: x = hi
+// + mid + lo in bf16 carries the 24 bits of an fp32 x, a product of two
+// such sums is the six bf16 products whose terms reach 2^-16 of the leading
+// one (the three left out are below 2^-24 of it), and bf16 products are
+// exact in the fp32 accumulator, so the result is the fp32 product up to
+// fp32 rounding at three eighths of the fp32 MFMA cycles.  The state update
+// always does so; Z = A1 R does so with bf16 d_o (R as three bf16 planes in
+// LDS), and with fp32 d_o, whose tile takes the LDS those planes would
+// need, stays on the fp32 16x16x4 MFMA.  With bf16 d_o, Qt^T dO takes dO as
+// is (three products); with fp32 d_o it stays on the fp32 MFMA.
 constexpr int WTS = 2 * C + 4;  // row stride of the transposed fp32 tile: 4 WTS = 16 (mod 64 banks)
 constexpr int DTS = C + 8;      // the bf16 tiles': 16-lane reads of 16 bytes land on distinct banks
 constexpr int FTS = C + 4;      // the fp32 d_o tile's
+// With bf16 d_o the walk also runs Z = A1 R on split-bf16 products, with R
+// as three bf16 planes; its three bf16 tiles then fit two workgroups per CU
+// (80 KB) only unpadded, with the 16-byte groups of a row XOR-swizzled so
+// that the 16 lanes of a read (rows 16 j + l, one group each) still hit
+// distinct banks.  Offsets in bf16 elements:
+//   R planes [3][64][128]: group g of row r at g ^ (r % 16);
+//   Z planes [3][64][64] and d_o [64][64]: group g of row r at g ^ (r / 2 % 8).
+__device__ __forceinline__ int rp_off(int p, int r, int k) {
+  return (p * 64 + r) * 128 + ((((k >> 3) ^ (r & 15))) << 3) + (k & 7);
+}
+__device__ __forceinline__ int zp_off(int p, int r, int k) {
+  return (p * 64 + r) * 64 + ((((k >> 3) ^ ((r >> 1) & 7))) << 3) + (k & 7);
+}
 __device__ __forceinline__ void split3(const chunk::f32x8& x, bf16x8& hi, bf16x8& mi, bf16x8& lo) {
   hi = __builtin_convertvector(x, bf16x8);
   const chunk::f32x8 r = x - __builtin_convertvector(hi, chunk::f32x8);
@@ -833,8 +848,14 @@ __device__ __forceinline__ void walk_dir(const float* __restrict__ img, const vo
                                          int64_t bos, int64_t L, int n, int h, int tile, int H,
                                          const float* __restrict__ R_init,
                                          float* __restrict__ rec, float* __restrict__ R_end,
-                                         float (*sRt)[WTS], uint16_t (*sZp)[64][DTS],
-                                         void* sDo) {
+                                         void* sR, void* sZ, void* sDo) {
+  // ZB: Z = A1 R on split-bf16 products (bf16 d_o), else on the fp32 MFMA
+  constexpr bool ZB = DOB;
+  float(*sRt)[WTS] = reinterpret_cast<float(*)[WTS]>(sR);  // fp32 R^T (not ZB)
+  uint16_t* sRp = reinterpret_cast<uint16_t*>(sR);          // R planes (ZB)
+  uint16_t* sZp = reinterpret_cast<uint16_t*>(sZ);
+  // element (p, r, k) of the Z planes; d_o (bf16) is plane 0 of its own tile
+  auto zo = [](int p, int r, int k) { return ZB ? zp_off(p, r, k) : (p * 64 + r) * DTS + k; };
   const int nch = static_cast<int>((L + C - 1) / C);
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, lr = lane & 15, lq = lane >> 4;
   const int64_t HD = (int64_t)H * D;
@@ -862,13 +883,16 @@ __device__ __forceinline__ void walk_dir(const float* __restrict__ img, const vo
     return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, vo, so, 0));
   };
   constexpr int A1 = FWD ? Rec::W : Rec::KD;
-  f32x4 zA[8];  // A1 rows 16 w + lr, contraction 16 u + 4 lq .. + 3
-  const int vo_zA = ((16 * w + lr) * D + 4 * lq) * 4;
+  // A1 rows 16 w + lr; fp32 MFMA: zA[u] the contraction 16 u + 4 lq .. + 3;
+  // ZB: zA[2 g + e] the contraction 32 g + 8 lq + 4 e .. + 3
+  f32x4 zA[8];
+  const int vo_zA = ((16 * w + lr) * D + (ZB ? 8 : 4) * lq) * 4;
   auto load_zA = [&](__amdgpu_buffer_rsrc_t rs) {
 #pragma unroll
     for (int u = 0; u < 8; ++u)
       zA[u] = __builtin_bit_cast(
-          f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, vo_zA, (A1 + 16 * u) * 4, 0));
+          f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                     rs, vo_zA, (A1 + (ZB ? 32 * (u >> 1) + 4 * (u & 1) : 16 * u)) * 4, 0));
   };
   if (nch > 0) load_zA(rec_buf(pair_of(0)));
   // the transposed update operand: K_D forward, W backward, as bf16 A
@@ -887,7 +911,15 @@ __device__ __forceinline__ void walk_dir(const float* __restrict__ img, const vo
       for (int j = 0; j < 4; ++j) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) rc[rrow(i, v) * D + 16 * j + lr] = R[i][j][v];
-        *reinterpret_cast<f32x4*>(&sRt[16 * j + lr][rrow(i, 0)]) = R[i][j];
+        if constexpr (ZB) {
+          bf16x4 ph, pm, pl;
+          split3(R[i][j], ph, pm, pl);
+          *reinterpret_cast<bf16x4*>(sRp + rp_off(0, 16 * j + lr, rrow(i, 0))) = ph;
+          *reinterpret_cast<bf16x4*>(sRp + rp_off(1, 16 * j + lr, rrow(i, 0))) = pm;
+          *reinterpret_cast<bf16x4*>(sRp + rp_off(2, 16 * j + lr, rrow(i, 0))) = pl;
+        } else {
+          *reinterpret_cast<f32x4*>(&sRt[16 * j + lr][rrow(i, 0)]) = R[i][j];
+        }
       }
     // the state update's operands, in flight during Z = A1 R
     float a2[2][2][8];  // [g][i][e]
@@ -960,15 +992,37 @@ __device__ __forceinline__ void walk_dir(const float* __restrict__ img, const vo
     f32x4 z[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) z[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (ZB) {  // six split products per contraction step of 32
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
+      for (int g = 0; g < 4; ++g) {
+        bf16x8 ah, am, al;
+        split3(__builtin_shufflevector(zA[2 * g], zA[2 * g + 1], 0, 1, 2, 3, 4, 5, 6, 7), ah, am,
+               al);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f32x4 b = *reinterpret_cast<const f32x4*>(&sRt[16 * j + lr][16 * u + 4 * lq]);
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-          z[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(zA[u][s], b[s], z[j], 0, 0, 0);
+        for (int j = 0; j < 4; ++j) {
+          const int r = 16 * j + lr, k = 32 * g + 8 * lq;
+          const bf16x8 b0 = *reinterpret_cast<const bf16x8*>(sRp + rp_off(0, r, k));
+          const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(sRp + rp_off(1, r, k));
+          const bf16x8 b2 = *reinterpret_cast<const bf16x8*>(sRp + rp_off(2, r, k));
+          z[j] = mfma_bf16(am, b1, z[j]);
+          z[j] = mfma_bf16(al, b0, z[j]);
+          z[j] = mfma_bf16(ah, b2, z[j]);
+          z[j] = mfma_bf16(am, b0, z[j]);
+          z[j] = mfma_bf16(ah, b1, z[j]);
+          z[j] = mfma_bf16(ah, b0, z[j]);
+        }
       }
+    } else {
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const f32x4 b = *reinterpret_cast<const f32x4*>(&sRt[16 * j + lr][16 * u + 4 * lq]);
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+            z[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(zA[u][s], b[s], z[j], 0, 0, 0);
+        }
+    }
     if (it + 1 < nch) load_zA(rec_buf(pair_of(it + 1)));
     // (3) U - Z (forward) or -Z (backward) as three bf16 planes, transposed,
     // and d_o, into LDS
@@ -976,16 +1030,17 @@ __device__ __forceinline__ void walk_dir(const float* __restrict__ img, const vo
     for (int j = 0; j < 4; ++j) {
       bf16x4 ph, pm, pl;
       split3(FWD ? ext[j] - z[j] : -z[j], ph, pm, pl);
-      *reinterpret_cast<bf16x4*>(&sZp[0][16 * j + lr][16 * w + 4 * lq]) = ph;
-      *reinterpret_cast<bf16x4*>(&sZp[1][16 * j + lr][16 * w + 4 * lq]) = pm;
-      *reinterpret_cast<bf16x4*>(&sZp[2][16 * j + lr][16 * w + 4 * lq]) = pl;
+      *reinterpret_cast<bf16x4*>(sZp + zo(0, 16 * j + lr, 16 * w + 4 * lq)) = ph;
+      *reinterpret_cast<bf16x4*>(sZp + zo(1, 16 * j + lr, 16 * w + 4 * lq)) = pm;
+      *reinterpret_cast<bf16x4*>(sZp + zo(2, 16 * j + lr, 16 * w + 4 * lq)) = pl;
     }
     if constexpr (!FWD) {
       if constexpr (DOB) {
-        uint16_t(*sDt)[DTS] = reinterpret_cast<uint16_t(*)[DTS]>(sDo);
+        uint16_t* sDt = reinterpret_cast<uint16_t*>(sDo);
 #pragma unroll
         for (int e = 0; e < 16; ++e)
-          sDt[16 * w + e][lane] = static_cast<uint16_t>(draw[e >> 3][(e & 7) >> 1] >> (16 * (e & 1)));
+          sDt[zo(0, 16 * w + e, lane)] =
+              static_cast<uint16_t>(draw[e >> 3][(e & 7) >> 1] >> (16 * (e & 1)));
       } else {
         float(*sDf)[FTS] = reinterpret_cast<float(*)[FTS]>(sDo);
 #pragma unroll
@@ -1007,7 +1062,7 @@ __device__ __forceinline__ void walk_dir(const float* __restrict__ img, const vo
       for (int p = 0; p < 3; ++p)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          bz[p][j] = *reinterpret_cast<const bf16x8*>(&sZp[p][16 * j + lr][32 * g + 8 * lq]);
+          bz[p][j] = *reinterpret_cast<const bf16x8*>(sZp + zo(p, 16 * j + lr, 32 * g + 8 * lq));
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         bf16x8 ah, am, al;
@@ -1027,13 +1082,13 @@ __device__ __forceinline__ void walk_dir(const float* __restrict__ img, const vo
       }
     }
     if constexpr (!FWD && DOB) {  // + Qt^T dO, dO exact in bf16
-      uint16_t(*sDt)[DTS] = reinterpret_cast<uint16_t(*)[DTS]>(sDo);
+      const uint16_t* sDt = reinterpret_cast<const uint16_t*>(sDo);
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
         bf16x8 bo[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          bo[j] = *reinterpret_cast<const bf16x8*>(&sDt[16 * j + lr][32 * g + 8 * lq]);
+          bo[j] = *reinterpret_cast<const bf16x8*>(sDt + zo(0, 16 * j + lr, 32 * g + 8 * lq));
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
           bf16x8 qh, qm, ql;
@@ -1082,10 +1137,15 @@ __global__ void __launch_bounds__(NT, 2) bwd_walk_kernel(
     const int32_t* __restrict__ cu, int N, int T_tot, int H, int both,
     const float* __restrict__ S0, float* __restrict__ rec_f, const float* __restrict__ dSf,
     float* __restrict__ dS0, float* __restrict__ rec_b) {
-  __shared__ __attribute__((aligned(16))) float sRt[64][WTS];  // sRt[j][cc] = R[cc][j]
-  __shared__ __attribute__((aligned(16))) uint16_t sZp[3][64][DTS];  // the update's B planes
-  // d_o of the chunk's tile, transposed: bf16 [64][DTS] or fp32 [64][FTS]
-  constexpr int DO_BYTES = DOB ? 64 * DTS * 2 : 64 * FTS * 4;
+  // R transposed: three bf16 planes (bf16 d_o) or fp32 [64][WTS]; the
+  // update's B operand as three bf16 planes; d_o of the chunk's tile,
+  // transposed, bf16 or fp32 [64][FTS] (walk_dir gives the layouts)
+  constexpr int R_BYTES = DOB ? 3 * 64 * 128 * 2 : 64 * WTS * 4;
+  constexpr int Z_BYTES = DOB ? 3 * 64 * 64 * 2 : 3 * 64 * DTS * 2;
+  constexpr int DO_BYTES = DOB ? 64 * 64 * 2 : 64 * FTS * 4;
+  static_assert(R_BYTES + Z_BYTES + DO_BYTES <= 80 * 1024, "two workgroups per CU");
+  __shared__ __attribute__((aligned(16))) unsigned char sR[R_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char sZ[Z_BYTES];
   __shared__ __attribute__((aligned(16))) unsigned char sDo[DO_BYTES];
   const int64_t nb = (int64_t)N * H * 2;
   int64_t b = blockIdx.x;
@@ -1100,9 +1160,9 @@ __global__ void __launch_bounds__(NT, 2) bwd_walk_kernel(
   eos = eos < bos ? bos : (eos > T_tot ? T_tot : eos);
   const int64_t L = eos - bos;
   if (fwd)
-    walk_dir<true, DOB>(img, d_o, bos, L, n, h, tile, H, S0, rec_f, nullptr, sRt, sZp, sDo);
+    walk_dir<true, DOB>(img, d_o, bos, L, n, h, tile, H, S0, rec_f, nullptr, sR, sZ, sDo);
   else
-    walk_dir<false, DOB>(img, d_o, bos, L, n, h, tile, H, dSf, rec_b, dS0, sRt, sZp, sDo);
+    walk_dir<false, DOB>(img, d_o, bos, L, n, h, tile, H, dSf, rec_b, dS0, sR, sZ, sDo);
 }
 
 // Three workgroups per CU (50 KB of LDS, at most 168 VGPRs): the kernel is
