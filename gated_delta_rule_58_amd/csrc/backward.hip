@@ -1340,19 +1340,35 @@ __global__ void __launch_bounds__(NT, 3) bwd_grad_kernel(
       for (int j = 0; j < 4; ++j) dMMt[orow<4>(i) * C + ocol(j)] = a4[0][j][i];
   }
   __syncthreads();
-  {  // dA = -M^T (dM M^T) on s < r
+  {  // dA = -M^T (dM M^T) on s < r; its epilogue adds sum_s dA[r, s] At[r, s]
+     // to dbeta (At read before the product, at the lane's elements) and
+     // stores dA scaled by beta_r, the factor the pairwise terms take it with
+    float at[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) at[i][j] = im[Rec::AT + orow<4>(i) * C + ocol(j)];
     f32x4 a4[1][4];
     zero(a4);
     gemm_staged2<4, 4, false, true>(a4, C, sa,
                                    [&](int r, int u) { return im[Rec::M + u * C + r]; },
                                    [&](int u, int s) { return dMMt[u * C + s]; });
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) {
+      const int r = orow<4>(i);
+      const float br = sB[r];
+      float part = 0.0f;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int r = orow<4>(i), s = ocol(j);
-        sT[r][s] = (s < r && r < Lc) ? -a4[0][j][i] : 0.0f;
+        const int s = ocol(j);
+        const float da = (s < r && r < Lc) ? -a4[0][j][i] : 0.0f;
+        part = fmaf(da, at[i][j], part);
+        sT[r][s] = da * br;
       }
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) part += __shfl_xor(part, off);
+      if (tc == 0) sDB[r] += part;  // the 16 lanes holding row r
+    }
   }
   {  // dK_E = -dX S^T, dQ_E = scale dO S^T, dK_D = Delta dS_next^T in one pipeline
     f32x4 acc[1][8];
@@ -1370,23 +1386,6 @@ __global__ void __launch_bounds__(NT, 3) bwd_grad_kernel(
             put8(c, Scr::DQE, scale);
         });
     put8(acc, Scr::DKD, 1.0f);
-  }
-  {  // dbeta += sum_s dA[r, s] At[r, s]: row r on lanes 4r .. 4r + 3; each lane
-     // then scales the dA entries it read by beta_r, the factor the pairwise
-     // terms below take them with (the barrier after it orders it)
-    const int r = t >> 2, qd = t & 3;
-    const float br = sB[r];
-    float a = 0.0f;
-#pragma unroll
-    for (int u = 0; u < C / 4; ++u) {
-      const int s2 = 4 * u + qd;
-      const float da = sT[r][s2];
-      a = fmaf(da, im[Rec::AT + r * C + s2], a);  // dA is 0 for s >= r
-      sT[r][s2] = da * br;
-    }
-    a += __shfl_xor(a, 1);
-    a += __shfl_xor(a, 2);
-    if (qd == 0) sDB[r] += a;
   }
   __syncthreads();  // dK_E, dQ_E, dK_D (scratch) and the scaled dA complete
   // The terms of the decay factors and the pairwise terms of At and P, 16
