@@ -562,6 +562,7 @@ __global__ void __launch_bounds__(NT, 3) bwd_prep_kernel(const void* __restrict_
   __shared__ float sPool[3 * C * (C + 1)];
   __shared__ float sB[C];
   static_assert(3 * SLAB <= C * (C + 1) && STAGE_FLOATS <= C * (C + 1), "slabs fit");
+  static_assert(2 * (C + D) * SKP <= 2 * C * (C + 1), "paired slabs fit in At's and P's place");
   float(*sA)[C + 1] = reinterpret_cast<float(*)[C + 1]>(sPool);
   float(*sP)[C + 1] = reinterpret_cast<float(*)[C + 1]>(sPool + C * (C + 1));
   float(*sM)[C + 1] = reinterpret_cast<float(*)[C + 1]>(sPool + 2 * C * (C + 1));
@@ -752,36 +753,35 @@ __global__ void __launch_bounds__(NT, 3) bwd_prep_kernel(const void* __restrict_
 #pragma unroll
       for (int j = 0; j < 8; ++j) im[Rec::W + orow<4>(i) * D + ocol(j)] = acc[0][j][i];
   }
-  {  // U = M diag(b) V
-    f32x4 acc[1][8];
-    zero(acc);
-    gemm_staged2<4, 8, true, true>(
-        acc, C, sa,
-        [&](int r, int s2) { return f32x4{sM[r][s2], sM[r][s2 + 1], sM[r][s2 + 2], sM[r][s2 + 3]}; },
-        [&](int s2, int j) { return sB[s2] * row_at<QB>(rv, HDi, s2, j); });
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) im[Rec::U + orow<4>(i) * D + ocol(j)] = acc[0][j][i];
-  }
   __syncthreads();  // W complete
-  {  // Qt = scale (Q_E - P W): acc starts at -Q_E (its reads overlap the product's)
-    f32x4 acc[1][8];
+  {  // U = M diag(b) V and Qt = scale (Q_E - P W) in one pipeline; Qt's
+     // accumulator starts at -Q_E (its reads overlap the product's)
+    f32x4 acc[1][8], aq[1][8];
+    zero(acc);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int r = orow<4>(i), cc = ocol(j);
-        acc[0][j][i] = -row_at<QB>(rq, HDi, r, cc) * __expf(Gf(r, cc));
+        aq[0][j][i] = -row_at<QB>(rq, HDi, r, cc) * __expf(Gf(r, cc));
       }
-    gemm_staged2<4, 8, true, true>(
-        acc, C, sa,
-        [&](int r, int s2) { return *reinterpret_cast<const f32x4*>(im + Rec::P + r * C + s2); },
-        [&](int s2, int cc) { return im[Rec::W + s2 * D + cc]; });
+    gemm_staged2_pair<4, 8>(
+        acc, aq, C, sa,
+        [&](int p2, int r, int s2) {
+          if (p2 == 0) return f32x4{sM[r][s2], sM[r][s2 + 1], sM[r][s2 + 2], sM[r][s2 + 3]};
+          return *reinterpret_cast<const f32x4*>(im + Rec::P + r * C + s2);
+        },
+        [&](int p2, int s2, int j) {
+          return p2 == 0 ? sB[s2] * row_at<QB>(rv, HDi, s2, j) : im[Rec::W + s2 * D + j];
+        },
+        [](int, const float*, const float*) {});
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) im[Rec::QT + orow<4>(i) * D + ocol(j)] = -scale * acc[0][j][i];
+      for (int j = 0; j < 8; ++j) {
+        im[Rec::U + orow<4>(i) * D + ocol(j)] = acc[0][j][i];
+        im[Rec::QT + orow<4>(i) * D + ocol(j)] = -scale * aq[0][j][i];
+      }
   }
   if (t < D) im[Rec::EC + t] = __expf(Gf(C - 1, t));
 }
