@@ -1328,8 +1328,7 @@ __global__ void __launch_bounds__(NT, 3) bwd_grad_kernel(
       }
   }
   __syncthreads();
-  float* dMMt = sc + Scr::DKE;  // [C][C], until dK_E is written
-  {  // dM M^T
+  {  // dM M^T, written over dM in sT (the product has read dM when it returns)
     f32x4 a4[1][4];
     zero(a4);
     gemm_staged2<4, 4, true, false>(a4, C, sa, [&](int r, int u) { return sT[r][u]; },
@@ -1337,12 +1336,13 @@ __global__ void __launch_bounds__(NT, 3) bwd_grad_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) dMMt[orow<4>(i) * C + ocol(j)] = a4[0][j][i];
+      for (int j = 0; j < 4; ++j) sT[orow<4>(i)][ocol(j)] = a4[0][j][i];
   }
-  __syncthreads();
+  barrier_lds();
   {  // dA = -M^T (dM M^T) on s < r; its epilogue adds sum_s dA[r, s] At[r, s]
      // to dbeta (At read before the product, at the lane's elements) and
-     // stores dA scaled by beta_r, the factor the pairwise terms take it with
+     // stores dA scaled by beta_r, the factor the pairwise terms take it
+     // with, over dM M^T in sT (read by the product when it returns)
     float at[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -1352,7 +1352,7 @@ __global__ void __launch_bounds__(NT, 3) bwd_grad_kernel(
     zero(a4);
     gemm_staged2<4, 4, false, true>(a4, C, sa,
                                    [&](int r, int u) { return im[Rec::M + u * C + r]; },
-                                   [&](int u, int s) { return dMMt[u * C + s]; });
+                                   [&](int u, int s) { return sT[u][s]; });
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = orow<4>(i);
