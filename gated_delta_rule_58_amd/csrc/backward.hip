@@ -28,8 +28,8 @@
 //             its own, in launches of at most grad_slots workgroups: with S
 //             and dS_next known, the chunk's gradients dq, dk, dv, dg, dbeta
 //             by the chain rule through the identities above (the pairwise
-//             decay terms of At and P per key channel, then a reverse
-//             cumulative sum for dg).
+//             decay terms of At and P per 16-channel slab, dg as the
+//             reverse cumulative sum of dgamma within the same slab).
 #include <type_traits>
 
 #include "chunk_common.hpp"
@@ -1414,7 +1414,7 @@ __global__ void __launch_bounds__(NT, 3) bwd_grad_kernel(
   // (ln, lq) of wave w then owns rows 16 w + 4 lq + v (v < 4) of channel
   // c0 + ln: it reads those elements' decay-factor gradients and g (for the
   // floor) itself, one slab ahead as well, adds the pairwise terms and writes
-  // dq, dk and dgamma.
+  // dq and dk; the slab's dgamma, summed down its 64 rows, gives dg.
   // (16 channels per slab: the MFMA tiles below use the 16 lanes of a row
   // as the slab's channels)
   static_assert(SC == 16, "one slab channel per lane of a 16-lane row");
