@@ -1215,6 +1215,15 @@ __global__ void __launch_bounds__(NT, 3) bwd_grad_kernel(
   // quads (4 consecutive contraction indices) for the staged products
   auto ld4 = [](const float* x) { return *reinterpret_cast<const f32x4*>(x); };
   auto dO4 = [&](int r, int cc) { return row4_at<DOB>(ro, HDi, r, cc); };
+  // a staged product's 64 x 128 result in the lane's own order: tile j of
+  // thread t at off + 4 (NT j + t), one 16-byte store (read back only by the
+  // same thread, in the pairwise phase)
+  auto put8own = [&](const f32x4 (&acc)[1][8], int off, float mul) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      *reinterpret_cast<f32x4*>(sc + off + 4 * (NT * j + t)) =
+          f32x4{mul * acc[0][j][0], mul * acc[0][j][1], mul * acc[0][j][2], mul * acc[0][j][3]};
+  };
   auto put8 = [&](f32x4 (&acc)[1][8], int off, float mul) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -1381,11 +1390,11 @@ __global__ void __launch_bounds__(NT, 3) bwd_grad_kernel(
         [&](int p2, int j, int cc) { return ld4((p2 == 2 ? dS : S) + cc * D + j); },
         [&](int p2, f32x4(&c)[1][8]) {
           if (p2 == 0)
-            put8(c, Scr::DKE, -1.0f);
+            put8own(c, Scr::DKE, -1.0f);
           else
-            put8(c, Scr::DQE, scale);
+            put8own(c, Scr::DQE, scale);
         });
-    put8(acc, Scr::DKD, 1.0f);
+    put8own(acc, Scr::DKD, 1.0f);
   }
   __syncthreads();  // dK_E, dQ_E, dK_D (scratch) and the scaled dA complete
   // The terms of the decay factors and the pairwise terms of At and P, 16
@@ -1412,9 +1421,10 @@ __global__ void __launch_bounds__(NT, 3) bwd_grad_kernel(
   // and gamma into LDS (4-wide loads, one slab ahead so that the reads stay
   // in flight across the slab's barriers, which order LDS only).  Lane
   // (ln, lq) of wave w then owns rows 16 w + 4 lq + v (v < 4) of channel
-  // c0 + ln: it reads those elements' decay-factor gradients and g (for the
-  // floor) itself, one slab ahead as well, adds the pairwise terms and writes
-  // dq and dk; the slab's dgamma, summed down its 64 rows, gives dg.
+  // c0 + ln: it reads those elements' decay-factor gradients (which it wrote
+  // itself, put8own) and g (for the floor), one slab ahead as well, adds the
+  // pairwise terms and writes dq and dk; the slab's dgamma, summed down its
+  // 64 rows, gives dg.
   // (16 channels per slab: the MFMA tiles below use the 16 lanes of a row
   // as the slab's channels)
   static_assert(SC == 16, "one slab channel per lane of a 16-lane row");
@@ -1428,14 +1438,14 @@ __global__ void __launch_bounds__(NT, 3) bwd_grad_kernel(
     pk = row4_at<QB>(rk, HDi, xr, cc);
     pq = row4_at<QB>(rq, HDi, xr, cc);
     pg = *reinterpret_cast<const f32x4*>(im + Rec::G + xr * D + cc);
-    const int x0 = 16 * w + 4 * lq, vo = (x0 * D + c0 + ln) * 4;
+    const int x0 = 16 * w + 4 * lq, vo = 4 * (NT * (c0 / SC) + t) * 4;
+    // the lane's own elements of dK_E, dQ_E, dK_D (put8own: tile c0 / 16)
+    eke = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rsc, vo, Scr::DKE * 4, 0));
+    eqe = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rsc, vo, Scr::DQE * 4, 0));
+    ekd = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rsc, vo, Scr::DKD * 4, 0));
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      eke[v] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsc, vo, (Scr::DKE + v * D) * 4, 0));
-      eqe[v] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsc, vo, (Scr::DQE + v * D) * 4, 0));
-      ekd[v] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsc, vo, (Scr::DKD + v * D) * 4, 0));
+    for (int v = 0; v < 4; ++v)
       egv[v] = row_at<false>(rgf, HDi, x0 + v, c0 + ln);  // rows past the chunk end read 0
-    }
   };
   fetch_slab(0);
   for (int c0 = 0; c0 < D; c0 += SC) {
