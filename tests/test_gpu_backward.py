@@ -237,6 +237,45 @@ def test_backward_config1_sampled_heads():
     check(sub, ref, "config 1 heads %s" % heads)
 
 
+def test_backward_config3_long_sequence_sampled_head():
+    """One sequence of 131,072 tokens, 96 heads (the long-context prefill
+    workload) through the whole backward on the GPU: 2,048 chunk steps per
+    walk, 196,704 (chunk, head) pairs (24 gradient launches; record offsets
+    past 2^31 floats).  g and beta are the backward's inputs: they come from a
+    plain fp32 gate in torch on the CPU (the gate kernel has its own parity
+    tests), and the oracle gets the same fp32 values.  One sampled head
+    against the oracle's reverse-mode gradient."""
+    need_gpu()
+    say("backward config 3 (T=131072, H=96), one sampled head")
+    dr = draw_config(3, device=DEV)
+    H = CONFIGS[3]["H"]
+    T = dr.q.shape[0]
+    say("  g, beta on the CPU (fp32)")
+    z = dr.x.cpu()
+    z += dr.dt_bias.cpu().reshape(1, H, 128)
+    g = torch.nn.functional.softplus(z, threshold=1e9)
+    del z
+    a = torch.exp(dr.A_log.cpu().double()).float()
+    g.mul_(-(a.reshape(1, H, 1) if a.numel() == H else a.reshape(1, H, 128)))
+    beta = torch.sigmoid(dr.b.cpu().float())
+    say("  d_o (bf16, seeded, CPU)")
+    d_o = torch.randn(T, H, 128, generator=torch.Generator().manual_seed(95)).to(torch.bfloat16)
+    say("  GPU backward")
+    got = kda.chunk_prefill_backward(dr.q, dr.k, dr.v, g.to(DEV), beta.to(DEV), d_o.to(DEV),
+                                     dr.cu_seqlens.to(DEV), None,
+                                     cu_seqlens_host=dr.cu_seqlens)
+    torch.cuda.synchronize()
+    heads = sample_heads(H, 1, 93)
+    say("  oracle on head", heads)
+    ref = oracle.prefill_backward(dr.q[:, heads].cpu(), dr.k[:, heads].cpu(),
+                                  dr.v[:, heads].cpu(), g[:, heads], beta[:, heads],
+                                  dr.cu_seqlens, None, d_o=d_o[:, heads].float())
+    sub = [None if t is None else t[:, heads].cpu() for t in got]
+    del got, dr, g, beta, d_o
+    torch.cuda.empty_cache()
+    check(sub, ref, "config 3 head %s" % heads)
+
+
 @pytest.mark.parametrize("per_channel,xdt", [(False, torch.float32), (True, torch.bfloat16)])
 def test_gate_backward_parity(per_channel, xdt):
     """kda_gate_backward against oracle.gate_backward: dx and db elementwise
