@@ -75,6 +75,27 @@ def test_backward_varlen_small(qdt, dodt):
     assert torch.equal(got[5][1].cpu(), dSf[1])
 
 
+@pytest.mark.parametrize("dodt", [torch.bfloat16, torch.float32])
+def test_backward_deterministic(dodt):
+    """Race detection: the whole backward, run three times on the same inputs
+    (four sequences, 8 heads, initial states, d_o and d_final_state), gives
+    bit-identical gradients.  No kernel of the path accumulates with atomics,
+    so any difference is a race on LDS or scratch."""
+    need_gpu()
+    say("backward determinism", dodt)
+    dr = draw_prefill([1500, 64, 777, 2000], H=8, dtype=torch.bfloat16, init_state=True,
+                      seed=97)
+    g, beta = oracle_gate_f32(dr)
+    r = torch.Generator().manual_seed(98)
+    d_o = torch.randn(dr.q.shape[0], 8, 128, generator=r).to(dodt)
+    dSf = torch.randn(4, 8, 128, 128, generator=r) * 0.1
+    first = _run(dr, g, beta, d_o, dSf, 1.0)
+    for _ in range(2):
+        again = _run(dr, g, beta, d_o, dSf, 1.0)
+        for name, a, b in zip(NAMES, first, again):
+            assert torch.equal(a, b), name
+
+
 def test_backward_no_state_terms():
     """No initial state, no d_final_state: the gradient of o alone, one
     sequence of 300 tokens (five chunks, ragged tail)."""
