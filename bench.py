@@ -109,11 +109,68 @@ def parse():
     ap.add_argument("--ws-chunks", type=int, default=T // C,
                     help="chunks per pass the prefill workspace holds (T/64 = one pass)")
     ap.add_argument("--only", choices=["all", "prefill", "decode", "prologue", "workloads",
-                                       "backward", "copy", "states"],
+                                       "backward", "copy", "states", "sweep"],
                     default="all",
                     help="profiling aid: run one part only (prints a diagnostic line, "
                          "not the bench line)")
     return ap.parse_args()
+
+
+def bench_length_sweep(args, torch, kda, synth):
+    """kda_chunk_prefill_gated (o bf16, fp32 final state) and
+    kda_chunk_prefill_backward (bf16 d_o) on one sequence of T tokens, H = 96,
+    for T = 1,024 .. 131,072 (the T=4096 recipe at other lengths).  Each point
+    first runs its call for 0.3 s so the clocks have settled, then times about
+    300 ms of calls (at least 2) with events."""
+    dev = "cuda:0"
+    import time
+
+    def timeit(fn, reps):
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < 0.3:
+            fn()
+            torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    points = []
+    for Tn in (1024, 2048, 4096, 8192, 16384, 32768, 65536, 131072):
+        dr = synth.draw_prefill([Tn], H, torch.bfloat16, False, 7, dev)
+        cu_h = dr.cu_seqlens
+        cu_d = cu_h.to(dev)
+        ws = torch.empty(kda.chunk_prefill_workspace_bytes(1, H, D, D, (Tn + C - 1) // C),
+                         dtype=torch.uint8, device=dev)
+        o = torch.empty((Tn, H, D), dtype=torch.bfloat16, device=dev)
+        Sf = torch.empty((1, H, D, D), dtype=torch.float32, device=dev)
+
+        def fwd():
+            kda.chunk_prefill_gated(dr.q, dr.k, dr.v, dr.x, dr.b, dr.A_log, dr.dt_bias, cu_d,
+                                    None, out=o, final_state=Sf, cu_seqlens_host=cu_h,
+                                    workspace=ws)
+        ms = timeit(fwd, max(5, 4_000_000 // Tn))
+        del ws, o, Sf
+        g, beta = kda.gate(dr.x, dr.b, dr.A_log, dr.dt_bias)
+        d_o = torch.randn((Tn, H, D), device=dev,
+                          generator=torch.Generator(device=dev).manual_seed(5)).to(torch.bfloat16)
+        wsb = torch.empty(kda.chunk_prefill_backward_workspace_bytes(Tn, 1, H), dtype=torch.uint8,
+                          device=dev)
+
+        def bwd():
+            kda.chunk_prefill_backward(dr.q, dr.k, dr.v, g, beta, d_o, cu_d, None,
+                                       want_d_initial_state=False, cu_seqlens_host=cu_h,
+                                       workspace=wsb)
+        bms = timeit(bwd, max(2, 400_000 // Tn))
+        points.append(dict(T=Tn, prefill_ms=ms, prefill_tokens_per_s=Tn / (ms * 1e-3),
+                           backward_ms=bms, backward_tokens_per_s=Tn / (bms * 1e-3)))
+        del dr, g, beta, d_o, wsb
+        torch.cuda.empty_cache()
+    return dict(workload="one sequence of T tokens, H=96, bf16 q/k/v, fp32 gate logits",
+                points=points)
 
 
 def bench_copy(args, torch):
@@ -482,7 +539,8 @@ def main():
               "backward": lambda: bench_backward(args, torch, kda, synth),
               "workloads": lambda: {str(i): bench_prefill_workload(args, torch, kda, synth, i)
                                     for i in (2, 3)},
-              "copy": lambda: bench_copy(args, torch)}[args.only]
+              "copy": lambda: bench_copy(args, torch),
+              "sweep": lambda: bench_length_sweep(args, torch, kda, synth)}[args.only]
         print(json.dumps({"diagnostic": args.only, **fn()}), flush=True)
         return
     pre = bench_prefill(args, torch, kda, synth)
