@@ -71,8 +71,8 @@ struct Rec {
 };
 // Per-(chunk, head) scratch of bwd_grad (offsets in floats, each [C][D]).
 struct Scr {
-  static constexpr int X = 0, DL = C * D, DD = 2 * C * D, DX = 3 * C * D, DKE = 4 * C * D,
-                       DQE = 5 * C * D, DKD = 6 * C * D, floats = 7 * C * D;
+  static constexpr int DL = 0, DD = C * D, DX = 2 * C * D, DKE = 3 * C * D, DQE = 4 * C * D,
+                       DKD = 5 * C * D, floats = 6 * C * D;
 };
 
 constexpr int KT = 16;
@@ -1178,21 +1178,27 @@ __global__ void __launch_bounds__(NT, 3) bwd_grad_kernel(
     const float* __restrict__ dSrec, float* __restrict__ scr, float* __restrict__ dq,
     float* __restrict__ dk, float* __restrict__ dv, float* __restrict__ dg,
     float* __restrict__ dbeta, int64_t item0) {
-  // sT, sDP: [C][C + 1] each, written from dM on; before that the first
-  // products' slabs (gemm_staged2_pair) and their per-wave row sums sit there.
-  // sU: the other products' LDS slabs, then (pairwise phase) K, Q and gamma of
+  // sT, sDP: [C][C + 1] each, written from dM on.  Before that the first
+  // products' slabs (gemm_staged2_pair) sit there, then X (sX, [C][D] with
+  // the 16-float groups of a row XOR-swizzled by row / 4, so that the lanes
+  // of an accumulator tile, rows 4 apart, hit distinct banks) until dM has
+  // read it.  sU: the other products' LDS slabs (and, during the first
+  // pipeline, its per-wave row sums), then (pairwise phase) K, Q and gamma of
   // a 16-channel slab and the per-wave partial sums.
   constexpr int SC = 16, SS = SC + 1;
   constexpr int PAIR_FLOATS = 3 * C * SS + 8 * SC;
   constexpr int TP = C * (C + 1);
   constexpr int STAGE_PAIR = 2 * (C + D) * SKP;
-  static_assert(STAGE_PAIR + 4 * D <= 2 * TP, "paired slabs and row sums fit in sT, sDP");
+  static_assert(STAGE_PAIR <= 2 * TP && C * D <= 2 * TP, "paired slabs, then X, in sT, sDP");
+  static_assert(4 * D <= STAGE_FLOATS, "row sums in sU");
   __shared__ float sPool[2 * TP + (PAIR_FLOATS > STAGE_FLOATS ? PAIR_FLOATS : STAGE_FLOATS)];
   __shared__ float sB[C], sDB[C], sGC[D];
   float(*sT)[C + 1] = reinterpret_cast<float(*)[C + 1]>(sPool);
   float(*sDP)[C + 1] = reinterpret_cast<float(*)[C + 1]>(sPool + TP);
   float* sU = sPool + 2 * TP;
-  float* sRed = sPool + STAGE_PAIR;  // [4][D]
+  float* sRed = sU;    // [4][D], during the first pipeline
+  float* sX = sPool;   // X, from the first pipeline's end until dM
+  auto xo = [](int r, int c) { return r * D + (c ^ (((r >> 2) & 3) << 4)); };
   float* sa = sU;
   ChunkPos p;
   if (!chunk_of_block(cu, N, T_tot, H, maxnch, p, item0 + blockIdx.x)) return;
@@ -1271,22 +1277,23 @@ __global__ void __launch_bounds__(NT, 3) bwd_grad_kernel(
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int r = orow<4>(i), col = ocol(j);
-        sc[Scr::X + r * D + col] = Vf(r, col) - acc[0][j][i];
+        sX[xo(r, col)] = Vf(r, col) - acc[0][j][i];
       }
   }
+  if (t < D)  // the gradient of gamma_C through e^gamma_C (the pairwise phase adds the rest)
+    sGC[t] = (sRed[t] + sRed[D + t] + sRed[2 * D + t] + sRed[3 * D + t]) * __expf(Gf(C - 1, t));
+  barrier_lds();  // X complete, the row sums read (sU takes the next slabs)
   // dDelta += scale P^T dO
   gemm_staged2<4, 8, false, true>(accD, C, sa,
                                  [&](int r, int s) { return scale * im[Rec::P + s * C + r]; },
                                  [&](int s, int j) { return dOf(s, j); });
   put8(accD, Scr::DD, 1.0f);
   __syncthreads();
-  if (t < D)  // the gradient of gamma_C through e^gamma_C (the pairwise phase adds the rest)
-    sGC[t] = (sRed[t] + sRed[D + t] + sRed[2 * D + t] + sRed[3 * D + t]) * __expf(Gf(C - 1, t));
   {  // Delta = M diag(b) X
     f32x4 acc[1][8];
     zero(acc);
     gemm_staged2<4, 8, true, true>(acc, C, sa, [&](int r, int s) { return ld4(im + Rec::M + r * C + s); },
-                                  [&](int s, int j) { return sB[s] * sc[Scr::X + s * D + j]; });
+                                  [&](int s, int j) { return sB[s] * sX[xo(s, j)]; });
     put8(acc, Scr::DL, 1.0f);
   }
   {  // dY = M^T dDelta, dX = diag(b) dY (= dv), dbeta += rowsum(dY . X)
@@ -1305,7 +1312,7 @@ __global__ void __launch_bounds__(NT, 3) bwd_grad_kernel(
         const float dX = sB[r] * acc[0][j][i];
         sc[Scr::DX + r * D + col] = dX;
         if (r < Lc) dv[tok(r, col)] = dX;
-        part = fmaf(acc[0][j][i], sc[Scr::X + r * D + col], part);
+        part = fmaf(acc[0][j][i], sX[xo(r, col)], part);
       }
 #pragma unroll
       for (int off = 1; off < 16; off <<= 1) part += __shfl_xor(part, off);
@@ -1313,14 +1320,16 @@ __global__ void __launch_bounds__(NT, 3) bwd_grad_kernel(
     }
   }
   __syncthreads();
-  {  // dM = dDelta Y^T, then dP = scale dO Delta^T on s <= r, in one pipeline
+  {  // dM = dDelta Y^T (Y = diag(b) X, X from LDS), then dP = scale dO Delta^T
+     // on s <= r, in one pipeline; dM goes over X once the pipeline has read
+     // it (X is read by the first product only)
     f32x4 a4[1][4];
     zero(a4);
     gemm_staged2_seq<2, 4, 4, true, false>(
         a4, D, sa,
         [&](int p2, int r, int j) { return p2 == 0 ? ld4(sc + Scr::DD + r * D + j) : dO4(r, j); },
         [&](int p2, int j, int s) {
-          return p2 == 0 ? sB[s] * ld4(sc + Scr::X + s * D + j) : ld4(sc + Scr::DL + s * D + j);
+          return p2 == 0 ? sB[s] * ld4(sX + xo(s, j)) : ld4(sc + Scr::DL + s * D + j);
         },
         [&](int, f32x4(&c)[1][4]) {
 #pragma unroll
@@ -1595,7 +1604,7 @@ __global__ void __launch_bounds__(NT, 3) bwd_grad_kernel(
 
 // The gradient kernel runs in launches of at most grad_slots workgroups, each
 // with a scratch slot of its own: one slot per (chunk, head) up to
-// GRAD_SLOTS_MAX (1.9 GB of scratch), so that up to that size one launch
+// GRAD_SLOTS_MAX (1.6 GB of scratch), so that up to that size one launch
 // covers every chunk and the GPU's dispatcher refills each CU as its
 // workgroups finish (a launch per 512 workgroups cost 4 % at T = 4096,
 // H = 96 in drained launch tails).

@@ -301,7 +301,7 @@ kda_status kda_chunk_prefill_gated_static(
  * The workspace (kda_chunk_prefill_backward_workspace_bytes) holds per (chunk,
  * head) the chunk's intermediate matrices, the recomputed entry state and the
  * state gradient, 344,576 bytes, for P = (T_tot / 64 + N) * H (chunk slot,
- * head) pairs, plus min(P, 8192) scratch slots of 229,376 bytes for the
+ * head) pairs, plus min(P, 8192) scratch slots of 196,608 bytes for the
  * gradient kernel (one workgroup per slot in a launch); the call never
  * allocates.  Requires dk == dv == 128; refusals as for
  * kda_chunk_prefill (the workspace check uses the backward size), plus NULL

@@ -304,12 +304,12 @@ def test_backward_refusals():
                                                              ctypes.c_int32]
     need = L.kda_chunk_prefill_backward_workspace_bytes(48, 2, 4, 128, 128)
     # per (chunk slot, head): the 344,576-byte record and states, plus a
-    # 229,376-byte scratch slot of the gradient kernel, up to 8192 slots
+    # 196,608-byte scratch slot of the gradient kernel, up to 8192 slots
     pairs = (48 // 64 + 2) * 4
-    assert need == pairs * (344576 + 229376)
+    assert need == pairs * (344576 + 196608)
     big_pairs = (1 << 20) // 64 * 96 + 96
     assert L.kda_chunk_prefill_backward_workspace_bytes(1 << 20, 1, 96, 128, 128) == \
-        big_pairs * 344576 + 8192 * 229376
+        big_pairs * 344576 + 8192 * 196608
     assert L.kda_chunk_prefill_backward_workspace_bytes(48, 2, 4, 64, 128) == 0
     cu = [0, 20, 48]
     assert _backward(L, cu, dk_dim=64) == 4
