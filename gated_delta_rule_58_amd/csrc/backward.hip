@@ -1297,6 +1297,11 @@ __global__ void __launch_bounds__(NT, 3) bwd_grad_kernel(
     put8(acc, Scr::DL, 1.0f);
   }
   {  // dY = M^T dDelta, dX = diag(b) dY (= dv), dbeta += rowsum(dY . X)
+    // (X through an opaque zero offset: its addresses are recomputed here
+    // rather than kept in registers, which spills, since X's epilogue)
+    int oz = 0;
+    asm volatile("" : "+v"(oz));
+    const float* qX = sX + oz;
     f32x4 acc[1][8];
     zero(acc);
     gemm_staged2<4, 8, false, true>(acc, C, sa,
@@ -1312,7 +1317,7 @@ __global__ void __launch_bounds__(NT, 3) bwd_grad_kernel(
         const float dX = sB[r] * acc[0][j][i];
         sc[Scr::DX + r * D + col] = dX;
         if (r < Lc) dv[tok(r, col)] = dX;
-        part = fmaf(acc[0][j][i], sX[xo(r, col)], part);
+        part = fmaf(acc[0][j][i], qX[xo(r, col)], part);
       }
 #pragma unroll
       for (int off = 1; off < 16; off <<= 1) part += __shfl_xor(part, off);
