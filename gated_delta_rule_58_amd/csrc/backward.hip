@@ -559,7 +559,7 @@ __global__ void __launch_bounds__(NT, 3) bwd_prep_kernel(const void* __restrict_
   // K, Q and gamma where M goes later, the products after M stage through At's
   // place
   constexpr int SLAB = C * (CS + 1);
-  __shared__ float sPool[3 * C * (C + 1)];
+  __shared__ __attribute__((aligned(16))) float sPool[3 * C * (C + 1)];
   __shared__ float sB[C];
   static_assert(3 * SLAB <= C * (C + 1) && STAGE_FLOATS <= C * (C + 1), "slabs fit");
   static_assert(2 * (C + D) * SKP <= 2 * C * (C + 1), "paired slabs fit in At's and P's place");
@@ -1179,10 +1179,10 @@ __global__ void __launch_bounds__(NT, 3) bwd_grad_kernel(
     float* __restrict__ dk, float* __restrict__ dv, float* __restrict__ dg,
     float* __restrict__ dbeta, int64_t item0) {
   // sT, sDP: [C][C + 1] each, written from dM on.  Before that the first
-  // products' slabs (gemm_staged2_pair) sit there, then X (sX, [C][D] with
-  // the 16-float groups of a row XOR-swizzled by row / 4, so that the lanes
-  // of an accumulator tile, rows 4 apart, hit distinct banks) until dM has
-  // read it.  sU: the other products' LDS slabs (and, during the first
+  // products' slabs (gemm_staged2_pair) sit there, then X transposed (sXT,
+  // [D][C]: X[r][c] in row c, its 4-float groups XOR-swizzled by c % 16, so
+  // that 16 lanes reading one group each of rows c .. c + 15 hit distinct
+  // banks) until dM has read it.  sU: the other products' LDS slabs (and, during the first
   // pipeline, its per-wave row sums), then (pairwise phase) K, Q and gamma of
   // a 16-channel slab and the per-wave partial sums.
   constexpr int SC = 16, SS = SC + 1;
@@ -1191,14 +1191,16 @@ __global__ void __launch_bounds__(NT, 3) bwd_grad_kernel(
   constexpr int STAGE_PAIR = 2 * (C + D) * SKP;
   static_assert(STAGE_PAIR <= 2 * TP && C * D <= 2 * TP, "paired slabs, then X, in sT, sDP");
   static_assert(4 * D <= STAGE_FLOATS, "row sums in sU");
-  __shared__ float sPool[2 * TP + (PAIR_FLOATS > STAGE_FLOATS ? PAIR_FLOATS : STAGE_FLOATS)];
-  __shared__ float sB[C], sDB[C], sGC[D];
+  __shared__ __attribute__((aligned(16))) float
+      sPool[2 * TP + (PAIR_FLOATS > STAGE_FLOATS ? PAIR_FLOATS : STAGE_FLOATS)];
+  __shared__ __attribute__((aligned(16))) float sB[C];
+  __shared__ float sDB[C], sGC[D];
   float(*sT)[C + 1] = reinterpret_cast<float(*)[C + 1]>(sPool);
   float(*sDP)[C + 1] = reinterpret_cast<float(*)[C + 1]>(sPool + TP);
   float* sU = sPool + 2 * TP;
   float* sRed = sU;    // [4][D], during the first pipeline
-  float* sX = sPool;   // X, from the first pipeline's end until dM
-  auto xo = [](int r, int c) { return r * D + (c ^ (((r >> 2) & 3) << 4)); };
+  float* sXT = sPool;  // X^T, from the first pipeline's end until dM
+  auto xto = [](int c, int r) { return c * C + ((((r >> 2) ^ (c & 15))) << 2) + (r & 3); };
   float* sa = sU;
   ChunkPos p;
   if (!chunk_of_block(cu, N, T_tot, H, maxnch, p, item0 + blockIdx.x)) return;
@@ -1272,13 +1274,16 @@ __global__ void __launch_bounds__(NT, 3) bwd_grad_kernel(
           part += __shfl_xor(part, 32);
           if (lq == 0) sRed[w * D + k0 + kk] = part;
         });
+    // lane (l % 16, l / 16) of wave w holds X rows 16 w + 4 (l / 16) + i
+    // (i < 4) of column 16 j + l % 16: one 16-byte group of X^T
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < 8; ++j) {
+      const int col = ocol(j), r0 = orow<4>(0);
+      f32x4 x;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int r = orow<4>(i), col = ocol(j);
-        sX[xo(r, col)] = Vf(r, col) - acc[0][j][i];
-      }
+      for (int i = 0; i < 4; ++i) x[i] = Vf(r0 + i, col) - acc[0][j][i];
+      *reinterpret_cast<f32x4*>(sXT + xto(col, r0)) = x;
+    }
   }
   if (t < D)  // the gradient of gamma_C through e^gamma_C (the pairwise phase adds the rest)
     sGC[t] = (sRed[t] + sRed[D + t] + sRed[2 * D + t] + sRed[3 * D + t]) * __expf(Gf(C - 1, t));
@@ -1289,11 +1294,27 @@ __global__ void __launch_bounds__(NT, 3) bwd_grad_kernel(
                                  [&](int s, int j) { return dOf(s, j); });
   put8(accD, Scr::DD, 1.0f);
   __syncthreads();
-  {  // Delta = M diag(b) X
+  {  // Delta = M diag(b) X, without staging: wave w forms rows 16 w .. + 15
+     // from its rows of M diag(b) in registers (lane (lr, lq): row 16 w + lr,
+     // contraction 16 u + 4 lq + s) and X^T read from LDS in the same order
+    const int lr = t & 15, lq = (t & 63) >> 4, w = t >> 6;
+    f32x4 am[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) am[u] = ld4(im + Rec::M + (16 * w + lr) * C + 16 * u + 4 * lq);
     f32x4 acc[1][8];
     zero(acc);
-    gemm_staged2<4, 8, true, true>(acc, C, sa, [&](int r, int s) { return ld4(im + Rec::M + r * C + s); },
-                                  [&](int s, int j) { return sB[s] * sX[xo(s, j)]; });
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const f32x4 bq = ld4(sB + 16 * u + 4 * lq);
+      const f32x4 a = am[u] * bq;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const f32x4 b = ld4(sXT + xto(16 * j + lr, 16 * u + 4 * lq));
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2)
+          acc[0][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s2], b[s2], acc[0][j], 0, 0, 0);
+      }
+    }
     put8(acc, Scr::DL, 1.0f);
   }
   {  // dY = M^T dDelta, dX = diag(b) dY (= dv), dbeta += rowsum(dY . X)
@@ -1301,12 +1322,15 @@ __global__ void __launch_bounds__(NT, 3) bwd_grad_kernel(
     // rather than kept in registers, which spills, since X's epilogue)
     int oz = 0;
     asm volatile("" : "+v"(oz));
-    const float* qX = sX + oz;
+    const float* qX = sXT + oz;
     f32x4 acc[1][8];
     zero(acc);
     gemm_staged2<4, 8, false, true>(acc, C, sa,
                                    [&](int r, int s) { return im[Rec::M + s * C + r]; },
                                    [&](int s, int j) { return sc[Scr::DD + s * D + j]; });
+    f32x4 xv[8];  // X at the lane's elements: one 16-byte group of X^T per tile
+#pragma unroll
+    for (int j = 0; j < 8; ++j) xv[j] = ld4(qX + xto(ocol(j), orow<4>(0)));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = orow<4>(i);
@@ -1317,7 +1341,7 @@ __global__ void __launch_bounds__(NT, 3) bwd_grad_kernel(
         const float dX = sB[r] * acc[0][j][i];
         sc[Scr::DX + r * D + col] = dX;
         if (r < Lc) dv[tok(r, col)] = dX;
-        part = fmaf(acc[0][j][i], qX[xo(r, col)], part);
+        part = fmaf(acc[0][j][i], xv[j][i], part);
       }
 #pragma unroll
       for (int off = 1; off < 16; off <<= 1) part += __shfl_xor(part, off);
@@ -1334,7 +1358,9 @@ __global__ void __launch_bounds__(NT, 3) bwd_grad_kernel(
         a4, D, sa,
         [&](int p2, int r, int j) { return p2 == 0 ? ld4(sc + Scr::DD + r * D + j) : dO4(r, j); },
         [&](int p2, int j, int s) {
-          return p2 == 0 ? sB[s] * ld4(sX + xo(s, j)) : ld4(sc + Scr::DL + s * D + j);
+          return p2 == 0 ? sB[s] * f32x4{sXT[xto(j, s)], sXT[xto(j + 1, s)], sXT[xto(j + 2, s)],
+                                         sXT[xto(j + 3, s)]}
+                         : ld4(sc + Scr::DL + s * D + j);
         },
         [&](int, f32x4(&c)[1][4]) {
 #pragma unroll
