@@ -1377,46 +1377,77 @@ __global__ void __launch_bounds__(NT, 3) bwd_grad_kernel(
       }
   }
   __syncthreads();
-  {  // dM M^T, written over dM in sT (the product has read dM when it returns)
-    f32x4 a4[1][4];
-    zero(a4);
-    gemm_staged2<4, 4, true, false>(a4, C, sa, [&](int r, int u) { return sT[r][u]; },
-                                   [&](int u, int s) { return ld4(im + Rec::M + s * C + u); });
+  // dM M^T and dA = -M^T (dM M^T) without staging: wave w forms rows
+  // 16 w .. + 15 of each product from its rows of M (or M^T) in registers and
+  // the other operand read from sT (lane (lr, lq), sub-step s: contraction
+  // index 16 u + 4 lq + s)
+  {
+    const int lr = t & 15, lq = (t & 63) >> 4, w = t >> 6;
+    {  // dM M^T as its transpose M dM^T (M's rows in registers); lane (lr, lq)
+       // then holds (dM M^T)[16 j + lr][16 w + 4 lq + v], written over dM once
+       // every wave has read it
+      f32x4 am[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int u = 0; u < 4; ++u) am[u] = ld4(im + Rec::M + (16 * w + lr) * C + 16 * u + 4 * lq);
+      f32x4 acc[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) sT[orow<4>(i)][ocol(j)] = a4[0][j][i];
-  }
-  barrier_lds();
-  {  // dA = -M^T (dM M^T) on s < r; its epilogue adds sum_s dA[r, s] At[r, s]
-     // to dbeta (At read before the product, at the lane's elements) and
-     // stores dA scaled by beta_r, the factor the pairwise terms take it
-     // with, over dM M^T in sT (read by the product when it returns)
-    float at[4][4];
+      for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) at[i][j] = im[Rec::AT + orow<4>(i) * C + ocol(j)];
-    f32x4 a4[1][4];
-    zero(a4);
-    gemm_staged2<4, 4, false, true>(a4, C, sa,
-                                   [&](int r, int u) { return im[Rec::M + u * C + r]; },
-                                   [&](int u, int s) { return sT[u][s]; });
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = orow<4>(i);
-      const float br = sB[r];
-      float part = 0.0f;
+          for (int s2 = 0; s2 < 4; ++s2)
+            acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(am[u][s2], sT[16 * j + lr][16 * u + 4 * lq + s2],
+                                                          acc[j], 0, 0, 0);
+      barrier_lds();  // dM read by every wave
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int s = ocol(j);
-        const float da = (s < r && r < Lc) ? -a4[0][j][i] : 0.0f;
-        part = fmaf(da, at[i][j], part);
-        sT[r][s] = da * br;
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) sT[16 * j + lr][16 * w + 4 * lq + v] = acc[j][v];
+    }
+    barrier_lds();
+    {  // dA = -M^T (dM M^T) on s < r; its epilogue adds sum_s dA[r, s] At[r, s]
+       // to dbeta (At read before the product, at the lane's elements) and
+       // stores dA scaled by beta_r, the factor the pairwise terms take it
+       // with, over dM M^T in sT once every wave has read that
+      float at[4][4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) at[i][j] = im[Rec::AT + orow<4>(i) * C + ocol(j)];
+      float mt[4][4];  // M^T row 16 w + lr: M[16 u + 4 lq + s][16 w + lr]
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) mt[u][s2] = im[Rec::M + (16 * u + 4 * lq + s2) * C + 16 * w + lr];
+      f32x4 a4[1][4];
+      zero(a4);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int s2 = 0; s2 < 4; ++s2)
+            a4[0][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(mt[u][s2], sT[16 * u + 4 * lq + s2][16 * j + lr],
+                                                            a4[0][j], 0, 0, 0);
+      barrier_lds();  // dM M^T read by every wave
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = orow<4>(i);
+        const float br = sB[r];
+        float part = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int s = ocol(j);
+          const float da = (s < r && r < Lc) ? -a4[0][j][i] : 0.0f;
+          part = fmaf(da, at[i][j], part);
+          sT[r][s] = da * br;
+        }
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) part += __shfl_xor(part, off);
+        if (tc == 0) sDB[r] += part;  // the 16 lanes holding row r
       }
-#pragma unroll
-      for (int off = 1; off < 16; off <<= 1) part += __shfl_xor(part, off);
-      if (tc == 0) sDB[r] += part;  // the 16 lanes holding row r
     }
   }
   {  // dK_E = -dX S^T, dQ_E = scale dO S^T, dK_D = Delta dS_next^T in one pipeline
