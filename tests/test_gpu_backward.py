@@ -235,16 +235,19 @@ def test_backward_config2_varlen_sampled_heads():
     check(sub, ref, "config 2 heads %s" % heads)
 
 
-def test_backward_config1_sampled_heads():
-    """T=4096, H=96 (the benchmarked prefill shape), bf16 q/k/v, bf16 d_o:
-    the whole backward on the GPU, sampled heads against the oracle."""
+@pytest.mark.parametrize("dodt", [torch.bfloat16, torch.float32])
+def test_backward_config1_sampled_heads(dodt):
+    """T=4096, H=96 (the benchmarked prefill shape), bf16 q/k/v, bf16 d_o (the
+    walk's products all on split-bf16 MFMA) or fp32 d_o (Z = A1 R and
+    Qt^T dO on the fp32 MFMA): the whole backward on the GPU, sampled heads
+    against the oracle."""
     need_gpu()
-    say("backward config 1 sampled heads")
+    say("backward config 1 sampled heads", dodt)
     dr = draw_config(1, device=DEV)
     g, beta = oracle_gate_f32(dr)
     H = CONFIGS[1]["H"]
     d_o = torch.randn(dr.q.shape[0], H, 128, generator=torch.Generator().manual_seed(77)).to(
-        torch.bfloat16)
+        dodt)
     got = kda.chunk_prefill_backward(dr.q, dr.k, dr.v, g.to(DEV), beta.to(DEV), d_o.to(DEV),
                                      dr.cu_seqlens.to(DEV), dr.initial_state,
                                      cu_seqlens_host=dr.cu_seqlens)
