@@ -483,15 +483,16 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 constexpr int ATP_LD = 17;  // row stride of the K / Q / gamma slabs (16 channels + 1)
+constexpr int ATP_GL = 2 * C + 2;  // row stride of gamma in LDS (all 128 channels)
 __device__ __forceinline__ void atp_diag(AtpDiag& d, int i, const float* sK, const float* sQ,
                                          const float* sG, int ch, int ln) {
   const int r = 16 * i + ln;
-  const float kr = sK[r * ATP_LD + ch], qr = sQ[r * ATP_LD + ch], gr = sG[r * ATP_LD + ch];
-  const float ga = sG[(16 * i + (ln < 8 ? 3 : 11)) * ATP_LD + ch];
+  const float kr = sK[r * ATP_LD + ch], qr = sQ[r * ATP_LD + ch], gr = sG[r * ATP_GL + ch];
+  const float ga = sG[(16 * i + (ln < 8 ? 3 : 11)) * ATP_GL + ch];
   const float e1 = __expf(gr - ga), b1 = kr * __expf(ga - gr);
   d.a1 = mfma4(kr * e1, b1, d.a1);
   d.p1 = mfma4(qr * e1, b1, d.p1);
-  const float g7 = sG[(16 * i + 7) * ATP_LD + ch];
+  const float g7 = sG[(16 * i + 7) * ATP_GL + ch];
   const bool lower = ln >= 8;  // row of the bottom half (A) / column of the top half (B)
   const float e3 = __expf(lower ? gr - g7 : g7 - gr);
   const float ka = lower ? kr * e3 : 0.0f, qa = lower ? qr * e3 : 0.0f;
@@ -506,14 +507,14 @@ __device__ __forceinline__ void atp_off(f32x4 (&oa)[3], f32x4 (&op)[3], int i, i
                                         int ch, int ln) {
   if (i == 0) return;
   const int r = 16 * i + ln;
-  const float gb = sG[(16 * i - 1) * ATP_LD + ch];
-  const float eo = __expf(sG[r * ATP_LD + ch] - gb);
+  const float gb = sG[(16 * i - 1) * ATP_GL + ch];
+  const float eo = __expf(sG[r * ATP_GL + ch] - gb);
   const float ka = sK[r * ATP_LD + ch] * eo, qa = sQ[r * ATP_LD + ch] * eo;
 #pragma unroll
   for (int j = 0; j < 3 - SLOT0; ++j) {
     if (j < n) {
       const int s = 16 * j + ln;
-      const float kb = sK[s * ATP_LD + ch] * __expf(gb - sG[s * ATP_LD + ch]);
+      const float kb = sK[s * ATP_LD + ch] * __expf(gb - sG[s * ATP_GL + ch]);
       oa[SLOT0 + j] = mfma4(ka, kb, oa[SLOT0 + j]);
       op[SLOT0 + j] = mfma4(qa, kb, op[SLOT0 + j]);
     }
@@ -555,18 +556,20 @@ __global__ void __launch_bounds__(NT, 3) bwd_prep_kernel(const void* __restrict_
                                                          int T_tot, int H, int maxnch,
                                                          float scale, float* __restrict__ img) {
   constexpr int CS = 16;  // channels per slab of the At / P sums
-  // At, P and M (three workgroups per CU); the At / P phase keeps its slabs of
-  // K, Q and gamma where M goes later, the products after M stage through At's
-  // place
+  // At, P and M (three workgroups per CU); the At / P phase keeps gamma (all
+  // channels) where At and P go later and its slabs of K and Q where M goes
+  // later, the products after M stage through At's place
   constexpr int SLAB = C * (CS + 1);
   __shared__ __attribute__((aligned(16))) float sPool[3 * C * (C + 1)];
   __shared__ float sB[C];
-  static_assert(3 * SLAB <= C * (C + 1) && STAGE_FLOATS <= C * (C + 1), "slabs fit");
+  static_assert(2 * SLAB <= C * (C + 1) && STAGE_FLOATS <= C * (C + 1), "slabs fit");
+  static_assert(C * ATP_GL <= 2 * C * (C + 1), "gamma fits in At's and P's place");
   static_assert(2 * (C + D) * SKP <= 2 * C * (C + 1), "paired slabs fit in At's and P's place");
   float(*sA)[C + 1] = reinterpret_cast<float(*)[C + 1]>(sPool);
   float(*sP)[C + 1] = reinterpret_cast<float(*)[C + 1]>(sPool + C * (C + 1));
   float(*sM)[C + 1] = reinterpret_cast<float(*)[C + 1]>(sPool + 2 * C * (C + 1));
   float* sS = sPool + 2 * C * (C + 1);  // the At / P slabs (over M)
+  float* sGam = sPool;                  // gamma [C][ATP_GL] until At and P are stored
   ChunkPos p;
   if (!chunk_of_block(cu, N, T_tot, H, maxnch, p, blockIdx.x)) return;
   const int t = threadIdx.x;
@@ -585,6 +588,7 @@ __global__ void __launch_bounds__(NT, 3) bwd_prep_kernel(const void* __restrict_
     for (int r = 0; r < C; ++r) {
       run += floor_decay(gv[r]);
       im[Rec::G + r * D + t] = run;
+      sGam[r * ATP_GL + t] = run;
     }
   }
   __syncthreads();
@@ -592,27 +596,22 @@ __global__ void __launch_bounds__(NT, 3) bwd_prep_kernel(const void* __restrict_
   {  // At and P (see atp_diag / atp_off): wave w sums the channels of half
      // w >> 1 for the row blocks {0, 3} (w even) or {1, 2} (w odd), 14
      // products per 4 channels either way.  Slab sl holds the channels
-     // 8 sl .. 8 sl + 7 (columns 0..7) and 64 + 8 sl .. 64 + 8 sl + 7 (8..15).
+     // 8 sl .. 8 sl + 7 (columns 0..7) and 64 + 8 sl .. 64 + 8 sl + 7 (8..15),
+     // so slab column ch of half hf is channel ch + 56 hf + 8 sl of gamma.
     float* sK = sS;
     float* sQ = sS + SLAB;
-    float* sG = sS + 2 * SLAB;
     const int l = t & 63, w = t >> 6, ln = l & 15, lq = l >> 4, hf = w >> 1;
     const int bA = w & 1, bB = 3 - bA;
-    for (int e = t; e < C * (C + 1); e += NT) {
-      (&sA[0][0])[e] = 0.0f;
-      (&sP[0][0])[e] = 0.0f;
-    }
     AtpDiag dA{}, dB{};
     f32x4 oa[3] = {}, op[3] = {};
     // thread t reads row t / 4, slab columns 4 (t % 4) .. + 3 (4 contiguous channels)
     static_assert(C * CS == 4 * NT, "one 4-channel group a thread");
     const int fr = t >> 2, fc = 4 * (t & 3);
-    f32x4 rk4, rq4, rg4;
+    f32x4 rk4, rq4;
     auto fetch_slab = [&](int sl) {
       const int cc = fc < 8 ? 8 * sl + fc : 64 + 8 * sl + fc - 8;
       rk4 = row4_at<QB>(rk, HDi, fr, cc);
       rq4 = row4_at<QB>(rq, HDi, fr, cc);
-      rg4 = *reinterpret_cast<const f32x4*>(im + Rec::G + fr * D + cc);
     };
     fetch_slab(0);
     for (int sl = 0; sl < D / CS; ++sl) {
@@ -620,10 +619,10 @@ __global__ void __launch_bounds__(NT, 3) bwd_prep_kernel(const void* __restrict_
       for (int i = 0; i < 4; ++i) {
         sK[fr * (CS + 1) + fc + i] = rk4[i];
         sQ[fr * (CS + 1) + fc + i] = rq4[i];
-        sG[fr * (CS + 1) + fc + i] = rg4[i];
       }
       barrier_lds();
       if (sl + 1 < D / CS) fetch_slab(sl + 1);
+      const float* sG = sGam + 56 * hf + 8 * sl;
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         const int ch = 8 * hf + 4 * kk + lq;
@@ -634,6 +633,15 @@ __global__ void __launch_bounds__(NT, 3) bwd_prep_kernel(const void* __restrict_
         if (bA == 1) atp_off<2>(oa, op, 1, 1, sK, sQ, sG, ch, ln);
       }
       barrier_lds();
+    }
+    // gamma is read for the last time above: the tiles above the diagonal
+    // (never summed) take zeros, the others are stored below
+    for (int e = t; e < C * (C + 1); e += NT) {
+      const int r = e / (C + 1), s2 = e % (C + 1);
+      if (s2 / 16 > r / 16) {
+        (&sA[0][0])[e] = 0.0f;
+        (&sP[0][0])[e] = 0.0f;
+      }
     }
     // the second channel half stores its sums, the first adds its own and
     // masks the diagonal tiles
