@@ -261,6 +261,27 @@ def test_backward_config1_sampled_heads(dodt):
     check(sub, ref, "config 1 heads %s" % heads)
 
 
+def test_backward_config1_every_head():
+    """T=4096, H=96, bf16 q/k/v and d_o: every head's gradients against the
+    oracle's (each tensor compared whole)."""
+    need_gpu()
+    say("backward config 1, every head")
+    dr = draw_config(1, device=DEV)
+    g, beta = oracle_gate_f32(dr)
+    H = CONFIGS[1]["H"]
+    d_o = torch.randn(dr.q.shape[0], H, 128, generator=torch.Generator().manual_seed(79)).to(
+        torch.bfloat16)
+    got = kda.chunk_prefill_backward(dr.q, dr.k, dr.v, g.to(DEV), beta.to(DEV), d_o.to(DEV),
+                                     dr.cu_seqlens.to(DEV), dr.initial_state,
+                                     cu_seqlens_host=dr.cu_seqlens)
+    torch.cuda.synchronize()
+    say("  oracle on all %d heads" % H)
+    S0 = None if dr.initial_state is None else dr.initial_state.cpu()
+    ref = oracle.prefill_backward(dr.q.cpu(), dr.k.cpu(), dr.v.cpu(), g, beta, dr.cu_seqlens,
+                                  S0, d_o=d_o.float())
+    check(got, ref, "config 1 every head")
+
+
 def test_backward_config3_long_sequence_sampled_head():
     """One sequence of 131,072 tokens, 96 heads (the long-context prefill
     workload) through the whole backward on the GPU: 2,048 chunk steps per

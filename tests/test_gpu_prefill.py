@@ -5,7 +5,8 @@ full-size workloads run the gated prefill in the one-pass launch
 configuration the bench times, and kda_gate then kda_chunk_prefill through
 the binding's capped workspace, both with an fp32 output held to the stated
 bound, and compare sampled heads (heads are independent) against the oracle
-gate then the oracle recurrence.
+gate then the oracle recurrence; the gated one-pass call is also compared on
+every head of each full-size workload.
 """
 import numpy as np
 import pytest
@@ -408,3 +409,73 @@ def test_gated_per_channel_alog(xdt):
     o_ref, S_ref = oracle.prefill(dr.q, dr.k, dr.v, gr, br, cu_h, dr.initial_state, scale=0.7)
     assert_out(o, o_ref, "gated per-channel A_log")
     assert_state(S, S_ref, "gated per-channel A_log")
+
+
+class _WholeTensor:
+    """The output and state metrics of the tolerances over every compared
+    head, accumulated over head groups: max |o_gpu - o_ref| over all of them
+    against their common RMS(o_ref), and the relative Frobenius error of all
+    their final states, as if the groups were one tensor."""
+
+    def __init__(self):
+        self.o_max, self.o_ss, self.o_n = 0.0, 0.0, 0
+        self.s_dd, self.s_rr = 0.0, 0.0
+
+    def add(self, o_gpu, o_ref, S_gpu, S_ref):
+        self.o_max = max(self.o_max, float(np.max(np.abs(to64(o_gpu) - o_ref))))
+        self.o_ss += float(np.sum(o_ref ** 2))
+        self.o_n += o_ref.size
+        self.s_dd += float(np.sum((to64(S_gpu) - S_ref) ** 2))
+        self.s_rr += float(np.sum(S_ref ** 2))
+
+    def errs(self):
+        rms = np.sqrt(self.o_ss / max(self.o_n, 1))
+        return self.o_max / max(rms, 1e-300), float(np.sqrt(self.s_dd / max(self.s_rr, 1e-300)))
+
+
+def _full_config_heads(idx, heads, group):
+    """Workload idx at full size through kda_chunk_prefill_gated in one pass
+    (the call the bench times, o fp32), compared on the given heads (groups
+    of `group` heads at a time against the oracle gate and recurrence) at the
+    stated bounds over all of them."""
+    c = CONFIGS[idx]
+    say("full config %d (%s), %d heads" % (idx, c["name"], len(heads)))
+    dr = draw_config(idx, device=DEV)
+    cu_h = dr.cu_seqlens
+    ws = _one_pass_workspace(cu_h, c["H"])
+    o, S = kda.chunk_prefill_gated(dr.q, dr.k, dr.v, dr.x, dr.b, dr.A_log, dr.dt_bias,
+                                   cu_h.to(DEV), dr.initial_state, cu_seqlens_host=cu_h,
+                                   o_dtype=torch.float32, workspace=ws)
+    torch.cuda.synchronize()
+    del ws
+    acc = _WholeTensor()
+    for i in range(0, len(heads), group):
+        hs = heads[i:i + group]
+        say("  oracle on heads %s .. %s" % (hs[0], hs[-1]))
+        gr, br = oracle_gate_f64(dr, hs)
+        S0 = None if dr.initial_state is None else dr.initial_state[:, hs].cpu()
+        o_ref, S_ref = oracle.prefill(dr.q[:, hs].cpu(), dr.k[:, hs].cpu(), dr.v[:, hs].cpu(),
+                                      gr, br, cu_h, S0)
+        acc.add(o[:, hs], o_ref, S[:, hs], S_ref)
+        del gr, br, o_ref, S_ref
+    eo, es = acc.errs()
+    say("  %d heads: fp32-o err / RMS %.3e (bound 5e-3), state rel-F %.3e (bound 1e-3)"
+        % (len(heads), eo, es))
+    assert eo <= O_TOL, "config %d output max-abs err %.3e x RMS" % (idx, eo)
+    assert es <= S_TOL, "config %d state rel-Frobenius err %.3e" % (idx, es)
+
+
+def test_config1_full_every_head():
+    need_gpu()
+    _full_config_heads(1, list(range(CONFIGS[1]["H"])), 96)
+
+
+def test_config2_full_every_head():
+    need_gpu()
+    _full_config_heads(2, list(range(CONFIGS[2]["H"])), 24)
+
+
+def test_config3_full_every_head():
+    """131,072 tokens (2,048 chunks a head), eight heads at a time."""
+    need_gpu()
+    _full_config_heads(3, list(range(CONFIGS[3]["H"])), 8)
