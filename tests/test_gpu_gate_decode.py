@@ -7,7 +7,7 @@ import oracle
 from synth import (CONFIGS, draw_alog_per_channel, draw_decode_params, draw_decode_step,
                    draw_prefill)
 from tests.gpu_util import DEV, need_gpu, oracle_gate_f32, say
-from tests.parity import assert_out, assert_state, out_err, state_err, to64
+from tests.parity import O_TOL, assert_out, assert_state, out_err, state_err, to64
 import gated_delta_rule_58_amd as kda
 
 pytestmark = pytest.mark.gpu
@@ -142,6 +142,42 @@ def test_decode_full_config_sampled():
         assert_out(o[ni, hi], o_ref[0], "decode step %d" % step)
     torch.cuda.synchronize()
     assert_state(state[ni, hi], S_ref, "decode after %d steps" % steps)
+
+
+def test_decode_full_config_every_pair():
+    """The same workload (256 sequences x 96 heads x 64 steps, HIP gate -> HIP
+    decode, fp32 state in place) with every (sequence, head) pair checked
+    against oracle gate -> oracle decode: o on every step against its RMS over
+    all pairs, the whole state after the last step by its Frobenius error."""
+    need_gpu()
+    c = CONFIGS[4]
+    N, H, steps, seed = c["N"], c["H"], c["steps"], c["seed"]
+    seqs = list(range(N))
+    say("decode full config N=%d H=%d steps=%d, every pair" % (N, H, steps))
+    A_log, dt_bias, S0 = draw_decode_params(N, H, seed=seed, device=DEV)
+    ni = torch.tensor([n for n in seqs for _ in range(H)])
+    hi = torch.tensor([h for _ in seqs for h in range(H)])
+    S_ref = to64(S0[ni, hi])                             # [pairs, 128, 128]
+    state = S0
+    o_max, o_ss, o_n = 0.0, 0.0, 0
+    for step in range(steps):
+        st = draw_decode_step(N, H, step, seed=seed, dtype=c["dtype"], device=DEV)
+        g, beta = kda.gate(st.x, st.b, A_log, dt_bias)
+        o = kda.recurrent_decode(st.q, st.k, st.v, g, beta, state, o_dtype=torch.float32)
+        gr, br = oracle.gate(st.x[ni, hi].cpu()[None], st.b[ni, hi].cpu()[None],
+                             A_log[hi].cpu(), dt_bias[hi].cpu())
+        o_ref, S_ref = oracle.decode(st.q[ni, hi].cpu()[None], st.k[ni, hi].cpu()[None],
+                                     st.v[ni, hi].cpu()[None], gr, br, S_ref[None])
+        S_ref = S_ref[0]
+        o_max = max(o_max, float(np.max(np.abs(to64(o[ni, hi]) - o_ref[0]))))
+        o_ss += float(np.sum(o_ref ** 2))
+        o_n += o_ref.size
+    torch.cuda.synchronize()
+    eo = o_max / max(np.sqrt(o_ss / o_n), 1e-300)
+    say("  o err / RMS over %d steps %.3e (bound 5e-3)" % (steps, eo))
+    assert eo <= O_TOL, "decode o max-abs err %.3e x RMS" % eo
+    es = assert_state(state[ni, hi], S_ref, "decode after %d steps" % steps)
+    say("  state rel-F after %d steps %.3e (bound 1e-3)" % (steps, es))
 
 
 def test_decode_deterministic():
