@@ -235,6 +235,42 @@ def test_backward_config2_varlen_sampled_heads():
     check(sub, ref, "config 2 heads %s" % heads)
 
 
+def test_backward_config2_every_head():
+    """The varlen workload (8 sequences, 32,768 tokens, initial states) with
+    every head against the oracle, 24 heads at a time; each gradient tensor's
+    max-abs error over all heads against its RMS over all heads."""
+    need_gpu()
+    say("backward config 2, every head")
+    dr = draw_config(2, device=DEV)
+    g, beta = oracle_gate_f32(dr)
+    H = CONFIGS[2]["H"]
+    d_o = torch.randn(dr.q.shape[0], H, 128, generator=torch.Generator().manual_seed(89)).to(
+        torch.bfloat16)
+    got = kda.chunk_prefill_backward(dr.q, dr.k, dr.v, g.to(DEV), beta.to(DEV), d_o.to(DEV),
+                                     dr.cu_seqlens.to(DEV), dr.initial_state,
+                                     cu_seqlens_host=dr.cu_seqlens)
+    torch.cuda.synchronize()
+    mx = {n: 0.0 for n in NAMES}
+    ss = {n: 0.0 for n in NAMES}
+    cnt = {n: 0 for n in NAMES}
+    for h0 in range(0, H, 24):
+        hs = list(range(h0, min(H, h0 + 24)))
+        say("  oracle on heads %d .. %d" % (hs[0], hs[-1]))
+        S0 = None if dr.initial_state is None else dr.initial_state[:, hs].cpu()
+        ref = oracle.prefill_backward(dr.q[:, hs].cpu(), dr.k[:, hs].cpu(), dr.v[:, hs].cpu(),
+                                      g[:, hs], beta[:, hs], dr.cu_seqlens, S0,
+                                      d_o=d_o[:, hs].float())
+        for n, a, b in zip(NAMES, got, ref):
+            mx[n] = max(mx[n], float(np.max(np.abs(to64(a[:, hs]) - b))))
+            ss[n] += float(np.sum(b ** 2))
+            cnt[n] += b.size
+        del ref
+    errs = {n: mx[n] / max(np.sqrt(ss[n] / cnt[n]), 1e-30) for n in NAMES}
+    say("config 2 every head", " ".join("%s %.2e" % kv for kv in errs.items()))
+    for n, e in errs.items():
+        assert e <= GRAD_TOL, ("config 2 every head", n, e)
+
+
 @pytest.mark.parametrize("dodt", [torch.bfloat16, torch.float32])
 def test_backward_config1_sampled_heads(dodt):
     """T=4096, H=96 (the benchmarked prefill shape), bf16 q/k/v, bf16 d_o (the
