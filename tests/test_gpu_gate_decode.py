@@ -7,7 +7,8 @@ import oracle
 from synth import (CONFIGS, draw_alog_per_channel, draw_decode_params, draw_decode_step,
                    draw_prefill)
 from tests.gpu_util import DEV, need_gpu, oracle_gate_f32, say
-from tests.parity import O_TOL, assert_out, assert_state, out_err, state_err, to64
+from tests.parity import (O_TOL, S_TOL_BF16_CHAINS, assert_out, assert_state, out_err,
+                          out_err_bf16_state, state_err, to64)
 import gated_delta_rule_58_amd as kda
 
 pytestmark = pytest.mark.gpu
@@ -296,10 +297,14 @@ def test_decode_gated_state_pool(sdt):
         assert_state(pool[idx[n]], S_ref[n], "pool slot %d" % idx[n])
 
 
-def test_decode_gated_full_size_bf16_sampled():
+def test_decode_gated_full_size_bf16_every_pair():
     """256 sequences x 96 heads, bf16 state pool of 256 slots addressed through
-    a permutation, bf16 logits, 8 steps; sampled (sequence, head) pairs against
-    the oracle gate and step with the state rounded to bf16 after each step."""
+    a permutation, bf16 logits, 8 steps; every (sequence, head) pair against
+    the oracle gate and step with the state rounded to bf16 after each step.
+    Both chains round their state to bf16 after every step, so an element
+    whose two pre-rounding values straddle a rounding boundary differs by one
+    bf16 step between them: o is held to the bound for outputs of such state
+    pairs, and the final states to the one for two rounding chains."""
     need_gpu()
     c = CONFIGS[4]
     N, H, seed, steps = c["N"], c["H"], c["seed"], 8
@@ -308,12 +313,10 @@ def test_decode_gated_full_size_bf16_sampled():
     pool = S0.to(torch.bfloat16)
     perm = torch.randperm(N, generator=torch.Generator().manual_seed(7)).to(torch.int32)
     ind = perm.to(DEV)
-    rng = np.random.default_rng(9)
-    pairs = [(int(a), int(b)) for a, b in zip(rng.integers(0, N, 24), rng.integers(0, H, 24))]
-    ni = torch.tensor([p[0] for p in pairs])
-    hi = torch.tensor([p[1] for p in pairs])
+    ni = torch.arange(N).repeat_interleave(H)
+    hi = torch.arange(H).repeat(N)
     si = perm[ni].long()
-    S_ref = to64(pool[si, hi])                            # [24, 128, 128]
+    S_ref = to64(pool[si, hi])                            # [N H, 128, 128]
     for step in range(steps):
         st = draw_decode_step(N, H, step, seed=seed, dtype=torch.bfloat16, device=DEV)
         x, b = st.x.to(torch.bfloat16), st.b.to(torch.bfloat16)
@@ -321,9 +324,11 @@ def test_decode_gated_full_size_bf16_sampled():
                                        state_indices=ind, o_dtype=torch.float32)
         gr, br = oracle.gate(x[ni, hi].cpu()[None].float(), b[ni, hi].cpu()[None].float(),
                              A_log[hi].cpu(), dt_bias[hi].cpu())
-        o_ref, S_new = oracle.decode(st.q[ni, hi].cpu()[None], st.k[ni, hi].cpu()[None],
-                                     st.v[ni, hi].cpu()[None], gr, br, S_ref[None])
+        qp, kp = st.q[ni, hi].cpu()[None], st.k[ni, hi].cpu()[None]
+        o_ref, S_new = oracle.decode(qp, kp, st.v[ni, hi].cpu()[None], gr, br, S_ref[None])
+        e = out_err_bf16_state(o[ni, hi][None], o_ref, S_ref[None], qp, kp, br, np.exp(gr))
+        assert e <= 1.0, "bf16 pool step %d: err ratio %.3f" % (step, e)
         S_ref = _bf16_round(S_new[0])
-        assert_out(o[ni, hi], o_ref[0], "bf16 pool step %d" % step)
     torch.cuda.synchronize()
-    assert_state(pool[si, hi], S_ref, "bf16 pool after %d steps" % steps)
+    assert_state(pool[si, hi], S_ref, "bf16 pool after %d steps" % steps,
+                 tol=S_TOL_BF16_CHAINS)
